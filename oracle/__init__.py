@@ -1,0 +1,14 @@
+"""CPU oracle for the ternary linear layer -- test infrastructure only.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It shares no code with the HIP library.
+"""
+from .tq_oracle import *  # noqa: F401,F403
+from .tq_oracle import (absmean_scale, absmean_scales, binarize, contract,
+                        contract_rows, epilogue, exact_abs_sum_units,
+                        exact_fraction_mean, fwht512, fwht_block,
+                        hadamard_matrix, pack_codes, pack_ternary,
+                        packed_bytes, quant_act_int8, rms_factor,
+                        rmsnorm_fwht_quant, rmsnorm_fwht_quant_literal,
+                        round_rational_to_f32, ternarize, ternary_linear,
+                        unpack_codes, bf16_round_from_f64, FWHT_NORM)

@@ -1,0 +1,461 @@
+"""CPU oracle for the ternary (absmean, 2-bit) linear layer.
+
+TEST INFRASTRUCTURE ONLY.  This module is the plain, slow reference that the
+HIP library is checked against.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import it; the product path never does.  It
+shares no code with the HIP library.
+
+Sources (cited by page title and section):
+
+* Foundry, docs/quantization.md -- "Ternary Format / Encoding" (2-bit codes,
+  LSB-first byte layout, packed size), "Ternary Quantization (BitNet b1.58) /
+  How It Works" (absmean scale, round-and-clamp), "Native Matmul Kernel"
+  (add/sub/skip contraction, then the scale).
+* Hetman-2b, src/quantization.py -- section 1 (FWHT-512 butterfly and its
+  1/sqrt(512) normaliser), section 2 (absmean weight quantizer, symmetric
+  int8 activation quantizer), section 4 (RMSNorm), section 5 (BitLinear order
+  of operations and its scale fusion), section 7 (integer GEMV emulator).
+* BitRASP, core_math.py -- ``fake_quant_int`` (per-token absmax int8),
+  ``ternarize_weight`` (per-output-row absmean), ``additive_ternary_linear_int8``
+  (y[o] = sum of x where W=+1 minus sum of x where W=-1).
+* qste 0.1.1 project description -- "What it costs and what it buys"
+  (binary +-1 weights with a per-row scale).
+
+Readings taken where the pages are silent or disagree (each is also listed
+in the design notes):
+
+* The absmean scale is the correctly rounded fp32 value of the exact mean of
+  |w| over the group, then floored at fp32(1e-6).  The pages compute the mean
+  in fp32 without fixing a summation order; the exact mean is the one value
+  every order approximates.
+* Weights are ternarized by round-half-even of the fp32 quotient w/gamma,
+  clamped to [-1, 1] (Foundry "How It Works", Hetman-2b section 2).  The
+  "Absmean Thresholding" block of the Foundry page (|w| > gamma) is not used.
+* Binary mode: +1 where w >= 0, else -1, with the same per-row absmean scale.
+* Activations: per-token eta = max|x| floored at 1e-6, optional clamp to
+  [eta_min, eta_max]; s = fp32(127/eta); q = clamp(rint(fp32(x*s)), -127, 127);
+  the dequantisation scale returned is sx = fp32(eta/127).
+* A partial last byte (only possible when the element count is not a multiple
+  of four) is padded with the zero code 0b01.
+* The fused RMSNorm -> FWHT -> int8 prologue uses the exact cancellation of
+  the positive per-token RMS factor and the 1/sqrt(512) normaliser inside
+  absmax quantisation (see ``rmsnorm_fwht_quant``).
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+F32 = np.float32
+GAMMA_EPS = F32(1e-6)          # floor on the absmean scale (Hetman-2b s.2, BitRASP)
+ACT_EPS = F32(1e-6)            # floor on the activation absmax (Hetman-2b s.2)
+QMAX = 127                     # symmetric int8 bound (Hetman-2b s.2)
+FWHT_BLOCK = 512               # Hetman-2b s.0
+FWHT_NORM = F32(1.0 / np.sqrt(512.0))   # fp32(1/sqrt(512)), Hetman-2b s.0 / s.1
+ETA_MIN_BITLINEAR = 0.05       # gain clamp used by BitLinear, Hetman-2b s.0 / s.5
+ETA_MAX_BITLINEAR = 40.0
+RMS_EPS = F32(1e-6)            # Hetman-2b s.4
+
+# --------------------------------------------------------------------------
+# Sizes
+# --------------------------------------------------------------------------
+
+
+def packed_bytes(numel: int) -> int:
+    """Bytes of a packed ternary tensor: (numel + 3) / 4, rounded down
+    (Foundry, "Ternary Format / Encoding")."""
+    return (int(numel) + 3) // 4
+
+
+# --------------------------------------------------------------------------
+# Exact rational arithmetic for the absmean scale
+# --------------------------------------------------------------------------
+
+
+def round_rational_to_f32(num: int, den: int) -> np.float32:
+    """Round the non-negative rational num/den to the nearest fp32, ties to
+    even (IEEE 754 roundTiesToEven).  Subnormal results use the fixed quantum
+    2**-149.  Raises OverflowError past the fp32 range."""
+    num, den = int(num), int(den)
+    if den <= 0 or num < 0:
+        raise ValueError("need num >= 0 and den > 0")
+    if num == 0:
+        return F32(0.0)
+    # exponent e with 2**e <= num/den < 2**(e+1)
+    e = num.bit_length() - den.bit_length()
+    if (num << max(-e, 0)) < (den << max(e, 0)):
+        e -= 1
+    e = max(e, -126)                      # below 2**-126 the spacing stays 2**-149
+    shift = 23 - e                        # scale so the quantum 2**(e-23) becomes 1
+    if shift >= 0:
+        n2, d2 = num << shift, den
+    else:
+        n2, d2 = num, den << (-shift)
+    m, r = divmod(n2, d2)
+    if 2 * r > d2 or (2 * r == d2 and (m & 1)):
+        m += 1
+    value = m * 2.0 ** (e - 23)           # exact in fp64: m <= 2**24
+    if value > float(np.finfo(np.float32).max):
+        raise OverflowError("result exceeds the fp32 range")
+    return F32(value)
+
+
+def exact_abs_sum_units(w: np.ndarray) -> int:
+    """Exact sum of |w| over a finite fp32 array, as an integer count of the
+    smallest fp32 quantum 2**-149.
+
+    Each finite fp32 magnitude is M * 2**(b-150) with b = max(E, 1), E the
+    biased exponent and M the 24-bit significand (implicit bit included when
+    E > 0), i.e. M << (b-1) quanta.  Significands are summed per exponent in
+    uint64 (exact while the group holds fewer than 2**40 elements) and the
+    per-exponent totals are combined as Python integers."""
+    a = np.ascontiguousarray(w, dtype=np.float32).ravel()
+    if not np.all(np.isfinite(a)):
+        raise ValueError("non-finite input")
+    bits = a.view(np.uint32) & np.uint32(0x7FFFFFFF)
+    expo = (bits >> np.uint32(23)).astype(np.int64)
+    mant = (bits & np.uint32(0x7FFFFF)).astype(np.uint64)
+    mant = np.where(expo > 0, mant | np.uint64(1 << 23), mant)
+    b = np.maximum(expo, 1)
+    total = 0
+    for e in np.unique(b):
+        s = int(mant[b == e].sum(dtype=np.uint64))
+        total += s << (int(e) - 1)
+    return total
+
+
+def absmean_scale(w_group: np.ndarray) -> np.float32:
+    """gamma = max(fp32(mean |w|), fp32(1e-6)) with the mean taken exactly and
+    rounded once (Foundry "How It Works" step 1; Hetman-2b s.2 absmean with
+    clamp(min=eps); BitRASP ``ternarize_weight`` per-row variant)."""
+    n = int(np.asarray(w_group).size)
+    if n == 0:
+        raise ValueError("absmean of an empty group is undefined")
+    total = exact_abs_sum_units(w_group)
+    gamma = round_rational_to_f32(total, n << 149)
+    return max(gamma, GAMMA_EPS)
+
+
+def absmean_scales(W: np.ndarray, granularity: str) -> np.ndarray:
+    """Scales for W [N, K]: one for the whole tensor ("tensor") or one per
+    output row ("row", Foundry per-channel ternary; BitRASP per-output scale)."""
+    W = np.asarray(W, dtype=np.float32)
+    if granularity == "tensor":
+        return np.array([absmean_scale(W)], dtype=np.float32)
+    if granularity == "row":
+        return np.array([absmean_scale(W[i]) for i in range(W.shape[0])],
+                        dtype=np.float32)
+    raise ValueError(granularity)
+
+
+# --------------------------------------------------------------------------
+# Weight codes and packing
+# --------------------------------------------------------------------------
+
+
+def ternarize(W: np.ndarray, gammas: np.ndarray) -> np.ndarray:
+    """q = clamp(rint(fp32(w / gamma)), -1, 1), round half to even
+    (Foundry "How It Works" step 2; Hetman-2b s.2 forward).  ``gammas`` holds
+    one scale, or one per row of W."""
+    W = np.asarray(W, dtype=np.float32)
+    g = np.asarray(gammas, dtype=np.float32)
+    g = g.reshape(-1, 1) if g.size > 1 else g.reshape(1, 1)
+    t = W / g                                   # IEEE fp32 division
+    return np.clip(np.rint(t), -1, 1).astype(np.int8)
+
+
+def binarize(W: np.ndarray) -> np.ndarray:
+    """Binary (+-1) weights: +1 where w >= 0 (zero and -0.0 included), else -1
+    (qste "What it costs and what it buys": a matrix of +-1 and a per-row scale)."""
+    W = np.asarray(W, dtype=np.float32)
+    return np.where(W >= 0, 1, -1).astype(np.int8)
+
+
+def pack_codes(q: np.ndarray) -> np.ndarray:
+    """Pack ternary values along the last axis, four per byte, LSB-first, with
+    -1 -> 0b00, 0 -> 0b01, +1 -> 0b10 (Foundry "Ternary Format / Encoding").
+    A partial last byte is padded with the zero code 0b01."""
+    q = np.asarray(q)
+    if q.ndim == 1:
+        q = q.reshape(1, -1)
+    if q.size and (q.min() < -1 or q.max() > 1):
+        raise ValueError("values outside {-1, 0, 1}")
+    n, k = q.shape
+    nb = packed_bytes(k)
+    codes = np.ones((n, nb * 4), dtype=np.uint8)            # 0b01 padding
+    codes[:, :k] = (q.astype(np.int16) + 1).astype(np.uint8)
+    codes = codes.reshape(n, nb, 4)
+    out = np.zeros((n, nb), dtype=np.uint8)
+    for slot in range(4):
+        out |= codes[:, :, slot] << np.uint8(2 * slot)
+    return out
+
+
+def unpack_codes(packed: np.ndarray, k: int) -> np.ndarray:
+    """Inverse of ``pack_codes`` for rows of k values.  The unused code 0b11
+    is rejected."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    if packed.ndim == 1:
+        packed = packed.reshape(1, -1)
+    n, nb = packed.shape
+    if nb != packed_bytes(k):
+        raise ValueError("row length does not match k")
+    codes = np.empty((n, nb, 4), dtype=np.uint8)
+    for slot in range(4):
+        codes[:, :, slot] = (packed >> np.uint8(2 * slot)) & np.uint8(3)
+    if np.any(codes == 3):
+        raise ValueError("code 0b11 is not a ternary value")
+    codes = codes.reshape(n, nb * 4)[:, :k]
+    return (codes.astype(np.int16) - 1).astype(np.int8)
+
+
+def pack_ternary(W: np.ndarray, granularity: str = "tensor", mode: str = "ternary"):
+    """Absmean scale(s) + codes + 2-bit packing of W [N, K] (rows along K).
+    Returns (packed uint8 [N, ceil(K/4)], scales fp32 [1] or [N])."""
+    W = np.asarray(W, dtype=np.float32)
+    gam = absmean_scales(W, granularity)
+    if mode == "ternary":
+        q = ternarize(W, gam)
+    elif mode == "binary":
+        q = binarize(W)
+    else:
+        raise ValueError(mode)
+    return pack_codes(q), gam
+
+
+# --------------------------------------------------------------------------
+# Activations
+# --------------------------------------------------------------------------
+
+
+def quant_act_int8(X: np.ndarray, eps=ACT_EPS, eta_min=None, eta_max=None):
+    """Per-token symmetric int8 quantisation (Hetman-2b s.2, reduced over the
+    last axis as its code does; BitRASP ``fake_quant_int`` is per-token too).
+
+    eta = max(max_k |x|, eps), optionally clamped to [eta_min, eta_max];
+    s = fp32(127 / eta); q = clamp(rint(fp32(x * s)), -127, 127);
+    returns (q int8 [M, K], sx fp32 [M] = fp32(eta / 127))."""
+    x = np.asarray(X, dtype=np.float32)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("non-finite input")
+    eta = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], F32)
+    eta = np.maximum(eta, F32(eps)).astype(np.float32)
+    if eta_min is not None and eta_max is not None:
+        eta = np.clip(eta, F32(eta_min), F32(eta_max)).astype(np.float32)
+    s = (F32(QMAX) / eta).astype(np.float32)
+    q = np.clip(np.rint(x * s[:, None]), -QMAX, QMAX).astype(np.int8)
+    sx = (eta / F32(QMAX)).astype(np.float32)
+    return q, sx
+
+
+# --------------------------------------------------------------------------
+# Walsh-Hadamard rotation
+# --------------------------------------------------------------------------
+
+
+def fwht_block(x: np.ndarray, normalize: bool) -> np.ndarray:
+    """Fast Walsh-Hadamard transform of length-512 rows in fp32
+    (Hetman-2b s.1): nine butterfly stages with half-widths h = 1, 2, ..., 256
+    in that order; at each stage every index i whose bit h is clear is paired
+    with i + h and the pair becomes (x_i + x_{i+h}, x_i - x_{i+h}).  When
+    normalising, the result is multiplied by fp32(1/sqrt(512)) after the last
+    stage."""
+    y = np.array(x, dtype=np.float32, copy=True)
+    if y.shape[-1] != FWHT_BLOCK:
+        raise ValueError("last axis must be 512")
+    idx = np.arange(FWHT_BLOCK)
+    h = 1
+    while h < FWHT_BLOCK:
+        lo = idx[(idx & h) == 0]
+        hi = lo + h
+        a = y[..., lo].copy()
+        b = y[..., hi].copy()
+        y[..., lo] = a + b
+        y[..., hi] = a - b
+        h *= 2
+    if normalize:
+        y = (y * FWHT_NORM).astype(np.float32)
+    return y
+
+
+def fwht512(X: np.ndarray, normalize: bool = True) -> np.ndarray:
+    """Blockwise FWHT over consecutive 512-wide blocks of the last axis, which
+    must be a multiple of 512 (Hetman-2b s.1, ``blockwise_fwht_forward``)."""
+    x = np.asarray(X, dtype=np.float32)
+    d = x.shape[-1]
+    if d % FWHT_BLOCK:
+        raise ValueError("last axis must be a multiple of 512")
+    blocks = x.reshape(*x.shape[:-1], d // FWHT_BLOCK, FWHT_BLOCK)
+    return fwht_block(blocks, normalize).reshape(x.shape)
+
+
+def rms_factor(x_row: np.ndarray) -> np.float32:
+    """r = fp32(1 / fp32(sqrt(fp32(mean(x^2)) + fp32(1e-6)))) (Hetman-2b s.4).
+    The mean of squares is formed in fp64 and rounded once; inputs whose
+    squares sum exactly in fp32 (every |x| a power of two, for instance) give
+    the same r from any summation order."""
+    x64 = np.asarray(x_row, dtype=np.float64)
+    ms = F32(np.sum(x64 * x64) / x64.size)
+    t = F32(ms + RMS_EPS)
+    return F32(F32(1.0) / np.sqrt(t, dtype=np.float32))
+
+
+def rmsnorm_fwht_quant(X: np.ndarray, eta_min=ETA_MIN_BITLINEAR,
+                       eta_max=ETA_MAX_BITLINEAR, rms_weight=None):
+    """BitLinear activation prologue (Hetman-2b s.5: RMSNorm -> blockwise
+    normalised FWHT-512 -> per-token int8 with gain clamp), evaluated through
+    the exact cancellation of positive per-token factors.
+
+    With z = FWHT_unnormalised(g * x) (fp32, butterfly order above), r the RMS
+    factor and c = fp32(1/sqrt(512)), the rotated activation is r*c*z and its
+    absmax is eta_true = r*c*max|z|.  Absmax codes do not change under a
+    positive per-token factor, so while the floor/clamp leaves eta_true as it
+    is, q is the plain quantiser applied to z with eta = max|z| (q = 0 for a
+    zero token) and the dequantisation scale is eta_true/127.  When the eps
+    floor or the [eta_min, eta_max] clamp moves eta to eta_eff, the codes are
+    q = clamp(rint(fp32(z * m)), -127, 127) with
+    m = fp32(fp32(r*c) * fp32(127/eta_eff)) and sx = fp32(eta_eff/127); here r
+    is the fp32 factor of ``rms_factor``.
+
+    Returns (q int8 [M, K], sx fp32 [M], sx_exact fp64 [M], bound bool [M]);
+    sx_exact is eta_eff/127 in fp64 (with the fp64 RMS factor when nothing
+    binds) for tolerance checks."""
+    xin = np.asarray(X, dtype=np.float32)
+    if xin.ndim == 1:
+        xin = xin.reshape(1, -1)
+    x = xin
+    if rms_weight is not None:
+        x = (x * np.asarray(rms_weight, dtype=np.float32)[None, :]).astype(np.float32)
+    z = fwht512(x, normalize=False)
+    M = x.shape[0]
+    q = np.empty(x.shape, dtype=np.int8)
+    sx = np.empty(M, dtype=np.float32)
+    sx_exact = np.empty(M, dtype=np.float64)
+    bound = np.zeros(M, dtype=bool)
+    c64 = float(FWHT_NORM)
+    for i in range(M):
+        x64 = xin[i].astype(np.float64)
+        r64 = 1.0 / np.sqrt(np.mean(x64 * x64) + float(RMS_EPS))
+        eta_z = F32(np.max(np.abs(z[i])))
+        eta_true = r64 * c64 * float(eta_z)
+        eta_eff = max(eta_true, float(ACT_EPS))
+        if eta_min is not None and eta_max is not None:
+            eta_eff = min(max(eta_eff, float(F32(eta_min))), float(F32(eta_max)))
+        if eta_eff == eta_true:
+            if eta_z == 0:
+                q[i] = 0
+            else:
+                s = F32(F32(QMAX) / eta_z)
+                q[i] = np.clip(np.rint(z[i] * s), -QMAX, QMAX).astype(np.int8)
+            sx[i] = F32(eta_true / QMAX)
+            sx_exact[i] = eta_true / QMAX
+        else:
+            bound[i] = True
+            e32 = F32(eta_eff)
+            r = rms_factor(xin[i])
+            m = F32(F32(r * FWHT_NORM) * F32(F32(QMAX) / e32))
+            q[i] = np.clip(np.rint(z[i] * m), -QMAX, QMAX).astype(np.int8)
+            sx[i] = F32(e32 / F32(QMAX))
+            sx_exact[i] = float(e32) / QMAX
+    return q, sx, sx_exact, bound
+
+
+def rmsnorm_fwht_quant_literal(X: np.ndarray, eta_min=ETA_MIN_BITLINEAR,
+                               eta_max=ETA_MAX_BITLINEAR):
+    """The same prologue evaluated step by step in fp64 (RMSNorm, normalised
+    FWHT, clamp, scale, round) -- used only to bound how far the fp32 fold
+    above can move a code (by at most one, at rounding boundaries)."""
+    x = np.asarray(X, dtype=np.float64)
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    xn = x / np.sqrt(ms + 1e-6)
+    H = hadamard_matrix(FWHT_BLOCK).astype(np.float64) / np.sqrt(512.0)
+    M, K = x.shape
+    xr = (xn.reshape(M, K // FWHT_BLOCK, FWHT_BLOCK) @ H.T).reshape(M, K)
+    eta = np.maximum(np.max(np.abs(xr), axis=1), 1e-6)
+    if eta_min is not None and eta_max is not None:
+        eta = np.clip(eta, eta_min, eta_max)
+    q = np.clip(np.rint(xr * (127.0 / eta)[:, None]), -127, 127).astype(np.int8)
+    return q, eta / 127.0
+
+
+def hadamard_matrix(n: int) -> np.ndarray:
+    """Sylvester-ordered Hadamard matrix H[i, j] = (-1)**popcount(i & j), int64."""
+    i = np.arange(n).reshape(-1, 1)
+    j = np.arange(n).reshape(1, -1)
+    v = i & j
+    pc = np.zeros_like(v)
+    while np.any(v):
+        pc += v & 1
+        v >>= 1
+    return np.where(pc % 2 == 0, 1, -1).astype(np.int64)
+
+
+# --------------------------------------------------------------------------
+# Contraction and epilogue
+# --------------------------------------------------------------------------
+
+
+def contract(q: np.ndarray, packed: np.ndarray, k: int) -> np.ndarray:
+    """acc[m, o] = sum_k q[m, k] * w[o, k] in int64 over the unpacked weight
+    codes (the add/sub/skip contraction of Foundry "Native Matmul Kernel" and
+    Hetman-2b s.7, which is this integer matrix product).  Returns int64 and
+    checks that every value fits in int32."""
+    w = unpack_codes(packed, k).astype(np.int64)
+    acc = np.asarray(q, dtype=np.int64) @ w.T
+    if acc.size and (acc.max() > 2**31 - 1 or acc.min() < -2**31):
+        raise OverflowError("accumulator exceeds int32")
+    return acc
+
+
+def contract_rows(q: np.ndarray, packed: np.ndarray, k: int, rows) -> np.ndarray:
+    """``contract`` restricted to the output rows ``rows`` -> int64 [M, len(rows)]."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return contract(q, np.asarray(packed)[rows], k)
+
+
+def epilogue(acc: np.ndarray, gammas: np.ndarray, sx: np.ndarray,
+             rows=None) -> np.ndarray:
+    """y[m, o] = acc[m, o] * gamma_o * sx_m evaluated in fp64 from the exact
+    accumulator (Foundry "How It Works" step 4: scale after the integer loop;
+    Hetman-2b s.5/s.7 scale fusion).  ``gammas`` is one scale or one per row;
+    ``rows`` selects the per-row scales of a column subset."""
+    g = np.asarray(gammas, dtype=np.float64).ravel()
+    if g.size > 1 and rows is not None:
+        g = g[np.asarray(rows)]
+    g = g.reshape(1, -1) if g.size > 1 else g.reshape(1, 1)
+    s = np.asarray(sx, dtype=np.float64).reshape(-1, 1)
+    return np.asarray(acc, dtype=np.float64) * g * s
+
+
+def bf16_round_from_f64(y: np.ndarray) -> np.ndarray:
+    """fp64 -> nearest fp32 -> nearest bf16 (ties to even), returned as fp32.
+    Used only to state the bf16-output tolerance."""
+    a = np.asarray(y, dtype=np.float64).astype(np.float32)
+    bits = a.view(np.uint32).astype(np.uint64)
+    lsb = (bits >> np.uint64(16)) & np.uint64(1)
+    bits = (bits + np.uint64(0x7FFF) + lsb) >> np.uint64(16) << np.uint64(16)
+    return bits.astype(np.uint32).view(np.float32)
+
+
+def ternary_linear(X: np.ndarray, W: np.ndarray, granularity: str = "tensor",
+                   mode: str = "ternary", prologue: bool = False):
+    """Whole layer: pack W, quantise X (with the BitLinear prologue if asked),
+    contract, rescale.  Returns a dict of every intermediate."""
+    packed, gam = pack_ternary(W, granularity, mode)
+    if prologue:
+        q, sx, _, _ = rmsnorm_fwht_quant(X)
+    else:
+        q, sx = quant_act_int8(X)
+    k = np.asarray(W).shape[1]
+    acc = contract(q, packed, k)
+    y = epilogue(acc, gam, sx)
+    return dict(packed=packed, scale=gam, q=q, sx=sx, acc=acc, y=y)
+
+
+def exact_fraction_mean(w: np.ndarray) -> Fraction:
+    """Mean of |w| as an exact Fraction (slow; for small arrays in tests)."""
+    vals = [Fraction(float(abs(v))) for v in np.asarray(w, dtype=np.float32).ravel()]
+    return sum(vals, Fraction(0)) / len(vals)

@@ -1,0 +1,520 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: worked
+values from the pages (tests/golden/), closed forms, exact rational
+arithmetic, textbook special cases and brute force on tiny inputs.
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import tq_inputs as ti
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def _golden(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            a, b = (p.strip() for p in line.split(";"))
+            rows.append((a, b))
+    return rows
+
+
+def _f32(bits):
+    return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+
+
+# ---------------------------------------------------------------- sizes / pack
+
+def test_packed_size_golden():
+    for a, b in _golden("sizes.txt"):
+        assert oracle.packed_bytes(int(a)) == int(b)
+
+
+def test_pack_worked_bytes_golden():
+    for a, b in _golden("pack_worked_bytes.txt"):
+        vals = np.array([int(v) for v in a.split(",")], dtype=np.int8)
+        want = np.array([int(h, 16) for h in b.split()], dtype=np.uint8)
+        got = oracle.pack_codes(vals)[0]
+        np.testing.assert_array_equal(got, want)
+        np.testing.assert_array_equal(oracle.unpack_codes(got, vals.size)[0], vals)
+
+
+def test_pack_roundtrip_64x1536():
+    # the pack/unpack identity at the shape Hetman-2b s.8 test 5 uses
+    q = ti.random_ternary(5, 64, 1536)
+    p = oracle.pack_codes(q)
+    assert p.shape == (64, 384)
+    np.testing.assert_array_equal(oracle.unpack_codes(p, 1536), q)
+
+
+def test_pack_bit_positions_exhaustive():
+    # every 4-tuple of values maps to the byte whose 2-bit field j holds v_j + 1
+    for a in range(-1, 2):
+        for b in range(-1, 2):
+            for c in range(-1, 2):
+                for d in range(-1, 2):
+                    byte = oracle.pack_codes(np.array([a, b, c, d]))[0, 0]
+                    fields = [(int(byte) >> (2 * j)) & 3 for j in range(4)]
+                    assert fields == [a + 1, b + 1, c + 1, d + 1]
+                    assert 3 not in fields
+
+
+def test_unpack_rejects_code_11():
+    with pytest.raises(ValueError):
+        oracle.unpack_codes(np.array([[0xFF]], dtype=np.uint8), 4)
+
+
+def test_pack_rejects_non_ternary():
+    with pytest.raises(ValueError):
+        oracle.pack_codes(np.array([[2, 0, 0, 0]]))
+
+
+# ------------------------------------------------------------- rational rounding
+
+def test_round_rational_representable_identity():
+    rng = np.random.default_rng(0)
+    vals = np.concatenate([
+        rng.standard_normal(2000).astype(np.float32),
+        (rng.standard_normal(500) * 1e-30).astype(np.float32),
+        np.array([1e-45, 2**-126, 3.4e38, 1.0, 0.5], dtype=np.float32)])
+    for v in np.abs(vals):
+        fr = Fraction(float(v))
+        if fr == 0:
+            continue
+        assert oracle.round_rational_to_f32(fr.numerator, fr.denominator) == v
+
+
+def test_round_rational_ties_to_even():
+    # midpoints between neighbouring fp32 values go to the even significand
+    one = Fraction(1)
+    ulp = Fraction(1, 2**23)
+    assert oracle.round_rational_to_f32(*_nd(one + ulp / 2)) == F32(1.0)
+    assert oracle.round_rational_to_f32(*_nd(one + 3 * ulp / 2)) == _f32(0x3F800002)
+    # just above / below a midpoint
+    eps = Fraction(1, 2**80)
+    assert oracle.round_rational_to_f32(*_nd(one + ulp / 2 + eps)) == _f32(0x3F800001)
+    assert oracle.round_rational_to_f32(*_nd(one + 3 * ulp / 2 - eps)) == _f32(0x3F800001)
+    # carry into the next binade
+    top = Fraction(2) - Fraction(1, 2**24)          # midpoint below 2.0
+    assert oracle.round_rational_to_f32(*_nd(top)) == F32(2.0)
+    # subnormal midpoint: 1.5 * 2**-149 -> 2 * 2**-149 (even)
+    assert oracle.round_rational_to_f32(3, 2**150) == _f32(2)
+
+
+def test_round_rational_matches_double_off_ties():
+    # away from fp32 midpoints, rounding the fp64 nearest value again is exact
+    rng = np.random.default_rng(1)
+    for _ in range(3000):
+        n = int(rng.integers(1, 2**62))
+        d = int(rng.integers(1, 2**40))
+        want = np.float32(n / d)
+        got = oracle.round_rational_to_f32(n, d)
+        v = Fraction(n, d)
+        lo = Fraction(float(np.nextafter(want, np.float32(0))))
+        hi = Fraction(float(np.nextafter(want, np.float32(np.inf))))
+        w = Fraction(float(want))
+        near_tie = min(abs(v - (w + lo) / 2), abs(v - (w + hi) / 2)) < w * Fraction(1, 2**50)
+        if not near_tie:
+            assert got == want
+
+
+def _nd(fr):
+    return fr.numerator, fr.denominator
+
+
+# -------------------------------------------------------------------- absmean
+
+def test_gamma_all_zero_is_eps():
+    assert oracle.absmean_scale(np.zeros(1000, np.float32)) == F32(1e-6)
+
+
+def test_gamma_constant_magnitude_exact():
+    for a in [0.02, 1.0, 3.1415927, 1e-3, 123.456]:
+        a = F32(a)
+        w = np.array([a, -a, a, -a, -a, a, a], dtype=np.float32)
+        assert oracle.absmean_scale(w) == a
+
+
+def test_gamma_small_cases():
+    assert oracle.absmean_scale(np.array([1.0, 3.0], np.float32)) == F32(2.0)
+    assert oracle.absmean_scale(np.array([-1.0, 3.0, -2.0], np.float32)) == F32(2.0)
+
+
+def test_gamma_exact_tie_goes_to_even():
+    # mean of [1, 1 + 2^-23] is 1 + 2^-24: a midpoint; ties-to-even gives 1.0
+    w = np.array([1.0, _f32(0x3F800001)], np.float32)
+    assert oracle.absmean_scale(w) == F32(1.0)
+    # mean of [1 + 2^-23, 1 + 2^-22] is 1 + 3*2^-24: midpoint; even is 1 + 2^-22
+    w = np.array([_f32(0x3F800001), _f32(0x3F800002)], np.float32)
+    assert oracle.absmean_scale(w) == _f32(0x3F800002)
+
+
+def test_gamma_beyond_double_precision():
+    # sum = 3 + 2^-23 + 2^-60, mean = 0.75 + 2^-25 + 2^-62: just above the
+    # midpoint between 0.75 and 0.75 + 2^-24, so it rounds up.  A sum carried
+    # in fp64 loses the 2^-60 term and lands exactly on the midpoint, which
+    # would round to the even neighbour 0.75 instead.
+    w = np.array([1.0, 1.0, _f32(0x3F800001), F32(2.0**-60)], np.float32)
+    assert oracle.absmean_scale(w) == _f32(0x3F400001)
+    naive = np.float32(np.sum(np.abs(w).astype(np.float64)) / 4)
+    assert naive == F32(0.75)
+
+
+def test_gamma_matches_fraction_mean_on_random_groups():
+    rng = np.random.default_rng(2)
+    for trial in range(40):
+        n = int(rng.integers(1, 300))
+        scale = 10.0 ** rng.integers(-30, 30)
+        w = (rng.standard_normal(n) * scale).astype(np.float32)
+        fr = oracle.exact_fraction_mean(w)
+        want = oracle.round_rational_to_f32(fr.numerator, fr.denominator)
+        want = max(want, F32(1e-6))
+        assert oracle.absmean_scale(w) == want
+
+
+def test_exact_abs_sum_against_fraction():
+    rng = np.random.default_rng(3)
+    w = np.concatenate([rng.standard_normal(500).astype(np.float32),
+                        np.array([1e-45, -3e-42, 1e30, -2.5e-38], np.float32)])
+    units = oracle.exact_abs_sum_units(w)
+    fr = sum((Fraction(float(abs(v))) for v in w), Fraction(0))
+    assert Fraction(units, 2**149) == fr
+
+
+def test_gamma_statistics_normal_weights():
+    # E|w| = sigma * sqrt(2/pi) for w ~ N(0, sigma^2)
+    W = ti.workload_weights("decode")
+    g = oracle.absmean_scales(W, "tensor")[0]
+    assert abs(g / (0.02 * np.sqrt(2 / np.pi)) - 1) < 2e-3
+    # and it agrees with the fp64 mean rounded to fp32 unless that mean sits
+    # within fp64 error of an fp32 midpoint
+    m64 = np.mean(np.abs(W).astype(np.float64))
+    assert abs(float(g) - m64) <= float(np.spacing(np.float32(g)))
+
+
+def test_gamma_per_row_uses_each_row():
+    W = np.array([[1, -3, 0, 0], [2, 2, -2, 2]], np.float32)
+    np.testing.assert_array_equal(oracle.absmean_scales(W, "row"),
+                                  np.array([1.0, 2.0], np.float32))
+    np.testing.assert_array_equal(oracle.absmean_scales(W, "tensor"),
+                                  np.array([1.5], np.float32))
+
+
+# -------------------------------------------------------------------- ternarize
+
+def test_ternarize_half_even_tie():
+    # W = [1, 3]: gamma = 2, w/gamma = [0.5, 1.5] -> [0, 1] (half to even, then
+    # clamp), packed with zero-code padding to 0x59
+    W = np.array([[1.0, 3.0]], np.float32)
+    packed, g = oracle.pack_ternary(W, "tensor")
+    assert g[0] == F32(2.0)
+    np.testing.assert_array_equal(oracle.ternarize(W, g), [[0, 1]])
+    assert packed[0, 0] == 0x59
+
+
+def test_ternarize_brute_force_grid():
+    # every w in {-4..4}/4 against gamma = 1: round half even then clamp
+    w = (np.arange(-16, 17, dtype=np.float32) / 4).reshape(1, -1)
+    q = oracle.ternarize(w, np.array([1.0], np.float32))[0]
+    for wi, qi in zip(w[0], q):
+        if abs(wi) <= 0.5:
+            assert qi == 0
+        else:
+            assert qi == (1 if wi > 0 else -1)
+
+
+def test_ternarize_equals_half_scale_comparison():
+    # For normal fp32 w and gamma, fp32(w/gamma) rounds above 0.5 exactly when
+    # w > gamma/2: the next fp32 above gamma/2 exceeds it by more than
+    # gamma*2^-25, half the spacing of fp32 values just above 0.5.  So the
+    # round-and-clamp rule is the comparison |w| > gamma/2, ties giving 0.
+    rng = np.random.default_rng(4)
+    for _ in range(200):
+        g = F32(np.abs(rng.standard_normal()) * 10.0 ** rng.integers(-5, 5) + 1e-6)
+        h = F32(g * F32(0.5))
+        near = [h, np.nextafter(h, F32(np.inf)), np.nextafter(h, F32(0)),
+                F32(1.5) * g, np.nextafter(F32(1.5) * g, F32(np.inf))]
+        w = np.array(near + [-v for v in near] +
+                     list((rng.standard_normal(20) * g).astype(np.float32)),
+                     np.float32).reshape(1, -1)
+        q = oracle.ternarize(w, np.array([g], np.float32))[0]
+        want = (w[0] > h).astype(np.int8) - (w[0] < -h).astype(np.int8)
+        np.testing.assert_array_equal(q, want)
+
+
+def test_zero_fraction_normal_weights():
+    # for N(0, s^2) and gamma = s*sqrt(2/pi): P(|w| <= gamma/2) = erf(sqrt(1/(4 pi)))
+    from math import erf, pi, sqrt
+    W = ti.workload_weights("tiny")
+    packed, g = oracle.pack_ternary(W, "tensor")
+    q = oracle.unpack_codes(packed, 256)
+    frac0 = np.mean(q == 0)
+    assert abs(frac0 - erf(sqrt(1 / (4 * pi)))) < 0.01
+
+
+def test_binary_mode():
+    W = np.array([[0.0, -0.0, 1e-30, -1e-30, 2.0, -3.0, 0.5, -0.5]], np.float32)
+    packed, g = oracle.pack_ternary(W, "row", "binary")
+    q = oracle.unpack_codes(packed, 8)
+    np.testing.assert_array_equal(q, [[1, 1, 1, -1, 1, -1, 1, -1]])
+    assert g[0] == oracle.absmean_scale(W[0])
+    assert set(np.unique(packed)) <= {b for b in range(256)
+                                      if all(((b >> (2 * j)) & 3) in (0, 2) for j in range(4))}
+
+
+# ----------------------------------------------------------- activation quant
+
+def test_act_quant_golden():
+    for a, b in _golden("act_quant_cases.txt"):
+        x = np.array([[float(v) for v in a.split(",")]], np.float32)
+        want = np.array([[int(v) for v in b.split(",")]], np.int8)
+        q, sx = oracle.quant_act_int8(x)
+        np.testing.assert_array_equal(q, want)
+        assert sx[0] == F32(1.0)
+
+
+def test_act_quant_argmax_hits_127_and_bounds():
+    X = ti.activations(11, 64, 777)
+    q, sx = oracle.quant_act_int8(X)
+    assert np.abs(q.astype(int)).max() <= 127
+    am = np.argmax(np.abs(X), axis=1)
+    np.testing.assert_array_equal(np.abs(q[np.arange(64), am]), 127)
+    np.testing.assert_array_equal(np.sign(q[np.arange(64), am]),
+                                  np.sign(X[np.arange(64), am]))
+
+
+def test_act_quant_zero_token():
+    q, sx = oracle.quant_act_int8(np.zeros((2, 16), np.float32))
+    assert not q.any()
+    np.testing.assert_array_equal(sx, np.float32(np.float32(1e-6) / np.float32(127)))
+
+
+def test_act_quant_power_of_two_invariance():
+    X = ti.activations(12, 8, 300, dtype="f32")
+    q0, s0 = oracle.quant_act_int8(X)
+    for k in (-20, -3, 1, 5, 30):
+        q1, s1 = oracle.quant_act_int8(X * np.float32(2.0**k))
+        np.testing.assert_array_equal(q0, q1)
+        np.testing.assert_array_equal(s1, s0 * np.float32(2.0**k))
+
+
+def test_act_quant_gain_clamp():
+    # Hetman-2b s.8 test 4: a x500 input and a x1e-5 input hit the eta bounds
+    rng = np.random.default_rng(42)
+    big = (rng.standard_normal((2, 512)) * 500).astype(np.float32)
+    tiny = (rng.standard_normal((2, 512)) * 1e-5).astype(np.float32)
+    _, sb = oracle.quant_act_int8(big, eta_min=0.05, eta_max=40.0)
+    _, st = oracle.quant_act_int8(tiny, eta_min=0.05, eta_max=40.0)
+    np.testing.assert_array_equal(sb, np.float32(np.float32(40.0) / np.float32(127)))
+    np.testing.assert_array_equal(st, np.float32(np.float32(0.05) / np.float32(127)))
+
+
+def test_act_quant_scale_is_single_fp32_division():
+    # s = fp32(127/eta), q = rint(fp32(x*s)); check one value by exact rationals
+    x = np.array([[0.3, -1.7, 2.9]], np.float32)
+    q, sx = oracle.quant_act_int8(x)
+    eta = Fraction(float(F32(2.9)))
+    s = oracle.round_rational_to_f32(*_nd(Fraction(127) / eta))
+    for j in range(3):
+        p = Fraction(float(x[0, j])) * Fraction(float(s))
+        pr = oracle.round_rational_to_f32(*_nd(abs(p)))
+        v = float(pr) * (1 if p >= 0 else -1)
+        assert q[0, j] == int(np.rint(v))
+
+
+# ------------------------------------------------------------------------ FWHT
+
+def _golden_dict(name):
+    return {a: b for a, b in _golden(name)}
+
+
+def test_fwht_normalizer_constant():
+    g = _golden_dict("fwht_constants.txt")
+    assert abs(float(oracle.FWHT_NORM) - float(g["normalizer"])) < 1e-9
+    assert oracle.FWHT_NORM == np.float32(1 / np.sqrt(512))
+
+
+def test_fwht_basis_vectors_closed_form():
+    # H e_j has entries (-1)^popcount(i & j), unnormalised, for every j
+    E = np.eye(512, dtype=np.float32)
+    Hx = oracle.fwht_block(E, normalize=False)      # row j = H e_j
+    for j in range(512):
+        i = np.arange(512)
+        sign = np.array([(-1) ** bin(int(v)).count("1") for v in (i & j)], np.float32)
+        np.testing.assert_array_equal(Hx[j], sign)
+
+
+def test_fwht_integer_inputs_exact():
+    # |x| <= 2^14: every partial sum is an integer below 2^24, so the fp32
+    # butterfly equals the integer matrix product with the Sylvester matrix
+    rng = np.random.default_rng(7)
+    x = rng.integers(-2**14, 2**14 + 1, size=(6, 512)).astype(np.int64)
+    H = oracle.hadamard_matrix(512)
+    want = x @ H.T
+    got = oracle.fwht_block(x.astype(np.float32), normalize=False)
+    np.testing.assert_array_equal(got.astype(np.int64), want)
+
+
+def test_fwht_isometry_involution_spike():
+    g = _golden_dict("fwht_constants.txt")
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((8, 512)).astype(np.float32)
+    y = oracle.fwht_block(x, normalize=True)
+    assert np.max(np.abs(np.linalg.norm(x, axis=1) - np.linalg.norm(y, axis=1))) \
+        < float(g["isometry_tol"])
+    assert np.max(np.abs(oracle.fwht_block(y, normalize=True) - x)) \
+        < float(g["involution_tol"])
+    spike = np.zeros((1, 512), np.float32)
+    spike[0, int(g["spike_index"])] = float(g["spike_value"])
+    s = oracle.fwht_block(spike, normalize=True)
+    peak = float(np.max(np.abs(s)))
+    assert abs(peak - float(g["spike_peak"])) < float(g["spike_tol"])
+    assert abs(100.0 / peak - float(g["attenuation"])) < 0.01
+    # signs: + for i < 256, - for i >= 256 (popcount of i & 256)
+    v = np.float32(np.float32(100.0) * oracle.FWHT_NORM)
+    np.testing.assert_array_equal(s[0, :256], v)
+    np.testing.assert_array_equal(s[0, 256:], -v)
+
+
+def test_fwht_blockwise_independent_blocks():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((3, 2048)).astype(np.float32)
+    y = oracle.fwht512(x, normalize=True)
+    for b in range(4):
+        np.testing.assert_array_equal(
+            y[:, 512 * b:512 * (b + 1)],
+            oracle.fwht_block(x[:, 512 * b:512 * (b + 1)], normalize=True))
+    with pytest.raises(ValueError):
+        oracle.fwht512(np.zeros((1, 500), np.float32))
+
+
+# ------------------------------------------------------------ prologue (fold)
+
+def test_fold_matches_literal_chain_up_to_boundaries():
+    X = ti.activations(5105, 64, 4096, dist="student_t3")
+    q, sx, sx_exact, bound = oracle.rmsnorm_fwht_quant(X)
+    ql, sxl = oracle.rmsnorm_fwht_quant_literal(X)
+    assert not bound.any()
+    d = np.abs(q.astype(int) - ql.astype(int))
+    assert d.max() <= 1
+    assert np.mean(d) < 1e-3
+    np.testing.assert_allclose(sx_exact, sxl, rtol=1e-6)
+    np.testing.assert_allclose(sx, sxl, rtol=2e-7)
+
+
+def test_fold_clamp_branches_exact_inputs():
+    rng = np.random.default_rng(9)
+    K = 4096
+    # (a) upper clamp: one block carries a Hadamard row pattern, the rest zero
+    H = oracle.hadamard_matrix(512)
+    xa = np.zeros(K, np.float32)
+    xa[1024:1536] = (H[37] * 2.0**3).astype(np.float32)
+    # (b) lower clamp: all |x| = 2^-20 (RMSNorm eps dominates)
+    xb = (rng.choice([-1.0, 1.0], size=K) * 2.0**-20).astype(np.float32)
+    # (c) zero token
+    xc = np.zeros(K, np.float32)
+    X = np.stack([xa, xb, xc])
+    q, sx, sx_exact, bound = oracle.rmsnorm_fwht_quant(X)
+    assert bound.all()
+    assert sx[0] == np.float32(np.float32(40.0) / np.float32(127))
+    assert sx[1] == np.float32(np.float32(0.05) / np.float32(127))
+    assert not q[2].any()
+    # (a): z has one non-zero entry 512*8 at index 1024+37; r = 2^-3*sqrt(8)
+    # (up to fp32 rounding), so the code there is rint(4096*m) with m as defined
+    nz = np.nonzero(q[0])[0]
+    np.testing.assert_array_equal(nz, [1024 + 37])
+    r = oracle.rms_factor(xa)
+    m = np.float32(np.float32(r * oracle.FWHT_NORM) *
+                   np.float32(np.float32(127) / np.float32(40.0)))
+    assert q[0, 1024 + 37] == np.clip(np.rint(np.float32(4096.0) * m), -127, 127)
+    assert q[0, 1024 + 37] == 127   # eta_true = 64 > 40, so the peak saturates
+    # (b): compare with fp64 evaluation of the literal chain
+    ql, _ = oracle.rmsnorm_fwht_quant_literal(X[1:2])
+    assert np.abs(q[1].astype(int) - ql[0].astype(int)).max() <= 1
+
+
+def test_fold_power_of_two_scaling_invariance():
+    X = ti.activations(77, 4, 1024, dist="student_t3")
+    q0, s0, _, _ = oracle.rmsnorm_fwht_quant(X)
+    q1, s1, _, _ = oracle.rmsnorm_fwht_quant(X * np.float32(8.0))
+    np.testing.assert_array_equal(q0, q1)
+    np.testing.assert_allclose(s0, s1, rtol=1e-6)   # RMSNorm removes the factor
+
+
+# ------------------------------------------------------------ contraction
+
+def _gather_reference(q, w):
+    # BitRASP additive_ternary_linear_int8: sum of x where W = +1 minus sum
+    # of x where W = -1, written independently here
+    M, N = q.shape[0], w.shape[0]
+    out = np.zeros((M, N), np.int64)
+    for o in range(N):
+        pos = np.nonzero(w[o] == 1)[0]
+        neg = np.nonzero(w[o] == -1)[0]
+        out[:, o] = q[:, pos].astype(np.int64).sum(1) - q[:, neg].astype(np.int64).sum(1)
+    return out
+
+
+def test_contraction_three_references_agree():
+    for (M, N, K, seed) in [(1, 3, 4, 1), (3, 17, 60, 2), (5, 33, 260, 3), (2, 64, 1024, 4)]:
+        q = ti.random_int8(seed, M, K)
+        w = ti.random_ternary(seed + 100, N, K)
+        packed = oracle.pack_codes(w)
+        acc = oracle.contract(q, packed, K)
+        np.testing.assert_array_equal(acc, _gather_reference(q, w))
+        if M * N * K <= 3 * 17 * 60:
+            for m in range(M):
+                for o in range(N):
+                    assert acc[m, o] == sum(int(q[m, k]) * int(w[o, k]) for k in range(K))
+
+
+def test_contraction_all_plus_one_and_bounds():
+    q = ti.random_int8(20, 4, 512)
+    w = np.ones((3, 512), np.int8)
+    acc = oracle.contract(q, oracle.pack_codes(w), 512)
+    np.testing.assert_array_equal(acc, np.repeat(q.astype(np.int64).sum(1)[:, None], 3, 1))
+    q = np.full((1, 6912), 127, np.int8)
+    w = -np.ones((1, 6912), np.int8)
+    acc = oracle.contract(q, oracle.pack_codes(w), 6912)
+    assert acc[0, 0] == -127 * 6912 and abs(acc[0, 0]) < 2**24
+
+
+def test_epilogue_identity_and_zero():
+    q = ti.random_int8(30, 3, 64)
+    w = ti.random_ternary(31, 5, 64)
+    acc = oracle.contract(q, oracle.pack_codes(w), 64)
+    g = np.array([0.0123], np.float32)
+    sx = np.array([0.01, 0.02, 0.5], np.float32)
+    y = oracle.epilogue(acc, g, sx)
+    np.testing.assert_allclose(y / (float(g[0]) * sx.astype(np.float64)[:, None]), acc,
+                               rtol=1e-15)
+    assert np.all(y[acc == 0] == 0)
+
+
+def test_whole_layer_tiny_matches_gemv_emulation():
+    # Hetman-2b s.7 GEMV semantics: per row, per packed byte, decode four
+    # weights, accumulate in integers, scale once.  Written out here with
+    # Python integers for a few rows of the tiny workload.
+    W = ti.workload_weights("tiny")
+    X = ti.workload_activations("tiny")
+    r = oracle.ternary_linear(X, W)
+    for m in range(X.shape[0]):
+        for o in (0, 1, 77, 255):
+            acc = 0
+            for j, byte in enumerate(r["packed"][o]):
+                for s in range(4):
+                    code = (int(byte) >> (2 * s)) & 3
+                    acc += int(r["q"][m, 4 * j + s]) * (code - 1)
+            assert acc == r["acc"][m, o]
+            y = float(acc) * float(r["scale"][0]) * float(r["sx"][m])
+            assert abs(y - r["y"][m, o]) <= 1e-12 * max(1.0, abs(y))
