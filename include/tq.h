@@ -1,0 +1,191 @@
+/*
+ * tq.h -- C ABI of libtq, a ternary (absmean, 2-bit) linear layer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The layer follows the BitNet-b1.58 recipe as the pages state it:
+ *   - Foundry, docs/quantization.md, "Ternary Quantization (BitNet b1.58) /
+ *     How It Works": gamma = mean|w|, q = round(w/gamma) clamped to
+ *     {-1, 0, +1}, pack four per byte, integer add/sub contraction, scale by
+ *     gamma afterwards; "Ternary Format / Encoding": -1 = 0b00, 0 = 0b01,
+ *     +1 = 0b10, byte = v0 | v1<<2 | v2<<4 | v3<<6, (numel+3)/4 bytes.
+ *   - Hetman-2b, src/quantization.py, sections 1, 2, 4, 5 and 7: FWHT-512,
+ *     absmean weight quantizer, per-token symmetric int8 activations with
+ *     scale 127/eta and codes in [-127, 127], RMSNorm, the BitLinear order
+ *     RMSNorm -> FWHT -> int8 -> integer contraction -> y*(gamma/s_x), and
+ *     the int32 GEMV emulator.
+ *   - BitRASP, core_math.py, ``additive_ternary_linear_int8``: the integer
+ *     identity y[o] = sum(x where W=+1) - sum(x where W=-1).
+ *
+ * Conventions shared by every call
+ *   - W is [N, K] row-major (N output rows, K inputs), as a PyTorch Linear
+ *     weight.  Packed weights are [N, K/4] bytes, row o holding the codes of
+ *     W[o, 0..K-1] in order, so K must be a multiple of 4.  With K % 4 == 0
+ *     this is byte-for-byte the flat LSB-first packing of the whole tensor.
+ *   - Activations X are [M, K] row-major (M tokens); int8 codes q are [M, K];
+ *     sx[m] is the dequantisation scale of token m (eta_m / 127).
+ *   - Outputs Y are [M, N] row-major: y[m, o] = acc[m, o] * scale_o * sx[m],
+ *     acc the exact int32 sum over k of q[m, k] * w[o, k].
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; libtq
+ *     never allocates, frees or retains device memory.  Work is enqueued
+ *     asynchronously on `stream` (0 = the null stream); results are ready
+ *     once the caller synchronises that stream.
+ *   - Arguments are checked before anything is enqueued; on an error status
+ *     nothing is launched and no output is written.  TQ_ERR_HIP reports a
+ *     failed launch (the HIP error is available from tq_last_hip_error()).
+ *   - M == 0 or N == 0 is a valid empty call: TQ_OK, nothing launched.
+ *   - Inputs must be finite; NaN/Inf inputs give unspecified (but in-bounds)
+ *     results.
+ *   - No call keeps state between calls; calls on different streams may run
+ *     concurrently as long as their output buffers do not overlap.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  TQ_ERR_SHAPE = 2,       /* negative size, K % 4 != 0, M out of range, ...  */
+  TQ_ERR_DTYPE = 3,       /* dtype not accepted by this call                 */
+  TQ_ERR_ALIGN = 4,       /* pointer misaligned for its element type         */
+  TQ_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required      */
+  TQ_ERR_UNSUPPORTED = 6, /* option combination or size beyond stated limits */
+  TQ_ERR_HIP = 7          /* the HIP runtime refused a launch                */
+} tq_status;
+
+typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1, TQ_I32 = 2 } tq_dtype;
+
+/* Granularity of the absmean scale: one for the whole tensor, or one per
+ * output row (Foundry "fq_quantize_ternary_per_channel"; BitRASP
+ * ``ternarize_weight`` keeps one scale per output row). */
+typedef enum tq_gran { TQ_PER_TENSOR = 0, TQ_PER_ROW = 1 } tq_gran;
+
+/* TQ_TERNARY_ABSMEAN: q = clamp(round_half_even(fp32(w / gamma)), -1, 1).
+ * TQ_BINARY_SIGN: q = +1 where w >= 0 else -1 (the +-1 weights with a
+ * per-row scale of the qste project description, "What it costs and what it
+ * buys"); stored in the same 2-bit codes (0b10 / 0b00). */
+typedef enum tq_wmode { TQ_TERNARY_ABSMEAN = 0, TQ_BINARY_SIGN = 1 } tq_wmode;
+
+/* Options of tq_quant_act_int8 (NULL = plain per-token absmax, eps 1e-6). */
+typedef struct tq_act_opts {
+  float eps;               /* floor on eta (Hetman-2b s.2 uses 1e-6)           */
+  int clamp;               /* 1: clamp eta to [eta_min, eta_max] (gain clamp)  */
+  float eta_min, eta_max;  /* BitLinear uses 0.05 and 40 (Hetman-2b s.0, s.5)  */
+  int rmsnorm;             /* 1: RMSNorm prologue (Hetman-2b s.4)              */
+  float rms_eps;           /* 1e-6 in Hetman-2b s.4                            */
+  const float* rms_weight; /* [K] device pointer, or NULL for all ones         */
+  int fwht_block;          /* 0 (off) or 512: blockwise FWHT-512 prologue      */
+} tq_act_opts;
+
+/* Bytes of a packed ternary tensor of `numel` values: (numel + 3) / 4
+ * (Foundry "Ternary Format / Encoding").  Returns 0 for numel <= 0. */
+size_t tq_packed_bytes(int64_t numel);
+
+/* Device workspace that tq_pack_ternary needs for an [N, K] weight at
+ * granularity g (0 for TQ_PER_ROW).  Returns 0 for invalid sizes. */
+size_t tq_pack_workspace_bytes(int64_t N, int64_t K, tq_gran g);
+
+/* Absmean scale + ternarize (or binarize) + 2-bit pack.
+ * (Foundry "How It Works" steps 1-3 and "Ternary Format / Encoding";
+ *  Hetman-2b s.2 AbsmeanWeightQuantizer forward and s.5 export_packed_weights.)
+ *
+ *   W       [N, K] fp32, 4-byte aligned.
+ *   packed  [N, K/4] bytes (output).
+ *   scale   fp32 output: [1] for TQ_PER_TENSOR, [N] for TQ_PER_ROW.
+ *           gamma = max(fp32 nearest to the exact mean of |w| over the group
+ *           (ties to even), fp32(1e-6)).  The mean is accumulated in fp64 and
+ *           re-computed exactly (integer exponent bins) whenever the fp64
+ *           value lies too close to an fp32 rounding boundary, so gamma does
+ *           not depend on the launch shape.
+ *   ws      device workspace of at least tq_pack_workspace_bytes(N, K, g)
+ *           bytes (may be NULL when that is 0); contents are scratch.
+ * Errors: NULL pointers, N < 0, K <= 0 or K % 4 != 0, N*K >= 2^40
+ * (TQ_ERR_UNSUPPORTED), short workspace, misaligned W. */
+tq_status tq_pack_ternary(const float* W, int64_t N, int64_t K, tq_gran g,
+                          tq_wmode mode, uint8_t* packed, float* scale,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Per-token symmetric int8 quantisation (Hetman-2b s.2
+ * SymmetricActivationQuantizer, reduced per token as its code does; BitRASP
+ * ``fake_quant_int``), with an optional BitLinear prologue (Hetman-2b s.5).
+ *
+ *   X     [M, K] fp32 or bf16 (xdt = TQ_F32 / TQ_BF16), element-aligned.
+ *   q     [M, K] int8 output, codes in [-127, 127].
+ *   sx    [M] fp32 output, the dequantisation scale eta_eff / 127.
+ * Plain path (opts NULL, or rmsnorm == 0 and fwht_block == 0):
+ *   eta = max(max_k |x|, eps), clamped to [eta_min, eta_max] when clamp;
+ *   s = fp32(127/eta); q = clamp(rint(fp32(x*s)), -127, 127);
+ *   sx = fp32(eta/127).  Bit-exact: q and sx.
+ * Prologue path (rmsnorm and/or fwht_block = 512, K % 512 == 0 for FWHT):
+ *   z = FWHT_unnormalised(g * x) blockwise in fp32 (stages h = 1..256), r the
+ *   RMS factor 1/sqrt(mean(x^2) + rms_eps) (1 without rmsnorm), c = fp32(1/sqrt(512))
+ *   (1 without FWHT).  The RMSNorm output rotated and normalised is r*c*z, and
+ *   its absmax codes equal those of z while the eps floor and the clamp leave
+ *   eta_true = r*c*max|z| unchanged: q = clamp(rint(fp32(z * fp32(127/max|z|))))
+ *   and sx = eta_true/127.  Otherwise q = clamp(rint(fp32(z*m))) with
+ *   m = fp32(fp32(r*c) * fp32(127/eta_eff)) and sx = fp32(eta_eff/127).
+ *   q is bit-exact given r; sx is exact to fp32 rounding of r.
+ * Errors: NULL pointers, M < 0, K <= 0, K % 512 != 0 with FWHT, fwht_block
+ * not 0 or 512, xdt not F32/BF16, K > 65536 with a prologue (UNSUPPORTED). */
+tq_status tq_quant_act_int8(const void* X, tq_dtype xdt, int64_t M, int64_t K,
+                            const tq_act_opts* opts, int8_t* q, float* sx,
+                            hipStream_t stream);
+
+/* Blockwise fast Walsh-Hadamard transform of length 512 along K
+ * (Hetman-2b s.1 fast_walsh_hadamard_transform_512 / blockwise_fwht_forward):
+ * nine butterfly stages h = 1, 2, ..., 256 in fp32, pairs (i, i+h) with bit h
+ * of i clear becoming (x_i + x_{i+h}, x_i - x_{i+h}); when `normalize` is
+ * non-zero the result is multiplied by fp32(1/sqrt(512)) after the last stage.
+ *   X [M, K] fp32 or bf16; Y [M, K] fp32 output (may not alias X).
+ * Bit-exact against the same expression tree.
+ * Errors: NULL pointers, M < 0, K <= 0 or K % 512 != 0, bad dtype. */
+tq_status tq_fwht512(const void* X, tq_dtype xdt, int64_t M, int64_t K,
+                     int normalize, float* Y, hipStream_t stream);
+
+/* Decode-shaped product for 1 <= M <= 16 tokens (Hetman-2b s.7 GEMV; Foundry
+ * "Native Matmul Kernel"; BitRASP additive_ternary_linear_int8):
+ *   acc[m, o] = sum_k q[m, k] * w[o, k] (exact int32),
+ *   y[m, o]   = acc[m, o] * scale_o * sx[m] in fp32 (TQ_F32), the same rounded
+ *               to bf16 (TQ_BF16), or acc itself (TQ_I32).
+ *   q [M, K] int8; sx [M] fp32; packed [N, K/4]; scale [1] or [N] fp32 per g;
+ *   Y [M, N] of dtype ydt, 4-byte aligned (2 for bf16).
+ * The packed weight is streamed from HBM once, 16 bytes per lane, and decoded
+ * in registers.  Errors: NULL pointers, M > 16, K <= 0 or K % 4 != 0,
+ * N < 0, bad ydt, K > 2^24 / 127 (int32 headroom). */
+tq_status tq_ternary_gemv(const int8_t* q, const float* sx, int64_t M,
+                          const uint8_t* packed, const float* scale, tq_gran g,
+                          int64_t N, int64_t K, void* Y, tq_dtype ydt,
+                          hipStream_t stream);
+
+/* Prefill-shaped product for any M >= 0, same contract as tq_ternary_gemv
+ * (same inputs, outputs and errors, without the M <= 16 limit).  Packed
+ * tiles are decoded to int8 in LDS once per workgroup and contracted with
+ * int8 MFMA (v_mfma_i32_32x32x32_i8). */
+tq_status tq_ternary_gemm(const int8_t* q, const float* sx, int64_t M,
+                          const uint8_t* packed, const float* scale, tq_gran g,
+                          int64_t N, int64_t K, void* Y, tq_dtype ydt,
+                          hipStream_t stream);
+
+/* Static description of a status code (never NULL). */
+const char* tq_status_str(tq_status s);
+
+/* Name of the last HIP error seen by this thread inside libtq ("hipSuccess"
+ * if none).  Pointer to a static string. */
+const char* tq_last_hip_error(void);
+
+/* Library version, e.g. "0.1.0". */
+const char* tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

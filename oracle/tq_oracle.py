@@ -304,18 +304,21 @@ def rms_factor(x_row: np.ndarray) -> np.float32:
 
 
 def rmsnorm_fwht_quant(X: np.ndarray, eta_min=ETA_MIN_BITLINEAR,
-                       eta_max=ETA_MAX_BITLINEAR, rms_weight=None):
+                       eta_max=ETA_MAX_BITLINEAR, rms_weight=None,
+                       rmsnorm: bool = True, fwht: bool = True, eps=ACT_EPS):
     """BitLinear activation prologue (Hetman-2b s.5: RMSNorm -> blockwise
     normalised FWHT-512 -> per-token int8 with gain clamp), evaluated through
-    the exact cancellation of positive per-token factors.
+    the exact cancellation of positive per-token factors.  Either stage can be
+    switched off (factor 1).
 
-    With z = FWHT_unnormalised(g * x) (fp32, butterfly order above), r the RMS
-    factor and c = fp32(1/sqrt(512)), the rotated activation is r*c*z and its
-    absmax is eta_true = r*c*max|z|.  Absmax codes do not change under a
-    positive per-token factor, so while the floor/clamp leaves eta_true as it
-    is, q is the plain quantiser applied to z with eta = max|z| (q = 0 for a
-    zero token) and the dequantisation scale is eta_true/127.  When the eps
-    floor or the [eta_min, eta_max] clamp moves eta to eta_eff, the codes are
+    With z = FWHT_unnormalised(g * x) (fp32, butterfly order above; z = g * x
+    without the FWHT), r the RMS factor and c = fp32(1/sqrt(512)), the
+    rotated activation is r*c*z and its absmax is eta_true = r*c*max|z|.
+    Absmax codes do not change under a positive per-token factor, so while
+    the eps floor and the [eta_min, eta_max] clamp leave eta_true as it is, q
+    is the plain quantiser applied to z with eta = max|z| (q = 0 for a zero
+    token) and the dequantisation scale is eta_true/127.  When the floor or
+    the clamp moves eta to eta_eff, the codes are
     q = clamp(rint(fp32(z * m)), -127, 127) with
     m = fp32(fp32(r*c) * fp32(127/eta_eff)) and sx = fp32(eta_eff/127); here r
     is the fp32 factor of ``rms_factor``.
@@ -329,19 +332,19 @@ def rmsnorm_fwht_quant(X: np.ndarray, eta_min=ETA_MIN_BITLINEAR,
     x = xin
     if rms_weight is not None:
         x = (x * np.asarray(rms_weight, dtype=np.float32)[None, :]).astype(np.float32)
-    z = fwht512(x, normalize=False)
+    z = fwht512(x, normalize=False) if fwht else x.copy()
+    c32 = FWHT_NORM if fwht else F32(1.0)
     M = x.shape[0]
     q = np.empty(x.shape, dtype=np.int8)
     sx = np.empty(M, dtype=np.float32)
     sx_exact = np.empty(M, dtype=np.float64)
     bound = np.zeros(M, dtype=bool)
-    c64 = float(FWHT_NORM)
     for i in range(M):
         x64 = xin[i].astype(np.float64)
-        r64 = 1.0 / np.sqrt(np.mean(x64 * x64) + float(RMS_EPS))
-        eta_z = F32(np.max(np.abs(z[i])))
-        eta_true = r64 * c64 * float(eta_z)
-        eta_eff = max(eta_true, float(ACT_EPS))
+        r64 = 1.0 / np.sqrt(np.mean(x64 * x64) + float(RMS_EPS)) if rmsnorm else 1.0
+        eta_z = F32(np.max(np.abs(z[i]))) if z.shape[1] else F32(0)
+        eta_true = r64 * float(c32) * float(eta_z)
+        eta_eff = max(eta_true, float(F32(eps)))
         if eta_min is not None and eta_max is not None:
             eta_eff = min(max(eta_eff, float(F32(eta_min))), float(F32(eta_max)))
         if eta_eff == eta_true:
@@ -355,8 +358,8 @@ def rmsnorm_fwht_quant(X: np.ndarray, eta_min=ETA_MIN_BITLINEAR,
         else:
             bound[i] = True
             e32 = F32(eta_eff)
-            r = rms_factor(xin[i])
-            m = F32(F32(r * FWHT_NORM) * F32(F32(QMAX) / e32))
+            r = rms_factor(xin[i]) if rmsnorm else F32(1.0)
+            m = F32(F32(r * c32) * F32(F32(QMAX) / e32))
             q[i] = np.clip(np.rint(z[i] * m), -QMAX, QMAX).astype(np.int8)
             sx[i] = F32(e32 / F32(QMAX))
             sx_exact[i] = float(e32) / QMAX

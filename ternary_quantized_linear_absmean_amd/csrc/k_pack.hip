@@ -1,0 +1,372 @@
+// Absmean scale, ternarization and 2-bit packing of a weight matrix.
+//
+// Foundry, docs/quantization.md, "Ternary Quantization (BitNet b1.58) / How
+// It Works": gamma = mean|w|, q = round(w/gamma) clamped to {-1, 0, +1},
+// four codes per byte; "Ternary Format / Encoding": -1 = 0b00, 0 = 0b01,
+// +1 = 0b10, LSB-first.  Hetman-2b, src/quantization.py, section 2: the mean
+// is floored at 1e-6 and the rounding is round-half-to-even.
+//
+// gamma is the fp32 value nearest to the exact mean of |w| (ties to even),
+// then floored.  The sum is carried in fp64; when the fp64 mean lies within
+// its error bound of an fp32 rounding boundary the group is summed again
+// exactly: each |w| is M * 2^(b-150) with b = max(biased exponent, 1) and M
+// the 24-bit significand, the M are added per b in 64-bit integers, and the
+// total is divided by the element count in multi-word integer arithmetic.
+//
+// Ternarization uses a comparison instead of the quotient: for normal fp32
+// w and gamma, rint(fp32(w/gamma)) is +1 exactly when w > gamma/2 (the next
+// fp32 above gamma/2 exceeds it by more than gamma * 2^-25, half the fp32
+// spacing just above 0.5), and -1 exactly when w < -gamma/2.
+
+#include "tq_device.hpp"
+#include "tq_internal.hpp"
+
+namespace tq {
+namespace {
+
+constexpr int kNT = 256;
+constexpr int kMaxPartials = 1024;
+constexpr size_t kWsPartials = 0;                                  // double[1024]
+constexpr size_t kWsFlag = kMaxPartials * sizeof(double);          // uint32
+constexpr size_t kWsBins = kWsFlag + 256;                          // uint64[256]
+constexpr size_t kWsTotal = kWsBins + 256 * sizeof(unsigned long long);
+
+constexpr float kGammaEps = 1e-6f;
+
+// --------------------------------------------------------------- exact mean
+
+// value of the fp32 nearest (ties to even) to (sum_b bins[b] * 2^(b-150)) / n,
+// or 0 when that value is below 2^-20 (callers floor at 1e-6 anyway).
+__device__ float exact_mean_from_bins(const unsigned long long* bins,
+                                      unsigned long long n) {
+  constexpr int kLimbs = 11;  // 352 bits: bins < 2^64 shifted by at most 253
+  uint32_t T[kLimbs];
+#pragma unroll
+  for (int i = 0; i < kLimbs; ++i) T[i] = 0u;
+  for (int b = 1; b < 255; ++b) {
+    const unsigned long long v = bins[b];
+    if (v == 0ull) continue;
+    const int s = b - 1;
+    const int li = s >> 5, bo = s & 31;
+    const unsigned long long lo = v << bo;
+    const unsigned long long hi = bo ? (v >> (64 - bo)) : 0ull;
+    const uint32_t add[3] = {static_cast<uint32_t>(lo),
+                             static_cast<uint32_t>(lo >> 32),
+                             static_cast<uint32_t>(hi)};
+    unsigned long long carry = 0ull;
+    for (int j = 0; li + j < kLimbs; ++j) {
+      if (j >= 3 && carry == 0ull) break;
+      const unsigned long long t = static_cast<unsigned long long>(T[li + j]) +
+                                   (j < 3 ? add[j] : 0u) + carry;
+      T[li + j] = static_cast<uint32_t>(t);
+      carry = t >> 32;
+    }
+  }
+  int top = -1;
+  for (int i = kLimbs - 1; i >= 0; --i) {
+    if (T[i]) {
+      top = i * 32 + 31 - __clz(static_cast<int>(T[i]));
+      break;
+    }
+  }
+  if (top < 0) return 0.f;
+  // restoring division, one quotient bit per step, from T's top bit down and
+  // on into fraction bits; stop after the leading bit + 23 + a guard bit
+  unsigned long long rem = 0ull, mant = 0ull;
+  int count = 0, lead = 0, pos = top;
+  bool started = false;
+  for (;; --pos) {
+    const unsigned bit = pos >= 0 ? (T[pos >> 5] >> (pos & 31)) & 1u : 0u;
+    rem = (rem << 1) | bit;
+    const unsigned qb = rem >= n ? 1u : 0u;
+    if (qb) rem -= n;
+    if (!started && qb) {
+      started = true;
+      lead = pos;
+    }
+    if (started) {
+      mant = (mant << 1) | qb;
+      if (++count == 25) break;
+    }
+  }
+  bool sticky = rem != 0ull;
+  for (int p = pos - 1; p >= 0 && !sticky; --p)
+    if ((T[p >> 5] >> (p & 31)) & 1u) sticky = true;
+  uint32_t m24 = static_cast<uint32_t>(mant >> 1);
+  const uint32_t guard = static_cast<uint32_t>(mant & 1ull);
+  if (guard && (sticky || (m24 & 1u))) ++m24;
+  if (m24 == (1u << 24)) {
+    m24 >>= 1;
+    ++lead;
+  }
+  // the quotient's leading bit is 2^lead quanta of 2^-149
+  const int biased = lead - 149 + 127;
+  if (biased < 107) return 0.f;  // below 2^-20
+  return __uint_as_float((static_cast<uint32_t>(biased) << 23) | (m24 & 0x7FFFFFu));
+}
+
+// gamma from an fp64 sum S of |w| over n elements whose relative error is at
+// most thr.  Returns true when S/n is too close to an fp32 rounding boundary
+// to decide, in which case *g is not final.
+__device__ inline bool gamma_from_fp64(double S, double n, double thr, float* g) {
+  const double mean = S / n;
+  if (mean < 0.5 * static_cast<double>(kGammaEps)) {
+    *g = kGammaEps;
+    return false;
+  }
+  const float f = __double2float_rn(mean);
+  const uint32_t fb = __float_as_uint(f);
+  const double fd = static_cast<double>(f);
+  const double up = static_cast<double>(__uint_as_float(fb + 1u)) - fd;
+  const double dn = fd - static_cast<double>(__uint_as_float(fb - 1u));
+  const double dist = fmin((fd + 0.5 * up) - mean, mean - (fd - 0.5 * dn));
+  *g = fmaxf(f, kGammaEps);
+  return dist <= thr * mean;
+}
+
+__device__ inline void bin_add(unsigned long long* lb, float w) {
+  const uint32_t u = __float_as_uint(w) & 0x7FFFFFFFu;
+  const uint32_t e = u >> 23;
+  const uint32_t m = (u & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+  const uint32_t b = e ? e : 1u;
+  atomicAdd(&lb[b], static_cast<unsigned long long>(m));
+}
+
+__device__ inline uint32_t code_of(float w, float h, int binary) {
+  if (binary) return w >= 0.f ? 2u : 0u;
+  return w > h ? 2u : (w < -h ? 0u : 1u);
+}
+
+__device__ inline uint32_t byte_of(float4 v, float h, int binary) {
+  return code_of(v.x, h, binary) | (code_of(v.y, h, binary) << 2) |
+         (code_of(v.z, h, binary) << 4) | (code_of(v.w, h, binary) << 6);
+}
+
+template <bool VEC>
+__device__ inline float4 load4(const float* p, int64_t i4) {
+  if (VEC) return reinterpret_cast<const float4*>(p)[i4];
+  return make_float4(p[4 * i4], p[4 * i4 + 1], p[4 * i4 + 2], p[4 * i4 + 3]);
+}
+
+// ------------------------------------------------------------ per tensor
+
+template <bool VEC>
+__global__ __launch_bounds__(kNT) void k_abssum_partial(const float* __restrict__ W,
+                                                        int64_t n4,
+                                                        double* __restrict__ partials) {
+  __shared__ double sh[kNT / kWave];
+  double acc = 0.0;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kNT;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kNT + threadIdx.x; i < n4;
+       i += stride) {
+    const float4 v = load4<VEC>(W, i);
+    acc += fabs(static_cast<double>(v.x));
+    acc += fabs(static_cast<double>(v.y));
+    acc += fabs(static_cast<double>(v.z));
+    acc += fabs(static_cast<double>(v.w));
+  }
+  const double s = block_sum<kNT>(acc, sh);
+  if (threadIdx.x == 0) partials[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kNT) void k_gamma_finalize(
+    const double* __restrict__ partials, int P, int64_t n, double thr,
+    uint32_t* __restrict__ flag, unsigned long long* __restrict__ bins,
+    float* __restrict__ scale) {
+  __shared__ double sh[kNT / kWave];
+  __shared__ int near_sh;
+  double v = 0.0;
+  for (int i = threadIdx.x; i < P; i += kNT) v += partials[i];
+  const double S = block_sum<kNT>(v, sh);
+  if (threadIdx.x == 0) {
+    float g;
+    const bool near = gamma_from_fp64(S, static_cast<double>(n), thr, &g);
+    near_sh = near ? 1 : 0;
+    *flag = near ? 1u : 0u;
+    if (!near) scale[0] = g;
+  }
+  __syncthreads();
+  if (near_sh) bins[threadIdx.x] = 0ull;
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kNT) void k_gamma_bins(const float* __restrict__ W,
+                                                    int64_t n4,
+                                                    const uint32_t* __restrict__ flag,
+                                                    unsigned long long* __restrict__ bins) {
+  if (*flag == 0u) return;
+  __shared__ unsigned long long lb[256];
+  lb[threadIdx.x] = 0ull;
+  __syncthreads();
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kNT;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kNT + threadIdx.x; i < n4;
+       i += stride) {
+    const float4 v = load4<VEC>(W, i);
+    bin_add(lb, v.x);
+    bin_add(lb, v.y);
+    bin_add(lb, v.z);
+    bin_add(lb, v.w);
+  }
+  __syncthreads();
+  if (lb[threadIdx.x]) atomicAdd(&bins[threadIdx.x], lb[threadIdx.x]);
+}
+
+__global__ void k_gamma_exact_final(const uint32_t* __restrict__ flag,
+                                    const unsigned long long* __restrict__ bins,
+                                    int64_t n, float* __restrict__ scale) {
+  if (*flag == 0u || threadIdx.x != 0) return;
+  scale[0] = fmaxf(exact_mean_from_bins(bins, static_cast<unsigned long long>(n)),
+                   kGammaEps);
+}
+
+// 16 weights -> one 32-bit word per step when VEC (W 16-byte and packed
+// 4-byte aligned); otherwise one byte per step.
+template <bool VEC>
+__global__ __launch_bounds__(kNT) void k_ternarize_pack(const float* __restrict__ W,
+                                                        int64_t nbytes, int binary,
+                                                        const float* __restrict__ scale,
+                                                        uint8_t* __restrict__ packed) {
+  const float h = scale[0] * 0.5f;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kNT;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kNT + threadIdx.x;
+  int64_t done = 0;
+  if (VEC) {
+    const int64_t nwords = nbytes / 4;
+    for (int64_t i = tid; i < nwords; i += stride) {
+      uint32_t word = 0u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        word |= byte_of(load4<true>(W, 4 * i + b), h, binary) << (8 * b);
+      reinterpret_cast<uint32_t*>(packed)[i] = word;
+    }
+    done = nwords * 4;
+  }
+  for (int64_t j = done + tid; j < nbytes; j += stride)
+    packed[j] = static_cast<uint8_t>(byte_of(load4<false>(W, j), h, binary));
+}
+
+// --------------------------------------------------------------- per row
+
+template <bool VEC>
+__global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
+                                                   int64_t K, int binary, double thr,
+                                                   uint8_t* __restrict__ packed,
+                                                   float* __restrict__ scale) {
+  __shared__ double sh[kNT / kWave];
+  __shared__ float g_sh;
+  __shared__ int near_sh;
+  __shared__ unsigned long long lb[256];
+  const int64_t row = blockIdx.x;
+  const float* w = W + row * K;
+  uint8_t* out = packed + row * (K / 4);
+  const int64_t nb = K / 4;
+  double acc = 0.0;
+  for (int64_t j = threadIdx.x; j < nb; j += kNT) {
+    const float4 v = load4<VEC>(w, j);
+    acc += fabs(static_cast<double>(v.x));
+    acc += fabs(static_cast<double>(v.y));
+    acc += fabs(static_cast<double>(v.z));
+    acc += fabs(static_cast<double>(v.w));
+  }
+  const double S = block_sum<kNT>(acc, sh);
+  if (threadIdx.x == 0) {
+    float g;
+    near_sh = gamma_from_fp64(S, static_cast<double>(K), thr, &g) ? 1 : 0;
+    g_sh = g;
+  }
+  __syncthreads();
+  if (near_sh) {  // block-uniform
+    lb[threadIdx.x] = 0ull;
+    __syncthreads();
+    for (int64_t j = threadIdx.x; j < nb; j += kNT) {
+      const float4 v = load4<VEC>(w, j);
+      bin_add(lb, v.x);
+      bin_add(lb, v.y);
+      bin_add(lb, v.z);
+      bin_add(lb, v.w);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0)
+      g_sh = fmaxf(exact_mean_from_bins(lb, static_cast<unsigned long long>(K)),
+                   kGammaEps);
+    __syncthreads();
+  }
+  const float g = g_sh;
+  if (threadIdx.x == 0) scale[row] = g;
+  const float h = g * 0.5f;
+  for (int64_t j = threadIdx.x; j < nb; j += kNT)
+    out[j] = static_cast<uint8_t>(byte_of(load4<VEC>(w, j), h, binary));
+}
+
+// Relative error bound of an fp64 sum of non-negative terms whose longest
+// chain of additions has `depth` steps, including the final division,
+// doubled for margin.
+double sum_error_bound(int64_t depth) {
+  return 2.0 * static_cast<double>(depth + 2) * 0x1p-53;
+}
+
+}  // namespace
+
+size_t pack_tensor_ws_bytes() { return kWsTotal; }
+
+hipError_t launch_pack_tensor(const float* W, int64_t numel, tq_wmode mode,
+                              uint8_t* packed, float* scale, void* ws,
+                              hipStream_t s) {
+  const int binary = mode == TQ_BINARY_SIGN ? 1 : 0;
+  char* base = static_cast<char*>(ws);
+  double* partials = reinterpret_cast<double*>(base + kWsPartials);
+  uint32_t* flag = reinterpret_cast<uint32_t*>(base + kWsFlag);
+  unsigned long long* bins = reinterpret_cast<unsigned long long*>(base + kWsBins);
+  const int64_t n4 = numel / 4;
+  int64_t P = (n4 + kNT * 4 - 1) / (kNT * 4);
+  if (P < 1) P = 1;
+  if (P > kMaxPartials) P = kMaxPartials;
+  const bool vec = (reinterpret_cast<uintptr_t>(W) & 15u) == 0u;
+  // longest addition chain: per-thread loop (4 adds per float4), wave (6) and
+  // block (4) reductions, then the same in the finalising block
+  const int64_t per_thread = (n4 + P * kNT - 1) / (P * kNT);
+  const int64_t depth = 4 * per_thread + 10 + (P + kNT - 1) / kNT + 10;
+  const double thr = sum_error_bound(depth);
+  if (vec)
+    hipLaunchKernelGGL(k_abssum_partial<true>, dim3(P), dim3(kNT), 0, s, W, n4, partials);
+  else
+    hipLaunchKernelGGL(k_abssum_partial<false>, dim3(P), dim3(kNT), 0, s, W, n4, partials);
+  hipLaunchKernelGGL(k_gamma_finalize, dim3(1), dim3(kNT), 0, s, partials,
+                     static_cast<int>(P), numel, thr, flag, bins, scale);
+  if (vec)
+    hipLaunchKernelGGL(k_gamma_bins<true>, dim3(P), dim3(kNT), 0, s, W, n4, flag, bins);
+  else
+    hipLaunchKernelGGL(k_gamma_bins<false>, dim3(P), dim3(kNT), 0, s, W, n4, flag, bins);
+  hipLaunchKernelGGL(k_gamma_exact_final, dim3(1), dim3(kWave), 0, s, flag, bins,
+                     numel, scale);
+  const int64_t nbytes = numel / 4;
+  const bool vec_pack = vec && (reinterpret_cast<uintptr_t>(packed) & 3u) == 0u;
+  int64_t work = vec_pack ? nbytes / 4 : nbytes;
+  int64_t grid = (work + kNT - 1) / kNT;
+  if (grid < 1) grid = 1;
+  if (grid > 8192) grid = 8192;
+  if (vec_pack)
+    hipLaunchKernelGGL(k_ternarize_pack<true>, dim3(grid), dim3(kNT), 0, s, W, nbytes,
+                       binary, scale, packed);
+  else
+    hipLaunchKernelGGL(k_ternarize_pack<false>, dim3(grid), dim3(kNT), 0, s, W, nbytes,
+                       binary, scale, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_rows(const float* W, int64_t N, int64_t K, tq_wmode mode,
+                            uint8_t* packed, float* scale, hipStream_t s) {
+  const int binary = mode == TQ_BINARY_SIGN ? 1 : 0;
+  const bool vec = (reinterpret_cast<uintptr_t>(W) & 15u) == 0u;
+  const int64_t per_thread = (K / 4 + kNT - 1) / kNT;
+  const double thr = sum_error_bound(4 * per_thread + 10);
+  if (vec)
+    hipLaunchKernelGGL(k_pack_rows<true>, dim3(N), dim3(kNT), 0, s, W, K, binary, thr,
+                       packed, scale);
+  else
+    hipLaunchKernelGGL(k_pack_rows<false>, dim3(N), dim3(kNT), 0, s, W, K, binary, thr,
+                       packed, scale);
+  return hipGetLastError();
+}
+
+}  // namespace tq

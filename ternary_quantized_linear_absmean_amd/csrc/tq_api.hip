@@ -1,0 +1,182 @@
+// C ABI of libtq: argument checks, then launches on the caller's stream.
+// Every check runs before any HIP call, so an error status means nothing was
+// enqueued.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "tq.h"
+#include "tq_internal.hpp"
+
+namespace {
+
+thread_local const char* g_last_hip_error = "hipSuccess";
+
+constexpr int64_t kMaxNumelPack = int64_t{1} << 40;  // exact-bin headroom
+constexpr int64_t kMaxKContract = (int64_t{1} << 24) / 127;  // |acc| < 2^24
+
+bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+tq_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return TQ_OK;
+  g_last_hip_error = hipGetErrorName(e);
+  return TQ_ERR_HIP;
+}
+
+tq_status check_contract(const int8_t* q, const float* sx, int64_t M,
+                         const uint8_t* packed, const float* scale, tq_gran g,
+                         int64_t N, int64_t K, void* Y, tq_dtype ydt) {
+  if (M < 0 || N < 0 || K <= 0 || (K % 4) != 0) return TQ_ERR_SHAPE;
+  if (g != TQ_PER_TENSOR && g != TQ_PER_ROW) return TQ_ERR_UNSUPPORTED;
+  if (ydt != TQ_F32 && ydt != TQ_BF16 && ydt != TQ_I32) return TQ_ERR_DTYPE;
+  if (K > kMaxKContract) return TQ_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return TQ_OK;
+  if (!q || !sx || !packed || !scale || !Y) return TQ_ERR_NULL;
+  if (!aligned(sx, 4) || !aligned(scale, 4)) return TQ_ERR_ALIGN;
+  if (!aligned(Y, ydt == TQ_BF16 ? 2 : 4)) return TQ_ERR_ALIGN;
+  return TQ_OK;
+}
+
+tq::GemmArgs make_args(const int8_t* q, const float* sx, int64_t M, const uint8_t* packed,
+                       const float* scale, tq_gran g, int64_t N, int64_t K, void* Y,
+                       tq_dtype ydt) {
+  tq::GemmArgs a;
+  a.q = q;
+  a.sx = sx;
+  a.packed = packed;
+  a.scale = scale;
+  a.per_row = g == TQ_PER_ROW ? 1 : 0;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.Y = Y;
+  a.ydt = static_cast<int>(ydt);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t tq_packed_bytes(int64_t numel) {
+  if (numel <= 0) return 0;
+  return static_cast<size_t>((numel + 3) / 4);
+}
+
+size_t tq_pack_workspace_bytes(int64_t N, int64_t K, tq_gran g) {
+  if (N < 0 || K <= 0 || (K % 4) != 0) return 0;
+  if (g == TQ_PER_TENSOR) return tq::pack_tensor_ws_bytes();
+  return 0;
+}
+
+tq_status tq_pack_ternary(const float* W, int64_t N, int64_t K, tq_gran g, tq_wmode mode,
+                          uint8_t* packed, float* scale, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (N < 0 || K <= 0 || (K % 4) != 0) return TQ_ERR_SHAPE;
+  if (g != TQ_PER_TENSOR && g != TQ_PER_ROW) return TQ_ERR_UNSUPPORTED;
+  if (mode != TQ_TERNARY_ABSMEAN && mode != TQ_BINARY_SIGN) return TQ_ERR_UNSUPPORTED;
+  if (K >= kMaxNumelPack || N >= kMaxNumelPack / K) return TQ_ERR_UNSUPPORTED;
+  if (N == 0) return TQ_OK;
+  if (!W || !packed || !scale) return TQ_ERR_NULL;
+  if (!aligned(W, 4) || !aligned(scale, 4)) return TQ_ERR_ALIGN;
+  if (g == TQ_PER_TENSOR) {
+    const size_t need = tq::pack_tensor_ws_bytes();
+    if (!ws || ws_bytes < need) return TQ_ERR_WORKSPACE;
+    if (!aligned(ws, 8)) return TQ_ERR_ALIGN;
+    return hip_status(tq::launch_pack_tensor(W, N * K, mode, packed, scale, ws, stream));
+  }
+  return hip_status(tq::launch_pack_rows(W, N, K, mode, packed, scale, stream));
+}
+
+tq_status tq_quant_act_int8(const void* X, tq_dtype xdt, int64_t M, int64_t K,
+                            const tq_act_opts* opts, int8_t* q, float* sx,
+                            hipStream_t stream) {
+  if (M < 0 || K <= 0) return TQ_ERR_SHAPE;
+  if (xdt != TQ_F32 && xdt != TQ_BF16) return TQ_ERR_DTYPE;
+  tq::ActParams p;
+  p.eps = 1e-6f;
+  p.clamp = 0;
+  p.eta_min = 0.f;
+  p.eta_max = 0.f;
+  p.rmsnorm = 0;
+  p.rms_eps = 1e-6f;
+  p.rms_weight = nullptr;
+  p.fwht = 0;
+  if (opts) {
+    p.eps = opts->eps;
+    p.clamp = opts->clamp ? 1 : 0;
+    p.eta_min = opts->eta_min;
+    p.eta_max = opts->eta_max;
+    p.rmsnorm = opts->rmsnorm ? 1 : 0;
+    p.rms_eps = opts->rms_eps;
+    p.rms_weight = opts->rms_weight;
+    if (opts->fwht_block != 0 && opts->fwht_block != 512) return TQ_ERR_UNSUPPORTED;
+    p.fwht = opts->fwht_block == 512 ? 1 : 0;
+  }
+  if (!(p.eps > 0.f) || !isfinite(p.eps)) return TQ_ERR_UNSUPPORTED;
+  if (p.clamp && !(p.eta_min > 0.f && p.eta_min <= p.eta_max && isfinite(p.eta_max)))
+    return TQ_ERR_UNSUPPORTED;
+  if (p.rmsnorm && (!(p.rms_eps >= 0.f) || !isfinite(p.rms_eps))) return TQ_ERR_UNSUPPORTED;
+  if (p.fwht && (K % 512) != 0) return TQ_ERR_SHAPE;
+  const bool prologue = p.rmsnorm || p.fwht;
+  if (prologue && K > tq::kPrologueMaxK) return TQ_ERR_UNSUPPORTED;
+  if (M == 0) return TQ_OK;
+  if (!X || !q || !sx) return TQ_ERR_NULL;
+  if (!aligned(X, xdt == TQ_F32 ? 4 : 2) || !aligned(sx, 4)) return TQ_ERR_ALIGN;
+  if (p.rms_weight && !aligned(p.rms_weight, 4)) return TQ_ERR_ALIGN;
+  const int bf16 = xdt == TQ_BF16 ? 1 : 0;
+  if (!prologue) return hip_status(tq::launch_quant_plain(X, bf16, M, K, p, q, sx, stream));
+  return hip_status(tq::launch_quant_prologue(X, bf16, M, K, p, q, sx, stream));
+}
+
+tq_status tq_fwht512(const void* X, tq_dtype xdt, int64_t M, int64_t K, int normalize,
+                     float* Y, hipStream_t stream) {
+  if (M < 0 || K <= 0 || (K % 512) != 0) return TQ_ERR_SHAPE;
+  if (xdt != TQ_F32 && xdt != TQ_BF16) return TQ_ERR_DTYPE;
+  if (M == 0) return TQ_OK;
+  if (!X || !Y) return TQ_ERR_NULL;
+  if (!aligned(X, xdt == TQ_F32 ? 4 : 2) || !aligned(Y, 4)) return TQ_ERR_ALIGN;
+  return hip_status(tq::launch_fwht512(X, xdt == TQ_BF16 ? 1 : 0, M, K, normalize ? 1 : 0,
+                                       Y, stream));
+}
+
+tq_status tq_ternary_gemv(const int8_t* q, const float* sx, int64_t M, const uint8_t* packed,
+                          const float* scale, tq_gran g, int64_t N, int64_t K, void* Y,
+                          tq_dtype ydt, hipStream_t stream) {
+  if (M > tq::kGemvMaxM) return TQ_ERR_SHAPE;
+  const tq_status st = check_contract(q, sx, M, packed, scale, g, N, K, Y, ydt);
+  if (st != TQ_OK || M == 0 || N == 0) return st;
+  return hip_status(tq::launch_gemv(make_args(q, sx, M, packed, scale, g, N, K, Y, ydt),
+                                    stream));
+}
+
+tq_status tq_ternary_gemm(const int8_t* q, const float* sx, int64_t M, const uint8_t* packed,
+                          const float* scale, tq_gran g, int64_t N, int64_t K, void* Y,
+                          tq_dtype ydt, hipStream_t stream) {
+  const tq_status st = check_contract(q, sx, M, packed, scale, g, N, K, Y, ydt);
+  if (st != TQ_OK || M == 0 || N == 0) return st;
+  return hip_status(tq::launch_gemm(make_args(q, sx, M, packed, scale, g, N, K, Y, ydt),
+                                    stream));
+}
+
+const char* tq_status_str(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_NULL: return "null pointer";
+    case TQ_ERR_SHAPE: return "invalid shape";
+    case TQ_ERR_DTYPE: return "unsupported dtype";
+    case TQ_ERR_ALIGN: return "misaligned pointer";
+    case TQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case TQ_ERR_UNSUPPORTED: return "unsupported option or size";
+    case TQ_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* tq_last_hip_error(void) { return g_last_hip_error; }
+
+const char* tq_version(void) { return "0.1.0"; }
+
+}  // extern "C"

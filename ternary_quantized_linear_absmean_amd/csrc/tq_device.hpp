@@ -1,0 +1,146 @@
+// Device-side helpers shared by the libtq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- reductions
+
+__device__ inline double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+__device__ inline int wave_isum(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Block-wide sum / max for blockDim.x == NT (multiple of 64).  `scratch`
+// holds NT/64 entries.  Every thread gets the result.  The partials of the
+// waves are combined in wave order, so the result does not depend on timing.
+template <int NT>
+__device__ inline double block_sum(double v, double* scratch) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) t += scratch[i];
+  __syncthreads();
+  return t;
+}
+
+template <int NT>
+__device__ inline float block_sum(float v, float* scratch) {
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  float t = 0.f;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) t += scratch[i];
+  __syncthreads();
+  return t;
+}
+
+template <int NT>
+__device__ inline float block_max(float v, float* scratch) {
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) scratch[w] = v;
+  __syncthreads();
+  float t = scratch[0];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) t = fmaxf(t, scratch[i]);
+  __syncthreads();
+  return t;
+}
+
+// ------------------------------------------------------------------ numbers
+
+__device__ inline float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ inline uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// round half to even, clamp to [-127, 127], as a byte
+__device__ inline uint32_t quant_byte(float x, float s) {
+  float t = __builtin_rintf(x * s);
+  t = fminf(fmaxf(t, -127.f), 127.f);
+  return static_cast<uint32_t>(static_cast<int>(t)) & 0xFFu;
+}
+
+// --------------------------------------------------------- 2-bit decoding
+
+// One packed 32-bit word holds 16 codes, code i in bits 2i..2i+1 (-1 = 0,
+// 0 = 1, +1 = 2).  Returns the 16 codes (values 0..2) as bytes in natural
+// order: byte j of out[t] is code 4t + j.
+__device__ inline v4i decode_codes_natural(uint32_t w) {
+  const uint32_t d0 = w & 0x03030303u;          // codes 0, 4, 8, 12
+  const uint32_t d1 = (w >> 2) & 0x03030303u;   // codes 1, 5, 9, 13
+  const uint32_t d2 = (w >> 4) & 0x03030303u;   // codes 2, 6, 10, 14
+  const uint32_t d3 = (w >> 6) & 0x03030303u;   // codes 3, 7, 11, 15
+  // 4x4 byte transpose (v_perm_b32: selector 0-3 picks the 2nd operand's bytes)
+  const uint32_t a_lo = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
+  const uint32_t a_hi = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
+  const uint32_t b_lo = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
+  const uint32_t b_hi = __builtin_amdgcn_perm(d3, d2, 0x07030602u);
+  v4i out;
+  out.x = static_cast<int>(__builtin_amdgcn_perm(b_lo, a_lo, 0x05040100u));
+  out.y = static_cast<int>(__builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u));
+  out.z = static_cast<int>(__builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u));
+  out.w = static_cast<int>(__builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u));
+  return out;
+}
+
+// Codes 0..2 in each byte -> signed values -1..+1 (0x7F + c never carries
+// out of its byte; flipping the top bit then gives c - 1 in two's complement).
+__device__ inline uint32_t codes_to_signed(uint32_t c) {
+  return (c + 0x7F7F7F7Fu) ^ 0x80808080u;
+}
+
+__device__ inline v4i decode_signed_natural(uint32_t w) {
+  v4i c = decode_codes_natural(w);
+  v4i s;
+  s.x = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.x)));
+  s.y = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.y)));
+  s.z = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.z)));
+  s.w = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.w)));
+  return s;
+}
+
+// sum of the four signed bytes of v, added to acc
+__device__ inline int byte_sum(uint32_t v, int acc) {
+  return __builtin_amdgcn_sdot4(static_cast<int>(v), 0x01010101, acc, false);
+}
+
+}  // namespace tq

@@ -1,0 +1,54 @@
+// Internal launch interface between the C ABI (tq_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+namespace tq {
+
+// ---- absmean + ternarize + pack (k_pack.hip)
+size_t pack_tensor_ws_bytes();
+hipError_t launch_pack_tensor(const float* W, int64_t numel, tq_wmode mode,
+                              uint8_t* packed, float* scale, void* ws,
+                              hipStream_t s);
+hipError_t launch_pack_rows(const float* W, int64_t N, int64_t K, tq_wmode mode,
+                            uint8_t* packed, float* scale, hipStream_t s);
+
+// ---- activations (k_quant.hip)
+struct ActParams {
+  float eps;
+  int clamp;
+  float eta_min, eta_max;
+  int rmsnorm;
+  float rms_eps;
+  const float* rms_weight;
+  int fwht;
+};
+hipError_t launch_quant_plain(const void* X, int bf16, int64_t M, int64_t K,
+                              const ActParams& p, int8_t* q, float* sx,
+                              hipStream_t s);
+hipError_t launch_quant_prologue(const void* X, int bf16, int64_t M, int64_t K,
+                                 const ActParams& p, int8_t* q, float* sx,
+                                 hipStream_t s);
+hipError_t launch_fwht512(const void* X, int bf16, int64_t M, int64_t K,
+                          int normalize, float* Y, hipStream_t s);
+constexpr int64_t kPrologueMaxK = 32768;
+
+// ---- contraction (k_gemv.hip, k_gemm.hip)
+struct GemmArgs {
+  const int8_t* q;
+  const float* sx;
+  const uint8_t* packed;
+  const float* scale;
+  int per_row;
+  int64_t M, N, K;
+  void* Y;
+  int ydt;  // tq_dtype
+};
+constexpr int kGemvMaxM = 16;
+hipError_t launch_gemv(const GemmArgs& a, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace tq

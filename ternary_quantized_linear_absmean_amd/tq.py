@@ -1,0 +1,225 @@
+"""Python binding of libtq (argument marshalling only).
+
+Each function has the name of the C entry point it calls and forwards torch
+tensors as raw device pointers plus the current HIP stream; every step of the
+computation runs in libtq's kernels.  PyTorch supplies device memory and
+streams.  Importing this module fails if libtq.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with "
+        "`python -m ternary_quantized_linear_absmean_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# enums of include/tq.h
+TQ_OK = 0
+STATUS_NAMES = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_DTYPE",
+                4: "TQ_ERR_ALIGN", 5: "TQ_ERR_WORKSPACE", 6: "TQ_ERR_UNSUPPORTED",
+                7: "TQ_ERR_HIP"}
+DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
+GRANULARITY = {"tensor": 0, "row": 1}
+MODES = {"ternary": 0, "binary": 1}
+EXPORTED = ["tq_packed_bytes", "tq_pack_workspace_bytes", "tq_pack_ternary",
+            "tq_quant_act_int8", "tq_fwht512", "tq_ternary_gemv", "tq_ternary_gemm",
+            "tq_status_str", "tq_last_hip_error", "tq_version"]
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+
+
+class TqActOpts(ctypes.Structure):
+    _fields_ = [("eps", ctypes.c_float), ("clamp", _int), ("eta_min", ctypes.c_float),
+                ("eta_max", ctypes.c_float), ("rmsnorm", _int), ("rms_eps", ctypes.c_float),
+                ("rms_weight", _vp), ("fwht_block", _int)]
+
+
+_lib.tq_packed_bytes.argtypes = [_i64]
+_lib.tq_packed_bytes.restype = ctypes.c_size_t
+_lib.tq_pack_workspace_bytes.argtypes = [_i64, _i64, _int]
+_lib.tq_pack_workspace_bytes.restype = ctypes.c_size_t
+_lib.tq_pack_ternary.argtypes = [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.tq_pack_ternary.restype = _int
+_lib.tq_quant_act_int8.argtypes = [_vp, _int, _i64, _i64, ctypes.POINTER(TqActOpts), _vp, _vp, _vp]
+_lib.tq_quant_act_int8.restype = _int
+_lib.tq_fwht512.argtypes = [_vp, _int, _i64, _i64, _int, _vp, _vp]
+_lib.tq_fwht512.restype = _int
+for _name in ("tq_ternary_gemv", "tq_ternary_gemm"):
+    getattr(_lib, _name).argtypes = [_vp, _vp, _i64, _vp, _vp, _int, _i64, _i64, _vp, _int, _vp]
+    getattr(_lib, _name).restype = _int
+_lib.tq_status_str.argtypes = [_int]
+_lib.tq_status_str.restype = ctypes.c_char_p
+_lib.tq_last_hip_error.argtypes = []
+_lib.tq_last_hip_error.restype = ctypes.c_char_p
+_lib.tq_version.argtypes = []
+_lib.tq_version.restype = ctypes.c_char_p
+
+
+class TqError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        self.status = status
+        msg = f"{call}: {STATUS_NAMES.get(status, status)} ({tq_status_str(status)})"
+        if status == 7:
+            msg += f" [{tq_last_hip_error()}]"
+        super().__init__(msg)
+
+
+def _check(status: int, call: str) -> None:
+    if status != TQ_OK:
+        raise TqError(status, call)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+_ACT_DT = {torch.float32: 0, torch.bfloat16: 1}
+_Y_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "i32": torch.int32}
+
+
+# ------------------------------------------------------------------- sizes
+
+def tq_packed_bytes(numel: int) -> int:
+    return int(_lib.tq_packed_bytes(int(numel)))
+
+
+def tq_pack_workspace_bytes(N: int, K: int, granularity: str = "tensor") -> int:
+    return int(_lib.tq_pack_workspace_bytes(int(N), int(K), GRANULARITY[granularity]))
+
+
+def tq_status_str(status: int) -> str:
+    return _lib.tq_status_str(int(status)).decode()
+
+
+def tq_last_hip_error() -> str:
+    return _lib.tq_last_hip_error().decode()
+
+
+def tq_version() -> str:
+    return _lib.tq_version().decode()
+
+
+# --------------------------------------------------------------- weights
+
+def tq_pack_ternary(W: torch.Tensor, granularity: str = "tensor", mode: str = "ternary",
+                    packed: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, stream=None):
+    """W [N, K] fp32 -> (packed uint8 [N, K/4], scale fp32 [1] or [N])."""
+    _dev(W, "W")
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float32 tensor")
+    N, K = W.shape
+    if packed is None:
+        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    if scale is None:
+        scale = torch.empty((1 if granularity == "tensor" else N,), dtype=torch.float32,
+                            device=W.device)
+    need = tq_pack_workspace_bytes(N, K, granularity)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=W.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.tq_pack_ternary(W.data_ptr(), N, K, GRANULARITY[granularity], MODES[mode],
+                                _ptr(packed), _ptr(scale), _ptr(workspace), ws_bytes,
+                                _stream(stream)), "tq_pack_ternary")
+    return packed, scale
+
+
+# ------------------------------------------------------------ activations
+
+def tq_quant_act_int8(X: torch.Tensor, eps: float = 1e-6, clamp=None, rmsnorm: bool = False,
+                      rms_eps: float = 1e-6, rms_weight: torch.Tensor | None = None,
+                      fwht_block: int = 0, q: torch.Tensor | None = None,
+                      sx: torch.Tensor | None = None, stream=None):
+    """X [M, K] fp32/bf16 -> (q int8 [M, K], sx fp32 [M]).  ``clamp`` is an
+    (eta_min, eta_max) pair or None."""
+    _dev(X, "X")
+    if X.dtype not in _ACT_DT or X.dim() != 2:
+        raise ValueError("X must be a 2-D float32 or bfloat16 tensor")
+    M, K = X.shape
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
+    opts = TqActOpts(eps=eps, clamp=1 if clamp else 0,
+                     eta_min=clamp[0] if clamp else 0.0, eta_max=clamp[1] if clamp else 0.0,
+                     rmsnorm=1 if rmsnorm else 0, rms_eps=rms_eps,
+                     rms_weight=_ptr(rms_weight), fwht_block=fwht_block)
+    _check(_lib.tq_quant_act_int8(X.data_ptr(), _ACT_DT[X.dtype], M, K, ctypes.byref(opts),
+                                  _ptr(q), _ptr(sx), _stream(stream)), "tq_quant_act_int8")
+    return q, sx
+
+
+def tq_fwht512(X: torch.Tensor, normalize: bool = True, Y: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """Blockwise FWHT-512 along the last axis of X [M, K] -> fp32 [M, K]."""
+    _dev(X, "X")
+    if X.dtype not in _ACT_DT or X.dim() != 2:
+        raise ValueError("X must be a 2-D float32 or bfloat16 tensor")
+    M, K = X.shape
+    if Y is None:
+        Y = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    _check(_lib.tq_fwht512(X.data_ptr(), _ACT_DT[X.dtype], M, K, 1 if normalize else 0,
+                           _ptr(Y), _stream(stream)), "tq_fwht512")
+    return Y
+
+
+# ------------------------------------------------------------ contraction
+
+def _contract(fn, name, q, sx, packed, scale, N, K, granularity, out_dtype, Y, stream):
+    _dev(q, "q")
+    _dev(sx, "sx")
+    _dev(packed, "packed")
+    _dev(scale, "scale")
+    if q.dtype != torch.int8 or packed.dtype != torch.uint8:
+        raise ValueError("q must be int8 and packed uint8")
+    M = q.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=_Y_TORCH[out_dtype], device=q.device)
+    _check(fn(q.data_ptr(), sx.data_ptr(), M, packed.data_ptr(), scale.data_ptr(),
+              GRANULARITY[granularity], N, K, _ptr(Y), DTYPES[out_dtype], _stream(stream)),
+           name)
+    return Y
+
+
+def tq_ternary_gemv(q, sx, packed, scale, N: int, K: int, granularity: str = "tensor",
+                    out_dtype: str = "f32", Y=None, stream=None) -> torch.Tensor:
+    """y = (q @ W^T) * scale * sx for M <= 16 tokens -> [M, N]."""
+    return _contract(_lib.tq_ternary_gemv, "tq_ternary_gemv", q, sx, packed, scale, N, K,
+                     granularity, out_dtype, Y, stream)
+
+
+def tq_ternary_gemm(q, sx, packed, scale, N: int, K: int, granularity: str = "tensor",
+                    out_dtype: str = "f32", Y=None, stream=None) -> torch.Tensor:
+    """Same contract as tq_ternary_gemv for any number of tokens."""
+    return _contract(_lib.tq_ternary_gemm, "tq_ternary_gemm", q, sx, packed, scale, N, K,
+                     granularity, out_dtype, Y, stream)
+
+
+def raw_library() -> ctypes.CDLL:
+    """The loaded libtq handle (for tests of the C ABI itself)."""
+    return _lib

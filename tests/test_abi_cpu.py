@@ -1,0 +1,170 @@
+"""The C ABI on the CPU: the library loads, exports what include/tq.h
+declares, and rejects bad arguments before touching HIP.
+
+No call here can reach a kernel launch: each one fails validation or is an
+empty (M == 0 / N == 0) call, which returns before any HIP call.
+"""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+tqmod = pytest.importorskip("ternary_quantized_linear_absmean_amd.tq",
+                            reason="libtq.so not built")
+lib = tqmod.raw_library()
+
+OK, NULL, SHAPE, DTYPE, ALIGN, WS, UNSUP = 0, 1, 2, 3, 4, 5, 6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert set(names) == set(tqmod.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_packed_bytes_and_workspace():
+    assert tqmod.tq_packed_bytes(4096 * 4096) == 4194304
+    assert tqmod.tq_packed_bytes(256) == 64
+    assert [tqmod.tq_packed_bytes(n) for n in range(0, 10)] == [0, 1, 1, 1, 1, 2, 2, 2, 2, 3]
+    assert tqmod.tq_packed_bytes(-5) == 0
+    assert tqmod.tq_pack_workspace_bytes(4096, 4096, "tensor") > 0
+    assert tqmod.tq_pack_workspace_bytes(4096, 4096, "row") == 0
+    assert tqmod.tq_pack_workspace_bytes(4, 6, "tensor") == 0
+
+
+def test_status_strings():
+    for s in range(8):
+        assert tqmod.tq_status_str(s)
+    assert tqmod.tq_status_str(99) == "unknown status"
+    assert tqmod.tq_version() == "0.1.0"
+    assert tqmod.tq_last_hip_error() == "hipSuccess"
+
+
+def _gemv(*a):
+    return lib.tq_ternary_gemv(*a)
+
+
+def _gemm(*a):
+    return lib.tq_ternary_gemm(*a)
+
+
+@pytest.mark.parametrize("fn", [_gemv, _gemm])
+def test_contract_validation(fn):
+    P = 0x10000  # never dereferenced: every call below fails validation
+    # shapes
+    assert fn(P, P, -1, P, P, 0, 16, 64, P, 0, None) == SHAPE
+    assert fn(P, P, 1, P, P, 0, -1, 64, P, 0, None) == SHAPE
+    assert fn(P, P, 1, P, P, 0, 16, 0, P, 0, None) == SHAPE
+    assert fn(P, P, 1, P, P, 0, 16, 62, P, 0, None) == SHAPE
+    # enums
+    assert fn(P, P, 1, P, P, 2, 16, 64, P, 0, None) == UNSUP
+    assert fn(P, P, 1, P, P, 0, 16, 64, P, 3, None) == DTYPE
+    # K beyond the int32 headroom of 127 * K < 2^24
+    assert fn(P, P, 1, P, P, 0, 16, 132108, P, 0, None) == UNSUP
+    # NULL pointers with a non-empty problem
+    assert fn(None, P, 1, P, P, 0, 16, 64, P, 0, None) == NULL
+    assert fn(P, None, 1, P, P, 0, 16, 64, P, 0, None) == NULL
+    assert fn(P, P, 1, None, P, 0, 16, 64, P, 0, None) == NULL
+    assert fn(P, P, 1, P, None, 0, 16, 64, P, 0, None) == NULL
+    assert fn(P, P, 1, P, P, 0, 16, 64, None, 0, None) == NULL
+    # misaligned fp32 pointers
+    assert fn(P, P + 1, 1, P, P, 0, 16, 64, P, 0, None) == ALIGN
+    assert fn(P, P, 1, P, P + 2, 0, 16, 64, P, 0, None) == ALIGN
+    assert fn(P, P, 1, P, P, 0, 16, 64, P + 2, 0, None) == ALIGN
+    assert fn(P, P, 1, P, P, 0, 16, 64, P + 1, 1, None) == ALIGN
+    # empty problems are valid no-ops, even with NULL pointers
+    assert fn(None, None, 0, None, None, 0, 16, 64, None, 0, None) == OK
+    assert fn(None, None, 1, None, None, 0, 0, 64, None, 0, None) == OK
+
+
+def test_gemv_token_limit():
+    P = 0x10000
+    assert _gemv(P, P, 17, P, P, 0, 16, 64, P, 0, None) == SHAPE
+    # the GEMM has no such limit: same call fails only on the NULL Y
+    assert _gemm(P, P, 17, P, P, 0, 16, 64, None, 0, None) == NULL
+
+
+def test_pack_validation():
+    P = 0x10000
+    f = lib.tq_pack_ternary
+    assert f(P, -1, 64, 0, 0, P, P, P, 1 << 20, None) == SHAPE
+    assert f(P, 4, 0, 0, 0, P, P, P, 1 << 20, None) == SHAPE
+    assert f(P, 4, 6, 0, 0, P, P, P, 1 << 20, None) == SHAPE
+    assert f(P, 4, 64, 5, 0, P, P, P, 1 << 20, None) == UNSUP
+    assert f(P, 4, 64, 0, 7, P, P, P, 1 << 20, None) == UNSUP
+    assert f(P, 1 << 20, 1 << 20, 0, 0, P, P, P, 1 << 20, None) == UNSUP   # 2^40 values
+    assert f(None, 4, 64, 0, 0, P, P, P, 1 << 20, None) == NULL
+    assert f(P, 4, 64, 0, 0, None, P, P, 1 << 20, None) == NULL
+    assert f(P, 4, 64, 0, 0, P, None, P, 1 << 20, None) == NULL
+    assert f(P + 2, 4, 64, 0, 0, P, P, P, 1 << 20, None) == ALIGN
+    assert f(P, 4, 64, 0, 0, P, P + 1, P, 1 << 20, None) == ALIGN
+    assert f(P, 4, 64, 0, 0, P, P, None, 1 << 20, None) == WS
+    assert f(P, 4, 64, 0, 0, P, P, P, 16, None) == WS
+    assert f(P, 4, 64, 0, 0, P, P, P + 4, 1 << 20, None) == ALIGN
+    assert f(None, 0, 64, 0, 0, None, None, None, 0, None) == OK
+
+
+def test_quant_validation():
+    P = 0x10000
+    f = lib.tq_quant_act_int8
+    O = tqmod.TqActOpts
+    assert f(P, 0, -1, 64, None, P, P, None) == SHAPE
+    assert f(P, 0, 1, 0, None, P, P, None) == SHAPE
+    assert f(P, 2, 1, 64, None, P, P, None) == DTYPE
+    assert f(None, 0, 1, 64, None, P, P, None) == NULL
+    assert f(P, 0, 1, 64, None, None, P, None) == NULL
+    assert f(P, 0, 1, 64, None, P, None, None) == NULL
+    assert f(P + 2, 0, 1, 64, None, P, P, None) == ALIGN
+    assert f(P + 1, 1, 1, 64, None, P, P, None) == ALIGN
+    assert f(P, 0, 1, 64, None, P, P + 2, None) == ALIGN
+    assert f(None, 0, 0, 64, None, None, None, None) == OK
+
+    def opts(**kw):
+        base = dict(eps=1e-6, clamp=0, eta_min=0.0, eta_max=0.0, rmsnorm=0, rms_eps=1e-6,
+                    rms_weight=None, fwht_block=0)
+        base.update(kw)
+        return O(**base)
+    import ctypes
+    r = lambda o, K=512: f(P, 0, 1, K, ctypes.byref(o), P, P, None)
+    assert r(opts(fwht_block=256)) == UNSUP
+    assert r(opts(fwht_block=512), K=1000) == SHAPE
+    assert r(opts(eps=0.0)) == UNSUP
+    assert r(opts(eps=float("nan"))) == UNSUP
+    assert r(opts(clamp=1, eta_min=0.0, eta_max=40.0)) == UNSUP
+    assert r(opts(clamp=1, eta_min=50.0, eta_max=40.0)) == UNSUP
+    assert r(opts(rmsnorm=1, rms_eps=-1.0)) == UNSUP
+    assert r(opts(rmsnorm=1), K=65536) == UNSUP
+    assert r(opts(rmsnorm=1, rms_weight=P + 2)) == ALIGN
+
+
+def test_fwht_validation():
+    P = 0x10000
+    f = lib.tq_fwht512
+    assert f(P, 0, 1, 500, 1, P, None) == SHAPE
+    assert f(P, 0, -1, 512, 1, P, None) == SHAPE
+    assert f(P, 3, 1, 512, 1, P, None) == DTYPE
+    assert f(None, 0, 1, 512, 1, P, None) == NULL
+    assert f(P, 0, 1, 512, 1, None, None) == NULL
+    assert f(P + 2, 0, 1, 512, 1, P, None) == ALIGN
+    assert f(P, 0, 1, 512, 1, P + 2, None) == ALIGN
+    assert f(None, 0, 0, 512, 1, None, None) == OK
+
+
+def test_product_path_has_no_cpu_fallback():
+    # nothing in the package imports the oracle or computes on the host
+    pkg = os.path.join(ROOT, "ternary_quantized_linear_absmean_amd")
+    for fn in os.listdir(pkg):
+        if fn.endswith(".py"):
+            src = open(os.path.join(pkg, fn)).read()
+            assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), fn
+            assert "numpy" not in src, fn

@@ -1,0 +1,495 @@
+"""GPU parity: every libtq entry point against the CPU oracle.
+
+Bars: packed bytes, scales of the plain paths, int8 codes and int32
+accumulators bit-exact; fp32 outputs within 1e-5 relative of the fp64
+oracle value; bf16 outputs within one bf16 step of the oracle's rounding.
+Full-size workloads are checked completely where the oracle is quick and on
+sampled output columns (every token) for the large GEMMs.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import tq_inputs as ti
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+tq = pytest.importorskip("ternary_quantized_linear_absmean_amd.tq")
+
+DEV = "cuda:0"
+RTOL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def dev_bf16(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV).to(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def f32_bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+def assert_y_close(y, yref):
+    y = np.asarray(y, np.float64)
+    err = np.abs(y - yref)
+    bad = err > RTOL * np.abs(yref)
+    assert not bad.any(), (f"{bad.sum()} outputs beyond {RTOL} relative; worst rel "
+                           f"{np.max(err / np.maximum(np.abs(yref), 1e-300))}")
+
+
+def assert_bf16_close(ybits, yref):
+    # y must be within one bf16 step of the bf16 nearest to the oracle value
+    y = (np.asarray(ybits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r = oracle.bf16_round_from_f64(yref).astype(np.float64)
+    step = np.abs(r) * 2.0 ** -7 + 1e-300
+    assert np.all(np.abs(y - r) <= step), "bf16 output off by more than one step"
+
+
+def x_to_device(x, dtype):
+    return dev_bf16(x) if dtype == "bf16" else dev(x.astype(np.float32))
+
+
+# ----------------------------------------------------------------- oracle cache
+
+@functools.lru_cache(maxsize=None)
+def ref_pack(name, j=0, mode="ternary"):
+    W = ti.workload_weights(name, j)
+    gran = ti.WORKLOADS[name]["gran"]
+    packed, scale = oracle.pack_ternary(W, gran, mode)
+    return W, packed, scale
+
+
+@functools.lru_cache(maxsize=None)
+def ref_quant(name, j=0, b=None):
+    X = ti.workload_activations(name, j, b)
+    if ti.WORKLOADS[name].get("prologue"):
+        q, sx, sxe, bound = oracle.rmsnorm_fwht_quant(X)
+        return X, q, sx, sxe
+    q, sx = oracle.quant_act_int8(X)
+    return X, q, sx, sx.astype(np.float64)
+
+
+# ------------------------------------------------------------------------ pack
+
+PACK_CASES = [("tiny", 0, "ternary"), ("decode", 0, "ternary"), ("ffn", 0, "ternary"),
+              ("ffn", 1, "ternary"), ("prefill", 0, "ternary"), ("bitlinear", 0, "ternary"),
+              ("bitlinear", 0, "binary")]
+
+
+@pytest.mark.parametrize("name,j,mode", PACK_CASES)
+def test_pack_workloads(name, j, mode):
+    W, packed_ref, scale_ref = ref_pack(name, j, mode)
+    gran = ti.WORKLOADS[name]["gran"]
+    say(f"pack {name}[{j}] {mode} {W.shape} {gran}")
+    packed, scale = tq.tq_pack_ternary(dev(W), gran, mode)
+    np.testing.assert_array_equal(f32_bits(host(scale)), f32_bits(scale_ref))
+    np.testing.assert_array_equal(host(packed), packed_ref)
+
+
+def _pack_pair(W, gran, mode="ternary"):
+    packed, scale = tq.tq_pack_ternary(dev(np.ascontiguousarray(W, np.float32)), gran, mode)
+    pr, sr = oracle.pack_ternary(W, gran, mode)
+    np.testing.assert_array_equal(f32_bits(host(scale)), f32_bits(sr))
+    np.testing.assert_array_equal(host(packed), pr)
+    return sr
+
+
+def _f32(bits):
+    return np.array([bits], np.uint32).view(np.float32)[0]
+
+
+def test_pack_gamma_exact_fallback():
+    # mean exactly on / just beyond an fp32 midpoint: the fp64 sum cannot
+    # decide, the exact integer path must (tensor and row granularity)
+    tie_up = np.array([1.0, 1.0, _f32(0x3F800001), 2.0**-60], np.float32)   # -> 0x3F400001
+    tie_even = np.array([1.0, _f32(0x3F800001), 1.0, _f32(0x3F800001)], np.float32)  # -> 1.0
+    for row in (tie_up, tie_even):
+        say("pack tie", row)
+        s = _pack_pair(row.reshape(1, 4), "tensor")
+        assert s[0] == oracle.absmean_scale(row)
+        _pack_pair(row.reshape(1, 4), "row")
+    assert _pack_pair(tie_up.reshape(1, 4), "tensor")[0] == _f32(0x3F400001)
+    # several tied rows among ordinary ones, per row
+    W = ti.normal_weights(77, 64, 128)
+    W[3] = np.tile(tie_up, 32)
+    W[40] = np.tile(tie_even, 32)
+    _pack_pair(W, "row")
+    # a large tensor whose mean is an exact midpoint
+    big = np.ones((1024, 1024), np.float32)
+    big[:, ::2] = _f32(0x3F800001)              # mean 1 + 2^-24: a midpoint
+    _pack_pair(big, "tensor")
+
+
+@pytest.mark.parametrize("N,K", [(1, 4), (3, 60), (17, 68), (257, 260), (5, 4096), (2, 8)])
+@pytest.mark.parametrize("gran", ["tensor", "row"])
+@pytest.mark.parametrize("mode", ["ternary", "binary"])
+def test_pack_awkward_shapes(N, K, gran, mode):
+    W = ti.normal_weights(1000 + N + K, N, K)
+    say(f"pack awkward {N}x{K} {gran} {mode}")
+    _pack_pair(W, gran, mode)
+
+
+def test_pack_edge_values():
+    # zeros (gamma = eps, all zero codes), signed zeros, exact half-gamma ties
+    say("pack edge values")
+    _pack_pair(np.zeros((4, 64), np.float32), "tensor")
+    _pack_pair(np.zeros((4, 64), np.float32), "row")
+    W = np.zeros((2, 8), np.float32)
+    W[0] = [1.0, -1.0, 3.0, -3.0, 1.0, 1.0, -3.0, 3.0]       # gamma 2: |w| = 1 ties at gamma/2
+    W[1] = [-0.0, 0.0, 1e-30, -1e-30, 5.0, -5.0, 0.0, 0.0]
+    _pack_pair(W, "row")
+    _pack_pair(W, "tensor")
+    _pack_pair(W, "row", "binary")
+    _pack_pair(np.full((3, 12), 1e-8, np.float32), "row")     # below the gamma floor
+
+
+def test_pack_unaligned_weights():
+    W = ti.normal_weights(5, 9, 64)
+    flat = torch.zeros(9 * 64 + 1, dtype=torch.float32, device=DEV)
+    flat[1:] = dev(W).reshape(-1)
+    Wd = flat[1:].view(9, 64)                                   # 4-byte aligned only
+    say("pack unaligned")
+    for gran in ("tensor", "row"):
+        packed, scale = tq.tq_pack_ternary(Wd, gran)
+        pr, sr = oracle.pack_ternary(W, gran)
+        np.testing.assert_array_equal(host(packed), pr)
+        np.testing.assert_array_equal(f32_bits(host(scale)), f32_bits(sr))
+
+
+# ------------------------------------------------------------------- act quant
+
+QUANT_CASES = [("tiny", 0, 4), ("decode", 0, 1), ("ffn", 0, 1), ("ffn", 0, 4), ("ffn", 0, 16),
+               ("ffn", 1, 1), ("ffn", 1, 16), ("prefill", 0, 2048)]
+
+
+@pytest.mark.parametrize("name,j,b", QUANT_CASES)
+def test_quant_workloads(name, j, b):
+    X, q_ref, sx_ref, _ = ref_quant(name, j, b)
+    say(f"quant {name}[{j}] b={b} {X.shape}")
+    q, sx = tq.tq_quant_act_int8(x_to_device(X, ti.WORKLOADS[name]["x_dtype"]))
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sx_ref))
+
+
+@pytest.mark.parametrize("M,K", [(1, 4), (3, 60), (2, 68), (5, 260), (17, 1000), (1, 7),
+                                 (2, 6912), (1, 40000)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_quant_awkward(M, K, dtype):
+    X = ti.activations(500 + M + K, M, K, dtype=dtype)
+    if M >= 3:
+        X[1] = 0.0                                  # zero token
+    say(f"quant awkward {M}x{K} {dtype}")
+    q, sx = tq.tq_quant_act_int8(x_to_device(X, dtype))
+    qr, sr = oracle.quant_act_int8(X)
+    np.testing.assert_array_equal(host(q), qr)
+    np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sr))
+
+
+def test_quant_clamp_and_ties():
+    rng = np.random.default_rng(42)
+    X = np.stack([(rng.standard_normal(512) * 500).astype(np.float32),
+                  (rng.standard_normal(512) * 1e-5).astype(np.float32),
+                  rng.standard_normal(512).astype(np.float32)])
+    say("quant clamp")
+    q, sx = tq.tq_quant_act_int8(dev(X), clamp=(0.05, 40.0))
+    qr, sr = oracle.quant_act_int8(X, eta_min=0.05, eta_max=40.0)
+    np.testing.assert_array_equal(host(q), qr)
+    np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sr))
+    T = np.zeros((3, 8), np.float32)
+    T[0, :5] = [0.5, 1.5, 2.5, -0.5, 127]
+    T[1, :5] = [-127, 3.5, -3.5, 4.5, -2.5]
+    T[2, :5] = [63.5, -63.5, 0, 1, 127]
+    q, sx = tq.tq_quant_act_int8(dev(T))
+    qr, sr = oracle.quant_act_int8(T)
+    np.testing.assert_array_equal(host(q), qr)
+
+
+def test_quant_scale_division_sweep():
+    # every token max is a different fp32; q and sx bit-exact checks the
+    # device's 127/eta and eta/127 against IEEE division
+    rng = np.random.default_rng(3)
+    M = 4096
+    X = rng.standard_normal((M, 64)).astype(np.float32) * \
+        np.float32(10.0) ** rng.uniform(-6, 6, (M, 1)).astype(np.float32)
+    say("quant division sweep")
+    q, sx = tq.tq_quant_act_int8(dev(X))
+    qr, sr = oracle.quant_act_int8(X)
+    np.testing.assert_array_equal(host(q), qr)
+    np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sr))
+
+
+# --------------------------------------------------------------------- FWHT
+
+@pytest.mark.parametrize("M,K", [(1, 512), (3, 1536), (64, 4096)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("normalize", [True, False])
+def test_fwht512(M, K, dtype, normalize):
+    X = ti.activations(900 + M + K, M, K, dist="student_t3", dtype=dtype)
+    say(f"fwht {M}x{K} {dtype} norm={normalize}")
+    Y = tq.tq_fwht512(x_to_device(X, dtype), normalize)
+    Yr = oracle.fwht512(X, normalize)
+    np.testing.assert_array_equal(f32_bits(host(Y)), f32_bits(Yr))
+
+
+def test_fwht512_integer_exact_and_spike():
+    rng = np.random.default_rng(7)
+    x = rng.integers(-2**14, 2**14 + 1, size=(4, 512)).astype(np.float32)
+    Y = host(tq.tq_fwht512(dev(x), False)).astype(np.int64)
+    np.testing.assert_array_equal(Y, x.astype(np.int64) @ oracle.hadamard_matrix(512).T)
+    spike = np.zeros((1, 512), np.float32)
+    spike[0, 256] = 100.0
+    Y = host(tq.tq_fwht512(dev(spike), True))
+    assert abs(np.max(np.abs(Y)) - 4.4194) < 1e-4
+
+
+# ----------------------------------------------------------------- prologue
+
+def test_prologue_bitlinear_workload():
+    X, q_ref, sx_ref, sxe = ref_quant("bitlinear")
+    say(f"prologue bitlinear {X.shape}")
+    q, sx = tq.tq_quant_act_int8(dev_bf16(X), clamp=(0.05, 40.0), rmsnorm=True,
+                                 fwht_block=512)
+    np.testing.assert_array_equal(host(q), q_ref)
+    np.testing.assert_allclose(host(sx).astype(np.float64), sxe, rtol=2e-6)
+
+
+@pytest.mark.parametrize("rmsnorm,fwht", [(True, False), (False, True), (True, True)])
+@pytest.mark.parametrize("M,K", [(3, 512), (2, 1536), (4, 8192), (1, 32768)])
+def test_prologue_variants(rmsnorm, fwht, M, K):
+    X = ti.activations(1200 + M + K, M, K, dist="student_t3", dtype="f32")
+    g = (1.0 + 0.25 * ti.activations(7, 1, K, dtype="f32")[0]).astype(np.float32)
+    say(f"prologue rms={rmsnorm} fwht={fwht} {M}x{K}")
+    for weight in (None, g):
+        q, sx = tq.tq_quant_act_int8(dev(X), clamp=(0.05, 40.0), rmsnorm=rmsnorm,
+                                     rms_weight=None if weight is None else dev(weight),
+                                     fwht_block=512 if fwht else 0)
+        qr, sr, sxe, bound = oracle.rmsnorm_fwht_quant(X, rms_weight=weight, rmsnorm=rmsnorm,
+                                                       fwht=fwht)
+        qg, sg = host(q), host(sx).astype(np.float64)
+        free = ~bound
+        # rows where the clamp binds take their codes through the fp32 RMS
+        # factor, whose summation order is free: allow one step there
+        np.testing.assert_array_equal(qg[free], qr[free])
+        assert np.abs(qg[bound].astype(int) - qr[bound].astype(int)).max(initial=0) <= 1
+        np.testing.assert_allclose(sg, sxe, rtol=2e-6)
+
+
+def test_prologue_clamp_branches():
+    rng = np.random.default_rng(9)
+    K = 4096
+    H = oracle.hadamard_matrix(512)
+    xa = np.zeros(K, np.float32)
+    xa[1024:1536] = (H[37] * 2.0**3).astype(np.float32)          # eta_true 64 > 40
+    xb = (rng.choice([-1.0, 1.0], size=K) * 2.0**-20).astype(np.float32)  # < 0.05
+    xc = np.zeros(K, np.float32)
+    xd = (rng.choice([-1.0, 1.0], size=K) * 2.0**5).astype(np.float32)    # no clamp
+    X = np.stack([xa, xb, xc, xd])
+    say("prologue clamp branches")
+    q, sx = tq.tq_quant_act_int8(dev(X), clamp=(0.05, 40.0), rmsnorm=True, fwht_block=512)
+    qr, sr, sxe, bound = oracle.rmsnorm_fwht_quant(X)
+    assert list(bound) == [True, True, True, False]
+    np.testing.assert_array_equal(host(q), qr)
+    sxg = host(sx)
+    np.testing.assert_array_equal(f32_bits(sxg[:3]), f32_bits(sr[:3]))
+    np.testing.assert_allclose(sxg[3], sxe[3], rtol=2e-6)
+
+
+# --------------------------------------------------------------- contraction
+
+def _contract_ref(q, packed, K, scale, sx, cols=None):
+    if cols is None:
+        acc = oracle.contract(q, packed, K)
+        y = oracle.epilogue(acc, scale, sx)
+    else:
+        acc = oracle.contract_rows(q, packed, K, cols)
+        y = oracle.epilogue(acc, scale, sx, rows=cols)
+    return acc, y
+
+
+def _check_outputs(fn, qd, sxd, pd, sd, N, K, gran, q, packed, scale, sx, cols=None):
+    acc_ref, y_ref = _contract_ref(q, packed, K, scale, sx, cols)
+    sel = (lambda a: a) if cols is None else (lambda a: a[:, cols])
+    acc = host(fn(qd, sxd, pd, sd, N, K, gran, "i32"))
+    np.testing.assert_array_equal(sel(acc).astype(np.int64), acc_ref)
+    y = host(fn(qd, sxd, pd, sd, N, K, gran, "f32"))
+    assert_y_close(sel(y), y_ref)
+    assert np.all(sel(y)[acc_ref == 0] == 0)
+    yb = host(fn(qd, sxd, pd, sd, N, K, gran, "bf16").view(torch.int16)).view(np.uint16)
+    assert_bf16_close(sel(yb), y_ref)
+
+
+GEMV_CASES = [("tiny", 0, 4), ("decode", 0, 1), ("ffn", 0, 1), ("ffn", 0, 4), ("ffn", 0, 16),
+              ("ffn", 1, 1), ("ffn", 1, 4), ("ffn", 1, 16)]
+
+
+@pytest.mark.parametrize("name,j,b", GEMV_CASES)
+def test_gemv_workloads(name, j, b):
+    W, packed, scale = ref_pack(name, j)
+    X, q, sx, _ = ref_quant(name, j, b)
+    N, K = W.shape
+    gran = ti.WORKLOADS[name]["gran"]
+    say(f"gemv {name}[{j}] b={b} N={N} K={K}")
+    _check_outputs(tq.tq_ternary_gemv, dev(q), dev(sx), dev(packed), dev(scale), N, K, gran,
+                   q, packed, scale, sx)
+
+
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 15, 16])
+@pytest.mark.parametrize("N,K", [(1, 4), (3, 60), (64, 64), (257, 68), (33, 260),
+                                 (100, 2560), (17, 1000)])
+def test_gemv_awkward(M, N, K):
+    q = ti.random_int8(M * 7 + N + K, M, K)
+    w = ti.random_ternary(N + 3 * K, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(N, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(M + 1, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    say(f"gemv awkward M={M} N={N} K={K}")
+    for gran, sc in (("row", scale), ("tensor", scale[:1])):
+        _check_outputs(tq.tq_ternary_gemv, dev(q), dev(sx), dev(packed), dev(sc), N, K, gran,
+                       q, packed, sc, sx)
+
+
+def test_gemv_extreme_accumulators():
+    # |acc| = 127*K at the largest K of the workloads, in both signs
+    K, N = 6912, 20
+    q = np.full((2, K), 127, np.int8)
+    q[1] = -127
+    w = np.ones((N, K), np.int8)
+    w[1::2] = -1
+    packed = oracle.pack_codes(w)
+    scale = np.array([0.5], np.float32)
+    sx = np.array([1.0, 2.0], np.float32)
+    say("gemv extremes")
+    _check_outputs(tq.tq_ternary_gemv, dev(q), dev(sx), dev(packed), dev(scale), N, K,
+                   "tensor", q, packed, scale, sx)
+    _check_outputs(tq.tq_ternary_gemm, dev(q), dev(sx), dev(packed), dev(scale), N, K,
+                   "tensor", q, packed, scale, sx)
+
+
+def test_gemv_unaligned_buffers():
+    M, N, K = 3, 40, 256
+    q = ti.random_int8(1, M, K)
+    w = ti.random_ternary(2, N, K)
+    packed = oracle.pack_codes(w)
+    scale = np.array([0.25], np.float32)
+    sx = np.array([0.1, 0.2, 0.3], np.float32)
+    qbuf = torch.zeros(M * K + 1, dtype=torch.int8, device=DEV)
+    qbuf[1:] = dev(q).reshape(-1)
+    pbuf = torch.zeros(N * K // 4 + 3, dtype=torch.uint8, device=DEV)
+    pbuf[3:] = dev(packed).reshape(-1)
+    qd, pd = qbuf[1:].view(M, K), pbuf[3:].view(N, K // 4)
+    say("contract unaligned")
+    for fn in (tq.tq_ternary_gemv, tq.tq_ternary_gemm):
+        _check_outputs(fn, qd, dev(sx), pd, dev(scale), N, K, "tensor", q, packed, scale, sx)
+
+
+@pytest.mark.parametrize("M", [17, 33, 100, 257])
+@pytest.mark.parametrize("N,K", [(1, 4), (3, 60), (64, 64), (257, 68), (130, 260),
+                                 (200, 2560)])
+def test_gemm_awkward(M, N, K):
+    q = ti.random_int8(M * 5 + N + K, M, K)
+    w = ti.random_ternary(N + 7 * K, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(N + 9, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(M + 2, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    say(f"gemm awkward M={M} N={N} K={K}")
+    for gran, sc in (("row", scale), ("tensor", scale[:1])):
+        _check_outputs(tq.tq_ternary_gemm, dev(q), dev(sx), dev(packed), dev(sc), N, K, gran,
+                       q, packed, sc, sx)
+
+
+def test_gemm_small_m_matches_gemv():
+    for M in (1, 5, 16):
+        q = ti.random_int8(M, M, 4096)
+        w = ti.random_ternary(M + 1, 300, 4096)
+        packed = oracle.pack_codes(w)
+        scale = np.array([0.02], np.float32)
+        sx = np.full(M, 0.01, np.float32)
+        say(f"gemm small M={M}")
+        a = host(tq.tq_ternary_gemm(dev(q), dev(sx), dev(packed), dev(scale), 300, 4096,
+                                    "tensor", "i32"))
+        b = host(tq.tq_ternary_gemv(dev(q), dev(sx), dev(packed), dev(scale), 300, 4096,
+                                    "tensor", "i32"))
+        np.testing.assert_array_equal(a, b)
+        np.testing.assert_array_equal(a.astype(np.int64), oracle.contract(q, packed, 4096))
+
+
+def _sample_cols(N, seed, n=96):
+    rng = np.random.default_rng(seed)
+    cols = np.unique(np.concatenate([rng.choice(N, size=min(n, N), replace=False),
+                                     [0, 1, 31, 32, 127, 128, N - 1]]))
+    return cols[cols < N]
+
+
+def test_gemm_prefill_workload_sampled():
+    W, packed, scale = ref_pack("prefill")
+    X, q, sx, _ = ref_quant("prefill")
+    N, K = W.shape
+    cols = _sample_cols(N, 4)
+    say(f"gemm prefill {q.shape} x {W.shape}, {cols.size} sampled columns")
+    _check_outputs(tq.tq_ternary_gemm, dev(q), dev(sx), dev(packed), dev(scale), N, K,
+                   "tensor", q, packed, scale, sx, cols=cols)
+
+
+@pytest.mark.parametrize("mode", ["ternary", "binary"])
+def test_gemm_bitlinear_workload_sampled(mode):
+    W, packed, scale = ref_pack("bitlinear", 0, mode)
+    X, q, sx, sxe = ref_quant("bitlinear")
+    N, K = W.shape
+    cols = _sample_cols(N, 5, 160)
+    say(f"gemm bitlinear {mode} {q.shape} x {W.shape}")
+    _check_outputs(tq.tq_ternary_gemm, dev(q), dev(sx), dev(packed), dev(scale), N, K,
+                   "row", q, packed, scale, sx, cols=cols)
+
+
+# ------------------------------------------------------------- whole layer
+
+@pytest.mark.parametrize("name,j,b", [("tiny", 0, 4), ("decode", 0, 1), ("ffn", 0, 16),
+                                      ("ffn", 1, 4)])
+def test_end_to_end_decode(name, j, b):
+    """pack -> quant -> GEMV all on the device, every intermediate checked."""
+    W, packed_ref, scale_ref = ref_pack(name, j)
+    X, q_ref, sx_ref, _ = ref_quant(name, j, b)
+    cfg = ti.WORKLOADS[name]
+    N, K = W.shape
+    say(f"end-to-end {name}[{j}] b={b}")
+    packed, scale = tq.tq_pack_ternary(dev(W), cfg["gran"])
+    q, sx = tq.tq_quant_act_int8(x_to_device(X, cfg["x_dtype"]))
+    y = tq.tq_ternary_gemv(q, sx, packed, scale, N, K, cfg["gran"], "f32")
+    np.testing.assert_array_equal(host(packed), packed_ref)
+    np.testing.assert_array_equal(host(q), q_ref)
+    acc_ref, y_ref = _contract_ref(q_ref, packed_ref, K, scale_ref, sx_ref)
+    assert_y_close(host(y), y_ref)
+
+
+def test_end_to_end_bitlinear_binary_and_ternary():
+    X, q_ref, sx_ref, sxe = ref_quant("bitlinear")
+    say("end-to-end bitlinear")
+    q, sx = tq.tq_quant_act_int8(dev_bf16(X), clamp=(0.05, 40.0), rmsnorm=True, fwht_block=512)
+    np.testing.assert_array_equal(host(q), q_ref)
+    for mode in ("ternary", "binary"):
+        W, packed_ref, scale_ref = ref_pack("bitlinear", 0, mode)
+        N, K = W.shape
+        packed, scale = tq.tq_pack_ternary(dev(W), "row", mode)
+        y = host(tq.tq_ternary_gemm(q, sx, packed, scale, N, K, "row", "f32"))
+        cols = _sample_cols(N, 6, 64)
+        acc_ref = oracle.contract_rows(q_ref, packed_ref, K, cols)
+        y_ref = oracle.epilogue(acc_ref, scale_ref, sxe, rows=cols)
+        err = np.abs(y[:, cols] - y_ref)
+        assert np.all(err <= 3e-6 * np.abs(y_ref) + 0), "bitlinear output off"

@@ -518,3 +518,32 @@ def test_whole_layer_tiny_matches_gemv_emulation():
             assert acc == r["acc"][m, o]
             y = float(acc) * float(r["scale"][0]) * float(r["sx"][m])
             assert abs(y - r["y"][m, o]) <= 1e-12 * max(1.0, abs(y))
+
+
+def test_prologue_off_reduces_to_plain_quantiser():
+    X = ti.activations(91, 6, 1024, dtype="f32")
+    X[2] = 0
+    q0, s0 = oracle.quant_act_int8(X)
+    q1, s1, _, _ = oracle.rmsnorm_fwht_quant(X, eta_min=None, eta_max=None,
+                                             rmsnorm=False, fwht=False)
+    np.testing.assert_array_equal(q0[[0, 1, 3, 4, 5]], q1[[0, 1, 3, 4, 5]])
+    np.testing.assert_array_equal(s0[[0, 1, 3, 4, 5]], s1[[0, 1, 3, 4, 5]])
+    assert not q1[2].any()
+    # with the clamp the bound branch is the plain clamped quantiser as well
+    q2, s2 = oracle.quant_act_int8(X * 100, eta_min=0.05, eta_max=40.0)
+    q3, s3, _, b3 = oracle.rmsnorm_fwht_quant(X * 100, rmsnorm=False, fwht=False)
+    assert b3.all()
+    np.testing.assert_array_equal(q2, q3)
+    np.testing.assert_array_equal(s2, s3)
+
+
+def test_prologue_rmsnorm_only_codes_equal_plain():
+    # RMSNorm alone multiplies each token by a positive factor: same codes
+    X = ti.activations(92, 8, 640)
+    q0, _ = oracle.quant_act_int8(X)
+    q1, _, sxe, b = oracle.rmsnorm_fwht_quant(X, eta_min=None, eta_max=None, fwht=False)
+    assert not b.any()
+    np.testing.assert_array_equal(q0, q1)
+    x64 = X.astype(np.float64)
+    r = 1 / np.sqrt(np.mean(x64 * x64, axis=1) + 1e-6)
+    np.testing.assert_allclose(sxe, r * np.max(np.abs(x64), axis=1) / 127, rtol=1e-12)
