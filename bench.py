@@ -1,0 +1,333 @@
+"""Benchmark of the ternary linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Workload (the headline): decode GEMV, W 4096x4096 ternary from N(0, 0.02)
+fp32 (per-tensor absmean scale, packed 4 MiB), one bf16 token ~N(0, 1)
+quantised per token to int8, fp32 output.  One step = per-token int8
+quantisation of the token + the packed-weight GEMV with its fused scale
+epilogue.  Steps rotate over 128 distinct packed-weight buffers (512 MiB,
+more than twice the 256 MB Infinity Cache) so that the weight stream comes
+from HBM, as it does when a decode pass walks through a model's layers.
+Inputs are resident in HBM before timing starts.  Launches are captured in a
+HIP graph (torch.cuda.CUDAGraph) so that the host never paces the GPU.
+
+Prints one JSON line.  ``value`` is algorithmic bytes of the step over its
+time (GB/s).  ``roofline`` describes the GEMV kernel: its algorithmic bytes
+per launch over its average launch time, against 8 TB/s.  ``cpu_baseline``
+times the CPU oracle on a bounded sample of the same workload.  ``extra``
+carries the prefill GEMM (int8 MFMA TOPS), the BitLinear prologue, the FFN
+decode shapes and the pack kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
+POOL = 128                     # distinct packed weights in the rotation
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2048)
+    p.add_argument("--warmup", type=int, default=256)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--only", default="",
+                   help="comma list of extra workloads to run: prefill,bitlinear,pack,ffn")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="also run a plain 256 MiB device copy (for counter scaling)")
+    return p.parse_args()
+
+
+def gemv_bytes(M, N, K, per_row):
+    # packed W + scale(s) + int8 tokens + sx + fp32 output
+    return N * K // 4 + (4 * N if per_row else 4) + M * K + 4 * M + 4 * M * N
+
+
+def quant_bytes(M, K, xbytes):
+    return M * K * xbytes + M * K + 4 * M
+
+
+def timed_graph(torch, graph, reps):
+    """Replay `graph` reps times between synchronisations; seconds per replay."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        graph.replay()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / 1e3 / reps
+
+
+def capture(torch, fn):
+    g = torch.cuda.CUDAGraph()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        fn()                                   # warm the path once outside capture
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import tq_inputs as ti
+    from ternary_quantized_linear_absmean_amd import tq
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ------------------------------------------------------------ decode
+    N, K = ti.WORKLOADS["decode"]["mats"][0]
+    W = torch.from_numpy(ti.workload_weights("decode")).to(dev)
+    X = torch.from_numpy(ti.workload_activations("decode")).to(dev).to(torch.bfloat16)
+    packed0, scale = tq.tq_pack_ternary(W, "tensor")
+    pool = [packed0.clone() for _ in range(POOL)]
+    del W
+    qbuf = torch.empty((1, K), dtype=torch.int8, device=dev)
+    sxbuf = torch.empty((1,), dtype=torch.float32, device=dev)
+    ybuf = torch.empty((1, N), dtype=torch.float32, device=dev)
+
+    def decode_pass():
+        # one decode step = per-token int8 quantisation + GEMV + scale epilogue
+        for p in pool:
+            tq.tq_quant_ternary_gemv(X, p, scale, N, K, "tensor", "f32", q=qbuf, sx=sxbuf,
+                                     Y=ybuf)
+
+    def decode_pass_two_calls():
+        for p in pool:
+            tq.tq_quant_act_int8(X, q=qbuf, sx=sxbuf)
+            tq.tq_ternary_gemv(qbuf, sxbuf, p, scale, N, K, "tensor", "f32", Y=ybuf)
+
+    def gemv_pass():
+        for p in pool:
+            tq.tq_ternary_gemv(qbuf, sxbuf, p, scale, N, K, "tensor", "f32", Y=ybuf)
+
+    g_step = capture(torch, decode_pass)
+    g_gemv = capture(torch, gemv_pass)
+    g_two = capture(torch, decode_pass_two_calls)
+    reps_w = max(1, args.warmup // POOL)
+    reps = max(1, args.steps // POOL)
+    steps = reps * POOL
+    timed_graph(torch, g_step, reps_w)
+    timed_graph(torch, g_gemv, reps_w)
+
+    # timed region: exactly `steps` steps between synchronisations
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    sec_per_pass = timed_graph(torch, g_step, reps)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_s = sec_per_pass / POOL
+    b_gemv = gemv_bytes(1, N, K, False)
+    b_step = b_gemv + quant_bytes(1, K, 2)
+    value = b_step / step_s / 1e9
+
+    gemv_s = timed_graph(torch, g_gemv, reps) / POOL
+    gemv_gbs = b_gemv / gemv_s / 1e9
+    two_s = timed_graph(torch, g_two, reps) / POOL
+
+    result = {
+        "metric": "ternary GEMV GB/s (% HBM peak) at K=N=4096 b=1; GEMM TOPS (% int8 MFMA peak)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": reps_w * POOL,
+        "ms_per_step": round(step_s * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 x ternary -> int32 acc, fp32 epilogue",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) bf16 token)",
+        "config": {"workload": "decode GEMV: bf16 token 1x4096 -> per-token int8, "
+                               "packed ternary W 4096x4096 (per-tensor absmean), fp32 out; "
+                               f"{POOL} distinct weight buffers in rotation",
+                   "M": 1, "N": N, "K": K, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "entry_point": "tq_quant_ternary_gemv (quantise + GEMV, one launch)",
+                   "two_call_step_us": round(two_s * 1e6, 3),
+                   "timed_wall_s": round(wall, 4)},
+        "roofline": {"bound": "hbm", "kernel": "k_gemv", "achieved": round(gemv_gbs, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gemv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": b_gemv, "avg_launch_us": round(gemv_s * 1e6, 3)},
+    }
+
+    if not args.no_extra:
+        only = set(x for x in args.only.split(",") if x)
+        result["extra"] = extras(torch, np, ti, tq, dev, only)
+    if args.copy_calibration:
+        result["copy_calibration"] = copy_calibration(torch, dev)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(np, ti, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def extras(torch, np, ti, tq, dev, only=frozenset()):
+    out = {}
+    want = (lambda name: not only or name in only)
+    if want("prefill") or want("pack"):
+        out.update(extra_prefill(torch, ti, tq, dev, want))
+    if want("bitlinear"):
+        out.update(extra_bitlinear(torch, ti, tq, dev))
+    if want("ffn"):
+        out.update(extra_ffn(torch, ti, tq, dev))
+    torch.cuda.synchronize()
+    return out
+
+
+def extra_prefill(torch, ti, tq, dev, want):
+    out = {}
+    # prefill GEMM 2048 x 11008 x 4096 -> bf16, int8 MFMA
+    M = 2048
+    N, K = ti.WORKLOADS["prefill"]["mats"][0]
+    W = torch.from_numpy(ti.workload_weights("prefill")).to(dev)
+    packed, scale = tq.tq_pack_ternary(W, "tensor")
+    X = torch.from_numpy(ti.workload_activations("prefill")).to(dev).to(torch.bfloat16)
+    q, sx = tq.tq_quant_act_int8(X)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    reps = 8
+    if want("prefill"):
+        g = capture(torch, lambda: [tq.tq_ternary_gemm(q, sx, packed, scale, N, K, "tensor",
+                                                       "bf16", Y=Y) for _ in range(reps)])
+        timed_graph(torch, g, 2)
+        t = timed_graph(torch, g, 5) / reps
+        tops = 2.0 * M * N * K / t / 1e12
+        out["prefill_gemm"] = {"shape": [M, N, K], "out": "bf16", "us": round(t * 1e6, 2),
+                               "TOPS": round(tops, 1),
+                               "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)}
+        qx = torch.empty_like(q)
+        sxx = torch.empty_like(sx)
+        g = capture(torch, lambda: [tq.tq_quant_act_int8(X, q=qx, sx=sxx) for _ in range(reps)])
+        t = timed_graph(torch, g, 5) / reps
+        out["prefill_quant"] = {"shape": [M, K], "us": round(t * 1e6, 2),
+                                "GBs": round(quant_bytes(M, K, 2) / t / 1e9, 1)}
+    if want("pack"):
+        # pack of the prefill weight (per-tensor: reduce + pack passes)
+        pk = torch.empty_like(packed)
+        sc = torch.empty_like(scale)
+        ws = torch.empty((tq.tq_pack_workspace_bytes(N, K, "tensor"),), dtype=torch.uint8,
+                         device=dev)
+        g = capture(torch, lambda: tq.tq_pack_ternary(W, "tensor", packed=pk, scale=sc,
+                                                      workspace=ws))
+        t = timed_graph(torch, g, 10)
+        out["pack_tensor"] = {"shape": [N, K], "us": round(t * 1e6, 2),
+                              "GBs": round((4 * N * K + N * K // 4) / t / 1e9, 1)}
+    return out
+
+
+def extra_bitlinear(torch, ti, tq, dev):
+    out = {}
+    reps = 8
+    # BitLinear: prologue (RMSNorm + FWHT-512 + int8) and GEMM 512 x 4096 x 4096, fp32 out
+    Wb = torch.from_numpy(ti.workload_weights("bitlinear")).to(dev)
+    Xb = torch.from_numpy(ti.workload_activations("bitlinear")).to(dev).to(torch.bfloat16)
+    pb, sb = tq.tq_pack_ternary(Wb, "row")
+    qb = torch.empty((512, 4096), dtype=torch.int8, device=dev)
+    sxb = torch.empty((512,), dtype=torch.float32, device=dev)
+    Yb = torch.empty((512, 4096), dtype=torch.float32, device=dev)
+    g = capture(torch, lambda: [tq.tq_quant_act_int8(Xb, clamp=(0.05, 40.0), rmsnorm=True,
+                                                     fwht_block=512, q=qb, sx=sxb)
+                                for _ in range(reps)])
+    t = timed_graph(torch, g, 5) / reps
+    out["bitlinear_prologue"] = {"shape": [512, 4096], "us": round(t * 1e6, 2),
+                                 "GBs": round(quant_bytes(512, 4096, 2) / t / 1e9, 1)}
+    g = capture(torch, lambda: [tq.tq_ternary_gemm(qb, sxb, pb, sb, 4096, 4096, "row", "f32",
+                                                   Y=Yb) for _ in range(reps)])
+    t = timed_graph(torch, g, 5) / reps
+    tops = 2.0 * 512 * 4096 * 4096 / t / 1e12
+    out["bitlinear_gemm"] = {"shape": [512, 4096, 4096], "us": round(t * 1e6, 2),
+                             "TOPS": round(tops, 1),
+                             "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)}
+    return out
+
+
+def extra_ffn(torch, ti, tq, dev):
+    out = {}
+    # FFN decode shapes (per-row scales), GEMV rotation over 64 buffers each
+    ffn = {}
+    for j, (N, K) in enumerate(ti.WORKLOADS["ffn"]["mats"]):
+        W = torch.from_numpy(ti.workload_weights("ffn", j)).to(dev)
+        p0, s0 = tq.tq_pack_ternary(W, "row")
+        del W
+        pool = [p0.clone() for _ in range(64)]
+        for b in ti.WORKLOADS["ffn"]["batches"]:
+            Xf = torch.from_numpy(ti.workload_activations("ffn", j, b)).to(dev).to(torch.bfloat16)
+            qf, sf = tq.tq_quant_act_int8(Xf)
+            Yf = torch.empty((b, N), dtype=torch.float32, device=dev)
+            g = capture(torch, lambda: [tq.tq_ternary_gemv(qf, sf, p, s0, N, K, "row", "f32",
+                                                           Y=Yf) for p in pool])
+            timed_graph(torch, g, 2)
+            t = timed_graph(torch, g, 10) / len(pool)
+            gb = gemv_bytes(b, N, K, True) / t / 1e9
+            ffn[f"{'up' if j == 0 else 'down'}_{N}x{K}_b{b}"] = {
+                "us": round(t * 1e6, 3), "GBs": round(gb, 1),
+                "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1)}
+        del pool
+    out["ffn_gemv"] = ffn
+    return out
+
+
+def copy_calibration(torch, dev):
+    n = 256 << 20
+    a = torch.empty(n, dtype=torch.uint8, device=dev)
+    b = torch.empty(n, dtype=torch.uint8, device=dev)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    return {"bytes_read": n, "bytes_written": n, "launches": 3}
+
+
+def cpu_baseline(np, ti, seconds):
+    """The oracle on the host: per-token quantisation + integer contraction
+    + fp64 epilogue for the decode workload, repeated for ~`seconds`."""
+    import oracle
+    N, K = ti.WORKLOADS["decode"]["mats"][0]
+    W = ti.workload_weights("decode")
+    X = ti.workload_activations("decode")
+    packed, scale = oracle.pack_ternary(W, "tensor")
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        q, sx = oracle.quant_act_int8(X)
+        acc = oracle.contract(q, packed, K)
+        oracle.epilogue(acc, scale, sx)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    per = el / n
+    b = gemv_bytes(1, N, K, False) + quant_bytes(1, K, 2)
+    return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} decode steps (quant + contraction + epilogue, 1x4096x4096) in "
+                      f"{el:.1f} s, numpy int64 on one host thread",
+            "ms_per_step": round(per * 1e3, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -134,7 +134,7 @@ tq_status tq_pack_ternary(const float* W, int64_t N, int64_t K, tq_gran g,
  *   m = fp32(fp32(r*c) * fp32(127/eta_eff)) and sx = fp32(eta_eff/127).
  *   q is bit-exact given r; sx is exact to fp32 rounding of r.
  * Errors: NULL pointers, M < 0, K <= 0, K % 512 != 0 with FWHT, fwht_block
- * not 0 or 512, xdt not F32/BF16, K > 65536 with a prologue (UNSUPPORTED). */
+ * not 0 or 512, xdt not F32/BF16, K > 32768 with a prologue (UNSUPPORTED). */
 tq_status tq_quant_act_int8(const void* X, tq_dtype xdt, int64_t M, int64_t K,
                             const tq_act_opts* opts, int8_t* q, float* sx,
                             hipStream_t stream);
@@ -173,6 +173,24 @@ tq_status tq_ternary_gemm(const int8_t* q, const float* sx, int64_t M,
                           const uint8_t* packed, const float* scale, tq_gran g,
                           int64_t N, int64_t K, void* Y, tq_dtype ydt,
                           hipStream_t stream);
+
+/* Decode step in one call: per-token int8 quantisation of X followed by the
+ * decode GEMV (Hetman-2b s.5 BitLinear: quantise, integer contraction, scale
+ * fusion; s.7 GEMV).  The results -- q, sx and Y -- are bit for bit those of
+ * tq_quant_act_int8(X, xdt, M, K, opts, q, sx) followed by
+ * tq_ternary_gemv(q, sx, M, packed, scale, g, N, K, Y, ydt).
+ * With the plain quantiser (no RMSNorm / FWHT), M <= 4, K % 64 == 0,
+ * M*K <= 65536 and 16-byte aligned X and packed, this is a single kernel
+ * launch: every workgroup quantises the tokens itself into LDS and
+ * workgroup 0 writes q and sx; otherwise it is the two launches.
+ *   X [M, K] fp32/bf16; q [M, K] int8 and sx [M] fp32 are outputs (required);
+ *   packed, scale, g, N, K, Y, ydt as for tq_ternary_gemv.
+ * Errors: those of the two calls; M > 16 is TQ_ERR_SHAPE. */
+tq_status tq_quant_ternary_gemv(const void* X, tq_dtype xdt, int64_t M,
+                                const tq_act_opts* opts, const uint8_t* packed,
+                                const float* scale, tq_gran g, int64_t N, int64_t K,
+                                int8_t* q, float* sx, void* Y, tq_dtype ydt,
+                                hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* tq_status_str(tq_status s);

@@ -9,6 +9,7 @@ from __future__ import annotations
 
 __all__ = ["tq_packed_bytes", "tq_pack_workspace_bytes", "tq_pack_ternary",
            "tq_quant_act_int8", "tq_fwht512", "tq_ternary_gemv", "tq_ternary_gemm",
+           "tq_quant_ternary_gemv",
            "tq_status_str", "tq_last_hip_error", "tq_version", "TqError"]
 
 

@@ -8,15 +8,22 @@
 // unpack-in-the-K-loop GEMM loses: the dot product running off the matrix
 // units and every packed byte being re-read for each of its values.  Here
 // each packed word is read from global memory once per workgroup tile,
-// decoded once into signed int8 in LDS, and every wave then feeds LDS
-// fragments to v_mfma_i32_32x32x32_i8.
+// decoded once into signed int8 in LDS, and fed to v_mfma_i32_32x32x32_i8.
 //
-// Tile: BM x BN outputs per workgroup, BK = 64 per stage, double-buffered
-// LDS (rows padded to 80 bytes so that 128-bit fragment reads from 8
-// consecutive rows touch disjoint banks).  Global loads of stage k+1 are in
-// flight while stage k is contracted.  The epilogue applies
-// y = acc * gamma * sx in fp32 and writes fp32, bf16 (round to nearest even)
-// or the raw int32 accumulator.
+// gfx950 mapping.  A workgroup computes a BM x BN tile with WM x WN waves.
+// Each wave owns TM = BM/WM rows of the token matrix: its int8 activation
+// fragments go straight from global memory into MFMA registers (16 bytes
+// per lane per fragment), prefetched two K-stages ahead, with no LDS round
+// trip.  The packed weight tile (BN rows x 16 bytes per 64-wide stage) is
+// loaded once per workgroup, decoded to signed int8 and written to a
+// double-buffered LDS tile (rows padded to 80 bytes so that 128-bit reads of
+// eight consecutive rows touch disjoint banks); every wave reads its weight
+// fragments from there.  Launch bounds allow two workgroups per CU, so one
+// can compute while the other waits on memory.  Workgroup ids are mapped so
+// that the workgroups resident on one XCD (ids congruent mod 8) share weight
+// columns in that XCD's L2.  The epilogue applies y = acc * gamma * sx in
+// fp32 and writes fp32, bf16 (round to nearest even) or the raw int32
+// accumulator.
 
 #include "tq_device.hpp"
 #include "tq_internal.hpp"
@@ -26,14 +33,23 @@ namespace {
 
 constexpr int kBK = 64;
 constexpr int kLD = kBK + 16;  // LDS row stride in bytes
+constexpr int kXcds = 8;
 
 template <bool ALIGNED>
-__device__ inline uint4 load_a_chunk(const uint8_t* row, int64_t k, int64_t K, bool ok) {
+__device__ inline v4i load_a_frag(const uint8_t* row, int64_t k, int64_t K, bool ok) {
   if (ALIGNED) {
-    if (ok && k < K) return *reinterpret_cast<const uint4*>(row + k);
-    return make_uint4(0u, 0u, 0u, 0u);
+    if (ok && k < K) {
+      const uint4 u = *reinterpret_cast<const uint4*>(row + k);
+      v4i a;
+      a.x = static_cast<int>(u.x);
+      a.y = static_cast<int>(u.y);
+      a.z = static_cast<int>(u.z);
+      a.w = static_cast<int>(u.w);
+      return a;
+    }
+    return v4i{0, 0, 0, 0};
   }
-  uint32_t w[4];
+  int w[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     uint32_t v = 0u;
@@ -42,9 +58,9 @@ __device__ inline uint4 load_a_chunk(const uint8_t* row, int64_t k, int64_t K, b
       const int64_t kk = k + 4 * i + b;
       v |= static_cast<uint32_t>((ok && kk < K) ? row[kk] : 0u) << (8 * b);
     }
-    w[i] = v;
+    w[i] = static_cast<int>(v);
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return v4i{w[0], w[1], w[2], w[3]};
 }
 
 // one packed word (16 codes) at byte offset `kb` of a row with `rowbytes`
@@ -66,17 +82,15 @@ __device__ inline uint32_t load_b_word(const uint8_t* row, int64_t kb, int64_t r
 }
 
 template <int BM, int BN, int WM, int WN, bool ALIGNED, int YT>
-__global__ __launch_bounds__(WM* WN* kWave) void k_gemm(
+__global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
     int64_t N, int64_t K, void* __restrict__ Y) {
   constexpr int NT = WM * WN * kWave;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int CA = BM * 4 / NT;   // 16-byte A chunks per thread per stage
-  constexpr int CB = BN * 4 / NT;   // packed B words per thread per stage
-  static_assert(CA >= 1 && CB >= 1, "tile too small for the thread count");
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * kLD];
+  constexpr int CB = BN * 4 / NT;  // packed words per thread per stage
+  static_assert(CB >= 1 && FM >= 1 && FN >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * kLD];
 
   const int tid = threadIdx.x;
@@ -84,48 +98,58 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(
   const int wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
   const int64_t tiles_m = (M + BM - 1) / BM;
-  const int64_t tm = blockIdx.x % tiles_m;
-  const int64_t tn = blockIdx.x / tiles_m;
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  // ids congruent mod 8 run on one XCD: give them neighbouring weight columns
+  const int64_t bid = blockIdx.x;
+  const int64_t local = bid / kXcds;
+  const int64_t tm = local % tiles_m;
+  const int64_t tn = (local / tiles_m) * kXcds + bid % kXcds;
+  if (tn >= tiles_n) return;  // padding ids (whole workgroup)
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t rowbytes = K >> 2;
-  const uint8_t* qb = reinterpret_cast<const uint8_t*>(q);
+  const int fr = lane & 31, kg = lane >> 5;
 
-  uint4 ra[CA];
-  uint32_t rb[CB];
-
-  auto load_stage = [&](int64_t kt) {
+  // activation rows of this lane's fragments
+  const uint8_t* arow[FM];
+  bool aok[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const int64_t m = m0 + wm * TM + 32 * i + fr;
+    aok[i] = m < M;
+    arow[i] = reinterpret_cast<const uint8_t*>(q) + (aok[i] ? m : 0) * K;
+  }
+  // A fragments of a stage: [i][ks] for the two 32-wide K steps.  Three
+  // register sets rotate (current stage, and two stages in flight); the loop
+  // is unrolled by three so that every set is addressed statically.
+  typedef v4i AFrags[FM][2];
+  AFrags ra0, ra1, ra2;
+  auto load_a = [&](int64_t kt, AFrags& dst) {
     const int64_t k0 = kt * kBK;
 #pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + NT * i;
-      const int r = c >> 2, cc = c & 3;
-      const int64_t m = m0 + r;
-      const bool ok = m < M;
-      ra[i] = load_a_chunk<ALIGNED>(qb + (ok ? m : 0) * K, k0 + 16 * cc, K, ok);
-    }
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        dst[i][ks] = load_a_frag<ALIGNED>(arow[i], k0 + 32 * ks + 16 * kg, K, aok[i]);
+  };
+  uint32_t rb[CB];
+  auto load_b = [&](int64_t kt) {
+    const int64_t kb0 = kt * (kBK / 4);
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       const int c = tid + NT * i;
       const int r = c >> 2, wi = c & 3;
       const int64_t n = n0 + r;
       const bool ok = n < N;
-      rb[i] = load_b_word<ALIGNED>(packed + (ok ? n : 0) * rowbytes, k0 / 4 + 4 * wi,
-                                   rowbytes, ok);
+      rb[i] = load_b_word<ALIGNED>(packed + (ok ? n : 0) * rowbytes, kb0 + 4 * wi, rowbytes,
+                                   ok);
     }
   };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < CA; ++i) {
-      const int c = tid + NT * i;
-      const int r = c >> 2, cc = c & 3;
-      *reinterpret_cast<uint4*>(&As[buf][r * kLD + 16 * cc]) = ra[i];
-    }
+  auto store_b = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CB; ++i) {
       const int c = tid + NT * i;
       const int r = c >> 2, wi = c & 3;
-      const v4i d = decode_signed_natural(rb[i]);
-      *reinterpret_cast<v4i*>(&Bs[buf][r * kLD + 16 * wi]) = d;
+      *reinterpret_cast<v4i*>(&Bs[buf][r * kLD + 16 * wi]) = decode_signed_natural(rb[i]);
     }
   };
 
@@ -138,32 +162,38 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
   const int64_t nk = (K + kBK - 1) / kBK;
-  load_stage(0);
-  store_stage(0);
-  __syncthreads();
-  const int fr = lane & 31, kg = lane >> 5;
-  for (int64_t kt = 0; kt < nk; ++kt) {
+  // one K stage: prefetch A two stages ahead and B one stage ahead, contract
+  // the current stage, then publish the next B tile
+  auto stage = [&](int64_t kt, AFrags& cur, AFrags& ahead) {
     const int buf = static_cast<int>(kt & 1);
-    if (kt + 1 < nk) load_stage(kt + 1);
+    if (kt + 2 < nk) load_a(kt + 2, ahead);
+    if (kt + 1 < nk) load_b(kt + 1);
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 32) {
-      v4i a[FM], b[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        a[i] = *reinterpret_cast<const v4i*>(
-            &As[buf][(wm * TM + 32 * i + fr) * kLD + kk + 16 * kg]);
+    for (int ks = 0; ks < 2; ++ks) {
+      v4i b[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
         b[j] = *reinterpret_cast<const v4i*>(
-            &Bs[buf][(wn * TN + 32 * j + fr) * kLD + kk + 16 * kg]);
+            &Bs[buf][(wn * TN + 32 * j + fr) * kLD + 32 * ks + 16 * kg]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(cur[i][ks], b[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) store_stage(buf ^ 1);
+    if (kt + 1 < nk) store_b(buf ^ 1);
     __syncthreads();
+  };
+
+  load_a(0, ra0);
+  if (nk > 1) load_a(1, ra1);
+  load_b(0);
+  store_b(0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; kt += 3) {
+    stage(kt, ra0, ra2);
+    if (kt + 1 < nk) stage(kt + 1, ra1, ra0);
+    if (kt + 2 < nk) stage(kt + 2, ra2, ra1);
   }
 
   // D layout of the 32x32 MFMA: lane l holds column l%32 and rows
@@ -195,12 +225,226 @@ __global__ __launch_bounds__(WM* WN* kWave) void k_gemm(
   }
 }
 
+// ------------------------------------------------------------------------
+// Fast path (K % 64 == 0, 16-byte aligned operands, both operands below
+// 2 GiB).  Both operand tiles pass through LDS:
+//   - activations: every 16-byte load of a stage covers 16 rows x 64
+//     contiguous bytes (four lanes per row), the widest pattern a 64-wide
+//     stage allows; an MFMA fragment loaded straight from global memory
+//     would touch 32 rows (32 cache lines) per instruction, and on gfx950
+//     the address path is limited by lines per instruction, not bytes;
+//   - packed weights: one 32-bit word (16 codes) per lane, decoded to signed
+//     int8 once per workgroup.
+// Global loads are raw buffer loads whose per-lane offset is fixed for the
+// K loop and whose K position rides in the scalar offset (no address
+// arithmetic in the loop; reads past the end return zero).  Loads run two
+// stages ahead in registers; each stage stores the next stage's tiles into
+// the other half of a double-buffered LDS tile.  LDS rows are 64 bytes with
+// the four 16-byte chunks XOR-swizzled by ((row >> 1) ^ (row >> 3)) & 3, so
+// the 16-byte stores and the fragment reads of 16 consecutive rows are free
+// of bank conflicts.  Fragment reads for the next 32-wide K step are issued
+// before the MFMAs of the current one.
+
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kKS = kBK / 32;          // MFMA K steps per stage
+
+__device__ inline int swz(int row, int chunk) {
+  return row * kBK + 16 * (chunk ^ (((row >> 1) ^ (row >> 3)) & 3));
+}
+
+template <int BM, int BN, int WM, int WN, int YT>
+__global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm_fast(
+    const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
+    const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
+    int64_t N, int64_t K, void* __restrict__ Y) {
+  constexpr int NT = WM * WN * kWave;
+  constexpr int TM = BM / WM, TN = BN / WN;
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int CA = BM * (kBK / 16) / NT;  // 16-byte activation chunks per thread
+  constexpr int CB = BN * (kBK / 16) / NT;  // packed words per thread
+  static_assert(CA >= 1 && CB >= 1 && FM >= 1 && FN >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * kBK];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * kBK];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave / WN, wn = wave % WN;
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  const int64_t tm = blockIdx.x % tiles_m;
+  const int64_t tn = blockIdx.x / tiles_m;
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int64_t rowbytes = K >> 2;
+  const int fr = lane & 31, kg = lane >> 5;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(q), static_cast<short>(0), static_cast<int>(M * K), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed), static_cast<short>(0), static_cast<int>(N * rowbytes),
+      kBufFlags);
+  // per-thread global offsets and LDS slots, fixed for the K loop
+  uint32_t aoff[CA];
+  int ast[CA];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) {
+    const int c = tid + NT * i;
+    const int r = c / (kBK / 16), ch = c % (kBK / 16);
+    aoff[i] = static_cast<uint32_t>((m0 + r) * K + 16 * ch);
+    ast[i] = swz(r, ch);
+  }
+  uint32_t boff[CB];
+  int bst[CB];
+#pragma unroll
+  for (int i = 0; i < CB; ++i) {
+    const int c = tid + NT * i;
+    const int r = c / (kBK / 16), wi = c % (kBK / 16);
+    boff[i] = static_cast<uint32_t>((n0 + r) * rowbytes + 4 * wi);
+    bst[i] = swz(r, wi);
+  }
+  int ard[FM][kKS], brd[FN][kKS];
+#pragma unroll
+  for (int ks = 0; ks < kKS; ++ks) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) ard[i][ks] = swz(wm * TM + 32 * i + fr, 2 * ks + kg);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) brd[j][ks] = swz(wn * TN + 32 * j + fr, 2 * ks + kg);
+  }
+
+  typedef v4i ARegs[CA];
+  typedef uint32_t BRegs[CB];
+  ARegs ra0, ra1, ra2;
+  BRegs rb0, rb1, rb2;
+  auto load_stage = [&](int64_t kt, ARegs& a, BRegs& b) {
+    const int soa = static_cast<int>(kt * kBK), sob = static_cast<int>(kt * (kBK / 4));
+#pragma unroll
+    for (int i = 0; i < CA; ++i)
+      a[i] = __builtin_bit_cast(v4i,
+                                __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff[i], soa, 0));
+#pragma unroll
+    for (int i = 0; i < CB; ++i) b[i] = __builtin_amdgcn_raw_buffer_load_b32(rb_rsrc, boff[i], sob, 0);
+  };
+  auto store_stage = [&](int buf, ARegs& a, BRegs& b) {
+#pragma unroll
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<v4i*>(&As[buf][ast[i]]) = a[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      *reinterpret_cast<v4i*>(&Bs[buf][bst[i]]) = decode_signed_natural(b[i]);
+  };
+
+  v16i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+  const int64_t nk = K / kBK;
+  // one stage: start the loads of stage kt+2, contract stage kt from LDS,
+  // publish stage kt+1 (loaded during the previous stage)
+  auto stage = [&](int64_t kt, ARegs& a_next, BRegs& b_next, ARegs& a_far, BRegs& b_far) {
+    const int buf = static_cast<int>(kt & 1);
+    if (kt + 2 < nk) load_stage(kt + 2, a_far, b_far);
+    v4i ac[FM], an[FM], bc[FN], bn[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) ac[i] = *reinterpret_cast<const v4i*>(&As[buf][ard[i][0]]);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bc[j] = *reinterpret_cast<const v4i*>(&Bs[buf][brd[j][0]]);
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      if (ks + 1 < kKS) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          an[i] = *reinterpret_cast<const v4i*>(&As[buf][ard[i][ks + 1]]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bn[j] = *reinterpret_cast<const v4i*>(&Bs[buf][brd[j][ks + 1]]);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ac[i], bc[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) ac[i] = an[i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bc[j] = bn[j];
+    }
+    if (kt + 1 < nk) store_stage(buf ^ 1, a_next, b_next);
+    __syncthreads();
+  };
+
+  load_stage(0, ra0, rb0);
+  if (nk > 1) load_stage(1, ra1, rb1);
+  store_stage(0, ra0, rb0);
+  __syncthreads();
+  // register sets rotate with period three: stage kt reads set (kt+1)%3 and
+  // fills set (kt+2)%3
+  for (int64_t kt = 0; kt < nk; kt += 3) {
+    stage(kt, ra1, rb1, ra2, rb2);
+    if (kt + 1 < nk) stage(kt + 1, ra2, rb2, ra0, rb0);
+    if (kt + 2 < nk) stage(kt + 2, ra0, rb0, ra1, rb1);
+  }
+
+  // D layout of the 32x32 MFMA: lane l holds column l%32 and rows
+  // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t n = n0 + wn * TN + 32 * j + fr;
+    if (n >= N) continue;
+    const float gam = YT == TQ_I32 ? 0.f : scale[per_row ? n : 0];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = m0 + wm * TM + 32 * i + 8 * (v / 4) + 4 * kg + (v % 4);
+        if (m >= M) continue;
+        const int64_t o = m * N + n;
+        const int accv = acc[i][j][v];
+        if (YT == TQ_I32) {
+          static_cast<int*>(Y)[o] = accv;
+        } else {
+          const float y = static_cast<float>(accv) * (gam * sx[m]);
+          if (YT == TQ_F32)
+            static_cast<float*>(Y)[o] = y;
+          else
+            static_cast<uint16_t*>(Y)[o] = f32_to_bf16(y);
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t gemm_fast_launch(const GemmArgs& a, hipStream_t s) {
+  const int64_t grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  constexpr int NT = WM * WN * kWave;
+#define TQ_GEMM_FAST(YTV)                                                                  \
+  hipLaunchKernelGGL((k_gemm_fast<BM, BN, WM, WN, YTV>), dim3(grid), dim3(NT), 0, s, a.q, \
+                     a.sx, a.M, a.packed, a.scale, a.per_row, a.N, a.K, a.Y)
+  if (a.ydt == TQ_F32) TQ_GEMM_FAST(TQ_F32);
+  else if (a.ydt == TQ_BF16) TQ_GEMM_FAST(TQ_BF16);
+  else TQ_GEMM_FAST(TQ_I32);
+#undef TQ_GEMM_FAST
+  return hipGetLastError();
+}
+
+hipError_t gemm_fast_dispatch(const GemmArgs& a, hipStream_t s) {
+  auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
+  constexpr int64_t kEnough = 384;
+  if (tiles(256, 128) >= kEnough) return gemm_fast_launch<256, 128, 2, 2>(a, s);
+  if (tiles(128, 128) >= kEnough) return gemm_fast_launch<128, 128, 2, 2>(a, s);
+  return gemm_fast_launch<128, 64, 4, 1>(a, s);
+}
+
 template <int BM, int BN, int WM, int WN, bool ALIGNED>
 hipError_t gemm_launch(const GemmArgs& a, hipStream_t s) {
-  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int64_t tiles_m = (a.M + BM - 1) / BM;
+  const int64_t tiles_n = (a.N + BN - 1) / BN;
+  const int64_t grid = tiles_m * ((tiles_n + kXcds - 1) / kXcds) * kXcds;
   constexpr int NT = WM * WN * kWave;
-#define TQ_GEMM(YTV)                                                                     \
-  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, ALIGNED, YTV>), dim3(tiles), dim3(NT), 0, s, \
+#define TQ_GEMM(YTV)                                                                    \
+  hipLaunchKernelGGL((k_gemm<BM, BN, WM, WN, ALIGNED, YTV>), dim3(grid), dim3(NT), 0, s, \
                      a.q, a.sx, a.M, a.packed, a.scale, a.per_row, a.N, a.K, a.Y)
   if (a.ydt == TQ_F32) TQ_GEMM(TQ_F32);
   else if (a.ydt == TQ_BF16) TQ_GEMM(TQ_BF16);
@@ -213,9 +457,9 @@ template <bool ALIGNED>
 hipError_t gemm_dispatch(const GemmArgs& a, hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   constexpr int64_t kEnough = 384;  // 1.5 workgroups per CU on 256 CUs
-  if (tiles(256, 128) >= kEnough) return gemm_launch<256, 128, 2, 2, ALIGNED>(a, s);
-  if (tiles(128, 128) >= kEnough) return gemm_launch<128, 128, 2, 2, ALIGNED>(a, s);
-  return gemm_launch<128, 64, 2, 2, ALIGNED>(a, s);
+  if (tiles(256, 128) >= kEnough) return gemm_launch<256, 128, 4, 1, ALIGNED>(a, s);
+  if (tiles(128, 128) >= kEnough) return gemm_launch<128, 128, 4, 1, ALIGNED>(a, s);
+  return gemm_launch<128, 64, 4, 1, ALIGNED>(a, s);
 }
 
 }  // namespace
@@ -224,6 +468,11 @@ hipError_t launch_gemm(const GemmArgs& a, hipStream_t s) {
   const bool aligned = (a.K % 64) == 0 &&
                        (reinterpret_cast<uintptr_t>(a.packed) & 15u) == 0u &&
                        (reinterpret_cast<uintptr_t>(a.q) & 15u) == 0u;
+  // buffer offsets are 32-bit: rows up to one tile past the end must stay
+  // below 2^31 bytes
+  constexpr int64_t kLim = int64_t{1} << 31;
+  const bool small = (a.M + 256) * a.K < kLim && (a.N + 256) * (a.K / 4) < kLim;
+  if (aligned && small) return gemm_fast_dispatch(a, s);
   return aligned ? gemm_dispatch<true>(a, s) : gemm_dispatch<false>(a, s);
 }
 

@@ -7,7 +7,8 @@
 // are unpacked on the fly, never into a dequantised buffer, and the result
 // is scaled by gamma afterwards.
 //
-// gfx950 mapping.  A workgroup (4 waves) owns 16 output rows; the waves
+// gfx950 mapping (general path, M <= 16).  A workgroup (4 waves) owns 16
+// output rows; the waves
 // split K in 256-wide sub-blocks.  Per sub-block a lane loads 16 packed bytes
 // (64 codes) of one row with a single 128-bit load, so a wave load covers
 // 16 rows x 64 contiguous bytes.  Each 32-bit word (16 codes) is decoded in
@@ -143,6 +144,198 @@ __global__ __launch_bounds__(kNT) void k_gemv(const int8_t* __restrict__ q,
   }
 }
 
+// ------------------------------------------------------------------------
+// Small-M path (M <= 4): the activations of the workgroup's whole K range are
+// staged once in LDS with each 16-byte chunk byte-transposed, which lets the
+// packed words be decoded with seven operations (decode_codes_strided)
+// instead of fifteen.  Eight waves split K; two accumulators alternate so
+// that consecutive MFMAs do not wait on each other.  With SRC != 0 the
+// kernel also performs the per-token int8 quantisation of X itself (the same
+// operations as k_quant_plain: eta = max(max|x|, eps), optional clamp,
+// s = 127/eta, q = clamp(rint(x*s)), sx = eta/127); every workgroup derives
+// the same codes, and workgroup 0 writes q and sx out.
+constexpr int kNTs = 512;
+constexpr int kWavesS = kNTs / kWave;
+constexpr int kUnrollS = 4;
+
+template <int SRC>
+__device__ inline void load16_act(const void* src, int64_t off, float (&v)[16]) {
+  if constexpr (SRC == 1) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(src) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 a = p[i];
+      v[4 * i] = a.x; v[4 * i + 1] = a.y; v[4 * i + 2] = a.z; v[4 * i + 3] = a.w;
+    }
+  } else {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + off);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint4 a = p[i];
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+        v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+template <int SRC, int YT>
+__global__ __launch_bounds__(kNTs) void k_gemv_lds(
+    const void* __restrict__ src, int M, float eps, int clamp, float lo, float hi,
+    int8_t* __restrict__ q_out, float* __restrict__ sx_io,
+    const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
+    int64_t N, int64_t K, void* __restrict__ Y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xt[];  // [M][K], chunks transposed
+  __shared__ v4i red[kWavesS][kWave];
+  __shared__ int tok_sum[4];
+  __shared__ uint32_t tok_max[4];
+  __shared__ float tok_eta[4];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int col = lane & 15;
+  const int g = lane >> 4;
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 16 + col;
+  const bool n_ok = n < N;
+  const int64_t rowbytes = K >> 2;
+  const uint8_t* wrow = packed + (n_ok ? n : 0) * rowbytes;
+  const int64_t nsb = (K + 255) >> 8;
+
+  auto load_w = [&](int64_t sb0, uint4 (&wv)[kUnrollS]) {
+#pragma unroll
+    for (int u = 0; u < kUnrollS; ++u) {
+      const int64_t sb = sb0 + kWavesS * u;
+      const int64_t off = sb * 64 + g * 16;
+      wv[u] = (n_ok && sb < nsb && off + 16 <= rowbytes)
+                  ? *reinterpret_cast<const uint4*>(wrow + off)
+                  : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+    }
+  };
+  uint4 wv[kUnrollS];
+  load_w(wave, wv);  // weight loads are in flight while the activations are staged
+
+  if (tid < 4) {
+    tok_sum[tid] = 0;
+    tok_max[tid] = 0u;
+  }
+  const int64_t cpr = K / 16;  // 16-byte chunks per token
+  const int64_t nchunk = static_cast<int64_t>(M) * cpr;
+  __syncthreads();
+  if (SRC != 0) {
+    for (int64_t c = tid; c < nchunk; c += kNTs) {
+      const int m = static_cast<int>(c / cpr);
+      float v[16];
+      load16_act<SRC>(src, m * K + (c - m * cpr) * 16, v);
+      float amax = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+      atomicMax(&tok_max[m], __float_as_uint(amax));  // non-negative: bit order = value order
+    }
+    __syncthreads();
+    if (tid < M) {
+      float eta = fmaxf(__uint_as_float(tok_max[tid]), eps);
+      if (clamp) eta = fminf(fmaxf(eta, lo), hi);
+      tok_eta[tid] = eta;
+      if (blockIdx.x == 0) sx_io[tid] = eta / 127.f;
+    }
+    __syncthreads();
+  }
+  for (int64_t c = tid; c < nchunk; c += kNTs) {
+    const int m = static_cast<int>(c / cpr);
+    const int64_t off = m * K + (c - m * cpr) * 16;
+    uint32_t d[4];
+    if (SRC == 0) {
+      const uint4 a = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(src) + off);
+      d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
+    } else {
+      const float s = 127.f / tok_eta[m];
+      float v[16];
+      load16_act<SRC>(src, off, v);
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        d[b] = quant_byte(v[4 * b], s) | (quant_byte(v[4 * b + 1], s) << 8) |
+               (quant_byte(v[4 * b + 2], s) << 16) | (quant_byte(v[4 * b + 3], s) << 24);
+      if (blockIdx.x == 0)
+        *reinterpret_cast<uint4*>(q_out + off) = make_uint4(d[0], d[1], d[2], d[3]);
+    }
+    *reinterpret_cast<v4i*>(xt + off) = transpose_bytes4x4(d[0], d[1], d[2], d[3]);
+    atomicAdd(&tok_sum[m], byte_sum(d[3], byte_sum(d[2], byte_sum(d[1], byte_sum(d[0], 0)))));
+  }
+  __syncthreads();
+
+  const bool m_ok = col < M;
+  v4i acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+  for (int64_t sb0 = wave; sb0 < nsb; sb0 += kWavesS * kUnrollS) {
+    if (sb0 != wave) load_w(sb0, wv);
+#pragma unroll
+    for (int u = 0; u < kUnrollS; ++u) {
+      const int64_t sb = sb0 + kWavesS * u;
+      if (sb >= nsb) break;  // uniform across the wave
+      const uint32_t words[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t k0 = sb * 256 + 64 * g + 16 * j;
+        v4i a = {0, 0, 0, 0};
+        if (m_ok && k0 < K) a = *reinterpret_cast<const v4i*>(xt + col * K + k0);
+        const v4i b = decode_codes_strided(words[j]);
+        if (j & 1)
+          acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc1, 0, 0, 0);
+        else
+          acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc0, 0, 0, 0);
+      }
+    }
+  }
+  red[wave][lane] = acc0 + acc1;
+  __syncthreads();
+  // D layout: lane l holds tokens 4*(l/16) + i of output column l%16; with
+  // M <= 4 only g == 0 carries tokens.  Wave w < 4 finishes element i = w.
+  if (wave >= 4 || g != 0) return;
+  const int m = wave;
+  if (m >= M || !n_ok) return;
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesS; ++w) total += red[w][lane][m];
+  const int accv = total - tok_sum[m];
+  const int64_t o = static_cast<int64_t>(m) * N + n;
+  if (YT == TQ_I32) {
+    static_cast<int*>(Y)[o] = accv;
+  } else {
+    const float sxm = SRC == 0 ? sx_io[m] : tok_eta[m] / 127.f;
+    const float gam = scale[per_row ? n : 0];
+    const float y = static_cast<float>(accv) * (gam * sxm);
+    if (YT == TQ_F32)
+      static_cast<float*>(Y)[o] = y;
+    else
+      static_cast<uint16_t*>(Y)[o] = f32_to_bf16(y);
+  }
+}
+
+template <int SRC>
+hipError_t gemv_lds_launch(const void* src, int M, const ActParams* p, int8_t* q_out,
+                           float* sx, const GemmArgs& a, hipStream_t s) {
+  const int64_t grid = (a.N + 15) / 16;
+  const size_t lds = static_cast<size_t>(M) * static_cast<size_t>(a.K);
+  const float eps = p ? p->eps : 0.f, lo = p ? p->eta_min : 0.f, hi = p ? p->eta_max : 0.f;
+  const int clamp = p ? p->clamp : 0;
+#define TQ_GEMV_LDS(YTV)                                                                 \
+  hipLaunchKernelGGL((k_gemv_lds<SRC, YTV>), dim3(grid), dim3(kNTs), lds, s, src, M, eps, \
+                     clamp, lo, hi, q_out, sx, a.packed, a.scale, a.per_row, a.N, a.K, a.Y)
+  if (a.ydt == TQ_F32) TQ_GEMV_LDS(TQ_F32);
+  else if (a.ydt == TQ_BF16) TQ_GEMV_LDS(TQ_BF16);
+  else TQ_GEMV_LDS(TQ_I32);
+#undef TQ_GEMV_LDS
+  return hipGetLastError();
+}
+
+bool lds_path_ok(int64_t M, int64_t K, const void* packed, const void* act) {
+  return M >= 1 && M <= 4 && (K % 64) == 0 && M * K <= kGemvLdsBytes &&
+         (reinterpret_cast<uintptr_t>(packed) & 15u) == 0u &&
+         (reinterpret_cast<uintptr_t>(act) & 15u) == 0u;
+}
+
 template <bool ALIGNED>
 hipError_t gemv_dispatch(const GemmArgs& a, hipStream_t s) {
   const int64_t grid = (a.N + 15) / 16;
@@ -159,10 +352,24 @@ hipError_t gemv_dispatch(const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
+  if (lds_path_ok(a.M, a.K, a.packed, a.q))
+    return gemv_lds_launch<0>(a.q, static_cast<int>(a.M), nullptr, nullptr,
+                              const_cast<float*>(a.sx), a, s);
   const bool aligned = (a.K % 64) == 0 &&
                        (reinterpret_cast<uintptr_t>(a.packed) & 15u) == 0u &&
                        (reinterpret_cast<uintptr_t>(a.q) & 15u) == 0u;
   return aligned ? gemv_dispatch<true>(a, s) : gemv_dispatch<false>(a, s);
+}
+
+bool fused_quant_gemv_ok(int64_t M, int64_t K, const void* packed, const void* X) {
+  return lds_path_ok(M, K, packed, X);
+}
+
+hipError_t launch_quant_gemv(const void* X, int bf16, const ActParams& p, int8_t* q,
+                             float* sx, const GemmArgs& a, hipStream_t s) {
+  const int M = static_cast<int>(a.M);
+  return bf16 ? gemv_lds_launch<2>(X, M, &p, q, sx, a, s)
+              : gemv_lds_launch<1>(X, M, &p, q, sx, a, s);
 }
 
 }  // namespace tq

@@ -90,45 +90,83 @@ tq_status tq_pack_ternary(const float* W, int64_t N, int64_t K, tq_gran g, tq_wm
   return hip_status(tq::launch_pack_rows(W, N, K, mode, packed, scale, stream));
 }
 
-tq_status tq_quant_act_int8(const void* X, tq_dtype xdt, int64_t M, int64_t K,
-                            const tq_act_opts* opts, int8_t* q, float* sx,
-                            hipStream_t stream) {
+// Checks of tq_quant_act_int8; fills p and tells whether a prologue is on.
+static tq_status check_quant(const void* X, tq_dtype xdt, int64_t M, int64_t K,
+                             const tq_act_opts* opts, int8_t* q, float* sx,
+                             tq::ActParams* p, bool* prologue) {
   if (M < 0 || K <= 0) return TQ_ERR_SHAPE;
   if (xdt != TQ_F32 && xdt != TQ_BF16) return TQ_ERR_DTYPE;
-  tq::ActParams p;
-  p.eps = 1e-6f;
-  p.clamp = 0;
-  p.eta_min = 0.f;
-  p.eta_max = 0.f;
-  p.rmsnorm = 0;
-  p.rms_eps = 1e-6f;
-  p.rms_weight = nullptr;
-  p.fwht = 0;
+  p->eps = 1e-6f;
+  p->clamp = 0;
+  p->eta_min = 0.f;
+  p->eta_max = 0.f;
+  p->rmsnorm = 0;
+  p->rms_eps = 1e-6f;
+  p->rms_weight = nullptr;
+  p->fwht = 0;
   if (opts) {
-    p.eps = opts->eps;
-    p.clamp = opts->clamp ? 1 : 0;
-    p.eta_min = opts->eta_min;
-    p.eta_max = opts->eta_max;
-    p.rmsnorm = opts->rmsnorm ? 1 : 0;
-    p.rms_eps = opts->rms_eps;
-    p.rms_weight = opts->rms_weight;
+    p->eps = opts->eps;
+    p->clamp = opts->clamp ? 1 : 0;
+    p->eta_min = opts->eta_min;
+    p->eta_max = opts->eta_max;
+    p->rmsnorm = opts->rmsnorm ? 1 : 0;
+    p->rms_eps = opts->rms_eps;
+    p->rms_weight = opts->rms_weight;
     if (opts->fwht_block != 0 && opts->fwht_block != 512) return TQ_ERR_UNSUPPORTED;
-    p.fwht = opts->fwht_block == 512 ? 1 : 0;
+    p->fwht = opts->fwht_block == 512 ? 1 : 0;
   }
-  if (!(p.eps > 0.f) || !isfinite(p.eps)) return TQ_ERR_UNSUPPORTED;
-  if (p.clamp && !(p.eta_min > 0.f && p.eta_min <= p.eta_max && isfinite(p.eta_max)))
+  if (!(p->eps > 0.f) || !isfinite(p->eps)) return TQ_ERR_UNSUPPORTED;
+  if (p->clamp && !(p->eta_min > 0.f && p->eta_min <= p->eta_max && isfinite(p->eta_max)))
     return TQ_ERR_UNSUPPORTED;
-  if (p.rmsnorm && (!(p.rms_eps >= 0.f) || !isfinite(p.rms_eps))) return TQ_ERR_UNSUPPORTED;
-  if (p.fwht && (K % 512) != 0) return TQ_ERR_SHAPE;
-  const bool prologue = p.rmsnorm || p.fwht;
-  if (prologue && K > tq::kPrologueMaxK) return TQ_ERR_UNSUPPORTED;
+  if (p->rmsnorm && (!(p->rms_eps >= 0.f) || !isfinite(p->rms_eps))) return TQ_ERR_UNSUPPORTED;
+  if (p->fwht && (K % 512) != 0) return TQ_ERR_SHAPE;
+  *prologue = p->rmsnorm || p->fwht;
+  if (*prologue && K > tq::kPrologueMaxK) return TQ_ERR_UNSUPPORTED;
   if (M == 0) return TQ_OK;
   if (!X || !q || !sx) return TQ_ERR_NULL;
   if (!aligned(X, xdt == TQ_F32 ? 4 : 2) || !aligned(sx, 4)) return TQ_ERR_ALIGN;
-  if (p.rms_weight && !aligned(p.rms_weight, 4)) return TQ_ERR_ALIGN;
+  if (p->rms_weight && !aligned(p->rms_weight, 4)) return TQ_ERR_ALIGN;
+  return TQ_OK;
+}
+
+static hipError_t launch_quant(const void* X, tq_dtype xdt, int64_t M, int64_t K,
+                               const tq::ActParams& p, bool prologue, int8_t* q, float* sx,
+                               hipStream_t stream) {
   const int bf16 = xdt == TQ_BF16 ? 1 : 0;
-  if (!prologue) return hip_status(tq::launch_quant_plain(X, bf16, M, K, p, q, sx, stream));
-  return hip_status(tq::launch_quant_prologue(X, bf16, M, K, p, q, sx, stream));
+  return prologue ? tq::launch_quant_prologue(X, bf16, M, K, p, q, sx, stream)
+                  : tq::launch_quant_plain(X, bf16, M, K, p, q, sx, stream);
+}
+
+tq_status tq_quant_act_int8(const void* X, tq_dtype xdt, int64_t M, int64_t K,
+                            const tq_act_opts* opts, int8_t* q, float* sx,
+                            hipStream_t stream) {
+  tq::ActParams p;
+  bool prologue = false;
+  const tq_status st = check_quant(X, xdt, M, K, opts, q, sx, &p, &prologue);
+  if (st != TQ_OK || M == 0) return st;
+  return hip_status(launch_quant(X, xdt, M, K, p, prologue, q, sx, stream));
+}
+
+tq_status tq_quant_ternary_gemv(const void* X, tq_dtype xdt, int64_t M,
+                                const tq_act_opts* opts, const uint8_t* packed,
+                                const float* scale, tq_gran g, int64_t N, int64_t K,
+                                int8_t* q, float* sx, void* Y, tq_dtype ydt,
+                                hipStream_t stream) {
+  if (M > tq::kGemvMaxM) return TQ_ERR_SHAPE;
+  tq::ActParams p;
+  bool prologue = false;
+  tq_status st = check_quant(X, xdt, M, K, opts, q, sx, &p, &prologue);
+  if (st != TQ_OK) return st;
+  st = check_contract(q, sx, M, packed, scale, g, N, K, Y, ydt);
+  if (st != TQ_OK || M == 0) return st;
+  if (N == 0) return hip_status(launch_quant(X, xdt, M, K, p, prologue, q, sx, stream));
+  const tq::GemmArgs a = make_args(q, sx, M, packed, scale, g, N, K, Y, ydt);
+  if (!prologue && tq::fused_quant_gemv_ok(M, K, packed, X))
+    return hip_status(
+        tq::launch_quant_gemv(X, xdt == TQ_BF16 ? 1 : 0, p, q, sx, a, stream));
+  const hipError_t e = launch_quant(X, xdt, M, K, p, prologue, q, sx, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(tq::launch_gemv(a, stream));
 }
 
 tq_status tq_fwht512(const void* X, tq_dtype xdt, int64_t M, int64_t K, int normalize,

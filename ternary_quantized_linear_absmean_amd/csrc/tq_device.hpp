@@ -101,15 +101,11 @@ __device__ inline uint32_t quant_byte(float x, float s) {
 
 // --------------------------------------------------------- 2-bit decoding
 
-// One packed 32-bit word holds 16 codes, code i in bits 2i..2i+1 (-1 = 0,
-// 0 = 1, +1 = 2).  Returns the 16 codes (values 0..2) as bytes in natural
-// order: byte j of out[t] is code 4t + j.
-__device__ inline v4i decode_codes_natural(uint32_t w) {
-  const uint32_t d0 = w & 0x03030303u;          // codes 0, 4, 8, 12
-  const uint32_t d1 = (w >> 2) & 0x03030303u;   // codes 1, 5, 9, 13
-  const uint32_t d2 = (w >> 4) & 0x03030303u;   // codes 2, 6, 10, 14
-  const uint32_t d3 = (w >> 6) & 0x03030303u;   // codes 3, 7, 11, 15
-  // 4x4 byte transpose (v_perm_b32: selector 0-3 picks the 2nd operand's bytes)
+// 4x4 byte transpose: out[s] holds byte s of d0, d1, d2, d3 (in that order).
+// Applied to 16 consecutive int8 values (d_b = values 4b..4b+3) it gives
+// out[s] byte b = value 4b + s, the order decode_codes_strided produces.
+__device__ inline v4i transpose_bytes4x4(uint32_t d0, uint32_t d1, uint32_t d2,
+                                         uint32_t d3) {
   const uint32_t a_lo = __builtin_amdgcn_perm(d1, d0, 0x05010400u);
   const uint32_t a_hi = __builtin_amdgcn_perm(d1, d0, 0x07030602u);
   const uint32_t b_lo = __builtin_amdgcn_perm(d3, d2, 0x05010400u);
@@ -119,6 +115,27 @@ __device__ inline v4i decode_codes_natural(uint32_t w) {
   out.y = static_cast<int>(__builtin_amdgcn_perm(b_lo, a_lo, 0x07060302u));
   out.z = static_cast<int>(__builtin_amdgcn_perm(b_hi, a_hi, 0x05040100u));
   out.w = static_cast<int>(__builtin_amdgcn_perm(b_hi, a_hi, 0x07060302u));
+  return out;
+}
+
+// One packed 32-bit word holds 16 codes, code i in bits 2i..2i+1 (-1 = 0,
+// 0 = 1, +1 = 2).  Returns the 16 codes (values 0..2) as bytes in natural
+// order: byte j of out[t] is code 4t + j.  (w >> 2s) & 0x03030303 holds codes
+// s, 4+s, 8+s, 12+s; a 4x4 byte transpose puts them in order.
+__device__ inline v4i decode_codes_natural(uint32_t w) {
+  return transpose_bytes4x4(w & 0x03030303u, (w >> 2) & 0x03030303u,
+                            (w >> 4) & 0x03030303u, (w >> 6) & 0x03030303u);
+}
+
+// The 16 codes of a packed word, values 0..2, in strided order: byte b of
+// out[s] is code 4b + s.  Seven integer operations; the matching activation
+// operand is the byte transpose above.
+__device__ inline v4i decode_codes_strided(uint32_t w) {
+  v4i out;
+  out.x = static_cast<int>(w & 0x03030303u);
+  out.y = static_cast<int>((w >> 2) & 0x03030303u);
+  out.z = static_cast<int>((w >> 4) & 0x03030303u);
+  out.w = static_cast<int>((w >> 6) & 0x03030303u);
   return out;
 }
 

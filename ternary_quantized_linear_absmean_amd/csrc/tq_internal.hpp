@@ -48,7 +48,13 @@ struct GemmArgs {
   int ydt;  // tq_dtype
 };
 constexpr int kGemvMaxM = 16;
+constexpr int64_t kGemvLdsBytes = 65536;  // activation staging of the small-M GEMV
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t s);
+// quantise X (plain path) and apply the GEMV in one launch; only when
+// fused_quant_gemv_ok() holds
+bool fused_quant_gemv_ok(int64_t M, int64_t K, const void* packed, const void* X);
+hipError_t launch_quant_gemv(const void* X, int bf16, const ActParams& p, int8_t* q,
+                             float* sx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
 }  // namespace tq

@@ -32,7 +32,7 @@ GRANULARITY = {"tensor": 0, "row": 1}
 MODES = {"ternary": 0, "binary": 1}
 EXPORTED = ["tq_packed_bytes", "tq_pack_workspace_bytes", "tq_pack_ternary",
             "tq_quant_act_int8", "tq_fwht512", "tq_ternary_gemv", "tq_ternary_gemm",
-            "tq_status_str", "tq_last_hip_error", "tq_version"]
+            "tq_quant_ternary_gemv", "tq_status_str", "tq_last_hip_error", "tq_version"]
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -58,6 +58,9 @@ _lib.tq_fwht512.restype = _int
 for _name in ("tq_ternary_gemv", "tq_ternary_gemm"):
     getattr(_lib, _name).argtypes = [_vp, _vp, _i64, _vp, _vp, _int, _i64, _i64, _vp, _int, _vp]
     getattr(_lib, _name).restype = _int
+_lib.tq_quant_ternary_gemv.argtypes = [_vp, _int, _i64, ctypes.POINTER(TqActOpts), _vp, _vp,
+                                       _int, _i64, _i64, _vp, _vp, _vp, _int, _vp]
+_lib.tq_quant_ternary_gemv.restype = _int
 _lib.tq_status_str.argtypes = [_int]
 _lib.tq_status_str.restype = ctypes.c_char_p
 _lib.tq_last_hip_error.argtypes = []
@@ -151,6 +154,13 @@ def tq_pack_ternary(W: torch.Tensor, granularity: str = "tensor", mode: str = "t
 
 # ------------------------------------------------------------ activations
 
+def _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block) -> TqActOpts:
+    return TqActOpts(eps=eps, clamp=1 if clamp else 0,
+                     eta_min=clamp[0] if clamp else 0.0, eta_max=clamp[1] if clamp else 0.0,
+                     rmsnorm=1 if rmsnorm else 0, rms_eps=rms_eps,
+                     rms_weight=_ptr(rms_weight), fwht_block=fwht_block)
+
+
 def tq_quant_act_int8(X: torch.Tensor, eps: float = 1e-6, clamp=None, rmsnorm: bool = False,
                       rms_eps: float = 1e-6, rms_weight: torch.Tensor | None = None,
                       fwht_block: int = 0, q: torch.Tensor | None = None,
@@ -165,10 +175,7 @@ def tq_quant_act_int8(X: torch.Tensor, eps: float = 1e-6, clamp=None, rmsnorm: b
         q = torch.empty((M, K), dtype=torch.int8, device=X.device)
     if sx is None:
         sx = torch.empty((M,), dtype=torch.float32, device=X.device)
-    opts = TqActOpts(eps=eps, clamp=1 if clamp else 0,
-                     eta_min=clamp[0] if clamp else 0.0, eta_max=clamp[1] if clamp else 0.0,
-                     rmsnorm=1 if rmsnorm else 0, rms_eps=rms_eps,
-                     rms_weight=_ptr(rms_weight), fwht_block=fwht_block)
+    opts = _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block)
     _check(_lib.tq_quant_act_int8(X.data_ptr(), _ACT_DT[X.dtype], M, K, ctypes.byref(opts),
                                   _ptr(q), _ptr(sx), _stream(stream)), "tq_quant_act_int8")
     return q, sx
@@ -218,6 +225,35 @@ def tq_ternary_gemm(q, sx, packed, scale, N: int, K: int, granularity: str = "te
     """Same contract as tq_ternary_gemv for any number of tokens."""
     return _contract(_lib.tq_ternary_gemm, "tq_ternary_gemm", q, sx, packed, scale, N, K,
                      granularity, out_dtype, Y, stream)
+
+
+def tq_quant_ternary_gemv(X: torch.Tensor, packed, scale, N: int, K: int,
+                          granularity: str = "tensor", out_dtype: str = "f32", eps: float = 1e-6,
+                          clamp=None, rmsnorm: bool = False, rms_eps: float = 1e-6,
+                          rms_weight: torch.Tensor | None = None, fwht_block: int = 0,
+                          q: torch.Tensor | None = None, sx: torch.Tensor | None = None,
+                          Y: torch.Tensor | None = None, stream=None):
+    """Quantise X [M, K] (M <= 16) and apply the decode GEMV in one call ->
+    (Y [M, N], q int8 [M, K], sx fp32 [M])."""
+    _dev(X, "X")
+    _dev(packed, "packed")
+    _dev(scale, "scale")
+    if X.dtype not in _ACT_DT or X.dim() != 2:
+        raise ValueError("X must be a 2-D float32 or bfloat16 tensor")
+    M = X.shape[0]
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=_Y_TORCH[out_dtype], device=X.device)
+    opts = _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block)
+    _check(_lib.tq_quant_ternary_gemv(X.data_ptr(), _ACT_DT[X.dtype], M, ctypes.byref(opts),
+                                      packed.data_ptr(), scale.data_ptr(),
+                                      GRANULARITY[granularity], N, K, _ptr(q), _ptr(sx),
+                                      _ptr(Y), DTYPES[out_dtype], _stream(stream)),
+           "tq_quant_ternary_gemv")
+    return Y, q, sx
 
 
 def raw_library() -> ctypes.CDLL:

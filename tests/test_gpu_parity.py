@@ -493,3 +493,76 @@ def test_end_to_end_bitlinear_binary_and_ternary():
         y_ref = oracle.epilogue(acc_ref, scale_ref, sxe, rows=cols)
         err = np.abs(y[:, cols] - y_ref)
         assert np.all(err <= 3e-6 * np.abs(y_ref) + 0), "bitlinear output off"
+
+
+# ------------------------------------------------- fused quantise + GEMV
+
+FUSED_CASES = [
+    (1, 4096, 4096, "bf16", "tensor"),   # the decode workload shape: one launch
+    (4, 300, 2560, "f32", "row"),
+    (3, 77, 64, "bf16", "tensor"),
+    (1, 5, 6912, "bf16", "row"),
+    (2, 33, 1024, "f32", "tensor"),
+    (8, 100, 512, "bf16", "row"),        # M > 4: quantiser + general GEMV
+    (1, 20, 68, "f32", "tensor"),        # K % 64 != 0: two launches
+    (4, 64, 32768, "bf16", "tensor"),    # M*K beyond the LDS staging limit
+]
+
+
+@pytest.mark.parametrize("M,N,K,dtype,gran", FUSED_CASES)
+def test_quant_ternary_gemv_matches_two_calls(M, N, K, dtype, gran):
+    X = ti.activations(3000 + M + N + K, M, K, dtype=dtype)
+    if M >= 3:
+        X[1] = 0.0
+    w = ti.random_ternary(4000 + N + K, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(N + 5, 1, N, dtype="f32")[0]) * 0.02 + 1e-3).astype(np.float32)
+    sc = scale if gran == "row" else scale[:1]
+    Xd, pd, sd = x_to_device(X, dtype), dev(packed), dev(sc)
+    say(f"quant+gemv M={M} N={N} K={K} {dtype} {gran}")
+    qr, sr = oracle.quant_act_int8(X, eta_min=0.05, eta_max=40.0)
+    for ydt in ("f32", "bf16", "i32"):
+        Y, q, sx = tq.tq_quant_ternary_gemv(Xd, pd, sd, N, K, gran, ydt, clamp=(0.05, 40.0))
+        q2, sx2 = tq.tq_quant_act_int8(Xd, clamp=(0.05, 40.0))
+        Y2 = tq.tq_ternary_gemv(q2, sx2, pd, sd, N, K, gran, ydt)
+        np.testing.assert_array_equal(host(q), host(q2))
+        np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(host(sx2)))
+        yb = Y.view(torch.int16) if ydt == "bf16" else Y
+        yb2 = Y2.view(torch.int16) if ydt == "bf16" else Y2
+        np.testing.assert_array_equal(host(yb), host(yb2))
+        np.testing.assert_array_equal(host(q), qr)
+        np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sr))
+        if ydt == "f32":
+            acc_ref, y_ref = _contract_ref(qr, packed, K, sc, sr)
+            assert_y_close(host(Y), y_ref)
+
+
+def test_quant_ternary_gemv_with_prologue_and_empty():
+    X = ti.activations(77, 2, 1024, dist="student_t3", dtype="f32")
+    w = ti.random_ternary(78, 40, 1024)
+    packed = oracle.pack_codes(w)
+    scale = np.array([0.03], np.float32)
+    say("quant+gemv prologue")
+    Y, q, sx = tq.tq_quant_ternary_gemv(dev(X), dev(packed), dev(scale), 40, 1024, "tensor",
+                                        "f32", clamp=(0.05, 40.0), rmsnorm=True, fwht_block=512)
+    qr, srr, sxe, bound = oracle.rmsnorm_fwht_quant(X, rmsnorm=True, fwht=True)
+    np.testing.assert_array_equal(host(q), qr)
+    acc_ref, y_ref = _contract_ref(qr, packed, 1024, scale, host(sx))
+    assert_y_close(host(Y), y_ref)
+    # N == 0 still quantises
+    Y0, q0, s0 = tq.tq_quant_ternary_gemv(dev(X), dev(packed), dev(scale), 0, 1024, "tensor")
+    q1, s1 = tq.tq_quant_act_int8(dev(X))
+    np.testing.assert_array_equal(host(q0), host(q1))
+
+
+def test_gemv_small_m_large_k_general_path():
+    # M*K beyond the LDS staging limit goes through the general kernel
+    M, N, K = 4, 48, 32768
+    q = ti.random_int8(5, M, K)
+    w = ti.random_ternary(6, N, K)
+    packed = oracle.pack_codes(w)
+    scale = np.array([0.01], np.float32)
+    sx = np.array([0.1, 0.2, 0.3, 0.4], np.float32)
+    say("gemv large K")
+    _check_outputs(tq.tq_ternary_gemv, dev(q), dev(sx), dev(packed), dev(scale), N, K,
+                   "tensor", q, packed, scale, sx)
