@@ -31,6 +31,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+PROFILE = os.path.join(ROOT, "profiles", "k_gemv_dot_decode_4096x4096_b1.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "ternary_quantized_linear_absmean_amd", "csrc", f)
+                  for f in ("k_gemv.hip", "tq_device.hpp")]
 INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, 5.0 POP/s
 POOL = 128                     # distinct packed weights in the rotation
 
@@ -44,7 +47,7 @@ def parse():
     p.add_argument("--no-extra", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--only", default="",
-                   help="comma list of extra workloads to run: prefill,bitlinear,pack,ffn")
+                   help="comma list of extra workloads to run: prefill,bitlinear,pack,ffn,context")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (for counter scaling)")
     return p.parse_args()
@@ -57,6 +60,41 @@ def gemv_bytes(M, N, K, per_row):
 
 def quant_bytes(M, K, xbytes):
     return M * K * xbytes + M * K + 4 * M
+
+
+def fused_bytes(M, N, K, xbytes, per_row):
+    # tokens in + packed W + scale(s) + int8 tokens and sx out + fp32 output
+    # (the int8 tokens are not read back: the kernel keeps them on chip)
+    return M * K * xbytes + N * K // 4 + (4 * N if per_row else 4) + M * K + 4 * M + 4 * M * N
+
+
+def source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic():
+    """HBM bytes per launch of the fused decode kernel, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when that summary is
+    missing or was taken on a different version of the kernel source."""
+    if not os.path.exists(PROFILE):
+        return None
+    fields = {}
+    with open(PROFILE) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256_16") != source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def timed_graph(torch, graph, reps):
@@ -143,12 +181,13 @@ def main():
     wall = time.perf_counter() - t0
     step_s = sec_per_pass / POOL
     b_gemv = gemv_bytes(1, N, K, False)
-    b_step = b_gemv + quant_bytes(1, K, 2)
+    b_step = fused_bytes(1, N, K, 2, False)
     value = b_step / step_s / 1e9
 
     gemv_s = timed_graph(torch, g_gemv, reps) / POOL
     gemv_gbs = b_gemv / gemv_s / 1e9
     two_s = timed_graph(torch, g_two, reps) / POOL
+    traffic = counter_traffic()
 
     result = {
         "metric": "ternary GEMV GB/s (% HBM peak) at K=N=4096 b=1; GEMM TOPS (% int8 MFMA peak)",
@@ -169,11 +208,17 @@ def main():
                    "M": 1, "N": N, "K": K, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "entry_point": "tq_quant_ternary_gemv (quantise + GEMV, one launch)",
                    "two_call_step_us": round(two_s * 1e6, 3),
+                   "kernel_source_sha256_16": source_digest(),
                    "timed_wall_s": round(wall, 4)},
-        "roofline": {"bound": "hbm", "kernel": "k_gemv", "achieved": round(gemv_gbs, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gemv_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": b_gemv, "avg_launch_us": round(gemv_s * 1e6, 3)},
+        # the step is one launch of the fused quantise + GEMV kernel, so its
+        # average launch time is the step time measured above
+        "roofline": {"bound": "hbm", "kernel": "k_gemv_dot<bf16 X, K<=4096> (tq_quant_ternary_gemv)",
+                     "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": b_step, "avg_launch_us": round(step_s * 1e6, 3)},
+        "gemv_int8_input": {"kernel": "k_gemv_dot<int8 q, K<=4096> (tq_ternary_gemv)",
+                            "bytes_per_launch": b_gemv, "avg_launch_us": round(gemv_s * 1e6, 3),
+                            "GBs": round(gemv_gbs, 2)},
     }
 
     if not args.no_extra:
@@ -195,6 +240,8 @@ def extras(torch, np, ti, tq, dev, only=frozenset()):
         out.update(extra_bitlinear(torch, ti, tq, dev))
     if want("ffn"):
         out.update(extra_ffn(torch, ti, tq, dev))
+    if want("context"):
+        out.update(extra_context(torch, dev))
     torch.cuda.synchronize()
     return out
 
@@ -291,16 +338,55 @@ def extra_ffn(torch, ti, tq, dev):
     return out
 
 
+def extra_context(torch, dev):
+    """Reference points, not this library's work: what a plain torch kernel
+    needs to stream 4 MiB per launch under the same 128-buffer rotation and
+    graph replay (the floor a 4 MiB decode GEMV sits on), and the vendor
+    int8 GEMM (hipBLASLt through torch._int_mm, int8 weights) on the prefill
+    shape."""
+    out = {}
+    pool = [torch.ones(1 << 20, dtype=torch.int32, device=dev) for _ in range(POOL)]
+    dst = torch.empty(1 << 20, dtype=torch.int32, device=dev)
+    res = torch.empty((), dtype=torch.int32, device=dev)
+    g = capture(torch, lambda: [dst.copy_(p) for p in pool])
+    timed_graph(torch, g, 2)
+    t = timed_graph(torch, g, 16) / POOL
+    out["torch_copy_4MiB_rotating"] = {"us": round(t * 1e6, 3),
+                                       "GBs_read_plus_write": round(8 * 2**20 / t / 1e9, 1)}
+    g = capture(torch, lambda: [torch.amax(p, dim=0, out=res) for p in pool])
+    timed_graph(torch, g, 2)
+    t = timed_graph(torch, g, 16) / POOL
+    out["torch_amax_4MiB_rotating"] = {"us": round(t * 1e6, 3),
+                                       "GBs_read": round(4 * 2**20 / t / 1e9, 1)}
+    del pool
+    try:
+        M, N, K = 2048, 11008, 4096
+        A = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+        B = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev)
+        g = capture(torch, lambda: [torch._int_mm(A, B.t()) for _ in range(8)])
+        timed_graph(torch, g, 2)
+        t = timed_graph(torch, g, 5) / 8
+        out["vendor_int8_gemm_prefill"] = {"api": "torch._int_mm (int8 x int8 -> int32)",
+                                           "shape": [M, N, K], "us": round(t * 1e6, 2),
+                                           "TOPS": round(2.0 * M * N * K / t / 1e12, 1)}
+    except Exception as e:  # the reference is optional context
+        out["vendor_int8_gemm_prefill"] = {"error": str(e)[:200]}
+    return out
+
+
 def copy_calibration(torch, dev):
-    n = 256 << 20
-    a = torch.empty(n, dtype=torch.uint8, device=dev)
-    b = torch.empty(n, dtype=torch.uint8, device=dev)
-    a.fill_(1)
+    """A plain elementwise kernel of known traffic (reads 256 MiB, writes
+    256 MiB, beyond the Infinity Cache): its FETCH_SIZE / WRITE_SIZE
+    readings scale the counters of the kernels above to bytes."""
+    n = 64 << 20                                   # fp32 elements = 256 MiB
+    a = torch.ones(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
     torch.cuda.synchronize()
     for _ in range(3):
-        b.copy_(a)
+        torch.neg(a, out=b)
     torch.cuda.synchronize()
-    return {"bytes_read": n, "bytes_written": n, "launches": 3}
+    return {"kernel": "torch.neg fp32", "bytes_read": 4 * n, "bytes_written": 4 * n,
+            "launches": 3}
 
 
 def cpu_baseline(np, ti, seconds):

@@ -154,9 +154,15 @@ __global__ __launch_bounds__(kNT) void k_gemv(const int8_t* __restrict__ q,
 // operations as k_quant_plain: eta = max(max|x|, eps), optional clamp,
 // s = 127/eta, q = clamp(rint(x*s)), sx = eta/127); every workgroup derives
 // the same codes, and workgroup 0 writes q and sx out.
-constexpr int kNTs = 512;
-constexpr int kWavesS = kNTs / kWave;
-constexpr int kUnrollS = 4;
+#ifndef TQ_GEMV_LDS_WAVES
+#define TQ_GEMV_LDS_WAVES 8
+#endif
+constexpr int kWavesS = TQ_GEMV_LDS_WAVES;
+constexpr int kNTs = kWavesS * kWave;
+#ifndef TQ_GEMV_LDS_UNROLL
+#define TQ_GEMV_LDS_UNROLL 4
+#endif
+constexpr int kUnrollS = TQ_GEMV_LDS_UNROLL;
 
 template <int SRC>
 __device__ inline void load16_act(const void* src, int64_t off, float (&v)[16]) {
@@ -313,6 +319,244 @@ __global__ __launch_bounds__(kNTs) void k_gemv_lds(
   }
 }
 
+// ------------------------------------------------------------------------
+// Row-per-wave path (M == 1, K <= 16384).  A single-token weight stream read
+// once is latency-bound: its time falls with the number of waves that each
+// hold one load in flight, not with the loads per wave, so every wave owns
+// one output row and fetches it with one 16-byte buffer load per lane per
+// 4096-wide K slice (64 codes a lane).  The loads are ordered so that no wave
+// waits on its weights before it must: the thread's share of the token
+// first, then the weights, then the epilogue operands.  The token work
+// (quantising fp32 / bf16 input exactly as k_quant_plain does when SRC != 0)
+// is done by four staging waves and leaves the int8 token in LDS,
+// byte-transposed to the order of decode_codes_strided (seven operations
+// per 32-bit word) and swizzled so that the lanes' 16-byte reads fall in
+// distinct banks.  Per-wave maxima and byte sums go through small LDS arrays,
+// so the token costs two barriers.  Products use v_dot4 and
+// sum_k q*(c-1) = sum_k q*c - sum_k q as in the tiled kernels; the wave sum
+// is a DPP reduction.
+#ifndef TQ_GEMV_DOT_WAVES
+#define TQ_GEMV_DOT_WAVES 16
+#endif
+constexpr int kRowsD = TQ_GEMV_DOT_WAVES;
+constexpr int kNTd = kRowsD * kWave;
+// The token is quantised and staged by four waves, one per SIMD: its fixed
+// per-wave cost (reductions, the exact divide) is then paid once per SIMD.
+constexpr int kStageWaves = 4;
+constexpr int kStageNT = kStageWaves * kWave;
+static_assert(kRowsD >= kStageWaves, "row-per-wave kernel needs at least four waves");
+constexpr int kMaxSlices = 4;        // K <= 16384
+constexpr int kBufRaw = 0x00020000;  // raw buffer resource, 32-bit data format
+
+// Four consecutive token values in their storage type.
+template <int SRC>
+struct RawQuad {
+  uint32_t w[SRC == 1 ? 4 : SRC == 2 ? 2 : 1];
+};
+
+template <int SRC>
+__device__ inline RawQuad<SRC> load_quad(__amdgpu_buffer_rsrc_t r, int q) {
+  RawQuad<SRC> out;
+  if constexpr (SRC == 1) {
+    const v4i v = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * q, 0, 0));
+    out.w[0] = v.x; out.w[1] = v.y; out.w[2] = v.z; out.w[3] = v.w;
+  } else if constexpr (SRC == 2) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 v = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(r, 8 * q, 0, 0));
+    out.w[0] = v.x; out.w[1] = v.y;
+  } else {
+    out.w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, 4 * q, 0, 0);
+  }
+  return out;
+}
+
+template <int SRC>
+__device__ inline void quad_to_f32(const RawQuad<SRC>& r, float (&v)[4]) {
+  if constexpr (SRC == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(r.w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      v[2 * i] = __uint_as_float(r.w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(r.w[i] & 0xFFFF0000u);
+    }
+  }
+}
+
+// LDS slot of 16-byte unit u of the staged token.  Reads take units 4l + j
+// (lane l, fixed j); XOR-ing the low two bits with bits 3 and 4 spreads any 8
+// or 16 consecutive lanes over distinct bank groups.
+__device__ inline int dot_slot(int u) { return (u ^ (((u >> 3) ^ (u >> 4)) & 3)) * 16; }
+
+template <int SRC, int S>
+__global__ __launch_bounds__(kNTd) void k_gemv_dot(
+    const void* __restrict__ src, float eps, int clamp, float lo, float hi,
+    int8_t* __restrict__ q_out, float* __restrict__ sx_io,
+    const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
+    int64_t N, int K, void* __restrict__ Y, int ydt) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xt[];  // K bytes
+  __shared__ float wave_max_part[kStageWaves];
+  __shared__ int wave_sum_part[kStageWaves];
+  __shared__ float tok_sx;
+  constexpr int kRounds = S * 4096 / 4 / kStageNT;  // quads per staging lane
+  constexpr int kEl = SRC == 1 ? 4 : SRC == 2 ? 2 : 1;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const bool stager = wave < kStageWaves;
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * kRowsD + wave;
+  const int rowbytes = K >> 2;
+  const int nquad = K >> 2;
+
+  // 1. the staging waves' quads of the token (reads past K return zero)
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(src), static_cast<short>(0), K * kEl, kBufRaw);
+  RawQuad<SRC> rq[kRounds];
+  if (stager) {
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) rq[i] = load_quad<SRC>(xr, tid + kStageNT * i);
+  }
+  // 2. the wave's row, chunk lane + 64*sl of each slice (rows >= N read zeros)
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed + (n < N ? n : 0) * rowbytes), static_cast<short>(0),
+      n < N ? rowbytes : 0, kBufRaw);
+  uint4 wv[S];
+#pragma unroll
+  for (int sl = 0; sl < S; ++sl)
+    wv[sl] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + kWave * sl) * 16, 0, 0));
+  // 3. epilogue operands
+  const int64_t nr = n < N ? n : N - 1;
+  const float gam = ydt == TQ_I32 ? 0.f : scale[per_row ? nr : 0];
+  const float sx_in = SRC == 0 ? sx_io[0] : 0.f;
+
+  // 4. token scale (SRC != 0): staging-wave maxima, folded by each stager
+  float sc = 0.f;
+  if (SRC != 0) {
+    if (stager) {
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < kRounds; ++i) {
+        float v[4];
+        quad_to_f32<SRC>(rq[i], v);  // zeros past K
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+      }
+      mx = wave_max_last(mx);
+      if (lane == kWave - 1) wave_max_part[wave] = mx;
+    }
+    __syncthreads();
+    if (stager) {
+      float amax = 0.f;
+#pragma unroll
+      for (int w = 0; w < kStageWaves; ++w) amax = fmaxf(amax, wave_max_part[w]);
+      float eta = fmaxf(amax, eps);
+      if (clamp) eta = fminf(fmaxf(eta, lo), hi);
+      sc = 127.f / eta;
+      if (tid == 0) {
+        const float sxv = eta / 127.f;
+        tok_sx = sxv;
+        if (blockIdx.x == 0) sx_io[0] = sxv;
+      }
+    }
+  }
+  // 5. int8 token -> transposed, swizzled LDS; byte sums
+  if (stager) {
+    int bsum = 0;
+#pragma unroll
+    for (int i = 0; i < kRounds; ++i) {
+      const int qi = tid + kStageNT * i;
+      if (qi < nquad) {
+        uint32_t d;
+        if (SRC == 0) {
+          d = rq[i].w[0];
+        } else {
+          float v[4];
+          quad_to_f32<SRC>(rq[i], v);
+          d = quant_byte(v[0], sc) | (quant_byte(v[1], sc) << 8) |
+              (quant_byte(v[2], sc) << 16) | (quant_byte(v[3], sc) << 24);
+          if (blockIdx.x == 0) reinterpret_cast<uint32_t*>(q_out)[qi] = d;
+        }
+        // quad qi is word b = qi % 4 of unit qi / 4; its byte s goes to
+        // byte b of word s of the transposed unit
+        uint8_t* dst = xt + dot_slot(qi >> 2) + (qi & 3);
+        dst[0] = static_cast<uint8_t>(d);
+        dst[4] = static_cast<uint8_t>(d >> 8);
+        dst[8] = static_cast<uint8_t>(d >> 16);
+        dst[12] = static_cast<uint8_t>(d >> 24);
+        bsum = byte_sum(d, bsum);
+      }
+    }
+    bsum = wave_isum_last(bsum);
+    if (lane == kWave - 1) wave_sum_part[wave] = bsum;
+  }
+  asm volatile("" ::"v"(gam));
+  asm volatile("" ::"v"(sx_in));
+  __syncthreads();
+
+  // 6. contraction of the wave's row
+  int acc = 0;
+#pragma unroll
+  for (int sl = 0; sl < S; ++sl) {
+    const int unit = 4 * (lane + kWave * sl);  // first 16-code unit of the chunk
+    if (16 * unit >= K) break;                  // this chunk, and every later one, is past K
+    const uint32_t words[4] = {wv[sl].x, wv[sl].y, wv[sl].z, wv[sl].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4i cd = decode_codes_strided(words[j]);
+      const v4i x = *reinterpret_cast<const v4i*>(xt + dot_slot(unit + j));
+      acc = __builtin_amdgcn_sdot4(x.x, cd.x, acc, false);
+      acc = __builtin_amdgcn_sdot4(x.y, cd.y, acc, false);
+      acc = __builtin_amdgcn_sdot4(x.z, cd.z, acc, false);
+      acc = __builtin_amdgcn_sdot4(x.w, cd.w, acc, false);
+    }
+  }
+  acc = wave_isum_last(acc);
+  if (lane != kWave - 1 || n >= N) return;
+  int tsum = 0;
+#pragma unroll
+  for (int w = 0; w < kStageWaves; ++w) tsum += wave_sum_part[w];
+  const int accv = acc - tsum;
+  if (ydt == TQ_I32) {
+    static_cast<int*>(Y)[n] = accv;
+  } else {
+    const float sxv = SRC == 0 ? sx_in : tok_sx;
+    const float y = static_cast<float>(accv) * (gam * sxv);
+    if (ydt == TQ_F32)
+      static_cast<float*>(Y)[n] = y;
+    else
+      static_cast<uint16_t*>(Y)[n] = f32_to_bf16(y);
+  }
+}
+
+template <int SRC, int S>
+hipError_t gemv_dot_launch_s(const void* src, const ActParams* p, int8_t* q_out, float* sx,
+                             const GemmArgs& a, hipStream_t s) {
+  const int64_t grid = (a.N + kRowsD - 1) / kRowsD;
+  const float eps = p ? p->eps : 0.f, lo = p ? p->eta_min : 0.f, hi = p ? p->eta_max : 0.f;
+  const int clamp = p ? p->clamp : 0;
+  hipLaunchKernelGGL((k_gemv_dot<SRC, S>), dim3(grid), dim3(kNTd), static_cast<size_t>(a.K), s,
+                     src, eps, clamp, lo, hi, q_out, sx, a.packed, a.scale, a.per_row, a.N,
+                     static_cast<int>(a.K), a.Y, a.ydt);
+  return hipGetLastError();
+}
+
+template <int SRC>
+hipError_t gemv_dot_launch(const void* src, const ActParams* p, int8_t* q_out, float* sx,
+                           const GemmArgs& a, hipStream_t s) {
+  if (a.K <= 4096) return gemv_dot_launch_s<SRC, 1>(src, p, q_out, sx, a, s);
+  if (a.K <= 8192) return gemv_dot_launch_s<SRC, 2>(src, p, q_out, sx, a, s);
+  return gemv_dot_launch_s<SRC, kMaxSlices>(src, p, q_out, sx, a, s);
+}
+
+// One token, K a multiple of 64 up to 16384 (the token and its LDS copy are
+// then at most 64 KiB, offsets 32-bit; the row offset n*K/4 is 64-bit).
+bool dot_path_ok(int64_t M, int64_t K, const void* packed, const void* act) {
+  return M == 1 && (K % 64) == 0 && K <= 4096 * kMaxSlices &&
+         (reinterpret_cast<uintptr_t>(packed) & 15u) == 0u &&
+         (reinterpret_cast<uintptr_t>(act) & 15u) == 0u;
+}
+
 template <int SRC>
 hipError_t gemv_lds_launch(const void* src, int M, const ActParams* p, int8_t* q_out,
                            float* sx, const GemmArgs& a, hipStream_t s) {
@@ -352,6 +596,8 @@ hipError_t gemv_dispatch(const GemmArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
+  if (dot_path_ok(a.M, a.K, a.packed, a.q))
+    return gemv_dot_launch<0>(a.q, nullptr, nullptr, const_cast<float*>(a.sx), a, s);
   if (lds_path_ok(a.M, a.K, a.packed, a.q))
     return gemv_lds_launch<0>(a.q, static_cast<int>(a.M), nullptr, nullptr,
                               const_cast<float*>(a.sx), a, s);
@@ -362,12 +608,14 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
 }
 
 bool fused_quant_gemv_ok(int64_t M, int64_t K, const void* packed, const void* X) {
-  return lds_path_ok(M, K, packed, X);
+  return dot_path_ok(M, K, packed, X) || lds_path_ok(M, K, packed, X);
 }
 
 hipError_t launch_quant_gemv(const void* X, int bf16, const ActParams& p, int8_t* q,
                              float* sx, const GemmArgs& a, hipStream_t s) {
   const int M = static_cast<int>(a.M);
+  if (dot_path_ok(a.M, a.K, a.packed, X))
+    return bf16 ? gemv_dot_launch<2>(X, &p, q, sx, a, s) : gemv_dot_launch<1>(X, &p, q, sx, a, s);
   return bf16 ? gemv_lds_launch<2>(X, M, &p, q, sx, a, s)
               : gemv_lds_launch<1>(X, M, &p, q, sx, a, s);
 }

@@ -37,6 +37,39 @@ __device__ inline int wave_isum(int v) {
   return v;
 }
 
+// Wave reductions through DPP row operations (no LDS round trips): pair and
+// quad swaps, half-row and row mirrors give every lane its 16-lane row's
+// value; row_bcast:15 and row_bcast:31 then fold rows 0..2 into row 3.  Only
+// lane 63 holds the wave's result.  Lanes a row_mask leaves out read the
+// identity 0, so the max form is for non-negative, non-NaN floats.
+template <int CTRL, int ROWS = 0xF>
+__device__ inline int dpp_get(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xF, false);
+}
+
+__device__ inline int wave_isum_last(int v) {
+  v += dpp_get<0xB1>(v);        // quad_perm 1,0,3,2
+  v += dpp_get<0x4E>(v);        // quad_perm 2,3,0,1
+  v += dpp_get<0x141>(v);       // row_half_mirror
+  v += dpp_get<0x140>(v);       // row_mirror
+  v += dpp_get<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_get<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
+// Non-negative, non-NaN floats order as their bit patterns, so their wave
+// max is an unsigned integer max.
+__device__ inline float wave_max_last(float v) {
+  uint32_t u = __float_as_uint(v);
+  u = max(u, static_cast<uint32_t>(dpp_get<0xB1>(static_cast<int>(u))));
+  u = max(u, static_cast<uint32_t>(dpp_get<0x4E>(static_cast<int>(u))));
+  u = max(u, static_cast<uint32_t>(dpp_get<0x141>(static_cast<int>(u))));
+  u = max(u, static_cast<uint32_t>(dpp_get<0x140>(static_cast<int>(u))));
+  u = max(u, static_cast<uint32_t>(dpp_get<0x142, 0xA>(static_cast<int>(u))));
+  u = max(u, static_cast<uint32_t>(dpp_get<0x143, 0xC>(static_cast<int>(u))));
+  return __uint_as_float(u);
+}
+
 // Block-wide sum / max for blockDim.x == NT (multiple of 64).  `scratch`
 // holds NT/64 entries.  Every thread gets the result.  The partials of the
 // waves are combined in wave order, so the result does not depend on timing.

@@ -506,6 +506,11 @@ FUSED_CASES = [
     (8, 100, 512, "bf16", "row"),        # M > 4: quantiser + general GEMV
     (1, 20, 68, "f32", "tensor"),        # K % 64 != 0: two launches
     (4, 64, 32768, "bf16", "tensor"),    # M*K beyond the LDS staging limit
+    (1, 70, 16384, "f32", "row"),        # row-per-wave kernel at its largest K
+    (1, 70, 8256, "bf16", "tensor"),     # row-per-wave kernel, a slice cut short by K
+    (4, 70, 16384, "f32", "row"),        # LDS-tiled kernel at its staging limit
+    (2, 90, 32768, "bf16", "row"),
+    (1, 9, 65536, "f32", "tensor"),
 ]
 
 
@@ -553,6 +558,22 @@ def test_quant_ternary_gemv_with_prologue_and_empty():
     Y0, q0, s0 = tq.tq_quant_ternary_gemv(dev(X), dev(packed), dev(scale), 0, 1024, "tensor")
     q1, s1 = tq.tq_quant_act_int8(dev(X))
     np.testing.assert_array_equal(host(q0), host(q1))
+
+
+@pytest.mark.parametrize("M,K", [(1, 16384), (1, 8256), (1, 4160), (1, 16448), (4, 16384),
+                                 (2, 32768), (1, 65536), (3, 192)])
+def test_gemv_kernel_boundaries(M, K):
+    # K and M*K at the limits that choose between the row-per-wave, LDS-tiled
+    # and general decode kernels; N not a multiple of any row tile
+    N = 37
+    q = ti.random_int8(11 + M + K, M, K)
+    w = ti.random_ternary(12 + K, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(N + 13, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(M + 14, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    say(f"gemv boundary M={M} K={K}")
+    _check_outputs(tq.tq_ternary_gemv, dev(q), dev(sx), dev(packed), dev(scale), N, K,
+                   "row", q, packed, scale, sx)
 
 
 def test_gemv_small_m_large_k_general_path():
