@@ -255,27 +255,30 @@ __device__ inline int swz(int row, int chunk) {
   return row * kBK + 16 * (chunk ^ (((row >> 1) ^ (row >> 4)) & 3));
 }
 
+// LDS bytes of one BM x BN tile: double-buffered activation and weight tiles.
+template <int BM, int BN>
+constexpr int fast_lds_bytes() { return 2 * (BM + BN) * kBK; }
+
+// One BM x BN output tile (tile coordinates tm, tn in units of BM, BN) by a
+// workgroup of WM x WN waves, staging through `lds`.
 template <int BM, int BN, int WM, int WN, int YT>
-__global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm_fast(
+__device__ __forceinline__ void gemm_fast_tile(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
-    int64_t N, int64_t K, void* __restrict__ Y) {
+    int64_t N, int64_t K, void* __restrict__ Y, int64_t tm, int64_t tn, uint8_t* lds) {
   constexpr int NT = WM * WN * kWave;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
   constexpr int CA = BM * (kBK / 16) / NT;  // 16-byte activation chunks per thread
   constexpr int CB = BN * (kBK / 16) / NT;  // packed words per thread
   static_assert(CA >= 1 && CB >= 1 && FM >= 1 && FN >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][BM * kBK];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][BN * kBK];
+  uint8_t* const As = lds;                  // [2][BM * kBK]
+  uint8_t* const Bs = lds + 2 * BM * kBK;   // [2][BN * kBK]
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int wm = wave / WN, wn = wave % WN;
-  const int64_t tiles_m = (M + BM - 1) / BM;
-  const int64_t tm = blockIdx.x % tiles_m;
-  const int64_t tn = blockIdx.x / tiles_m;
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t rowbytes = K >> 2;
   const int fr = lane & 31, kg = lane >> 5;
@@ -328,10 +331,10 @@ __global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm_fast(
   };
   auto store_stage = [&](int buf, ARegs& a, BRegs& b) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i) *reinterpret_cast<v4i*>(&As[buf][ast[i]]) = a[i];
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<v4i*>(&As[(buf) * (BM * kBK) + ast[i]]) = a[i];
 #pragma unroll
     for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<v4i*>(&Bs[buf][bst[i]]) = decode_signed_natural(b[i]);
+      *reinterpret_cast<v4i*>(&Bs[(buf) * (BN * kBK) + bst[i]]) = decode_signed_natural(b[i]);
   };
 
   v16i acc[FM][FN];
@@ -357,18 +360,18 @@ __global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm_fast(
     if (!GUARD || kt + 2 < nk) load_stage(kt + 2, a_far, b_far);
     v4i ac[FM], an[FM], bc[FN], bn[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) ac[i] = *reinterpret_cast<const v4i*>(&As[buf][ard[i][0]]);
+    for (int i = 0; i < FM; ++i) ac[i] = *reinterpret_cast<const v4i*>(&As[(buf) * (BM * kBK) + ard[i][0]]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bc[j] = *reinterpret_cast<const v4i*>(&Bs[buf][brd[j][0]]);
+    for (int j = 0; j < FN; ++j) bc[j] = *reinterpret_cast<const v4i*>(&Bs[(buf) * (BN * kBK) + brd[j][0]]);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       if (ks + 1 < kKS) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-          an[i] = *reinterpret_cast<const v4i*>(&As[buf][ard[i][ks + 1]]);
+          an[i] = *reinterpret_cast<const v4i*>(&As[(buf) * (BM * kBK) + ard[i][ks + 1]]);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          bn[j] = *reinterpret_cast<const v4i*>(&Bs[buf][brd[j][ks + 1]]);
+          bn[j] = *reinterpret_cast<const v4i*>(&Bs[(buf) * (BN * kBK) + brd[j][ks + 1]]);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -431,6 +434,17 @@ __global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm_fast(
       }
     }
   }
+}
+
+template <int BM, int BN, int WM, int WN, int YT>
+__global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm_fast(
+    const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
+    const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
+    int64_t N, int64_t K, void* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[fast_lds_bytes<BM, BN>()];
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  gemm_fast_tile<BM, BN, WM, WN, YT>(q, sx, M, packed, scale, per_row, N, K, Y,
+                                     blockIdx.x % tiles_m, blockIdx.x / tiles_m, lds);
 }
 
 template <int BM, int BN, int WM, int WN>

@@ -414,6 +414,20 @@ def test_gemm_awkward(M, N, K):
                        q, packed, sc, sx)
 
 
+@pytest.mark.parametrize("M,N,K", [(2048, 8960, 64), (512, 38400, 128), (2048, 8960, 192)])
+def test_gemm_multi_round(M, N, K):
+    # more 256x128 tiles than one round of resident workgroups, K from one
+    # to three 64-wide stages (the main loop's unguarded stages and its tail)
+    q = ti.random_int8(31 + K, M, K)
+    w = ti.random_ternary(32 + K, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(N + 33, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(M + 34, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    say(f"gemm multi-round M={M} N={N} K={K}")
+    _check_outputs(tq.tq_ternary_gemm, dev(q), dev(sx), dev(packed), dev(scale), N, K, "row",
+                   q, packed, scale, sx)
+
+
 def test_gemm_small_m_matches_gemv():
     for M in (1, 5, 16):
         q = ti.random_int8(M, M, 4096)
