@@ -17,7 +17,8 @@ time (GB/s).  ``roofline`` describes the GEMV kernel: its algorithmic bytes
 per launch over its average launch time, against 8 TB/s.  ``cpu_baseline``
 times the CPU oracle on a bounded sample of the same workload.  ``extra``
 carries the prefill GEMM (int8 MFMA TOPS), the BitLinear prologue, the FFN
-decode shapes and the pack kernel.
+decode shapes, the pack kernel and the steady-state GEMV rate (stacked
+projections in one launch).
 """
 from __future__ import annotations
 
@@ -47,7 +48,7 @@ def parse():
     p.add_argument("--no-extra", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--only", default="",
-                   help="comma list of extra workloads to run: prefill,bitlinear,pack,ffn,context")
+                   help="comma list of extra workloads to run: prefill,bitlinear,pack,ffn,steady,context")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (for counter scaling)")
     return p.parse_args()
@@ -240,6 +241,8 @@ def extras(torch, np, ti, tq, dev, only=frozenset()):
         out.update(extra_bitlinear(torch, ti, tq, dev))
     if want("ffn"):
         out.update(extra_ffn(torch, ti, tq, dev))
+    if want("steady"):
+        out.update(extra_steady(torch, ti, tq, dev))
     if want("context"):
         out.update(extra_context(torch, dev))
     torch.cuda.synchronize()
@@ -336,6 +339,35 @@ def extra_ffn(torch, ti, tq, dev):
         del pool
     out["ffn_gemv"] = ffn
     return out
+
+
+def extra_steady(torch, ti, tq, dev):
+    """Steady-state decode GEMV throughput, labelled as such: G stacked 4096x4096
+    projections that share one token (N = 4096*G rows), one launch each, the
+    stacked weights rotating over at least 512 MiB.  One 4 MiB launch is bound
+    by latency; this shows the rate once more bytes are in flight."""
+    K = 4096
+    W = torch.from_numpy(ti.workload_weights("decode", 0)).to(dev)
+    p0, s0 = tq.tq_pack_ternary(W, "tensor")
+    del W
+    X = torch.from_numpy(ti.workload_activations("decode", 0, 1)).to(dev).to(torch.bfloat16)
+    q, sx = tq.tq_quant_act_int8(X)
+    out = {}
+    for G in (8, 32):
+        N = 4096 * G
+        stacked = torch.cat([p0] * G, dim=0)
+        pool = [stacked.clone() for _ in range(max(2, 128 // G))]
+        del stacked
+        Y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        g = capture(torch, lambda: [tq.tq_ternary_gemv(q, sx, p, s0, N, K, "tensor", "f32", Y=Y)
+                                    for p in pool])
+        timed_graph(torch, g, 2)
+        t = timed_graph(torch, g, 8) / len(pool)
+        gb = gemv_bytes(1, N, K, False) / t / 1e9
+        out[f"stacked_{G}x4096x4096_b1"] = {"us": round(t * 1e6, 3), "GBs": round(gb, 1),
+                                             "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1)}
+        del pool
+    return {"gemv_steady_state": out}
 
 
 def extra_context(torch, dev):

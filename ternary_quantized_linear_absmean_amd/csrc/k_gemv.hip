@@ -405,8 +405,8 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const bool stager = wave < kStageWaves;
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * kRowsD + wave;
   const int rowbytes = K >> 2;
+  const int64_t nrg = (N + kRowsD - 1) / kRowsD;  // row groups, one per workgroup pass
   const int nquad = K >> 2;
 
   // 1. the staging waves' quads of the token (reads past K return zero)
@@ -417,18 +417,24 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
 #pragma unroll
     for (int i = 0; i < kRounds; ++i) rq[i] = load_quad<SRC>(xr, tid + kStageNT * i);
   }
-  // 2. the wave's row, chunk lane + 64*sl of each slice (rows >= N read zeros)
-  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(packed + (n < N ? n : 0) * rowbytes), static_cast<short>(0),
-      n < N ? rowbytes : 0, kBufRaw);
-  uint4 wv[S];
+  // 2. the wave's row in row group rg: chunk lane + 64*sl of each slice,
+  // and the row's scale.  Rows >= N (also whole groups past the end) read
+  // zeros, so the loads are never conditional.
+  auto load_row = [&](int64_t rg, uint4 (&w)[S]) -> float {
+    const int64_t n = rg * kRowsD + wave;
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(packed + (n < N ? n : 0) * rowbytes), static_cast<short>(0),
+        n < N ? rowbytes : 0, kBufRaw);
 #pragma unroll
-  for (int sl = 0; sl < S; ++sl)
-    wv[sl] = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + kWave * sl) * 16, 0, 0));
-  // 3. epilogue operands
-  const int64_t nr = n < N ? n : N - 1;
-  const float gam = ydt == TQ_I32 ? 0.f : scale[per_row ? nr : 0];
+    for (int sl = 0; sl < S; ++sl)
+      w[sl] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + kWave * sl) * 16, 0, 0));
+    return ydt == TQ_I32 ? 0.f : scale[per_row ? (n < N ? n : N - 1) : 0];
+  };
+  uint4 wa[S], wb[S];
+  int64_t rg = blockIdx.x;
+  float ga = load_row(rg, wa), gb = 0.f;
+  // 3. epilogue operand of the token
   const float sx_in = SRC == 0 ? sx_io[0] : 0.f;
 
   // 4. token scale (SRC != 0): staging-wave maxima, folded by each stager
@@ -490,49 +496,90 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
     bsum = wave_isum_last(bsum);
     if (lane == kWave - 1) wave_sum_part[wave] = bsum;
   }
-  asm volatile("" ::"v"(gam));
+  asm volatile("" ::"v"(ga));
   asm volatile("" ::"v"(sx_in));
   __syncthreads();
-
-  // 6. contraction of the wave's row
-  int acc = 0;
-#pragma unroll
-  for (int sl = 0; sl < S; ++sl) {
-    const int unit = 4 * (lane + kWave * sl);  // first 16-code unit of the chunk
-    if (16 * unit >= K) break;                  // this chunk, and every later one, is past K
-    const uint32_t words[4] = {wv[sl].x, wv[sl].y, wv[sl].z, wv[sl].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v4i cd = decode_codes_strided(words[j]);
-      const v4i x = *reinterpret_cast<const v4i*>(xt + dot_slot(unit + j));
-      acc = __builtin_amdgcn_sdot4(x.x, cd.x, acc, false);
-      acc = __builtin_amdgcn_sdot4(x.y, cd.y, acc, false);
-      acc = __builtin_amdgcn_sdot4(x.z, cd.z, acc, false);
-      acc = __builtin_amdgcn_sdot4(x.w, cd.w, acc, false);
-    }
-  }
-  acc = wave_isum_last(acc);
-  if (lane != kWave - 1 || n >= N) return;
   int tsum = 0;
 #pragma unroll
   for (int w = 0; w < kStageWaves; ++w) tsum += wave_sum_part[w];
-  const int accv = acc - tsum;
-  if (ydt == TQ_I32) {
-    static_cast<int*>(Y)[n] = accv;
-  } else {
-    const float sxv = SRC == 0 ? sx_in : tok_sx;
-    const float y = static_cast<float>(accv) * (gam * sxv);
-    if (ydt == TQ_F32)
-      static_cast<float*>(Y)[n] = y;
-    else
-      static_cast<uint16_t*>(Y)[n] = f32_to_bf16(y);
+  const float sxv = SRC == 0 ? sx_in : tok_sx;
+
+  // 6. contraction of the wave's row in group rg
+  auto finish = [&](int64_t rg, const uint4 (&w)[S], float gam) {
+    const int64_t n = rg * kRowsD + wave;
+    int acc = 0;
+#pragma unroll
+    for (int sl = 0; sl < S; ++sl) {
+      const int unit = 4 * (lane + kWave * sl);  // first 16-code unit of the chunk
+      if (16 * unit >= K) break;                  // this chunk, and every later one, is past K
+      const uint32_t words[4] = {w[sl].x, w[sl].y, w[sl].z, w[sl].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const v4i cd = decode_codes_strided(words[j]);
+        const v4i x = *reinterpret_cast<const v4i*>(xt + dot_slot(unit + j));
+        acc = __builtin_amdgcn_sdot4(x.x, cd.x, acc, false);
+        acc = __builtin_amdgcn_sdot4(x.y, cd.y, acc, false);
+        acc = __builtin_amdgcn_sdot4(x.z, cd.z, acc, false);
+        acc = __builtin_amdgcn_sdot4(x.w, cd.w, acc, false);
+      }
+    }
+    acc = wave_isum_last(acc);
+    if (lane != kWave - 1 || n >= N) return;
+    const int accv = acc - tsum;
+    if (ydt == TQ_I32) {
+      static_cast<int*>(Y)[n] = accv;
+    } else {
+      const float y = static_cast<float>(accv) * (gam * sxv);
+      if (ydt == TQ_F32)
+        static_cast<float*>(Y)[n] = y;
+      else
+        static_cast<uint16_t*>(Y)[n] = f32_to_bf16(y);
+    }
+  };
+  // Row groups rg, rg + gridDim.x, ...: the next group's row is loaded
+  // before the current one is contracted, alternating two named register
+  // sets so that no copy of a load in flight is needed.  The last group
+  // issues no load: a load past the end would still have to return before
+  // the wave may end.
+  const int64_t step = gridDim.x;
+  for (;;) {
+    if (rg + step >= nrg) {
+      finish(rg, wa, ga);
+      break;
+    }
+    gb = load_row(rg + step, wb);
+    finish(rg, wa, ga);
+    rg += step;
+    if (rg + step >= nrg) {
+      finish(rg, wb, gb);
+      break;
+    }
+    ga = load_row(rg + step, wa);
+    finish(rg, wb, gb);
+    rg += step;
   }
+}
+
+// Compute units of the current device (0 if the query fails), cached per
+// device.
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0 &&
+      hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus[dev] = 0;
+  return cus[dev];
 }
 
 template <int SRC, int S>
 hipError_t gemv_dot_launch_s(const void* src, const ActParams* p, int8_t* q_out, float* sx,
                              const GemmArgs& a, hipStream_t s) {
-  const int64_t grid = (a.N + kRowsD - 1) / kRowsD;
+  // one workgroup per row group up to two per compute unit (the resident
+  // limit of 1024-thread workgroups); past that, workgroups loop over groups
+  const int64_t groups = (a.N + kRowsD - 1) / kRowsD;
+  const int64_t cap = 2 * static_cast<int64_t>(device_cus() > 0 ? device_cus() : 256);
+  const int64_t grid = groups < cap ? groups : cap;
   const float eps = p ? p->eps : 0.f, lo = p ? p->eta_min : 0.f, hi = p ? p->eta_max : 0.f;
   const int clamp = p ? p->clamp : 0;
   hipLaunchKernelGGL((k_gemv_dot<SRC, S>), dim3(grid), dim3(kNTd), static_cast<size_t>(a.K), s,
