@@ -640,11 +640,265 @@ hipError_t gemv_dispatch(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------
+// 2..16 tokens on matrix cores (K % 256 == 0).  A workgroup owns 16 output
+// rows and W = min(16, K/256) waves; wave w takes the 256-code K blocks
+// w, w + W, ...  Per block a lane holds 16 packed bytes, 64 codes, of row
+// l % 16 at byte offset 16 * (l / 16) of the block (one 128-bit buffer load
+// per lane, rows past N read zeros).  Its four words feed four
+// v_mfma_i32_16x16x64_i8: in MFMA j, lane l's 16-slot group stands for the
+// codes 64 * (l / 16) + 16 * j + 0..15 of the block.  Because the dot product
+// is unchanged by any permutation of K applied to both operands, the token
+// fragment for that MFMA is the matching 16 token bytes, a contiguous
+// 16-byte read.  Weight words decode in 7 operations to codes 0..2 (the
+// strided order, matched by staging the tokens byte-transposed) plus 8 to
+// the signed values c - 1, so the accumulators are the exact int32 sums.
+// The workgroup stages the M int8 tokens once in LDS with a row pitch of
+// K + 16 bytes (lanes of a fragment read then fall in distinct banks); rows
+// M..15 of the MFMA read zeros.  The waves' 16 x 16 partial tiles are summed
+// through LDS and 256 threads apply the epilogue.
+constexpr int kMfmaRows = 16;
+constexpr int kMfmaMaxWaves = 16;
+
+// 16 consecutive token values in their storage type: int8 (one 16-byte
+// word), fp32 (four) or bf16 (two).
+template <int SRC>
+struct RawUnit {
+  static constexpr int kWords = SRC == 1 ? 4 : SRC == 2 ? 2 : 1;
+  v4i w[kWords];
+};
+
+template <int SRC>
+__device__ inline RawUnit<SRC> load_unit(__amdgpu_buffer_rsrc_t r, int c) {
+  RawUnit<SRC> u;
+#pragma unroll
+  for (int i = 0; i < RawUnit<SRC>::kWords; ++i)
+    u.w[i] = __builtin_bit_cast(
+        v4i, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * (RawUnit<SRC>::kWords * c + i), 0, 0));
+  return u;
+}
+
+template <int SRC>
+__device__ inline void unit_to_f32(const RawUnit<SRC>& u, float (&v)[16]) {
+#pragma unroll
+  for (int i = 0; i < RawUnit<SRC>::kWords; ++i) {
+    const uint32_t w[4] = {static_cast<uint32_t>(u.w[i].x), static_cast<uint32_t>(u.w[i].y),
+                           static_cast<uint32_t>(u.w[i].z), static_cast<uint32_t>(u.w[i].w)};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (SRC == 1) {
+        v[4 * i + k] = __uint_as_float(w[k]);
+      } else {
+        v[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+        v[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+    }
+  }
+}
+
+template <int SRC, int KBW>
+__global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
+    const void* __restrict__ src, float eps, int clamp, float lo, float hi,
+    int8_t* __restrict__ q_out, float* __restrict__ sx_io, int M,
+    const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
+    int64_t N, int K, void* __restrict__ Y, int ydt) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // M x (K + 16) bytes
+  __shared__ uint32_t tok_max[kMfmaRows];
+  __shared__ float tok_sc[kMfmaRows];  // 127 / eta
+  __shared__ float tok_sx[kMfmaRows];  // eta / 127
+  constexpr int kEl = SRC == 1 ? 4 : SRC == 2 ? 2 : 1;
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int nw = blockDim.x / kWave;
+  const int nt = blockDim.x;
+  const int pitch = K + 16;
+  const int upr = K >> 4;          // 16-value units per token
+  const int nkb = K >> 8;          // 256-code blocks
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kMfmaRows;
+  const int rowbytes = K >> 2;
+
+  // 1. the thread's first token unit (a read past the end returns zero),
+  // then its weight blocks
+  const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(src), static_cast<short>(0), M * K * kEl, kBufRaw);
+  const int nunits = M * upr;
+  const RawUnit<SRC> u0 = load_unit<SRC>(qr, tid);
+  const int64_t rows_here = N - n0 < kMfmaRows ? N - n0 : kMfmaRows;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed + n0 * rowbytes), static_cast<short>(0),
+      static_cast<int>(rows_here * rowbytes), kBufRaw);
+  const int fr = lane & 15, fg = lane >> 4;
+  uint4 wv[KBW];
+#pragma unroll
+  for (int i = 0; i < KBW; ++i) {
+    const int kb = wave + nw * i;  // blocks past the end read zeros and are skipped
+    wv[i] = __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                   wr, fr * rowbytes + 64 * (kb < nkb ? kb : 0) + 16 * fg, 0, 0));
+  }
+  // epilogue operands of the thread's output (token m, row n0 + n)
+  const int em = tid >> 4, en = tid & 15;
+  const bool eout = tid < kMfmaRows * kMfmaRows && em < M && n0 + en < N;
+  float egam = 0.f, esx = 0.f;
+  if (eout && ydt != TQ_I32) {
+    egam = scale[per_row ? n0 + en : 0];
+    if (SRC == 0) esx = sx_io[em];
+  }
+
+  // 2. (fp32 / bf16 tokens) per-token absmax and scale, as k_quant_plain
+  if (SRC != 0) {
+    if (tid < kMfmaRows) tok_max[tid] = 0u;
+    __syncthreads();
+    auto unit_max = [&](const RawUnit<SRC>& u, int c) {
+      float v[16];
+      unit_to_f32<SRC>(u, v);
+      float mx = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(v[i]));
+      atomicMax(&tok_max[c / upr], __float_as_uint(mx));
+    };
+    if (tid < nunits) unit_max(u0, tid);
+    for (int c = tid + nt; c < nunits; c += nt) unit_max(load_unit<SRC>(qr, c), c);
+    __syncthreads();
+    if (tid < M) {
+      float eta = fmaxf(__uint_as_float(tok_max[tid]), eps);
+      if (clamp) eta = fminf(fmaxf(eta, lo), hi);
+      tok_sc[tid] = 127.f / eta;
+      const float sxv = eta / 127.f;
+      tok_sx[tid] = sxv;
+      if (blockIdx.x == 0) sx_io[tid] = sxv;
+    }
+    __syncthreads();
+  }
+  // 3. int8 tokens -> LDS, each 16-byte unit byte-transposed
+  auto stage = [&](const RawUnit<SRC>& u, int c) {
+    const int m = c / upr, uu = c - m * upr;
+    uint32_t d[4];
+    if (SRC == 0) {
+      d[0] = u.w[0].x; d[1] = u.w[0].y; d[2] = u.w[0].z; d[3] = u.w[0].w;
+    } else {
+      float v[16];
+      unit_to_f32<SRC>(u, v);
+      const float sc = tok_sc[m];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        d[b] = quant_byte(v[4 * b], sc) | (quant_byte(v[4 * b + 1], sc) << 8) |
+               (quant_byte(v[4 * b + 2], sc) << 16) | (quant_byte(v[4 * b + 3], sc) << 24);
+      if (blockIdx.x == 0)
+        *reinterpret_cast<uint4*>(q_out + 16 * static_cast<int64_t>(c)) =
+            make_uint4(d[0], d[1], d[2], d[3]);
+    }
+    *reinterpret_cast<v4i*>(xs + m * pitch + 16 * uu) = transpose_bytes4x4(d[0], d[1], d[2], d[3]);
+  };
+  if (tid < nunits) stage(u0, tid);
+  for (int c = tid + nt; c < nunits; c += nt) stage(load_unit<SRC>(qr, c), c);
+  __syncthreads();
+  if (SRC != 0 && eout) esx = tok_sx[em];
+
+  // 4. contraction of the wave's blocks
+  v4i acc = {0, 0, 0, 0};
+  const bool arow = fr < M;
+  const uint8_t* abase = xs + (arow ? fr : 0) * pitch + 64 * fg;
+#pragma unroll
+  for (int i = 0; i < KBW; ++i) {
+    const int kb = wave + nw * i;
+    if (kb >= nkb) break;
+    const uint32_t words[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const v4i c = decode_codes_strided(words[j]);
+      v4i b;
+      b.x = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.x)));
+      b.y = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.y)));
+      b.z = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.z)));
+      b.w = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.w)));
+      v4i a = *reinterpret_cast<const v4i*>(abase + 256 * kb + 16 * j);
+      if (!arow) a = v4i{0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+    }
+  }
+  __syncthreads();  // every wave is done with the tokens: reuse LDS
+
+  // 5. sum the waves' tiles; D layout: lane l holds rows 4 * (l / 16) + i,
+  // column l % 16
+  int* red = reinterpret_cast<int*>(xs);  // [nw][16 x 16]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[wave * 256 + (4 * fg + i) * 16 + fr] = acc[i];
+  __syncthreads();
+  if (!eout) return;
+  int tot = 0;
+  for (int w = 0; w < nw; ++w) tot += red[w * 256 + tid];
+  const int64_t o = static_cast<int64_t>(em) * N + n0 + en;
+  if (ydt == TQ_I32) {
+    static_cast<int*>(Y)[o] = tot;
+  } else {
+    const float y = static_cast<float>(tot) * (egam * esx);
+    if (ydt == TQ_F32)
+      static_cast<float*>(Y)[o] = y;
+    else
+      static_cast<uint16_t*>(Y)[o] = f32_to_bf16(y);
+  }
+}
+
+constexpr int64_t kMfmaLdsMax = 120 * 1024;
+
+int64_t mfma_lds_bytes(int64_t M, int64_t K) {
+  const int64_t stage = M * (K + 16);
+  const int64_t red = static_cast<int64_t>(kMfmaMaxWaves) * 256 * 4;
+  return stage > red ? stage : red;
+}
+
+bool mfma_path_ok(int64_t M, int64_t K, const void* packed, const void* act) {
+  return M >= 2 && M <= 16 && (K % 256) == 0 && K <= 16384 &&
+         mfma_lds_bytes(M, K) <= kMfmaLdsMax &&
+         (reinterpret_cast<uintptr_t>(packed) & 15u) == 0u &&
+         (reinterpret_cast<uintptr_t>(act) & 15u) == 0u;
+}
+
+template <int SRC, int KBW>
+hipError_t gemv_mfma_launch_k(const void* src, const ActParams* p, int8_t* q_out, float* sx,
+                              const GemmArgs& a, int waves, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(mfma_lds_bytes(a.M, a.K));
+  // allow the kernel more than 64 KiB of dynamic LDS, once per device
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_mfma<SRC, KBW>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(kMfmaLdsMax));
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) attr_set[dev] = true;
+  }
+  const int64_t grid = (a.N + kMfmaRows - 1) / kMfmaRows;
+  const float eps = p ? p->eps : 0.f, lo = p ? p->eta_min : 0.f, hi = p ? p->eta_max : 0.f;
+  const int clamp = p ? p->clamp : 0;
+  hipLaunchKernelGGL((k_gemv_mfma<SRC, KBW>), dim3(grid), dim3(waves * kWave), lds, s, src, eps,
+                     clamp, lo, hi, q_out, sx, static_cast<int>(a.M), a.packed, a.scale,
+                     a.per_row, a.N, static_cast<int>(a.K), a.Y, a.ydt);
+  return hipGetLastError();
+}
+
+template <int SRC>
+hipError_t gemv_mfma_launch(const void* src, const ActParams* p, int8_t* q_out, float* sx,
+                            const GemmArgs& a, hipStream_t s) {
+  const int64_t nkb = a.K / 256;
+  const int waves = static_cast<int>(nkb < kMfmaMaxWaves ? nkb : kMfmaMaxWaves);
+  const int64_t per = (nkb + waves - 1) / waves;  // blocks per wave
+  if (per <= 1) return gemv_mfma_launch_k<SRC, 1>(src, p, q_out, sx, a, waves, s);
+  if (per <= 2) return gemv_mfma_launch_k<SRC, 2>(src, p, q_out, sx, a, waves, s);
+  return gemv_mfma_launch_k<SRC, 4>(src, p, q_out, sx, a, waves, s);
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
   if (dot_path_ok(a.M, a.K, a.packed, a.q))
     return gemv_dot_launch<0>(a.q, nullptr, nullptr, const_cast<float*>(a.sx), a, s);
+  if (mfma_path_ok(a.M, a.K, a.packed, a.q))
+    return gemv_mfma_launch<0>(a.q, nullptr, nullptr, const_cast<float*>(a.sx), a, s);
   if (lds_path_ok(a.M, a.K, a.packed, a.q))
     return gemv_lds_launch<0>(a.q, static_cast<int>(a.M), nullptr, nullptr,
                               const_cast<float*>(a.sx), a, s);
@@ -654,8 +908,13 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
   return aligned ? gemv_dispatch<true>(a, s) : gemv_dispatch<false>(a, s);
 }
 
+// Fusing the quantiser costs every workgroup the whole token work, which
+// beyond four tokens is more than a separate quantiser launch.
+constexpr int64_t kFusedMfmaMaxM = 4;
+
 bool fused_quant_gemv_ok(int64_t M, int64_t K, const void* packed, const void* X) {
-  return dot_path_ok(M, K, packed, X) || lds_path_ok(M, K, packed, X);
+  return dot_path_ok(M, K, packed, X) ||
+         (M <= kFusedMfmaMaxM && mfma_path_ok(M, K, packed, X)) || lds_path_ok(M, K, packed, X);
 }
 
 hipError_t launch_quant_gemv(const void* X, int bf16, const ActParams& p, int8_t* q,
@@ -663,6 +922,8 @@ hipError_t launch_quant_gemv(const void* X, int bf16, const ActParams& p, int8_t
   const int M = static_cast<int>(a.M);
   if (dot_path_ok(a.M, a.K, a.packed, X))
     return bf16 ? gemv_dot_launch<2>(X, &p, q, sx, a, s) : gemv_dot_launch<1>(X, &p, q, sx, a, s);
+  if (a.M <= kFusedMfmaMaxM && mfma_path_ok(a.M, a.K, a.packed, X))
+    return bf16 ? gemv_mfma_launch<2>(X, &p, q, sx, a, s) : gemv_mfma_launch<1>(X, &p, q, sx, a, s);
   return bf16 ? gemv_lds_launch<2>(X, M, &p, q, sx, a, s)
               : gemv_lds_launch<1>(X, M, &p, q, sx, a, s);
 }

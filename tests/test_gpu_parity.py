@@ -522,7 +522,10 @@ FUSED_CASES = [
     (4, 64, 32768, "bf16", "tensor"),    # M*K beyond the LDS staging limit
     (1, 70, 16384, "f32", "row"),        # row-per-wave kernel at its largest K
     (1, 70, 8256, "bf16", "tensor"),     # row-per-wave kernel, a slice cut short by K
-    (4, 70, 16384, "f32", "row"),        # LDS-tiled kernel at its staging limit
+    (4, 70, 16384, "f32", "row"),        # matrix-core kernel, four blocks per wave
+    (3, 45, 6912, "bf16", "row"),        # matrix-core kernel, two blocks per wave
+    (4, 19, 256, "bf16", "tensor"),      # matrix-core kernel, one wave
+    (16, 30, 2560, "f32", "row"),        # past four tokens: quantiser + GEMV
     (2, 90, 32768, "bf16", "row"),
     (1, 9, 65536, "f32", "tensor"),
 ]
@@ -588,6 +591,23 @@ def test_gemv_kernel_boundaries(M, K):
     say(f"gemv boundary M={M} K={K}")
     _check_outputs(tq.tq_ternary_gemv, dev(q), dev(sx), dev(packed), dev(scale), N, K,
                    "row", q, packed, scale, sx)
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 19, 256), (5, 70, 16384), (16, 37, 6912), (16, 40, 7424),
+                                   (16, 21, 7680), (9, 33, 4096)])
+def test_gemv_matrix_core_boundaries(M, N, K):
+    # 2..16 tokens on matrix cores: one wave (K = 256), four blocks per wave
+    # (K = 16384), token staging above 64 KiB of LDS up to its 120 KiB limit,
+    # and one step past it (K = 7680 at 16 tokens, another kernel)
+    q = ti.random_int8(41 + M + K, M, K)
+    w = ti.random_ternary(42 + K, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(N + 43, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(M + 44, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    say(f"gemv matrix cores M={M} N={N} K={K}")
+    for gran, sc in (("row", scale), ("tensor", scale[:1])):
+        _check_outputs(tq.tq_ternary_gemv, dev(q), dev(sx), dev(packed), dev(sc), N, K, gran,
+                       q, packed, sc, sx)
 
 
 def test_gemv_small_m_large_k_general_path():
