@@ -11,4 +11,6 @@ from .tq_oracle import (absmean_scale, absmean_scales, binarize, contract,
                         packed_bytes, quant_act_int8, rms_factor,
                         rmsnorm_fwht_quant, rmsnorm_fwht_quant_literal,
                         round_rational_to_f32, ternarize, ternary_linear,
-                        unpack_codes, bf16_round_from_f64, FWHT_NORM)
+                        unpack_codes, bf16_round_from_f64, FWHT_NORM,
+                        packed1_bytes, pack_signs, unpack_signs, pack_binary1,
+                        contract_signs)

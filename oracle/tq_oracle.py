@@ -19,7 +19,8 @@ Sources (cited by page title and section):
   ``ternarize_weight`` (per-output-row absmean), ``additive_ternary_linear_int8``
   (y[o] = sum of x where W=+1 minus sum of x where W=-1).
 * qste 0.1.1 project description -- "What it costs and what it buys"
-  (binary +-1 weights with a per-row scale).
+  (binary +-1 weights with a per-row scale, deployed as R*C/8 bytes of
+  packed signs plus 4*R bytes of scales).
 
 Readings taken where the pages are silent or disagree (each is also listed
 in the design notes):
@@ -37,6 +38,9 @@ in the design notes):
   the dequantisation scale returned is sx = fp32(eta/127).
 * A partial last byte (only possible when the element count is not a multiple
   of four) is padded with the zero code 0b01.
+* 1-bit sign packing of binary weights (qste "What it costs and what it
+  buys" gives the size, not the layout): eight signs per byte, LSB-first,
+  bit 1 for +1 and bit 0 for -1, rows of K/8 bytes along K.
 * The fused RMSNorm -> FWHT -> int8 prologue uses the exact cancellation of
   the positive per-token RMS factor and the 1/sqrt(512) normaliser inside
   absmax quantisation (see ``rmsnorm_fwht_quant``).
@@ -222,6 +226,64 @@ def pack_ternary(W: np.ndarray, granularity: str = "tensor", mode: str = "ternar
     else:
         raise ValueError(mode)
     return pack_codes(q), gam
+
+
+def packed1_bytes(numel: int) -> int:
+    """Bytes of a 1-bit sign-packed tensor: (numel + 7) / 8, rounded down
+    (qste "What it costs and what it buys": R*C/8 bytes of packed signs)."""
+    if numel < 0:
+        raise ValueError("numel must be >= 0")
+    return (numel + 7) // 8
+
+
+def pack_signs(b: np.ndarray) -> np.ndarray:
+    """Pack +-1 values along the last axis, eight per byte, LSB-first, bit 1
+    for +1 and bit 0 for -1.  Rows must be a whole number of bytes."""
+    b = np.asarray(b)
+    if b.ndim == 1:
+        b = b.reshape(1, -1)
+    n, k = b.shape
+    if k % 8:
+        raise ValueError("row length must be a multiple of 8")
+    if b.size and not np.all((b == 1) | (b == -1)):
+        raise ValueError("values outside {-1, +1}")
+    bits = (b == 1).astype(np.uint8).reshape(n, k // 8, 8)
+    out = np.zeros((n, k // 8), dtype=np.uint8)
+    for slot in range(8):
+        out |= bits[:, :, slot] << np.uint8(slot)
+    return out
+
+
+def unpack_signs(packed: np.ndarray, k: int) -> np.ndarray:
+    """Inverse of ``pack_signs`` for rows of k values -> int8 +-1."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    if packed.ndim == 1:
+        packed = packed.reshape(1, -1)
+    n, nb = packed.shape
+    if k % 8 or nb != k // 8:
+        raise ValueError("row length does not match k")
+    bits = np.empty((n, nb, 8), dtype=np.int8)
+    for slot in range(8):
+        bits[:, :, slot] = (packed >> np.uint8(slot)) & np.uint8(1)
+    return (2 * bits.reshape(n, k) - 1).astype(np.int8)
+
+
+def pack_binary1(W: np.ndarray, granularity: str = "row"):
+    """Binary weights in 1-bit form: absmean scale(s) (the same rule as the
+    ternary scale), signs (+1 where w >= 0) packed eight per byte.  Returns
+    (packed uint8 [N, K/8], scales fp32 [1] or [N])."""
+    W = np.asarray(W, dtype=np.float32)
+    return pack_signs(binarize(W)), absmean_scales(W, granularity)
+
+
+def contract_signs(q: np.ndarray, packed: np.ndarray, k: int) -> np.ndarray:
+    """acc[m, o] = sum_k q[m, k] * b[o, k] over the unpacked +-1 weights, in
+    int64, checked to fit int32."""
+    b = unpack_signs(packed, k).astype(np.int64)
+    acc = np.asarray(q, dtype=np.int64) @ b.T
+    if acc.size and (acc.max() > 2**31 - 1 or acc.min() < -2**31):
+        raise OverflowError("accumulator exceeds int32")
+    return acc
 
 
 # --------------------------------------------------------------------------

@@ -547,3 +547,61 @@ def test_prologue_rmsnorm_only_codes_equal_plain():
     x64 = X.astype(np.float64)
     r = 1 / np.sqrt(np.mean(x64 * x64, axis=1) + 1e-6)
     np.testing.assert_allclose(sxe, r * np.max(np.abs(x64), axis=1) / 127, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- 1-bit signs
+
+def test_sign_pack_golden_sizes_and_bytes():
+    for a, b in _golden("sign_pack.txt"):
+        kind, *vals = a.split()
+        if kind == "size":
+            R, C = int(vals[0]), int(vals[1])
+            nbytes, sbytes, mb, ratio = b.split()
+            packed = oracle.packed1_bytes(R * C)
+            assert packed == int(nbytes) == R * C // 8
+            assert 4 * R == int(sbytes)
+            assert f"{(packed + 4 * R) / 1e6:.2f}" == mb
+            assert f"{4 * R * C / (packed + 4 * R):.1f}" == ratio
+        else:
+            v = np.array([int(x) for x in vals], dtype=np.int8)
+            assert int(oracle.pack_signs(v)[0, 0]) == int(b, 16)
+
+
+def test_sign_pack_roundtrip_and_rejects():
+    rng = np.random.default_rng(5)
+    b = np.where(rng.random((7, 64)) < 0.5, 1, -1).astype(np.int8)
+    assert np.array_equal(oracle.unpack_signs(oracle.pack_signs(b), 64), b)
+    with pytest.raises(ValueError):
+        oracle.pack_signs(np.ones((1, 12), np.int8))
+    with pytest.raises(ValueError):
+        oracle.pack_signs(np.zeros((1, 8), np.int8))
+
+
+def test_binary1_agrees_with_two_bit_binary():
+    # the same binary weights and scales as the 2-bit binary mode, only the
+    # storage differs
+    W = ti.normal_weights(77, 24, 96)
+    W[0, :5] = 0.0
+    W[1, 3] = -0.0
+    p1, s1 = oracle.pack_binary1(W, "row")
+    p2, s2 = oracle.pack_ternary(W, "row", mode="binary")
+    assert np.array_equal(oracle.unpack_signs(p1, 96), oracle.unpack_codes(p2, 96))
+    assert np.array_equal(s1.view(np.uint32), s2.view(np.uint32))
+    assert oracle.unpack_signs(p1, 96)[0, :5].tolist() == [1] * 5   # sign(0) -> +1
+    assert oracle.unpack_signs(p1, 96)[1, 3] == 1                   # -0.0 -> +1
+
+
+def test_contract_signs_brute_force_and_identity():
+    rng = np.random.default_rng(6)
+    M, N, K = 3, 5, 40
+    q = rng.integers(-127, 128, (M, K)).astype(np.int8)
+    b = np.where(rng.random((N, K)) < 0.5, 1, -1).astype(np.int8)
+    acc = oracle.contract_signs(q, oracle.pack_signs(b), K)
+    for m in range(M):
+        for o in range(N):
+            ref = 0
+            for k in range(K):
+                ref += int(q[m, k]) * int(b[o, k])
+            assert acc[m, o] == ref
+            plus = sum(int(q[m, k]) for k in range(K) if b[o, k] == 1)
+            assert acc[m, o] == 2 * plus - int(q[m].astype(np.int64).sum())
