@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--no-extra", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--only", default="",
-                   help="comma list of extra workloads to run: prefill,bitlinear,pack,ffn,steady,context")
+                   help="comma list of extra workloads to run: "
+                        "prefill,bitlinear,pack,ffn,steady,binary1,context")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (for counter scaling)")
     return p.parse_args()
@@ -243,6 +244,8 @@ def extras(torch, np, ti, tq, dev, only=frozenset()):
         out.update(extra_ffn(torch, ti, tq, dev))
     if want("steady"):
         out.update(extra_steady(torch, ti, tq, dev))
+    if want("binary1"):
+        out.update(extra_binary1(torch, ti, tq, dev))
     if want("context"):
         out.update(extra_context(torch, dev))
     torch.cuda.synchronize()
@@ -368,6 +371,36 @@ def extra_steady(torch, ti, tq, dev):
                                              "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1)}
         del pool
     return {"gemv_steady_state": out}
+
+
+def extra_binary1(torch, ti, tq, dev):
+    """1-bit sign-packed binary weights (R*C/8 bytes) against the same binary
+    weights in the 2-bit code format, decode GEMV 4096x4096 per-row scales,
+    1 and 16 tokens, the packed weights rotating over 512 MiB per form."""
+    N = K = 4096
+    W = torch.from_numpy(ti.workload_weights("bitlinear", 0)).to(dev)
+    p1, s1 = tq.tq_pack_binary1(W, "row")
+    p2, s2 = tq.tq_pack_ternary(W, "row", "binary")
+    del W
+    out = {}
+    for b in (1, 16):
+        X = torch.from_numpy(ti.workload_activations("bitlinear", 0, b)[:b]).to(dev)
+        q, sx = tq.tq_quant_act_int8(X)
+        Y = torch.empty((b, N), dtype=torch.float32, device=dev)
+        for name, fn, p0, s0, wbytes in (
+                ("1bit", tq.tq_binary1_gemv, p1, s1, N * K // 8),
+                ("2bit", tq.tq_ternary_gemv, p2, s2, N * K // 4)):
+            pool = [p0.clone() for _ in range(max(2, (512 << 20) // wbytes))]
+            g = capture(torch, lambda: [fn(q, sx, p, s0, N, K, "row", "f32", Y=Y) for p in pool])
+            timed_graph(torch, g, 2)
+            t = timed_graph(torch, g, 8) / len(pool)
+            nbytes = wbytes + 4 * N + b * K + 4 * b + 4 * b * N
+            gb = nbytes / t / 1e9
+            out[f"{name}_4096x4096_b{b}"] = {"us": round(t * 1e6, 3), "bytes": nbytes,
+                                             "GBs": round(gb, 1),
+                                             "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1)}
+            del pool
+    return {"binary_gemv": out}
 
 
 def extra_context(torch, dev):

@@ -179,10 +179,11 @@ tq_status tq_ternary_gemm(const int8_t* q, const float* sx, int64_t M,
  * fusion; s.7 GEMV).  The results -- q, sx and Y -- are bit for bit those of
  * tq_quant_act_int8(X, xdt, M, K, opts, q, sx) followed by
  * tq_ternary_gemv(q, sx, M, packed, scale, g, N, K, Y, ydt).
- * With the plain quantiser (no RMSNorm / FWHT), M <= 4, K % 64 == 0,
- * M*K <= 65536 and 16-byte aligned X and packed, this is a single kernel
- * launch: every workgroup quantises the tokens itself into LDS and
- * workgroup 0 writes q and sx; otherwise it is the two launches.
+ * With the plain quantiser (no RMSNorm / FWHT), M <= 4, K % 64 == 0 and
+ * 16-byte aligned X and packed, most shapes run as a single kernel launch:
+ * every workgroup quantises the tokens itself into LDS and workgroup 0
+ * writes q and sx.  Otherwise (M > 4, a prologue, other shapes) it is the
+ * two launches.  The results do not depend on which.
  *   X [M, K] fp32/bf16; q [M, K] int8 and sx [M] fp32 are outputs (required);
  *   packed, scale, g, N, K, Y, ydt as for tq_ternary_gemv.
  * Errors: those of the two calls; M > 16 is TQ_ERR_SHAPE. */
@@ -191,6 +192,41 @@ tq_status tq_quant_ternary_gemv(const void* X, tq_dtype xdt, int64_t M,
                                 const float* scale, tq_gran g, int64_t N, int64_t K,
                                 int8_t* q, float* sx, void* Y, tq_dtype ydt,
                                 hipStream_t stream);
+
+/* ---- 1-bit sign-packed binary weights ------------------------------------
+ * (qste 0.1.1 project description, "What it costs and what it buys": a
+ * binary matrix of +-1 with a per-row scale is deployed as R*C/8 bytes of
+ * packed signs plus 4*R bytes of scales.)  The pages give the size, not the
+ * bit layout; this library packs eight signs per byte, LSB-first, bit 1 for
+ * +1 and bit 0 for -1, rows of K/8 bytes along K. */
+
+/* Bytes of a 1-bit sign-packed tensor of numel values: (numel + 7) / 8
+ * (0 for numel <= 0). */
+size_t tq_packed1_bytes(int64_t numel);
+
+/* Binarize W (+1 where w >= 0, -0.0 and 0 included, else -1) with the
+ * absmean scale of tq_pack_ternary (same exact-mean rule, per tensor or per
+ * row) and pack the signs.
+ *   W       [N, K] fp32, 4-byte aligned, K % 8 == 0.
+ *   packed  [N, K/8] bytes (output).
+ *   scale   fp32 output, [1] (TQ_PER_TENSOR) or [N] (TQ_PER_ROW).
+ *   ws      as for tq_pack_ternary (tq_pack_workspace_bytes(N, K, g) bytes).
+ * Errors: those of tq_pack_ternary; K % 8 != 0 is TQ_ERR_SHAPE. */
+tq_status tq_pack_binary1(const float* W, int64_t N, int64_t K, tq_gran g,
+                          uint8_t* packed, float* scale, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* tq_ternary_gemv for 1-bit sign-packed weights: acc[m, o] = sum_k q[m, k] *
+ * b[o, k] with b = +-1 from packed [N, K/8], exact in int32, then
+ * y = acc * gamma_o * sx_m as tq_ternary_gemv.  1 <= M <= 16, K % 8 == 0.
+ * One token with K % 64 == 0 (K <= 16384) and 2..16 tokens with
+ * K % 256 == 0 run on the fast kernels when q and packed are 16-byte
+ * aligned; other shapes on a simple kernel.  Same inputs, outputs and errors
+ * as tq_ternary_gemv; K % 8 != 0 is TQ_ERR_SHAPE. */
+tq_status tq_binary1_gemv(const int8_t* q, const float* sx, int64_t M,
+                          const uint8_t* packed, const float* scale, tq_gran g,
+                          int64_t N, int64_t K, void* Y, tq_dtype ydt,
+                          hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* tq_status_str(tq_status s);

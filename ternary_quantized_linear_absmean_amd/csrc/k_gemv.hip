@@ -389,7 +389,13 @@ __device__ inline void quad_to_f32(const RawQuad<SRC>& r, float (&v)[4]) {
 // or 16 consecutive lanes over distinct bank groups.
 __device__ inline int dot_slot(int u) { return (u ^ (((u >> 3) ^ (u >> 4)) & 3)) * 16; }
 
-template <int SRC, int S>
+// BITS 2: ternary codes, 64 per 16-byte lane chunk.  BITS 1: the signs of
+// binary weights, 64 per 8-byte lane chunk (one 64-bit load), so a slice is
+// 4096 codes for both widths; each packed word decodes to eight words of 0/1
+// bytes, (w >> s) & 0x01010101 holding the signs of codes 8b + s, the token
+// is staged as the matching 8 x 4 byte transpose of each 32-value group, and
+// sum_k q*(2b - 1) = 2 * sum_k q*b - sum_k q.
+template <int SRC, int S, int BITS>
 __global__ __launch_bounds__(kNTd) void k_gemv_dot(
     const void* __restrict__ src, float eps, int clamp, float lo, float hi,
     int8_t* __restrict__ q_out, float* __restrict__ sx_io,
@@ -399,13 +405,15 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   __shared__ float wave_max_part[kStageWaves];
   __shared__ int wave_sum_part[kStageWaves];
   __shared__ float tok_sx;
-  constexpr int kRounds = S * 4096 / 4 / kStageNT;  // quads per staging lane
+  // S: K <= 4096 * S, one 4096-code slice of the 64 lanes' chunks each
+  constexpr int kRounds = S * 4096 / 4 / kStageNT;    // quads per staging lane
+  constexpr int kSl = S;                              // weight slices
   constexpr int kEl = SRC == 1 ? 4 : SRC == 2 ? 2 : 1;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const bool stager = wave < kStageWaves;
-  const int rowbytes = K >> 2;
+  const int rowbytes = BITS == 2 ? K >> 2 : K >> 3;
   const int64_t nrg = (N + kRowsD - 1) / kRowsD;  // row groups, one per workgroup pass
   const int nquad = K >> 2;
 
@@ -420,18 +428,26 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   // 2. the wave's row in row group rg: chunk lane + 64*sl of each slice,
   // and the row's scale.  Rows >= N (also whole groups past the end) read
   // zeros, so the loads are never conditional.
-  auto load_row = [&](int64_t rg, uint4 (&w)[S]) -> float {
+  auto load_row = [&](int64_t rg, uint4 (&w)[kSl]) -> float {
     const int64_t n = rg * kRowsD + wave;
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(packed + (n < N ? n : 0) * rowbytes), static_cast<short>(0),
         n < N ? rowbytes : 0, kBufRaw);
 #pragma unroll
-    for (int sl = 0; sl < S; ++sl)
-      w[sl] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + kWave * sl) * 16, 0, 0));
+    for (int sl = 0; sl < kSl; ++sl) {
+      if (BITS == 2) {
+        w[sl] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + kWave * sl) * 16, 0, 0));
+      } else {
+        typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+        const u2 v = __builtin_bit_cast(
+            u2, __builtin_amdgcn_raw_buffer_load_b64(wr, (lane + kWave * sl) * 8, 0, 0));
+        w[sl] = make_uint4(v.x, v.y, 0u, 0u);
+      }
+    }
     return ydt == TQ_I32 ? 0.f : scale[per_row ? (n < N ? n : N - 1) : 0];
   };
-  uint4 wa[S], wb[S];
+  uint4 wa[kSl], wb[kSl];
   int64_t rg = blockIdx.x;
   float ga = load_row(rg, wa), gb = 0.f;
   // 3. epilogue operand of the token
@@ -483,9 +499,12 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
               (quant_byte(v[2], sc) << 16) | (quant_byte(v[3], sc) << 24);
           if (blockIdx.x == 0) reinterpret_cast<uint32_t*>(q_out)[qi] = d;
         }
-        // quad qi is word b = qi % 4 of unit qi / 4; its byte s goes to
-        // byte b of word s of the transposed unit
-        uint8_t* dst = xt + dot_slot(qi >> 2) + (qi & 3);
+        // BITS 2: quad qi is word b = qi % 4 of unit qi / 4; its byte s goes
+        // to byte b of word s of the transposed unit.  BITS 1: value
+        // v = 4 qi + s of group v / 32 goes to byte (v % 32) / 8 of word v % 8
+        // of the group's two units.
+        uint8_t* dst = BITS == 2 ? xt + dot_slot(qi >> 2) + (qi & 3)
+                                 : xt + dot_slot(2 * (qi >> 3) + (qi & 1)) + ((qi >> 1) & 3);
         dst[0] = static_cast<uint8_t>(d);
         dst[4] = static_cast<uint8_t>(d >> 8);
         dst[8] = static_cast<uint8_t>(d >> 16);
@@ -505,27 +524,47 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   const float sxv = SRC == 0 ? sx_in : tok_sx;
 
   // 6. contraction of the wave's row in group rg
-  auto finish = [&](int64_t rg, const uint4 (&w)[S], float gam) {
+  auto finish = [&](int64_t rg, const uint4 (&w)[kSl], float gam) {
     const int64_t n = rg * kRowsD + wave;
     int acc = 0;
 #pragma unroll
-    for (int sl = 0; sl < S; ++sl) {
-      const int unit = 4 * (lane + kWave * sl);  // first 16-code unit of the chunk
-      if (16 * unit >= K) break;                  // this chunk, and every later one, is past K
+    for (int sl = 0; sl < kSl; ++sl) {
+      const int chunk = lane + kWave * sl;
       const uint32_t words[4] = {w[sl].x, w[sl].y, w[sl].z, w[sl].w};
+      if (BITS == 2) {
+        const int unit = 4 * chunk;   // first 16-code unit of the chunk
+        if (16 * unit >= K) break;    // this chunk, and every later one, is past K
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v4i cd = decode_codes_strided(words[j]);
-        const v4i x = *reinterpret_cast<const v4i*>(xt + dot_slot(unit + j));
-        acc = __builtin_amdgcn_sdot4(x.x, cd.x, acc, false);
-        acc = __builtin_amdgcn_sdot4(x.y, cd.y, acc, false);
-        acc = __builtin_amdgcn_sdot4(x.z, cd.z, acc, false);
-        acc = __builtin_amdgcn_sdot4(x.w, cd.w, acc, false);
+        for (int j = 0; j < 4; ++j) {
+          const v4i cd = decode_codes_strided(words[j]);
+          const v4i x = *reinterpret_cast<const v4i*>(xt + dot_slot(unit + j));
+          acc = __builtin_amdgcn_sdot4(x.x, cd.x, acc, false);
+          acc = __builtin_amdgcn_sdot4(x.y, cd.y, acc, false);
+          acc = __builtin_amdgcn_sdot4(x.z, cd.z, acc, false);
+          acc = __builtin_amdgcn_sdot4(x.w, cd.w, acc, false);
+        }
+      } else {
+        const int group = 2 * chunk;  // first 32-code group of the chunk
+        if (32 * group >= K) break;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const v4i x0 = *reinterpret_cast<const v4i*>(xt + dot_slot(2 * (group + j)));
+          const v4i x1 = *reinterpret_cast<const v4i*>(xt + dot_slot(2 * (group + j) + 1));
+          const uint32_t wj = words[j];
+          acc = __builtin_amdgcn_sdot4(x0.x, static_cast<int>(wj & 0x01010101u), acc, false);
+          acc = __builtin_amdgcn_sdot4(x0.y, static_cast<int>((wj >> 1) & 0x01010101u), acc, false);
+          acc = __builtin_amdgcn_sdot4(x0.z, static_cast<int>((wj >> 2) & 0x01010101u), acc, false);
+          acc = __builtin_amdgcn_sdot4(x0.w, static_cast<int>((wj >> 3) & 0x01010101u), acc, false);
+          acc = __builtin_amdgcn_sdot4(x1.x, static_cast<int>((wj >> 4) & 0x01010101u), acc, false);
+          acc = __builtin_amdgcn_sdot4(x1.y, static_cast<int>((wj >> 5) & 0x01010101u), acc, false);
+          acc = __builtin_amdgcn_sdot4(x1.z, static_cast<int>((wj >> 6) & 0x01010101u), acc, false);
+          acc = __builtin_amdgcn_sdot4(x1.w, static_cast<int>((wj >> 7) & 0x01010101u), acc, false);
+        }
       }
     }
     acc = wave_isum_last(acc);
     if (lane != kWave - 1 || n >= N) return;
-    const int accv = acc - tsum;
+    const int accv = BITS == 2 ? acc - tsum : 2 * acc - tsum;
     if (ydt == TQ_I32) {
       static_cast<int*>(Y)[n] = accv;
     } else {
@@ -572,7 +611,7 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int SRC, int S>
+template <int SRC, int S, int BITS>
 hipError_t gemv_dot_launch_s(const void* src, const ActParams* p, int8_t* q_out, float* sx,
                              const GemmArgs& a, hipStream_t s) {
   // one workgroup per row group up to two per compute unit (the resident
@@ -582,18 +621,18 @@ hipError_t gemv_dot_launch_s(const void* src, const ActParams* p, int8_t* q_out,
   const int64_t grid = groups < cap ? groups : cap;
   const float eps = p ? p->eps : 0.f, lo = p ? p->eta_min : 0.f, hi = p ? p->eta_max : 0.f;
   const int clamp = p ? p->clamp : 0;
-  hipLaunchKernelGGL((k_gemv_dot<SRC, S>), dim3(grid), dim3(kNTd), static_cast<size_t>(a.K), s,
+  hipLaunchKernelGGL((k_gemv_dot<SRC, S, BITS>), dim3(grid), dim3(kNTd), static_cast<size_t>(a.K), s,
                      src, eps, clamp, lo, hi, q_out, sx, a.packed, a.scale, a.per_row, a.N,
                      static_cast<int>(a.K), a.Y, a.ydt);
   return hipGetLastError();
 }
 
-template <int SRC>
+template <int SRC, int BITS = 2>
 hipError_t gemv_dot_launch(const void* src, const ActParams* p, int8_t* q_out, float* sx,
                            const GemmArgs& a, hipStream_t s) {
-  if (a.K <= 4096) return gemv_dot_launch_s<SRC, 1>(src, p, q_out, sx, a, s);
-  if (a.K <= 8192) return gemv_dot_launch_s<SRC, 2>(src, p, q_out, sx, a, s);
-  return gemv_dot_launch_s<SRC, kMaxSlices>(src, p, q_out, sx, a, s);
+  if (a.K <= 4096) return gemv_dot_launch_s<SRC, 1, BITS>(src, p, q_out, sx, a, s);
+  if (a.K <= 8192) return gemv_dot_launch_s<SRC, 2, BITS>(src, p, q_out, sx, a, s);
+  return gemv_dot_launch_s<SRC, kMaxSlices, BITS>(src, p, q_out, sx, a, s);
 }
 
 // One token, K a multiple of 64 up to 16384 (the token and its LDS copy are
@@ -696,7 +735,14 @@ __device__ inline void unit_to_f32(const RawUnit<SRC>& u, float (&v)[16]) {
   }
 }
 
-template <int SRC, int KBW>
+// BITS 1 (signs of binary weights): a lane holds 8 packed bytes, 64 signs,
+// of its row per block (one 64-bit load).  MFMA j takes 32-bit word j / 2 and
+// its operand word t is (w >> (4 (j % 2) + t)) & 0x01010101, byte b holding
+// the sign of code 8 b + 4 (j % 2) + t of the word, mapped to -1 / +1 by one
+// byte permute.  The matching token operand is the 4 x 4 byte transpose of
+// the quads 4 (j % 2) / 4 + {0, 2, 4, 6} of the 32 values, so each 32-value
+// group is staged as two transposes, in place.
+template <int SRC, int KBW, int BITS>
 __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
     const void* __restrict__ src, float eps, int clamp, float lo, float hi,
     int8_t* __restrict__ q_out, float* __restrict__ sx_io, int M,
@@ -716,14 +762,18 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
   const int upr = K >> 4;          // 16-value units per token
   const int nkb = K >> 8;          // 256-code blocks
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * kMfmaRows;
-  const int rowbytes = K >> 2;
+  const int rowbytes = BITS == 2 ? K >> 2 : K >> 3;
 
   // 1. the thread's first token unit (a read past the end returns zero),
   // then its weight blocks
   const __amdgpu_buffer_rsrc_t qr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(src), static_cast<short>(0), M * K * kEl, kBufRaw);
   const int nunits = M * upr;
-  const RawUnit<SRC> u0 = load_unit<SRC>(qr, tid);
+  static_assert(BITS == 2 || SRC == 0, "1-bit weights take int8 tokens");
+  // BITS 2: one 16-value unit per thread per round; BITS 1: a 32-value
+  // group (two units) per thread per round
+  const RawUnit<SRC> u0 = load_unit<SRC>(qr, BITS == 2 ? tid : 2 * tid);
+  const RawUnit<SRC> u1 = BITS == 2 ? u0 : load_unit<SRC>(qr, 2 * tid + 1);
   const int64_t rows_here = N - n0 < kMfmaRows ? N - n0 : kMfmaRows;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(packed + n0 * rowbytes), static_cast<short>(0),
@@ -733,9 +783,16 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
 #pragma unroll
   for (int i = 0; i < KBW; ++i) {
     const int kb = wave + nw * i;  // blocks past the end read zeros and are skipped
-    wv[i] = __builtin_bit_cast(
-        uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                   wr, fr * rowbytes + 64 * (kb < nkb ? kb : 0) + 16 * fg, 0, 0));
+    const int kbl = kb < nkb ? kb : 0;
+    if (BITS == 2) {
+      wv[i] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, fr * rowbytes + 64 * kbl + 16 * fg, 0, 0));
+    } else {
+      typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+      const u2 v = __builtin_bit_cast(
+          u2, __builtin_amdgcn_raw_buffer_load_b64(wr, fr * rowbytes + 32 * kbl + 8 * fg, 0, 0));
+      wv[i] = make_uint4(v.x, v.y, 0u, 0u);
+    }
   }
   // epilogue operands of the thread's output (token m, row n0 + n)
   const int em = tid >> 4, en = tid & 15;
@@ -791,8 +848,25 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
     }
     *reinterpret_cast<v4i*>(xs + m * pitch + 16 * uu) = transpose_bytes4x4(d[0], d[1], d[2], d[3]);
   };
-  if (tid < nunits) stage(u0, tid);
-  for (int c = tid + nt; c < nunits; c += nt) stage(load_unit<SRC>(qr, c), c);
+  if (BITS == 2) {
+    if (tid < nunits) stage(u0, tid);
+    for (int c = tid + nt; c < nunits; c += nt) stage(load_unit<SRC>(qr, c), c);
+  } else {
+    // group g: quads Q0..Q7 = a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w
+    auto stage1 = [&](const RawUnit<SRC>& a, const RawUnit<SRC>& b, int g) {
+      const int gpr = upr >> 1;
+      const int m = g / gpr, gg = g - m * gpr;
+      uint8_t* dst = xs + m * pitch + 32 * gg;
+      *reinterpret_cast<v4i*>(dst) =
+          transpose_bytes4x4(a.w[0].x, a.w[0].z, b.w[0].x, b.w[0].z);
+      *reinterpret_cast<v4i*>(dst + 16) =
+          transpose_bytes4x4(a.w[0].y, a.w[0].w, b.w[0].y, b.w[0].w);
+    };
+    const int ngroups = nunits >> 1;
+    if (tid < ngroups) stage1(u0, u1, tid);
+    for (int g = tid + nt; g < ngroups; g += nt)
+      stage1(load_unit<SRC>(qr, 2 * g), load_unit<SRC>(qr, 2 * g + 1), g);
+  }
   __syncthreads();
   if (SRC != 0 && eout) esx = tok_sx[em];
 
@@ -807,12 +881,24 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
     const uint32_t words[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const v4i c = decode_codes_strided(words[j]);
       v4i b;
-      b.x = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.x)));
-      b.y = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.y)));
-      b.z = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.z)));
-      b.w = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.w)));
+      if (BITS == 2) {
+        const v4i c = decode_codes_strided(words[j]);
+        b.x = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.x)));
+        b.y = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.y)));
+        b.z = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.z)));
+        b.w = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c.w)));
+      } else {
+        // bytes 0 / 1 select 0xFF (-1) / 0x01 (+1) from the permute pool
+        auto pm = [](uint32_t x) {
+          return static_cast<int>(__builtin_amdgcn_perm(0u, 0x000001FFu, x & 0x01010101u));
+        };
+        const uint32_t wj = words[j >> 1] >> (4 * (j & 1));
+        b.x = pm(wj);
+        b.y = pm(wj >> 1);
+        b.z = pm(wj >> 2);
+        b.w = pm(wj >> 3);
+      }
       v4i a = *reinterpret_cast<const v4i*>(abase + 256 * kb + 16 * j);
       if (!arow) a = v4i{0, 0, 0, 0};
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
@@ -856,7 +942,7 @@ bool mfma_path_ok(int64_t M, int64_t K, const void* packed, const void* act) {
          (reinterpret_cast<uintptr_t>(act) & 15u) == 0u;
 }
 
-template <int SRC, int KBW>
+template <int SRC, int KBW, int BITS>
 hipError_t gemv_mfma_launch_k(const void* src, const ActParams* p, int8_t* q_out, float* sx,
                               const GemmArgs& a, int waves, hipStream_t s) {
   const size_t lds = static_cast<size_t>(mfma_lds_bytes(a.M, a.K));
@@ -866,7 +952,7 @@ hipError_t gemv_mfma_launch_k(const void* src, const ActParams* p, int8_t* q_out
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_mfma<SRC, KBW>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_mfma<SRC, KBW, BITS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(kMfmaLdsMax));
     if (e != hipSuccess) return e;
@@ -875,21 +961,78 @@ hipError_t gemv_mfma_launch_k(const void* src, const ActParams* p, int8_t* q_out
   const int64_t grid = (a.N + kMfmaRows - 1) / kMfmaRows;
   const float eps = p ? p->eps : 0.f, lo = p ? p->eta_min : 0.f, hi = p ? p->eta_max : 0.f;
   const int clamp = p ? p->clamp : 0;
-  hipLaunchKernelGGL((k_gemv_mfma<SRC, KBW>), dim3(grid), dim3(waves * kWave), lds, s, src, eps,
+  hipLaunchKernelGGL((k_gemv_mfma<SRC, KBW, BITS>), dim3(grid), dim3(waves * kWave), lds, s, src, eps,
                      clamp, lo, hi, q_out, sx, static_cast<int>(a.M), a.packed, a.scale,
                      a.per_row, a.N, static_cast<int>(a.K), a.Y, a.ydt);
   return hipGetLastError();
 }
 
-template <int SRC>
+template <int SRC, int BITS = 2>
 hipError_t gemv_mfma_launch(const void* src, const ActParams* p, int8_t* q_out, float* sx,
                             const GemmArgs& a, hipStream_t s) {
   const int64_t nkb = a.K / 256;
   const int waves = static_cast<int>(nkb < kMfmaMaxWaves ? nkb : kMfmaMaxWaves);
   const int64_t per = (nkb + waves - 1) / waves;  // blocks per wave
-  if (per <= 1) return gemv_mfma_launch_k<SRC, 1>(src, p, q_out, sx, a, waves, s);
-  if (per <= 2) return gemv_mfma_launch_k<SRC, 2>(src, p, q_out, sx, a, waves, s);
-  return gemv_mfma_launch_k<SRC, 4>(src, p, q_out, sx, a, waves, s);
+  if (per <= 1) return gemv_mfma_launch_k<SRC, 1, BITS>(src, p, q_out, sx, a, waves, s);
+  if (per <= 2) return gemv_mfma_launch_k<SRC, 2, BITS>(src, p, q_out, sx, a, waves, s);
+  return gemv_mfma_launch_k<SRC, 4, BITS>(src, p, q_out, sx, a, waves, s);
+}
+
+// ------------------------------------------------------------------------
+// 1-bit sign-packed binary weights, any K % 8 == 0, 1 <= M <= 16, any
+// alignment: one wave per output row, lanes stride over the row's packed
+// bytes and read the tokens from global memory.  The shapes the two fast
+// kernels do not take.
+__global__ __launch_bounds__(256) void k_gemv1_generic(
+    const int8_t* __restrict__ q, const float* __restrict__ sx, int M,
+    const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
+    int64_t N, int64_t K, void* __restrict__ Y, int ydt) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (n >= N) return;  // no barriers in this kernel
+  const int64_t nb = K / 8;
+  const uint8_t* row = packed + n * nb;
+  int acc[kGemvMaxM];
+#pragma unroll
+  for (int m = 0; m < kGemvMaxM; ++m) acc[m] = 0;
+  for (int64_t j = lane; j < nb; j += kWave) {
+    const uint32_t byte = row[j];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const bool plus = (byte >> t) & 1u;
+#pragma unroll
+      for (int m = 0; m < kGemvMaxM; ++m) {
+        if (m < M) {
+          const int x = q[m * K + 8 * j + t];
+          acc[m] += plus ? x : -x;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kGemvMaxM; ++m)
+    if (m < M) acc[m] = wave_isum_last(acc[m]);
+  if (lane != kWave - 1) return;
+  const float gam = ydt == TQ_I32 ? 0.f : scale[per_row ? n : 0];
+  for (int m = 0; m < M; ++m) {
+    const int64_t o = static_cast<int64_t>(m) * N + n;
+    if (ydt == TQ_I32) {
+      static_cast<int*>(Y)[o] = acc[m];
+    } else {
+      const float y = static_cast<float>(acc[m]) * (gam * sx[m]);
+      if (ydt == TQ_F32)
+        static_cast<float*>(Y)[o] = y;
+      else
+        static_cast<uint16_t*>(Y)[o] = f32_to_bf16(y);
+    }
+  }
+}
+
+// One token, 1-bit weights: 64-code lane chunks, K <= 16384.
+bool dot1_path_ok(int64_t M, int64_t K, const void* packed, const void* act) {
+  return M == 1 && (K % 64) == 0 && K <= 16384 &&
+         (reinterpret_cast<uintptr_t>(packed) & 15u) == 0u &&
+         (reinterpret_cast<uintptr_t>(act) & 15u) == 0u;
 }
 
 }  // namespace
@@ -926,6 +1069,17 @@ hipError_t launch_quant_gemv(const void* X, int bf16, const ActParams& p, int8_t
     return bf16 ? gemv_mfma_launch<2>(X, &p, q, sx, a, s) : gemv_mfma_launch<1>(X, &p, q, sx, a, s);
   return bf16 ? gemv_lds_launch<2>(X, M, &p, q, sx, a, s)
               : gemv_lds_launch<1>(X, M, &p, q, sx, a, s);
+}
+
+hipError_t launch_gemv1(const GemmArgs& a, hipStream_t s) {
+  if (dot1_path_ok(a.M, a.K, a.packed, a.q))
+    return gemv_dot_launch<0, 1>(a.q, nullptr, nullptr, const_cast<float*>(a.sx), a, s);
+  if (mfma_path_ok(a.M, a.K, a.packed, a.q))
+    return gemv_mfma_launch<0, 1>(a.q, nullptr, nullptr, const_cast<float*>(a.sx), a, s);
+  const int64_t grid = (a.N + 3) / 4;
+  hipLaunchKernelGGL(k_gemv1_generic, dim3(grid), dim3(256), 0, s, a.q, a.sx,
+                     static_cast<int>(a.M), a.packed, a.scale, a.per_row, a.N, a.K, a.Y, a.ydt);
+  return hipGetLastError();
 }
 
 }  // namespace tq

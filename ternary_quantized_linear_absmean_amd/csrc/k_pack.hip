@@ -245,9 +245,39 @@ __global__ __launch_bounds__(kNT) void k_ternarize_pack(const float* __restrict_
     packed[j] = static_cast<uint8_t>(byte_of(load4<false>(W, j), h, binary));
 }
 
-// --------------------------------------------------------------- per row
+// 1-bit sign packing of binary weights: bit t of byte j is 1 when weight
+// 8j + t is >= 0 (+1), LSB-first; 32 weights -> one 32-bit word per step.
+__device__ inline uint32_t sign_bits4(float4 v) {
+  return (v.x >= 0.f ? 1u : 0u) | (v.y >= 0.f ? 2u : 0u) | (v.z >= 0.f ? 4u : 0u) |
+         (v.w >= 0.f ? 8u : 0u);
+}
 
 template <bool VEC>
+__global__ __launch_bounds__(kNT) void k_sign_pack(const float* __restrict__ W, int64_t nbytes,
+                                                   uint8_t* __restrict__ packed) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kNT;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kNT + threadIdx.x;
+  int64_t done = 0;
+  if (VEC) {
+    const int64_t nwords = nbytes / 4;
+    for (int64_t i = tid; i < nwords; i += stride) {
+      uint32_t word = 0u;
+#pragma unroll
+      for (int n = 0; n < 8; ++n) word |= sign_bits4(load4<true>(W, 8 * i + n)) << (4 * n);
+      reinterpret_cast<uint32_t*>(packed)[i] = word;
+    }
+    done = nwords * 4;
+  }
+  for (int64_t j = done + tid; j < nbytes; j += stride)
+    packed[j] = static_cast<uint8_t>(sign_bits4(load4<false>(W, 2 * j)) |
+                                     (sign_bits4(load4<false>(W, 2 * j + 1)) << 4));
+}
+
+// --------------------------------------------------------------- per row
+
+// BITS 2: ternary or binary codes, four per byte; BITS 1: signs, eight per
+// byte (binary weights only).
+template <bool VEC, int BITS>
 __global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
                                                    int64_t K, int binary, double thr,
                                                    uint8_t* __restrict__ packed,
@@ -258,7 +288,7 @@ __global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
   __shared__ unsigned long long lb[256];
   const int64_t row = blockIdx.x;
   const float* w = W + row * K;
-  uint8_t* out = packed + row * (K / 4);
+  uint8_t* out = packed + row * (K * BITS / 8);
   const int64_t nb = K / 4;
   double acc = 0.0;
   for (int64_t j = threadIdx.x; j < nb; j += kNT) {
@@ -294,8 +324,14 @@ __global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
   const float g = g_sh;
   if (threadIdx.x == 0) scale[row] = g;
   const float h = g * 0.5f;
-  for (int64_t j = threadIdx.x; j < nb; j += kNT)
-    out[j] = static_cast<uint8_t>(byte_of(load4<VEC>(w, j), h, binary));
+  if (BITS == 2) {
+    for (int64_t j = threadIdx.x; j < nb; j += kNT)
+      out[j] = static_cast<uint8_t>(byte_of(load4<VEC>(w, j), h, binary));
+  } else {
+    for (int64_t j = threadIdx.x; j < K / 8; j += kNT)
+      out[j] = static_cast<uint8_t>(sign_bits4(load4<VEC>(w, 2 * j)) |
+                                    (sign_bits4(load4<VEC>(w, 2 * j + 1)) << 4));
+  }
 }
 
 // Relative error bound of an fp64 sum of non-negative terms whose longest
@@ -311,7 +347,7 @@ size_t pack_tensor_ws_bytes() { return kWsTotal; }
 
 hipError_t launch_pack_tensor(const float* W, int64_t numel, tq_wmode mode,
                               uint8_t* packed, float* scale, void* ws,
-                              hipStream_t s) {
+                              hipStream_t s, int bits) {
   const int binary = mode == TQ_BINARY_SIGN ? 1 : 0;
   char* base = static_cast<char*>(ws);
   double* partials = reinterpret_cast<double*>(base + kWsPartials);
@@ -339,6 +375,18 @@ hipError_t launch_pack_tensor(const float* W, int64_t numel, tq_wmode mode,
     hipLaunchKernelGGL(k_gamma_bins<false>, dim3(P), dim3(kNT), 0, s, W, n4, flag, bins);
   hipLaunchKernelGGL(k_gamma_exact_final, dim3(1), dim3(kWave), 0, s, flag, bins,
                      numel, scale);
+  if (bits == 1) {
+    const int64_t nb1 = numel / 8;
+    const bool vec1 = vec && (reinterpret_cast<uintptr_t>(packed) & 3u) == 0u;
+    int64_t grid1 = ((vec1 ? nb1 / 4 : nb1) + kNT - 1) / kNT;
+    if (grid1 < 1) grid1 = 1;
+    if (grid1 > 8192) grid1 = 8192;
+    if (vec1)
+      hipLaunchKernelGGL(k_sign_pack<true>, dim3(grid1), dim3(kNT), 0, s, W, nb1, packed);
+    else
+      hipLaunchKernelGGL(k_sign_pack<false>, dim3(grid1), dim3(kNT), 0, s, W, nb1, packed);
+    return hipGetLastError();
+  }
   const int64_t nbytes = numel / 4;
   const bool vec_pack = vec && (reinterpret_cast<uintptr_t>(packed) & 3u) == 0u;
   int64_t work = vec_pack ? nbytes / 4 : nbytes;
@@ -355,17 +403,22 @@ hipError_t launch_pack_tensor(const float* W, int64_t numel, tq_wmode mode,
 }
 
 hipError_t launch_pack_rows(const float* W, int64_t N, int64_t K, tq_wmode mode,
-                            uint8_t* packed, float* scale, hipStream_t s) {
+                            uint8_t* packed, float* scale, hipStream_t s, int bits) {
   const int binary = mode == TQ_BINARY_SIGN ? 1 : 0;
   const bool vec = (reinterpret_cast<uintptr_t>(W) & 15u) == 0u;
   const int64_t per_thread = (K / 4 + kNT - 1) / kNT;
   const double thr = sum_error_bound(4 * per_thread + 10);
-  if (vec)
-    hipLaunchKernelGGL(k_pack_rows<true>, dim3(N), dim3(kNT), 0, s, W, K, binary, thr,
-                       packed, scale);
-  else
-    hipLaunchKernelGGL(k_pack_rows<false>, dim3(N), dim3(kNT), 0, s, W, K, binary, thr,
-                       packed, scale);
+#define TQ_PACK_ROWS(V, B)                                                                  \
+  hipLaunchKernelGGL((k_pack_rows<V, B>), dim3(N), dim3(kNT), 0, s, W, K, binary, thr, packed, \
+                     scale)
+  if (bits == 1) {
+    if (vec) TQ_PACK_ROWS(true, 1);
+    else TQ_PACK_ROWS(false, 1);
+  } else {
+    if (vec) TQ_PACK_ROWS(true, 2);
+    else TQ_PACK_ROWS(false, 2);
+  }
+#undef TQ_PACK_ROWS
   return hipGetLastError();
 }
 

@@ -137,6 +137,40 @@ static hipError_t launch_quant(const void* X, tq_dtype xdt, int64_t M, int64_t K
                   : tq::launch_quant_plain(X, bf16, M, K, p, q, sx, stream);
 }
 
+size_t tq_packed1_bytes(int64_t numel) {
+  if (numel <= 0) return 0;
+  return static_cast<size_t>((numel + 7) / 8);
+}
+
+tq_status tq_pack_binary1(const float* W, int64_t N, int64_t K, tq_gran g, uint8_t* packed,
+                          float* scale, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (N < 0 || K <= 0 || (K % 8) != 0) return TQ_ERR_SHAPE;
+  if (g != TQ_PER_TENSOR && g != TQ_PER_ROW) return TQ_ERR_UNSUPPORTED;
+  if (K >= kMaxNumelPack || N >= kMaxNumelPack / K) return TQ_ERR_UNSUPPORTED;
+  if (N == 0) return TQ_OK;
+  if (!W || !packed || !scale) return TQ_ERR_NULL;
+  if (!aligned(W, 4) || !aligned(scale, 4)) return TQ_ERR_ALIGN;
+  if (g == TQ_PER_TENSOR) {
+    const size_t need = tq::pack_tensor_ws_bytes();
+    if (!ws || ws_bytes < need) return TQ_ERR_WORKSPACE;
+    if (!aligned(ws, 8)) return TQ_ERR_ALIGN;
+    return hip_status(
+        tq::launch_pack_tensor(W, N * K, TQ_BINARY_SIGN, packed, scale, ws, stream, 1));
+  }
+  return hip_status(tq::launch_pack_rows(W, N, K, TQ_BINARY_SIGN, packed, scale, stream, 1));
+}
+
+tq_status tq_binary1_gemv(const int8_t* q, const float* sx, int64_t M, const uint8_t* packed,
+                          const float* scale, tq_gran g, int64_t N, int64_t K, void* Y,
+                          tq_dtype ydt, hipStream_t stream) {
+  if (M > tq::kGemvMaxM) return TQ_ERR_SHAPE;
+  if (K > 0 && (K % 8) != 0) return TQ_ERR_SHAPE;
+  const tq_status st = check_contract(q, sx, M, packed, scale, g, N, K, Y, ydt);
+  if (st != TQ_OK || M == 0 || N == 0) return st;
+  return hip_status(tq::launch_gemv1(make_args(q, sx, M, packed, scale, g, N, K, Y, ydt),
+                                     stream));
+}
+
 tq_status tq_quant_act_int8(const void* X, tq_dtype xdt, int64_t M, int64_t K,
                             const tq_act_opts* opts, int8_t* q, float* sx,
                             hipStream_t stream) {

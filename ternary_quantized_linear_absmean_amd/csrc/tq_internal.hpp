@@ -10,11 +10,12 @@ namespace tq {
 
 // ---- absmean + ternarize + pack (k_pack.hip)
 size_t pack_tensor_ws_bytes();
+// bits: 2 (codes, four per byte) or 1 (signs of binary weights, eight per byte)
 hipError_t launch_pack_tensor(const float* W, int64_t numel, tq_wmode mode,
                               uint8_t* packed, float* scale, void* ws,
-                              hipStream_t s);
+                              hipStream_t s, int bits = 2);
 hipError_t launch_pack_rows(const float* W, int64_t N, int64_t K, tq_wmode mode,
-                            uint8_t* packed, float* scale, hipStream_t s);
+                            uint8_t* packed, float* scale, hipStream_t s, int bits = 2);
 
 // ---- activations (k_quant.hip)
 struct ActParams {
@@ -50,6 +51,8 @@ struct GemmArgs {
 constexpr int kGemvMaxM = 16;
 constexpr int64_t kGemvLdsBytes = 65536;  // activation staging of the small-M GEMV
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t s);
+// the same product with 1-bit sign-packed binary weights ([N][K/8] bytes)
+hipError_t launch_gemv1(const GemmArgs& a, hipStream_t s);
 // quantise X (plain path) and apply the GEMV in one launch; only when
 // fused_quant_gemv_ok() holds
 bool fused_quant_gemv_ok(int64_t M, int64_t K, const void* packed, const void* X);

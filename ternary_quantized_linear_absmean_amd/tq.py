@@ -32,7 +32,8 @@ GRANULARITY = {"tensor": 0, "row": 1}
 MODES = {"ternary": 0, "binary": 1}
 EXPORTED = ["tq_packed_bytes", "tq_pack_workspace_bytes", "tq_pack_ternary",
             "tq_quant_act_int8", "tq_fwht512", "tq_ternary_gemv", "tq_ternary_gemm",
-            "tq_quant_ternary_gemv", "tq_status_str", "tq_last_hip_error", "tq_version"]
+            "tq_quant_ternary_gemv", "tq_packed1_bytes", "tq_pack_binary1",
+            "tq_binary1_gemv", "tq_status_str", "tq_last_hip_error", "tq_version"]
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -61,6 +62,12 @@ for _name in ("tq_ternary_gemv", "tq_ternary_gemm"):
 _lib.tq_quant_ternary_gemv.argtypes = [_vp, _int, _i64, ctypes.POINTER(TqActOpts), _vp, _vp,
                                        _int, _i64, _i64, _vp, _vp, _vp, _int, _vp]
 _lib.tq_quant_ternary_gemv.restype = _int
+_lib.tq_packed1_bytes.argtypes = [_i64]
+_lib.tq_packed1_bytes.restype = ctypes.c_size_t
+_lib.tq_pack_binary1.argtypes = [_vp, _i64, _i64, _int, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.tq_pack_binary1.restype = _int
+_lib.tq_binary1_gemv.argtypes = [_vp, _vp, _i64, _vp, _vp, _int, _i64, _i64, _vp, _int, _vp]
+_lib.tq_binary1_gemv.restype = _int
 _lib.tq_status_str.argtypes = [_int]
 _lib.tq_status_str.restype = ctypes.c_char_p
 _lib.tq_last_hip_error.argtypes = []
@@ -152,6 +159,33 @@ def tq_pack_ternary(W: torch.Tensor, granularity: str = "tensor", mode: str = "t
     return packed, scale
 
 
+def tq_packed1_bytes(numel: int) -> int:
+    return int(_lib.tq_packed1_bytes(numel))
+
+
+def tq_pack_binary1(W: torch.Tensor, granularity: str = "row",
+                    packed: torch.Tensor | None = None, scale: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None, stream=None):
+    """W [N, K] fp32 -> (packed uint8 [N, K/8] signs, scale fp32 [1] or [N])."""
+    _dev(W, "W")
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float32 tensor")
+    N, K = W.shape
+    if packed is None:
+        packed = torch.empty((N, K // 8), dtype=torch.uint8, device=W.device)
+    if scale is None:
+        scale = torch.empty((1 if granularity == "tensor" else N,), dtype=torch.float32,
+                            device=W.device)
+    need = tq_pack_workspace_bytes(N, K, granularity)
+    if workspace is None and need:
+        workspace = torch.empty((need,), dtype=torch.uint8, device=W.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_lib.tq_pack_binary1(W.data_ptr(), N, K, GRANULARITY[granularity], _ptr(packed),
+                                _ptr(scale), _ptr(workspace), ws_bytes, _stream(stream)),
+           "tq_pack_binary1")
+    return packed, scale
+
+
 # ------------------------------------------------------------ activations
 
 def _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block) -> TqActOpts:
@@ -217,6 +251,13 @@ def tq_ternary_gemv(q, sx, packed, scale, N: int, K: int, granularity: str = "te
                     out_dtype: str = "f32", Y=None, stream=None) -> torch.Tensor:
     """y = (q @ W^T) * scale * sx for M <= 16 tokens -> [M, N]."""
     return _contract(_lib.tq_ternary_gemv, "tq_ternary_gemv", q, sx, packed, scale, N, K,
+                     granularity, out_dtype, Y, stream)
+
+
+def tq_binary1_gemv(q, sx, packed, scale, N: int, K: int, granularity: str = "row",
+                    out_dtype: str = "f32", Y=None, stream=None) -> torch.Tensor:
+    """tq_ternary_gemv with 1-bit sign-packed weights (packed [N, K/8])."""
+    return _contract(_lib.tq_binary1_gemv, "tq_binary1_gemv", q, sx, packed, scale, N, K,
                      granularity, out_dtype, Y, stream)
 
 

@@ -58,7 +58,11 @@ def _gemm(*a):
     return lib.tq_ternary_gemm(*a)
 
 
-@pytest.mark.parametrize("fn", [_gemv, _gemm])
+def _gemv1(*a):
+    return lib.tq_binary1_gemv(*a)
+
+
+@pytest.mark.parametrize("fn", [_gemv, _gemm, _gemv1])
 def test_contract_validation(fn):
     P = 0x10000  # never dereferenced: every call below fails validation
     # shapes
@@ -70,7 +74,7 @@ def test_contract_validation(fn):
     assert fn(P, P, 1, P, P, 2, 16, 64, P, 0, None) == UNSUP
     assert fn(P, P, 1, P, P, 0, 16, 64, P, 3, None) == DTYPE
     # K beyond the int32 headroom of 127 * K < 2^24
-    assert fn(P, P, 1, P, P, 0, 16, 132108, P, 0, None) == UNSUP
+    assert fn(P, P, 1, P, P, 0, 16, 132112, P, 0, None) == UNSUP
     # NULL pointers with a non-empty problem
     assert fn(None, P, 1, P, P, 0, 16, 64, P, 0, None) == NULL
     assert fn(P, None, 1, P, P, 0, 16, 64, P, 0, None) == NULL
@@ -92,6 +96,24 @@ def test_gemv_token_limit():
     assert _gemv(P, P, 17, P, P, 0, 16, 64, P, 0, None) == SHAPE
     # the GEMM has no such limit: same call fails only on the NULL Y
     assert _gemm(P, P, 17, P, P, 0, 16, 64, None, 0, None) == NULL
+
+
+def test_binary1_validation():
+    P = 0x10000
+    # 1-bit rows are whole bytes: K % 8
+    assert _gemv1(P, P, 1, P, P, 0, 16, 12, P, 0, None) == SHAPE
+    assert _gemv1(P, P, 17, P, P, 0, 16, 64, P, 0, None) == SHAPE
+    f = lib.tq_pack_binary1
+    assert f(P, 4, 12, 0, P, P, P, 1 << 20, None) == SHAPE
+    assert f(P, -1, 64, 0, P, P, P, 1 << 20, None) == SHAPE
+    assert f(P, 4, 64, 5, P, P, P, 1 << 20, None) == UNSUP
+    assert f(None, 4, 64, 1, P, P, None, 0, None) == NULL
+    assert f(P, 4, 64, 0, P, P, None, 1 << 20, None) == WS
+    assert f(P + 2, 4, 64, 1, P, P, None, 0, None) == ALIGN
+    assert f(None, 0, 64, 1, None, None, None, 0, None) == OK
+    assert tqmod.tq_packed1_bytes(0) == 0
+    assert tqmod.tq_packed1_bytes(2048 * 2048) == 2048 * 2048 // 8
+    assert tqmod.tq_packed1_bytes(9) == 2
 
 
 def test_pack_validation():

@@ -621,3 +621,115 @@ def test_gemv_small_m_large_k_general_path():
     say("gemv large K")
     _check_outputs(tq.tq_ternary_gemv, dev(q), dev(sx), dev(packed), dev(scale), N, K,
                    "tensor", q, packed, scale, sx)
+
+
+# ------------------------------------------------- 1-bit sign-packed binary
+
+def _pack1_pair(W, gran):
+    packed, scale = tq.tq_pack_binary1(dev(np.ascontiguousarray(W, np.float32)), gran)
+    pr, sr = oracle.pack_binary1(W, gran)
+    np.testing.assert_array_equal(f32_bits(host(scale)), f32_bits(sr))
+    np.testing.assert_array_equal(host(packed), pr)
+    return pr, sr
+
+
+@pytest.mark.parametrize("N,K", [(1, 8), (3, 24), (17, 136), (257, 264), (5, 4096), (33, 2560)])
+@pytest.mark.parametrize("gran", ["tensor", "row"])
+def test_pack_binary1_shapes(N, K, gran):
+    W = ti.normal_weights(2000 + N + K, N, K)
+    W[0, : min(K, 6)] = 0.0
+    W[-1, -1] = -0.0
+    say(f"pack 1-bit {N}x{K} {gran}")
+    _pack1_pair(W, gran)
+
+
+def test_pack_binary1_bitlinear_workload_and_unaligned():
+    W = ti.workload_weights("bitlinear", 0)
+    say(f"pack 1-bit bitlinear {W.shape}")
+    _pack1_pair(W, "row")
+    # W at an odd float offset and the packed rows at odd byte offsets
+    N, K = 40, 200
+    W = ti.normal_weights(2100, N, K)
+    Wbuf = torch.zeros(N * K + 1, dtype=torch.float32, device=DEV)
+    Wbuf[1:] = dev(W).reshape(-1)
+    pbuf = torch.zeros(N * K // 8 + 3, dtype=torch.uint8, device=DEV)
+    pd = pbuf[3:].view(N, K // 8)
+    for gran in ("tensor", "row"):
+        _, s = tq.tq_pack_binary1(Wbuf[1:].view(N, K), gran, packed=pd)
+        pr, sr = oracle.pack_binary1(W, gran)
+        np.testing.assert_array_equal(host(pd), pr)
+        np.testing.assert_array_equal(f32_bits(host(s)), f32_bits(sr))
+
+
+def _check1(qd, sxd, pd, sd, N, K, gran, q, packed, scale, sx):
+    acc_ref = oracle.contract_signs(q, packed, K)
+    y_ref = oracle.epilogue(acc_ref, scale, sx)
+    acc = host(tq.tq_binary1_gemv(qd, sxd, pd, sd, N, K, gran, "i32"))
+    np.testing.assert_array_equal(acc.astype(np.int64), acc_ref)
+    y = host(tq.tq_binary1_gemv(qd, sxd, pd, sd, N, K, gran, "f32"))
+    assert_y_close(y, y_ref)
+    assert np.all(y[acc_ref == 0] == 0)
+    yb = host(tq.tq_binary1_gemv(qd, sxd, pd, sd, N, K, gran, "bf16").view(torch.int16))
+    assert_bf16_close(yb.view(np.uint16), y_ref)
+
+
+# (M, N, K): one token on the row-per-wave kernel (K % 128 == 0, one and two
+# slices, a slice cut short), 2..16 tokens on matrix cores (K % 256 == 0),
+# and the simple kernel (other K)
+BIN1_CASES = [(1, 4096, 4096), (1, 70, 2560), (1, 37, 16384), (1, 45, 8320), (1, 19, 128), (1, 23, 4160), (1, 11, 64),
+              (2, 33, 256), (4, 300, 2560), (16, 40, 6912), (7, 21, 16384),
+              (1, 9, 8), (3, 17, 24), (16, 5, 1000), (1, 30, 2600), (5, 12, 136)]
+
+
+@pytest.mark.parametrize("M,N,K", BIN1_CASES)
+def test_binary1_gemv(M, N, K):
+    W = ti.normal_weights(3000 + M + N + K, N, K)
+    packed, scale = oracle.pack_binary1(W, "row")
+    q = ti.random_int8(3100 + M + K, M, K)
+    sx = (np.abs(ti.activations(M + 3200, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    say(f"gemv 1-bit M={M} N={N} K={K}")
+    for gran, sc in (("row", scale), ("tensor", scale[:1])):
+        _check1(dev(q), dev(sx), dev(packed), dev(sc), N, K, gran, q, packed, sc, sx)
+
+
+def test_binary1_gemv_extremes_and_unaligned():
+    # |acc| = 127 * K in both signs; then q and packed at odd offsets
+    K, N = 6912, 20
+    q = np.full((2, K), 127, np.int8)
+    q[1] = -127
+    b = np.ones((N, K), np.int8)
+    b[1::2] = -1
+    packed = oracle.pack_signs(b)
+    scale = np.array([0.5], np.float32)
+    sx = np.array([1.0, 2.0], np.float32)
+    say("gemv 1-bit extremes")
+    _check1(dev(q), dev(sx), dev(packed), dev(scale), N, K, "tensor", q, packed, scale, sx)
+    M, N, K = 1, 40, 4096
+    q = ti.random_int8(3300, M, K)
+    W = ti.normal_weights(3301, N, K)
+    packed, scale = oracle.pack_binary1(W, "row")
+    sx = np.array([0.02], np.float32)
+    qbuf = torch.zeros(M * K + 1, dtype=torch.int8, device=DEV)
+    qbuf[1:] = dev(q).reshape(-1)
+    pbuf = torch.zeros(N * K // 8 + 3, dtype=torch.uint8, device=DEV)
+    pbuf[3:] = dev(packed).reshape(-1)
+    say("gemv 1-bit unaligned")
+    _check1(qbuf[1:].view(M, K), dev(sx), pbuf[3:].view(N, K // 8), dev(scale), N, K, "row",
+            q, packed, scale, sx)
+
+
+def test_binary1_matches_two_bit_binary():
+    # the same binary layer through both storage forms gives identical outputs
+    W = ti.workload_weights("bitlinear", 0)[:512]
+    N, K = W.shape
+    X = ti.activations(3400, 4, K, dtype="f32")
+    Xd = dev(X)
+    q, sx = tq.tq_quant_act_int8(Xd)
+    p2, s2 = tq.tq_pack_ternary(dev(W), "row", "binary")
+    p1, s1 = tq.tq_pack_binary1(dev(W), "row")
+    np.testing.assert_array_equal(f32_bits(host(s1)), f32_bits(host(s2)))
+    say("1-bit vs 2-bit binary")
+    for ydt in ("i32", "f32"):
+        y2 = host(tq.tq_ternary_gemv(q, sx, p2, s2, N, K, "row", ydt))
+        y1 = host(tq.tq_binary1_gemv(q, sx, p1, s1, N, K, "row", ydt))
+        np.testing.assert_array_equal(y1, y2)
