@@ -14,7 +14,9 @@ Sources (cited by page title and section):
 * Hetman-2b, src/quantization.py -- section 1 (FWHT-512 butterfly and its
   1/sqrt(512) normaliser), section 2 (absmean weight quantizer, symmetric
   int8 activation quantizer), section 4 (RMSNorm), section 5 (BitLinear order
-  of operations and its scale fusion), section 7 (integer GEMV emulator).
+  of operations and its scale fusion), section 6 (SwiGLUClamped: SiLU gate
+  times up projection, clamped to +-10 before the down projection),
+  section 7 (integer GEMV emulator).
 * BitRASP, core_math.py -- ``fake_quant_int`` (per-token absmax int8),
   ``ternarize_weight`` (per-output-row absmean), ``additive_ternary_linear_int8``
   (y[o] = sum of x where W=+1 minus sum of x where W=-1).
@@ -518,6 +520,35 @@ def ternary_linear(X: np.ndarray, W: np.ndarray, granularity: str = "tensor",
     acc = contract(q, packed, k)
     y = epilogue(acc, gam, sx)
     return dict(packed=packed, scale=gam, q=q, sx=sx, acc=acc, y=y)
+
+
+SWIGLU_CLAMP = 10.0           # Hetman-2b s.6 default clamp value
+
+
+def swiglu_clamped(g: np.ndarray, u: np.ndarray, clamp_val: float = SWIGLU_CLAMP) -> np.ndarray:
+    """h = clamp(silu(g) * u, -c, c) with silu(g) = g / (1 + exp(-g)), in fp64
+    (Hetman-2b s.6 SwiGLUClamped: gate = SiLU(W_gate x), up = W_up x,
+    clamped activation before W_down)."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    silu = g / (1.0 + np.exp(-g))
+    return np.clip(silu * u, -clamp_val, clamp_val)
+
+
+def ffn_swiglu_decode(X: np.ndarray, gate, up, down, clamp_val: float = SWIGLU_CLAMP):
+    """Decode FFN of ternary layers (Hetman-2b s.6 with the plain quantiser):
+    gate, up and down are (packed, scales) pairs.  Returns (h fp64 [M, N_ffn],
+    the gate and up outputs g, u, and y fp64 [M, d]) where the down
+    projection quantises h per token exactly as ``quant_act_int8`` does."""
+    X = np.asarray(X, dtype=np.float32)
+    q, sx = quant_act_int8(X)
+    k = X.shape[1]
+    g = epilogue(contract(q, gate[0], k), gate[1], sx)
+    u = epilogue(contract(q, up[0], k), up[1], sx)
+    h = swiglu_clamped(g, u, clamp_val)
+    hq, hs = quant_act_int8(h.astype(np.float32))
+    y = epilogue(contract(hq, down[0], h.shape[1]), down[1], hs)
+    return h, g, u, y
 
 
 def exact_fraction_mean(w: np.ndarray) -> Fraction:

@@ -605,3 +605,46 @@ def test_contract_signs_brute_force_and_identity():
             assert acc[m, o] == ref
             plus = sum(int(q[m, k]) for k in range(K) if b[o, k] == 1)
             assert acc[m, o] == 2 * plus - int(q[m].astype(np.int64).sum())
+
+
+# ---------------------------------------------------------------- SwiGLU clamp
+
+def test_swiglu_clamped_closed_forms():
+    from scipy.special import expit
+    g = np.array([-30.0, -3.0, -0.5, 0.0, 0.5, 3.0, 30.0])
+    u = np.array([2.0, -1.5, 4.0, 7.0, -2.0, 0.25, 0.1])
+    h = oracle.swiglu_clamped(g, u)
+    # silu(g) = g * sigmoid(g) through an independent library sigmoid
+    ref = np.clip(g * expit(g) * u, -10.0, 10.0)
+    np.testing.assert_allclose(h, ref, rtol=1e-14, atol=0)
+    assert h[3] == 0.0                                  # silu(0) = 0
+    # silu(g) - silu(-g) = g (odd part of g * sigmoid(g))
+    gg = np.linspace(-8, 8, 33)
+    one = np.ones_like(gg)
+    np.testing.assert_allclose(oracle.swiglu_clamped(gg, one, 1e9) -
+                               oracle.swiglu_clamped(-gg, one, 1e9), gg, atol=1e-12)
+    # the clamp binds at exactly +-10 and only there
+    big = oracle.swiglu_clamped(np.array([20.0, 20.0, 4.0]), np.array([3.0, -3.0, 1.0]))
+    assert big[0] == 10.0 and big[1] == -10.0 and abs(big[2] - 4.0 * expit(4.0)) < 1e-14
+
+
+def test_ffn_swiglu_decode_matches_stepwise_float_reference():
+    # the whole FFN against float matrix products of the unpacked weights
+    rng = np.random.default_rng(9)
+    d, f, M = 64, 96, 3
+    X = rng.standard_normal((M, d)).astype(np.float32)
+    mats = []
+    for (n, k), seed in (((f, d), 1), ((f, d), 2), ((d, f), 3)):
+        mats.append(oracle.pack_ternary(ti.normal_weights(50 + seed, n, k), "row"))
+    h, g, u, y = oracle.ffn_swiglu_decode(X, *mats)
+    q, sx = oracle.quant_act_int8(X)
+    wg = oracle.unpack_codes(mats[0][0], d).astype(np.float64) * mats[0][1][:, None]
+    wu = oracle.unpack_codes(mats[1][0], d).astype(np.float64) * mats[1][1][:, None]
+    xq = q.astype(np.float64) * sx[:, None].astype(np.float64)
+    np.testing.assert_allclose(g, xq @ wg.T, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(u, xq @ wu.T, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(h, np.clip(g / (1 + np.exp(-g)) * u, -10, 10), rtol=1e-14)
+    hq, hs = oracle.quant_act_int8(h.astype(np.float32))
+    wd = oracle.unpack_codes(mats[2][0], f).astype(np.float64) * mats[2][1][:, None]
+    np.testing.assert_allclose(y, (hq.astype(np.float64) * hs[:, None]) @ wd.T, rtol=1e-12,
+                               atol=1e-15)
