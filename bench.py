@@ -49,7 +49,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--only", default="",
                    help="comma list of extra workloads to run: "
-                        "prefill,bitlinear,pack,ffn,steady,binary1,context")
+                        "prefill,bitlinear,pack,ffn,steady,binary1,ffn_decode,context")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (for counter scaling)")
     return p.parse_args()
@@ -246,6 +246,8 @@ def extras(torch, np, ti, tq, dev, only=frozenset()):
         out.update(extra_steady(torch, ti, tq, dev))
     if want("binary1"):
         out.update(extra_binary1(torch, ti, tq, dev))
+    if want("ffn_decode"):
+        out.update(extra_ffn_decode(torch, ti, tq, dev))
     if want("context"):
         out.update(extra_context(torch, dev))
     torch.cuda.synchronize()
@@ -401,6 +403,36 @@ def extra_binary1(torch, ti, tq, dev):
                                              "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1)}
             del pool
     return {"binary_gemv": out}
+
+
+def extra_ffn_decode(torch, ti, tq, dev):
+    """Decode FFN with the SwiGLU clamp (gate/up 6912x2560, down 2560x6912,
+    per-row scales): tq_ffn_swiglu_decode, two launches per step, the three
+    packed matrices rotating over 40 sets (about 530 MB)."""
+    d_model, d_ffn = 2560, 6912
+    mats = []
+    for W in (ti.normal_weights(ti.weight_seed(ti.WORKLOADS["ffn"]["cfg"], 2), d_ffn, d_model),
+              ti.workload_weights("ffn", 0), ti.workload_weights("ffn", 1)):
+        p0, s0 = tq.tq_pack_ternary(torch.from_numpy(W).to(dev), "row")
+        mats.append((p0, s0))
+    sets = [[(p.clone(), s) for (p, s) in mats] for _ in range(40)]
+    wbytes = 3 * d_ffn * d_model // 4 + 4 * (2 * d_ffn + d_model)
+    out = {}
+    for b in (1, 4, 16):
+        X = torch.from_numpy(ti.workload_activations("ffn", 0, b)).to(dev).to(torch.bfloat16)
+        Y, buf = tq.tq_ffn_swiglu_decode(X, *mats, d_model, d_ffn)
+        g = capture(torch, lambda: [tq.tq_ffn_swiglu_decode(X, *st, d_model, d_ffn, buffers=buf,
+                                                            Y=Y) for st in sets])
+        timed_graph(torch, g, 2)
+        t = timed_graph(torch, g, 8) / len(sets)
+        # weights + X in, q_x/sx_x out, H out and back in, q_h/sx_h out, Y out
+        nbytes = (wbytes + 2 * b * d_model + (b * d_model + 4 * b) + 2 * 4 * b * d_ffn +
+                  (b * d_ffn + 4 * b) + 4 * b * d_model)
+        gb = nbytes / t / 1e9
+        out[f"b{b}"] = {"us": round(t * 1e6, 3), "bytes": nbytes, "GBs": round(gb, 1),
+                        "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1), "launches": 2}
+    del sets
+    return {"ffn_swiglu_decode": out}
 
 
 def extra_context(torch, dev):

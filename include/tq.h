@@ -193,6 +193,49 @@ tq_status tq_quant_ternary_gemv(const void* X, tq_dtype xdt, int64_t M,
                                 int8_t* q, float* sx, void* Y, tq_dtype ydt,
                                 hipStream_t stream);
 
+/* ---- SwiGLU-clamped decode FFN ---------------------------------------------
+ * (Hetman-2b s.6 SwiGLUClamped: gate = SiLU(W_gate x), up = W_up x, the
+ * product clamped to [-clamp_val, +clamp_val] (default 10) before W_down.)
+ * Here each projection is the ternary layer of this library with the per
+ * token int8 quantiser; the FFN workload (up 6912 x 2560, down 2560 x 6912,
+ * per-row scales) is this shape with d_model = 2560, d_ffn = 6912. */
+
+/* The gate and up projections of the same tokens and the SwiGLU epilogue:
+ * q, sx = tq_quant_act_int8(X, opts); g = tq_ternary_gemv(gate), u =
+ * tq_ternary_gemv(up) (fp32, per-row or per-tensor scales of the two
+ * matrices); H = clamp(g / (1 + exp(-g)) * u, -clamp_val, clamp_val) in fp32,
+ * stored as fp32 or bf16 (hdt).  q and sx are bit-exact; H is within fp32
+ * rounding of that formula (a few ulp: expf and the division).
+ *   X [M, K] fp32/bf16 (1 <= M <= 16); packed_gate / packed_up [N, K/4] and
+ *   their scales as for tq_ternary_gemv; q [M, K], sx [M], H [M, N] outputs.
+ * One token, and up to four tokens with K % 256 == 0, run as one launch
+ * when X and both packed matrices are 16-byte aligned and the quantiser is
+ * plain; otherwise the quantiser runs first.
+ * Errors: those of tq_quant_ternary_gemv for either matrix; hdt not
+ * F32/BF16 is TQ_ERR_DTYPE; clamp_val not finite and > 0 is
+ * TQ_ERR_UNSUPPORTED. */
+tq_status tq_swiglu_gemv(const void* X, tq_dtype xdt, int64_t M, const tq_act_opts* opts,
+                         const uint8_t* packed_gate, const float* scale_gate,
+                         const uint8_t* packed_up, const float* scale_up, tq_gran g,
+                         int64_t N, int64_t K, float clamp_val, int8_t* q, float* sx,
+                         void* H, tq_dtype hdt, hipStream_t stream);
+
+/* The whole decode FFN in two launches: tq_swiglu_gemv (N = d_ffn,
+ * K = d_model, H fp32) and then tq_quant_ternary_gemv(H, TQ_F32, M, plain
+ * quantiser, packed_down [d_model, d_ffn/4], scale_down, g, d_model, d_ffn,
+ * q_h, sx_h, Y, ydt).  opts applies to X only; H is quantised per token with
+ * the plain quantiser (eps 1e-6, no clamp).  Every check of both stages runs
+ * before anything is launched.  All buffers are the caller's: q_x [M,
+ * d_model], sx_x [M], H [M, d_ffn] fp32, q_h [M, d_ffn], sx_h [M], Y [M,
+ * d_model] of ydt. */
+tq_status tq_ffn_swiglu_decode(const void* X, tq_dtype xdt, int64_t M, const tq_act_opts* opts,
+                               const uint8_t* packed_gate, const float* scale_gate,
+                               const uint8_t* packed_up, const float* scale_up,
+                               const uint8_t* packed_down, const float* scale_down, tq_gran g,
+                               int64_t d_model, int64_t d_ffn, float clamp_val, int8_t* q_x,
+                               float* sx_x, float* H, int8_t* q_h, float* sx_h, void* Y,
+                               tq_dtype ydt, hipStream_t stream);
+
 /* ---- 1-bit sign-packed binary weights ------------------------------------
  * (qste 0.1.1 project description, "What it costs and what it buys": a
  * binary matrix of +-1 with a per-row scale is deployed as R*C/8 bytes of

@@ -395,12 +395,17 @@ __device__ inline int dot_slot(int u) { return (u ^ (((u >> 3) ^ (u >> 4)) & 3))
 // bytes, (w >> s) & 0x01010101 holding the signs of codes 8b + s, the token
 // is staged as the matching 8 x 4 byte transpose of each 32-value group, and
 // sum_k q*(2b - 1) = 2 * sum_k q*b - sum_k q.
-template <int SRC, int S, int BITS>
+// DUAL (SwiGLU, BITS 2): every wave also contracts the row of a second
+// matrix (packed2, scale2) against the same staged token, and the epilogue
+// writes h = clamp(silu(g) * u, -clampv, clampv) from the two outputs g and u.
+template <int SRC, int S, int BITS, bool DUAL>
 __global__ __launch_bounds__(kNTd) void k_gemv_dot(
     const void* __restrict__ src, float eps, int clamp, float lo, float hi,
     int8_t* __restrict__ q_out, float* __restrict__ sx_io,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
-    int64_t N, int K, void* __restrict__ Y, int ydt) {
+    int64_t N, int K, void* __restrict__ Y, int ydt,
+    const uint8_t* __restrict__ packed2, const float* __restrict__ scale2, float clampv) {
+  static_assert(!DUAL || BITS == 2, "the SwiGLU pair takes ternary codes");
   extern __shared__ __attribute__((aligned(16))) uint8_t xt[];  // K bytes
   __shared__ float wave_max_part[kStageWaves];
   __shared__ int wave_sum_part[kStageWaves];
@@ -428,10 +433,16 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   // 2. the wave's row in row group rg: chunk lane + 64*sl of each slice,
   // and the row's scale.  Rows >= N (also whole groups past the end) read
   // zeros, so the loads are never conditional.
-  auto load_row = [&](int64_t rg, uint4 (&w)[kSl]) -> float {
+  struct Row {
+    uint4 w[kSl];
+    uint4 w2[DUAL ? kSl : 1];
+    float g, g2;
+  };
+  auto load_one = [&](const uint8_t* base, const float* sc, int64_t rg,
+                      uint4 (&w)[kSl]) -> float {
     const int64_t n = rg * kRowsD + wave;
     const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(packed + (n < N ? n : 0) * rowbytes), static_cast<short>(0),
+        const_cast<uint8_t*>(base + (n < N ? n : 0) * rowbytes), static_cast<short>(0),
         n < N ? rowbytes : 0, kBufRaw);
 #pragma unroll
     for (int sl = 0; sl < kSl; ++sl) {
@@ -445,11 +456,15 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
         w[sl] = make_uint4(v.x, v.y, 0u, 0u);
       }
     }
-    return ydt == TQ_I32 ? 0.f : scale[per_row ? (n < N ? n : N - 1) : 0];
+    return ydt == TQ_I32 ? 0.f : sc[per_row ? (n < N ? n : N - 1) : 0];
   };
-  uint4 wa[kSl], wb[kSl];
+  auto load_row = [&](int64_t rg, Row& r) {
+    r.g = load_one(packed, scale, rg, r.w);
+    if constexpr (DUAL) r.g2 = load_one(packed2, scale2, rg, r.w2);
+  };
+  Row ra, rb;
   int64_t rg = blockIdx.x;
-  float ga = load_row(rg, wa), gb = 0.f;
+  load_row(rg, ra);
   // 3. epilogue operand of the token
   const float sx_in = SRC == 0 ? sx_io[0] : 0.f;
 
@@ -515,7 +530,8 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
     bsum = wave_isum_last(bsum);
     if (lane == kWave - 1) wave_sum_part[wave] = bsum;
   }
-  asm volatile("" ::"v"(ga));
+  asm volatile("" ::"v"(ra.g));
+  if constexpr (DUAL) asm volatile("" ::"v"(ra.g2));
   asm volatile("" ::"v"(sx_in));
   __syncthreads();
   int tsum = 0;
@@ -524,13 +540,13 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   const float sxv = SRC == 0 ? sx_in : tok_sx;
 
   // 6. contraction of the wave's row in group rg
-  auto finish = [&](int64_t rg, const uint4 (&w)[kSl], float gam) {
+  auto finish = [&](int64_t rg, const Row& r) {
     const int64_t n = rg * kRowsD + wave;
-    int acc = 0;
+    int acc = 0, acc2 = 0;
 #pragma unroll
     for (int sl = 0; sl < kSl; ++sl) {
       const int chunk = lane + kWave * sl;
-      const uint32_t words[4] = {w[sl].x, w[sl].y, w[sl].z, w[sl].w};
+      const uint32_t words[4] = {r.w[sl].x, r.w[sl].y, r.w[sl].z, r.w[sl].w};
       if (BITS == 2) {
         const int unit = 4 * chunk;   // first 16-code unit of the chunk
         if (16 * unit >= K) break;    // this chunk, and every later one, is past K
@@ -542,6 +558,14 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
           acc = __builtin_amdgcn_sdot4(x.y, cd.y, acc, false);
           acc = __builtin_amdgcn_sdot4(x.z, cd.z, acc, false);
           acc = __builtin_amdgcn_sdot4(x.w, cd.w, acc, false);
+          if constexpr (DUAL) {
+            const uint32_t words2[4] = {r.w2[sl].x, r.w2[sl].y, r.w2[sl].z, r.w2[sl].w};
+            const v4i cu = decode_codes_strided(words2[j]);
+            acc2 = __builtin_amdgcn_sdot4(x.x, cu.x, acc2, false);
+            acc2 = __builtin_amdgcn_sdot4(x.y, cu.y, acc2, false);
+            acc2 = __builtin_amdgcn_sdot4(x.z, cu.z, acc2, false);
+            acc2 = __builtin_amdgcn_sdot4(x.w, cu.w, acc2, false);
+          }
         }
       } else {
         const int group = 2 * chunk;  // first 32-code group of the chunk
@@ -563,12 +587,21 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
       }
     }
     acc = wave_isum_last(acc);
+    if constexpr (DUAL) acc2 = wave_isum_last(acc2);
     if (lane != kWave - 1 || n >= N) return;
     const int accv = BITS == 2 ? acc - tsum : 2 * acc - tsum;
-    if (ydt == TQ_I32) {
+    if constexpr (DUAL) {
+      const float gv = static_cast<float>(accv) * (r.g * sxv);
+      const float uv = static_cast<float>(acc2 - tsum) * (r.g2 * sxv);
+      const float h = fminf(fmaxf(gv / (1.f + expf(-gv)) * uv, -clampv), clampv);
+      if (ydt == TQ_F32)
+        static_cast<float*>(Y)[n] = h;
+      else
+        static_cast<uint16_t*>(Y)[n] = f32_to_bf16(h);
+    } else if (ydt == TQ_I32) {
       static_cast<int*>(Y)[n] = accv;
     } else {
-      const float y = static_cast<float>(accv) * (gam * sxv);
+      const float y = static_cast<float>(accv) * (r.g * sxv);
       if (ydt == TQ_F32)
         static_cast<float*>(Y)[n] = y;
       else
@@ -583,18 +616,18 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   const int64_t step = gridDim.x;
   for (;;) {
     if (rg + step >= nrg) {
-      finish(rg, wa, ga);
+      finish(rg, ra);
       break;
     }
-    gb = load_row(rg + step, wb);
-    finish(rg, wa, ga);
+    load_row(rg + step, rb);
+    finish(rg, ra);
     rg += step;
     if (rg + step >= nrg) {
-      finish(rg, wb, gb);
+      finish(rg, rb);
       break;
     }
-    ga = load_row(rg + step, wa);
-    finish(rg, wb, gb);
+    load_row(rg + step, ra);
+    finish(rg, rb);
     rg += step;
   }
 }
@@ -611,9 +644,16 @@ int device_cus() {
   return cus[dev];
 }
 
-template <int SRC, int S, int BITS>
+// Second matrix of the SwiGLU pair (DUAL launches only).
+struct DualArgs {
+  const uint8_t* packed2 = nullptr;
+  const float* scale2 = nullptr;
+  float clampv = 0.f;
+};
+
+template <int SRC, int S, int BITS, bool DUAL>
 hipError_t gemv_dot_launch_s(const void* src, const ActParams* p, int8_t* q_out, float* sx,
-                             const GemmArgs& a, hipStream_t s) {
+                             const GemmArgs& a, const DualArgs& d, hipStream_t s) {
   // one workgroup per row group up to two per compute unit (the resident
   // limit of 1024-thread workgroups); past that, workgroups loop over groups
   const int64_t groups = (a.N + kRowsD - 1) / kRowsD;
@@ -621,18 +661,19 @@ hipError_t gemv_dot_launch_s(const void* src, const ActParams* p, int8_t* q_out,
   const int64_t grid = groups < cap ? groups : cap;
   const float eps = p ? p->eps : 0.f, lo = p ? p->eta_min : 0.f, hi = p ? p->eta_max : 0.f;
   const int clamp = p ? p->clamp : 0;
-  hipLaunchKernelGGL((k_gemv_dot<SRC, S, BITS>), dim3(grid), dim3(kNTd), static_cast<size_t>(a.K), s,
-                     src, eps, clamp, lo, hi, q_out, sx, a.packed, a.scale, a.per_row, a.N,
-                     static_cast<int>(a.K), a.Y, a.ydt);
+  hipLaunchKernelGGL((k_gemv_dot<SRC, S, BITS, DUAL>), dim3(grid), dim3(kNTd),
+                     static_cast<size_t>(a.K), s, src, eps, clamp, lo, hi, q_out, sx, a.packed,
+                     a.scale, a.per_row, a.N, static_cast<int>(a.K), a.Y, a.ydt, d.packed2,
+                     d.scale2, d.clampv);
   return hipGetLastError();
 }
 
-template <int SRC, int BITS = 2>
+template <int SRC, int BITS = 2, bool DUAL = false>
 hipError_t gemv_dot_launch(const void* src, const ActParams* p, int8_t* q_out, float* sx,
-                           const GemmArgs& a, hipStream_t s) {
-  if (a.K <= 4096) return gemv_dot_launch_s<SRC, 1, BITS>(src, p, q_out, sx, a, s);
-  if (a.K <= 8192) return gemv_dot_launch_s<SRC, 2, BITS>(src, p, q_out, sx, a, s);
-  return gemv_dot_launch_s<SRC, kMaxSlices, BITS>(src, p, q_out, sx, a, s);
+                           const GemmArgs& a, hipStream_t s, const DualArgs& d = DualArgs()) {
+  if (a.K <= 4096) return gemv_dot_launch_s<SRC, 1, BITS, DUAL>(src, p, q_out, sx, a, d, s);
+  if (a.K <= 8192) return gemv_dot_launch_s<SRC, 2, BITS, DUAL>(src, p, q_out, sx, a, d, s);
+  return gemv_dot_launch_s<SRC, kMaxSlices, BITS, DUAL>(src, p, q_out, sx, a, d, s);
 }
 
 // One token, K a multiple of 64 up to 16384 (the token and its LDS copy are
@@ -742,12 +783,17 @@ __device__ inline void unit_to_f32(const RawUnit<SRC>& u, float (&v)[16]) {
 // byte permute.  The matching token operand is the 4 x 4 byte transpose of
 // the quads 4 (j % 2) / 4 + {0, 2, 4, 6} of the 32 values, so each 32-value
 // group is staged as two transposes, in place.
-template <int SRC, int KBW, int BITS>
+// DUAL (SwiGLU, BITS 2): the row block of a second matrix (packed2, scale2)
+// is contracted against the same token fragments into a second tile, and the
+// epilogue writes h = clamp(silu(g) * u, -clampv, clampv).
+template <int SRC, int KBW, int BITS, bool DUAL>
 __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
     const void* __restrict__ src, float eps, int clamp, float lo, float hi,
     int8_t* __restrict__ q_out, float* __restrict__ sx_io, int M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
-    int64_t N, int K, void* __restrict__ Y, int ydt) {
+    int64_t N, int K, void* __restrict__ Y, int ydt,
+    const uint8_t* __restrict__ packed2, const float* __restrict__ scale2, float clampv) {
+  static_assert(!DUAL || BITS == 2, "the SwiGLU pair takes ternary codes");
   extern __shared__ __attribute__((aligned(16))) uint8_t xs[];  // M x (K + 16) bytes
   __shared__ uint32_t tok_max[kMfmaRows];
   __shared__ float tok_sc[kMfmaRows];  // 127 / eta
@@ -779,7 +825,11 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
       const_cast<uint8_t*>(packed + n0 * rowbytes), static_cast<short>(0),
       static_cast<int>(rows_here * rowbytes), kBufRaw);
   const int fr = lane & 15, fg = lane >> 4;
+  const __amdgpu_buffer_rsrc_t wr2 = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(DUAL ? packed2 + n0 * rowbytes : packed), static_cast<short>(0),
+      DUAL ? static_cast<int>(rows_here * rowbytes) : 0, kBufRaw);
   uint4 wv[KBW];
+  uint4 wv2[DUAL ? KBW : 1];
 #pragma unroll
   for (int i = 0; i < KBW; ++i) {
     const int kb = wave + nw * i;  // blocks past the end read zeros and are skipped
@@ -787,6 +837,9 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
     if (BITS == 2) {
       wv[i] = __builtin_bit_cast(
           uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, fr * rowbytes + 64 * kbl + 16 * fg, 0, 0));
+      if constexpr (DUAL)
+        wv2[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               wr2, fr * rowbytes + 64 * kbl + 16 * fg, 0, 0));
     } else {
       typedef uint32_t u2 __attribute__((ext_vector_type(2)));
       const u2 v = __builtin_bit_cast(
@@ -797,9 +850,10 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
   // epilogue operands of the thread's output (token m, row n0 + n)
   const int em = tid >> 4, en = tid & 15;
   const bool eout = tid < kMfmaRows * kMfmaRows && em < M && n0 + en < N;
-  float egam = 0.f, esx = 0.f;
+  float egam = 0.f, egam2 = 0.f, esx = 0.f;
   if (eout && ydt != TQ_I32) {
     egam = scale[per_row ? n0 + en : 0];
+    if (DUAL) egam2 = scale2[per_row ? n0 + en : 0];
     if (SRC == 0) esx = sx_io[em];
   }
 
@@ -871,7 +925,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
   if (SRC != 0 && eout) esx = tok_sx[em];
 
   // 4. contraction of the wave's blocks
-  v4i acc = {0, 0, 0, 0};
+  v4i acc = {0, 0, 0, 0}, acc2 = {0, 0, 0, 0};
   const bool arow = fr < M;
   const uint8_t* abase = xs + (arow ? fr : 0) * pitch + 64 * fg;
 #pragma unroll
@@ -902,20 +956,46 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
       v4i a = *reinterpret_cast<const v4i*>(abase + 256 * kb + 16 * j);
       if (!arow) a = v4i{0, 0, 0, 0};
       acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+      if constexpr (DUAL) {
+        const uint32_t words2[4] = {wv2[i].x, wv2[i].y, wv2[i].z, wv2[i].w};
+        const v4i c2 = decode_codes_strided(words2[j]);
+        v4i b2;
+        b2.x = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c2.x)));
+        b2.y = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c2.y)));
+        b2.z = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c2.z)));
+        b2.w = static_cast<int>(codes_to_signed(static_cast<uint32_t>(c2.w)));
+        acc2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b2, acc2, 0, 0, 0);
+      }
     }
   }
   __syncthreads();  // every wave is done with the tokens: reuse LDS
 
   // 5. sum the waves' tiles; D layout: lane l holds rows 4 * (l / 16) + i,
   // column l % 16
-  int* red = reinterpret_cast<int*>(xs);  // [nw][16 x 16]
+  int* red = reinterpret_cast<int*>(xs);  // [nw][16 x 16], then the second tile
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[wave * 256 + (4 * fg + i) * 16 + fr] = acc[i];
+  if constexpr (DUAL) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[(nw + wave) * 256 + (4 * fg + i) * 16 + fr] = acc2[i];
+  }
   __syncthreads();
   if (!eout) return;
   int tot = 0;
   for (int w = 0; w < nw; ++w) tot += red[w * 256 + tid];
   const int64_t o = static_cast<int64_t>(em) * N + n0 + en;
+  if constexpr (DUAL) {
+    int tot2 = 0;
+    for (int w = 0; w < nw; ++w) tot2 += red[(nw + w) * 256 + tid];
+    const float gv = static_cast<float>(tot) * (egam * esx);
+    const float uv = static_cast<float>(tot2) * (egam2 * esx);
+    const float h = fminf(fmaxf(gv / (1.f + expf(-gv)) * uv, -clampv), clampv);
+    if (ydt == TQ_F32)
+      static_cast<float*>(Y)[o] = h;
+    else
+      static_cast<uint16_t*>(Y)[o] = f32_to_bf16(h);
+    return;
+  }
   if (ydt == TQ_I32) {
     static_cast<int*>(Y)[o] = tot;
   } else {
@@ -929,9 +1009,9 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
 
 constexpr int64_t kMfmaLdsMax = 120 * 1024;
 
-int64_t mfma_lds_bytes(int64_t M, int64_t K) {
+int64_t mfma_lds_bytes(int64_t M, int64_t K, bool dual = false) {
   const int64_t stage = M * (K + 16);
-  const int64_t red = static_cast<int64_t>(kMfmaMaxWaves) * 256 * 4;
+  const int64_t red = static_cast<int64_t>(kMfmaMaxWaves) * 256 * 4 * (dual ? 2 : 1);
   return stage > red ? stage : red;
 }
 
@@ -942,17 +1022,17 @@ bool mfma_path_ok(int64_t M, int64_t K, const void* packed, const void* act) {
          (reinterpret_cast<uintptr_t>(act) & 15u) == 0u;
 }
 
-template <int SRC, int KBW, int BITS>
+template <int SRC, int KBW, int BITS, bool DUAL>
 hipError_t gemv_mfma_launch_k(const void* src, const ActParams* p, int8_t* q_out, float* sx,
-                              const GemmArgs& a, int waves, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(mfma_lds_bytes(a.M, a.K));
+                              const GemmArgs& a, const DualArgs& d, int waves, hipStream_t s) {
+  const size_t lds = static_cast<size_t>(mfma_lds_bytes(a.M, a.K, DUAL));
   // allow the kernel more than 64 KiB of dynamic LDS, once per device
   static bool attr_set[64] = {false};
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64 || !attr_set[dev]) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_mfma<SRC, KBW, BITS>),
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemv_mfma<SRC, KBW, BITS, DUAL>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(kMfmaLdsMax));
     if (e != hipSuccess) return e;
@@ -961,21 +1041,22 @@ hipError_t gemv_mfma_launch_k(const void* src, const ActParams* p, int8_t* q_out
   const int64_t grid = (a.N + kMfmaRows - 1) / kMfmaRows;
   const float eps = p ? p->eps : 0.f, lo = p ? p->eta_min : 0.f, hi = p ? p->eta_max : 0.f;
   const int clamp = p ? p->clamp : 0;
-  hipLaunchKernelGGL((k_gemv_mfma<SRC, KBW, BITS>), dim3(grid), dim3(waves * kWave), lds, s, src, eps,
-                     clamp, lo, hi, q_out, sx, static_cast<int>(a.M), a.packed, a.scale,
-                     a.per_row, a.N, static_cast<int>(a.K), a.Y, a.ydt);
+  hipLaunchKernelGGL((k_gemv_mfma<SRC, KBW, BITS, DUAL>), dim3(grid), dim3(waves * kWave), lds, s,
+                     src, eps, clamp, lo, hi, q_out, sx, static_cast<int>(a.M), a.packed,
+                     a.scale, a.per_row, a.N, static_cast<int>(a.K), a.Y, a.ydt, d.packed2,
+                     d.scale2, d.clampv);
   return hipGetLastError();
 }
 
-template <int SRC, int BITS = 2>
+template <int SRC, int BITS = 2, bool DUAL = false>
 hipError_t gemv_mfma_launch(const void* src, const ActParams* p, int8_t* q_out, float* sx,
-                            const GemmArgs& a, hipStream_t s) {
+                            const GemmArgs& a, hipStream_t s, const DualArgs& d = DualArgs()) {
   const int64_t nkb = a.K / 256;
   const int waves = static_cast<int>(nkb < kMfmaMaxWaves ? nkb : kMfmaMaxWaves);
   const int64_t per = (nkb + waves - 1) / waves;  // blocks per wave
-  if (per <= 1) return gemv_mfma_launch_k<SRC, 1, BITS>(src, p, q_out, sx, a, waves, s);
-  if (per <= 2) return gemv_mfma_launch_k<SRC, 2, BITS>(src, p, q_out, sx, a, waves, s);
-  return gemv_mfma_launch_k<SRC, 4, BITS>(src, p, q_out, sx, a, waves, s);
+  if (per <= 1) return gemv_mfma_launch_k<SRC, 1, BITS, DUAL>(src, p, q_out, sx, a, d, waves, s);
+  if (per <= 2) return gemv_mfma_launch_k<SRC, 2, BITS, DUAL>(src, p, q_out, sx, a, d, waves, s);
+  return gemv_mfma_launch_k<SRC, 4, BITS, DUAL>(src, p, q_out, sx, a, d, waves, s);
 }
 
 // ------------------------------------------------------------------------
@@ -1025,6 +1106,62 @@ __global__ __launch_bounds__(256) void k_gemv1_generic(
       else
         static_cast<uint16_t*>(Y)[o] = f32_to_bf16(y);
     }
+  }
+}
+
+// ------------------------------------------------------------------------
+// SwiGLU pair, any K % 4 == 0, 1 <= M <= 16, any alignment: one wave per
+// output row contracts the gate and up rows (natural decode, tokens from
+// global memory) and writes h = clamp(silu(g) * u, -clampv, clampv).  The
+// shapes the two fast kernels do not take.
+__global__ __launch_bounds__(256) void k_gemv_swiglu_generic(
+    const int8_t* __restrict__ q, const float* __restrict__ sx, int M,
+    const uint8_t* __restrict__ pg, const float* __restrict__ sg,
+    const uint8_t* __restrict__ pu, const float* __restrict__ su, int per_row, int64_t N,
+    int64_t K, void* __restrict__ H, int hdt, float clampv) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * 4 + threadIdx.x / kWave;
+  if (n >= N) return;  // no barriers in this kernel
+  const int64_t nb = K / 4;
+  const uint8_t* rg = pg + n * nb;
+  const uint8_t* ru = pu + n * nb;
+  int ag[kGemvMaxM], au[kGemvMaxM];
+#pragma unroll
+  for (int m = 0; m < kGemvMaxM; ++m) ag[m] = au[m] = 0;
+  for (int64_t j = lane; j < nb; j += kWave) {
+    const uint32_t bg = rg[j], bu = ru[j];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int cg = static_cast<int>((bg >> (2 * t)) & 3u) - 1;
+      const int cu = static_cast<int>((bu >> (2 * t)) & 3u) - 1;
+#pragma unroll
+      for (int m = 0; m < kGemvMaxM; ++m) {
+        if (m < M) {
+          const int x = q[m * K + 4 * j + t];
+          ag[m] += cg * x;
+          au[m] += cu * x;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < kGemvMaxM; ++m) {
+    if (m < M) {
+      ag[m] = wave_isum_last(ag[m]);
+      au[m] = wave_isum_last(au[m]);
+    }
+  }
+  if (lane != kWave - 1) return;
+  const float gg = sg[per_row ? n : 0], gu = su[per_row ? n : 0];
+  for (int m = 0; m < M; ++m) {
+    const float gv = static_cast<float>(ag[m]) * (gg * sx[m]);
+    const float uv = static_cast<float>(au[m]) * (gu * sx[m]);
+    const float h = fminf(fmaxf(gv / (1.f + expf(-gv)) * uv, -clampv), clampv);
+    const int64_t o = static_cast<int64_t>(m) * N + n;
+    if (hdt == TQ_F32)
+      static_cast<float*>(H)[o] = h;
+    else
+      static_cast<uint16_t*>(H)[o] = f32_to_bf16(h);
   }
 }
 
@@ -1079,6 +1216,45 @@ hipError_t launch_gemv1(const GemmArgs& a, hipStream_t s) {
   const int64_t grid = (a.N + 3) / 4;
   hipLaunchKernelGGL(k_gemv1_generic, dim3(grid), dim3(256), 0, s, a.q, a.sx,
                      static_cast<int>(a.M), a.packed, a.scale, a.per_row, a.N, a.K, a.Y, a.ydt);
+  return hipGetLastError();
+}
+
+bool fused_quant_swiglu_ok(int64_t M, int64_t K, const void* pg, const void* pu, const void* X) {
+  const bool up_ok = (reinterpret_cast<uintptr_t>(pu) & 15u) == 0u;
+  return up_ok && (dot_path_ok(M, K, pg, X) ||
+                   (M <= kFusedMfmaMaxM && mfma_path_ok(M, K, pg, X)));
+}
+
+hipError_t launch_quant_swiglu_gemv(const void* X, int bf16, const ActParams& p, int8_t* q,
+                                    float* sx, const GemmArgs& a, const uint8_t* packed_up,
+                                    const float* scale_up, float clampv, hipStream_t s) {
+  DualArgs d;
+  d.packed2 = packed_up;
+  d.scale2 = scale_up;
+  d.clampv = clampv;
+  if (dot_path_ok(a.M, a.K, a.packed, X))
+    return bf16 ? gemv_dot_launch<2, 2, true>(X, &p, q, sx, a, s, d)
+                : gemv_dot_launch<1, 2, true>(X, &p, q, sx, a, s, d);
+  return bf16 ? gemv_mfma_launch<2, 2, true>(X, &p, q, sx, a, s, d)
+              : gemv_mfma_launch<1, 2, true>(X, &p, q, sx, a, s, d);
+}
+
+hipError_t launch_swiglu_gemv(const GemmArgs& a, const uint8_t* packed_up, const float* scale_up,
+                              float clampv, hipStream_t s) {
+  DualArgs d;
+  d.packed2 = packed_up;
+  d.scale2 = scale_up;
+  d.clampv = clampv;
+  const bool up_ok = (reinterpret_cast<uintptr_t>(packed_up) & 15u) == 0u;
+  float* sxm = const_cast<float*>(a.sx);
+  if (up_ok && dot_path_ok(a.M, a.K, a.packed, a.q))
+    return gemv_dot_launch<0, 2, true>(a.q, nullptr, nullptr, sxm, a, s, d);
+  if (up_ok && mfma_path_ok(a.M, a.K, a.packed, a.q))
+    return gemv_mfma_launch<0, 2, true>(a.q, nullptr, nullptr, sxm, a, s, d);
+  const int64_t grid = (a.N + 3) / 4;
+  hipLaunchKernelGGL(k_gemv_swiglu_generic, dim3(grid), dim3(256), 0, s, a.q, a.sx,
+                     static_cast<int>(a.M), a.packed, a.scale, packed_up, scale_up, a.per_row,
+                     a.N, a.K, a.Y, a.ydt, clampv);
   return hipGetLastError();
 }
 

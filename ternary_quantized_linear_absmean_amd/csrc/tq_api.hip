@@ -203,6 +203,83 @@ tq_status tq_quant_ternary_gemv(const void* X, tq_dtype xdt, int64_t M,
   return hip_status(tq::launch_gemv(a, stream));
 }
 
+// Checks of tq_swiglu_gemv; fills p and tells whether a prologue is on.
+static tq_status check_swiglu(const void* X, tq_dtype xdt, int64_t M, const tq_act_opts* opts,
+                              const uint8_t* pg, const float* sg, const uint8_t* pu,
+                              const float* su, tq_gran g, int64_t N, int64_t K, float clampv,
+                              int8_t* q, float* sx, void* H, tq_dtype hdt, tq::ActParams* p,
+                              bool* prologue) {
+  if (M > tq::kGemvMaxM) return TQ_ERR_SHAPE;
+  if (hdt != TQ_F32 && hdt != TQ_BF16) return TQ_ERR_DTYPE;
+  if (!(clampv > 0.f) || !isfinite(clampv)) return TQ_ERR_UNSUPPORTED;
+  tq_status st = check_quant(X, xdt, M, K, opts, q, sx, p, prologue);
+  if (st != TQ_OK) return st;
+  st = check_contract(q, sx, M, pg, sg, g, N, K, H, hdt);
+  if (st != TQ_OK) return st;
+  return check_contract(q, sx, M, pu, su, g, N, K, H, hdt);
+}
+
+static hipError_t launch_swiglu(const void* X, tq_dtype xdt, int64_t M, const tq::ActParams& p,
+                                bool prologue, const uint8_t* pg, const float* sg,
+                                const uint8_t* pu, const float* su, tq_gran g, int64_t N,
+                                int64_t K, float clampv, int8_t* q, float* sx, void* H,
+                                tq_dtype hdt, hipStream_t stream) {
+  if (N == 0) return launch_quant(X, xdt, M, K, p, prologue, q, sx, stream);
+  const tq::GemmArgs a = make_args(q, sx, M, pg, sg, g, N, K, H, hdt);
+  if (!prologue && tq::fused_quant_swiglu_ok(M, K, pg, pu, X))
+    return tq::launch_quant_swiglu_gemv(X, xdt == TQ_BF16 ? 1 : 0, p, q, sx, a, pu, su, clampv,
+                                        stream);
+  const hipError_t e = launch_quant(X, xdt, M, K, p, prologue, q, sx, stream);
+  if (e != hipSuccess) return e;
+  return tq::launch_swiglu_gemv(a, pu, su, clampv, stream);
+}
+
+tq_status tq_swiglu_gemv(const void* X, tq_dtype xdt, int64_t M, const tq_act_opts* opts,
+                         const uint8_t* packed_gate, const float* scale_gate,
+                         const uint8_t* packed_up, const float* scale_up, tq_gran g, int64_t N,
+                         int64_t K, float clamp_val, int8_t* q, float* sx, void* H, tq_dtype hdt,
+                         hipStream_t stream) {
+  tq::ActParams p;
+  bool prologue = false;
+  const tq_status st = check_swiglu(X, xdt, M, opts, packed_gate, scale_gate, packed_up,
+                                    scale_up, g, N, K, clamp_val, q, sx, H, hdt, &p, &prologue);
+  if (st != TQ_OK || M == 0) return st;
+  return hip_status(launch_swiglu(X, xdt, M, p, prologue, packed_gate, scale_gate, packed_up,
+                                  scale_up, g, N, K, clamp_val, q, sx, H, hdt, stream));
+}
+
+tq_status tq_ffn_swiglu_decode(const void* X, tq_dtype xdt, int64_t M, const tq_act_opts* opts,
+                               const uint8_t* packed_gate, const float* scale_gate,
+                               const uint8_t* packed_up, const float* scale_up,
+                               const uint8_t* packed_down, const float* scale_down, tq_gran g,
+                               int64_t d_model, int64_t d_ffn, float clamp_val, int8_t* q_x,
+                               float* sx_x, float* H, int8_t* q_h, float* sx_h, void* Y,
+                               tq_dtype ydt, hipStream_t stream) {
+  // every check of both stages before anything is launched
+  tq::ActParams p, ph;
+  bool prologue = false, prologue_h = false;
+  tq_status st = check_swiglu(X, xdt, M, opts, packed_gate, scale_gate, packed_up, scale_up, g,
+                              d_ffn, d_model, clamp_val, q_x, sx_x, H, TQ_F32, &p, &prologue);
+  if (st != TQ_OK) return st;
+  st = check_quant(H, TQ_F32, M, d_ffn, nullptr, q_h, sx_h, &ph, &prologue_h);
+  if (st != TQ_OK) return st;
+  st = check_contract(q_h, sx_h, M, packed_down, scale_down, g, d_model, d_ffn, Y, ydt);
+  if (st != TQ_OK || M == 0) return st;
+  hipError_t e = launch_swiglu(X, xdt, M, p, prologue, packed_gate, scale_gate, packed_up,
+                               scale_up, g, d_ffn, d_model, clamp_val, q_x, sx_x, H, TQ_F32,
+                               stream);
+  if (e != hipSuccess) return hip_status(e);
+  if (d_model == 0) return hip_status(launch_quant(H, TQ_F32, M, d_ffn, ph, false, q_h, sx_h,
+                                                   stream));
+  const tq::GemmArgs a = make_args(q_h, sx_h, M, packed_down, scale_down, g, d_model, d_ffn, Y,
+                                   ydt);
+  if (tq::fused_quant_gemv_ok(M, d_ffn, packed_down, H))
+    return hip_status(tq::launch_quant_gemv(H, 0, ph, q_h, sx_h, a, stream));
+  e = launch_quant(H, TQ_F32, M, d_ffn, ph, false, q_h, sx_h, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(tq::launch_gemv(a, stream));
+}
+
 tq_status tq_fwht512(const void* X, tq_dtype xdt, int64_t M, int64_t K, int normalize,
                      float* Y, hipStream_t stream) {
   if (M < 0 || K <= 0 || (K % 512) != 0) return TQ_ERR_SHAPE;

@@ -53,6 +53,16 @@ constexpr int64_t kGemvLdsBytes = 65536;  // activation staging of the small-M G
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t s);
 // the same product with 1-bit sign-packed binary weights ([N][K/8] bytes)
 hipError_t launch_gemv1(const GemmArgs& a, hipStream_t s);
+// SwiGLU pair (a.packed / a.scale = gate, the second matrix = up):
+// h = clamp(silu(g) * u, -clampv, clampv) into a.Y (fp32 or bf16), from int8
+// tokens, or (fused, when fused_quant_swiglu_ok holds) from fp32/bf16 tokens
+// quantised in the same launch
+hipError_t launch_swiglu_gemv(const GemmArgs& a, const uint8_t* packed_up, const float* scale_up,
+                              float clampv, hipStream_t s);
+bool fused_quant_swiglu_ok(int64_t M, int64_t K, const void* pg, const void* pu, const void* X);
+hipError_t launch_quant_swiglu_gemv(const void* X, int bf16, const ActParams& p, int8_t* q,
+                                    float* sx, const GemmArgs& a, const uint8_t* packed_up,
+                                    const float* scale_up, float clampv, hipStream_t s);
 // quantise X (plain path) and apply the GEMV in one launch; only when
 // fused_quant_gemv_ok() holds
 bool fused_quant_gemv_ok(int64_t M, int64_t K, const void* packed, const void* X);

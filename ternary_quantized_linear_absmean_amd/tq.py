@@ -33,7 +33,8 @@ MODES = {"ternary": 0, "binary": 1}
 EXPORTED = ["tq_packed_bytes", "tq_pack_workspace_bytes", "tq_pack_ternary",
             "tq_quant_act_int8", "tq_fwht512", "tq_ternary_gemv", "tq_ternary_gemm",
             "tq_quant_ternary_gemv", "tq_packed1_bytes", "tq_pack_binary1",
-            "tq_binary1_gemv", "tq_status_str", "tq_last_hip_error", "tq_version"]
+            "tq_binary1_gemv", "tq_swiglu_gemv", "tq_ffn_swiglu_decode", "tq_status_str",
+            "tq_last_hip_error", "tq_version"]
 
 _vp = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -62,6 +63,13 @@ for _name in ("tq_ternary_gemv", "tq_ternary_gemm"):
 _lib.tq_quant_ternary_gemv.argtypes = [_vp, _int, _i64, ctypes.POINTER(TqActOpts), _vp, _vp,
                                        _int, _i64, _i64, _vp, _vp, _vp, _int, _vp]
 _lib.tq_quant_ternary_gemv.restype = _int
+_lib.tq_swiglu_gemv.argtypes = [_vp, _int, _i64, ctypes.POINTER(TqActOpts), _vp, _vp, _vp, _vp,
+                                _int, _i64, _i64, ctypes.c_float, _vp, _vp, _vp, _int, _vp]
+_lib.tq_swiglu_gemv.restype = _int
+_lib.tq_ffn_swiglu_decode.argtypes = [_vp, _int, _i64, ctypes.POINTER(TqActOpts), _vp, _vp, _vp,
+                                      _vp, _vp, _vp, _int, _i64, _i64, ctypes.c_float, _vp, _vp,
+                                      _vp, _vp, _vp, _vp, _int, _vp]
+_lib.tq_ffn_swiglu_decode.restype = _int
 _lib.tq_packed1_bytes.argtypes = [_i64]
 _lib.tq_packed1_bytes.restype = ctypes.c_size_t
 _lib.tq_pack_binary1.argtypes = [_vp, _i64, _i64, _int, _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -295,6 +303,65 @@ def tq_quant_ternary_gemv(X: torch.Tensor, packed, scale, N: int, K: int,
                                       _ptr(Y), DTYPES[out_dtype], _stream(stream)),
            "tq_quant_ternary_gemv")
     return Y, q, sx
+
+
+def tq_swiglu_gemv(X: torch.Tensor, packed_gate, scale_gate, packed_up, scale_up, N: int,
+                   K: int, granularity: str = "row", clamp_val: float = 10.0,
+                   out_dtype: str = "f32", eps: float = 1e-6, clamp=None, rmsnorm: bool = False,
+                   rms_eps: float = 1e-6, rms_weight: torch.Tensor | None = None,
+                   fwht_block: int = 0, q: torch.Tensor | None = None,
+                   sx: torch.Tensor | None = None, H: torch.Tensor | None = None, stream=None):
+    """Gate and up projections of X [M, K] (M <= 16) with the SwiGLU-clamp
+    epilogue -> (H [M, N], q int8 [M, K], sx fp32 [M])."""
+    for t, name in ((X, "X"), (packed_gate, "packed_gate"), (scale_gate, "scale_gate"),
+                    (packed_up, "packed_up"), (scale_up, "scale_up")):
+        _dev(t, name)
+    if X.dtype not in _ACT_DT or X.dim() != 2:
+        raise ValueError("X must be a 2-D float32 or bfloat16 tensor")
+    M = X.shape[0]
+    if q is None:
+        q = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if sx is None:
+        sx = torch.empty((M,), dtype=torch.float32, device=X.device)
+    if H is None:
+        H = torch.empty((M, N), dtype=_Y_TORCH[out_dtype], device=X.device)
+    opts = _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block)
+    _check(_lib.tq_swiglu_gemv(X.data_ptr(), _ACT_DT[X.dtype], M, ctypes.byref(opts),
+                               packed_gate.data_ptr(), scale_gate.data_ptr(),
+                               packed_up.data_ptr(), scale_up.data_ptr(),
+                               GRANULARITY[granularity], N, K, clamp_val, _ptr(q), _ptr(sx),
+                               _ptr(H), DTYPES[out_dtype], _stream(stream)), "tq_swiglu_gemv")
+    return H, q, sx
+
+
+def tq_ffn_swiglu_decode(X: torch.Tensor, gate, up, down, d_model: int, d_ffn: int,
+                         granularity: str = "row", clamp_val: float = 10.0,
+                         out_dtype: str = "f32", eps: float = 1e-6, clamp=None,
+                         buffers: dict | None = None, Y: torch.Tensor | None = None,
+                         stream=None):
+    """Decode FFN: gate, up, down are (packed, scale) pairs.  Returns
+    (Y [M, d_model], buffers) where buffers holds q_x, sx_x, H, q_h, sx_h."""
+    _dev(X, "X")
+    if X.dtype not in _ACT_DT or X.dim() != 2:
+        raise ValueError("X must be a 2-D float32 or bfloat16 tensor")
+    M = X.shape[0]
+    b = dict(buffers or {})
+    dv = X.device
+    b.setdefault("q_x", torch.empty((M, d_model), dtype=torch.int8, device=dv))
+    b.setdefault("sx_x", torch.empty((M,), dtype=torch.float32, device=dv))
+    b.setdefault("H", torch.empty((M, d_ffn), dtype=torch.float32, device=dv))
+    b.setdefault("q_h", torch.empty((M, d_ffn), dtype=torch.int8, device=dv))
+    b.setdefault("sx_h", torch.empty((M,), dtype=torch.float32, device=dv))
+    if Y is None:
+        Y = torch.empty((M, d_model), dtype=_Y_TORCH[out_dtype], device=dv)
+    opts = _opts(eps, clamp, False, 1e-6, None, 0)
+    _check(_lib.tq_ffn_swiglu_decode(
+        X.data_ptr(), _ACT_DT[X.dtype], M, ctypes.byref(opts), gate[0].data_ptr(),
+        gate[1].data_ptr(), up[0].data_ptr(), up[1].data_ptr(), down[0].data_ptr(),
+        down[1].data_ptr(), GRANULARITY[granularity], d_model, d_ffn, clamp_val,
+        _ptr(b["q_x"]), _ptr(b["sx_x"]), _ptr(b["H"]), _ptr(b["q_h"]), _ptr(b["sx_h"]),
+        _ptr(Y), DTYPES[out_dtype], _stream(stream)), "tq_ffn_swiglu_decode")
+    return Y, b
 
 
 def raw_library() -> ctypes.CDLL:

@@ -116,6 +116,31 @@ def test_binary1_validation():
     assert tqmod.tq_packed1_bytes(9) == 2
 
 
+def test_swiglu_validation():
+    P = 0x10000
+    f = lib.tq_swiglu_gemv
+    opts = None
+    # (X, xdt, M, opts, pg, sg, pu, su, g, N, K, clamp, q, sx, H, hdt, stream)
+    assert f(P, 1, 17, opts, P, P, P, P, 1, 16, 64, 10.0, P, P, P, 0, None) == SHAPE
+    assert f(P, 1, 1, opts, P, P, P, P, 1, 16, 64, 10.0, P, P, P, 2, None) == DTYPE   # int32 H
+    assert f(P, 1, 1, opts, P, P, P, P, 1, 16, 64, 0.0, P, P, P, 0, None) == UNSUP
+    assert f(P, 1, 1, opts, P, P, P, P, 1, 16, 64, float("inf"), P, P, P, 0, None) == UNSUP
+    assert f(P, 1, 1, opts, P, P, None, P, 1, 16, 64, 10.0, P, P, P, 0, None) == NULL
+    assert f(P, 1, 1, opts, P, P, P, P + 2, 1, 16, 64, 10.0, P, P, P, 0, None) == ALIGN
+    assert f(P, 1, 1, opts, P, P, P, P, 1, 16, 62, 10.0, P, P, P, 0, None) == SHAPE
+    assert f(None, 1, 0, opts, None, None, None, None, 1, 16, 64, 10.0, None, None, None, 0,
+             None) == OK
+    d = lib.tq_ffn_swiglu_decode
+    # (X, xdt, M, opts, pg, sg, pu, su, pd, sd, g, d_model, d_ffn, clamp,
+    #  q_x, sx_x, H, q_h, sx_h, Y, ydt, stream): a bad down stage fails before launch
+    assert d(P, 1, 1, None, P, P, P, P, None, P, 1, 64, 128, 10.0, P, P, P, P, P, P, 0,
+             None) == NULL
+    assert d(P, 1, 1, None, P, P, P, P, P, P, 1, 64, 128, 10.0, P, P, P, P, P, P, 3,
+             None) == DTYPE
+    assert d(P, 1, 1, None, P, P, P, P, P, P, 1, 64, 128, 10.0, P, P, P + 2, P, P, P, 0,
+             None) == ALIGN
+
+
 def test_pack_validation():
     P = 0x10000
     f = lib.tq_pack_ternary

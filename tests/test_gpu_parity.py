@@ -733,3 +733,80 @@ def test_binary1_matches_two_bit_binary():
         y2 = host(tq.tq_ternary_gemv(q, sx, p2, s2, N, K, "row", ydt))
         y1 = host(tq.tq_binary1_gemv(q, sx, p1, s1, N, K, "row", ydt))
         np.testing.assert_array_equal(y1, y2)
+
+
+# ------------------------------------------------- SwiGLU-clamped decode FFN
+
+def _ffn_mats(d_model, d_ffn, gran="row"):
+    """gate and up [d_ffn, d_model], down [d_model, d_ffn]: up and down are
+    the FFN workload's matrices when the shapes match, the gate is the next
+    matrix of the same generator."""
+    if (d_ffn, d_model) == tuple(ti.WORKLOADS["ffn"]["mats"][0]):
+        Wu = ti.workload_weights("ffn", 0)
+        Wd = ti.workload_weights("ffn", 1)
+        Wg = ti.normal_weights(ti.weight_seed(ti.WORKLOADS["ffn"]["cfg"], 2), d_ffn, d_model)
+    else:
+        Wg = ti.normal_weights(4100 + d_ffn, d_ffn, d_model)
+        Wu = ti.normal_weights(4200 + d_ffn, d_ffn, d_model)
+        Wd = ti.normal_weights(4300 + d_ffn, d_model, d_ffn)
+    return [oracle.pack_ternary(W, gran) for W in (Wg, Wu, Wd)]
+
+
+def _assert_h_close(h, href):
+    # fp32 evaluation of silu(g) * u (expf, a division, products) against
+    # the fp64 formula on the exact accumulators
+    tol = 1e-5 * np.abs(href) + 1e-30
+    bad = np.abs(h.astype(np.float64) - href) > tol
+    assert not bad.any(), (np.argwhere(bad)[:5], h[bad][:5], href[bad][:5])
+
+
+SWIGLU_CASES = [(1, 6912, 2560, "bf16", "row"), (4, 6912, 2560, "f32", "row"),
+                (16, 300, 4096, "bf16", "tensor"), (2, 33, 256, "f32", "row"),
+                (3, 70, 1000, "bf16", "row"), (1, 50, 4100, "f32", "tensor")]
+
+
+@pytest.mark.parametrize("M,N,K,dtype,gran", SWIGLU_CASES)
+def test_swiglu_gemv(M, N, K, dtype, gran):
+    gate, up, _ = _ffn_mats(K, N, gran)
+    X = ti.activations(4400 + M + N, M, K, dtype=dtype)
+    say(f"swiglu M={M} N={N} K={K} {dtype} {gran}")
+    qr, sr = oracle.quant_act_int8(X)
+    g = oracle.epilogue(oracle.contract(qr, gate[0], K), gate[1], sr)
+    u = oracle.epilogue(oracle.contract(qr, up[0], K), up[1], sr)
+    for clamp_val in (10.0, 0.002):   # the second binds on most outputs
+        href = oracle.swiglu_clamped(g, u, clamp_val)
+        H, q, sx = tq.tq_swiglu_gemv(x_to_device(X, dtype), dev(gate[0]), dev(gate[1]),
+                                     dev(up[0]), dev(up[1]), N, K, gran, clamp_val)
+        np.testing.assert_array_equal(host(q), qr)
+        np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sr))
+        _assert_h_close(host(H), href)
+        Hb, _, _ = tq.tq_swiglu_gemv(x_to_device(X, dtype), dev(gate[0]), dev(gate[1]),
+                                     dev(up[0]), dev(up[1]), N, K, gran, clamp_val,
+                                     out_dtype="bf16")
+        assert_bf16_close(host(Hb.view(torch.int16)).view(np.uint16), href)
+
+
+@pytest.mark.parametrize("b", [1, 4, 16])
+def test_ffn_swiglu_decode_workload(b):
+    d_model, d_ffn = 2560, 6912
+    gate, up, down = _ffn_mats(d_model, d_ffn)
+    X = ti.workload_activations("ffn", 0, b)
+    say(f"ffn decode b={b}")
+    Xd = x_to_device(X, "bf16")
+    Y, buf = tq.tq_ffn_swiglu_decode(Xd, [dev(t) for t in gate], [dev(t) for t in up],
+                                     [dev(t) for t in down], d_model, d_ffn)
+    href, _, _, _ = oracle.ffn_swiglu_decode(X, gate, up, down)
+    H = host(buf["H"])
+    _assert_h_close(H, href)
+    # the down stage from the GPU's own H: the int8 decisions on equal inputs
+    qh, sh = oracle.quant_act_int8(H)
+    np.testing.assert_array_equal(host(buf["q_h"]), qh)
+    np.testing.assert_array_equal(f32_bits(host(buf["sx_h"])), f32_bits(sh))
+    y_ref = oracle.epilogue(oracle.contract(qh, down[0], d_ffn), down[1], sh)
+    assert_y_close(host(Y), y_ref)
+    # same as the calls one by one
+    H2, q2, s2 = tq.tq_swiglu_gemv(Xd, dev(gate[0]), dev(gate[1]), dev(up[0]), dev(up[1]),
+                                   d_ffn, d_model)
+    np.testing.assert_array_equal(host(H2), H)
+    Y2, _, _ = tq.tq_quant_ternary_gemv(H2, dev(down[0]), dev(down[1]), d_model, d_ffn, "row")
+    np.testing.assert_array_equal(host(Y2), host(Y))
