@@ -179,11 +179,12 @@ tq_status tq_ternary_gemm(const int8_t* q, const float* sx, int64_t M,
  * fusion; s.7 GEMV).  The results -- q, sx and Y -- are bit for bit those of
  * tq_quant_act_int8(X, xdt, M, K, opts, q, sx) followed by
  * tq_ternary_gemv(q, sx, M, packed, scale, g, N, K, Y, ydt).
- * With the plain quantiser (no RMSNorm / FWHT), M <= 4, K % 64 == 0 and
- * 16-byte aligned X and packed, most shapes run as a single kernel launch:
- * every workgroup quantises the tokens itself into LDS and workgroup 0
- * writes q and sx.  Otherwise (M > 4, a prologue, other shapes) it is the
- * two launches.  The results do not depend on which.
+ * With the plain quantiser (no RMSNorm / FWHT), 16-byte aligned X and
+ * packed, K % 64 == 0, and one token or up to four tokens with M*K <= 16384,
+ * this is a single kernel launch: every workgroup quantises the tokens
+ * itself into LDS and workgroup 0 writes q and sx.  Otherwise (more token
+ * work, a prologue, other shapes) it is the two launches, which are then the
+ * faster form.  The results do not depend on which.
  *   X [M, K] fp32/bf16; q [M, K] int8 and sx [M] fp32 are outputs (required);
  *   packed, scale, g, N, K, Y, ydt as for tq_ternary_gemv.
  * Errors: those of the two calls; M > 16 is TQ_ERR_SHAPE. */

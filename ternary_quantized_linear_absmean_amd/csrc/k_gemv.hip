@@ -1188,13 +1188,20 @@ hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
   return aligned ? gemv_dispatch<true>(a, s) : gemv_dispatch<false>(a, s);
 }
 
-// Fusing the quantiser costs every workgroup the whole token work, which
-// beyond four tokens is more than a separate quantiser launch.
+// Fusing the quantiser costs every workgroup the whole token work (M*K
+// values); past four tokens or 16384 values that is more than a separate
+// quantiser launch (measured at the FFN and 4096 x 4096 shapes).
 constexpr int64_t kFusedMfmaMaxM = 4;
+constexpr int64_t kFusedMfmaMaxMK = 16384;
+
+bool fused_mfma_ok(int64_t M, int64_t K, const void* packed, const void* X) {
+  return M <= kFusedMfmaMaxM && M * K <= kFusedMfmaMaxMK && mfma_path_ok(M, K, packed, X);
+}
 
 bool fused_quant_gemv_ok(int64_t M, int64_t K, const void* packed, const void* X) {
-  return dot_path_ok(M, K, packed, X) ||
-         (M <= kFusedMfmaMaxM && mfma_path_ok(M, K, packed, X)) || lds_path_ok(M, K, packed, X);
+  // the LDS-tiled fused kernel only where no matrix-core GEMV takes the shape
+  return dot_path_ok(M, K, packed, X) || fused_mfma_ok(M, K, packed, X) ||
+         (!mfma_path_ok(M, K, packed, X) && lds_path_ok(M, K, packed, X));
 }
 
 hipError_t launch_quant_gemv(const void* X, int bf16, const ActParams& p, int8_t* q,
@@ -1202,7 +1209,7 @@ hipError_t launch_quant_gemv(const void* X, int bf16, const ActParams& p, int8_t
   const int M = static_cast<int>(a.M);
   if (dot_path_ok(a.M, a.K, a.packed, X))
     return bf16 ? gemv_dot_launch<2>(X, &p, q, sx, a, s) : gemv_dot_launch<1>(X, &p, q, sx, a, s);
-  if (a.M <= kFusedMfmaMaxM && mfma_path_ok(a.M, a.K, a.packed, X))
+  if (fused_mfma_ok(a.M, a.K, a.packed, X))
     return bf16 ? gemv_mfma_launch<2>(X, &p, q, sx, a, s) : gemv_mfma_launch<1>(X, &p, q, sx, a, s);
   return bf16 ? gemv_lds_launch<2>(X, M, &p, q, sx, a, s)
               : gemv_lds_launch<1>(X, M, &p, q, sx, a, s);
@@ -1221,8 +1228,7 @@ hipError_t launch_gemv1(const GemmArgs& a, hipStream_t s) {
 
 bool fused_quant_swiglu_ok(int64_t M, int64_t K, const void* pg, const void* pu, const void* X) {
   const bool up_ok = (reinterpret_cast<uintptr_t>(pu) & 15u) == 0u;
-  return up_ok && (dot_path_ok(M, K, pg, X) ||
-                   (M <= kFusedMfmaMaxM && mfma_path_ok(M, K, pg, X)));
+  return up_ok && (dot_path_ok(M, K, pg, X) || fused_mfma_ok(M, K, pg, X));
 }
 
 hipError_t launch_quant_swiglu_gemv(const void* X, int bf16, const ActParams& p, int8_t* q,

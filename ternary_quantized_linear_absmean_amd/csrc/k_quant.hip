@@ -111,6 +111,55 @@ __global__ __launch_bounds__(kNT) void k_quant_plain(const T* __restrict__ X, in
   if (threadIdx.x == 0) sx[row] = eta / 127.f;
 }
 
+// Few tokens: a token's values are read once.  1024 threads per token, each
+// holding CH chunks of 8 values in registers; wave maxima (DPP) meet in LDS.
+// Same eta, scale and codes as k_quant_plain (the max is exact).
+constexpr int kNTs = 1024;
+
+template <typename T, bool VEC, int CH>
+__global__ __launch_bounds__(kNTs) void k_quant_small(const T* __restrict__ X, int64_t K,
+                                                      float eps, int clamp, float lo, float hi,
+                                                      int8_t* __restrict__ q,
+                                                      float* __restrict__ sx) {
+  __shared__ float part[kNTs / kWave];
+  const int64_t row = blockIdx.x;
+  const T* x = X + row * K;
+  int8_t* qo = q + row * K;
+  const int64_t nchunk = (K + 7) / 8;
+  const int tid = threadIdx.x;
+  float v[CH][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = tid + static_cast<int64_t>(kNTs) * i;
+    if (c < nchunk) {
+      load8<T, VEC>(x + 8 * c, K - 8 * c, v[i]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[i][e]));
+    }
+  }
+  amax = wave_max_last(amax);
+  if ((tid & (kWave - 1)) == kWave - 1) part[tid / kWave] = amax;
+  __syncthreads();
+  amax = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNTs / kWave; ++w) amax = fmaxf(amax, part[w]);
+  float eta = fmaxf(amax, eps);
+  if (clamp) eta = fminf(fmaxf(eta, lo), hi);
+  const float s = 127.f / eta;
+#pragma unroll
+  for (int i = 0; i < CH; ++i) {
+    const int64_t c = tid + static_cast<int64_t>(kNTs) * i;
+    if (c < nchunk) {
+      uint32_t b[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) b[e] = quant_byte(v[i][e], s);
+      store8_q<VEC>(qo + 8 * c, K - 8 * c, b);
+    }
+  }
+  if (tid == 0) sx[row] = eta / 127.f;
+}
+
 // ---------------------------------------------------------------- FWHT-512
 
 // In-place FWHT of one 512-block held by a wave: lane l holds elements
@@ -261,10 +310,39 @@ hipError_t prologue_dispatch(const T* X, int64_t M, int64_t K, const ActParams& 
 
 }  // namespace
 
+template <typename T, bool VEC>
+hipError_t quant_small_launch(const T* x, int64_t M, int64_t K, const ActParams& p, int8_t* q,
+                              float* sx, hipStream_t s) {
+  const int64_t ch = ((K + 7) / 8 + kNTs - 1) / kNTs;  // chunks per thread
+#define TQ_QSMALL(C)                                                                      \
+  hipLaunchKernelGGL((k_quant_small<T, VEC, C>), dim3(M), dim3(kNTs), 0, s, x, K, p.eps, \
+                     p.clamp, p.eta_min, p.eta_max, q, sx)
+  if (ch <= 1) TQ_QSMALL(1);
+  else if (ch <= 2) TQ_QSMALL(2);
+  else TQ_QSMALL(4);
+#undef TQ_QSMALL
+  return hipGetLastError();
+}
+
+// Tokens below which one workgroup per token leaves the GPU latency-bound:
+// there, each token's values are read once (k_quant_small, K <= 32768).
+constexpr int64_t kQuantSmallM = 64;
+constexpr int64_t kQuantSmallMaxK = 4 * 8 * kNTs;
+
 hipError_t launch_quant_plain(const void* X, int bf16, int64_t M, int64_t K,
                               const ActParams& p, int8_t* q, float* sx, hipStream_t s) {
   const bool vec = (K % 8) == 0 && (reinterpret_cast<uintptr_t>(X) & 15u) == 0u &&
                    (reinterpret_cast<uintptr_t>(q) & 7u) == 0u;
+  if (M < kQuantSmallM && K <= kQuantSmallMaxK) {
+    if (bf16) {
+      const uint16_t* x = static_cast<const uint16_t*>(X);
+      return vec ? quant_small_launch<uint16_t, true>(x, M, K, p, q, sx, s)
+                 : quant_small_launch<uint16_t, false>(x, M, K, p, q, sx, s);
+    }
+    const float* x = static_cast<const float*>(X);
+    return vec ? quant_small_launch<float, true>(x, M, K, p, q, sx, s)
+               : quant_small_launch<float, false>(x, M, K, p, q, sx, s);
+  }
   if (bf16) {
     const uint16_t* x = static_cast<const uint16_t*>(X);
     if (vec)
