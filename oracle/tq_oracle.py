@@ -20,6 +20,11 @@ Sources (cited by page title and section):
 * BitRASP, core_math.py -- ``fake_quant_int`` (per-token absmax int8),
   ``ternarize_weight`` (per-output-row absmean), ``additive_ternary_linear_int8``
   (y[o] = sum of x where W=+1 minus sum of x where W=-1).
+* Foundry, docs/quantization.md -- "Ternary Training (Backward Pass +
+  Stochastic Flip) / Backward Pass": the input gradient multiplies the output
+  gradient against the packed ternary weights, summing over N, accumulated
+  with += into a caller-zeroed buffer; the weight gradient is the plain float
+  product X^T dY with no ternary part and no scale.
 * qste 0.1.1 project description -- "What it costs and what it buys"
   (binary +-1 weights with a per-row scale, deployed as R*C/8 bytes of
   packed signs plus 4*R bytes of scales).
@@ -43,6 +48,10 @@ in the design notes):
 * 1-bit sign packing of binary weights (qste "What it costs and what it
   buys" gives the size, not the layout): eight signs per byte, LSB-first,
   bit 1 for +1 and bit 0 for -1, rows of K/8 bytes along K.
+* Backward through the input: the layer computes y = gamma * x w^T (the
+  activation quantiser passed straight through, as the pages' straight-
+  through estimator does), so dX = (dY * gamma) w; the page does not say
+  whether its input gradient applies the scale, and the gradient of y does.
 * The fused RMSNorm -> FWHT -> int8 prologue uses the exact cancellation of
   the positive per-token RMS factor and the 1/sqrt(512) normaliser inside
   absmax quantisation (see ``rmsnorm_fwht_quant``).
@@ -520,6 +529,23 @@ def ternary_linear(X: np.ndarray, W: np.ndarray, granularity: str = "tensor",
     acc = contract(q, packed, k)
     y = epilogue(acc, gam, sx)
     return dict(packed=packed, scale=gam, q=q, sx=sx, acc=acc, y=y)
+
+
+def backward_input(dY: np.ndarray, packed: np.ndarray, gammas: np.ndarray, k: int) -> np.ndarray:
+    """dX[m, k] = sum_n dY[m, n] * gamma_n * w[n, k] in fp64 (Foundry
+    "Backward Pass", fq_matmul_ternary_backward_input; gamma per tensor or
+    per output row n).  The caller adds it to its accumulator."""
+    w = unpack_codes(packed, k).astype(np.float64)
+    g = np.asarray(gammas, dtype=np.float64)
+    dYs = np.asarray(dY, dtype=np.float64) * (g if g.size > 1 else g[0])
+    return dYs @ w
+
+
+def backward_weight(X: np.ndarray, dY: np.ndarray) -> np.ndarray:
+    """dW[n, k] = sum_m dY[m, n] * X[m, k] in fp64 (Foundry "Backward Pass",
+    fq_matmul_ternary_backward_weight: the float product X^T dY, no scale),
+    laid out [N, K] like the weight."""
+    return np.asarray(dY, dtype=np.float64).T @ np.asarray(X, dtype=np.float64)
 
 
 SWIGLU_CLAMP = 10.0           # Hetman-2b s.6 default clamp value

@@ -648,3 +648,48 @@ def test_ffn_swiglu_decode_matches_stepwise_float_reference():
     wd = oracle.unpack_codes(mats[2][0], f).astype(np.float64) * mats[2][1][:, None]
     np.testing.assert_allclose(y, (hq.astype(np.float64) * hs[:, None]) @ wd.T, rtol=1e-12,
                                atol=1e-15)
+
+
+# ---------------------------------------------------------------- backward
+
+def test_backward_adjoint_identities():
+    # the layer y = gamma * X w^T is linear in X and in W: its gradients are
+    # fixed by <dY, y(V)> = <dX, V> and <dY, X U^T> = <dW, U> for any V, U
+    rng = np.random.default_rng(11)
+    M, N, K = 5, 7, 24
+    w = ti.random_ternary(12, N, K)
+    packed = oracle.pack_codes(w)
+    for gam in (np.array([0.37], np.float32), (rng.random(N) + 0.5).astype(np.float32)):
+        dY = rng.standard_normal((M, N))
+        V = rng.standard_normal((M, K))
+        g = gam.astype(np.float64) if gam.size > 1 else np.full(N, float(gam[0]))
+        yV = V @ (w.astype(np.float64) * g[:, None]).T        # y(V) = gamma * V w^T
+        dX = oracle.backward_input(dY, packed, gam, K)
+        assert abs(np.sum(dY * yV) - np.sum(dX * V)) < 1e-10 * np.sum(np.abs(dY * yV))
+    X = rng.standard_normal((M, K))
+    U = rng.standard_normal((N, K))
+    dW = oracle.backward_weight(X, dY)
+    assert dW.shape == (N, K)
+    assert abs(np.sum(dY * (X @ U.T)) - np.sum(dW * U)) < 1e-10 * np.sum(np.abs(dY * (X @ U.T)))
+
+
+def test_backward_brute_force():
+    rng = np.random.default_rng(13)
+    M, N, K = 2, 3, 8
+    w = ti.random_ternary(14, N, K)
+    packed = oracle.pack_codes(w)
+    gam = np.array([0.5, 2.0, 0.25], np.float32)
+    dY = rng.standard_normal((M, N))
+    X = rng.standard_normal((M, K))
+    dX = oracle.backward_input(dY, packed, gam, K)
+    dW = oracle.backward_weight(X, dY)
+    for m in range(M):
+        for k in range(K):
+            ref = 0.0
+            for n in range(N):
+                ref += dY[m, n] * float(gam[n]) * int(w[n, k])
+            assert abs(dX[m, k] - ref) < 1e-12
+    for n in range(N):
+        for k in range(K):
+            ref = sum(dY[m, n] * X[m, k] for m in range(M))
+            assert abs(dW[n, k] - ref) < 1e-12
