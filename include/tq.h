@@ -272,6 +272,35 @@ tq_status tq_binary1_gemv(const int8_t* q, const float* sx, int64_t M,
                           int64_t N, int64_t K, void* Y, tq_dtype ydt,
                           hipStream_t stream);
 
+/* ---- backward through the packed weights ---------------------------------
+ * (Foundry, docs/quantization.md, "Ternary Training (Backward Pass +
+ * Stochastic Flip) / Backward Pass": the input gradient multiplies the
+ * output gradient against the packed ternary weights, with the same unpacking
+ * as the forward, summing over the N outputs.)  The forward being
+ * y[m, o] = gamma_o * sum_k x[m, k] w[o, k], this call takes the scale into
+ * the gradient (the page's example uses one scale per tensor; a per-row
+ * scale multiplies each output's gradient):
+ *     dX[m, k] = sum_n dY[m, n] * gamma_n * w[n, k]
+ *   dY       [M, N] fp32 or bf16 (dydt), element-aligned.
+ *   packed   [N, K/4] codes of tq_pack_ternary (K % 4 == 0).
+ *   scale    fp32, [1] (TQ_PER_TENSOR) or [N] (TQ_PER_ROW).
+ *   dX       [M, K] fp32, 4-byte aligned.  accumulate = 0 overwrites dX;
+ *            accumulate != 0 adds the result to it (the page's += form).
+ * Arithmetic: each product dY * gamma_n * w is formed exactly (w is -1, 0 or
+ * +1; with a per-row scale, dY * gamma_n is first rounded to fp32) and the
+ * sum over n is accumulated in fp32, so the error is that of an fp32 dot
+ * product of length N; a per-tensor gamma multiplies the fp32 sum.  Inputs
+ * need |dY * gamma| < 3.3e38 (the bf16 range).  N % 8 == 0 with 16-byte
+ * aligned dY, dX (and scale, per row) runs on the matrix cores; other shapes
+ * on a simple kernel.  N == 0 writes zeros (or leaves dX, with accumulate).
+ * Errors: M, N < 0, K <= 0 or K % 4 != 0 is TQ_ERR_SHAPE; dydt other than
+ * F32/BF16 is TQ_ERR_DTYPE; NULL dX, or NULL dY, packed or scale with
+ * M, N > 0, is TQ_ERR_NULL. */
+tq_status tq_ternary_backward_input(const void* dY, tq_dtype dydt, int64_t M,
+                                    const uint8_t* packed, const float* scale, tq_gran g,
+                                    int64_t N, int64_t K, float* dX, int accumulate,
+                                    hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* tq_status_str(tq_status s);
 

@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
 ARCH = "gfx950"
-SOURCES = ["tq_api.hip", "k_pack.hip", "k_quant.hip", "k_gemv.hip", "k_gemm.hip"]
+SOURCES = ["tq_api.hip", "k_pack.hip", "k_quant.hip", "k_gemv.hip", "k_gemm.hip", "k_bwd.hip"]
 
 # -ffp-contract=off: the quantisers' fp32 products must round on their own
 # (no fused multiply-add) to match the stated expression order.  Correctly

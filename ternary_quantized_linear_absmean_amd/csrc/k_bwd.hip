@@ -1,0 +1,387 @@
+// Backward through the ternary layer (Foundry, docs/quantization.md,
+// "Ternary Training (Backward Pass + Stochastic Flip) / Backward Pass").
+//
+// The forward is y[m, o] = gamma_o * sum_k x[m, k] w[o, k] with w in
+// {-1, 0, +1} held as 2-bit codes, W = [N, K] rows of K/4 bytes.  The input
+// gradient contracts the output gradient with the same codes over the output
+// index:
+//     dX[m, k] = sum_n dY[m, n] * gamma_n * w[n, k]
+// which reads the packed rows transposed (the contraction runs down the
+// columns of W).
+//
+// Matrix-core mapping (gfx950).  The products dY * w are exact in any float
+// format that holds dY exactly, because w is -1, 0 or +1.  An fp32 value
+// splits exactly into three bf16 terms, h = bf16(v), m = bf16(v - h),
+// l = bf16(v - h - m) (each residual is exact in fp32 and has at most 16,
+// then 8 significant bits), so sum_n v_n w_n is three bf16 MFMA contractions
+// into one fp32 accumulator: the products stay exact and only the fp32
+// accumulation rounds, the same arithmetic as an fp32 dot product, at three
+// bf16 matrix-core passes instead of the 8x slower fp32 matrix path.  A bf16
+// dY with one scale per tensor is exact in one term, and the scale is applied
+// to the finished sum; a per-row scale multiplies dY in fp32 first and takes
+// the three-term split.
+//
+// A workgroup (8 waves, 2 x 4) owns a 128-token x 256-column dX tile and
+// walks the contraction in steps of 32 rows of W.  Each step it stages
+//   - the dY tile (128 x 32), split into its bf16 planes once per workgroup,
+//     in 64-byte LDS rows whose 16-byte chunks are XOR-swizzled by row so that
+//     the 16 rows of an MFMA operand read hit disjoint banks;
+//   - the code tile (32 rows x 64 bytes, loaded a byte per lane and row)
+//     transposed to [column byte][row], 40-byte rows, so that one 8-byte read gives a lane the codes of eight
+//     consecutive W rows for four adjacent dX columns (a byte holds four
+//     columns).  Each lane decodes them to four bf16 B operands with byte
+//     permutes; B fragment f covers columns 4j + f (j = lane % 16), so a lane
+//     ends with four adjacent columns of each output row, stored as one
+//     16-byte write.
+// Global loads are raw buffer loads issued two steps ahead into rotating
+// register sets (bytes past a buffer read as zero); the dY columns past N are
+// zeroed on staging.
+
+#include <type_traits>
+
+#include "tq_device.hpp"
+#include "tq_internal.hpp"
+
+namespace tq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
+constexpr int kXcds = 8;
+
+constexpr int kBM = 128;                  // dX rows (tokens) per workgroup
+constexpr int kBK = 256;                  // dX columns per workgroup
+constexpr int kBN = 32;                   // W rows per contraction step
+constexpr int kWM = 2, kWK = 4;           // waves
+constexpr int kNT = kWM * kWK * kWave;    // 512 threads
+constexpr int kArow = kBN * 2;            // bytes of one bf16 plane row
+constexpr int kPlane = kBM * kArow;       // bytes of one bf16 plane
+constexpr int kWrow = 40;                 // bytes of one transposed code row
+constexpr int kWbytes = (kBK / 4) * kWrow;
+
+template <int P>
+constexpr int bwd_stage_bytes() { return P * kPlane + kWbytes; }
+
+// two fp32 -> two bf16 (round to nearest even), and back
+__device__ inline uint32_t pk_bf16(float a, float b) {
+  const f2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ inline float bf_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ inline float bf_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+// x = h + m + l exactly, each as packed bf16 pairs (element 2i in the low half)
+__device__ inline void split3(const float (&x)[8], v4i& h, v4i& m, v4i& l) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float a = x[2 * i], b = x[2 * i + 1];
+    const uint32_t hu = pk_bf16(a, b);
+    const float ra = a - bf_lo(hu), rb = b - bf_hi(hu);
+    const uint32_t mu = pk_bf16(ra, rb);
+    const uint32_t lu = pk_bf16(ra - bf_lo(mu), rb - bf_hi(mu));
+    h[i] = static_cast<int>(hu);
+    m[i] = static_cast<int>(mu);
+    l[i] = static_cast<int>(lu);
+  }
+}
+
+// bf16 bit patterns of the codes 0, 1, 2 (-1, 0, +1): low bytes in LUT_LO
+// bytes 0..2, high bytes in LUT_HI bytes 0..2 (byte-permute indices 4..6)
+constexpr uint32_t kLutLo = 0x00800080u;
+constexpr uint32_t kLutHi = 0x003F00BFu;
+
+// Codes of eight consecutive W rows for one column (u0: rows 0..3, u1: rows
+// 4..7, one byte per row, the column's code at bits 2F..2F+1) as eight bf16.
+template <int F>
+__device__ inline bf16x8 decode_column(uint32_t u0, uint32_t u1) {
+  const uint32_t t0 = (u0 >> (2 * F)) & 0x03030303u;
+  const uint32_t t1 = (u1 >> (2 * F)) & 0x03030303u;
+  const uint32_t s0 = t0 + 0x04040404u, s1 = t1 + 0x04040404u;
+  v4i o;
+  o.x = static_cast<int>(__builtin_amdgcn_perm(kLutHi, kLutLo, __builtin_amdgcn_perm(s0, t0, 0x05010400u)));
+  o.y = static_cast<int>(__builtin_amdgcn_perm(kLutHi, kLutLo, __builtin_amdgcn_perm(s0, t0, 0x07030602u)));
+  o.z = static_cast<int>(__builtin_amdgcn_perm(kLutHi, kLutLo, __builtin_amdgcn_perm(s1, t1, 0x05010400u)));
+  o.w = static_cast<int>(__builtin_amdgcn_perm(kLutHi, kLutLo, __builtin_amdgcn_perm(s1, t1, 0x07030602u)));
+  return __builtin_bit_cast(bf16x8, o);
+}
+
+// DT: 0 = fp32 dY, 1 = bf16 dY.  ROWG: one scale per W row.  ACC: add into dX.
+template <int DT, bool ROWG, bool ACC>
+__global__ __launch_bounds__(kNT, 1) void k_bwd_input(
+    const void* __restrict__ dY, int64_t M, const uint8_t* __restrict__ packed,
+    const float* __restrict__ scale, int64_t N, int64_t K, float* __restrict__ dX) {
+  constexpr int P = (DT == 0 || ROWG) ? 3 : 1;  // bf16 planes
+  constexpr int ES = DT == 0 ? 4 : 2;           // bytes per dY element
+  constexpr int kStage = bwd_stage_bytes<P>();
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int wm = wave / kWK, wk = wave % kWK;
+  const int64_t tiles_m = (M + kBM - 1) / kBM;
+  const int64_t tiles_k = (K + kBK - 1) / kBK;
+  // ids congruent mod 8 run on one XCD: give them the same dY rows
+  const int64_t bid = blockIdx.x;
+  const int64_t local = bid / kXcds;
+  const int64_t tk = local % tiles_k;
+  const int64_t tm = (local / tiles_k) * kXcds + bid % kXcds;
+  if (tm >= tiles_m) return;  // padding ids (whole workgroup)
+  const int64_t m0 = tm * kBM, k0 = tk * kBK;
+  const int64_t rows = M - m0 < kBM ? M - m0 : kBM;
+  const int64_t rowbytes = K / 4;
+
+  const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(dY) + m0 * N * ES), static_cast<short>(0),
+      static_cast<int>(rows * N * ES), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed + k0 / 4), static_cast<short>(0),
+      static_cast<int>(N * rowbytes - k0 / 4), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(scale), static_cast<short>(0), static_cast<int>(ROWG ? N * 4 : 4),
+      kBufFlags);
+
+  // staging roles: every thread one row x 8 columns of dY, and one code byte
+  // (column byte `lane`) of four consecutive W rows (4 * wave ..)
+  const int sr = tid >> 2, sc = tid & 3;
+  const uint32_t yoff = static_cast<uint32_t>((sr * N + 8 * sc) * ES);
+  const int yst = sr * kArow + 16 * (sc ^ ((sr >> 2) & 3));
+  const uint32_t woff = static_cast<uint32_t>(4 * wave * rowbytes + lane);
+  const int wst = P * kPlane + lane * kWrow + 4 * wave;
+
+  // fragment reads
+  const int fr = lane & 15, fg = lane >> 4;
+  int ard[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int r = wm * 64 + 16 * a + fr;
+    ard[a] = r * kArow + 16 * (fg ^ ((r >> 2) & 3));
+  }
+  const int brd = P * kPlane + (wk * 16 + fr) * kWrow + 8 * fg;
+
+  struct Regs {
+    v4i y[ES == 4 ? 2 : 1];
+    v4i gm[ROWG ? 2 : 1];
+    uint32_t w[4];  // one code byte each
+  };
+  auto load_stage = [&](int64_t kt, Regs& r) {
+    const int so = static_cast<int>(kt * kBN * ES);
+    r.y[0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ry, yoff, so, 0));
+    if constexpr (ES == 4)
+      r.y[1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ry, yoff + 16, so, 0));
+    if constexpr (ROWG) {
+      const uint32_t go = static_cast<uint32_t>((kt * kBN + 8 * sc) * 4);
+      r.gm[0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rg, go, 0, 0));
+      r.gm[1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rg, go + 16, 0, 0));
+    }
+    const int sw = static_cast<int>(kt * kBN * rowbytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r.w[i] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(
+          rw, woff + static_cast<uint32_t>(i * rowbytes), sw, 0));
+  };
+  auto store_stage = [&](int buf, int64_t kt, Regs& r) {
+    uint8_t* st = lds + buf * kStage;
+    // the loaded values enter here: without this the compiler combines the
+    // code bytes right after their loads and waits for them a step early
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(r.w[i]));
+    const bool ok = kt * kBN + 8 * sc < N;
+    if constexpr (P == 1) {
+      const v4i z = {0, 0, 0, 0};
+      *reinterpret_cast<v4i*>(st + yst) = ok ? r.y[0] : z;
+    } else {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (ES == 4) {
+          x[e] = __int_as_float(r.y[e / 4][e % 4]);
+        } else {
+          const uint32_t u = static_cast<uint32_t>(r.y[0][e / 2]);
+          x[e] = (e & 1) ? bf_hi(u) : bf_lo(u);
+        }
+        x[e] = ok ? x[e] : 0.f;
+        if constexpr (ROWG) x[e] *= __int_as_float(r.gm[e / 4][e % 4]);
+      }
+      v4i h, m, l;
+      split3(x, h, m, l);
+      *reinterpret_cast<v4i*>(st + yst) = h;
+      *reinterpret_cast<v4i*>(st + kPlane + yst) = m;
+      *reinterpret_cast<v4i*>(st + 2 * kPlane + yst) = l;
+    }
+    *reinterpret_cast<uint32_t*>(st + wst) =
+        r.w[0] | (r.w[1] << 8) | (r.w[2] << 16) | (r.w[3] << 24);
+  };
+
+  f4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int f = 0; f < 4; ++f) acc[a][f] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t nk = (N + kBN - 1) / kBN;
+  // one step: start the loads of step kt+2, contract step kt from LDS,
+  // publish step kt+1.  In the main loop every step loads and stores
+  // unconditionally (a branch around the loads would make the compiler wait
+  // for all loads in flight); loads past the last step read zeros or data
+  // that is never used, and a store of step nk goes to the LDS half that no
+  // later step reads.
+  auto step = [&](int64_t kt, Regs& r_next, Regs& r_far, auto guard) {
+    constexpr bool GUARD = decltype(guard)::value;
+    const int buf = static_cast<int>(kt & 1);
+    if (!GUARD || kt + 2 < nk) load_stage(kt + 2, r_far);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* st = lds + buf * kStage;
+    const uint2 wb = *reinterpret_cast<const uint2*>(st + brd);
+    bf16x8 av[P][4];
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        av[p][a] = *reinterpret_cast<const bf16x8*>(st + p * kPlane + ard[a]);
+    bf16x8 b[4];
+    b[0] = decode_column<0>(wb.x, wb.y);
+    b[1] = decode_column<1>(wb.x, wb.y);
+    b[2] = decode_column<2>(wb.x, wb.y);
+    b[3] = decode_column<3>(wb.x, wb.y);
+#pragma unroll
+    for (int p = 0; p < P; ++p)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int f = 0; f < 4; ++f)
+          acc[a][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[p][a], b[f], acc[a][f], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!GUARD || kt + 1 < nk) store_stage(buf ^ 1, kt + 1, r_next);
+    __syncthreads();
+  };
+  using Free = std::false_type;
+  using Guarded = std::true_type;
+
+  Regs r0, r1, r2;
+  load_stage(0, r0);
+  load_stage(1, r1);
+  store_stage(0, 0, r0);
+  __syncthreads();
+  int64_t kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    step(kt, r1, r2, Free{});
+    step(kt + 1, r2, r0, Free{});
+    step(kt + 2, r0, r1, Free{});
+  }
+  if (kt < nk) step(kt, r1, r2, Guarded{});
+  if (kt + 1 < nk) step(kt + 1, r2, r0, Guarded{});
+
+  // D of the 16x16 MFMA: lane l holds rows 4(l/16)+i of column l%16, and
+  // fragment f is column 4(l%16)+f of the wave's 64
+  const float g0 = ROWG ? 1.f : scale[0];
+  const int64_t col = k0 + wk * 64 + 4 * fr;
+  if (col >= K) return;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = m0 + wm * 64 + 16 * a + 4 * fg + i;
+      if (row >= M) continue;
+      f4 v = {acc[a][0][i], acc[a][1][i], acc[a][2][i], acc[a][3][i]};
+      if (!ROWG) v = v * g0;
+      f4* o = reinterpret_cast<f4*>(dX + row * K + col);
+      if (ACC) v = v + *o;
+      *o = v;
+    }
+  }
+}
+
+// Any shape: one thread per dX element, the contraction in fp32 in row order.
+template <int DT, bool ACC>
+__global__ __launch_bounds__(256) void k_bwd_input_generic(
+    const void* __restrict__ dY, int64_t M, const uint8_t* __restrict__ packed,
+    const float* __restrict__ scale, int per_row, int64_t N, int64_t K, float* __restrict__ dX) {
+  const int64_t total = M * K;
+  const int64_t rowbytes = K / 4;
+  for (int64_t idx = blockIdx.x * int64_t{256} + threadIdx.x; idx < total;
+       idx += int64_t{gridDim.x} * 256) {
+    const int64_t m = idx / K, k = idx % K;
+    float acc = 0.f;
+    for (int64_t n = 0; n < N; ++n) {
+      const uint32_t c = (packed[n * rowbytes + k / 4] >> (2 * (k % 4))) & 3u;
+      if (c != 0u && c != 2u) continue;
+      float v = DT == 0 ? static_cast<const float*>(dY)[m * N + n]
+                        : bf16_to_f32(static_cast<const uint16_t*>(dY)[m * N + n]);
+      if (per_row) v *= scale[n];
+      acc += c == 2u ? v : -v;
+    }
+    if (!per_row) acc *= scale[0];
+    dX[idx] = ACC ? dX[idx] + acc : acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t{256} + threadIdx.x; i < n;
+       i += int64_t{gridDim.x} * 256)
+    p[i] = 0.f;
+}
+
+template <int DT, bool ROWG, bool ACC>
+hipError_t bwd_input_fast(const BwdInputArgs& a, hipStream_t s) {
+  const int64_t tiles_m = (a.M + kBM - 1) / kBM;
+  const int64_t tiles_k = (a.K + kBK - 1) / kBK;
+  const int64_t grid = tiles_k * ((tiles_m + kXcds - 1) / kXcds) * kXcds;
+  hipLaunchKernelGGL((k_bwd_input<DT, ROWG, ACC>), dim3(grid), dim3(kNT), 0, s, a.dY, a.M,
+                     a.packed, a.scale, a.N, a.K, a.dX);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t bwd_input_fast_dt(const BwdInputArgs& a, hipStream_t s) {
+  if (a.per_row) return a.accumulate ? bwd_input_fast<DT, true, true>(a, s)
+                                     : bwd_input_fast<DT, true, false>(a, s);
+  return a.accumulate ? bwd_input_fast<DT, false, true>(a, s)
+                      : bwd_input_fast<DT, false, false>(a, s);
+}
+
+int64_t grid_for(int64_t n) {
+  const int64_t g = (n + 255) / 256;
+  return g < 65536 ? g : 65536;
+}
+
+}  // namespace
+
+bool bwd_input_fast_ok(const BwdInputArgs& a) {
+  const int64_t es = a.bf16 ? 2 : 4;
+  constexpr int64_t kLim = int64_t{1} << 31;
+  return (a.N % 8) == 0 && (reinterpret_cast<uintptr_t>(a.dY) & 15u) == 0u &&
+         (reinterpret_cast<uintptr_t>(a.dX) & 15u) == 0u &&
+         (!a.per_row || (reinterpret_cast<uintptr_t>(a.scale) & 15u) == 0u) &&
+         int64_t{kBM} * a.N * es < kLim && (a.N + 2 * kBN) * (a.K / 4) < kLim &&
+         (a.N + 2 * kBN) * 4 < kLim;
+}
+
+hipError_t launch_backward_input(const BwdInputArgs& a, hipStream_t s) {
+  if (a.M == 0 || a.K == 0) return hipSuccess;
+  if (a.N == 0) {
+    if (a.accumulate) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_zero, dim3(grid_for(a.M * a.K)), dim3(256), 0, s, a.dX,
+                       a.M * a.K);
+    return hipGetLastError();
+  }
+  if (bwd_input_fast_ok(a)) return a.bf16 ? bwd_input_fast_dt<1>(a, s) : bwd_input_fast_dt<0>(a, s);
+#define TQ_BWD_GENERIC(DTV, ACCV)                                                          \
+  hipLaunchKernelGGL((k_bwd_input_generic<DTV, ACCV>), dim3(grid_for(a.M * a.K)), dim3(256), \
+                     0, s, a.dY, a.M, a.packed, a.scale, a.per_row, a.N, a.K, a.dX)
+  if (a.bf16) {
+    if (a.accumulate) TQ_BWD_GENERIC(1, true);
+    else TQ_BWD_GENERIC(1, false);
+  } else {
+    if (a.accumulate) TQ_BWD_GENERIC(0, true);
+    else TQ_BWD_GENERIC(0, false);
+  }
+#undef TQ_BWD_GENERIC
+  return hipGetLastError();
+}
+
+}  // namespace tq

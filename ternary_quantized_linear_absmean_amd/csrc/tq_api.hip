@@ -310,6 +310,34 @@ tq_status tq_ternary_gemm(const int8_t* q, const float* sx, int64_t M, const uin
                                     stream));
 }
 
+tq_status tq_ternary_backward_input(const void* dY, tq_dtype dydt, int64_t M,
+                                    const uint8_t* packed, const float* scale, tq_gran g,
+                                    int64_t N, int64_t K, float* dX, int accumulate,
+                                    hipStream_t stream) {
+  if (M < 0 || N < 0 || K <= 0 || (K % 4) != 0) return TQ_ERR_SHAPE;
+  if (g != TQ_PER_TENSOR && g != TQ_PER_ROW) return TQ_ERR_UNSUPPORTED;
+  if (dydt != TQ_F32 && dydt != TQ_BF16) return TQ_ERR_DTYPE;
+  if (M == 0) return TQ_OK;
+  if (!dX) return TQ_ERR_NULL;
+  if (!aligned(dX, 4)) return TQ_ERR_ALIGN;
+  if (N > 0) {
+    if (!dY || !packed || !scale) return TQ_ERR_NULL;
+    if (!aligned(dY, dydt == TQ_BF16 ? 2 : 4) || !aligned(scale, 4)) return TQ_ERR_ALIGN;
+  }
+  tq::BwdInputArgs a;
+  a.dY = dY;
+  a.bf16 = dydt == TQ_BF16 ? 1 : 0;
+  a.packed = packed;
+  a.scale = scale;
+  a.per_row = g == TQ_PER_ROW ? 1 : 0;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.dX = dX;
+  a.accumulate = accumulate ? 1 : 0;
+  return hip_status(tq::launch_backward_input(a, stream));
+}
+
 const char* tq_status_str(tq_status s) {
   switch (s) {
     case TQ_OK: return "ok";

@@ -70,4 +70,18 @@ hipError_t launch_quant_gemv(const void* X, int bf16, const ActParams& p, int8_t
                              float* sx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
 
+// ---- backward through the packed weights (k_bwd.hip)
+struct BwdInputArgs {
+  const void* dY;  // [M, N] fp32 or bf16
+  int bf16;
+  const uint8_t* packed;
+  const float* scale;
+  int per_row;
+  int64_t M, N, K;
+  float* dX;       // [M, K]
+  int accumulate;
+};
+bool bwd_input_fast_ok(const BwdInputArgs& a);
+hipError_t launch_backward_input(const BwdInputArgs& a, hipStream_t s);
+
 }  // namespace tq

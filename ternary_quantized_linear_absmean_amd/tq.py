@@ -33,7 +33,8 @@ MODES = {"ternary": 0, "binary": 1}
 EXPORTED = ["tq_packed_bytes", "tq_pack_workspace_bytes", "tq_pack_ternary",
             "tq_quant_act_int8", "tq_fwht512", "tq_ternary_gemv", "tq_ternary_gemm",
             "tq_quant_ternary_gemv", "tq_packed1_bytes", "tq_pack_binary1",
-            "tq_binary1_gemv", "tq_swiglu_gemv", "tq_ffn_swiglu_decode", "tq_status_str",
+            "tq_binary1_gemv", "tq_swiglu_gemv", "tq_ffn_swiglu_decode",
+            "tq_ternary_backward_input", "tq_status_str",
             "tq_last_hip_error", "tq_version"]
 
 _vp = ctypes.c_void_p
@@ -76,6 +77,9 @@ _lib.tq_pack_binary1.argtypes = [_vp, _i64, _i64, _int, _vp, _vp, _vp, ctypes.c_
 _lib.tq_pack_binary1.restype = _int
 _lib.tq_binary1_gemv.argtypes = [_vp, _vp, _i64, _vp, _vp, _int, _i64, _i64, _vp, _int, _vp]
 _lib.tq_binary1_gemv.restype = _int
+_lib.tq_ternary_backward_input.argtypes = [_vp, _int, _i64, _vp, _vp, _int, _i64, _i64, _vp,
+                                           _int, _vp]
+_lib.tq_ternary_backward_input.restype = _int
 _lib.tq_status_str.argtypes = [_int]
 _lib.tq_status_str.restype = ctypes.c_char_p
 _lib.tq_last_hip_error.argtypes = []
@@ -362,6 +366,31 @@ def tq_ffn_swiglu_decode(X: torch.Tensor, gate, up, down, d_model: int, d_ffn: i
         _ptr(b["q_x"]), _ptr(b["sx_x"]), _ptr(b["H"]), _ptr(b["q_h"]), _ptr(b["sx_h"]),
         _ptr(Y), DTYPES[out_dtype], _stream(stream)), "tq_ffn_swiglu_decode")
     return Y, b
+
+
+def tq_ternary_backward_input(dY: torch.Tensor, packed, scale, K: int,
+                              granularity: str = "tensor", dX: torch.Tensor | None = None,
+                              accumulate: bool = False, stream=None) -> torch.Tensor:
+    """dX [M, K] fp32 = (dY [M, N] * gamma) contracted with the packed codes
+    over N; with accumulate the result is added to the given dX."""
+    for t, name in ((dY, "dY"), (packed, "packed"), (scale, "scale")):
+        _dev(t, name)
+    if dY.dtype not in _ACT_DT or dY.dim() != 2:
+        raise ValueError("dY must be a 2-D float32 or bfloat16 tensor")
+    M, N = dY.shape
+    if dX is None:
+        if accumulate:
+            raise ValueError("accumulate needs dX")
+        dX = torch.empty((M, K), dtype=torch.float32, device=dY.device)
+    _dev(dX, "dX")
+    if dX.dtype != torch.float32 or tuple(dX.shape) != (M, K):
+        raise ValueError("dX must be float32 [M, K]")
+    _check(_lib.tq_ternary_backward_input(dY.data_ptr(), _ACT_DT[dY.dtype], M,
+                                          packed.data_ptr(), scale.data_ptr(),
+                                          GRANULARITY[granularity], N, K, dX.data_ptr(),
+                                          1 if accumulate else 0, _stream(stream)),
+           "tq_ternary_backward_input")
+    return dX
 
 
 def raw_library() -> ctypes.CDLL:

@@ -116,6 +116,26 @@ def test_binary1_validation():
     assert tqmod.tq_packed1_bytes(9) == 2
 
 
+def test_backward_input_validation():
+    P = 0x10000
+    f = lib.tq_ternary_backward_input
+    # (dY, dydt, M, packed, scale, g, N, K, dX, accumulate, stream)
+    assert f(P, 0, 4, P, P, 0, 8, 6, P, 0, None) == SHAPE          # K % 4
+    assert f(P, 0, 4, P, P, 0, 8, 0, P, 0, None) == SHAPE          # K <= 0
+    assert f(P, 0, -1, P, P, 0, 8, 64, P, 0, None) == SHAPE
+    assert f(P, 0, 4, P, P, 0, -8, 64, P, 0, None) == SHAPE
+    assert f(P, 2, 4, P, P, 0, 8, 64, P, 0, None) == DTYPE         # int32 dY
+    assert f(P, 0, 4, P, P, 7, 8, 64, P, 0, None) == UNSUP
+    assert f(P, 0, 4, P, P, 0, 8, 64, None, 0, None) == NULL
+    assert f(None, 0, 4, P, P, 0, 8, 64, P, 0, None) == NULL
+    assert f(P, 0, 4, None, P, 1, 8, 64, P, 0, None) == NULL
+    assert f(P, 0, 4, P, None, 1, 8, 64, P, 0, None) == NULL
+    assert f(P + 2, 0, 4, P, P, 0, 8, 64, P, 0, None) == ALIGN     # fp32 dY
+    assert f(P, 0, 4, P, P, 0, 8, 64, P + 2, 0, None) == ALIGN     # dX
+    assert f(P, 0, 4, P, P + 1, 0, 8, 64, P, 0, None) == ALIGN     # scale
+    assert f(None, 0, 0, None, None, 0, 8, 64, None, 0, None) == OK  # M == 0
+
+
 def test_swiglu_validation():
     P = 0x10000
     f = lib.tq_swiglu_gemv

@@ -810,3 +810,125 @@ def test_ffn_swiglu_decode_workload(b):
     np.testing.assert_array_equal(host(H2), H)
     Y2, _, _ = tq.tq_quant_ternary_gemv(H2, dev(down[0]), dev(down[1]), d_model, d_ffn, "row")
     np.testing.assert_array_equal(host(Y2), host(Y))
+
+
+# ------------------------------------------------------------ backward input
+
+def _bwd_ref_and_bound(dY, packed, scale, K, rows=None):
+    """Oracle dX and the fp32 dot-product bound gamma_{N+2} * sum_n |terms|
+    (the products are exact; N accumulations, the dY * gamma rounding and the
+    final scale multiply each round once in fp32)."""
+    dY = np.asarray(dY, np.float64)
+    if rows is not None:
+        dY = dY[rows]
+    ref = oracle.backward_input(dY, packed, scale, K)
+    w = np.abs(oracle.unpack_codes(packed, K).astype(np.float64))
+    g = np.abs(np.asarray(scale, np.float64))
+    S = (np.abs(dY) * (g if g.size > 1 else g[0])) @ w
+    u = 2.0 ** -24
+    n = dY.shape[1] + 2
+    return ref, S * (n * u / (1 - n * u))
+
+
+def _assert_bwd_close(dx, ref, bound, what=""):
+    err = np.abs(np.asarray(dx, np.float64) - ref)
+    bad = err > bound + 1e-37
+    rel = np.max(err / np.maximum(bound, 1e-300)) if err.size else 0.0
+    say(f"{what} max err / bound {rel:.3g}")
+    assert not bad.any(), f"{bad.sum()} of {err.size} dX values beyond the fp32 bound"
+
+
+def _bwd_inputs(M, N, K, dtype, gran, seed):
+    W = ti.normal_weights(seed, N, K)
+    packed, scale = oracle.pack_ternary(W, gran)
+    dY = ti.output_grads(seed + 1, M, N, dtype)
+    return packed, scale, dY
+
+
+BWD_CASES = [
+    (1, 8, 4, "f32", "tensor", False), (5, 40, 260, "f32", "row", False),
+    (130, 72, 516, "f32", "tensor", True), (257, 104, 1028, "bf16", "tensor", False),
+    (129, 264, 772, "bf16", "row", True), (300, 520, 1536, "f32", "row", False),
+    (64, 37, 64, "f32", "tensor", False), (33, 45, 132, "bf16", "row", True),
+]
+
+
+@pytest.mark.parametrize("M,N,K,dtype,gran,acc", BWD_CASES)
+def test_backward_input(M, N, K, dtype, gran, acc):
+    say(f"backward_input M={M} N={N} K={K} {dtype} {gran} acc={acc}")
+    packed, scale, dY = _bwd_inputs(M, N, K, dtype, gran, 7000 + M + N + K)
+    ref, bound = _bwd_ref_and_bound(dY, packed, scale, K)
+    base = ti.output_grads(7, M, K) if acc else None
+    dXd = dev(base) if acc else None
+    out = tq.tq_ternary_backward_input(x_to_device(dY, dtype), dev(packed), dev(scale), K,
+                                       gran, dX=dXd, accumulate=acc)
+    dx = host(out).astype(np.float64)
+    if acc:
+        # the kernel adds its fp32 result to dX: one more rounding
+        dx = dx - base.astype(np.float64)
+        bound = bound + np.abs(ref + base) * 2.0 ** -24
+    _assert_bwd_close(dx, ref, bound, "backward_input")
+
+
+def test_backward_input_single_term_columns_exact():
+    # one nonzero weight per column: dX = gamma * (+-dY) with no accumulation,
+    # so the three-way bf16 split must give back every fp32 bit of dY
+    M, N, K = 200, 64, 512
+    rng = np.random.default_rng(71)
+    w = np.zeros((N, K), np.int8)
+    w[rng.integers(0, N, K), np.arange(K)] = rng.choice(np.array([-1, 1], np.int8), K)
+    packed = oracle.pack_codes(w)
+    dY = (rng.standard_normal((M, N)) * np.exp2(rng.integers(-40, 40, (M, N)))).astype(np.float32)
+    for gam in (np.array([1.0], np.float32), np.array([0.37], np.float32)):
+        dx = host(tq.tq_ternary_backward_input(dev(dY), dev(packed), dev(gam), K, "tensor"))
+        n_of_k = np.argmax(w != 0, axis=0)
+        expect = (dY[:, n_of_k] * w[n_of_k, np.arange(K)].astype(np.float32)) * gam[0]
+        assert np.array_equal(f32_bits(dx), f32_bits(expect.astype(np.float32)))
+    # per-row scales: dX = fl(dY * gamma_n) * w
+    gam = (rng.random(N) + 0.5).astype(np.float32)
+    dx = host(tq.tq_ternary_backward_input(dev(dY), dev(packed), dev(gam), K, "row"))
+    n_of_k = np.argmax(w != 0, axis=0)
+    expect = (dY[:, n_of_k] * gam[n_of_k]) * w[n_of_k, np.arange(K)].astype(np.float32)
+    assert np.array_equal(f32_bits(dx), f32_bits(expect.astype(np.float32)))
+
+
+def test_backward_input_wide_range_and_unaligned():
+    M, N, K = 96, 128, 768
+    rng = np.random.default_rng(72)
+    packed, scale, _ = _bwd_inputs(M, N, K, "f32", "row", 7100)
+    dY = (rng.standard_normal((M, N)) * np.exp2(rng.integers(-60, 60, (M, N)))).astype(np.float32)
+    ref, bound = _bwd_ref_and_bound(dY, packed, scale, K)
+    dx = host(tq.tq_ternary_backward_input(dev(dY), dev(packed), dev(scale), K, "row"))
+    _assert_bwd_close(dx, ref, bound, "wide range")
+    # dY one element off 16-byte alignment: the simple kernel
+    big = torch.zeros(M * N + 1, dtype=torch.float32, device=DEV)
+    big[1:] = dev(dY.reshape(-1))
+    dYu = big[1:].view(M, N)
+    dx = host(tq.tq_ternary_backward_input(dYu, dev(packed), dev(scale), K, "row"))
+    _assert_bwd_close(dx, ref, bound, "unaligned dY")
+
+
+def test_backward_input_empty_contraction():
+    M, K = 3, 8
+    dY = torch.zeros((M, 0), dtype=torch.float32, device=DEV)
+    packed = torch.zeros((0, K // 4), dtype=torch.uint8, device=DEV)
+    scale = torch.ones(1, dtype=torch.float32, device=DEV)
+    dX = torch.full((M, K), 5.0, dtype=torch.float32, device=DEV)
+    tq.tq_ternary_backward_input(dY, packed, scale, K, dX=dX, accumulate=True)
+    assert np.all(host(dX) == 5.0)
+    tq.tq_ternary_backward_input(dY, packed, scale, K, dX=dX)
+    assert np.all(host(dX) == 0.0)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_input_prefill_workload_sampled(dtype):
+    # the prefill matrix (11008 x 4096, per-tensor scale), 2048 tokens of
+    # output gradient; the oracle checks 48 sampled token rows in full
+    say(f"backward_input prefill workload {dtype}")
+    _, packed, scale = ref_pack("prefill")
+    dY = ti.workload_output_grads("prefill", dtype=dtype)
+    M, K = dY.shape[0], 4096
+    dx = host(tq.tq_ternary_backward_input(x_to_device(dY, dtype), dev(packed), dev(scale), K))
+    rows = np.sort(np.random.default_rng(73).choice(M, 48, replace=False))
+    ref, bound = _bwd_ref_and_bound(dY, packed, scale, K, rows)
+    _assert_bwd_close(dx[rows], ref, bound, f"prefill {dtype}")

@@ -15,9 +15,13 @@ Workloads (weights are [N_out, K_in] row-major, activations are [M, K]):
 * ``bitlinear`` X 512x4096 Student-t(3) bf16, RMSNorm + FWHT-512 prologue;
                 W 4096x4096 ~N(0, 0.02) per-row, ternary and binary (sign).
 
-Seeds: weights use ``1000*cfg + j`` and activations ``1000*cfg + 100 + j + b``
-where ``cfg`` is the workload number (1..5 in the order above), ``j`` the
-matrix index (up=0, down=1) and ``b`` the batch size.
+Output gradients for the backward through a workload's matrix are dY [b, N_out]
+~N(0, 1) fp32 (bf16-rounded when asked for).
+
+Seeds: weights use ``1000*cfg + j``, activations ``1000*cfg + 100 + j + b`` and
+output gradients ``1000*cfg + 500 + j + b``, where ``cfg`` is the workload
+number (1..5 in the order above), ``j`` the matrix index (up=0, down=1) and
+``b`` the batch size.
 """
 from __future__ import annotations
 
@@ -66,6 +70,10 @@ def act_seed(cfg: int, j: int, b: int) -> int:
     return 1000 * cfg + 100 + j + b
 
 
+def grad_seed(cfg: int, j: int, b: int) -> int:
+    return 1000 * cfg + 500 + j + b
+
+
 def normal_weights(seed: int, n: int, k: int, sigma=WEIGHT_SIGMA) -> np.ndarray:
     rng = np.random.default_rng(seed)
     return rng.standard_normal((n, k), dtype=np.float32) * np.float32(sigma)
@@ -97,6 +105,21 @@ def workload_activations(name: str, j: int = 0, b: int | None = None) -> np.ndar
     if b is None:
         b = w["batches"][0]
     return activations(act_seed(w["cfg"], j, b), b, k, w["x_dist"], w["x_dtype"])
+
+
+def output_grads(seed: int, m: int, n: int, dtype: str = "f32") -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((m, n), dtype=np.float32)
+    return to_bf16_values(g) if dtype == "bf16" else g
+
+
+def workload_output_grads(name: str, j: int = 0, b: int | None = None,
+                          dtype: str = "f32") -> np.ndarray:
+    w = WORKLOADS[name]
+    n, k = w["mats"][j]
+    if b is None:
+        b = w["batches"][0]
+    return output_grads(grad_seed(w["cfg"], j, b), b, n, dtype)
 
 
 def random_ternary(seed: int, n: int, k: int) -> np.ndarray:
