@@ -288,8 +288,9 @@ tq_status tq_binary1_gemv(const int8_t* q, const float* sx, int64_t M,
  *            accumulate != 0 adds the result to it (the page's += form).
  * Arithmetic: each product dY * gamma_n * w is formed exactly (w is -1, 0 or
  * +1; with a per-row scale, dY * gamma_n is first rounded to fp32) and the
- * sum over n is accumulated in fp32, so the error is that of an fp32 dot
- * product of length N; a per-tensor gamma multiplies the fp32 sum.  Inputs
+ * sum over n is accumulated in fp32 (on the matrix cores each step of 32
+ * rows rounds within one ulp), so the error is that of an fp32 dot product
+ * of length N; a per-tensor gamma multiplies the fp32 sum.  Inputs
  * need |dY * gamma| < 3.3e38 (the bf16 range).  N % 8 == 0 with 16-byte
  * aligned dY, dX (and scale, per row) runs on the matrix cores; other shapes
  * on a simple kernel.  N == 0 writes zeros (or leaves dX, with accumulate).
@@ -300,6 +301,26 @@ tq_status tq_ternary_backward_input(const void* dY, tq_dtype dydt, int64_t M,
                                     const uint8_t* packed, const float* scale, tq_gran g,
                                     int64_t N, int64_t K, float* dX, int accumulate,
                                     hipStream_t stream);
+
+/* The weight gradient of the same page: the float product
+ *     dW[n, k] = sum_m dY[m, n] * X[m, k]        (X^T dY, laid out [N, K])
+ * with no codes and no scale.
+ *   X   [M, K] fp32 or bf16 (xdt), dY [M, N] fp32 or bf16 (dydt),
+ *       element-aligned.
+ *   dW  [N, K] fp32, 4-byte aligned; accumulate != 0 adds to it.
+ * Arithmetic: products of a bf16 operand with anything are formed exactly;
+ * with both operands fp32 each product carries an error of at most about
+ * 2^-23 |dY X| (three-term bf16 splits, the smallest cross terms dropped).
+ * Sums are accumulated in fp32 over M (on the matrix cores each accumulation
+ * step rounds within one ulp).  N % 8 == 0, K % 8 == 0 and 16-byte
+ * aligned X, dY run on the matrix cores; other shapes on a simple kernel.
+ * M == 0 writes zeros (or leaves dW, with accumulate).
+ * Errors: M, N, K < 0 is TQ_ERR_SHAPE; xdt or dydt other than F32/BF16 is
+ * TQ_ERR_DTYPE; NULL dW with N, K > 0, or NULL X, dY with M, N, K > 0, is
+ * TQ_ERR_NULL. */
+tq_status tq_ternary_backward_weight(const void* X, tq_dtype xdt, const void* dY, tq_dtype dydt,
+                                     int64_t M, int64_t N, int64_t K, float* dW, int accumulate,
+                                     hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* tq_status_str(tq_status s);

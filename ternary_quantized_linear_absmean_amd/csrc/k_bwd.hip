@@ -89,6 +89,15 @@ __device__ inline void split3(const float (&x)[8], v4i& h, v4i& m, v4i& l) {
   }
 }
 
+// Offset of 16-byte chunk `chunk` of row `row` in a tile of 64-byte rows.
+// The XOR swizzle keeps both the 16x16x32 operand reads (16 consecutive rows
+// at one chunk per lane group) and the staging writes (whole rows) free of
+// LDS bank conflicts (measured with the LDS bank-conflict counter and by
+// timing; the plain (row >> 2) swizzle costs the reads 40%).
+__device__ inline int swz64(int row, int chunk) {
+  return row * 64 + 16 * (chunk ^ (((row >> 1) ^ (row >> 4)) & 3));
+}
+
 // bf16 bit patterns of the codes 0, 1, 2 (-1, 0, +1): low bytes in LUT_LO
 // bytes 0..2, high bytes in LUT_HI bytes 0..2 (byte-permute indices 4..6)
 constexpr uint32_t kLutLo = 0x00800080u;
@@ -121,7 +130,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform in the wave
   const int wm = wave / kWK, wk = wave % kWK;
   const int64_t tiles_m = (M + kBM - 1) / kBM;
   const int64_t tiles_k = (K + kBK - 1) / kBK;
@@ -149,7 +158,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
   // (column byte `lane`) of four consecutive W rows (4 * wave ..)
   const int sr = tid >> 2, sc = tid & 3;
   const uint32_t yoff = static_cast<uint32_t>((sr * N + 8 * sc) * ES);
-  const int yst = sr * kArow + 16 * (sc ^ ((sr >> 2) & 3));
+  const int yst = swz64(sr, sc);
   const uint32_t woff = static_cast<uint32_t>(4 * wave * rowbytes + lane);
   const int wst = P * kPlane + lane * kWrow + 4 * wave;
 
@@ -159,7 +168,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
     const int r = wm * 64 + 16 * a + fr;
-    ard[a] = r * kArow + 16 * (fg ^ ((r >> 2) & 3));
+    ard[a] = swz64(r, fg);
   }
   const int brd = P * kPlane + (wk * 16 + fr) * kWrow + 8 * fg;
 
@@ -249,7 +258,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
     b[2] = decode_column<2>(wb.x, wb.y);
     b[3] = decode_column<3>(wb.x, wb.y);
 #pragma unroll
-    for (int p = 0; p < P; ++p)
+    for (int p = P - 1; p >= 0; --p)  // smallest terms first
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -349,7 +358,324 @@ int64_t grid_for(int64_t n) {
   return g < 65536 ? g : 65536;
 }
 
+// ------------------------------------------------------------ weight gradient
+//
+// dW[n, k] = sum_m dY[m, n] * X[m, k]: the float product X^T dY of the page,
+// with no codes and no scale.  Both operands run down their rows (the
+// contraction is over tokens), so each workgroup transposes its tiles while
+// staging them: a thread loads 8 consecutive token rows of two adjacent
+// columns (one 8- or 4-byte load per row; 64 lanes read 512 or 256
+// contiguous bytes of a row) and writes, per column, the 8 values as one
+// 16-byte chunk of that column's LDS row.  fp32 operands are split into
+// three bf16 terms (a = a1 + a2 + a3 exactly); with both operands fp32 the
+// products a_p * b_q with p + q <= 2 (six MFMA passes) are kept, the dropped
+// terms adding at most about 2^-23 |a b| per product; with a bf16 operand
+// the kept terms give every product exactly.  The terms are accumulated
+// smallest first: with a bf16 operand the partial sums of one product's terms
+// are then exact (a2 + a3 = a - a1 has at most 16 significant bits), so a
+// single token's contribution is its product with a single rounding (the
+// matrix cores' accumulation rounds faithfully, not always to nearest).
+//
+// A workgroup (8 waves, 4 x 2, 32 x 64 each) owns a 128 x 128 dW tile.  A
+// stage holds KS = 2 MFMA steps (64 tokens) when LDS allows, one (32 tokens)
+// with both operands fp32; with two steps every thread stages one unit
+// (8 rows x 2 columns) of each operand, with one step threads 0..255 stage
+// dY and 256..511 stage X.  Either way all threads issue the same loads.
+
+constexpr int kGN = 128, kGK = 128;  // dW tile
+constexpr int kGPlane = 128 * 64;    // one plane: 128 rows of 32 bf16
+constexpr int kPN = 4, kPK = 8;      // tiles of a patch (one per CU of an XCD)
+
+__host__ __device__ constexpr int planes_of(int dt) { return dt == 0 ? 3 : 1; }
+__host__ __device__ constexpr int wgt_ks(int da, int db) { return (da == 0 && db == 0) ? 1 : 2; }
+template <int DA, int DB>
+constexpr int wgt_lds_bytes() {
+  return 2 * wgt_ks(DA, DB) * (planes_of(DA) + planes_of(DB)) * kGPlane;
+}
+
+// DA: dtype of dY, DB: dtype of X (0 = fp32, 1 = bf16).  ACC: add into dW.
+template <int DA, int DB, bool ACC>
+__global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
+    const void* __restrict__ dY, const void* __restrict__ X, int64_t M, int64_t N, int64_t K,
+    float* __restrict__ dW) {
+  constexpr int PA = planes_of(DA), PB = planes_of(DB);
+  constexpr int KS = wgt_ks(DA, DB);
+  constexpr int kGM = 32 * KS;                 // tokens per stage
+  constexpr int kStep = (PA + PB) * kGPlane;   // LDS bytes of one MFMA step
+  constexpr int kStage = KS * kStep;
+  constexpr bool kRoles = KS == 1;             // half the threads per operand
+  constexpr int ESA = DA == 0 ? 4 : 2, ESB = DB == 0 ? 4 : 2;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform in the wave
+  const int wn = wave / 2, wk = wave % 2;
+  const int64_t tiles_n = (N + kGN - 1) / kGN;
+  const int64_t tiles_k = (K + kGK - 1) / kGK;
+  // ids congruent mod 8 run on one XCD: its 32 workgroups in flight take a
+  // 4 x 8 patch of tiles, which share 4 dY and 8 X column blocks in its L2
+  const int64_t pcols = (tiles_n + kPN - 1) / kPN;
+  const int64_t bid = blockIdx.x;
+  const int64_t local = bid / kXcds;
+  const int64_t patch = (local / (kPN * kPK)) * kXcds + bid % kXcds;
+  const int64_t q = local % (kPN * kPK);
+  const int64_t tn = (patch % pcols) * kPN + q % kPN;
+  const int64_t tk = (patch / pcols) * kPK + q / kPN;
+  if (tn >= tiles_n || tk >= tiles_k) return;  // padding ids (whole workgroup)
+  const int64_t n0 = tn * kGN, k0 = tk * kGK;
+
+  // staging unit of this thread: columns 2cp, 2cp+1, token rows 8o..8o+7 of
+  // the stage (o < 4 KS); with roles, waves 0..3 stage dY and 4..7 stage X
+  const bool role_a = !kRoles || wave < 4;
+  const int ut = kRoles ? (tid & 255) : tid;
+  const int cp = ut & 63, uo = ut >> 6;
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(dY) + n0 * ESA), static_cast<short>(0),
+      static_cast<int>(M * N * ESA - n0 * ESA), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(X) + k0 * ESB), static_cast<short>(0),
+      static_cast<int>(M * K * ESB - k0 * ESB), kBufFlags);
+  const uint32_t aoff = static_cast<uint32_t>((8 * uo * N + 2 * cp) * ESA);
+  const uint32_t boff = static_cast<uint32_t>((8 * uo * K + 2 * cp) * ESB);
+  // LDS offsets of the unit's two column rows within its operand's plane 0
+  const int ubase = (uo >> 2) * kStep;
+  const int wo0 = ubase + swz64(2 * cp, uo & 3), wo1 = ubase + swz64(2 * cp + 1, uo & 3);
+
+  struct Regs { uint2 a[8]; uint2 b[kRoles ? 1 : 8]; };
+  // 8 rows of one unit: fp32 pairs (8 bytes) or bf16 pairs (4 bytes, in .x)
+  auto load_unit = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t str, int so, int es,
+                       uint2 (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (es == 4) {
+        v[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off + i * str, so, 0));
+      } else {
+        v[i].x = __builtin_amdgcn_raw_buffer_load_b32(r, off + i * str, so, 0);
+        v[i].y = 0u;
+      }
+    }
+  };
+  auto load_stage = [&](int64_t st, Regs& r) {
+    if constexpr (kRoles) {
+      // both operands fp32: the same loads, buffer and offsets by role
+      const int64_t rl = role_a ? N : K;
+      load_unit(role_a ? ra : rb, role_a ? aoff : boff, static_cast<uint32_t>(rl * 4),
+                static_cast<int>(st * kGM * rl * 4), 4, r.a);
+    } else {
+      load_unit(ra, aoff, static_cast<uint32_t>(N * ESA), static_cast<int>(st * kGM * N * ESA),
+                ESA, r.a);
+      load_unit(rb, boff, static_cast<uint32_t>(K * ESB), static_cast<int>(st * kGM * K * ESB),
+                ESB, r.b);
+    }
+  };
+  // one unit -> its operand's planes (plane 0 at `base`)
+  auto put_unit = [&](uint8_t* base, int es, uint2 (&v)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y));
+    if (es == 4) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(c ? v[i].y : v[i].x);
+        v4i h, m, l;
+        split3(x, h, m, l);
+        const int o = c ? wo1 : wo0;
+        *reinterpret_cast<v4i*>(base + o) = h;
+        *reinterpret_cast<v4i*>(base + kGPlane + o) = m;
+        *reinterpret_cast<v4i*>(base + 2 * kGPlane + o) = l;
+      }
+    } else {
+      // bf16 pairs (column 2cp in the low half): each column's 8 halves
+      v4i c0, c1;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        c0[t] = static_cast<int>(__builtin_amdgcn_perm(v[2 * t + 1].x, v[2 * t].x, 0x05040100u));
+        c1[t] = static_cast<int>(__builtin_amdgcn_perm(v[2 * t + 1].x, v[2 * t].x, 0x07060302u));
+      }
+      *reinterpret_cast<v4i*>(base + wo0) = c0;
+      *reinterpret_cast<v4i*>(base + wo1) = c1;
+    }
+  };
+  auto store_stage = [&](int buf, Regs& r) {
+    uint8_t* st = lds + buf * kStage;
+    if constexpr (kRoles) {
+      put_unit(st + (role_a ? 0 : PA * kGPlane), 4, r.a);
+    } else {
+      put_unit(st, ESA, r.a);
+      put_unit(st + PA * kGPlane, ESB, r.b);
+    }
+  };
+
+  const int fr = lane & 15, fg = lane >> 4;
+  int ard[2], brd[4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) ard[a] = swz64(wn * 32 + 16 * a + fr, fg);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) brd[b] = PA * kGPlane + swz64(wk * 64 + 16 * b + fr, fg);
+
+  f4 acc[2][4];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t ns = (M + kGM - 1) / kGM;
+  auto step = [&](int64_t s, Regs& r_next, Regs& r_far, auto guard) {
+    constexpr bool GUARD = decltype(guard)::value;
+    const int buf = static_cast<int>(s & 1);
+    if (!GUARD || s + 2 < ns) load_stage(s + 2, r_far);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint8_t* st = lds + buf * kStage + ks * kStep;
+      bf16x8 av[PA][2], bv[PB][4];
+#pragma unroll
+      for (int p = 0; p < PA; ++p)
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          av[p][a] = *reinterpret_cast<const bf16x8*>(st + p * kGPlane + ard[a]);
+#pragma unroll
+      for (int p = 0; p < PB; ++p)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          bv[p][b] = *reinterpret_cast<const bf16x8*>(st + p * kGPlane + brd[b]);
+      // smallest terms first (see above)
+#pragma unroll
+      for (int lvl = 2; lvl >= 0; --lvl)
+#pragma unroll
+        for (int pa = PA - 1; pa >= 0; --pa) {
+          const int pb = lvl - pa;
+          if (pb < 0 || pb >= PB) continue;
+#pragma unroll
+          for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+              acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[pa][a], bv[pb][b],
+                                                                  acc[a][b], 0, 0, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (!GUARD || s + 1 < ns) store_stage(buf ^ 1, r_next);
+    __syncthreads();
+  };
+  using Free = std::false_type;
+  using Guarded = std::true_type;
+
+  Regs r0, r1, r2;
+  load_stage(0, r0);
+  load_stage(1, r1);
+  store_stage(0, r0);
+  __syncthreads();
+  int64_t s = 0;
+  for (; s + 3 <= ns; s += 3) {
+    step(s, r1, r2, Free{});
+    step(s + 1, r2, r0, Free{});
+    step(s + 2, r0, r1, Free{});
+  }
+  if (s < ns) step(s, r1, r2, Guarded{});
+  if (s + 1 < ns) step(s + 1, r2, r0, Guarded{});
+
+  // D of the 16x16 MFMA: lane l holds rows 4(l/16)+i of column l%16
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int64_t k = k0 + wk * 64 + 16 * b + fr;
+    if (k >= K) continue;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t n = n0 + wn * 32 + 16 * a + 4 * fg + i;
+        if (n >= N) continue;
+        float* o = dW + n * K + k;
+        *o = ACC ? *o + acc[a][b][i] : acc[a][b][i];
+      }
+    }
+  }
+}
+
+// Any shape: one thread per dW element, products and sum in fp32, token order.
+template <int DA, int DB, bool ACC>
+__global__ __launch_bounds__(256) void k_bwd_weight_generic(
+    const void* __restrict__ dY, const void* __restrict__ X, int64_t M, int64_t N, int64_t K,
+    float* __restrict__ dW) {
+  const int64_t total = N * K;
+  for (int64_t idx = blockIdx.x * int64_t{256} + threadIdx.x; idx < total;
+       idx += int64_t{gridDim.x} * 256) {
+    const int64_t n = idx / K, k = idx % K;
+    float acc = 0.f;
+    for (int64_t m = 0; m < M; ++m) {
+      const float a = DA == 0 ? static_cast<const float*>(dY)[m * N + n]
+                              : bf16_to_f32(static_cast<const uint16_t*>(dY)[m * N + n]);
+      const float b = DB == 0 ? static_cast<const float*>(X)[m * K + k]
+                              : bf16_to_f32(static_cast<const uint16_t*>(X)[m * K + k]);
+      acc += a * b;
+    }
+    dW[idx] = ACC ? dW[idx] + acc : acc;
+  }
+}
+
+template <int DA, int DB, bool ACC>
+hipError_t bwd_weight_fast(const BwdWeightArgs& a, hipStream_t s) {
+  constexpr int lds_bytes = wgt_lds_bytes<DA, DB>();
+  static bool attr_set[64] = {false};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64 || !attr_set[dev]) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_weight<DA, DB, ACC>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) attr_set[dev] = true;
+  }
+  const int64_t tiles_n = (a.N + kGN - 1) / kGN;
+  const int64_t tiles_k = (a.K + kGK - 1) / kGK;
+  const int64_t patches = ((tiles_n + kPN - 1) / kPN) * ((tiles_k + kPK - 1) / kPK);
+  const int64_t grid = ((patches + kXcds - 1) / kXcds) * kXcds * kPN * kPK;
+  hipLaunchKernelGGL((k_bwd_weight<DA, DB, ACC>), dim3(grid), dim3(kNT), lds_bytes, s, a.dY,
+                     a.X, a.M, a.N, a.K, a.dW);
+  return hipGetLastError();
+}
+
+template <int DA, int DB>
+hipError_t bwd_weight_dispatch(const BwdWeightArgs& a, bool fast, hipStream_t s) {
+  if (fast) return a.accumulate ? bwd_weight_fast<DA, DB, true>(a, s)
+                                : bwd_weight_fast<DA, DB, false>(a, s);
+  const int64_t g = grid_for(a.N * a.K);
+  if (a.accumulate)
+    hipLaunchKernelGGL((k_bwd_weight_generic<DA, DB, true>), dim3(g), dim3(256), 0, s, a.dY, a.X,
+                       a.M, a.N, a.K, a.dW);
+  else
+    hipLaunchKernelGGL((k_bwd_weight_generic<DA, DB, false>), dim3(g), dim3(256), 0, s, a.dY,
+                       a.X, a.M, a.N, a.K, a.dW);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool bwd_weight_fast_ok(const BwdWeightArgs& a) {
+  const int64_t ea = a.dy_bf16 ? 2 : 4, eb = a.x_bf16 ? 2 : 4;
+  constexpr int64_t kLim = int64_t{1} << 31;
+  return (a.N % 8) == 0 && (a.K % 8) == 0 &&
+         (reinterpret_cast<uintptr_t>(a.dY) & 15u) == 0u &&
+         (reinterpret_cast<uintptr_t>(a.X) & 15u) == 0u &&
+         (a.M + 192) * a.N * ea < kLim && (a.M + 192) * a.K * eb < kLim;
+}
+
+hipError_t launch_backward_weight(const BwdWeightArgs& a, hipStream_t s) {
+  if (a.N == 0 || a.K == 0) return hipSuccess;
+  if (a.M == 0) {
+    if (a.accumulate) return hipSuccess;
+    hipLaunchKernelGGL(k_fill_zero, dim3(grid_for(a.N * a.K)), dim3(256), 0, s, a.dW,
+                       a.N * a.K);
+    return hipGetLastError();
+  }
+  const bool fast = bwd_weight_fast_ok(a);
+  if (a.dy_bf16) return a.x_bf16 ? bwd_weight_dispatch<1, 1>(a, fast, s)
+                                 : bwd_weight_dispatch<1, 0>(a, fast, s);
+  return a.x_bf16 ? bwd_weight_dispatch<0, 1>(a, fast, s) : bwd_weight_dispatch<0, 0>(a, fast, s);
+}
 
 bool bwd_input_fast_ok(const BwdInputArgs& a) {
   const int64_t es = a.bf16 ? 2 : 4;

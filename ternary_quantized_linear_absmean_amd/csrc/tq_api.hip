@@ -338,6 +338,33 @@ tq_status tq_ternary_backward_input(const void* dY, tq_dtype dydt, int64_t M,
   return hip_status(tq::launch_backward_input(a, stream));
 }
 
+tq_status tq_ternary_backward_weight(const void* X, tq_dtype xdt, const void* dY, tq_dtype dydt,
+                                     int64_t M, int64_t N, int64_t K, float* dW, int accumulate,
+                                     hipStream_t stream) {
+  if (M < 0 || N < 0 || K < 0) return TQ_ERR_SHAPE;
+  if ((xdt != TQ_F32 && xdt != TQ_BF16) || (dydt != TQ_F32 && dydt != TQ_BF16))
+    return TQ_ERR_DTYPE;
+  if (N == 0 || K == 0) return TQ_OK;
+  if (!dW) return TQ_ERR_NULL;
+  if (!aligned(dW, 4)) return TQ_ERR_ALIGN;
+  if (M > 0) {
+    if (!X || !dY) return TQ_ERR_NULL;
+    if (!aligned(X, xdt == TQ_BF16 ? 2 : 4) || !aligned(dY, dydt == TQ_BF16 ? 2 : 4))
+      return TQ_ERR_ALIGN;
+  }
+  tq::BwdWeightArgs a;
+  a.X = X;
+  a.x_bf16 = xdt == TQ_BF16 ? 1 : 0;
+  a.dY = dY;
+  a.dy_bf16 = dydt == TQ_BF16 ? 1 : 0;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.dW = dW;
+  a.accumulate = accumulate ? 1 : 0;
+  return hip_status(tq::launch_backward_weight(a, stream));
+}
+
 const char* tq_status_str(tq_status s) {
   switch (s) {
     case TQ_OK: return "ok";

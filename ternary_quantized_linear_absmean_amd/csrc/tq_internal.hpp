@@ -83,5 +83,16 @@ struct BwdInputArgs {
 };
 bool bwd_input_fast_ok(const BwdInputArgs& a);
 hipError_t launch_backward_input(const BwdInputArgs& a, hipStream_t s);
+struct BwdWeightArgs {
+  const void* X;   // [M, K] fp32 or bf16
+  int x_bf16;
+  const void* dY;  // [M, N] fp32 or bf16
+  int dy_bf16;
+  int64_t M, N, K;
+  float* dW;       // [N, K]
+  int accumulate;
+};
+bool bwd_weight_fast_ok(const BwdWeightArgs& a);
+hipError_t launch_backward_weight(const BwdWeightArgs& a, hipStream_t s);
 
 }  // namespace tq

@@ -34,7 +34,7 @@ EXPORTED = ["tq_packed_bytes", "tq_pack_workspace_bytes", "tq_pack_ternary",
             "tq_quant_act_int8", "tq_fwht512", "tq_ternary_gemv", "tq_ternary_gemm",
             "tq_quant_ternary_gemv", "tq_packed1_bytes", "tq_pack_binary1",
             "tq_binary1_gemv", "tq_swiglu_gemv", "tq_ffn_swiglu_decode",
-            "tq_ternary_backward_input", "tq_status_str",
+            "tq_ternary_backward_input", "tq_ternary_backward_weight", "tq_status_str",
             "tq_last_hip_error", "tq_version"]
 
 _vp = ctypes.c_void_p
@@ -80,6 +80,9 @@ _lib.tq_binary1_gemv.restype = _int
 _lib.tq_ternary_backward_input.argtypes = [_vp, _int, _i64, _vp, _vp, _int, _i64, _i64, _vp,
                                            _int, _vp]
 _lib.tq_ternary_backward_input.restype = _int
+_lib.tq_ternary_backward_weight.argtypes = [_vp, _int, _vp, _int, _i64, _i64, _i64, _vp, _int,
+                                            _vp]
+_lib.tq_ternary_backward_weight.restype = _int
 _lib.tq_status_str.argtypes = [_int]
 _lib.tq_status_str.restype = ctypes.c_char_p
 _lib.tq_last_hip_error.argtypes = []
@@ -391,6 +394,32 @@ def tq_ternary_backward_input(dY: torch.Tensor, packed, scale, K: int,
                                           1 if accumulate else 0, _stream(stream)),
            "tq_ternary_backward_input")
     return dX
+
+
+def tq_ternary_backward_weight(X: torch.Tensor, dY: torch.Tensor, dW: torch.Tensor | None = None,
+                               accumulate: bool = False, stream=None) -> torch.Tensor:
+    """dW [N, K] fp32 = dY^T X over the M tokens; with accumulate the result
+    is added to the given dW."""
+    for t, name in ((X, "X"), (dY, "dY")):
+        _dev(t, name)
+        if t.dtype not in _ACT_DT or t.dim() != 2:
+            raise ValueError(f"{name} must be a 2-D float32 or bfloat16 tensor")
+    M, K = X.shape
+    if dY.shape[0] != M:
+        raise ValueError("X and dY must have the same number of rows")
+    N = dY.shape[1]
+    if dW is None:
+        if accumulate:
+            raise ValueError("accumulate needs dW")
+        dW = torch.empty((N, K), dtype=torch.float32, device=X.device)
+    _dev(dW, "dW")
+    if dW.dtype != torch.float32 or tuple(dW.shape) != (N, K):
+        raise ValueError("dW must be float32 [N, K]")
+    _check(_lib.tq_ternary_backward_weight(X.data_ptr(), _ACT_DT[X.dtype], dY.data_ptr(),
+                                           _ACT_DT[dY.dtype], M, N, K, dW.data_ptr(),
+                                           1 if accumulate else 0, _stream(stream)),
+           "tq_ternary_backward_weight")
+    return dW
 
 
 def raw_library() -> ctypes.CDLL:

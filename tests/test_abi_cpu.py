@@ -136,6 +136,24 @@ def test_backward_input_validation():
     assert f(None, 0, 0, None, None, 0, 8, 64, None, 0, None) == OK  # M == 0
 
 
+def test_backward_weight_validation():
+    P = 0x10000
+    f = lib.tq_ternary_backward_weight
+    # (X, xdt, dY, dydt, M, N, K, dW, accumulate, stream)
+    assert f(P, 0, P, 0, -1, 8, 8, P, 0, None) == SHAPE
+    assert f(P, 0, P, 0, 4, -8, 8, P, 0, None) == SHAPE
+    assert f(P, 0, P, 0, 4, 8, -8, P, 0, None) == SHAPE
+    assert f(P, 2, P, 0, 4, 8, 8, P, 0, None) == DTYPE
+    assert f(P, 0, P, 2, 4, 8, 8, P, 0, None) == DTYPE
+    assert f(P, 0, P, 0, 4, 8, 8, None, 0, None) == NULL
+    assert f(None, 0, P, 0, 4, 8, 8, P, 0, None) == NULL
+    assert f(P, 0, None, 0, 4, 8, 8, P, 0, None) == NULL
+    assert f(P + 2, 0, P, 0, 4, 8, 8, P, 0, None) == ALIGN
+    assert f(P, 0, P + 2, 0, 4, 8, 8, P, 0, None) == ALIGN
+    assert f(P, 0, P, 0, 4, 8, 8, P + 1, 0, None) == ALIGN
+    assert f(None, 0, None, 0, 4, 0, 8, None, 0, None) == OK   # empty dW
+
+
 def test_swiglu_validation():
     P = 0x10000
     f = lib.tq_swiglu_gemv

@@ -814,10 +814,19 @@ def test_ffn_swiglu_decode_workload(b):
 
 # ------------------------------------------------------------ backward input
 
+# Bounds of the backward products.  The products dY * gamma * w are exact, so
+# dX carries only accumulation error.  An fp32 add in row order rounds to
+# nearest (u = 2^-24 of the running sum); a matrix-core accumulation step is
+# taken to round faithfully (within one ulp, 2u): with S = sum |terms| the
+# error is at most max(n_add u, 2 n_mfma u) S, n_add = N adds plus the dY *
+# gamma and scale roundings, n_mfma = 3 bf16 planes times ceil(N / 32) steps.
+def _gamma(n):
+    u = 2.0 ** -24
+    return n * u / (1 - n * u)
+
+
 def _bwd_ref_and_bound(dY, packed, scale, K, rows=None):
-    """Oracle dX and the fp32 dot-product bound gamma_{N+2} * sum_n |terms|
-    (the products are exact; N accumulations, the dY * gamma rounding and the
-    final scale multiply each round once in fp32)."""
+    """Oracle dX and its bound (above)."""
     dY = np.asarray(dY, np.float64)
     if rows is not None:
         dY = dY[rows]
@@ -825,9 +834,8 @@ def _bwd_ref_and_bound(dY, packed, scale, K, rows=None):
     w = np.abs(oracle.unpack_codes(packed, K).astype(np.float64))
     g = np.abs(np.asarray(scale, np.float64))
     S = (np.abs(dY) * (g if g.size > 1 else g[0])) @ w
-    u = 2.0 ** -24
-    n = dY.shape[1] + 2
-    return ref, S * (n * u / (1 - n * u))
+    N = dY.shape[1]
+    return ref, S * _gamma(max(N + 2, 2 * 3 * -(-N // 32) + 2))
 
 
 def _assert_bwd_close(dx, ref, bound, what=""):
@@ -932,3 +940,85 @@ def test_backward_input_prefill_workload_sampled(dtype):
     rows = np.sort(np.random.default_rng(73).choice(M, 48, replace=False))
     ref, bound = _bwd_ref_and_bound(dY, packed, scale, K, rows)
     _assert_bwd_close(dx[rows], ref, bound, f"prefill {dtype}")
+
+
+# ----------------------------------------------------------- backward weight
+
+def _wgt_ref_and_bound(X, dY, both_f32, rows=None):
+    """Oracle dW and its bound: accumulation over M as for dX (at most six
+    bf16 products per 32-token step), plus, with both operands fp32, the
+    dropped cross terms of the splits (about 2u |dY X| per product)."""
+    X = np.asarray(X, np.float64)
+    dY = np.asarray(dY, np.float64)
+    if rows is not None:
+        dY = dY[:, rows]
+    ref = oracle.backward_weight(X, dY)
+    S = np.abs(dY).T @ np.abs(X)
+    M = X.shape[0]
+    extra = 3 if both_f32 else 1
+    return ref, S * _gamma(max(M + 2, 2 * 6 * -(-M // 32)) + extra)
+
+
+WGT_CASES = [
+    (32, 128, 128, "f32", "f32", False), (100, 136, 264, "f32", "f32", True),
+    (257, 256, 384, "bf16", "f32", False), (96, 264, 136, "f32", "bf16", True),
+    (2048, 128, 256, "bf16", "bf16", False), (7, 13, 12, "f32", "f32", False),
+    (64, 24, 20, "bf16", "f32", True),
+]
+
+
+@pytest.mark.parametrize("M,N,K,xdt,dydt,acc", WGT_CASES)
+def test_backward_weight(M, N, K, xdt, dydt, acc):
+    say(f"backward_weight M={M} N={N} K={K} X {xdt} dY {dydt} acc={acc}")
+    X = ti.activations(7300 + M, M, K, "normal", xdt)
+    dY = ti.output_grads(7400 + N, M, N, dydt)
+    ref, bound = _wgt_ref_and_bound(X, dY, xdt == dydt == "f32")
+    base = ti.output_grads(8, N, K) if acc else None
+    out = tq.tq_ternary_backward_weight(x_to_device(X, xdt), x_to_device(dY, dydt),
+                                        dW=dev(base) if acc else None, accumulate=acc)
+    dw = host(out).astype(np.float64)
+    if acc:
+        dw = dw - base.astype(np.float64)
+        bound = bound + np.abs(ref + base) * 2.0 ** -24
+    _assert_bwd_close(dw, ref, bound, "backward_weight")
+
+
+def test_backward_weight_single_token_exact_and_empty():
+    # one token, X bf16: the split terms of dY * X sum exactly until the
+    # last step, which rounds once (faithfully: within one ulp)
+    rng = np.random.default_rng(74)
+    N, K = 136, 264
+    X = ti.to_bf16_values(rng.standard_normal((1, K)).astype(np.float32))
+    dY = (rng.standard_normal((1, N)) * np.exp2(rng.integers(-30, 30, (1, N)))).astype(np.float32)
+    dw = host(tq.tq_ternary_backward_weight(dev_bf16(X), dev(dY))).astype(np.float64)
+    exact = dY.T.astype(np.float64) * X.astype(np.float64)
+    assert np.all(np.abs(dw - exact) <= np.abs(exact) * 2.0 ** -23)
+    # both fp32: six of the nine split products, the dropped terms below
+    # 2^-23 |dY X|, then the same rounding
+    Xf = (rng.standard_normal((1, K)) * np.exp2(rng.integers(-30, 30, (1, K)))).astype(np.float32)
+    dw = host(tq.tq_ternary_backward_weight(dev(Xf), dev(dY))).astype(np.float64)
+    exact = dY.T.astype(np.float64) * Xf.astype(np.float64)
+    assert np.all(np.abs(dw - exact) <= np.abs(exact) * 2.0 ** -21)
+    # no tokens: zeros, or dW left as it was with accumulate
+    Xe = torch.zeros((0, K), dtype=torch.float32, device=DEV)
+    dYe = torch.zeros((0, N), dtype=torch.float32, device=DEV)
+    dW = torch.full((N, K), 3.0, dtype=torch.float32, device=DEV)
+    tq.tq_ternary_backward_weight(Xe, dYe, dW=dW, accumulate=True)
+    assert np.all(host(dW) == 3.0)
+    tq.tq_ternary_backward_weight(Xe, dYe, dW=dW)
+    assert np.all(host(dW) == 0.0)
+
+
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_backward_weight_prefill_workload_sampled(xdt):
+    # the prefill layer (2048 tokens, 4096 -> 11008): dW [11008, 4096] in
+    # full on the GPU, 48 sampled rows against the oracle
+    say(f"backward_weight prefill workload X {xdt}")
+    X = ti.workload_activations("prefill")
+    if xdt == "f32":
+        X = ti.activations(ti.act_seed(4, 0, 2048) + 1, 2048, 4096, "normal", "f32")
+    dY = ti.workload_output_grads("prefill")
+    dw = host(tq.tq_ternary_backward_weight(x_to_device(X, xdt), dev(dY)))
+    rows = np.sort(np.random.default_rng(75).choice(dY.shape[1], 48, replace=False))
+    ref, bound = _wgt_ref_and_bound(X, dY, xdt == "f32", rows)
+    _assert_bwd_close(dw[rows], ref, bound, f"prefill dW X {xdt}")
