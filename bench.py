@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--only", default="",
                    help="comma list of extra workloads to run: "
-                        "prefill,bitlinear,pack,ffn,steady,binary1,ffn_decode,context")
+                        "prefill,bitlinear,pack,ffn,steady,binary1,ffn_decode,backward,"
+                        "context")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (for counter scaling)")
     return p.parse_args()
@@ -248,6 +249,8 @@ def extras(torch, np, ti, tq, dev, only=frozenset()):
         out.update(extra_binary1(torch, ti, tq, dev))
     if want("ffn_decode"):
         out.update(extra_ffn_decode(torch, ti, tq, dev))
+    if want("backward"):
+        out.update(extra_backward(torch, ti, tq, dev))
     if want("context"):
         out.update(extra_context(torch, dev))
     torch.cuda.synchronize()
@@ -433,6 +436,54 @@ def extra_ffn_decode(torch, ti, tq, dev):
                         "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1), "launches": 2}
     del sets
     return {"ffn_swiglu_decode": out}
+
+
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def extra_backward(torch, ti, tq, dev):
+    """Backward through the prefill layer (2048 tokens, W 11008 x 4096,
+    per-tensor scale): the input gradient through the packed codes and the
+    weight gradient X^T dY, seeded gradients ~N(0, 1).  TFLOP/s counts the
+    2 M N K of the product; mfma_frac counts the bf16 matrix-core passes the
+    kernel issues (three per fp32 operand split) against the dense bf16 peak.
+    torch's dense fp32 and bf16 products of the same shape are context."""
+    M, N, K = 2048, 11008, 4096
+    W = torch.from_numpy(ti.workload_weights("prefill")).to(dev)
+    packed, scale = tq.tq_pack_ternary(W, "tensor")
+    del W
+    dY32 = torch.from_numpy(ti.workload_output_grads("prefill")).to(dev)
+    X16 = torch.from_numpy(ti.workload_activations("prefill")).to(dev).to(torch.bfloat16)
+    X32 = X16.float()
+    flops = 2.0 * M * N * K
+    out = {}
+    R = 5
+
+    def timed(fn):
+        g = capture(torch, lambda: [fn() for _ in range(R)])
+        timed_graph(torch, g, 1)
+        return timed_graph(torch, g, 3) / R
+
+    dX = torch.empty((M, K), dtype=torch.float32, device=dev)
+    for name, dY, passes in (("f32", dY32, 3), ("bf16", dY32.bfloat16(), 1)):
+        t = timed(lambda: tq.tq_ternary_backward_input(dY, packed, scale, K, dX=dX))
+        out[f"input_grad_dY_{name}"] = {
+            "us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
+            "mfma_frac": round(passes * flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS, 3)}
+    dW = torch.empty((N, K), dtype=torch.float32, device=dev)
+    for name, X, dY, passes in (("X_f32_dY_f32", X32, dY32, 6), ("X_bf16_dY_f32", X16, dY32, 3),
+                                ("X_bf16_dY_bf16", X16, dY32.bfloat16(), 1)):
+        t = timed(lambda: tq.tq_ternary_backward_weight(X, dY, dW=dW))
+        out[f"weight_grad_{name}"] = {
+            "us": round(t * 1e6, 1), "TFLOPs": round(flops / t / 1e12, 1),
+            "mfma_frac": round(passes * flops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS, 3)}
+    Wd = torch.randn((N, K), device=dev)
+    for name, dt in (("f32", torch.float32), ("bf16", torch.bfloat16)):
+        a, b = dY32.to(dt), Wd.to(dt)
+        t = timed(lambda: torch.mm(a, b))
+        out[f"context_torch_dense_mm_{name}"] = {"us": round(t * 1e6, 1),
+                                                "TFLOPs": round(flops / t / 1e12, 1)}
+    return {"backward_prefill_2048x11008x4096": out}
 
 
 def extra_context(torch, dev):
