@@ -63,6 +63,15 @@ constexpr int kPlane = kBM * kArow;       // bytes of one bf16 plane
 constexpr int kWrow = 40;                 // bytes of one transposed code row
 constexpr int kWbytes = (kBK / 4) * kWrow;
 
+#ifndef TQ_BWD_KS3
+#define TQ_BWD_KS3 2
+#endif
+#ifndef TQ_BWD_KS1
+#define TQ_BWD_KS1 4
+#endif
+// MFMA steps (of kBN rows) per LDS stage, with three bf16 planes or one
+constexpr int kBwdKS3 = TQ_BWD_KS3, kBwdKS1 = TQ_BWD_KS1;
+
 template <int P>
 constexpr int bwd_stage_bytes() { return P * kPlane + kWbytes; }
 
@@ -125,7 +134,10 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
     const float* __restrict__ scale, int64_t N, int64_t K, float* __restrict__ dX) {
   constexpr int P = (DT == 0 || ROWG) ? 3 : 1;  // bf16 planes
   constexpr int ES = DT == 0 ? 4 : 2;           // bytes per dY element
-  constexpr int kStage = bwd_stage_bytes<P>();
+  constexpr int KS = P == 3 ? kBwdKS3 : kBwdKS1;  // MFMA steps per stage
+  constexpr int kStep = bwd_stage_bytes<P>();   // LDS bytes of one MFMA step
+  constexpr int kStage = KS * kStep;
+  constexpr int YL = ES == 4 ? 2 : 1;           // 16-byte dY loads per step
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
 
   const int tid = threadIdx.x;
@@ -154,8 +166,8 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
       const_cast<float*>(scale), static_cast<short>(0), static_cast<int>(ROWG ? N * 4 : 4),
       kBufFlags);
 
-  // staging roles: every thread one row x 8 columns of dY, and one code byte
-  // (column byte `lane`) of four consecutive W rows (4 * wave ..)
+  // staging roles, per MFMA step: every thread one row x 8 columns of dY,
+  // and one code byte (column byte `lane`) of four consecutive W rows
   const int sr = tid >> 2, sc = tid & 3;
   const uint32_t yoff = static_cast<uint32_t>((sr * N + 8 * sc) * ES);
   const int yst = swz64(sr, sc);
@@ -173,57 +185,72 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
   const int brd = P * kPlane + (wk * 16 + fr) * kWrow + 8 * fg;
 
   struct Regs {
-    v4i y[ES == 4 ? 2 : 1];
-    v4i gm[ROWG ? 2 : 1];
-    uint32_t w[4];  // one code byte each
+    v4i y[KS][YL];
+    uint32_t w[KS][4];  // one code byte each
   };
+  typedef v4i Gam[ROWG ? KS : 1][2];
   auto load_stage = [&](int64_t kt, Regs& r) {
-    const int so = static_cast<int>(kt * kBN * ES);
-    r.y[0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ry, yoff, so, 0));
-    if constexpr (ES == 4)
-      r.y[1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ry, yoff + 16, so, 0));
-    if constexpr (ROWG) {
-      const uint32_t go = static_cast<uint32_t>((kt * kBN + 8 * sc) * 4);
-      r.gm[0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rg, go, 0, 0));
-      r.gm[1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rg, go + 16, 0, 0));
-    }
-    const int sw = static_cast<int>(kt * kBN * rowbytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      r.w[i] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(
-          rw, woff + static_cast<uint32_t>(i * rowbytes), sw, 0));
+    for (int ks = 0; ks < KS; ++ks) {
+      const int64_t j = kt * KS + ks;
+      const int so = static_cast<int>(j * kBN * ES);
+#pragma unroll
+      for (int i = 0; i < YL; ++i)
+        r.y[ks][i] = __builtin_bit_cast(
+            v4i, __builtin_amdgcn_raw_buffer_load_b128(ry, yoff + 16 * i, so, 0));
+      const int sw = static_cast<int>(j * kBN * rowbytes);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        r.w[ks][i] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(
+            rw, woff + static_cast<uint32_t>(i * rowbytes), sw, 0));
+    }
   };
-  auto store_stage = [&](int buf, int64_t kt, Regs& r) {
-    uint8_t* st = lds + buf * kStage;
-    // the loaded values enter here: without this the compiler combines the
-    // code bytes right after their loads and waits for them a step early
+  // per-row scales of a stage's columns (issued before the far loads of the
+  // same step, so that waiting for them leaves those in flight)
+  auto load_gamma = [&](int64_t kt, Gam& g) {
+    if constexpr (ROWG) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(r.w[i]));
-    const bool ok = kt * kBN + 8 * sc < N;
-    if constexpr (P == 1) {
-      const v4i z = {0, 0, 0, 0};
-      *reinterpret_cast<v4i*>(st + yst) = ok ? r.y[0] : z;
-    } else {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        if constexpr (ES == 4) {
-          x[e] = __int_as_float(r.y[e / 4][e % 4]);
-        } else {
-          const uint32_t u = static_cast<uint32_t>(r.y[0][e / 2]);
-          x[e] = (e & 1) ? bf_hi(u) : bf_lo(u);
-        }
-        x[e] = ok ? x[e] : 0.f;
-        if constexpr (ROWG) x[e] *= __int_as_float(r.gm[e / 4][e % 4]);
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t go = static_cast<uint32_t>(((kt * KS + ks) * kBN + 8 * sc) * 4);
+        g[ks][0] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rg, go, 0, 0));
+        g[ks][1] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rg, go + 16, 0, 0));
       }
-      v4i h, m, l;
-      split3(x, h, m, l);
-      *reinterpret_cast<v4i*>(st + yst) = h;
-      *reinterpret_cast<v4i*>(st + kPlane + yst) = m;
-      *reinterpret_cast<v4i*>(st + 2 * kPlane + yst) = l;
     }
-    *reinterpret_cast<uint32_t*>(st + wst) =
-        r.w[0] | (r.w[1] << 8) | (r.w[2] << 16) | (r.w[3] << 24);
+  };
+  auto store_stage = [&](int buf, int64_t kt, Regs& r, Gam& g) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      uint8_t* st = lds + buf * kStage + ks * kStep;
+      // the loaded values enter here: without this the compiler combines the
+      // code bytes right after their loads and waits for them a step early
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(r.w[ks][i]));
+      const bool ok = (kt * KS + ks) * kBN + 8 * sc < N;
+      if constexpr (P == 1) {
+        const v4i z = {0, 0, 0, 0};
+        *reinterpret_cast<v4i*>(st + yst) = ok ? r.y[ks][0] : z;
+      } else {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          if constexpr (ES == 4) {
+            x[e] = __int_as_float(r.y[ks][e / 4][e % 4]);
+          } else {
+            const uint32_t u = static_cast<uint32_t>(r.y[ks][0][e / 2]);
+            x[e] = (e & 1) ? bf_hi(u) : bf_lo(u);
+          }
+          x[e] = ok ? x[e] : 0.f;
+          if constexpr (ROWG) x[e] *= __int_as_float(g[ks][e / 4][e % 4]);
+        }
+        v4i h, m, l;
+        split3(x, h, m, l);
+        *reinterpret_cast<v4i*>(st + yst) = h;
+        *reinterpret_cast<v4i*>(st + kPlane + yst) = m;
+        *reinterpret_cast<v4i*>(st + 2 * kPlane + yst) = l;
+      }
+      *reinterpret_cast<uint32_t*>(st + wst) =
+          r.w[ks][0] | (r.w[ks][1] << 8) | (r.w[ks][2] << 16) | (r.w[ks][3] << 24);
+    }
   };
 
   f4 acc[4][4];
@@ -232,49 +259,56 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
 #pragma unroll
     for (int f = 0; f < 4; ++f) acc[a][f] = f4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t nk = (N + kBN - 1) / kBN;
-  // one step: start the loads of step kt+2, contract step kt from LDS,
-  // publish step kt+1.  In the main loop every step loads and stores
+  const int64_t nk = (N + KS * kBN - 1) / (KS * kBN);  // stages
+  // one stage: start the loads of stage kt+2, contract stage kt from LDS,
+  // publish stage kt+1.  In the main loop every stage loads and stores
   // unconditionally (a branch around the loads would make the compiler wait
-  // for all loads in flight); loads past the last step read zeros or data
-  // that is never used, and a store of step nk goes to the LDS half that no
-  // later step reads.
+  // for all loads in flight); loads past the last stage read zeros or data
+  // that is never used (columns past N are zeroed on staging), and a store of
+  // stage nk goes to the LDS half that no later stage reads.
   auto step = [&](int64_t kt, Regs& r_next, Regs& r_far, auto guard) {
     constexpr bool GUARD = decltype(guard)::value;
     const int buf = static_cast<int>(kt & 1);
+    Gam g;
+    if (!GUARD || kt + 1 < nk) load_gamma(kt + 1, g);
     if (!GUARD || kt + 2 < nk) load_stage(kt + 2, r_far);
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* st = lds + buf * kStage;
-    const uint2 wb = *reinterpret_cast<const uint2*>(st + brd);
-    bf16x8 av[P][4];
 #pragma unroll
-    for (int p = 0; p < P; ++p)
+    for (int ks = 0; ks < KS; ++ks) {
+      const uint8_t* st = lds + buf * kStage + ks * kStep;
+      const uint2 wb = *reinterpret_cast<const uint2*>(st + brd);
+      bf16x8 av[P][4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        av[p][a] = *reinterpret_cast<const bf16x8*>(st + p * kPlane + ard[a]);
-    bf16x8 b[4];
-    b[0] = decode_column<0>(wb.x, wb.y);
-    b[1] = decode_column<1>(wb.x, wb.y);
-    b[2] = decode_column<2>(wb.x, wb.y);
-    b[3] = decode_column<3>(wb.x, wb.y);
+      for (int p = 0; p < P; ++p)
 #pragma unroll
-    for (int p = P - 1; p >= 0; --p)  // smallest terms first
+        for (int a = 0; a < 4; ++a)
+          av[p][a] = *reinterpret_cast<const bf16x8*>(st + p * kPlane + ard[a]);
+      bf16x8 b[4];
+      b[0] = decode_column<0>(wb.x, wb.y);
+      b[1] = decode_column<1>(wb.x, wb.y);
+      b[2] = decode_column<2>(wb.x, wb.y);
+      b[3] = decode_column<3>(wb.x, wb.y);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int p = P - 1; p >= 0; --p)  // smallest terms first
 #pragma unroll
-        for (int f = 0; f < 4; ++f)
-          acc[a][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[p][a], b[f], acc[a][f], 0, 0, 0);
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int f = 0; f < 4; ++f)
+            acc[a][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[p][a], b[f], acc[a][f], 0, 0, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if (!GUARD || kt + 1 < nk) store_stage(buf ^ 1, kt + 1, r_next);
+    if (!GUARD || kt + 1 < nk) store_stage(buf ^ 1, kt + 1, r_next, g);
     __syncthreads();
   };
   using Free = std::false_type;
   using Guarded = std::true_type;
 
   Regs r0, r1, r2;
+  Gam g0;
+  load_gamma(0, g0);
   load_stage(0, r0);
   load_stage(1, r1);
-  store_stage(0, 0, r0);
+  store_stage(0, 0, r0, g0);
   __syncthreads();
   int64_t kt = 0;
   for (; kt + 3 <= nk; kt += 3) {
@@ -287,7 +321,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
 
   // D of the 16x16 MFMA: lane l holds rows 4(l/16)+i of column l%16, and
   // fragment f is column 4(l%16)+f of the wave's 64
-  const float g0 = ROWG ? 1.f : scale[0];
+  const float gt = ROWG ? 1.f : scale[0];
   const int64_t col = k0 + wk * 64 + 4 * fr;
   if (col >= K) return;
 #pragma unroll
@@ -297,7 +331,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
       const int64_t row = m0 + wm * 64 + 16 * a + 4 * fg + i;
       if (row >= M) continue;
       f4 v = {acc[a][0][i], acc[a][1][i], acc[a][2][i], acc[a][3][i]};
-      if (!ROWG) v = v * g0;
+      if (!ROWG) v = v * gt;
       f4* o = reinterpret_cast<f4*>(dX + row * K + col);
       if (ACC) v = v + *o;
       *o = v;
@@ -377,17 +411,24 @@ int64_t grid_for(int64_t n) {
 // matrix cores' accumulation rounds faithfully, not always to nearest).
 //
 // A workgroup (8 waves, 4 x 2, 32 x 64 each) owns a 128 x 128 dW tile.  A
-// stage holds KS = 2 MFMA steps (64 tokens) when LDS allows, one (32 tokens)
-// with both operands fp32; with two steps every thread stages one unit
-// (8 rows x 2 columns) of each operand, with one step threads 0..255 stage
-// dY and 256..511 stage X.  Either way all threads issue the same loads.
+// stage holds KS MFMA steps of 32 tokens, as many as double-buffered LDS
+// allows (4 with two bf16 operands, 2 with one fp32 operand, 1 with two);
+// with KS >= 2 every thread stages KS/2 units (8 rows x 2 columns) of each
+// operand, with one step threads 0..255 stage dY and 256..511 stage X.
+// Either way all threads issue the same loads.
 
 constexpr int kGN = 128, kGK = 128;  // dW tile
 constexpr int kGPlane = 128 * 64;    // one plane: 128 rows of 32 bf16
 constexpr int kPN = 4, kPK = 8;      // tiles of a patch (one per CU of an XCD)
 
 __host__ __device__ constexpr int planes_of(int dt) { return dt == 0 ? 3 : 1; }
-__host__ __device__ constexpr int wgt_ks(int da, int db) { return (da == 0 && db == 0) ? 1 : 2; }
+#ifndef TQ_WGT_KS_BF16
+#define TQ_WGT_KS_BF16 4
+#endif
+// MFMA steps per LDS stage: as many as 160 KiB of double-buffered LDS allow
+__host__ __device__ constexpr int wgt_ks(int da, int db) {
+  return (da == 0 && db == 0) ? 1 : (da == 1 && db == 1) ? TQ_WGT_KS_BF16 : 2;
+}
 template <int DA, int DB>
 constexpr int wgt_lds_bytes() {
   return 2 * wgt_ks(DA, DB) * (planes_of(DA) + planes_of(DB)) * kGPlane;
@@ -425,8 +466,10 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
   if (tn >= tiles_n || tk >= tiles_k) return;  // padding ids (whole workgroup)
   const int64_t n0 = tn * kGN, k0 = tk * kGK;
 
-  // staging unit of this thread: columns 2cp, 2cp+1, token rows 8o..8o+7 of
-  // the stage (o < 4 KS); with roles, waves 0..3 stage dY and 4..7 stage X
+  // staging units of this thread: columns 2cp, 2cp+1, token rows 8o..8o+7 of
+  // the stage for o = uo + 8u (u < U); with roles, waves 0..3 stage dY and
+  // 4..7 stage X
+  constexpr int U = kRoles ? 1 : KS / 2;
   const bool role_a = !kRoles || wave < 4;
   const int ut = kRoles ? (tid & 255) : tid;
   const int cp = ut & 63, uo = ut >> 6;
@@ -438,47 +481,63 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
       static_cast<int>(M * K * ESB - k0 * ESB), kBufFlags);
   const uint32_t aoff = static_cast<uint32_t>((8 * uo * N + 2 * cp) * ESA);
   const uint32_t boff = static_cast<uint32_t>((8 * uo * K + 2 * cp) * ESB);
-  // LDS offsets of the unit's two column rows within its operand's plane 0
+  // LDS offsets of unit 0's two column rows within its operand's plane 0;
+  // unit u sits 2u MFMA steps further
   const int ubase = (uo >> 2) * kStep;
   const int wo0 = ubase + swz64(2 * cp, uo & 3), wo1 = ubase + swz64(2 * cp + 1, uo & 3);
 
-  struct Regs { uint2 a[8]; uint2 b[kRoles ? 1 : 8]; };
-  // 8 rows of one unit: fp32 pairs (8 bytes) or bf16 pairs (4 bytes, in .x)
-  auto load_unit = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t str, int so, int es,
-                       uint2 (&v)[8]) {
+  // a unit: 8 rows of two fp32 (two words) or two bf16 (one word) columns
+  struct Regs {
+    uint32_t a[U][8][ESA / 2];
+    uint32_t b[kRoles ? 1 : U][8][ESB / 2];
+  };
+  auto load_unit = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t str, int so, auto es,
+                       auto& v) {
+    constexpr int E = decltype(es)::value;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (es == 4) {
-        v[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off + i * str, so, 0));
+      if constexpr (E == 4) {
+        const uint2 t = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(r, off + i * str, so, 0));
+        v[i][0] = t.x;
+        v[i][E / 2 - 1] = t.y;
       } else {
-        v[i].x = __builtin_amdgcn_raw_buffer_load_b32(r, off + i * str, so, 0);
-        v[i].y = 0u;
+        v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(r, off + i * str, so, 0);
       }
     }
   };
+  using EA = std::integral_constant<int, ESA>;
+  using EB = std::integral_constant<int, ESB>;
   auto load_stage = [&](int64_t st, Regs& r) {
     if constexpr (kRoles) {
       // both operands fp32: the same loads, buffer and offsets by role
       const int64_t rl = role_a ? N : K;
       load_unit(role_a ? ra : rb, role_a ? aoff : boff, static_cast<uint32_t>(rl * 4),
-                static_cast<int>(st * kGM * rl * 4), 4, r.a);
+                static_cast<int>(st * kGM * rl * 4), EA{}, r.a[0]);
     } else {
-      load_unit(ra, aoff, static_cast<uint32_t>(N * ESA), static_cast<int>(st * kGM * N * ESA),
-                ESA, r.a);
-      load_unit(rb, boff, static_cast<uint32_t>(K * ESB), static_cast<int>(st * kGM * K * ESB),
-                ESB, r.b);
+      const uint32_t sa = static_cast<uint32_t>(N * ESA), sb = static_cast<uint32_t>(K * ESB);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        load_unit(ra, aoff + 64 * u * sa, sa, static_cast<int>(st * kGM * N * ESA), EA{},
+                  r.a[u]);
+        load_unit(rb, boff + 64 * u * sb, sb, static_cast<int>(st * kGM * K * ESB), EB{},
+                  r.b[u]);
+      }
     }
   };
   // one unit -> its operand's planes (plane 0 at `base`)
-  auto put_unit = [&](uint8_t* base, int es, uint2 (&v)[8]) {
+  auto put_unit = [&](uint8_t* base, auto es, auto& v) {
+    constexpr int E = decltype(es)::value;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(v[i].x), "+v"(v[i].y));
-    if (es == 4) {
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < E / 2; ++j) asm volatile("" : "+v"(v[i][j]));
+    if constexpr (E == 4) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         float x[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(c ? v[i].y : v[i].x);
+        for (int i = 0; i < 8; ++i) x[i] = __uint_as_float(v[i][c * (E / 2 - 1)]);
         v4i h, m, l;
         split3(x, h, m, l);
         const int o = c ? wo1 : wo0;
@@ -491,8 +550,8 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
       v4i c0, c1;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        c0[t] = static_cast<int>(__builtin_amdgcn_perm(v[2 * t + 1].x, v[2 * t].x, 0x05040100u));
-        c1[t] = static_cast<int>(__builtin_amdgcn_perm(v[2 * t + 1].x, v[2 * t].x, 0x07060302u));
+        c0[t] = static_cast<int>(__builtin_amdgcn_perm(v[2 * t + 1][0], v[2 * t][0], 0x05040100u));
+        c1[t] = static_cast<int>(__builtin_amdgcn_perm(v[2 * t + 1][0], v[2 * t][0], 0x07060302u));
       }
       *reinterpret_cast<v4i*>(base + wo0) = c0;
       *reinterpret_cast<v4i*>(base + wo1) = c1;
@@ -501,10 +560,13 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
   auto store_stage = [&](int buf, Regs& r) {
     uint8_t* st = lds + buf * kStage;
     if constexpr (kRoles) {
-      put_unit(st + (role_a ? 0 : PA * kGPlane), 4, r.a);
+      put_unit(st + (role_a ? 0 : PA * kGPlane), EA{}, r.a[0]);
     } else {
-      put_unit(st, ESA, r.a);
-      put_unit(st + PA * kGPlane, ESB, r.b);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        put_unit(st + 2 * u * kStep, EA{}, r.a[u]);
+        put_unit(st + 2 * u * kStep + PA * kGPlane, EB{}, r.b[u]);
+      }
     }
   };
 
@@ -660,7 +722,7 @@ bool bwd_weight_fast_ok(const BwdWeightArgs& a) {
   return (a.N % 8) == 0 && (a.K % 8) == 0 &&
          (reinterpret_cast<uintptr_t>(a.dY) & 15u) == 0u &&
          (reinterpret_cast<uintptr_t>(a.X) & 15u) == 0u &&
-         (a.M + 192) * a.N * ea < kLim && (a.M + 192) * a.K * eb < kLim;
+         (a.M + 384) * a.N * ea < kLim && (a.M + 384) * a.K * eb < kLim;
 }
 
 hipError_t launch_backward_weight(const BwdWeightArgs& a, hipStream_t s) {
@@ -683,8 +745,8 @@ bool bwd_input_fast_ok(const BwdInputArgs& a) {
   return (a.N % 8) == 0 && (reinterpret_cast<uintptr_t>(a.dY) & 15u) == 0u &&
          (reinterpret_cast<uintptr_t>(a.dX) & 15u) == 0u &&
          (!a.per_row || (reinterpret_cast<uintptr_t>(a.scale) & 15u) == 0u) &&
-         int64_t{kBM} * a.N * es < kLim && (a.N + 2 * kBN) * (a.K / 4) < kLim &&
-         (a.N + 2 * kBN) * 4 < kLim;
+         int64_t{kBM} * a.N * es < kLim && (a.N + 3 * 4 * kBN) * (a.K / 4) < kLim &&
+         (a.N + 3 * 4 * kBN) * 4 < kLim;
 }
 
 hipError_t launch_backward_input(const BwdInputArgs& a, hipStream_t s) {

@@ -858,6 +858,7 @@ BWD_CASES = [
     (130, 72, 516, "f32", "tensor", True), (257, 104, 1028, "bf16", "tensor", False),
     (129, 264, 772, "bf16", "row", True), (300, 520, 1536, "f32", "row", False),
     (64, 37, 64, "f32", "tensor", False), (33, 45, 132, "bf16", "row", True),
+    (200, 392, 520, "bf16", "tensor", True), (130, 200, 264, "f32", "tensor", False),
 ]
 
 
@@ -963,7 +964,8 @@ WGT_CASES = [
     (32, 128, 128, "f32", "f32", False), (100, 136, 264, "f32", "f32", True),
     (257, 256, 384, "bf16", "f32", False), (96, 264, 136, "f32", "bf16", True),
     (2048, 128, 256, "bf16", "bf16", False), (7, 13, 12, "f32", "f32", False),
-    (64, 24, 20, "bf16", "f32", True),
+    (64, 24, 20, "bf16", "f32", True), (300, 136, 264, "bf16", "bf16", True),
+    (161, 264, 136, "f32", "f32", False),
 ]
 
 
