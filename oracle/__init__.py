@@ -14,4 +14,6 @@ from .tq_oracle import (absmean_scale, absmean_scales, binarize, contract,
                         unpack_codes, bf16_round_from_f64, FWHT_NORM,
                         packed1_bytes, pack_signs, unpack_signs, pack_binary1,
                         contract_signs, swiglu_clamped, ffn_swiglu_decode,
-                        SWIGLU_CLAMP, backward_input, backward_weight)
+                        SWIGLU_CLAMP, backward_input, backward_weight,
+                        ternarize_threshold, encode_format, decode_format,
+                        convert_codes, FORMATS)

@@ -25,6 +25,17 @@ Sources (cited by page title and section):
   gradient against the packed ternary weights, summing over N, accumulated
   with += into a caller-zeroed buffer; the weight gradient is the plain float
   product X^T dY with no ternary part and no scale.
+* Foundry, docs/quantization.md -- "Absmean Thresholding (BitNet b1.58)"
+  (+1 above the threshold, -1 below its negative, 0 between, the threshold
+  being mean|w| or a manual value, and the scale the threshold) and the API
+  reference (``fq_quantize_ternary_threshold``).
+* BitRASP, core_math.py -- ``ternarize_weight``: per-row absmean scale and
+  codes w > 0.55*scale -> +1, w < -0.55*scale -> -1, else 0.
+* Hetman-2b, src/quantization.py, section 3 (PackedTernaryStorage): Format 0
+  (0 -> 00, +1 -> 01, -1 -> 11, 10 reserved as 0) and Format 1 (0 -> 00,
+  +1 -> 01, -1 -> 10, 11 reserved as 0), four codes per byte LSB-first,
+  decoded with P = B & 0x55, N = (B >> 1) & 0x55 as P - 2(P & N) (Format 0)
+  or P - N (Format 1).
 * qste 0.1.1 project description -- "What it costs and what it buys"
   (binary +-1 weights with a per-row scale, deployed as R*C/8 bytes of
   packed signs plus 4*R bytes of scales).
@@ -48,6 +59,13 @@ in the design notes):
 * 1-bit sign packing of binary weights (qste "What it costs and what it
   buys" gives the size, not the layout): eight signs per byte, LSB-first,
   bit 1 for +1 and bit 0 for -1, rows of K/8 bytes along K.
+* Threshold options: the comparisons are strict and taken in fp32 against
+  fp32(f * gamma) (a factor of the absmean scale, as BitRASP computes
+  threshold * scale in its tensor precision) or against the manual value t,
+  whose scale is t itself (Foundry: the scale is the threshold).
+* Code formats: this library's own codes (-1 = 00, 0 = 01, +1 = 10) convert
+  to and from Hetman-2b's Formats 0 and 1 value by value; the reserved code
+  of each format (11 here, 10 in Format 0, 11 in Format 1) reads as 0.
 * Backward through the input: the layer computes y = gamma * x w^T (the
   activation quantiser passed straight through, as the pages' straight-
   through estimator does), so dX = (dY * gamma) w; the page does not say
@@ -237,6 +255,86 @@ def pack_ternary(W: np.ndarray, granularity: str = "tensor", mode: str = "ternar
     else:
         raise ValueError(mode)
     return pack_codes(q), gam
+
+
+def ternarize_threshold(W: np.ndarray, granularity: str, kind: str, value: float):
+    """Codes and scales by a threshold (Foundry "Absmean Thresholding" and
+    ``fq_quantize_ternary_threshold``; BitRASP ``ternarize_weight``).
+    kind "relative": gamma = the absmean scale (per tensor or row), threshold
+    h = fp32(fp32(value) * gamma), scale gamma; value 1 is Foundry's absmean
+    rule, 0.55 BitRASP's.  kind "absolute": h = fp32(value) and the scale is h
+    (per tensor).  q = +1 where w > h, -1 where w < -h, else 0."""
+    W = np.asarray(W, dtype=np.float32)
+    if kind == "relative":
+        gam = absmean_scales(W, granularity)
+        h = (F32(value) * gam).astype(np.float32)          # fp32 product
+        scales = gam
+    elif kind == "absolute":
+        if granularity != "tensor":
+            raise ValueError("a manual threshold is one value for the tensor")
+        h = np.array([F32(value)], dtype=np.float32)
+        scales = h.copy()
+    else:
+        raise ValueError(kind)
+    hh = h.reshape(-1, 1) if h.size > 1 else h.reshape(1, 1)
+    q = np.zeros(W.shape, dtype=np.int8)
+    q[W > hh] = 1
+    q[W < -hh] = -1
+    return q, scales
+
+
+FORMATS = ("native", "f0", "f1")
+
+
+def encode_format(q: np.ndarray, fmt: str) -> np.ndarray:
+    """Pack ternary values along the last axis, four per byte LSB-first, in
+    this library's codes ("native") or Hetman-2b s.3 Format 0 / Format 1.
+    Format 0's code is the low two bits of the two's-complement int8 value;
+    Format 1 maps -1 to 0b10."""
+    q = np.asarray(q).astype(np.int8)
+    if q.ndim == 1:
+        q = q.reshape(1, -1)
+    if q.shape[-1] % 4:
+        raise ValueError("rows must hold a multiple of four values")
+    if fmt == "native":
+        return pack_codes(q)
+    if fmt == "f0":
+        codes = (q.view(np.uint8) & np.uint8(3))              # w & 3
+    elif fmt == "f1":
+        codes = np.where(q == -1, 2, np.where(q == 1, 1, 0)).astype(np.uint8)
+    else:
+        raise ValueError(fmt)
+    n, k = q.shape
+    c = codes.reshape(n, k // 4, 4)
+    return (c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)).astype(np.uint8)
+
+
+def decode_format(packed: np.ndarray, fmt: str) -> np.ndarray:
+    """Values of packed codes in any format (reserved codes read as 0).
+    Formats 0 and 1 by the page's bitmasks: per 2-bit field, p = low bit and
+    n = high bit; Format 0 v = p - 2(p & n), Format 1 v = p - n.  Native codes
+    c = 0, 1, 2 are v = c - 1, with c = 3 read as 0."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    if packed.ndim == 1:
+        packed = packed.reshape(1, -1)
+    n, nb = packed.shape
+    fields = np.stack([(packed >> np.uint8(2 * t)) & np.uint8(3) for t in range(4)], axis=-1)
+    p = (fields & 1).astype(np.int8)
+    hi = ((fields >> 1) & 1).astype(np.int8)
+    if fmt == "f0":
+        v = p - 2 * (p & hi)
+    elif fmt == "f1":
+        v = p - hi
+    elif fmt == "native":
+        v = np.where(fields == 3, 0, fields.astype(np.int16) - 1).astype(np.int8)
+    else:
+        raise ValueError(fmt)
+    return v.reshape(n, nb * 4).astype(np.int8)
+
+
+def convert_codes(packed: np.ndarray, src: str, dst: str) -> np.ndarray:
+    """Re-encode packed codes from one format to another, value by value."""
+    return encode_format(decode_format(packed, src), dst)
 
 
 def packed1_bytes(numel: int) -> int:

@@ -29,6 +29,11 @@ def _golden(name):
     return rows
 
 
+def _golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [line.strip() for line in f if line.strip() and not line.startswith("#")]
+
+
 def _f32(bits):
     return np.array([bits], dtype=np.uint32).view(np.float32)[0]
 
@@ -693,3 +698,87 @@ def test_backward_brute_force():
         for k in range(K):
             ref = sum(dY[m, n] * X[m, k] for m in range(M))
             assert abs(dW[n, k] - ref) < 1e-12
+
+
+# ----------------------------------------------------- thresholds and formats
+
+def test_code_formats_golden():
+    for a, b in _golden("code_formats.txt"):
+        kind, *vals = a.split()
+        if kind == "enc":
+            v = np.array([int(x) for x in vals], dtype=np.int8)
+            for fmt, hx in zip(("native", "f0", "f1"), b.split()):
+                byte = oracle.encode_format(v, fmt)
+                assert int(byte[0, 0]) == int(hx, 16), (vals, fmt)
+                assert np.array_equal(oracle.decode_format(byte, fmt)[0], v)
+        else:
+            fmt, hx = vals
+            got = oracle.decode_format(np.array([int(hx, 16)], np.uint8), fmt)[0]
+            assert got.tolist() == [int(x) for x in b.split()]
+
+
+def test_code_formats_roundtrip_and_conversion():
+    q = ti.random_ternary(21, 9, 64)
+    enc = {f: oracle.encode_format(q, f) for f in oracle.FORMATS}
+    assert np.array_equal(enc["native"], oracle.pack_codes(q))
+    for f in oracle.FORMATS:
+        assert np.array_equal(oracle.decode_format(enc[f], f), q)
+        for g in oracle.FORMATS:
+            assert np.array_equal(oracle.convert_codes(enc[f], f, g), enc[g])
+    # Format 0 is the two's-complement low bits of the value (the page's w & 3)
+    for v in (-1, 0, 1):
+        assert int(oracle.encode_format(np.full(4, v, np.int8), "f0")[0, 0]) == \
+            sum((v & 3) << (2 * i) for i in range(4))
+    # every byte decodes to values in {-1, 0, 1}, and re-encoding a decoded
+    # byte maps reserved codes to the format's zero code
+    allb = np.arange(256, dtype=np.uint8).reshape(1, -1)
+    for f in oracle.FORMATS:
+        v = oracle.decode_format(allb, f)
+        assert set(np.unique(v)) <= {-1, 0, 1}
+        again = oracle.encode_format(v, f)
+        assert np.array_equal(oracle.decode_format(again, f), v)
+
+
+def test_thresholds_golden():
+    for a, b, c in (line.split(";") for line in _golden_lines("thresholds.txt")):
+        kind, value, *w = a.split()
+        W = np.array([[float(x) for x in w]], dtype=np.float32)
+        q, sc = oracle.ternarize_threshold(W, "tensor", kind, float(value))
+        assert q[0].tolist() == [int(x) for x in b.split()], a
+        assert float(sc[0]) == float(c)
+
+
+def test_threshold_half_factor_is_the_rounding_rule():
+    # |w| > gamma/2 is round(w/gamma) != 0 (ties to even put 0.5 at 0), and
+    # fp32(0.5) * gamma = gamma/2 exactly: the two routes must agree
+    for gran in ("tensor", "row"):
+        W = ti.normal_weights(22, 64, 256)
+        q, sc = oracle.ternarize_threshold(W, gran, "relative", 0.5)
+        gam = oracle.absmean_scales(W, gran)
+        assert np.array_equal(q, oracle.ternarize(W, gam))
+        assert np.array_equal(sc, gam)
+    # exact ties at gamma/2 stay zero on both routes
+    W = np.array([[0.5, -0.5, 1.5, -1.5]], np.float32)      # gamma = 1
+    q, _ = oracle.ternarize_threshold(W, "tensor", "relative", 0.5)
+    assert q[0].tolist() == oracle.ternarize(W, np.array([1.0], np.float32))[0].tolist() == [0, 0, 1, -1]
+
+
+def test_threshold_monotone_and_brute_force():
+    W = ti.normal_weights(23, 16, 128)
+    prev = None
+    for f in (0.0, 0.3, 0.55, 1.0, 2.0):
+        q, gam = oracle.ternarize_threshold(W, "row", "relative", f)
+        nz = np.count_nonzero(q)
+        if prev is not None:
+            assert nz <= prev
+        prev = nz
+        if f == 0.0:
+            assert np.array_equal(q, np.sign(W).astype(np.int8))
+        for i in range(0, 16, 5):
+            h = np.float32(np.float32(f) * gam[i])
+            for j in range(0, 128, 7):
+                w = W[i, j]
+                assert q[i, j] == (1 if w > h else (-1 if w < -h else 0))
+    q, sc = oracle.ternarize_threshold(W, "tensor", "absolute", 0.01)
+    assert float(sc[0]) == float(np.float32(0.01))
+    assert np.array_equal(q, (W > np.float32(0.01)).astype(np.int8) - (W < -np.float32(0.01)).astype(np.int8))
