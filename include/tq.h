@@ -322,6 +322,49 @@ tq_status tq_ternary_backward_weight(const void* X, tq_dtype xdt, const void* dY
                                      int64_t M, int64_t N, int64_t K, float* dW, int accumulate,
                                      hipStream_t stream);
 
+/* ---- quantiser and format options -----------------------------------------
+ * Threshold ternarization (Foundry docs/quantization.md "Absmean Thresholding
+ * (BitNet b1.58)" and fq_quantize_ternary_threshold; BitRASP core_math.py
+ * ternarize_weight): q = +1 where w > h, -1 where w < -h, 0 otherwise, in
+ * fp32 with strict comparisons. */
+typedef enum tq_thresh {
+  TQ_THRESH_RELATIVE = 0, /* h = fp32(value * gamma), gamma the absmean scale of
+                             tq_pack_ternary (per tensor or row), scale = gamma;
+                             value 1 is Foundry's absmean rule, 0.55 BitRASP's,
+                             0.5 reproduces tq_pack_ternary                    */
+  TQ_THRESH_ABSOLUTE = 1  /* h = value (> 0), scale[0] = value, per tensor only */
+} tq_thresh;
+
+/* tq_pack_ternary with a threshold rule.  value must be finite, >= 0
+ * (relative) or > 0 (absolute), else TQ_ERR_UNSUPPORTED; TQ_THRESH_ABSOLUTE
+ * with TQ_PER_ROW is TQ_ERR_UNSUPPORTED and needs no workspace.  Other
+ * arguments and errors as tq_pack_ternary (ternary codes only). */
+tq_status tq_pack_ternary_threshold(const float* W, int64_t N, int64_t K, tq_gran g,
+                                    tq_thresh kind, float value, uint8_t* packed, float* scale,
+                                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Code formats of packed 2-bit weights, four values per byte LSB-first:
+ * this library's (Foundry "Ternary Format / Encoding") and Hetman-2b
+ * src/quantization.py section 3's Formats 0 and 1.  Each format's unused
+ * code reads as 0. */
+typedef enum tq_codes {
+  TQ_CODES_NATIVE = 0, /* -1 = 00, 0 = 01, +1 = 10 (11 unused)             */
+  TQ_CODES_F0 = 1,     /* 0 = 00, +1 = 01, -1 = 11 (10 reserved)            */
+  TQ_CODES_F1 = 2      /* 0 = 00, +1 = 01, -1 = 10 (11 reserved)            */
+} tq_codes;
+
+/* Re-encode nbytes packed bytes from src_fmt to dst_fmt, value by value.
+ * src == dst (in place) is allowed; other overlaps are not.
+ * Errors: nbytes < 0 is TQ_ERR_SHAPE; an unknown format TQ_ERR_UNSUPPORTED;
+ * NULL src or dst with nbytes > 0 TQ_ERR_NULL. */
+tq_status tq_convert_codes(const uint8_t* src, tq_codes src_fmt, uint8_t* dst, tq_codes dst_fmt,
+                           int64_t nbytes, hipStream_t stream);
+
+/* Values of numel packed codes (ceil(numel/4) bytes) as int8 -1/0/+1.
+ * Errors as tq_convert_codes. */
+tq_status tq_unpack_codes(const uint8_t* packed, tq_codes fmt, int64_t numel, int8_t* out,
+                          hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* tq_status_str(tq_status s);
 

@@ -16,7 +16,13 @@
 // Ternarization uses a comparison instead of the quotient: for normal fp32
 // w and gamma, rint(fp32(w/gamma)) is +1 exactly when w > gamma/2 (the next
 // fp32 above gamma/2 exceeds it by more than gamma * 2^-25, half the fp32
-// spacing just above 0.5), and -1 exactly when w < -gamma/2.
+// spacing just above 0.5), and -1 exactly when w < -gamma/2.  The same
+// kernels take other thresholds h = fp32(f * gamma) (Foundry "Absmean
+// Thresholding": f = 1; BitRASP ternarize_weight: f = 0.55) or a manual h
+// (Foundry fq_quantize_ternary_threshold, whose scale is h itself).
+//
+// The end of the file converts packed codes between this library's format
+// and Hetman-2b's Formats 0 and 1 (src/quantization.py, section 3).
 
 #include "tq_device.hpp"
 #include "tq_internal.hpp"
@@ -223,10 +229,10 @@ __global__ void k_gamma_exact_final(const uint32_t* __restrict__ flag,
 // 4-byte aligned); otherwise one byte per step.
 template <bool VEC>
 __global__ __launch_bounds__(kNT) void k_ternarize_pack(const float* __restrict__ W,
-                                                        int64_t nbytes, int binary,
+                                                        int64_t nbytes, int binary, float hf,
                                                         const float* __restrict__ scale,
                                                         uint8_t* __restrict__ packed) {
-  const float h = scale[0] * 0.5f;
+  const float h = scale[0] * hf;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kNT;
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * kNT + threadIdx.x;
   int64_t done = 0;
@@ -279,7 +285,7 @@ __global__ __launch_bounds__(kNT) void k_sign_pack(const float* __restrict__ W, 
 // byte (binary weights only).
 template <bool VEC, int BITS>
 __global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
-                                                   int64_t K, int binary, double thr,
+                                                   int64_t K, int binary, float hf, double thr,
                                                    uint8_t* __restrict__ packed,
                                                    float* __restrict__ scale) {
   __shared__ double sh[kNT / kWave];
@@ -323,7 +329,7 @@ __global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
   }
   const float g = g_sh;
   if (threadIdx.x == 0) scale[row] = g;
-  const float h = g * 0.5f;
+  const float h = g * hf;
   if (BITS == 2) {
     for (int64_t j = threadIdx.x; j < nb; j += kNT)
       out[j] = static_cast<uint8_t>(byte_of(load4<VEC>(w, j), h, binary));
@@ -332,6 +338,112 @@ __global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
       out[j] = static_cast<uint8_t>(sign_bits4(load4<VEC>(w, 2 * j)) |
                                     (sign_bits4(load4<VEC>(w, 2 * j + 1)) << 4));
   }
+}
+
+__global__ void k_set_scale(float* __restrict__ scale, float v) {
+  if (threadIdx.x == 0) scale[0] = v;
+}
+
+// ------------------------------------------------------------ code formats
+
+// Per 2-bit field of a word (bits at even positions): +1 and -1 masks of
+// this library's codes (fmt 0: -1 = 00, 0 = 01, +1 = 10), Format 0 (fmt 1:
+// +1 = 01, -1 = 11) and Format 1 (fmt 2: +1 = 01, -1 = 10); the reserved
+// code of each format is a zero.
+__device__ inline void code_masks(uint32_t w, int fmt, uint32_t& plus, uint32_t& minus) {
+  const uint32_t lo = w & 0x55555555u, hi = (w >> 1) & 0x55555555u;
+  if (fmt == 0) {
+    plus = hi & ~lo;
+    minus = ~hi & ~lo & 0x55555555u;
+  } else if (fmt == 1) {
+    plus = lo & ~hi;
+    minus = lo & hi;
+  } else {
+    plus = lo & ~hi;
+    minus = hi & ~lo;
+  }
+}
+
+__device__ inline uint32_t encode_masks(uint32_t plus, uint32_t minus, int fmt) {
+  if (fmt == 0) return (plus << 1) | (~plus & ~minus & 0x55555555u);
+  if (fmt == 1) return plus | minus | (minus << 1);
+  return plus | (minus << 1);
+}
+
+__device__ inline uint32_t convert_word(uint32_t w, int sf, int df) {
+  uint32_t p, m;
+  code_masks(w, sf, p, m);
+  return encode_masks(p, m, df);
+}
+
+// VEC: 16 bytes per step (both pointers 16-byte aligned), then single bytes.
+template <bool VEC>
+__global__ __launch_bounds__(kNT) void k_convert_codes(const uint8_t* src, int sf, uint8_t* dst,
+                                                       int df, int64_t nbytes) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kNT;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kNT + threadIdx.x;
+  int64_t done = 0;
+  if (VEC) {
+    const int64_t n16 = nbytes / 16;
+    for (int64_t i = tid; i < n16; i += stride) {
+      uint4 v = reinterpret_cast<const uint4*>(src)[i];
+      v.x = convert_word(v.x, sf, df);
+      v.y = convert_word(v.y, sf, df);
+      v.z = convert_word(v.z, sf, df);
+      v.w = convert_word(v.w, sf, df);
+      reinterpret_cast<uint4*>(dst)[i] = v;
+    }
+    done = n16 * 16;
+  }
+  for (int64_t j = done + tid; j < nbytes; j += stride)
+    dst[j] = static_cast<uint8_t>(convert_word(src[j], sf, df));
+}
+
+// one packed byte (its masks in the low 8 bits) -> four int8 values
+__device__ inline uint32_t values_of_byte(uint32_t p, uint32_t m) {
+  const uint32_t ps = (p & 1u) | ((p & 4u) << 6) | ((p & 16u) << 12) | ((p & 64u) << 18);
+  const uint32_t ms = (m & 1u) | ((m & 4u) << 6) | ((m & 16u) << 12) | ((m & 64u) << 18);
+  return ps | (ms * 0xFFu);  // bytes 0, 1 or 0xFF (-1)
+}
+
+// VEC: a 32-bit word (16 values) per step, 16-byte stores (packed 4-byte and
+// out 16-byte aligned); then single bytes, the last one partial.
+template <bool VEC>
+__global__ __launch_bounds__(kNT) void k_unpack_codes(const uint8_t* __restrict__ packed, int fmt,
+                                                      int64_t numel, int8_t* __restrict__ out) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kNT;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kNT + threadIdx.x;
+  int64_t done = 0;
+  if (VEC) {
+    const int64_t nw = numel / 16;
+    for (int64_t i = tid; i < nw; i += stride) {
+      uint32_t p, m;
+      code_masks(reinterpret_cast<const uint32_t*>(packed)[i], fmt, p, m);
+      uint4 o;
+      o.x = values_of_byte(p, m);
+      o.y = values_of_byte(p >> 8, m >> 8);
+      o.z = values_of_byte(p >> 16, m >> 16);
+      o.w = values_of_byte(p >> 24, m >> 24);
+      reinterpret_cast<uint4*>(out)[i] = o;
+    }
+    done = nw * 4;  // bytes
+  }
+  const int64_t nb = (numel + 3) / 4;
+  for (int64_t j = done + tid; j < nb; j += stride) {
+    uint32_t p, m;
+    code_masks(packed[j], fmt, p, m);
+    const uint32_t v = values_of_byte(p, m);
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (4 * j + t < numel) out[4 * j + t] = static_cast<int8_t>((v >> (8 * t)) & 0xFFu);
+  }
+}
+
+int64_t elementwise_grid(int64_t work) {
+  int64_t g = (work + kNT - 1) / kNT;
+  if (g < 1) g = 1;
+  if (g > 8192) g = 8192;
+  return g;
 }
 
 // Relative error bound of an fp64 sum of non-negative terms whose longest
@@ -347,7 +459,7 @@ size_t pack_tensor_ws_bytes() { return kWsTotal; }
 
 hipError_t launch_pack_tensor(const float* W, int64_t numel, tq_wmode mode,
                               uint8_t* packed, float* scale, void* ws,
-                              hipStream_t s, int bits) {
+                              hipStream_t s, int bits, float hf) {
   const int binary = mode == TQ_BINARY_SIGN ? 1 : 0;
   char* base = static_cast<char*>(ws);
   double* partials = reinterpret_cast<double*>(base + kWsPartials);
@@ -395,22 +507,61 @@ hipError_t launch_pack_tensor(const float* W, int64_t numel, tq_wmode mode,
   if (grid > 8192) grid = 8192;
   if (vec_pack)
     hipLaunchKernelGGL(k_ternarize_pack<true>, dim3(grid), dim3(kNT), 0, s, W, nbytes,
-                       binary, scale, packed);
+                       binary, hf, scale, packed);
   else
     hipLaunchKernelGGL(k_ternarize_pack<false>, dim3(grid), dim3(kNT), 0, s, W, nbytes,
-                       binary, scale, packed);
+                       binary, hf, scale, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_manual(const float* W, int64_t numel, float t, uint8_t* packed,
+                              float* scale, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_scale, dim3(1), dim3(kWave), 0, s, scale, t);
+  const int64_t nbytes = numel / 4;
+  const bool vec = (reinterpret_cast<uintptr_t>(W) & 15u) == 0u &&
+                   (reinterpret_cast<uintptr_t>(packed) & 3u) == 0u;
+  const int64_t grid = elementwise_grid(vec ? nbytes / 4 : nbytes);
+  if (vec)
+    hipLaunchKernelGGL(k_ternarize_pack<true>, dim3(grid), dim3(kNT), 0, s, W, nbytes, 0, 1.0f,
+                       scale, packed);
+  else
+    hipLaunchKernelGGL(k_ternarize_pack<false>, dim3(grid), dim3(kNT), 0, s, W, nbytes, 0, 1.0f,
+                       scale, packed);
+  return hipGetLastError();
+}
+
+hipError_t launch_convert_codes(const uint8_t* src, int sf, uint8_t* dst, int df, int64_t nbytes,
+                                hipStream_t s) {
+  const bool vec = ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) == 0u;
+  const int64_t grid = elementwise_grid(vec ? nbytes / 16 : nbytes);
+  if (vec)
+    hipLaunchKernelGGL(k_convert_codes<true>, dim3(grid), dim3(kNT), 0, s, src, sf, dst, df, nbytes);
+  else
+    hipLaunchKernelGGL(k_convert_codes<false>, dim3(grid), dim3(kNT), 0, s, src, sf, dst, df, nbytes);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpack_codes(const uint8_t* packed, int fmt, int64_t numel, int8_t* out,
+                               hipStream_t s) {
+  const bool vec = (reinterpret_cast<uintptr_t>(packed) & 3u) == 0u &&
+                   (reinterpret_cast<uintptr_t>(out) & 15u) == 0u;
+  const int64_t grid = elementwise_grid(vec ? numel / 16 : (numel + 3) / 4);
+  if (vec)
+    hipLaunchKernelGGL(k_unpack_codes<true>, dim3(grid), dim3(kNT), 0, s, packed, fmt, numel, out);
+  else
+    hipLaunchKernelGGL(k_unpack_codes<false>, dim3(grid), dim3(kNT), 0, s, packed, fmt, numel, out);
   return hipGetLastError();
 }
 
 hipError_t launch_pack_rows(const float* W, int64_t N, int64_t K, tq_wmode mode,
-                            uint8_t* packed, float* scale, hipStream_t s, int bits) {
+                            uint8_t* packed, float* scale, hipStream_t s, int bits, float hf) {
   const int binary = mode == TQ_BINARY_SIGN ? 1 : 0;
   const bool vec = (reinterpret_cast<uintptr_t>(W) & 15u) == 0u;
   const int64_t per_thread = (K / 4 + kNT - 1) / kNT;
   const double thr = sum_error_bound(4 * per_thread + 10);
 #define TQ_PACK_ROWS(V, B)                                                                  \
-  hipLaunchKernelGGL((k_pack_rows<V, B>), dim3(N), dim3(kNT), 0, s, W, K, binary, thr, packed, \
-                     scale)
+  hipLaunchKernelGGL((k_pack_rows<V, B>), dim3(N), dim3(kNT), 0, s, W, K, binary, hf, thr, \
+                     packed, scale)
   if (bits == 1) {
     if (vec) TQ_PACK_ROWS(true, 1);
     else TQ_PACK_ROWS(false, 1);

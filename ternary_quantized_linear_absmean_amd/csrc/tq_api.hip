@@ -365,6 +365,55 @@ tq_status tq_ternary_backward_weight(const void* X, tq_dtype xdt, const void* dY
   return hip_status(tq::launch_backward_weight(a, stream));
 }
 
+tq_status tq_pack_ternary_threshold(const float* W, int64_t N, int64_t K, tq_gran g,
+                                    tq_thresh kind, float value, uint8_t* packed, float* scale,
+                                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (N < 0 || K <= 0 || (K % 4) != 0) return TQ_ERR_SHAPE;
+  if (g != TQ_PER_TENSOR && g != TQ_PER_ROW) return TQ_ERR_UNSUPPORTED;
+  if (kind != TQ_THRESH_RELATIVE && kind != TQ_THRESH_ABSOLUTE) return TQ_ERR_UNSUPPORTED;
+  if (!isfinite(value) || value < 0.f) return TQ_ERR_UNSUPPORTED;
+  if (kind == TQ_THRESH_ABSOLUTE && (g != TQ_PER_TENSOR || !(value > 0.f)))
+    return TQ_ERR_UNSUPPORTED;
+  if (K >= kMaxNumelPack || N >= kMaxNumelPack / K) return TQ_ERR_UNSUPPORTED;
+  if (N == 0) return TQ_OK;
+  if (!W || !packed || !scale) return TQ_ERR_NULL;
+  if (!aligned(W, 4) || !aligned(scale, 4)) return TQ_ERR_ALIGN;
+  if (kind == TQ_THRESH_ABSOLUTE)
+    return hip_status(tq::launch_pack_manual(W, N * K, value, packed, scale, stream));
+  if (g == TQ_PER_TENSOR) {
+    const size_t need = tq::pack_tensor_ws_bytes();
+    if (!ws || ws_bytes < need) return TQ_ERR_WORKSPACE;
+    if (!aligned(ws, 8)) return TQ_ERR_ALIGN;
+    return hip_status(tq::launch_pack_tensor(W, N * K, TQ_TERNARY_ABSMEAN, packed, scale, ws,
+                                             stream, 2, value));
+  }
+  return hip_status(tq::launch_pack_rows(W, N, K, TQ_TERNARY_ABSMEAN, packed, scale, stream, 2,
+                                         value));
+}
+
+static bool valid_codes(tq_codes f) {
+  return f == TQ_CODES_NATIVE || f == TQ_CODES_F0 || f == TQ_CODES_F1;
+}
+
+tq_status tq_convert_codes(const uint8_t* src, tq_codes src_fmt, uint8_t* dst, tq_codes dst_fmt,
+                           int64_t nbytes, hipStream_t stream) {
+  if (nbytes < 0) return TQ_ERR_SHAPE;
+  if (!valid_codes(src_fmt) || !valid_codes(dst_fmt)) return TQ_ERR_UNSUPPORTED;
+  if (nbytes == 0) return TQ_OK;
+  if (!src || !dst) return TQ_ERR_NULL;
+  return hip_status(tq::launch_convert_codes(src, static_cast<int>(src_fmt), dst,
+                                             static_cast<int>(dst_fmt), nbytes, stream));
+}
+
+tq_status tq_unpack_codes(const uint8_t* packed, tq_codes fmt, int64_t numel, int8_t* out,
+                          hipStream_t stream) {
+  if (numel < 0) return TQ_ERR_SHAPE;
+  if (!valid_codes(fmt)) return TQ_ERR_UNSUPPORTED;
+  if (numel == 0) return TQ_OK;
+  if (!packed || !out) return TQ_ERR_NULL;
+  return hip_status(tq::launch_unpack_codes(packed, static_cast<int>(fmt), numel, out, stream));
+}
+
 const char* tq_status_str(tq_status s) {
   switch (s) {
     case TQ_OK: return "ok";

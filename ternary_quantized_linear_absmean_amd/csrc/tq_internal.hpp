@@ -10,12 +10,23 @@ namespace tq {
 
 // ---- absmean + ternarize + pack (k_pack.hip)
 size_t pack_tensor_ws_bytes();
-// bits: 2 (codes, four per byte) or 1 (signs of binary weights, eight per byte)
+// bits: 2 (codes, four per byte) or 1 (signs of binary weights, eight per
+// byte); hf: the ternarization threshold as a factor of gamma (0.5 is the
+// rounding rule)
 hipError_t launch_pack_tensor(const float* W, int64_t numel, tq_wmode mode,
                               uint8_t* packed, float* scale, void* ws,
-                              hipStream_t s, int bits = 2);
+                              hipStream_t s, int bits = 2, float hf = 0.5f);
 hipError_t launch_pack_rows(const float* W, int64_t N, int64_t K, tq_wmode mode,
-                            uint8_t* packed, float* scale, hipStream_t s, int bits = 2);
+                            uint8_t* packed, float* scale, hipStream_t s, int bits = 2,
+                            float hf = 0.5f);
+// manual threshold t: codes by |w| > t, scale[0] = t
+hipError_t launch_pack_manual(const float* W, int64_t numel, float t, uint8_t* packed,
+                              float* scale, hipStream_t s);
+// code formats: 0 this library's, 1 Format 0, 2 Format 1
+hipError_t launch_convert_codes(const uint8_t* src, int sf, uint8_t* dst, int df, int64_t nbytes,
+                                hipStream_t s);
+hipError_t launch_unpack_codes(const uint8_t* packed, int fmt, int64_t numel, int8_t* out,
+                               hipStream_t s);
 
 // ---- activations (k_quant.hip)
 struct ActParams {

@@ -30,11 +30,14 @@ STATUS_NAMES = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_DTYP
 DTYPES = {"f32": 0, "bf16": 1, "i32": 2}
 GRANULARITY = {"tensor": 0, "row": 1}
 MODES = {"ternary": 0, "binary": 1}
+THRESHOLDS = {"relative": 0, "absolute": 1}
+CODES = {"native": 0, "f0": 1, "f1": 2}
 EXPORTED = ["tq_packed_bytes", "tq_pack_workspace_bytes", "tq_pack_ternary",
             "tq_quant_act_int8", "tq_fwht512", "tq_ternary_gemv", "tq_ternary_gemm",
             "tq_quant_ternary_gemv", "tq_packed1_bytes", "tq_pack_binary1",
             "tq_binary1_gemv", "tq_swiglu_gemv", "tq_ffn_swiglu_decode",
-            "tq_ternary_backward_input", "tq_ternary_backward_weight", "tq_status_str",
+            "tq_ternary_backward_input", "tq_ternary_backward_weight",
+            "tq_pack_ternary_threshold", "tq_convert_codes", "tq_unpack_codes", "tq_status_str",
             "tq_last_hip_error", "tq_version"]
 
 _vp = ctypes.c_void_p
@@ -83,6 +86,13 @@ _lib.tq_ternary_backward_input.restype = _int
 _lib.tq_ternary_backward_weight.argtypes = [_vp, _int, _vp, _int, _i64, _i64, _i64, _vp, _int,
                                             _vp]
 _lib.tq_ternary_backward_weight.restype = _int
+_lib.tq_pack_ternary_threshold.argtypes = [_vp, _i64, _i64, _int, _int, ctypes.c_float, _vp, _vp,
+                                           _vp, ctypes.c_size_t, _vp]
+_lib.tq_pack_ternary_threshold.restype = _int
+_lib.tq_convert_codes.argtypes = [_vp, _int, _vp, _int, _i64, _vp]
+_lib.tq_convert_codes.restype = _int
+_lib.tq_unpack_codes.argtypes = [_vp, _int, _i64, _vp, _vp]
+_lib.tq_unpack_codes.restype = _int
 _lib.tq_status_str.argtypes = [_int]
 _lib.tq_status_str.restype = ctypes.c_char_p
 _lib.tq_last_hip_error.argtypes = []
@@ -420,6 +430,62 @@ def tq_ternary_backward_weight(X: torch.Tensor, dY: torch.Tensor, dW: torch.Tens
                                            1 if accumulate else 0, _stream(stream)),
            "tq_ternary_backward_weight")
     return dW
+
+
+def tq_pack_ternary_threshold(W: torch.Tensor, granularity: str = "tensor",
+                              kind: str = "relative", value: float = 0.55,
+                              packed: torch.Tensor | None = None,
+                              scale: torch.Tensor | None = None, stream=None):
+    """Threshold ternarization + 2-bit packing of W [N, K] fp32 -> (packed
+    uint8 [N, K/4], scale fp32 [1] or [N])."""
+    _dev(W, "W")
+    if W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError("W must be a 2-D float32 tensor")
+    N, K = W.shape
+    if packed is None:
+        packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
+    if scale is None:
+        scale = torch.empty((N if granularity == "row" else 1,), dtype=torch.float32,
+                            device=W.device)
+    nws = tq_pack_workspace_bytes(N, K, granularity)
+    ws = torch.empty((max(nws, 8),), dtype=torch.uint8, device=W.device)
+    _check(_lib.tq_pack_ternary_threshold(W.data_ptr(), N, K, GRANULARITY[granularity],
+                                          THRESHOLDS[kind], value, packed.data_ptr(),
+                                          scale.data_ptr(), ws.data_ptr(), ws.numel(),
+                                          _stream(stream)), "tq_pack_ternary_threshold")
+    return packed, scale
+
+
+def tq_convert_codes(src: torch.Tensor, src_fmt: str, dst_fmt: str,
+                     dst: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Re-encode packed codes (uint8, any shape) from one format to another."""
+    _dev(src, "src")
+    if src.dtype != torch.uint8:
+        raise ValueError("src must be uint8")
+    if dst is None:
+        dst = torch.empty_like(src)
+    _dev(dst, "dst")
+    if dst.dtype != torch.uint8 or dst.numel() != src.numel():
+        raise ValueError("dst must be uint8 with src's size")
+    _check(_lib.tq_convert_codes(src.data_ptr(), CODES[src_fmt], dst.data_ptr(), CODES[dst_fmt],
+                                 src.numel(), _stream(stream)), "tq_convert_codes")
+    return dst
+
+
+def tq_unpack_codes(packed: torch.Tensor, fmt: str, numel: int,
+                    out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Values -1/0/+1 (int8, numel of them) of packed codes in a format."""
+    _dev(packed, "packed")
+    if packed.dtype != torch.uint8 or packed.numel() * 4 < numel:
+        raise ValueError("packed must be uint8 with at least ceil(numel/4) bytes")
+    if out is None:
+        out = torch.empty((numel,), dtype=torch.int8, device=packed.device)
+    _dev(out, "out")
+    if out.dtype != torch.int8 or out.numel() != numel:
+        raise ValueError("out must be int8 with numel elements")
+    _check(_lib.tq_unpack_codes(packed.data_ptr(), CODES[fmt], numel, out.data_ptr(),
+                                _stream(stream)), "tq_unpack_codes")
+    return out
 
 
 def raw_library() -> ctypes.CDLL:

@@ -154,6 +154,33 @@ def test_backward_weight_validation():
     assert f(None, 0, None, 0, 4, 0, 8, None, 0, None) == OK   # empty dW
 
 
+def test_threshold_and_format_validation():
+    P = 0x10000
+    f = lib.tq_pack_ternary_threshold
+    # (W, N, K, g, kind, value, packed, scale, ws, ws_bytes, stream)
+    assert f(P, 4, 6, 0, 0, 0.55, P, P, P, 1 << 20, None) == SHAPE
+    assert f(P, 4, 64, 0, 2, 0.55, P, P, P, 1 << 20, None) == UNSUP       # unknown kind
+    assert f(P, 4, 64, 0, 0, -0.1, P, P, P, 1 << 20, None) == UNSUP       # negative factor
+    assert f(P, 4, 64, 0, 0, float("nan"), P, P, P, 1 << 20, None) == UNSUP
+    assert f(P, 4, 64, 1, 1, 0.05, P, P, None, 0, None) == UNSUP          # manual per row
+    assert f(P, 4, 64, 0, 1, 0.0, P, P, None, 0, None) == UNSUP           # manual t = 0
+    assert f(P, 4, 64, 0, 0, 0.55, P, P, None, 0, None) == WS             # tensor needs ws
+    assert f(None, 4, 64, 1, 0, 0.55, P, P, None, 0, None) == NULL
+    assert f(P + 2, 4, 64, 1, 0, 0.55, P, P, None, 0, None) == ALIGN
+    assert f(None, 0, 64, 1, 0, 0.55, None, None, None, 0, None) == OK
+    g = lib.tq_convert_codes
+    assert g(P, 0, P, 1, -1, None) == SHAPE
+    assert g(P, 3, P, 1, 16, None) == UNSUP
+    assert g(P, 0, P, 7, 16, None) == UNSUP
+    assert g(None, 0, P, 1, 16, None) == NULL
+    assert g(None, 0, None, 1, 0, None) == OK
+    u = lib.tq_unpack_codes
+    assert u(P, 0, -4, P, None) == SHAPE
+    assert u(P, 5, 4, P, None) == UNSUP
+    assert u(P, 1, 4, None, None) == NULL
+    assert u(None, 2, 0, None, None) == OK
+
+
 def test_swiglu_validation():
     P = 0x10000
     f = lib.tq_swiglu_gemv

@@ -1024,3 +1024,74 @@ def test_backward_weight_prefill_workload_sampled(xdt):
     rows = np.sort(np.random.default_rng(75).choice(dY.shape[1], 48, replace=False))
     ref, bound = _wgt_ref_and_bound(X, dY, xdt == "f32", rows)
     _assert_bwd_close(dw[rows], ref, bound, f"prefill dW X {xdt}")
+
+
+# ------------------------------------------------- thresholds, code formats
+
+THRESH_CASES = [("tensor", "relative", 0.55), ("row", "relative", 0.55), ("tensor", "relative", 1.0),
+                ("row", "relative", 1.0), ("row", "relative", 0.0), ("tensor", "absolute", 0.02)]
+
+
+@pytest.mark.parametrize("gran,kind,value", THRESH_CASES)
+def test_pack_threshold(gran, kind, value):
+    say(f"pack_threshold {gran} {kind} {value}")
+    for (N, K) in ((64, 256), (37, 1028), (3, 4)):
+        W = ti.normal_weights(7600 + N + K, N, K)
+        q, sc = oracle.ternarize_threshold(W, gran, kind, value)
+        p, s = tq.tq_pack_ternary_threshold(dev(W), gran, kind, value)
+        assert np.array_equal(host(p), oracle.pack_codes(q)), (N, K)
+        assert np.array_equal(f32_bits(host(s)), f32_bits(sc)), (N, K)
+
+
+def test_pack_threshold_half_factor_matches_rounding_and_prefill():
+    W = ti.normal_weights(7700, 96, 512)
+    for gran in ("tensor", "row"):
+        p0, s0 = tq.tq_pack_ternary(dev(W), gran)
+        p1, s1 = tq.tq_pack_ternary_threshold(dev(W), gran, "relative", 0.5)
+        assert torch.equal(p0, p1) and torch.equal(s0, s1)
+    # the prefill matrix with BitRASP's factor, per tensor
+    Wp, _, _ = ref_pack("prefill")
+    q, sc = oracle.ternarize_threshold(Wp, "tensor", "relative", 0.55)
+    p, s = tq.tq_pack_ternary_threshold(dev(Wp), "tensor", "relative", 0.55)
+    assert np.array_equal(host(p), oracle.pack_codes(q))
+    assert np.array_equal(f32_bits(host(s)), f32_bits(sc))
+
+
+@pytest.mark.parametrize("src", ["native", "f0", "f1"])
+@pytest.mark.parametrize("dst", ["native", "f0", "f1"])
+def test_convert_codes(src, dst):
+    rng = np.random.default_rng(77)
+    for n in (256, 4096 + 13, 1 << 20):
+        b = rng.integers(0, 256, n, dtype=np.uint8)
+        b[:256] = np.arange(256, dtype=np.uint8)                  # every byte once
+        want = oracle.convert_codes(b.reshape(1, -1), src, dst).reshape(-1)
+        got = host(tq.tq_convert_codes(dev(b), src, dst))
+        assert np.array_equal(got, want), n
+    # in place, and from an address off 16-byte alignment
+    big = torch.zeros(4097, dtype=torch.uint8, device=DEV)
+    big[1:] = dev(b[:4096])
+    view = big[1:]
+    tq.tq_convert_codes(view, src, dst, dst=view)
+    assert np.array_equal(host(view), oracle.convert_codes(b[:4096].reshape(1, -1), src, dst)[0])
+
+
+@pytest.mark.parametrize("fmt", ["native", "f0", "f1"])
+def test_unpack_codes(fmt):
+    rng = np.random.default_rng(78)
+    for numel in (4, 13, 64, 1000, 4096 * 3 + 7):
+        nb = (numel + 3) // 4
+        b = rng.integers(0, 256, nb, dtype=np.uint8)
+        want = oracle.decode_format(b.reshape(1, -1), fmt).reshape(-1)[:numel]
+        got = host(tq.tq_unpack_codes(dev(b), fmt, numel))
+        assert np.array_equal(got, want), numel
+
+
+def test_format_roundtrip_through_gemv():
+    # a weight packed here, converted to Format 0 and back, multiplies the same
+    W = ti.normal_weights(7800, 64, 256)
+    p, s = tq.tq_pack_ternary(dev(W), "row")
+    f0 = tq.tq_convert_codes(p, "native", "f0")
+    back = tq.tq_convert_codes(f0, "f0", "native")
+    assert torch.equal(back, p)
+    vals = host(tq.tq_unpack_codes(f0, "f0", 64 * 256)).reshape(64, 256)
+    assert np.array_equal(vals, oracle.unpack_codes(host(p), 256))
