@@ -17,8 +17,10 @@ time (GB/s).  ``roofline`` describes the GEMV kernel: its algorithmic bytes
 per launch over its average launch time, against 8 TB/s.  ``cpu_baseline``
 times the CPU oracle on a bounded sample of the same workload.  ``extra``
 carries the prefill GEMM (int8 MFMA TOPS), the BitLinear prologue, the FFN
-decode shapes, the pack kernel and the steady-state GEMV rate (stacked
-projections in one launch).
+decode shapes, the pack kernels (absmean, threshold, code-format
+conversion), the steady-state GEMV rate (stacked projections in one launch),
+1-bit binary weights, the SwiGLU decode FFN and the backward of the prefill
+layer.
 """
 from __future__ import annotations
 
@@ -294,6 +296,22 @@ def extra_prefill(torch, ti, tq, dev, want):
         t = timed_graph(torch, g, 10)
         out["pack_tensor"] = {"shape": [N, K], "us": round(t * 1e6, 2),
                               "GBs": round((4 * N * K + N * K // 4) / t / 1e9, 1)}
+        # BitRASP's 0.55 threshold per row, and conversion of the packed
+        # weight to Hetman-2b's Format 0 (11 MB read + 11 MB written)
+        pr = torch.empty_like(packed)
+        sr = torch.empty((N,), dtype=torch.float32, device=dev)
+        g = capture(torch, lambda: tq.tq_pack_ternary_threshold(W, "row", "relative", 0.55,
+                                                                packed=pr, scale=sr))
+        t = timed_graph(torch, g, 10)
+        out["pack_threshold_row_0.55"] = {"shape": [N, K], "us": round(t * 1e6, 2),
+                                          "GBs": round((4 * N * K + N * K // 4) / t / 1e9, 1)}
+        f0 = torch.empty_like(packed)
+        g = capture(torch, lambda: [tq.tq_convert_codes(packed, "native", "f0", dst=f0)
+                                    for _ in range(reps)])
+        timed_graph(torch, g, 2)
+        t = timed_graph(torch, g, 10) / reps
+        out["convert_codes_to_f0"] = {"bytes": 2 * packed.numel(), "us": round(t * 1e6, 2),
+                                      "GBs": round(2 * packed.numel() / t / 1e9, 1)}
     return out
 
 
