@@ -49,7 +49,8 @@ in the design notes):
   every order approximates.
 * Weights are ternarized by round-half-even of the fp32 quotient w/gamma,
   clamped to [-1, 1] (Foundry "How It Works", Hetman-2b section 2).  The
-  "Absmean Thresholding" block of the Foundry page (|w| > gamma) is not used.
+  "Absmean Thresholding" block of the Foundry page (|w| > gamma) is a
+  separate option, ``ternarize_threshold``.
 * Binary mode: +1 where w >= 0, else -1, with the same per-row absmean scale.
 * Activations: per-token eta = max|x| floored at 1e-6, optional clamp to
   [eta_min, eta_max]; s = fp32(127/eta); q = clamp(rint(fp32(x*s)), -127, 127);
