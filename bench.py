@@ -114,6 +114,17 @@ def timed_graph(torch, graph, reps):
     return s.elapsed_time(e) / 1e3 / reps
 
 
+def warm(torch, graph, seconds=0.05):
+    """Replay `graph` for about `seconds` untimed: the GPU leaves its idle
+    clocks only after some milliseconds of sustained matrix-core work, and a
+    compute-bound kernel timed straight after latency-bound work reads 10-15%
+    slow otherwise."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        graph.replay()
+        torch.cuda.synchronize()
+
+
 def capture(torch, fn):
     g = torch.cuda.CUDAGraph()
     stream = torch.cuda.Stream()
@@ -273,7 +284,7 @@ def extra_prefill(torch, ti, tq, dev, want):
     if want("prefill"):
         g = capture(torch, lambda: [tq.tq_ternary_gemm(q, sx, packed, scale, N, K, "tensor",
                                                        "bf16", Y=Y) for _ in range(reps)])
-        timed_graph(torch, g, 2)
+        warm(torch, g)
         t = timed_graph(torch, g, 5) / reps
         tops = 2.0 * M * N * K / t / 1e12
         out["prefill_gemm"] = {"shape": [M, N, K], "out": "bf16", "us": round(t * 1e6, 2),
@@ -333,6 +344,7 @@ def extra_bitlinear(torch, ti, tq, dev):
                                  "GBs": round(quant_bytes(512, 4096, 2) / t / 1e9, 1)}
     g = capture(torch, lambda: [tq.tq_ternary_gemm(qb, sxb, pb, sb, 4096, 4096, "row", "f32",
                                                    Y=Yb) for _ in range(reps)])
+    warm(torch, g)
     t = timed_graph(torch, g, 5) / reps
     tops = 2.0 * 512 * 4096 * 4096 / t / 1e12
     out["bitlinear_gemm"] = {"shape": [512, 4096, 4096], "us": round(t * 1e6, 2),
@@ -479,7 +491,7 @@ def extra_backward(torch, ti, tq, dev):
 
     def timed(fn):
         g = capture(torch, lambda: [fn() for _ in range(R)])
-        timed_graph(torch, g, 1)
+        warm(torch, g)
         return timed_graph(torch, g, 3) / R
 
     dX = torch.empty((M, K), dtype=torch.float32, device=dev)
@@ -530,7 +542,7 @@ def extra_context(torch, dev):
         A = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
         B = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev)
         g = capture(torch, lambda: [torch._int_mm(A, B.t()) for _ in range(8)])
-        timed_graph(torch, g, 2)
+        warm(torch, g)
         t = timed_graph(torch, g, 5) / 8
         out["vendor_int8_gemm_prefill"] = {"api": "torch._int_mm (int8 x int8 -> int32)",
                                            "shape": [M, N, K], "us": round(t * 1e6, 2),
