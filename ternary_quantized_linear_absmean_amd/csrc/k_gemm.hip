@@ -237,6 +237,10 @@ __global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm(
 //     the address path is limited by lines per instruction, not bytes;
 //   - packed weights: one 32-bit word (16 codes) per lane, decoded to signed
 //     int8 once per workgroup.
+// Small grids (fewer than 384 tiles of 128 x 128) use 128 x 64 tiles with
+// two groups of four waves: a stage holds 128 of K, each group contracts one
+// 64-deep half, and the two int32 sums meet in LDS at the end, so a tile gets
+// eight waves instead of four.
 // Global loads are raw buffer loads whose per-lane offset is fixed for the
 // K loop and whose K position rides in the scalar offset (no address
 // arithmetic in the loop; reads past the end return zero).  Loads run two
@@ -255,30 +259,41 @@ __device__ inline int swz(int row, int chunk) {
   return row * kBK + 16 * (chunk ^ (((row >> 1) ^ (row >> 4)) & 3));
 }
 
-// LDS bytes of one BM x BN tile: double-buffered activation and weight tiles.
-template <int BM, int BN>
-constexpr int fast_lds_bytes() { return 2 * (BM + BN) * kBK; }
+// LDS bytes of one BM x BN tile: double-buffered activation and weight tiles
+// of KG 64-deep sub-tiles each.
+template <int BM, int BN, int KG = 1>
+constexpr int fast_lds_bytes() { return 2 * KG * (BM + BN) * kBK; }
 
 // One BM x BN output tile (tile coordinates tm, tn in units of BM, BN) by a
-// workgroup of WM x WN waves, staging through `lds`.
-template <int BM, int BN, int WM, int WN, int YT>
+// workgroup of KG groups of WM x WN waves, staging through `lds`.  A stage
+// covers KG x 64 of K; group g contracts the stage's 64-deep sub-tile g into
+// its own accumulators, and the groups' sums meet in LDS at the end (exact
+// int32 additions).  KG = 2 gives small grids twice the waves per tile.
+template <int BM, int BN, int WM, int WN, int YT, int KG = 1>
 __device__ __forceinline__ void gemm_fast_tile(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
     int64_t N, int64_t K, void* __restrict__ Y, int64_t tm, int64_t tn, uint8_t* lds) {
-  constexpr int NT = WM * WN * kWave;
+  constexpr int NW = WM * WN;                 // waves per group
+  constexpr int NT = NW * KG * kWave;
   constexpr int TM = BM / WM, TN = BN / WN;
   constexpr int FM = TM / 32, FN = TN / 32;
-  constexpr int CA = BM * (kBK / 16) / NT;  // 16-byte activation chunks per thread
-  constexpr int CB = BN * (kBK / 16) / NT;  // packed words per thread
+  constexpr int CPR = KG * (kBK / 16);       // 16-byte chunks per row and stage
+  constexpr int CA = BM * CPR / NT;          // 16-byte activation chunks per thread
+  constexpr int CB = BN * CPR / NT;          // packed words per thread
+  constexpr int ASZ = BM * kBK, BSZ = BN * kBK;  // bytes of one 64-deep sub-tile
   static_assert(CA >= 1 && CB >= 1 && FM >= 1 && FN >= 1, "tile shape");
-  uint8_t* const As = lds;                  // [2][BM * kBK]
-  uint8_t* const Bs = lds + 2 * BM * kBK;   // [2][BN * kBK]
+  static_assert(KG == 1 || NW * FM * FN * 16 * kWave * 4 <= 2 * KG * (ASZ + BSZ),
+                "group sums must fit in the staging LDS");
+  constexpr int SA = KG * ASZ, SB = KG * BSZ;  // bytes of one stage
+  uint8_t* const As = lds;                     // [2][KG][BM * kBK]
+  uint8_t* const Bs = lds + 2 * SA;            // [2][KG][BN * kBK]
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int wm = wave / WN, wn = wave % WN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform in the wave
+  const int grp = wave / NW, wl = wave % NW;
+  const int wm = wl / WN, wn = wl % WN;
   const int64_t m0 = tm * BM, n0 = tn * BN;
   const int64_t rowbytes = K >> 2;
   const int fr = lane & 31, kg = lane >> 5;
@@ -294,26 +309,27 @@ __device__ __forceinline__ void gemm_fast_tile(
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
     const int c = tid + NT * i;
-    const int r = c / (kBK / 16), ch = c % (kBK / 16);
+    const int r = c / CPR, ch = c % CPR;
     aoff[i] = static_cast<uint32_t>((m0 + r) * K + 16 * ch);
-    ast[i] = swz(r, ch);
+    ast[i] = (ch / 4) * ASZ + swz(r, ch % 4);
   }
   uint32_t boff[CB];
   int bst[CB];
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int c = tid + NT * i;
-    const int r = c / (kBK / 16), wi = c % (kBK / 16);
+    const int r = c / CPR, wi = c % CPR;
     boff[i] = static_cast<uint32_t>((n0 + r) * rowbytes + 4 * wi);
-    bst[i] = swz(r, wi);
+    bst[i] = (wi / 4) * BSZ + swz(r, wi % 4);
   }
+  // this group's fragments: sub-tile grp of each stage
   int ard[FM][kKS], brd[FN][kKS];
 #pragma unroll
   for (int ks = 0; ks < kKS; ++ks) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) ard[i][ks] = swz(wm * TM + 32 * i + fr, 2 * ks + kg);
+    for (int i = 0; i < FM; ++i) ard[i][ks] = grp * ASZ + swz(wm * TM + 32 * i + fr, 2 * ks + kg);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) brd[j][ks] = swz(wn * TN + 32 * j + fr, 2 * ks + kg);
+    for (int j = 0; j < FN; ++j) brd[j][ks] = grp * BSZ + swz(wn * TN + 32 * j + fr, 2 * ks + kg);
   }
 
   typedef v4i ARegs[CA];
@@ -321,7 +337,7 @@ __device__ __forceinline__ void gemm_fast_tile(
   ARegs ra0, ra1, ra2;
   BRegs rb0, rb1, rb2;
   auto load_stage = [&](int64_t kt, ARegs& a, BRegs& b) {
-    const int soa = static_cast<int>(kt * kBK), sob = static_cast<int>(kt * (kBK / 4));
+    const int soa = static_cast<int>(kt * kBK * KG), sob = static_cast<int>(kt * (kBK / 4) * KG);
 #pragma unroll
     for (int i = 0; i < CA; ++i)
       a[i] = __builtin_bit_cast(v4i,
@@ -331,10 +347,10 @@ __device__ __forceinline__ void gemm_fast_tile(
   };
   auto store_stage = [&](int buf, ARegs& a, BRegs& b) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i) *reinterpret_cast<v4i*>(&As[(buf) * (BM * kBK) + ast[i]]) = a[i];
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<v4i*>(&As[(buf) * SA + ast[i]]) = a[i];
 #pragma unroll
     for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<v4i*>(&Bs[(buf) * (BN * kBK) + bst[i]]) = decode_signed_natural(b[i]);
+      *reinterpret_cast<v4i*>(&Bs[(buf) * SB + bst[i]]) = decode_signed_natural(b[i]);
   };
 
   v16i acc[FM][FN];
@@ -345,7 +361,7 @@ __device__ __forceinline__ void gemm_fast_tile(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
-  const int64_t nk = K / kBK;
+  const int64_t nk = K / (kBK * KG);
   // one stage: start the loads of stage kt+2, contract stage kt from LDS,
   // publish stage kt+1 (loaded during the previous stage).  In the main loop
   // (GUARD false) every stage issues its loads and stores unconditionally:
@@ -360,18 +376,18 @@ __device__ __forceinline__ void gemm_fast_tile(
     if (!GUARD || kt + 2 < nk) load_stage(kt + 2, a_far, b_far);
     v4i ac[FM], an[FM], bc[FN], bn[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) ac[i] = *reinterpret_cast<const v4i*>(&As[(buf) * (BM * kBK) + ard[i][0]]);
+    for (int i = 0; i < FM; ++i) ac[i] = *reinterpret_cast<const v4i*>(&As[(buf) * SA + ard[i][0]]);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bc[j] = *reinterpret_cast<const v4i*>(&Bs[(buf) * (BN * kBK) + brd[j][0]]);
+    for (int j = 0; j < FN; ++j) bc[j] = *reinterpret_cast<const v4i*>(&Bs[(buf) * SB + brd[j][0]]);
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       if (ks + 1 < kKS) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
-          an[i] = *reinterpret_cast<const v4i*>(&As[(buf) * (BM * kBK) + ard[i][ks + 1]]);
+          an[i] = *reinterpret_cast<const v4i*>(&As[(buf) * SA + ard[i][ks + 1]]);
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          bn[j] = *reinterpret_cast<const v4i*>(&Bs[(buf) * (BN * kBK) + brd[j][ks + 1]]);
+          bn[j] = *reinterpret_cast<const v4i*>(&Bs[(buf) * SB + brd[j][ks + 1]]);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -407,6 +423,35 @@ __device__ __forceinline__ void gemm_fast_tile(
   if (kt < nk) stage(kt, ra1, rb1, ra2, rb2, Guarded{});
   if (kt + 1 < nk) stage(kt + 1, ra2, rb2, ra0, rb0, Guarded{});
 
+  if constexpr (KG > 1) {
+    // groups 1.. leave their sums in LDS (the staging tiles are free after
+    // the last stage's barrier); group 0 adds them in group order
+    int* const red = reinterpret_cast<int*>(lds);
+    const int slot = (wl * FM * FN) * 16 * kWave + lane;
+    if (grp > 0) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            red[(grp - 1) * NW * FM * FN * 16 * kWave + slot + ((i * FN + j) * 16 + v) * kWave] =
+                acc[i][j][v];
+    }
+    __syncthreads();
+    if (grp > 0) return;
+#pragma unroll
+    for (int g = 1; g < KG; ++g)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            acc[i][j][v] +=
+                red[(g - 1) * NW * FM * FN * 16 * kWave + slot + ((i * FN + j) * 16 + v) * kWave];
+  }
+
   // D layout of the 32x32 MFMA: lane l holds column l%32 and rows
   // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
 #pragma unroll
@@ -436,23 +481,23 @@ __device__ __forceinline__ void gemm_fast_tile(
   }
 }
 
-template <int BM, int BN, int WM, int WN, int YT>
-__global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm_fast(
+template <int BM, int BN, int WM, int WN, int YT, int KG>
+__global__ __launch_bounds__(WM* WN* KG* kWave, 2) void k_gemm_fast(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
     int64_t N, int64_t K, void* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[fast_lds_bytes<BM, BN>()];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[fast_lds_bytes<BM, BN, KG>()];
   const int64_t tiles_m = (M + BM - 1) / BM;
-  gemm_fast_tile<BM, BN, WM, WN, YT>(q, sx, M, packed, scale, per_row, N, K, Y,
-                                     blockIdx.x % tiles_m, blockIdx.x / tiles_m, lds);
+  gemm_fast_tile<BM, BN, WM, WN, YT, KG>(q, sx, M, packed, scale, per_row, N, K, Y,
+                                         blockIdx.x % tiles_m, blockIdx.x / tiles_m, lds);
 }
 
-template <int BM, int BN, int WM, int WN>
+template <int BM, int BN, int WM, int WN, int KG = 1>
 hipError_t gemm_fast_launch(const GemmArgs& a, hipStream_t s) {
   const int64_t grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
-  constexpr int NT = WM * WN * kWave;
-#define TQ_GEMM_FAST(YTV)                                                                  \
-  hipLaunchKernelGGL((k_gemm_fast<BM, BN, WM, WN, YTV>), dim3(grid), dim3(NT), 0, s, a.q, \
+  constexpr int NT = WM * WN * KG * kWave;
+#define TQ_GEMM_FAST(YTV)                                                                      \
+  hipLaunchKernelGGL((k_gemm_fast<BM, BN, WM, WN, YTV, KG>), dim3(grid), dim3(NT), 0, s, a.q, \
                      a.sx, a.M, a.packed, a.scale, a.per_row, a.N, a.K, a.Y)
   if (a.ydt == TQ_F32) TQ_GEMM_FAST(TQ_F32);
   else if (a.ydt == TQ_BF16) TQ_GEMM_FAST(TQ_BF16);
@@ -466,6 +511,8 @@ hipError_t gemm_fast_dispatch(const GemmArgs& a, hipStream_t s) {
   constexpr int64_t kEnough = 384;
   if (tiles(256, 128) >= kEnough) return gemm_fast_launch<256, 128, 4, 2>(a, s);
   if (tiles(128, 128) >= kEnough) return gemm_fast_launch<128, 128, 2, 2>(a, s);
+  // small grids: two wave groups split each 128-deep stage (needs K % 128)
+  if (a.K % 128 == 0) return gemm_fast_launch<128, 64, 4, 1, 2>(a, s);
   return gemm_fast_launch<128, 64, 4, 1>(a, s);
 }
 

@@ -401,7 +401,7 @@ def test_gemv_unaligned_buffers():
 
 @pytest.mark.parametrize("M", [17, 33, 100, 257])
 @pytest.mark.parametrize("N,K", [(1, 4), (3, 60), (64, 64), (257, 68), (130, 260),
-                                 (200, 2560)])
+                                 (200, 2560), (130, 384), (96, 640)])
 def test_gemm_awkward(M, N, K):
     q = ti.random_int8(M * 5 + N + K, M, K)
     w = ti.random_ternary(N + 7 * K, N, K)
