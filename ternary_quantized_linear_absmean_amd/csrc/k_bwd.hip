@@ -417,21 +417,26 @@ int64_t grid_for(int64_t n) {
 // operand, with one step threads 0..255 stage dY and 256..511 stage X.
 // Either way all threads issue the same loads.
 
-constexpr int kGN = 128, kGK = 128;  // dW tile
+constexpr int kGK = 128;             // dW columns per tile
 constexpr int kGPlane = 128 * 64;    // one plane: 128 rows of 32 bf16
 constexpr int kPN = 4, kPK = 8;      // tiles of a patch (one per CU of an XCD)
 
 __host__ __device__ constexpr int planes_of(int dt) { return dt == 0 ? 3 : 1; }
-#ifndef TQ_WGT_KS_BF16
-#define TQ_WGT_KS_BF16 4
+#ifndef TQ_WGT_WIDE
+#define TQ_WGT_WIDE 1
 #endif
+// dW rows per tile: 256 with two bf16 operands (64 x 64 per wave, half the
+// LDS fragment reads per MFMA of a 32 x 64 wave tile), else 128
+__host__ __device__ constexpr int wgt_gn(int da, int db) {
+  return (TQ_WGT_WIDE && da == 1 && db == 1) ? 256 : 128;
+}
 // MFMA steps per LDS stage: as many as 160 KiB of double-buffered LDS allow
 __host__ __device__ constexpr int wgt_ks(int da, int db) {
-  return (da == 0 && db == 0) ? 1 : (da == 1 && db == 1) ? TQ_WGT_KS_BF16 : 2;
+  return (da == 0 && db == 0) ? 1 : (da == 1 && db == 1) ? (wgt_gn(da, db) == 256 ? 2 : 4) : 2;
 }
 template <int DA, int DB>
 constexpr int wgt_lds_bytes() {
-  return 2 * wgt_ks(DA, DB) * (planes_of(DA) + planes_of(DB)) * kGPlane;
+  return 2 * wgt_ks(DA, DB) * (planes_of(DA) * wgt_gn(DA, DB) * 64 + planes_of(DB) * kGPlane);
 }
 
 // DA: dtype of dY, DB: dtype of X (0 = fp32, 1 = bf16).  ACC: add into dW.
@@ -441,8 +446,12 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
     float* __restrict__ dW) {
   constexpr int PA = planes_of(DA), PB = planes_of(DB);
   constexpr int KS = wgt_ks(DA, DB);
+  constexpr int GN = wgt_gn(DA, DB);           // dW rows (dY columns) per tile
+  constexpr int TW = GN / 4;                   // rows per wave
+  constexpr int FA = TW / 16;                  // A fragments per wave
+  constexpr int kAPlane = GN * 64;             // one A plane: GN rows of 32 bf16
   constexpr int kGM = 32 * KS;                 // tokens per stage
-  constexpr int kStep = (PA + PB) * kGPlane;   // LDS bytes of one MFMA step
+  constexpr int kStep = PA * kAPlane + PB * kGPlane;  // LDS bytes of one MFMA step
   constexpr int kStage = KS * kStep;
   constexpr bool kRoles = KS == 1;             // half the threads per operand
   constexpr int ESA = DA == 0 ? 4 : 2, ESB = DB == 0 ? 4 : 2;
@@ -452,7 +461,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform in the wave
   const int wn = wave / 2, wk = wave % 2;
-  const int64_t tiles_n = (N + kGN - 1) / kGN;
+  const int64_t tiles_n = (N + GN - 1) / GN;
   const int64_t tiles_k = (K + kGK - 1) / kGK;
   // ids congruent mod 8 run on one XCD: its 32 workgroups in flight take a
   // 4 x 8 patch of tiles, which share 4 dY and 8 X column blocks in its L2
@@ -464,12 +473,14 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
   const int64_t tn = (patch % pcols) * kPN + q % kPN;
   const int64_t tk = (patch / pcols) * kPK + q / kPN;
   if (tn >= tiles_n || tk >= tiles_k) return;  // padding ids (whole workgroup)
-  const int64_t n0 = tn * kGN, k0 = tk * kGK;
+  const int64_t n0 = tn * GN, k0 = tk * kGK;
 
   // staging units of this thread: columns 2cp, 2cp+1, token rows 8o..8o+7 of
-  // the stage for o = uo + 8u (u < U); with roles, waves 0..3 stage dY and
-  // 4..7 stage X
+  // the stage for o = uo + 8u (u < U); an A tile of 256 columns takes a
+  // second unit for columns 128 + 2cp, 128 + 2cp + 1; with roles, waves
+  // 0..3 stage dY and 4..7 stage X
   constexpr int U = kRoles ? 1 : KS / 2;
+  constexpr int PRA = GN / 128;                // A column blocks of 128
   const bool role_a = !kRoles || wave < 4;
   const int ut = kRoles ? (tid & 255) : tid;
   const int cp = ut & 63, uo = ut >> 6;
@@ -488,7 +499,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
 
   // a unit: 8 rows of two fp32 (two words) or two bf16 (one word) columns
   struct Regs {
-    uint32_t a[U][8][ESA / 2];
+    uint32_t a[U * PRA][8][ESA / 2];
     uint32_t b[kRoles ? 1 : U][8][ESB / 2];
   };
   auto load_unit = [&](__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t str, int so, auto es,
@@ -518,15 +529,17 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
       const uint32_t sa = static_cast<uint32_t>(N * ESA), sb = static_cast<uint32_t>(K * ESB);
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        load_unit(ra, aoff + 64 * u * sa, sa, static_cast<int>(st * kGM * N * ESA), EA{},
-                  r.a[u]);
+#pragma unroll
+        for (int pb = 0; pb < PRA; ++pb)
+          load_unit(ra, aoff + 64 * u * sa + 128 * pb * ESA, sa,
+                    static_cast<int>(st * kGM * N * ESA), EA{}, r.a[u * PRA + pb]);
         load_unit(rb, boff + 64 * u * sb, sb, static_cast<int>(st * kGM * K * ESB), EB{},
                   r.b[u]);
       }
     }
   };
   // one unit -> its operand's planes (plane 0 at `base`)
-  auto put_unit = [&](uint8_t* base, auto es, auto& v) {
+  auto put_unit = [&](uint8_t* base, int plane, auto es, auto& v) {
     constexpr int E = decltype(es)::value;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
@@ -542,8 +555,8 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
         split3(x, h, m, l);
         const int o = c ? wo1 : wo0;
         *reinterpret_cast<v4i*>(base + o) = h;
-        *reinterpret_cast<v4i*>(base + kGPlane + o) = m;
-        *reinterpret_cast<v4i*>(base + 2 * kGPlane + o) = l;
+        *reinterpret_cast<v4i*>(base + plane + o) = m;
+        *reinterpret_cast<v4i*>(base + 2 * plane + o) = l;
       }
     } else {
       // bf16 pairs (column 2cp in the low half): each column's 8 halves
@@ -560,26 +573,28 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
   auto store_stage = [&](int buf, Regs& r) {
     uint8_t* st = lds + buf * kStage;
     if constexpr (kRoles) {
-      put_unit(st + (role_a ? 0 : PA * kGPlane), EA{}, r.a[0]);
+      put_unit(st + (role_a ? 0 : PA * kAPlane), role_a ? kAPlane : kGPlane, EA{}, r.a[0]);
     } else {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        put_unit(st + 2 * u * kStep, EA{}, r.a[u]);
-        put_unit(st + 2 * u * kStep + PA * kGPlane, EB{}, r.b[u]);
+#pragma unroll
+        for (int pb = 0; pb < PRA; ++pb)
+          put_unit(st + 2 * u * kStep + pb * 128 * 64, kAPlane, EA{}, r.a[u * PRA + pb]);
+        put_unit(st + 2 * u * kStep + PA * kAPlane, kGPlane, EB{}, r.b[u]);
       }
     }
   };
 
   const int fr = lane & 15, fg = lane >> 4;
-  int ard[2], brd[4];
+  int ard[FA], brd[4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) ard[a] = swz64(wn * 32 + 16 * a + fr, fg);
+  for (int a = 0; a < FA; ++a) ard[a] = swz64(wn * TW + 16 * a + fr, fg);
 #pragma unroll
-  for (int b = 0; b < 4; ++b) brd[b] = PA * kGPlane + swz64(wk * 64 + 16 * b + fr, fg);
+  for (int b = 0; b < 4; ++b) brd[b] = PA * kAPlane + swz64(wk * 64 + 16 * b + fr, fg);
 
-  f4 acc[2][4];
+  f4 acc[FA][4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int a = 0; a < FA; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
@@ -592,12 +607,12 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint8_t* st = lds + buf * kStage + ks * kStep;
-      bf16x8 av[PA][2], bv[PB][4];
+      bf16x8 av[PA][FA], bv[PB][4];
 #pragma unroll
       for (int p = 0; p < PA; ++p)
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
-          av[p][a] = *reinterpret_cast<const bf16x8*>(st + p * kGPlane + ard[a]);
+        for (int a = 0; a < FA; ++a)
+          av[p][a] = *reinterpret_cast<const bf16x8*>(st + p * kAPlane + ard[a]);
 #pragma unroll
       for (int p = 0; p < PB; ++p)
 #pragma unroll
@@ -611,7 +626,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
           const int pb = lvl - pa;
           if (pb < 0 || pb >= PB) continue;
 #pragma unroll
-          for (int a = 0; a < 2; ++a)
+          for (int a = 0; a < FA; ++a)
 #pragma unroll
             for (int b = 0; b < 4; ++b)
               acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[pa][a], bv[pb][b],
@@ -645,10 +660,10 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
     const int64_t k = k0 + wk * 64 + 16 * b + fr;
     if (k >= K) continue;
 #pragma unroll
-    for (int a = 0; a < 2; ++a) {
+    for (int a = 0; a < FA; ++a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int64_t n = n0 + wn * 32 + 16 * a + 4 * fg + i;
+        const int64_t n = n0 + wn * TW + 16 * a + 4 * fg + i;
         if (n >= N) continue;
         float* o = dW + n * K + k;
         *o = ACC ? *o + acc[a][b][i] : acc[a][b][i];
@@ -691,7 +706,7 @@ hipError_t bwd_weight_fast(const BwdWeightArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     if (dev >= 0 && dev < 64) attr_set[dev] = true;
   }
-  const int64_t tiles_n = (a.N + kGN - 1) / kGN;
+  const int64_t tiles_n = (a.N + wgt_gn(DA, DB) - 1) / wgt_gn(DA, DB);
   const int64_t tiles_k = (a.K + kGK - 1) / kGK;
   const int64_t patches = ((tiles_n + kPN - 1) / kPN) * ((tiles_k + kPK - 1) / kPK);
   const int64_t grid = ((patches + kXcds - 1) / kXcds) * kXcds * kPN * kPK;

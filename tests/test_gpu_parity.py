@@ -965,6 +965,7 @@ WGT_CASES = [
     (257, 256, 384, "bf16", "f32", False), (96, 264, 136, "f32", "bf16", True),
     (2048, 128, 256, "bf16", "bf16", False), (7, 13, 12, "f32", "f32", False),
     (64, 24, 20, "bf16", "f32", True), (300, 136, 264, "bf16", "bf16", True),
+    (200, 392, 264, "bf16", "bf16", False),
     (161, 264, 136, "f32", "f32", False),
 ]
 
