@@ -167,12 +167,19 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
       kBufFlags);
 
   // staging roles, per MFMA step: every thread one row x 8 columns of dY,
-  // and one code byte (column byte `lane`) of four consecutive W rows
+  // and one code byte (column byte `lane`) of four consecutive W rows.  With
+  // 128 W rows per stage (four steps) a thread instead loads one word (four
+  // column bytes 4d..4d+3) of four rows 4g..4g+3 and transposes the 4 x 4
+  // bytes in registers: four loads per stage instead of sixteen.
+  constexpr bool kW4 = KS * kBN == 128;
   const int sr = tid >> 2, sc = tid & 3;
   const uint32_t yoff = static_cast<uint32_t>((sr * N + 8 * sc) * ES);
   const int yst = swz64(sr, sc);
-  const uint32_t woff = static_cast<uint32_t>(4 * wave * rowbytes + lane);
-  const int wst = P * kPlane + lane * kWrow + 4 * wave;
+  const int wg4 = tid >> 4, wd4 = tid & 15;
+  const uint32_t woff = kW4 ? static_cast<uint32_t>(4 * wg4 * rowbytes + 4 * wd4)
+                            : static_cast<uint32_t>(4 * wave * rowbytes + lane);
+  const int wst = kW4 ? (wg4 / 8) * kStep + P * kPlane + 4 * wd4 * kWrow + 4 * (wg4 % 8)
+                      : P * kPlane + lane * kWrow + 4 * wave;
 
   // fragment reads
   const int fr = lane & 15, fg = lane >> 4;
@@ -198,11 +205,20 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
       for (int i = 0; i < YL; ++i)
         r.y[ks][i] = __builtin_bit_cast(
             v4i, __builtin_amdgcn_raw_buffer_load_b128(ry, yoff + 16 * i, so, 0));
-      const int sw = static_cast<int>(j * kBN * rowbytes);
+      if constexpr (!kW4) {
+        const int sw = static_cast<int>(j * kBN * rowbytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          r.w[ks][i] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(
+              rw, woff + static_cast<uint32_t>(i * rowbytes), sw, 0));
+      }
+    }
+    if constexpr (kW4) {
+      const int sw = static_cast<int>(kt * KS * kBN * rowbytes);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        r.w[ks][i] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(
-            rw, woff + static_cast<uint32_t>(i * rowbytes), sw, 0));
+        r.w[0][i] = __builtin_amdgcn_raw_buffer_load_b32(
+            rw, woff + static_cast<uint32_t>(i * rowbytes), sw, 0);
     }
   };
   // per-row scales of a stage's columns (issued before the far loads of the
@@ -223,8 +239,10 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
       uint8_t* st = lds + buf * kStage + ks * kStep;
       // the loaded values enter here: without this the compiler combines the
       // code bytes right after their loads and waits for them a step early
+      if constexpr (!kW4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(r.w[ks][i]));
+        for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(r.w[ks][i]));
+      }
       const bool ok = (kt * KS + ks) * kBN + 8 * sc < N;
       if constexpr (P == 1) {
         const v4i z = {0, 0, 0, 0};
@@ -248,8 +266,18 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
         *reinterpret_cast<v4i*>(st + kPlane + yst) = m;
         *reinterpret_cast<v4i*>(st + 2 * kPlane + yst) = l;
       }
-      *reinterpret_cast<uint32_t*>(st + wst) =
-          r.w[ks][0] | (r.w[ks][1] << 8) | (r.w[ks][2] << 16) | (r.w[ks][3] << 24);
+      if constexpr (!kW4)
+        *reinterpret_cast<uint32_t*>(st + wst) =
+            r.w[ks][0] | (r.w[ks][1] << 8) | (r.w[ks][2] << 16) | (r.w[ks][3] << 24);
+    }
+    if constexpr (kW4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(r.w[0][i]));
+      // out[s] holds column byte 4d+s of rows 4g..4g+3
+      const v4i t = transpose_bytes4x4(r.w[0][0], r.w[0][1], r.w[0][2], r.w[0][3]);
+      uint8_t* st = lds + buf * kStage;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) *reinterpret_cast<int*>(st + wst + s4 * kWrow) = t[s4];
     }
   };
 
