@@ -128,7 +128,9 @@ __device__ inline bf16x8 decode_column(uint32_t u0, uint32_t u1) {
 }
 
 // DT: 0 = fp32 dY, 1 = bf16 dY.  ROWG: one scale per W row.  ACC: add into dX.
-template <int DT, bool ROWG, bool ACC>
+// W4: stage the codes by words (needs K % 16 == 0, so that rows start on
+// 4-byte boundaries and no word straddles the end of the codes).
+template <int DT, bool ROWG, bool ACC, bool W4>
 __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
     const void* __restrict__ dY, int64_t M, const uint8_t* __restrict__ packed,
     const float* __restrict__ scale, int64_t N, int64_t K, float* __restrict__ dX) {
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
   // 128 W rows per stage (four steps) a thread instead loads one word (four
   // column bytes 4d..4d+3) of four rows 4g..4g+3 and transposes the 4 x 4
   // bytes in registers: four loads per stage instead of sixteen.
-  constexpr bool kW4 = KS * kBN == 128;
+  constexpr bool kW4 = W4 && KS * kBN == 128;
   const int sr = tid >> 2, sc = tid & 3;
   const uint32_t yoff = static_cast<uint32_t>((sr * N + 8 * sc) * ES);
   const int yst = swz64(sr, sc);
@@ -397,22 +399,26 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* __restrict__ p, int64_
     p[i] = 0.f;
 }
 
-template <int DT, bool ROWG, bool ACC>
+template <int DT, bool ROWG, bool ACC, bool W4>
 hipError_t bwd_input_fast(const BwdInputArgs& a, hipStream_t s) {
   const int64_t tiles_m = (a.M + kBM - 1) / kBM;
   const int64_t tiles_k = (a.K + kBK - 1) / kBK;
   const int64_t grid = tiles_k * ((tiles_m + kXcds - 1) / kXcds) * kXcds;
-  hipLaunchKernelGGL((k_bwd_input<DT, ROWG, ACC>), dim3(grid), dim3(kNT), 0, s, a.dY, a.M,
+  hipLaunchKernelGGL((k_bwd_input<DT, ROWG, ACC, W4>), dim3(grid), dim3(kNT), 0, s, a.dY, a.M,
                      a.packed, a.scale, a.N, a.K, a.dX);
   return hipGetLastError();
 }
 
 template <int DT>
 hipError_t bwd_input_fast_dt(const BwdInputArgs& a, hipStream_t s) {
-  if (a.per_row) return a.accumulate ? bwd_input_fast<DT, true, true>(a, s)
-                                     : bwd_input_fast<DT, true, false>(a, s);
-  return a.accumulate ? bwd_input_fast<DT, false, true>(a, s)
-                      : bwd_input_fast<DT, false, false>(a, s);
+  if (a.per_row) return a.accumulate ? bwd_input_fast<DT, true, true, false>(a, s)
+                                     : bwd_input_fast<DT, true, false, false>(a, s);
+  // word staging of the codes only where it applies (one bf16 plane)
+  if (DT == 1 && a.K % 16 == 0)
+    return a.accumulate ? bwd_input_fast<DT, false, true, true>(a, s)
+                        : bwd_input_fast<DT, false, false, true>(a, s);
+  return a.accumulate ? bwd_input_fast<DT, false, true, false>(a, s)
+                      : bwd_input_fast<DT, false, false, false>(a, s);
 }
 
 int64_t grid_for(int64_t n) {

@@ -859,6 +859,7 @@ BWD_CASES = [
     (129, 264, 772, "bf16", "row", True), (300, 520, 1536, "f32", "row", False),
     (64, 37, 64, "f32", "tensor", False), (33, 45, 132, "bf16", "row", True),
     (200, 392, 520, "bf16", "tensor", True), (130, 200, 264, "f32", "tensor", False),
+    (120, 200, 1040, "bf16", "tensor", False), (70, 136, 784, "bf16", "tensor", True),
 ]
 
 
