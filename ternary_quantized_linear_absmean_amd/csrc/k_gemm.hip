@@ -23,7 +23,13 @@
 // that the workgroups resident on one XCD (ids congruent mod 8) share weight
 // columns in that XCD's L2.  The epilogue applies y = acc * gamma * sx in
 // fp32 and writes fp32, bf16 (round to nearest even) or the raw int32
-// accumulator.
+// accumulator; it passes each wave's tile through LDS so that every lane
+// stores 16 contiguous bytes (8 for bf16): element-wise stores straight from
+// the MFMA layout cost more than the main loop's last third.
+//
+// Large grids whose tile rounds fill the chip use wide tiles instead:
+// 256 x 256 per workgroup of four waves, one workgroup per CU, both operands
+// staged through LDS (see k_gemm_wide).
 
 #include <type_traits>
 
@@ -36,6 +42,61 @@ namespace {
 constexpr int kBK = 64;
 constexpr int kLD = kBK + 16;  // LDS row stride in bytes
 constexpr int kXcds = 8;
+
+// Epilogue of a wave holding FM x FN accumulators of the 32x32 MFMA, whose
+// top-left output is (mb, nb).  D layout: lane l holds column l%32 and rows
+// 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.  y = acc * (gamma * sx) in fp32,
+// stored as fp32, bf16 (round to nearest even) or the raw int32.  Stores and
+// loads share one memory counter on this chip, so a load issued between two
+// stores would wait for every store before it: all scale factors are loaded
+// first (rows and columns past the end read the last valid one and are not
+// stored).
+template <int YT, int FM, int FN>
+__device__ inline void store_acc32(const v16i (&acc)[FM][FN], int64_t mb, int64_t nb, int lane,
+                                   const float* __restrict__ sx,
+                                   const float* __restrict__ scale, int per_row, int64_t M,
+                                   int64_t N, void* __restrict__ Y) {
+  const int fr = lane & 31, kg = lane >> 5;
+  float sv[FM][16], gv[FN];
+  if (YT != TQ_I32) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = mb + 32 * i + 8 * (v / 4) + 4 * kg + (v % 4);
+        sv[i][v] = sx[m < M ? m : M - 1];
+      }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t n = nb + 32 * j + fr;
+      gv[j] = scale[per_row ? (n < N ? n : N - 1) : 0];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int64_t n = nb + 32 * j + fr;
+    if (n >= N) continue;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int64_t m = mb + 32 * i + 8 * (v / 4) + 4 * kg + (v % 4);
+        if (m >= M) continue;
+        const int64_t o = m * N + n;
+        const int accv = acc[i][j][v];
+        if (YT == TQ_I32) {
+          static_cast<int*>(Y)[o] = accv;
+        } else {
+          const float y = static_cast<float>(accv) * (gv[j] * sv[i][v]);
+          if (YT == TQ_F32)
+            static_cast<float*>(Y)[o] = y;
+          else
+            static_cast<uint16_t*>(Y)[o] = f32_to_bf16(y);
+        }
+      }
+    }
+  }
+}
 
 template <bool ALIGNED>
 __device__ inline v4i load_a_frag(const uint8_t* row, int64_t k, int64_t K, bool ok) {
@@ -198,32 +259,99 @@ __global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm(
     if (kt + 2 < nk) stage(kt + 2, ra2, ra1);
   }
 
-  // D layout of the 32x32 MFMA: lane l holds column l%32 and rows
-  // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
+  store_acc32<YT>(acc, m0 + wm * TM, n0 + wn * TN, lane, sx, scale, per_row, M, N, Y);
+}
+
+// The same epilogue staged through LDS, for a wave with FM x FN fragments
+// and a private LDS area of 32 x (32 FN + 8) words.  Each 32-row block of the
+// wave tile goes into LDS as raw int32 (lanes 0..31 and 32..63 land on
+// disjoint banks), then is read back four columns per lane, so that every
+// lane stores 16 contiguous bytes (8 for bf16) instead of single elements.
+// The row factors sx and column factors gamma of the wave tile are read from
+// LDS copies (sxl[r], gml[c] for tile row r and column c), so that no global
+// load sits between the stores.
+template <int FN>
+constexpr int staged_lds_words() { return 32 * (32 * FN + 8); }
+
+template <int YT, int FM, int FN>
+__device__ inline void store_acc32_staged(const v16i (&acc)[FM][FN], int64_t mb, int64_t nb,
+                                          int lane, const float* sxl, const float* gml,
+                                          int64_t M, int64_t N, void* __restrict__ Y,
+                                          int* buf) {
+  constexpr int W = 32 * FN;    // columns of the wave tile
+  constexpr int LDW = W + 8;    // LDS row stride in words
+  constexpr int CPR = W / 4;    // four-column chunks per row
+  constexpr int RPI = 64 / CPR; // rows one wave-wide pass covers
+  constexpr int T = 32 / RPI;   // passes per 32-row block
+  const int fr = lane & 31, kg = lane >> 5;
+  const int c4 = lane % CPR, rr = lane / CPR;
+  const int64_t n = nb + 4 * c4;
+  const bool vec = (N & 3) == 0 && (reinterpret_cast<uintptr_t>(Y) & 15u) == 0;
+  float gv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (YT != TQ_I32) {
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int64_t n = n0 + wn * TN + 32 * j + fr;
-    if (n >= N) continue;
-    const float gam = YT == TQ_I32 ? 0.f : scale[per_row ? n : 0];
+    for (int e = 0; e < 4; ++e) gv[e] = gml[4 * c4 + e];
+  }
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * TM + 32 * i + 8 * (v / 4) + 4 * kg + (v % 4);
-        if (m >= M) continue;
-        const int64_t o = m * N + n;
-        const int accv = acc[i][j][v];
-        if (YT == TQ_I32) {
-          static_cast<int*>(Y)[o] = accv;
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        buf[(8 * (v / 4) + 4 * kg + (v % 4)) * LDW + 32 * j + fr] = acc[i][j][v];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    v4i av[T];
+    float sv[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      av[t] = *reinterpret_cast<const v4i*>(buf + (RPI * t + rr) * LDW + 4 * c4);
+      sv[t] = YT == TQ_I32 ? 0.f : sxl[32 * i + RPI * t + rr];
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      const int64_t m = mb + 32 * i + RPI * t + rr;
+      const v4i a = av[t];
+      if (m >= M || n >= N) continue;
+      const int64_t o = m * N + n;
+      if (YT == TQ_I32) {
+        if (vec && n + 3 < N) {
+          *reinterpret_cast<v4i*>(static_cast<int*>(Y) + o) = a;
         } else {
-          const float y = static_cast<float>(accv) * (gam * sx[m]);
-          if (YT == TQ_F32)
-            static_cast<float*>(Y)[o] = y;
-          else
-            static_cast<uint16_t*>(Y)[o] = f32_to_bf16(y);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) static_cast<int*>(Y)[o + e] = a[e];
+        }
+      } else {
+        float y[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = static_cast<float>(a[e]) * (gv[e] * sv[t]);
+        if (YT == TQ_F32) {
+          if (vec && n + 3 < N) {
+            *reinterpret_cast<float4*>(static_cast<float*>(Y) + o) =
+                make_float4(y[0], y[1], y[2], y[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) static_cast<float*>(Y)[o + e] = y[e];
+          }
+        } else {
+          if (vec && n + 3 < N) {
+            const uint32_t lo = f32_to_bf16(y[0]) | (uint32_t{f32_to_bf16(y[1])} << 16);
+            const uint32_t hi = f32_to_bf16(y[2]) | (uint32_t{f32_to_bf16(y[3])} << 16);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + o) = make_uint2(lo, hi);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (n + e < N) static_cast<uint16_t*>(Y)[o + e] = f32_to_bf16(y[e]);
+          }
         }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -263,6 +391,16 @@ __device__ inline int swz(int row, int chunk) {
 // of KG 64-deep sub-tiles each.
 template <int BM, int BN, int KG = 1>
 constexpr int fast_lds_bytes() { return 2 * KG * (BM + BN) * kBK; }
+template <int BM, int BN, int WM, int WN>
+constexpr int fast_epi_bytes() {
+  return (WM * WN * staged_lds_words<BN / WN / 32>() + BM + BN) * 4;
+}
+template <int BM, int BN, int WM, int WN, int KG>
+constexpr int fast_lds_size() {
+  return fast_lds_bytes<BM, BN, KG>() > fast_epi_bytes<BM, BN, WM, WN>()
+             ? fast_lds_bytes<BM, BN, KG>()
+             : fast_epi_bytes<BM, BN, WM, WN>();
+}
 
 // One BM x BN output tile (tile coordinates tm, tn in units of BM, BN) by a
 // workgroup of KG groups of WM x WN waves, staging through `lds`.  A stage
@@ -439,46 +577,42 @@ __device__ __forceinline__ void gemm_fast_tile(
                 acc[i][j][v];
     }
     __syncthreads();
-    if (grp > 0) return;
+    if (grp == 0) {
 #pragma unroll
-    for (int g = 1; g < KG; ++g)
+      for (int g = 1; g < KG; ++g)
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+          for (int j = 0; j < FN; ++j)
 #pragma unroll
-          for (int v = 0; v < 16; ++v)
-            acc[i][j][v] +=
-                red[(g - 1) * NW * FM * FN * 16 * kWave + slot + ((i * FN + j) * 16 + v) * kWave];
-  }
-
-  // D layout of the 32x32 MFMA: lane l holds column l%32 and rows
-  // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int64_t n = n0 + wn * TN + 32 * j + fr;
-    if (n >= N) continue;
-    const float gam = YT == TQ_I32 ? 0.f : scale[per_row ? n : 0];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wm * TM + 32 * i + 8 * (v / 4) + 4 * kg + (v % 4);
-        if (m >= M) continue;
-        const int64_t o = m * N + n;
-        const int accv = acc[i][j][v];
-        if (YT == TQ_I32) {
-          static_cast<int*>(Y)[o] = accv;
-        } else {
-          const float y = static_cast<float>(accv) * (gam * sx[m]);
-          if (YT == TQ_F32)
-            static_cast<float*>(Y)[o] = y;
-          else
-            static_cast<uint16_t*>(Y)[o] = f32_to_bf16(y);
-        }
-      }
+            for (int v = 0; v < 16; ++v)
+              acc[i][j][v] +=
+                  red[(g - 1) * NW * FM * FN * 16 * kWave + slot + ((i * FN + j) * 16 + v) * kWave];
     }
   }
+
+  // staged epilogue: the wave areas, then the tile's row and column factors
+  // (every wave is past its last LDS read once the barrier below is passed)
+  static_assert(fast_epi_bytes<BM, BN, WM, WN>() <= fast_lds_size<BM, BN, WM, WN, KG>(),
+                "epilogue LDS");
+  int* const ep = reinterpret_cast<int*>(lds);
+  float* const sxs = reinterpret_cast<float*>(ep + NW * staged_lds_words<FN>());
+  float* const gms = sxs + BM;
+  __syncthreads();
+  if (YT != TQ_I32) {
+    for (int r = tid; r < BM; r += NT) {
+      const int64_t m = m0 + r;
+      sxs[r] = sx[m < M ? m : M - 1];
+    }
+    for (int c = tid; c < BN; c += NT) {
+      const int64_t n = n0 + c;
+      gms[c] = scale[per_row ? (n < N ? n : N - 1) : 0];
+    }
+  }
+  __syncthreads();
+  if (grp == 0)
+    store_acc32_staged<YT>(acc, m0 + wm * TM, n0 + wn * TN, lane, sxs + wm * TM, gms + wn * TN,
+                           M, N, Y, ep + wl * staged_lds_words<FN>());
 }
 
 template <int BM, int BN, int WM, int WN, int YT, int KG>
@@ -486,7 +620,7 @@ __global__ __launch_bounds__(WM* WN* KG* kWave, 2) void k_gemm_fast(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
     int64_t N, int64_t K, void* __restrict__ Y) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[fast_lds_bytes<BM, BN, KG>()];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[fast_lds_size<BM, BN, WM, WN, KG>()];
   const int64_t tiles_m = (M + BM - 1) / BM;
   gemm_fast_tile<BM, BN, WM, WN, YT, KG>(q, sx, M, packed, scale, per_row, N, K, Y,
                                          blockIdx.x % tiles_m, blockIdx.x / tiles_m, lds);
@@ -506,9 +640,198 @@ hipError_t gemm_fast_launch(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Wide tiles for large grids: 256 x 256 outputs per workgroup of four waves,
+// each wave 128 x 128 (4 x 4 accumulators of 32 x 32, held in the
+// accumulation registers), 128 of K per stage, one workgroup per CU.  A wave
+// issues 64 MFMAs per stage against 32 fragment reads: half the LDS feed per
+// MFMA of a 64 x 64 wave tile, and one barrier per 64 MFMAs.  LDS rows are
+// 144 bytes (128 + 16 of padding): the 16 rows a fragment read touches per
+// quarter-wave fall on distinct banks, and every LDS offset is a base plus a
+// constant, which keeps the architectural registers free for the loads in
+// flight and the fragments read ahead.
+constexpr int kWBM = 256, kWBN = 256, kWBK = 128;
+constexpr int kWNT = 4 * kWave;
+constexpr int kWLD = kWBK + 16;                      // LDS row stride
+constexpr int kWTile = kWBM * kWLD;                  // one operand tile (A or B)
+constexpr int kWStage = 2 * kWTile;
+
+template <int YT>
+__global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
+    const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
+    const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
+    int64_t N, int64_t K, void* __restrict__ Y) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kWStage];
+  constexpr int FM = 4, FN = 4;
+  constexpr int CA = kWBM * (kWBK / 16) / kWNT;  // 8 activation chunks per thread
+  constexpr int CB = kWBN * (kWBK / 16) / kWNT;  // 8 packed words per thread
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int wm = wave / 2, wn = wave % 2;
+  const int64_t tiles_m = (M + kWBM - 1) / kWBM;
+  const int64_t m0 = (blockIdx.x % tiles_m) * kWBM, n0 = (blockIdx.x / tiles_m) * kWBN;
+  const int64_t rowbytes = K >> 2;
+  const int fr = lane & 31, kg = lane >> 5;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(q), static_cast<short>(0), static_cast<int>(M * K), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed), static_cast<short>(0), static_cast<int>(N * rowbytes),
+      kBufFlags);
+  // staging: eight consecutive threads cover a row's 128 bytes of tokens or
+  // 32 bytes of packed codes; chunk i of a thread is 32 rows further
+  const int sr = tid / 8, sc = tid % 8;
+  const uint32_t aoff = static_cast<uint32_t>((m0 + sr) * K + 16 * sc);
+  const uint32_t boff = static_cast<uint32_t>((n0 + sr) * rowbytes + 4 * sc);
+  const uint32_t astep = static_cast<uint32_t>(32 * K), bstep = static_cast<uint32_t>(32 * rowbytes);
+  const int st_off = sr * kWLD + 16 * sc;
+  // fragment reads: row l%32 of each 32-row fragment, bytes 16*(l/32) of a
+  // 32-wide K step
+  const int ard = (wm * 128 + fr) * kWLD + 16 * kg;
+  const int brd = kWTile + (wn * 128 + fr) * kWLD + 16 * kg;
+
+  // two register sets: the loads run two stages ahead of the products
+  struct Regs {
+    v4i a[CA];
+    uint32_t b[CB];
+  };
+  Regs r0, r1;
+  const int64_t nk = K / kWBK;
+  auto load_stage = [&](Regs& r, int64_t kt) {
+    kt = kt < nk ? kt : nk - 1;  // past the end: reload the last stage (unused)
+    const int soa = static_cast<int>(kt * kWBK), sob = static_cast<int>(kt * (kWBK / 4));
+#pragma unroll
+    for (int i = 0; i < CA; ++i)
+      r.a[i] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff + i * astep, soa, 0));
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      r.b[i] = __builtin_amdgcn_raw_buffer_load_b32(rb_rsrc, boff + i * bstep, sob, 0);
+  };
+  auto store_stage = [&](Regs& r, int buf) {
+    uint8_t* st = lds + buf * kWStage + st_off;
+#pragma unroll
+    for (int i = 0; i < CB; ++i) asm volatile("" : "+v"(r.b[i]));
+#pragma unroll
+    for (int i = 0; i < CA; ++i) *reinterpret_cast<v4i*>(st + i * 32 * kWLD) = r.a[i];
+#pragma unroll
+    for (int i = 0; i < CB; ++i)
+      *reinterpret_cast<v4i*>(st + kWTile + i * 32 * kWLD) = decode_signed_natural(r.b[i]);
+  };
+
+  v16i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+  // one of the sixteen pieces of moving a stage from registers into LDS:
+  // even pieces store an activation chunk, odd ones decode and store a
+  // packed word
+  auto put_piece = [&](Regs& r, int buf, int p) {
+    uint8_t* st = lds + buf * kWStage + st_off + (p >> 1) * 32 * kWLD;
+    if (p & 1) {
+      asm volatile("" : "+v"(r.b[p >> 1]));
+      *reinterpret_cast<v4i*>(st + kWTile) = decode_signed_natural(r.b[p >> 1]);
+    } else {
+      *reinterpret_cast<v4i*>(st) = r.a[p >> 1];
+    }
+  };
+  // multiply stage kt out of LDS half buf; between groups of four products
+  // the next stage moves from registers st into the other half
+  auto compute = [&](int buf, Regs& st) {
+    const uint8_t* sa = lds + buf * kWStage + ard;
+    const uint8_t* sb = lds + buf * kWStage + brd;
+    v4i ac[FM], an[FM], bc[FN], bn[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) ac[i] = *reinterpret_cast<const v4i*>(sa + i * 32 * kWLD);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bc[j] = *reinterpret_cast<const v4i*>(sb + j * 32 * kWLD);
+#pragma unroll
+    for (int kk = 0; kk < kWBK / 32; ++kk) {
+      if (kk + 1 < kWBK / 32) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          an[i] = *reinterpret_cast<const v4i*>(sa + i * 32 * kWLD + 32 * (kk + 1));
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bn[j] = *reinterpret_cast<const v4i*>(sb + j * 32 * kWLD + 32 * (kk + 1));
+      }
+      // the reads for the next K step stay ahead of this step's products
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ac[i], bc[j], acc[i][j], 0, 0, 0);
+        put_piece(st, buf ^ 1, kk * FM + i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) ac[i] = an[i];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bc[j] = bn[j];
+    }
+  };
+  // one stage: start the loads of stage kt + 2 into the set stage kt came
+  // from, multiply stage kt while stage kt + 1 moves into the other LDS half
+  auto stage = [&](Regs& ld, Regs& st, int64_t kt) {
+    load_stage(ld, kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(static_cast<int>(kt & 1), st);
+    __syncthreads();
+  };
+
+  load_stage(r0, 0);
+  load_stage(r1, 1);
+  store_stage(r0, 0);
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; kt += 2) {  // nk is even
+    stage(r0, r1, kt);
+    stage(r1, r0, kt + 1);
+  }
+
+  // the last stage ended on a barrier: LDS is free for the staged epilogue,
+  // four wave areas followed by the tile's row and column factors
+  constexpr int kEpi = 4 * staged_lds_words<FN>();
+  static_assert((kEpi + kWBM + kWBN) * 4 <= 2 * kWStage, "epilogue LDS");
+  static_assert(kWNT == kWBM && kWNT == kWBN, "one row and one column factor per thread");
+  int* ep = reinterpret_cast<int*>(lds);
+  float* sxs = reinterpret_cast<float*>(ep + kEpi);
+  float* gms = sxs + kWBM;
+  if (YT != TQ_I32) {
+    const int64_t m = m0 + tid, n = n0 + tid;
+    sxs[tid] = sx[m < M ? m : M - 1];
+    gms[tid] = scale[per_row ? (n < N ? n : N - 1) : 0];
+  }
+  __syncthreads();
+  store_acc32_staged<YT>(acc, m0 + wm * 128, n0 + wn * 128, lane, sxs + wm * 128,
+                         gms + wn * 128, M, N, Y, ep + wave * staged_lds_words<FN>());
+}
+
+hipError_t gemm_wide_launch(const GemmArgs& a, hipStream_t s) {
+  const int64_t grid = ((a.M + kWBM - 1) / kWBM) * ((a.N + kWBN - 1) / kWBN);
+#define TQ_GEMM_WIDE(YTV)                                                                   \
+  hipLaunchKernelGGL((k_gemm_wide<YTV>), dim3(grid), dim3(kWNT), 0, s, a.q, a.sx, a.M,      \
+                     a.packed, a.scale, a.per_row, a.N, a.K, a.Y)
+  if (a.ydt == TQ_F32) TQ_GEMM_WIDE(TQ_F32);
+  else if (a.ydt == TQ_BF16) TQ_GEMM_WIDE(TQ_BF16);
+  else TQ_GEMM_WIDE(TQ_I32);
+#undef TQ_GEMM_WIDE
+  return hipGetLastError();
+}
+
 hipError_t gemm_fast_dispatch(const GemmArgs& a, hipStream_t s) {
   auto tiles = [&](int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); };
   constexpr int64_t kEnough = 384;
+  // wide tiles run one workgroup per CU: they pay off when every round of
+  // tiles, the last one included, fills at least half of the chip
+  const int64_t cus = device_cus() > 0 ? device_cus() : 256;
+  const int64_t tw = tiles(kWBM, kWBN), last = tw % cus;
+  if (tw >= cus && (last == 0 || 2 * last >= cus) && a.K % (2 * kWBK) == 0)
+    return gemm_wide_launch(a, s);
   if (tiles(256, 128) >= kEnough) return gemm_fast_launch<256, 128, 4, 2>(a, s);
   if (tiles(128, 128) >= kEnough) return gemm_fast_launch<128, 128, 2, 2>(a, s);
   // small grids: two wave groups split each 128-deep stage (needs K % 128)

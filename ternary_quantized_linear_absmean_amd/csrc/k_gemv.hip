@@ -632,18 +632,6 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   }
 }
 
-// Compute units of the current device (0 if the query fails), cached per
-// device.
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cus[dev] == 0 &&
-      hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus[dev] = 0;
-  return cus[dev];
-}
-
 // Second matrix of the SwiGLU pair (DUAL launches only).
 struct DualArgs {
   const uint8_t* packed2 = nullptr;
@@ -1173,6 +1161,18 @@ bool dot1_path_ok(int64_t M, int64_t K, const void* packed, const void* act) {
 }
 
 }  // namespace
+
+// Compute units of the current device (0 if the query fails), cached per
+// device.
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cus[dev] == 0 &&
+      hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus[dev] = 0;
+  return cus[dev];
+}
 
 hipError_t launch_gemv(const GemmArgs& a, hipStream_t s) {
   if (dot_path_ok(a.M, a.K, a.packed, a.q))

@@ -80,6 +80,8 @@ bool fused_quant_gemv_ok(int64_t M, int64_t K, const void* packed, const void* X
 hipError_t launch_quant_gemv(const void* X, int bf16, const ActParams& p, int8_t* q,
                              float* sx, const GemmArgs& a, hipStream_t s);
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t s);
+// compute units of the current device (0 if the query fails), cached per device
+int device_cus();
 
 // ---- backward through the packed weights (k_bwd.hip)
 struct BwdInputArgs {

@@ -461,6 +461,27 @@ def test_gemm_prefill_workload_sampled():
                    "tensor", q, packed, scale, sx, cols=cols)
 
 
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 512), (4000, 3900, 768), (4000, 3898, 256),
+                                   (3841, 6913, 256)])
+def test_gemm_wide_tiles(M, N, K):
+    # shapes with one or more full rounds of 256 x 256 tiles (one workgroup
+    # per CU), ragged in M and N; N % 4 != 0 takes the element-wise tail
+    # stores; all tokens, sampled columns including both sides of every
+    # wave-tile and workgroup-tile edge near the start and the last columns
+    q = ti.random_int8(M + K, M, K)
+    w = ti.random_ternary(N + K, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(N + 35, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(M + 36, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    cols = np.unique(np.concatenate([_sample_cols(N, M, 48),
+                                     [3, 4, 5, 127, 128, 255, 256, 257, 511, 512,
+                                      N - 5, N - 4, N - 3, N - 2]]))
+    say(f"gemm wide tiles M={M} N={N} K={K}")
+    for gran, sc in (("row", scale), ("tensor", scale[:1])):
+        _check_outputs(tq.tq_ternary_gemm, dev(q), dev(sx), dev(packed), dev(sc), N, K, gran,
+                       q, packed, sc, sx, cols=cols)
+
+
 @pytest.mark.parametrize("mode", ["ternary", "binary"])
 def test_gemm_bitlinear_workload_sampled(mode):
     W, packed, scale = ref_pack("bitlinear", 0, mode)
