@@ -351,9 +351,22 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
 
   // D of the 16x16 MFMA: lane l holds rows 4(l/16)+i of column l%16, and
   // fragment f is column 4(l%16)+f of the wave's 64
+  // (when accumulating, every old value is loaded before the first store:
+  // loads and stores share one memory counter, so a load issued after a
+  // store would wait for it)
   const float gt = ROWG ? 1.f : scale[0];
   const int64_t col = k0 + wk * 64 + 4 * fr;
   if (col >= K) return;
+  f4 old[4][4];
+  if (ACC) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = m0 + wm * 64 + 16 * a + 4 * fg + i;
+        if (row < M) old[a][i] = *reinterpret_cast<const f4*>(dX + row * K + col);
+      }
+  }
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
 #pragma unroll
@@ -362,9 +375,8 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
       if (row >= M) continue;
       f4 v = {acc[a][0][i], acc[a][1][i], acc[a][2][i], acc[a][3][i]};
       if (!ROWG) v = v * gt;
-      f4* o = reinterpret_cast<f4*>(dX + row * K + col);
-      if (ACC) v = v + *o;
-      *o = v;
+      if (ACC) v = v + old[a][i];
+      *reinterpret_cast<f4*>(dX + row * K + col) = v;
     }
   }
 }
@@ -688,7 +700,22 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
   if (s < ns) step(s, r1, r2, Guarded{});
   if (s + 1 < ns) step(s + 1, r2, r0, Guarded{});
 
-  // D of the 16x16 MFMA: lane l holds rows 4(l/16)+i of column l%16
+  // D of the 16x16 MFMA: lane l holds rows 4(l/16)+i of column l%16.  When
+  // accumulating, all old values are loaded before the first store.
+  float old[4][FA][4];
+  if (ACC) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int64_t k = k0 + wk * 64 + 16 * b + fr;
+#pragma unroll
+      for (int a = 0; a < FA; ++a)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t n = n0 + wn * TW + 16 * a + 4 * fg + i;
+          if (k < K && n < N) old[b][a][i] = dW[n * K + k];
+        }
+    }
+  }
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int64_t k = k0 + wk * 64 + 16 * b + fr;
@@ -699,8 +726,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
       for (int i = 0; i < 4; ++i) {
         const int64_t n = n0 + wn * TW + 16 * a + 4 * fg + i;
         if (n >= N) continue;
-        float* o = dW + n * K + k;
-        *o = ACC ? *o + acc[a][b][i] : acc[a][b][i];
+        dW[n * K + k] = ACC ? old[b][a][i] + acc[a][b][i] : acc[a][b][i];
       }
     }
   }
