@@ -407,7 +407,7 @@ constexpr int fast_lds_size() {
 // covers KG x 64 of K; group g contracts the stage's 64-deep sub-tile g into
 // its own accumulators, and the groups' sums meet in LDS at the end (exact
 // int32 additions).  KG = 2 gives small grids twice the waves per tile.
-template <int BM, int BN, int WM, int WN, int YT, int KG = 1>
+template <int BM, int BN, int WM, int WN, int YT, int KG = 1, bool SPREAD = true>
 __device__ __forceinline__ void gemm_fast_tile(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
@@ -474,21 +474,27 @@ __device__ __forceinline__ void gemm_fast_tile(
   typedef uint32_t BRegs[CB];
   ARegs ra0, ra1, ra2;
   BRegs rb0, rb1, rb2;
-  auto load_stage = [&](int64_t kt, ARegs& a, BRegs& b) {
+  // piece p of a stage: p < CA an activation chunk, else a packed word
+  auto load_piece = [&](int64_t kt, ARegs& a, BRegs& b, int p) {
     const int soa = static_cast<int>(kt * kBK * KG), sob = static_cast<int>(kt * (kBK / 4) * KG);
+    if (p < CA)
+      a[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff[p], soa, 0));
+    else
+      b[p - CA] = __builtin_amdgcn_raw_buffer_load_b32(rb_rsrc, boff[p - CA], sob, 0);
+  };
+  auto store_piece = [&](int buf, ARegs& a, BRegs& b, int p) {
+    if (p < CA)
+      *reinterpret_cast<v4i*>(&As[(buf) * SA + ast[p]]) = a[p];
+    else
+      *reinterpret_cast<v4i*>(&Bs[(buf) * SB + bst[p - CA]]) = decode_signed_natural(b[p - CA]);
+  };
+  auto load_stage = [&](int64_t kt, ARegs& a, BRegs& b) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i)
-      a[i] = __builtin_bit_cast(v4i,
-                                __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff[i], soa, 0));
-#pragma unroll
-    for (int i = 0; i < CB; ++i) b[i] = __builtin_amdgcn_raw_buffer_load_b32(rb_rsrc, boff[i], sob, 0);
+    for (int p = 0; p < CA + CB; ++p) load_piece(kt, a, b, p);
   };
   auto store_stage = [&](int buf, ARegs& a, BRegs& b) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i) *reinterpret_cast<v4i*>(&As[(buf) * SA + ast[i]]) = a[i];
-#pragma unroll
-    for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<v4i*>(&Bs[(buf) * SB + bst[i]]) = decode_signed_natural(b[i]);
+    for (int p = 0; p < CA + CB; ++p) store_piece(buf, a, b, p);
   };
 
   v16i acc[FM][FN];
@@ -500,18 +506,25 @@ __device__ __forceinline__ void gemm_fast_tile(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
   const int64_t nk = K / (kBK * KG);
-  // one stage: start the loads of stage kt+2, contract stage kt from LDS,
-  // publish stage kt+1 (loaded during the previous stage).  In the main loop
-  // (GUARD false) every stage issues its loads and stores unconditionally:
-  // a branch around the loads would leave the compiler unable to count the
-  // loads in flight, and it would then wait for all of them, the ones just
-  // issued included.  Loads past stage nk-1 read zeros or data that is never
-  // stored; a store of stage nk goes to the LDS half no later stage reads.
+  // one stage: contract stage kt from LDS, move stage kt+1 (loaded during
+  // the previous stage) from registers into the other LDS half, load stage
+  // kt+2.  With SPREAD the pieces of the move and the loads go out after
+  // each group of FN products, so that neither arrives in one burst from
+  // every wave; without it (for workgroups with enough waves per SIMD to
+  // overlap these phases on their own) the loads go out first and the move
+  // follows the products.  In the main loop (GUARD false) every stage issues its
+  // loads and stores unconditionally: a branch around the loads would leave
+  // the compiler unable to count the loads in flight, and it would then wait
+  // for all of them, the ones just issued included.  Loads past stage nk-1
+  // read zeros or data that is never stored; a store of stage nk goes to the
+  // LDS half no later stage reads.
+  constexpr int kGroups = kKS * FM, kPieces = CA + CB;
   auto stage = [&](int64_t kt, ARegs& a_next, BRegs& b_next, ARegs& a_far, BRegs& b_far,
                    auto guard) {
     constexpr bool GUARD = decltype(guard)::value;
     const int buf = static_cast<int>(kt & 1);
-    if (!GUARD || kt + 2 < nk) load_stage(kt + 2, a_far, b_far);
+    const bool do_load = !GUARD || kt + 2 < nk, do_store = !GUARD || kt + 1 < nk;
+    if (!SPREAD && do_load) load_stage(kt + 2, a_far, b_far);
     v4i ac[FM], an[FM], bc[FN], bn[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) ac[i] = *reinterpret_cast<const v4i*>(&As[(buf) * SA + ard[i][0]]);
@@ -527,20 +540,33 @@ __device__ __forceinline__ void gemm_fast_tile(
         for (int j = 0; j < FN; ++j)
           bn[j] = *reinterpret_cast<const v4i*>(&Bs[(buf) * SB + brd[j][ks + 1]]);
       }
+      if constexpr (SPREAD) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ac[i], bc[j], acc[i][j], 0, 0, 0);
+        if constexpr (SPREAD) {
+          const int g = ks * FM + i;
+#pragma unroll
+          for (int p = g; p < kPieces; p += kGroups) {
+            if (do_store) store_piece(buf ^ 1, a_next, b_next, p);
+            if (do_load) load_piece(kt + 2, a_far, b_far, p);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < FM; ++i) ac[i] = an[i];
 #pragma unroll
       for (int j = 0; j < FN; ++j) bc[j] = bn[j];
     }
-    // keep the decode of stage kt+1 here: hoisted above the MFMAs it would
-    // wait for that stage's loads one stage early
-    __builtin_amdgcn_sched_barrier(0);
-    if (!GUARD || kt + 1 < nk) store_stage(buf ^ 1, a_next, b_next);
+    // without SPREAD, stage kt+1 moves to LDS after the products (hoisted
+    // above them, its decode would wait for that stage's loads early)
+    if constexpr (!SPREAD) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (do_store) store_stage(buf ^ 1, a_next, b_next);
+    }
     __syncthreads();
   };
   using Free = std::false_type;
@@ -615,23 +641,23 @@ __device__ __forceinline__ void gemm_fast_tile(
                            M, N, Y, ep + wl * staged_lds_words<FN>());
 }
 
-template <int BM, int BN, int WM, int WN, int YT, int KG>
+template <int BM, int BN, int WM, int WN, int YT, int KG, bool SPREAD>
 __global__ __launch_bounds__(WM* WN* KG* kWave, 2) void k_gemm_fast(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
     int64_t N, int64_t K, void* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[fast_lds_size<BM, BN, WM, WN, KG>()];
   const int64_t tiles_m = (M + BM - 1) / BM;
-  gemm_fast_tile<BM, BN, WM, WN, YT, KG>(q, sx, M, packed, scale, per_row, N, K, Y,
+  gemm_fast_tile<BM, BN, WM, WN, YT, KG, SPREAD>(q, sx, M, packed, scale, per_row, N, K, Y,
                                          blockIdx.x % tiles_m, blockIdx.x / tiles_m, lds);
 }
 
-template <int BM, int BN, int WM, int WN, int KG = 1>
+template <int BM, int BN, int WM, int WN, int KG = 1, bool SPREAD = true>
 hipError_t gemm_fast_launch(const GemmArgs& a, hipStream_t s) {
   const int64_t grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int NT = WM * WN * KG * kWave;
 #define TQ_GEMM_FAST(YTV)                                                                      \
-  hipLaunchKernelGGL((k_gemm_fast<BM, BN, WM, WN, YTV, KG>), dim3(grid), dim3(NT), 0, s, a.q, \
+  hipLaunchKernelGGL((k_gemm_fast<BM, BN, WM, WN, YTV, KG, SPREAD>), dim3(grid), dim3(NT), 0, s, a.q, \
                      a.sx, a.M, a.packed, a.scale, a.per_row, a.N, a.K, a.Y)
   if (a.ydt == TQ_F32) TQ_GEMM_FAST(TQ_F32);
   else if (a.ydt == TQ_BF16) TQ_GEMM_FAST(TQ_BF16);
@@ -697,16 +723,19 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
   };
   Regs r0, r1;
   const int64_t nk = K / kWBK;
-  auto load_stage = [&](Regs& r, int64_t kt) {
+  // load p of a stage: even p an activation chunk, odd p a packed word
+  auto load_piece = [&](Regs& r, int64_t kt, int p) {
     kt = kt < nk ? kt : nk - 1;  // past the end: reload the last stage (unused)
     const int soa = static_cast<int>(kt * kWBK), sob = static_cast<int>(kt * (kWBK / 4));
+    if (p & 1)
+      r.b[p >> 1] = __builtin_amdgcn_raw_buffer_load_b32(rb_rsrc, boff + (p >> 1) * bstep, sob, 0);
+    else
+      r.a[p >> 1] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff + (p >> 1) * astep, soa, 0));
+  };
+  auto load_stage = [&](Regs& r, int64_t kt) {
 #pragma unroll
-    for (int i = 0; i < CA; ++i)
-      r.a[i] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff + i * astep, soa, 0));
-#pragma unroll
-    for (int i = 0; i < CB; ++i)
-      r.b[i] = __builtin_amdgcn_raw_buffer_load_b32(rb_rsrc, boff + i * bstep, sob, 0);
+    for (int p = 0; p < CA + CB; ++p) load_piece(r, kt, p);
   };
   auto store_stage = [&](Regs& r, int buf) {
     uint8_t* st = lds + buf * kWStage + st_off;
@@ -740,8 +769,12 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
     }
   };
   // multiply stage kt out of LDS half buf; between groups of four products
-  // the next stage moves from registers st into the other half
-  auto compute = [&](int buf, Regs& st) {
+  // the next stage moves from registers st into the other half and one load
+  // of stage kld goes out into registers ld (sixteen of each per stage:
+  // spread over the stage, the loads do not reach the memory system in one
+  // burst from every wave at once)
+  static_assert(CA + CB == 4 * FM && CA == CB, "one load and one store piece per group");
+  auto compute = [&](int buf, Regs& st, Regs& ld, int64_t kld) {
     const uint8_t* sa = lds + buf * kWStage + ard;
     const uint8_t* sb = lds + buf * kWStage + brd;
     v4i ac[FM], an[FM], bc[FN], bn[FN];
@@ -767,6 +800,7 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ac[i], bc[j], acc[i][j], 0, 0, 0);
         put_piece(st, buf ^ 1, kk * FM + i);
+        load_piece(ld, kld, kk * FM + i);
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
@@ -775,12 +809,10 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
       for (int j = 0; j < FN; ++j) bc[j] = bn[j];
     }
   };
-  // one stage: start the loads of stage kt + 2 into the set stage kt came
-  // from, multiply stage kt while stage kt + 1 moves into the other LDS half
+  // one stage: multiply stage kt while stage kt + 1 moves into the other LDS
+  // half and stage kt + 2 is loaded into the set stage kt came from
   auto stage = [&](Regs& ld, Regs& st, int64_t kt) {
-    load_stage(ld, kt + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(static_cast<int>(kt & 1), st);
+    compute(static_cast<int>(kt & 1), st, ld, kt + 2);
     __syncthreads();
   };
 
@@ -832,7 +864,7 @@ hipError_t gemm_fast_dispatch(const GemmArgs& a, hipStream_t s) {
   const int64_t tw = tiles(kWBM, kWBN), last = tw % cus;
   if (tw >= cus && (last == 0 || 2 * last >= cus) && a.K % (2 * kWBK) == 0)
     return gemm_wide_launch(a, s);
-  if (tiles(256, 128) >= kEnough) return gemm_fast_launch<256, 128, 4, 2>(a, s);
+  if (tiles(256, 128) >= kEnough) return gemm_fast_launch<256, 128, 4, 2, 1, false>(a, s);
   if (tiles(128, 128) >= kEnough) return gemm_fast_launch<128, 128, 2, 2>(a, s);
   // small grids: two wave groups split each 128-deep stage (needs K % 128)
   if (a.K % 128 == 0) return gemm_fast_launch<128, 64, 4, 1, 2>(a, s);
