@@ -338,9 +338,8 @@ __device__ inline void store_acc32_staged(const v16i (&acc)[FM][FN], int64_t mb,
           }
         } else {
           if (vec && n + 3 < N) {
-            const uint32_t lo = f32_to_bf16(y[0]) | (uint32_t{f32_to_bf16(y[1])} << 16);
-            const uint32_t hi = f32_to_bf16(y[2]) | (uint32_t{f32_to_bf16(y[3])} << 16);
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + o) = make_uint2(lo, hi);
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + o) =
+                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)

@@ -118,11 +118,16 @@ __device__ inline float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
+// fp32 -> bf16 bits, round to nearest even: the chip's own conversion
+// (v_cvt_pk_bf16_f32; NaN stays NaN, subnormals are rounded, not flushed).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ inline uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+}
+// two values in one conversion: lo in bits 0..15, hi in bits 16..31
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // round half to even, clamp to [-127, 127], as a byte

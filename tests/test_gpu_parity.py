@@ -482,6 +482,37 @@ def test_gemm_wide_tiles(M, N, K):
                        q, packed, sc, sx, cols=cols)
 
 
+def _rne_bf16_bits(y32):
+    # round-to-nearest-even of finite fp32 values to bf16, on the bit pattern
+    u = np.ascontiguousarray(y32, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 256), (2048, 6144, 256), (1100, 3000, 256), (200, 520, 512),
+                                   (37, 300, 68), (3, 777, 512)])
+@pytest.mark.parametrize("tiny", [False, True])
+def test_bf16_output_is_rounded_fp32_output(M, N, K, tiny):
+    # the bf16 output must be the fp32 output rounded to nearest even, bit
+    # for bit, also where the fp32 outputs are subnormal (tiny scales);
+    # shapes reach the wide tiles, the 256x128 and 128x64 tiles, the
+    # unaligned kernel and the decode path
+    q = ti.random_int8(M + 2 * K, M, K)
+    w = ti.random_ternary(N + 3 * K, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(N + 37, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(M + 38, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    if tiny:
+        scale = (scale * np.float32(1e-36)).astype(np.float32)
+    say(f"bf16 rounding M={M} N={N} K={K} tiny={tiny}")
+    fn = tq.tq_ternary_gemv if M <= 16 else tq.tq_ternary_gemm
+    qd, sxd, pd, sd = dev(q), dev(sx), dev(packed), dev(scale)
+    y32 = host(fn(qd, sxd, pd, sd, N, K, "row", "f32"))
+    yb = host(fn(qd, sxd, pd, sd, N, K, "row", "bf16").view(torch.int16)).view(np.uint16)
+    if tiny:
+        assert np.any((y32 != 0) & (np.abs(y32) < np.finfo(np.float32).tiny))
+    np.testing.assert_array_equal(yb, _rne_bf16_bits(y32))
+
+
 @pytest.mark.parametrize("mode", ["ternary", "binary"])
 def test_gemm_bitlinear_workload_sampled(mode):
     W, packed, scale = ref_pack("bitlinear", 0, mode)
