@@ -689,6 +689,7 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
   constexpr int FM = 4, FN = 4;
   constexpr int CA = kWBM * (kWBK / 16) / kWNT;  // 8 activation chunks per thread
   constexpr int CB = kWBN * (kWBK / 16) / kWNT;  // 8 packed words per thread
+  constexpr int LB = CB / 4;                      // in 2 loads of 16 bytes
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -703,13 +704,16 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
   const __amdgpu_buffer_rsrc_t rb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(packed), static_cast<short>(0), static_cast<int>(N * rowbytes),
       kBufFlags);
-  // staging: eight consecutive threads cover a row's 128 bytes of tokens or
-  // 32 bytes of packed codes; chunk i of a thread is 32 rows further
+  // staging: eight consecutive threads cover a row's 128 bytes of tokens,
+  // chunk i of a thread 32 rows further; two threads cover a row's 32 bytes
+  // of packed codes, 16 bytes (four words) each, load i 128 rows further
   const int sr = tid / 8, sc = tid % 8;
+  const int br = tid / 2, bh = tid % 2;
   const uint32_t aoff = static_cast<uint32_t>((m0 + sr) * K + 16 * sc);
-  const uint32_t boff = static_cast<uint32_t>((n0 + sr) * rowbytes + 4 * sc);
-  const uint32_t astep = static_cast<uint32_t>(32 * K), bstep = static_cast<uint32_t>(32 * rowbytes);
+  const uint32_t boff = static_cast<uint32_t>((n0 + br) * rowbytes + 16 * bh);
+  const uint32_t astep = static_cast<uint32_t>(32 * K), bstep = static_cast<uint32_t>(128 * rowbytes);
   const int st_off = sr * kWLD + 16 * sc;
+  const int bst_off = kWTile + br * kWLD + 64 * bh;
   // fragment reads: row l%32 of each 32-row fragment, bytes 16*(l/32) of a
   // 32-wide K step
   const int ard = (wm * 128 + fr) * kWLD + 16 * kg;
@@ -718,33 +722,26 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
   // two register sets: the loads run two stages ahead of the products
   struct Regs {
     v4i a[CA];
-    uint32_t b[CB];
+    v4i b[LB];
   };
   Regs r0, r1;
   const int64_t nk = K / kWBK;
-  // load p of a stage: even p an activation chunk, odd p a packed word
+  // load slot p of a stage: even p an activation chunk; odd p = 2q + 1 the
+  // packed load q / 4 when q % 4 == 0 (ten loads per stage)
   auto load_piece = [&](Regs& r, int64_t kt, int p) {
     kt = kt < nk ? kt : nk - 1;  // past the end: reload the last stage (unused)
     const int soa = static_cast<int>(kt * kWBK), sob = static_cast<int>(kt * (kWBK / 4));
-    if (p & 1)
-      r.b[p >> 1] = __builtin_amdgcn_raw_buffer_load_b32(rb_rsrc, boff + (p >> 1) * bstep, sob, 0);
-    else
-      r.a[p >> 1] = __builtin_bit_cast(
-          v4i, __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff + (p >> 1) * astep, soa, 0));
+    const int q = p >> 1;
+    if (!(p & 1))
+      r.a[q] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, aoff + q * astep, soa, 0));
+    else if (q % 4 == 0)
+      r.b[q / 4] = __builtin_bit_cast(
+          v4i, __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, boff + (q / 4) * bstep, sob, 0));
   };
   auto load_stage = [&](Regs& r, int64_t kt) {
 #pragma unroll
     for (int p = 0; p < CA + CB; ++p) load_piece(r, kt, p);
-  };
-  auto store_stage = [&](Regs& r, int buf) {
-    uint8_t* st = lds + buf * kWStage + st_off;
-#pragma unroll
-    for (int i = 0; i < CB; ++i) asm volatile("" : "+v"(r.b[i]));
-#pragma unroll
-    for (int i = 0; i < CA; ++i) *reinterpret_cast<v4i*>(st + i * 32 * kWLD) = r.a[i];
-#pragma unroll
-    for (int i = 0; i < CB; ++i)
-      *reinterpret_cast<v4i*>(st + kWTile + i * 32 * kWLD) = decode_signed_natural(r.b[i]);
   };
 
   v16i acc[FM][FN];
@@ -759,13 +756,19 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
   // even pieces store an activation chunk, odd ones decode and store a
   // packed word
   auto put_piece = [&](Regs& r, int buf, int p) {
-    uint8_t* st = lds + buf * kWStage + st_off + (p >> 1) * 32 * kWLD;
+    const int q = p >> 1;
     if (p & 1) {
-      asm volatile("" : "+v"(r.b[p >> 1]));
-      *reinterpret_cast<v4i*>(st + kWTile) = decode_signed_natural(r.b[p >> 1]);
+      uint32_t w = static_cast<uint32_t>(r.b[q / 4][q % 4]);
+      asm volatile("" : "+v"(w));
+      *reinterpret_cast<v4i*>(lds + buf * kWStage + bst_off + (q / 4) * 128 * kWLD +
+                              16 * (q % 4)) = decode_signed_natural(w);
     } else {
-      *reinterpret_cast<v4i*>(st) = r.a[p >> 1];
+      *reinterpret_cast<v4i*>(lds + buf * kWStage + st_off + q * 32 * kWLD) = r.a[q];
     }
+  };
+  auto store_stage = [&](Regs& r, int buf) {
+#pragma unroll
+    for (int p = 0; p < CA + CB; ++p) put_piece(r, buf, p);
   };
   // multiply stage kt out of LDS half buf; between groups of four products
   // the next stage moves from registers st into the other half and one load
