@@ -16,7 +16,8 @@ Prints one JSON line.  ``value`` is algorithmic bytes of the step over its
 time (GB/s).  ``roofline`` describes the GEMV kernel: its algorithmic bytes
 per launch over its average launch time, against 8 TB/s.  ``cpu_baseline``
 times the CPU oracle on a bounded sample of the same workload.  ``extra``
-carries the prefill GEMM (int8 MFMA TOPS), the BitLinear prologue, the FFN
+carries the prefill GEMM (int8 MFMA TOPS), a 4096^3 GEMM (one full round of
+wide tiles) with the vendor int8 GEMM beside it, the BitLinear prologue, the FFN
 decode shapes, the pack kernels (absmean, threshold, code-format
 conversion), the steady-state GEMV rate (stacked projections in one launch),
 1-bit binary weights, the SwiGLU decode FFN and the backward of the prefill
@@ -51,7 +52,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--only", default="",
                    help="comma list of extra workloads to run: "
-                        "prefill,bitlinear,pack,ffn,steady,binary1,ffn_decode,backward,"
+                        "prefill,square,bitlinear,pack,ffn,steady,binary1,ffn_decode,backward,"
                         "context")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (for counter scaling)")
@@ -252,6 +253,8 @@ def extras(torch, np, ti, tq, dev, only=frozenset()):
     want = (lambda name: not only or name in only)
     if want("prefill") or want("pack"):
         out.update(extra_prefill(torch, ti, tq, dev, want))
+    if want("square"):
+        out.update(extra_square(torch, tq, dev))
     if want("bitlinear"):
         out.update(extra_bitlinear(torch, ti, tq, dev))
     if want("ffn"):
@@ -323,6 +326,40 @@ def extra_prefill(torch, ti, tq, dev, want):
         t = timed_graph(torch, g, 10) / reps
         out["convert_codes_to_f0"] = {"bytes": 2 * packed.numel(), "us": round(t * 1e6, 2),
                                       "GBs": round(2 * packed.numel() / t / 1e9, 1)}
+    return out
+
+
+def extra_square(torch, tq, dev):
+    """GEMM 4096 x 4096 x 4096 -> bf16: 256 tiles of 256 x 256, one full
+    round of the wide-tile kernel (one workgroup per CU), next to the vendor
+    int8 GEMM on the same shape."""
+    M = N = K = 4096
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4096)
+    W = torch.randn((N, K), generator=gen, device=dev) * 0.02
+    packed, scale = tq.tq_pack_ternary(W, "tensor")
+    X = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+    q, sx = tq.tq_quant_act_int8(X)
+    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    reps = 8
+    g = capture(torch, lambda: [tq.tq_ternary_gemm(q, sx, packed, scale, N, K, "tensor", "bf16",
+                                                   Y=Y) for _ in range(reps)])
+    warm(torch, g)
+    t = timed_graph(torch, g, 5) / reps
+    tops = 2.0 * M * N * K / t / 1e12
+    out = {"gemm_4096x4096x4096": {"shape": [M, N, K], "out": "bf16", "kernel": "k_gemm_wide",
+                                   "us": round(t * 1e6, 2), "TOPS": round(tops, 1),
+                                   "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)}}
+    try:
+        B = (torch.randint(-1, 2, (N, K), generator=gen, device=dev)).to(torch.int8)
+        g = capture(torch, lambda: [torch._int_mm(q, B.t()) for _ in range(reps)])
+        warm(torch, g)
+        t = timed_graph(torch, g, 5) / reps
+        out["vendor_int8_gemm_4096x4096x4096"] = {
+            "api": "torch._int_mm (int8 x int8 -> int32)", "us": round(t * 1e6, 2),
+            "TOPS": round(2.0 * M * N * K / t / 1e12, 1)}
+    except Exception as e:  # the reference is optional context
+        out["vendor_int8_gemm_4096x4096x4096"] = {"error": str(e)[:200]}
     return out
 
 
