@@ -10,26 +10,25 @@
 // each packed word is read from global memory once per workgroup tile,
 // decoded once into signed int8 in LDS, and fed to v_mfma_i32_32x32x32_i8.
 //
-// gfx950 mapping.  A workgroup computes a BM x BN tile with WM x WN waves.
-// Each wave owns TM = BM/WM rows of the token matrix: its int8 activation
-// fragments go straight from global memory into MFMA registers (16 bytes
-// per lane per fragment), prefetched two K-stages ahead, with no LDS round
-// trip.  The packed weight tile (BN rows x 16 bytes per 64-wide stage) is
-// loaded once per workgroup, decoded to signed int8 and written to a
-// double-buffered LDS tile (rows padded to 80 bytes so that 128-bit reads of
-// eight consecutive rows touch disjoint banks); every wave reads its weight
-// fragments from there.  Launch bounds allow two workgroups per CU, so one
-// can compute while the other waits on memory.  Workgroup ids are mapped so
-// that the workgroups resident on one XCD (ids congruent mod 8) share weight
-// columns in that XCD's L2.  The epilogue applies y = acc * gamma * sx in
-// fp32 and writes fp32, bf16 (round to nearest even) or the raw int32
-// accumulator; it passes each wave's tile through LDS so that every lane
-// stores 16 contiguous bytes (8 for bf16): element-wise stores straight from
-// the MFMA layout cost more than the main loop's last third.
-//
-// Large grids whose tile rounds fill the chip use wide tiles instead:
-// 256 x 256 per workgroup of four waves, one workgroup per CU, both operands
-// staged through LDS (see k_gemm_wide).
+// Three kernels, picked by shape:
+//   - k_gemm_fast (K % 64 == 0, aligned): both operand tiles staged through a
+//     double-buffered, swizzled LDS tile, eight- or four-wave workgroups,
+//     two workgroups per CU (see the fast-path notes below);
+//   - k_gemm_wide (K % 256 == 0, aligned, every round of 256 x 256 tiles at
+//     least half full): 256 x 256 per workgroup of four 128 x 128 waves, one
+//     workgroup per CU, half the LDS reads per MFMA of the fast tiles;
+//   - k_gemm (any shape): each wave owns TM = BM/WM token rows whose int8
+//     fragments go straight from global memory into MFMA registers (byte
+//     loads where K or the pointers are unaligned); the packed weight tile is
+//     decoded to signed int8 into a double-buffered LDS tile with 80-byte rows.
+// In k_gemm, workgroup ids are mapped so that the workgroups resident on one
+// XCD (ids congruent mod 8) share weight columns in that XCD's L2; the fast
+// and wide kernels take tiles with the token-row index fastest.  The epilogue
+// applies y = acc * gamma * sx in fp32 and writes fp32, bf16 (round to
+// nearest even) or the raw int32 accumulator.  The fast and wide kernels
+// pass each wave's tile through LDS so that every lane stores 16 contiguous
+// bytes (8 for bf16): element-wise stores straight from the MFMA layout cost
+// more than the main loop's last third.
 
 #include <type_traits>
 
