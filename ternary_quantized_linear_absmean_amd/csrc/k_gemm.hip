@@ -640,7 +640,7 @@ __device__ __forceinline__ void gemm_fast_tile(
 }
 
 template <int BM, int BN, int WM, int WN, int YT, int KG, bool SPREAD>
-__global__ __launch_bounds__(WM* WN* KG* kWave, 2) void k_gemm_fast(
+__global__ __launch_bounds__(WM* WN* KG* kWave, WM* WN* KG >= 16 ? 1 : 2) void k_gemm_fast(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
     int64_t N, int64_t K, void* __restrict__ Y) {
