@@ -865,7 +865,9 @@ hipError_t gemm_fast_dispatch(const GemmArgs& a, hipStream_t s) {
   const int64_t tw = tiles(kWBM, kWBN), last = tw % cus;
   if (tw >= cus && (last == 0 || 2 * last >= cus) && a.K % (2 * kWBK) == 0)
     return gemm_wide_launch(a, s);
-  if (tiles(256, 128) >= kEnough) return gemm_fast_launch<256, 128, 4, 2, 1, false>(a, s);
+  // 256 x 128 tiles from one per CU on (measured: 2048 x 4096 runs 7% faster
+  // on 256 of them than on 512 tiles of 128 x 128)
+  if (tiles(256, 128) >= cus) return gemm_fast_launch<256, 128, 4, 2, 1, false>(a, s);
   if (tiles(128, 128) >= kEnough) return gemm_fast_launch<128, 128, 2, 2>(a, s);
   // small grids: two wave groups split each 128-deep stage (needs K % 128)
   if (a.K % 128 == 0) return gemm_fast_launch<128, 64, 4, 1, 2>(a, s);
