@@ -371,12 +371,13 @@ __device__ inline void store_acc32_staged(const v16i (&acc)[FM][FN], int64_t mb,
 // K loop and whose K position rides in the scalar offset (no address
 // arithmetic in the loop; reads past the end return zero).  Loads run two
 // stages ahead in registers; each stage stores the next stage's tiles into
-// the other half of a double-buffered LDS tile.  LDS rows are 64 bytes with
-// the four 16-byte chunks XOR-swizzled by ((row >> 1) ^ (row >> 4)) & 3:
-// measured on gfx950 with the LDS bank-conflict counter, this is free of
-// conflicts for the tile stores (four lanes per row) and for the MFMA
-// fragment reads of both 32-wide K steps (32 rows, two chunks).  Fragment reads for the next 32-wide K step are issued
-// before the MFMAs of the current one.
+// the other half of a double-buffered LDS tile, both spread over the
+// stage's MFMAs.  LDS rows are 64 bytes with the four 16-byte chunks
+// XOR-swizzled by ((row >> 1) ^ (row >> 4)) & 3: measured on gfx950 with the
+// LDS bank-conflict counter, this is free of conflicts for the tile stores
+// (four lanes per row) and for the MFMA fragment reads of both 32-wide K
+// steps (32 rows, two chunks).  Fragment reads for the next 32-wide K step
+// are issued before the MFMAs of the current one.
 
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kKS = kBK / 32;          // MFMA K steps per stage
@@ -405,7 +406,7 @@ constexpr int fast_lds_size() {
 // covers KG x 64 of K; group g contracts the stage's 64-deep sub-tile g into
 // its own accumulators, and the groups' sums meet in LDS at the end (exact
 // int32 additions).  KG = 2 gives small grids twice the waves per tile.
-template <int BM, int BN, int WM, int WN, int YT, int KG = 1, bool SPREAD = true>
+template <int BM, int BN, int WM, int WN, int YT, int KG = 1>
 __device__ __forceinline__ void gemm_fast_tile(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
@@ -506,11 +507,9 @@ __device__ __forceinline__ void gemm_fast_tile(
   const int64_t nk = K / (kBK * KG);
   // one stage: contract stage kt from LDS, move stage kt+1 (loaded during
   // the previous stage) from registers into the other LDS half, load stage
-  // kt+2.  With SPREAD the pieces of the move and the loads go out after
-  // each group of FN products, so that neither arrives in one burst from
-  // every wave; without it (for workgroups with enough waves per SIMD to
-  // overlap these phases on their own) the loads go out first and the move
-  // follows the products.  In the main loop (GUARD false) every stage issues its
+  // kt+2.  The pieces of the move and the loads go out after each group of
+  // FN products, so that neither arrives in one burst from every wave.  In
+  // the main loop (GUARD false) every stage issues its
   // loads and stores unconditionally: a branch around the loads would leave
   // the compiler unable to count the loads in flight, and it would then wait
   // for all of them, the ones just issued included.  Loads past stage nk-1
@@ -522,7 +521,6 @@ __device__ __forceinline__ void gemm_fast_tile(
     constexpr bool GUARD = decltype(guard)::value;
     const int buf = static_cast<int>(kt & 1);
     const bool do_load = !GUARD || kt + 2 < nk, do_store = !GUARD || kt + 1 < nk;
-    if (!SPREAD && do_load) load_stage(kt + 2, a_far, b_far);
     v4i ac[FM], an[FM], bc[FN], bn[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) ac[i] = *reinterpret_cast<const v4i*>(&As[(buf) * SA + ard[i][0]]);
@@ -538,32 +536,24 @@ __device__ __forceinline__ void gemm_fast_tile(
         for (int j = 0; j < FN; ++j)
           bn[j] = *reinterpret_cast<const v4i*>(&Bs[(buf) * SB + brd[j][ks + 1]]);
       }
-      if constexpr (SPREAD) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ac[i], bc[j], acc[i][j], 0, 0, 0);
-        if constexpr (SPREAD) {
-          const int g = ks * FM + i;
+        const int g = ks * FM + i;
 #pragma unroll
-          for (int p = g; p < kPieces; p += kGroups) {
-            if (do_store) store_piece(buf ^ 1, a_next, b_next, p);
-            if (do_load) load_piece(kt + 2, a_far, b_far, p);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+        for (int p = g; p < kPieces; p += kGroups) {
+          if (do_store) store_piece(buf ^ 1, a_next, b_next, p);
+          if (do_load) load_piece(kt + 2, a_far, b_far, p);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i) ac[i] = an[i];
 #pragma unroll
       for (int j = 0; j < FN; ++j) bc[j] = bn[j];
-    }
-    // without SPREAD, stage kt+1 moves to LDS after the products (hoisted
-    // above them, its decode would wait for that stage's loads early)
-    if constexpr (!SPREAD) {
-      __builtin_amdgcn_sched_barrier(0);
-      if (do_store) store_stage(buf ^ 1, a_next, b_next);
     }
     __syncthreads();
   };
@@ -639,23 +629,23 @@ __device__ __forceinline__ void gemm_fast_tile(
                            M, N, Y, ep + wl * staged_lds_words<FN>());
 }
 
-template <int BM, int BN, int WM, int WN, int YT, int KG, bool SPREAD>
+template <int BM, int BN, int WM, int WN, int YT, int KG>
 __global__ __launch_bounds__(WM* WN* KG* kWave, WM* WN* KG >= 16 ? 1 : 2) void k_gemm_fast(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
     int64_t N, int64_t K, void* __restrict__ Y) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[fast_lds_size<BM, BN, WM, WN, KG>()];
   const int64_t tiles_m = (M + BM - 1) / BM;
-  gemm_fast_tile<BM, BN, WM, WN, YT, KG, SPREAD>(q, sx, M, packed, scale, per_row, N, K, Y,
+  gemm_fast_tile<BM, BN, WM, WN, YT, KG>(q, sx, M, packed, scale, per_row, N, K, Y,
                                          blockIdx.x % tiles_m, blockIdx.x / tiles_m, lds);
 }
 
-template <int BM, int BN, int WM, int WN, int KG = 1, bool SPREAD = true>
+template <int BM, int BN, int WM, int WN, int KG = 1>
 hipError_t gemm_fast_launch(const GemmArgs& a, hipStream_t s) {
   const int64_t grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   constexpr int NT = WM * WN * KG * kWave;
 #define TQ_GEMM_FAST(YTV)                                                                      \
-  hipLaunchKernelGGL((k_gemm_fast<BM, BN, WM, WN, YTV, KG, SPREAD>), dim3(grid), dim3(NT), 0, s, a.q, \
+  hipLaunchKernelGGL((k_gemm_fast<BM, BN, WM, WN, YTV, KG>), dim3(grid), dim3(NT), 0, s, a.q, \
                      a.sx, a.M, a.packed, a.scale, a.per_row, a.N, a.K, a.Y)
   if (a.ydt == TQ_F32) TQ_GEMM_FAST(TQ_F32);
   else if (a.ydt == TQ_BF16) TQ_GEMM_FAST(TQ_BF16);
@@ -865,9 +855,10 @@ hipError_t gemm_fast_dispatch(const GemmArgs& a, hipStream_t s) {
   const int64_t tw = tiles(kWBM, kWBN), last = tw % cus;
   if (tw >= cus && (last == 0 || 2 * last >= cus) && a.K % (2 * kWBK) == 0)
     return gemm_wide_launch(a, s);
-  // 256 x 128 tiles from one per CU on (measured: 2048 x 4096 runs 7% faster
-  // on 256 of them than on 512 tiles of 128 x 128)
-  if (tiles(256, 128) >= cus) return gemm_fast_launch<256, 128, 4, 2, 1, false>(a, s);
+  // 256 x 128 tiles (four waves of 128 x 64) from one per CU on (measured:
+  // 2048 x 4096 runs 7% faster on 256 of them than on 512 tiles of
+  // 128 x 128; eight waves of 64 x 64 per tile measured 3% slower)
+  if (tiles(256, 128) >= cus) return gemm_fast_launch<256, 128, 2, 2>(a, s);
   if (tiles(128, 128) >= kEnough) return gemm_fast_launch<128, 128, 2, 2>(a, s);
   // small grids: two wave groups split each 128-deep stage (needs K % 128)
   if (a.K % 128 == 0) return gemm_fast_launch<128, 64, 4, 1, 2>(a, s);
