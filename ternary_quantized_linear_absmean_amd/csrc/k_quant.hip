@@ -162,6 +162,31 @@ __global__ __launch_bounds__(kNTs) void k_quant_small(const T* __restrict__ X, i
 
 // ---------------------------------------------------------------- FWHT-512
 
+// v from lane l ^ LM: DPP row operations for LM = 1, 2 (quad swaps), 4 (half
+// mirror, then quad reversal) and 8 (row mirror, then half mirror), a
+// swizzle for 16 and a permute through LDS for 32.  The moves leave the
+// values untouched.
+template <int LM>
+__device__ inline float lane_xor(float v) {
+  const int i = __float_as_int(v);
+  if constexpr (LM == 1) return __int_as_float(dpp_get<0xB1>(i));
+  else if constexpr (LM == 2) return __int_as_float(dpp_get<0x4E>(i));
+  else if constexpr (LM == 4) return __int_as_float(dpp_get<0x1B>(dpp_get<0x141>(i)));
+  else if constexpr (LM == 8) return __int_as_float(dpp_get<0x141>(dpp_get<0x140>(i)));
+  else if constexpr (LM == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x401F));
+  else return __shfl_xor(v, LM, kWave);
+}
+
+template <int LM>
+__device__ inline void fwht_lane_stage(float (&v)[8], int lane) {
+  const bool upper = (lane & LM) != 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float other = lane_xor<LM>(v[e]);
+    v[e] = upper ? (other - v[e]) : (v[e] + other);
+  }
+}
+
 // In-place FWHT of one 512-block held by a wave: lane l holds elements
 // 8l .. 8l+7.  Stages h = 1, 2, 4 pair elements inside a lane; stages
 // h = 8 .. 256 pair lane l with lane l ^ (h/8).  The lower index of a pair
@@ -179,15 +204,12 @@ __device__ inline void fwht512_wave(float (&v)[8]) {
     }
   }
   const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-  for (int lm = 1; lm < kWave; lm <<= 1) {
-    const bool upper = (lane & lm) != 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float other = __shfl_xor(v[e], lm, kWave);
-      v[e] = upper ? (other - v[e]) : (v[e] + other);
-    }
-  }
+  fwht_lane_stage<1>(v, lane);
+  fwht_lane_stage<2>(v, lane);
+  fwht_lane_stage<4>(v, lane);
+  fwht_lane_stage<8>(v, lane);
+  fwht_lane_stage<16>(v, lane);
+  fwht_lane_stage<32>(v, lane);
 }
 
 template <typename T, bool VEC>
@@ -232,6 +254,7 @@ __global__ __launch_bounds__(kNT) void k_quant_prologue(
   const int64_t nseg = (K + 511) / 512;
   float v[NB][8];
   float ss = 0.f;
+  // every segment's load goes out before the first one is used
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int64_t seg = wave + kWavesPerBlock * j;
@@ -242,6 +265,11 @@ __global__ __launch_bounds__(kNT) void k_quant_prologue(
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
     }
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int64_t seg = wave + kWavesPerBlock * j;
+    const int64_t base = seg * 512 + 8 * lane;
 #pragma unroll
     for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
     if (gweight != nullptr && seg < nseg) {
