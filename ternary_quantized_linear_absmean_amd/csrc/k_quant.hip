@@ -163,18 +163,37 @@ __global__ __launch_bounds__(kNTs) void k_quant_small(const T* __restrict__ X, i
 // ---------------------------------------------------------------- FWHT-512
 
 // v from lane l ^ LM: DPP row operations for LM = 1, 2 (quad swaps), 4 (half
-// mirror, then quad reversal) and 8 (row mirror, then half mirror), a
-// swizzle for 16 and a permute through LDS for 32.  The moves leave the
-// values untouched.
+// mirror, then quad reversal) and 8 (row mirror, then half mirror);
+// v_permlane16_swap / v_permlane32_swap of v with itself for 16 / 32 (the
+// first result holds, in the upper lane of each pair, the lower one's value,
+// the second result the reverse).  The moves leave the values untouched.
 template <int LM>
 __device__ inline float lane_xor(float v) {
   const int i = __float_as_int(v);
-  if constexpr (LM == 1) return __int_as_float(dpp_get<0xB1>(i));
-  else if constexpr (LM == 2) return __int_as_float(dpp_get<0x4E>(i));
-  else if constexpr (LM == 4) return __int_as_float(dpp_get<0x1B>(dpp_get<0x141>(i)));
-  else if constexpr (LM == 8) return __int_as_float(dpp_get<0x141>(dpp_get<0x140>(i)));
-  else if constexpr (LM == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x401F));
-  else return __shfl_xor(v, LM, kWave);
+  if constexpr (LM == 1) {
+    return __int_as_float(dpp_get<0xB1>(i));
+  } else if constexpr (LM == 2) {
+    return __int_as_float(dpp_get<0x4E>(i));
+  } else if constexpr (LM == 4) {
+    return __int_as_float(dpp_get<0x1B>(dpp_get<0x141>(i)));
+  } else if constexpr (LM == 8) {
+    return __int_as_float(dpp_get<0x141>(dpp_get<0x140>(i)));
+  } else {
+    static_assert(LM == 16 || LM == 32, "lane distance");
+    const unsigned u = static_cast<unsigned>(i);
+    unsigned r0, r1;
+    if constexpr (LM == 16) {
+      const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+      r0 = r[0];
+      r1 = r[1];
+    } else {
+      const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+      r0 = r[0];
+      r1 = r[1];
+    }
+    const bool upper = (threadIdx.x & LM) != 0;
+    return __uint_as_float(upper ? r0 : r1);
+  }
 }
 
 template <int LM>
@@ -292,7 +311,13 @@ __global__ __launch_bounds__(kNT) void k_quant_prologue(
   for (int j = 0; j < NB; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) zmax = fmaxf(zmax, fabsf(v[j][e]));
-  zmax = block_max<kNT>(zmax, sh);
+  // block max of |z| (non-negative: DPP wave maxima, lane 63 holds them)
+  zmax = wave_max_last(zmax);
+  if (lane == kWave - 1) sh[wave] = zmax;
+  __syncthreads();
+  zmax = sh[0];
+#pragma unroll
+  for (int w = 1; w < kWavesPerBlock; ++w) zmax = fmaxf(zmax, sh[w]);
   const float rc = r * (fwht ? kFwhtNorm : 1.f);
   const float eta_true = rc * zmax;
   float eta = fmaxf(eta_true, eps);
