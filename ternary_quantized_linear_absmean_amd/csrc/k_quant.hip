@@ -111,16 +111,18 @@ __global__ __launch_bounds__(kNT) void k_quant_plain(const T* __restrict__ X, in
   if (threadIdx.x == 0) sx[row] = eta / 127.f;
 }
 
-// Few tokens: a token's values are read once.  1024 threads per token, each
-// holding CH chunks of 8 values in registers; wave maxima (DPP) meet in LDS.
-// Same eta, scale and codes as k_quant_plain (the max is exact).
+// A token's values read once: NT threads per token, each holding CH chunks
+// of 8 values in registers; wave maxima (DPP) meet in LDS.  Same eta, scale
+// and codes as k_quant_plain (the max is exact).  Few tokens take 1024
+// threads per token (more waves in flight per token), many tokens 256.
 constexpr int kNTs = 1024;
 
-template <typename T, bool VEC, int CH>
-__global__ __launch_bounds__(kNTs) void k_quant_small(const T* __restrict__ X, int64_t K,
-                                                      float eps, int clamp, float lo, float hi,
-                                                      int8_t* __restrict__ q,
-                                                      float* __restrict__ sx) {
+template <typename T, bool VEC, int CH, int NT = kNTs>
+__global__ __launch_bounds__(NT) void k_quant_small(const T* __restrict__ X, int64_t K,
+                                                    float eps, int clamp, float lo, float hi,
+                                                    int8_t* __restrict__ q,
+                                                    float* __restrict__ sx) {
+  constexpr int kNTs = NT;
   __shared__ float part[kNTs / kWave];
   const int64_t row = blockIdx.x;
   const T* x = X + row * K;
@@ -363,16 +365,17 @@ hipError_t prologue_dispatch(const T* X, int64_t M, int64_t K, const ActParams& 
 
 }  // namespace
 
-template <typename T, bool VEC>
+template <typename T, bool VEC, int NT = kNTs>
 hipError_t quant_small_launch(const T* x, int64_t M, int64_t K, const ActParams& p, int8_t* q,
                               float* sx, hipStream_t s) {
-  const int64_t ch = ((K + 7) / 8 + kNTs - 1) / kNTs;  // chunks per thread
-#define TQ_QSMALL(C)                                                                      \
-  hipLaunchKernelGGL((k_quant_small<T, VEC, C>), dim3(M), dim3(kNTs), 0, s, x, K, p.eps, \
+  const int64_t ch = ((K + 7) / 8 + NT - 1) / NT;  // chunks per thread
+#define TQ_QSMALL(C)                                                                        \
+  hipLaunchKernelGGL((k_quant_small<T, VEC, C, NT>), dim3(M), dim3(NT), 0, s, x, K, p.eps, \
                      p.clamp, p.eta_min, p.eta_max, q, sx)
   if (ch <= 1) TQ_QSMALL(1);
   else if (ch <= 2) TQ_QSMALL(2);
-  else TQ_QSMALL(4);
+  else if (ch <= 4) TQ_QSMALL(4);
+  else TQ_QSMALL(8);
 #undef TQ_QSMALL
   return hipGetLastError();
 }
@@ -395,6 +398,18 @@ hipError_t launch_quant_plain(const void* X, int bf16, int64_t M, int64_t K,
     const float* x = static_cast<const float*>(X);
     return vec ? quant_small_launch<float, true>(x, M, K, p, q, sx, s)
                : quant_small_launch<float, false>(x, M, K, p, q, sx, s);
+  }
+  // many tokens, K up to 8 chunks of 8 per thread of 256: the values stay in
+  // registers between the max and the codes (k_quant_plain reads them twice)
+  if (K <= 8 * 8 * kNT) {
+    if (bf16) {
+      const uint16_t* x = static_cast<const uint16_t*>(X);
+      return vec ? quant_small_launch<uint16_t, true, kNT>(x, M, K, p, q, sx, s)
+                 : quant_small_launch<uint16_t, false, kNT>(x, M, K, p, q, sx, s);
+    }
+    const float* x = static_cast<const float*>(X);
+    return vec ? quant_small_launch<float, true, kNT>(x, M, K, p, q, sx, s)
+               : quant_small_launch<float, false, kNT>(x, M, K, p, q, sx, s);
   }
   if (bf16) {
     const uint16_t* x = static_cast<const uint16_t*>(X);

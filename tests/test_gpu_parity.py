@@ -189,7 +189,8 @@ def test_quant_workloads(name, j, b):
 
 
 @pytest.mark.parametrize("M,K", [(1, 4), (3, 60), (2, 68), (5, 260), (17, 1000), (1, 7),
-                                 (2, 6912), (1, 40000), (16, 32768), (63, 8200), (64, 256)])
+                                 (2, 6912), (1, 40000), (16, 32768), (63, 8200), (64, 256),
+                                 (65, 2050), (100, 16384), (128, 4100), (70, 16392)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_quant_awkward(M, K, dtype):
     X = ti.activations(500 + M + K, M, K, dtype=dtype)
