@@ -514,6 +514,48 @@ def test_bf16_output_is_rounded_fp32_output(M, N, K, tiny):
     np.testing.assert_array_equal(yb, _rne_bf16_bits(y32))
 
 
+def _random_contract_cases(n=24, seed=20261203):
+    # seeded random shapes across every contraction kernel: M log-uniform in
+    # 1..4200, N in 1..7000, K a multiple of 4, 64 or 256 up to 4400 (so the
+    # aligned and unaligned paths, the decode kernels and every GEMM tile are
+    # reached), buffers offset from 16-byte alignment in some cases
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = int(np.exp(rng.uniform(0.0, np.log(4200.0))))
+        N = int(rng.integers(1, 7001))
+        unit = int(rng.choice([4, 64, 256], p=[0.3, 0.3, 0.4]))
+        K = unit * int(rng.integers(1, 4400 // unit + 1))
+        shift = int(rng.choice([0, 0, 0, 1, 4, 8]))
+        gran = str(rng.choice(["tensor", "row"]))
+        cases.append((i, max(M, 1), N, K, shift, gran))
+    return cases
+
+
+@pytest.mark.parametrize("i,M,N,K,shift,gran", _random_contract_cases())
+def test_contract_random_shapes(i, M, N, K, shift, gran):
+    q = ti.random_int8(7000 + i, M, K)
+    w = ti.random_ternary(8000 + i, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(9000 + i, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(9500 + i, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    sc = scale if gran == "row" else scale[:1]
+    # token and weight buffers shifted by `shift` bytes from 16-byte alignment
+    qbuf = torch.zeros(M * K + shift, dtype=torch.int8, device=DEV)
+    qbuf[shift:] = dev(q).reshape(-1)
+    pbuf = torch.zeros(N * K // 4 + shift, dtype=torch.uint8, device=DEV)
+    pbuf[shift:] = dev(packed).reshape(-1)
+    qd, pd = qbuf[shift:].view(M, K), pbuf[shift:].view(N, K // 4)
+    ncols = int(max(1, min(N, 3e8 // max(1, M * K))))
+    cols = np.unique(np.concatenate([np.random.default_rng(i).choice(N, size=min(ncols, N),
+                                                                     replace=False),
+                                     [0, N - 1]]))
+    say(f"contract random #{i} M={M} N={N} K={K} shift={shift} {gran}, {cols.size} columns")
+    fns = [tq.tq_ternary_gemm] + ([tq.tq_ternary_gemv] if M <= 16 else [])
+    for fn in fns:
+        _check_outputs(fn, qd, dev(sx), pd, dev(sc), N, K, gran, q, packed, sc, sx, cols=cols)
+
+
 @pytest.mark.parametrize("mode", ["ternary", "binary"])
 def test_gemm_bitlinear_workload_sampled(mode):
     W, packed, scale = ref_pack("bitlinear", 0, mode)
