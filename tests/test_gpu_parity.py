@@ -1082,6 +1082,51 @@ def test_backward_weight(M, N, K, xdt, dydt, acc):
     _assert_bwd_close(dw, ref, bound, "backward_weight")
 
 
+def _random_bwd_cases(n=16, seed=20261204):
+    # seeded random shapes for both gradients: token counts 1..600, N and K
+    # up to 1200 (K % 4 == 0 for the packed codes; multiples of 8 in about
+    # half the cases, the fast kernels' condition), random dtypes, scale
+    # granularity and accumulate flag
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = int(rng.integers(1, 601))
+        unit = int(rng.choice([4, 8]))
+        N = unit * int(rng.integers(1, 1200 // unit + 1))
+        K = unit * int(rng.integers(1, 1200 // unit + 1))
+        cases.append((i, M, N, K, str(rng.choice(["f32", "bf16"])), str(rng.choice(["f32", "bf16"])),
+                      str(rng.choice(["tensor", "row"])), bool(rng.integers(0, 2))))
+    return cases
+
+
+@pytest.mark.parametrize("i,M,N,K,dt1,dt2,gran,acc", _random_bwd_cases())
+def test_backward_random_shapes(i, M, N, K, dt1, dt2, gran, acc):
+    say(f"backward random #{i} M={M} N={N} K={K} {dt1}/{dt2} {gran} acc={acc}")
+    # input gradient: dY dtype dt1
+    packed, scale, dY = _bwd_inputs(M, N, K, dt1, gran, 7600 + i)
+    ref, bound = _bwd_ref_and_bound(dY, packed, scale, K)
+    base = ti.output_grads(9 + i, M, K) if acc else None
+    out = tq.tq_ternary_backward_input(x_to_device(dY, dt1), dev(packed), dev(scale), K, gran,
+                                       dX=dev(base) if acc else None, accumulate=acc)
+    dx = host(out).astype(np.float64)
+    if acc:
+        dx = dx - base.astype(np.float64)
+        bound = bound + np.abs(ref + base) * 2.0 ** -24
+    _assert_bwd_close(dx, ref, bound, "backward_input random")
+    # weight gradient: X dtype dt1, dY dtype dt2
+    X = ti.activations(7700 + i, M, K, "normal", dt1)
+    dY2 = ti.output_grads(7800 + i, M, N, dt2)
+    ref, bound = _wgt_ref_and_bound(X, dY2, dt1 == dt2 == "f32")
+    base = ti.output_grads(30 + i, N, K) if acc else None
+    out = tq.tq_ternary_backward_weight(x_to_device(X, dt1), x_to_device(dY2, dt2),
+                                        dW=dev(base) if acc else None, accumulate=acc)
+    dw = host(out).astype(np.float64)
+    if acc:
+        dw = dw - base.astype(np.float64)
+        bound = bound + np.abs(ref + base) * 2.0 ** -24
+    _assert_bwd_close(dw, ref, bound, "backward_weight random")
+
+
 def test_backward_weight_single_token_exact_and_empty():
     # one token, X bf16: the split terms of dY * X sum exactly until the
     # last step, which rounds once (faithfully: within one ulp)
