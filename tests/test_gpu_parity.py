@@ -146,6 +146,41 @@ def test_pack_awkward_shapes(N, K, gran, mode):
     _pack_pair(W, gran, mode)
 
 
+def _random_pack_cases(n=12, seed=20261205):
+    # seeded random weights: shapes up to 700 x 2000 (K % 8 == 0 so the 1-bit
+    # form applies), normal, heavy-tailed (Student-t, df 2) or sparse values
+    # with exact zeros, over a random power-of-two magnitude
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        N = int(rng.integers(1, 701))
+        K = 8 * int(rng.integers(1, 251))
+        cases.append((i, N, K, str(rng.choice(["normal", "t2", "sparse"])),
+                      int(rng.integers(-30, 31))))
+    return cases
+
+
+@pytest.mark.parametrize("i,N,K,dist,e", _random_pack_cases())
+def test_pack_random(i, N, K, dist, e):
+    rng = np.random.default_rng(5000 + i)
+    if dist == "normal":
+        W = rng.standard_normal((N, K))
+    elif dist == "t2":
+        W = rng.standard_t(2.0, (N, K))
+    else:
+        W = rng.standard_normal((N, K)) * (rng.random((N, K)) < 0.3)
+    W = (W * 2.0 ** e).astype(np.float32)
+    say(f"pack random #{i} {N}x{K} {dist} 2^{e}")
+    for gran in ("tensor", "row"):
+        for mode in ("ternary", "binary"):
+            _pack_pair(W, gran, mode)
+    for gran in ("tensor", "row"):
+        p1, s1 = tq.tq_pack_binary1(dev(W), gran)
+        pr, sr = oracle.pack_binary1(W, gran)
+        np.testing.assert_array_equal(f32_bits(host(s1)), f32_bits(sr))
+        np.testing.assert_array_equal(host(p1), pr)
+
+
 def test_pack_edge_values():
     # zeros (gamma = eps, all zero codes), signed zeros, exact half-gamma ties
     say("pack edge values")
