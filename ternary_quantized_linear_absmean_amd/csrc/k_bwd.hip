@@ -471,6 +471,9 @@ __host__ __device__ constexpr int planes_of(int dt) { return dt == 0 ? 3 : 1; }
 #ifndef TQ_WGT_WIDE
 #define TQ_WGT_WIDE 1
 #endif
+#ifndef TQ_WGT_SPREAD
+#define TQ_WGT_SPREAD 1
+#endif
 // dW rows per tile: 256 with two bf16 operands (64 x 64 per wave, half the
 // LDS fragment reads per MFMA of a 32 x 64 wave tile), else 128
 __host__ __device__ constexpr int wgt_gn(int da, int db) {
@@ -630,6 +633,51 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
       }
     }
   };
+  // the same work in pieces (without roles): unit `uid` < U*PRA is A unit
+  // (uid / PRA, uid % PRA), the rest B units; row i of a unit is one load
+  constexpr int NU = kRoles ? 0 : U * PRA + U;
+  auto load_row = [&](int64_t st, Regs& r, int uid, int i) {
+    if constexpr (!kRoles) {
+      const uint32_t sa = static_cast<uint32_t>(N * ESA), sb = static_cast<uint32_t>(K * ESB);
+      if (uid < U * PRA) {
+        const int u = uid / PRA, pb = uid % PRA;
+        auto& v = r.a[uid];
+        const uint32_t off = aoff + 64 * u * sa + 128 * pb * ESA + i * sa;
+        const int so = static_cast<int>(st * kGM * N * ESA);
+        if constexpr (ESA == 4) {
+          const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ra, off, so, 0));
+          v[i][0] = t.x;
+          v[i][ESA / 2 - 1] = t.y;
+        } else {
+          v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(ra, off, so, 0);
+        }
+      } else {
+        const int u = uid - U * PRA;
+        auto& v = r.b[u];
+        const uint32_t off = boff + 64 * u * sb + i * sb;
+        const int so = static_cast<int>(st * kGM * K * ESB);
+        if constexpr (ESB == 4) {
+          const uint2 t = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rb, off, so, 0));
+          v[i][0] = t.x;
+          v[i][ESB / 2 - 1] = t.y;
+        } else {
+          v[i][0] = __builtin_amdgcn_raw_buffer_load_b32(rb, off, so, 0);
+        }
+      }
+    }
+  };
+  auto put_one = [&](int buf, Regs& r, int uid) {
+    if constexpr (!kRoles) {
+      uint8_t* st = lds + buf * kStage;
+      if (uid < U * PRA) {
+        const int u = uid / PRA, pb = uid % PRA;
+        put_unit(st + 2 * u * kStep + pb * 128 * 64, kAPlane, EA{}, r.a[uid]);
+      } else {
+        const int u = uid - U * PRA;
+        put_unit(st + 2 * u * kStep + PA * kAPlane, kGPlane, EB{}, r.b[u]);
+      }
+    }
+  };
 
   const int fr = lane & 15, fg = lane >> 4;
   int ard[FA], brd[4];
@@ -645,11 +693,36 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
     for (int b = 0; b < 4; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
   const int64_t ns = (M + kGM - 1) / kGM;
+  // without roles, the loads of stage s+2 and the LDS moves of stage s+1
+  // are spread over the MFMA groups of stage s (one group = FA x 4 MFMAs)
+  constexpr bool kSpread = !kRoles && TQ_WGT_SPREAD;
+  constexpr int NC = [] {  // (pa, pb) terms per k step
+    int n = 0;
+    for (int pa = 0; pa < PA; ++pa)
+      for (int pb = 0; pb < PB; ++pb) n += pa + pb <= 2;
+    return n;
+  }();
+  constexpr int NG = KS * NC * FA;                   // MFMA groups per stage
+  constexpr int NL = NU * 8;                         // loads per stage
   auto step = [&](int64_t s, Regs& r_next, Regs& r_far, auto guard) {
     constexpr bool GUARD = decltype(guard)::value;
     const int buf = static_cast<int>(s & 1);
-    if (!GUARD || s + 2 < ns) load_stage(s + 2, r_far);
+    const bool do_load = !GUARD || s + 2 < ns, do_store = !GUARD || s + 1 < ns;
+    if (!kSpread && do_load) load_stage(s + 2, r_far);
     __builtin_amdgcn_sched_barrier(0);
+    int g = 0;
+    auto pieces = [&]() {
+      if constexpr (kSpread) {
+#pragma unroll
+        for (int q = g * NL / NG; q < (g + 1) * NL / NG; ++q)
+          if (do_load) load_row(s + 2, r_far, q / 8, q % 8);
+#pragma unroll
+        for (int q = g * NU / NG; q < (g + 1) * NU / NG; ++q)
+          if (do_store) put_one(buf ^ 1, r_next, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      ++g;
+    };
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint8_t* st = lds + buf * kStage + ks * kStep;
@@ -672,15 +745,17 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
           const int pb = lvl - pa;
           if (pb < 0 || pb >= PB) continue;
 #pragma unroll
-          for (int a = 0; a < FA; ++a)
+          for (int a = 0; a < FA; ++a) {
 #pragma unroll
             for (int b = 0; b < 4; ++b)
               acc[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[pa][a], bv[pb][b],
                                                                   acc[a][b], 0, 0, 0);
+            pieces();
+          }
         }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (!GUARD || s + 1 < ns) store_stage(buf ^ 1, r_next);
+    if (!kSpread && do_store) store_stage(buf ^ 1, r_next);
     __syncthreads();
   };
   using Free = std::false_type;
