@@ -63,6 +63,9 @@ constexpr int kPlane = kBM * kArow;       // bytes of one bf16 plane
 constexpr int kWrow = 40;                 // bytes of one transposed code row
 constexpr int kWbytes = (kBK / 4) * kWrow;
 
+#ifndef TQ_BWD_SPREAD
+#define TQ_BWD_SPREAD 1
+#endif
 #ifndef TQ_BWD_KS3
 #define TQ_BWD_KS3 2
 #endif
@@ -235,9 +238,10 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
       }
     }
   };
-  auto store_stage = [&](int buf, int64_t kt, Regs& r, Gam& g) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
+  // staging of step ks of a stage (and, with word-loaded codes, ks == KS:
+  // the transposed codes of the whole stage)
+  auto put_step = [&](int buf, int64_t kt, Regs& r, Gam& g, int ks) {
+    if (ks < KS) {
       uint8_t* st = lds + buf * kStage + ks * kStep;
       // the loaded values enter here: without this the compiler combines the
       // code bytes right after their loads and waits for them a step early
@@ -271,8 +275,7 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
       if constexpr (!kW4)
         *reinterpret_cast<uint32_t*>(st + wst) =
             r.w[ks][0] | (r.w[ks][1] << 8) | (r.w[ks][2] << 16) | (r.w[ks][3] << 24);
-    }
-    if constexpr (kW4) {
+    } else if constexpr (kW4) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(r.w[0][i]));
       // out[s] holds column byte 4d+s of rows 4g..4g+3
@@ -280,6 +283,32 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
       uint8_t* st = lds + buf * kStage;
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4) *reinterpret_cast<int*>(st + wst + s4 * kWrow) = t[s4];
+    }
+  };
+  constexpr int NPUT = KS + (kW4 ? 1 : 0);  // staging pieces per stage
+  auto store_stage = [&](int buf, int64_t kt, Regs& r, Gam& g) {
+#pragma unroll
+    for (int q = 0; q < NPUT; ++q) put_step(buf, kt, r, g, q);
+  };
+  // load q of a stage: the dY loads first (KS x YL), then the code loads
+  // (four words, or KS x 4 bytes)
+  constexpr int NLD = KS * YL + (kW4 ? 4 : KS * 4);
+  auto load_one = [&](int64_t kt, Regs& r, int q) {
+    if (q < KS * YL) {
+      const int ks = q / YL, i = q % YL;
+      const int so = static_cast<int>((kt * KS + ks) * kBN * ES);
+      r.y[ks][i] =
+          __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ry, yoff + 16 * i, so, 0));
+    } else if constexpr (kW4) {
+      const int i = q - KS * YL;
+      const int sw = static_cast<int>(kt * KS * kBN * rowbytes);
+      r.w[0][i] = __builtin_amdgcn_raw_buffer_load_b32(
+          rw, woff + static_cast<uint32_t>(i * rowbytes), sw, 0);
+    } else {
+      const int ks = (q - KS * YL) / 4, i = (q - KS * YL) % 4;
+      const int sw = static_cast<int>((kt * KS + ks) * kBN * rowbytes);
+      r.w[ks][i] = static_cast<uint32_t>(__builtin_amdgcn_raw_buffer_load_b8(
+          rw, woff + static_cast<uint32_t>(i * rowbytes), sw, 0));
     }
   };
 
@@ -296,13 +325,31 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
   // for all loads in flight); loads past the last stage read zeros or data
   // that is never used (columns past N are zeroed on staging), and a store of
   // stage nk goes to the LDS half that no later stage reads.
+  // With TQ_BWD_SPREAD the far loads and the staging are issued in pieces
+  // after each group of four MFMAs instead of in one block each.
+  constexpr bool kSpread = TQ_BWD_SPREAD;
+  constexpr int NG = KS * P * 4;  // MFMA groups per stage
   auto step = [&](int64_t kt, Regs& r_next, Regs& r_far, auto guard) {
     constexpr bool GUARD = decltype(guard)::value;
     const int buf = static_cast<int>(kt & 1);
+    const bool do_load = !GUARD || kt + 2 < nk, do_store = !GUARD || kt + 1 < nk;
     Gam g;
     if (!GUARD || kt + 1 < nk) load_gamma(kt + 1, g);
-    if (!GUARD || kt + 2 < nk) load_stage(kt + 2, r_far);
+    if (!kSpread && do_load) load_stage(kt + 2, r_far);
     __builtin_amdgcn_sched_barrier(0);
+    int grp = 0;
+    auto pieces = [&]() {
+      if constexpr (kSpread) {
+#pragma unroll
+        for (int q = grp * NLD / NG; q < (grp + 1) * NLD / NG; ++q)
+          if (do_load) load_one(kt + 2, r_far, q);
+#pragma unroll
+        for (int q = grp * NPUT / NG; q < (grp + 1) * NPUT / NG; ++q)
+          if (do_store) put_step(buf ^ 1, kt + 1, r_next, g, q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      ++grp;
+    };
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const uint8_t* st = lds + buf * kStage + ks * kStep;
@@ -321,13 +368,15 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_input(
 #pragma unroll
       for (int p = P - 1; p >= 0; --p)  // smallest terms first
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
+        for (int a = 0; a < 4; ++a) {
 #pragma unroll
           for (int f = 0; f < 4; ++f)
             acc[a][f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[p][a], b[f], acc[a][f], 0, 0, 0);
+          pieces();
+        }
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (!GUARD || kt + 1 < nk) store_stage(buf ^ 1, kt + 1, r_next, g);
+    if (!kSpread && do_store) store_stage(buf ^ 1, kt + 1, r_next, g);
     __syncthreads();
   };
   using Free = std::false_type;
@@ -633,11 +682,20 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
       }
     }
   };
-  // the same work in pieces (without roles): unit `uid` < U*PRA is A unit
-  // (uid / PRA, uid % PRA), the rest B units; row i of a unit is one load
-  constexpr int NU = kRoles ? 0 : U * PRA + U;
+  // the same work in pieces: with roles, one unit per thread; without,
+  // unit `uid` < U*PRA is A unit (uid / PRA, uid % PRA), the rest B units.
+  // Row i of a unit is one load.
+  constexpr int NU = kRoles ? 1 : U * PRA + U;
   auto load_row = [&](int64_t st, Regs& r, int uid, int i) {
-    if constexpr (!kRoles) {
+    if constexpr (kRoles) {
+      const int64_t rl = role_a ? N : K;
+      const uint32_t off = (role_a ? aoff : boff) + i * static_cast<uint32_t>(rl * 4);
+      const uint2 t = __builtin_bit_cast(
+          uint2, __builtin_amdgcn_raw_buffer_load_b64(role_a ? ra : rb, off,
+                                                      static_cast<int>(st * kGM * rl * 4), 0));
+      r.a[0][i][0] = t.x;
+      r.a[0][i][1] = t.y;
+    } else {
       const uint32_t sa = static_cast<uint32_t>(N * ESA), sb = static_cast<uint32_t>(K * ESB);
       if (uid < U * PRA) {
         const int u = uid / PRA, pb = uid % PRA;
@@ -667,7 +725,10 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
     }
   };
   auto put_one = [&](int buf, Regs& r, int uid) {
-    if constexpr (!kRoles) {
+    if constexpr (kRoles) {
+      uint8_t* st = lds + buf * kStage;
+      put_unit(st + (role_a ? 0 : PA * kAPlane), role_a ? kAPlane : kGPlane, EA{}, r.a[0]);
+    } else {
       uint8_t* st = lds + buf * kStage;
       if (uid < U * PRA) {
         const int u = uid / PRA, pb = uid % PRA;
@@ -693,9 +754,9 @@ __global__ __launch_bounds__(kNT, 1) void k_bwd_weight(
     for (int b = 0; b < 4; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
   const int64_t ns = (M + kGM - 1) / kGM;
-  // without roles, the loads of stage s+2 and the LDS moves of stage s+1
-  // are spread over the MFMA groups of stage s (one group = FA x 4 MFMAs)
-  constexpr bool kSpread = !kRoles && TQ_WGT_SPREAD;
+  // the loads of stage s+2 and the LDS moves of stage s+1 are spread over
+  // the MFMA groups of stage s (one group = 4 MFMAs)
+  constexpr bool kSpread = TQ_WGT_SPREAD;
   constexpr int NC = [] {  // (pa, pb) terms per k step
     int n = 0;
     for (int pa = 0; pa < PA; ++pa)
