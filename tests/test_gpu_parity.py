@@ -518,6 +518,25 @@ def test_gemm_wide_tiles(M, N, K):
                        q, packed, sc, sx, cols=cols)
 
 
+@pytest.mark.parametrize("M,N,K", [(256, 4096, 4096), (200, 3000, 512), (33, 8000, 768),
+                                   (130, 260, 256)])
+def test_gemm_small_grid_tiles(M, N, K):
+    # at most one 64 x 64 tile per CU: the four-K-group 64 x 64 tile, ragged
+    # in M and N; all tokens, sampled columns including tile edges
+    q = ti.random_int8(M + 3 * K, M, K)
+    w = ti.random_ternary(N + 3 * K, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(N + 5, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(M + 6, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    cols = np.unique(np.concatenate([_sample_cols(N, M + N, 48),
+                                     [31, 32, 63, 64, 65, 127, 128, N - 2, N - 1]]))
+    cols = cols[cols < N]
+    say(f"gemm small grid M={M} N={N} K={K}")
+    for gran, sc in (("row", scale), ("tensor", scale[:1])):
+        _check_outputs(tq.tq_ternary_gemm, dev(q), dev(sx), dev(packed), dev(sc), N, K, gran,
+                       q, packed, sc, sx, cols=cols)
+
+
 def _rne_bf16_bits(y32):
     # round-to-nearest-even of finite fp32 values to bf16, on the bit pattern
     u = np.ascontiguousarray(y32, np.float32).view(np.uint32).astype(np.uint64)
