@@ -225,8 +225,7 @@ __global__ void k_gamma_exact_final(const uint32_t* __restrict__ flag,
                    kGammaEps);
 }
 
-// 16 weights -> one 32-bit word per step when VEC (W 16-byte and packed
-// 4-byte aligned); otherwise one byte per step.
+// One packed byte (four weights) per lane and step; VEC: W 16-byte aligned.
 template <bool VEC>
 __global__ __launch_bounds__(kNT) void k_ternarize_pack(const float* __restrict__ W,
                                                         int64_t nbytes, int binary, float hf,
@@ -235,20 +234,21 @@ __global__ __launch_bounds__(kNT) void k_ternarize_pack(const float* __restrict_
   const float h = scale[0] * hf;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * kNT;
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * kNT + threadIdx.x;
-  int64_t done = 0;
+  int64_t j = tid;
   if (VEC) {
-    const int64_t nwords = nbytes / 4;
-    for (int64_t i = tid; i < nwords; i += stride) {
-      uint32_t word = 0u;
+    // one byte (four weights, one 16-byte load) per lane and step: a wave's
+    // load reads 1 KiB of consecutive weights; four loads in flight
+    for (; j + 3 * stride < nbytes; j += 4 * stride) {
+      float4 v[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        word |= byte_of(load4<true>(W, 4 * i + b), h, binary) << (8 * b);
-      reinterpret_cast<uint32_t*>(packed)[i] = word;
+      for (int u = 0; u < 4; ++u) v[u] = load4<true>(W, j + u * stride);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        packed[j + u * stride] = static_cast<uint8_t>(byte_of(v[u], h, binary));
     }
-    done = nwords * 4;
   }
-  for (int64_t j = done + tid; j < nbytes; j += stride)
-    packed[j] = static_cast<uint8_t>(byte_of(load4<false>(W, j), h, binary));
+  for (; j < nbytes; j += stride)
+    packed[j] = static_cast<uint8_t>(byte_of(load4<VEC>(W, j), h, binary));
 }
 
 // 1-bit sign packing of binary weights: bit t of byte j is 1 when weight
@@ -282,8 +282,10 @@ __global__ __launch_bounds__(kNT) void k_sign_pack(const float* __restrict__ W, 
 // --------------------------------------------------------------- per row
 
 // BITS 2: ternary or binary codes, four per byte; BITS 1: signs, eight per
-// byte (binary weights only).
-template <bool VEC, int BITS>
+// byte (binary weights only).  R > 0 (BITS 2, K <= 4 R kNT): each thread keeps
+// its R four-weight groups of the row in registers, so the row is read from
+// memory once for the sum, the exact mean and the codes.
+template <bool VEC, int BITS, int R = 0>
 __global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
                                                    int64_t K, int binary, float hf, double thr,
                                                    uint8_t* __restrict__ packed,
@@ -297,12 +299,29 @@ __global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
   uint8_t* out = packed + row * (K * BITS / 8);
   const int64_t nb = K / 4;
   double acc = 0.0;
-  for (int64_t j = threadIdx.x; j < nb; j += kNT) {
-    const float4 v = load4<VEC>(w, j);
-    acc += fabs(static_cast<double>(v.x));
-    acc += fabs(static_cast<double>(v.y));
-    acc += fabs(static_cast<double>(v.z));
-    acc += fabs(static_cast<double>(v.w));
+  float4 rv[R > 0 ? R : 1];
+  if constexpr (R > 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t j = threadIdx.x + int64_t{kNT} * r;
+      rv[r] = j < nb ? load4<VEC>(w, j) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {  // the same order as the loop below
+      if (threadIdx.x + int64_t{kNT} * r >= nb) break;
+      acc += fabs(static_cast<double>(rv[r].x));
+      acc += fabs(static_cast<double>(rv[r].y));
+      acc += fabs(static_cast<double>(rv[r].z));
+      acc += fabs(static_cast<double>(rv[r].w));
+    }
+  } else {
+    for (int64_t j = threadIdx.x; j < nb; j += kNT) {
+      const float4 v = load4<VEC>(w, j);
+      acc += fabs(static_cast<double>(v.x));
+      acc += fabs(static_cast<double>(v.y));
+      acc += fabs(static_cast<double>(v.z));
+      acc += fabs(static_cast<double>(v.w));
+    }
   }
   const double S = block_sum<kNT>(acc, sh);
   if (threadIdx.x == 0) {
@@ -314,12 +333,23 @@ __global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
   if (near_sh) {  // block-uniform
     lb[threadIdx.x] = 0ull;
     __syncthreads();
-    for (int64_t j = threadIdx.x; j < nb; j += kNT) {
-      const float4 v = load4<VEC>(w, j);
-      bin_add(lb, v.x);
-      bin_add(lb, v.y);
-      bin_add(lb, v.z);
-      bin_add(lb, v.w);
+    if constexpr (R > 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        if (threadIdx.x + int64_t{kNT} * r >= nb) break;
+        bin_add(lb, rv[r].x);
+        bin_add(lb, rv[r].y);
+        bin_add(lb, rv[r].z);
+        bin_add(lb, rv[r].w);
+      }
+    } else {
+      for (int64_t j = threadIdx.x; j < nb; j += kNT) {
+        const float4 v = load4<VEC>(w, j);
+        bin_add(lb, v.x);
+        bin_add(lb, v.y);
+        bin_add(lb, v.z);
+        bin_add(lb, v.w);
+      }
     }
     __syncthreads();
     if (threadIdx.x == 0)
@@ -330,7 +360,13 @@ __global__ __launch_bounds__(kNT) void k_pack_rows(const float* __restrict__ W,
   const float g = g_sh;
   if (threadIdx.x == 0) scale[row] = g;
   const float h = g * hf;
-  if (BITS == 2) {
+  if constexpr (BITS == 2 && R > 0) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int64_t j = threadIdx.x + int64_t{kNT} * r;
+      if (j < nb) out[j] = static_cast<uint8_t>(byte_of(rv[r], h, binary));
+    }
+  } else if constexpr (BITS == 2) {
     for (int64_t j = threadIdx.x; j < nb; j += kNT)
       out[j] = static_cast<uint8_t>(byte_of(load4<VEC>(w, j), h, binary));
   } else {
@@ -565,6 +601,15 @@ hipError_t launch_pack_rows(const float* W, int64_t N, int64_t K, tq_wmode mode,
   if (bits == 1) {
     if (vec) TQ_PACK_ROWS(true, 1);
     else TQ_PACK_ROWS(false, 1);
+  } else if (per_thread <= 8) {  // the row fits in registers
+#define TQ_PACK_ROWS_R(V, RV)                                                                   \
+  hipLaunchKernelGGL((k_pack_rows<V, 2, RV>), dim3(N), dim3(kNT), 0, s, W, K, binary, hf, thr, \
+                     packed, scale)
+    if (per_thread <= 1) { if (vec) TQ_PACK_ROWS_R(true, 1); else TQ_PACK_ROWS_R(false, 1); }
+    else if (per_thread <= 2) { if (vec) TQ_PACK_ROWS_R(true, 2); else TQ_PACK_ROWS_R(false, 2); }
+    else if (per_thread <= 4) { if (vec) TQ_PACK_ROWS_R(true, 4); else TQ_PACK_ROWS_R(false, 4); }
+    else { if (vec) TQ_PACK_ROWS_R(true, 8); else TQ_PACK_ROWS_R(false, 8); }
+#undef TQ_PACK_ROWS_R
   } else {
     if (vec) TQ_PACK_ROWS(true, 2);
     else TQ_PACK_ROWS(false, 2);
