@@ -115,6 +115,19 @@ def _f32(bits):
     return np.array([bits], np.uint32).view(np.float32)[0]
 
 
+@pytest.mark.parametrize("N,K", [(3, 4100), (5, 6148), (3, 8192), (2, 8196), (4, 12000)])
+def test_pack_rows_long_rows_and_ties(N, K):
+    # per-row packing where a row's groups of four fill up to eight per
+    # thread (K <= 8192) and past that; rows whose mean is an fp32 midpoint
+    # take the exact-mean path in both
+    W = ti.normal_weights(300 + N + K, N, K)
+    tie_up = np.array([1.0, 1.0, _f32(0x3F800001), 2.0**-60], np.float32)
+    W[N // 2] = np.tile(tie_up, K // 4)
+    say(f"pack rows long {N}x{K}")
+    for mode in ("ternary", "binary"):
+        _pack_pair(W, "row", mode)
+
+
 def test_pack_gamma_exact_fallback():
     # mean exactly on / just beyond an fp32 midpoint: the fp64 sum cannot
     # decide, the exact integer path must (tensor and row granularity)
