@@ -42,6 +42,55 @@ constexpr int kBK = 64;
 constexpr int kLD = kBK + 16;  // LDS row stride in bytes
 constexpr int kXcds = 8;
 
+// Tile of workgroup `bid` for the fast and wide kernels.  Workgroup ids are
+// handed to the eight XCDs round-robin (ids congruent mod 8 share an XCD and
+// its L2), so XCD x takes a contiguous share of the tiles in an order that
+// walks gm token-row tiles fastest inside each column: its share is a patch
+// of about gm token-row slabs by T/(8 gm) weight-column slabs, and each L2
+// streams only that patch's operands instead of every weight column.  The
+// map is a bijection of [0, T) onto the tiles.
+__device__ inline void xcd_tile(int64_t bid, int64_t tiles_m, int64_t tiles_n, int64_t gm,
+                                int64_t& tm, int64_t& tn) {
+  const int64_t T = tiles_m * tiles_n;
+  const int64_t x = bid % kXcds, li = bid / kXcds;
+  const int64_t per = T / kXcds, extra = T % kXcds;
+  const int64_t t = x * per + (x < extra ? x : extra) + li;
+  const int64_t g = t / (gm * tiles_n);            // group of gm token-row tiles
+  const int64_t m_first = g * gm;
+  const int64_t rows = tiles_m - m_first < gm ? tiles_m - m_first : gm;
+  const int64_t r = t - g * gm * tiles_n;
+  tm = m_first + r % rows;
+  tn = r / rows;
+}
+
+// Group size for xcd_tile: the gm in 1..min(tiles_m, 16) whose map gives the
+// eight XCDs the fewest operand bytes per K step in all (an XCD's share
+// counts gm-row token slabs at BM bytes and weight-column slabs at BN / 4
+// bytes; a share that spans two groups counts the slabs of each piece).
+inline int64_t xcd_group_m(int64_t tiles_m, int64_t tiles_n, int BM, int BN) {
+  const int64_t T = tiles_m * tiles_n, per = T / kXcds, extra = T % kXcds;
+  int64_t best = 1, best_cost = INT64_MAX;
+  for (int64_t g = 1; g <= tiles_m && g <= 16; ++g) {
+    int64_t cost = 0;
+    for (int64_t x = 0; x < kXcds; ++x) {
+      int64_t t = x * per + (x < extra ? x : extra);
+      const int64_t end = t + per + (x < extra ? 1 : 0);
+      while (t < end) {  // one piece per group the share touches
+        const int64_t grp = t / (g * tiles_n), first = grp * g * tiles_n;
+        const int64_t rows = tiles_m - grp * g < g ? tiles_m - grp * g : g;
+        const int64_t stop = first + rows * tiles_n < end ? first + rows * tiles_n : end;
+        const int64_t r0 = t - first, r1 = stop - first;
+        const int64_t nm = r1 - r0 >= rows ? rows : r1 - r0;
+        const int64_t nn = (r1 - 1) / rows - r0 / rows + 1;
+        cost += nm * BM + nn * (BN / 4);
+        t = stop;
+      }
+    }
+    if (cost < best_cost) { best_cost = cost; best = g; }
+  }
+  return best;
+}
+
 // Epilogue of a wave holding FM x FN accumulators of the 32x32 MFMA, whose
 // top-left output is (mb, nb).  D layout: lane l holds column l%32 and rows
 // 8*(v/4) + 4*(l/32) + v%4 for v = 0..15.  y = acc * (gamma * sx) in fp32,
@@ -633,20 +682,23 @@ template <int BM, int BN, int WM, int WN, int YT, int KG>
 __global__ __launch_bounds__(WM* WN* KG* kWave, WM* WN* KG >= 16 ? 1 : 2) void k_gemm_fast(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
-    int64_t N, int64_t K, void* __restrict__ Y) {
+    int64_t N, int64_t K, void* __restrict__ Y, int64_t gm) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[fast_lds_size<BM, BN, WM, WN, KG>()];
-  const int64_t tiles_m = (M + BM - 1) / BM;
-  gemm_fast_tile<BM, BN, WM, WN, YT, KG>(q, sx, M, packed, scale, per_row, N, K, Y,
-                                         blockIdx.x % tiles_m, blockIdx.x / tiles_m, lds);
+  int64_t tm, tn;
+  xcd_tile(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, gm, tm, tn);
+  gemm_fast_tile<BM, BN, WM, WN, YT, KG>(q, sx, M, packed, scale, per_row, N, K, Y, tm, tn,
+                                         lds);
 }
 
 template <int BM, int BN, int WM, int WN, int KG = 1>
 hipError_t gemm_fast_launch(const GemmArgs& a, hipStream_t s) {
-  const int64_t grid = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  const int64_t grid = tiles_m * tiles_n;
+  const int64_t gm = xcd_group_m(tiles_m, tiles_n, BM, BN);
   constexpr int NT = WM * WN * KG * kWave;
 #define TQ_GEMM_FAST(YTV)                                                                      \
   hipLaunchKernelGGL((k_gemm_fast<BM, BN, WM, WN, YTV, KG>), dim3(grid), dim3(NT), 0, s, a.q, \
-                     a.sx, a.M, a.packed, a.scale, a.per_row, a.N, a.K, a.Y)
+                     a.sx, a.M, a.packed, a.scale, a.per_row, a.N, a.K, a.Y, gm)
   if (a.ydt == TQ_F32) TQ_GEMM_FAST(TQ_F32);
   else if (a.ydt == TQ_BF16) TQ_GEMM_FAST(TQ_BF16);
   else TQ_GEMM_FAST(TQ_I32);
@@ -673,7 +725,7 @@ template <int YT>
 __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
-    int64_t N, int64_t K, void* __restrict__ Y) {
+    int64_t N, int64_t K, void* __restrict__ Y, int64_t gm) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kWStage];
   constexpr int FM = 4, FN = 4;
   constexpr int CA = kWBM * (kWBK / 16) / kWNT;  // 8 activation chunks per thread
@@ -683,8 +735,9 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int wm = wave / 2, wn = wave % 2;
-  const int64_t tiles_m = (M + kWBM - 1) / kWBM;
-  const int64_t m0 = (blockIdx.x % tiles_m) * kWBM, n0 = (blockIdx.x / tiles_m) * kWBN;
+  int64_t tm, tn;
+  xcd_tile(blockIdx.x, (M + kWBM - 1) / kWBM, (N + kWBN - 1) / kWBN, gm, tm, tn);
+  const int64_t m0 = tm * kWBM, n0 = tn * kWBN;
   const int64_t rowbytes = K >> 2;
   const int fr = lane & 31, kg = lane >> 5;
 
@@ -835,10 +888,12 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
 }
 
 hipError_t gemm_wide_launch(const GemmArgs& a, hipStream_t s) {
-  const int64_t grid = ((a.M + kWBM - 1) / kWBM) * ((a.N + kWBN - 1) / kWBN);
+  const int64_t tiles_m = (a.M + kWBM - 1) / kWBM, tiles_n = (a.N + kWBN - 1) / kWBN;
+  const int64_t grid = tiles_m * tiles_n;
+  const int64_t gm = xcd_group_m(tiles_m, tiles_n, kWBM, kWBN);
 #define TQ_GEMM_WIDE(YTV)                                                                   \
   hipLaunchKernelGGL((k_gemm_wide<YTV>), dim3(grid), dim3(kWNT), 0, s, a.q, a.sx, a.M,      \
-                     a.packed, a.scale, a.per_row, a.N, a.K, a.Y)
+                     a.packed, a.scale, a.per_row, a.N, a.K, a.Y, gm)
   if (a.ydt == TQ_F32) TQ_GEMM_WIDE(TQ_F32);
   else if (a.ydt == TQ_BF16) TQ_GEMM_WIDE(TQ_BF16);
   else TQ_GEMM_WIDE(TQ_I32);
