@@ -9,7 +9,8 @@ from .tq_oracle import (absmean_scale, absmean_scales, binarize, contract,
                         exact_fraction_mean, fwht512, fwht_block,
                         hadamard_matrix, pack_codes, pack_ternary,
                         packed_bytes, quant_act_int8, rms_factor,
-                        rmsnorm_fwht_quant, rmsnorm_fwht_quant_literal,
+                        mean_of_squares, rmsnorm, bitlinear_prologue,
+                        bitlinear_prologue_fp64, BITLINEAR_BOUNDS,
                         round_rational_to_f32, ternarize, ternary_linear,
                         unpack_codes, bf16_round_from_f64, FWHT_NORM,
                         packed1_bytes, pack_signs, unpack_signs, pack_binary1,

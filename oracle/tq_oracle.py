@@ -55,6 +55,9 @@ in the design notes):
 * Activations: per-token eta = max|x| floored at 1e-6, optional clamp to
   [eta_min, eta_max]; s = fp32(127/eta); q = clamp(rint(fp32(x*s)), -127, 127);
   the dequantisation scale returned is sx = fp32(eta/127).
+* RMSNorm's mean of squares is the exact mean of the fp32 squares rounded
+  once to fp32 (the page fixes no summation order), and rsqrt is a correctly
+  rounded square root followed by a correctly rounded division.
 * A partial last byte (only possible when the element count is not a multiple
   of four) is padded with the zero code 0b01.
 * 1-bit sign packing of binary weights (qste "What it costs and what it
@@ -71,9 +74,9 @@ in the design notes):
   activation quantiser passed straight through, as the pages' straight-
   through estimator does), so dX = (dY * gamma) w; the page does not say
   whether its input gradient applies the scale, and the gradient of y does.
-* The fused RMSNorm -> FWHT -> int8 prologue uses the exact cancellation of
-  the positive per-token RMS factor and the 1/sqrt(512) normaliser inside
-  absmax quantisation (see ``rmsnorm_fwht_quant``).
+* The BitLinear activation prologue (RMSNorm -> FWHT -> int8) runs the
+  page's three steps in order with fp32 intermediates (the page rounds back
+  to the input dtype between steps, which is the identity for fp32 input).
 """
 from __future__ import annotations
 
@@ -401,25 +404,32 @@ def contract_signs(q: np.ndarray, packed: np.ndarray, k: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
-def quant_act_int8(X: np.ndarray, eps=ACT_EPS, eta_min=None, eta_max=None):
-    """Per-token symmetric int8 quantisation (Hetman-2b s.2, reduced over the
-    last axis as its code does; BitRASP ``fake_quant_int`` is per-token too).
+def quant_act_int8(X: np.ndarray, eps=ACT_EPS, bounds=None):
+    """Per-token symmetric int8 quantisation (Hetman-2b s.2; its code reduces
+    over the last axis, and BitRASP ``fake_quant_int`` is per token too).
 
-    eta = max(max_k |x|, eps), optionally clamped to [eta_min, eta_max];
-    s = fp32(127 / eta); q = clamp(rint(fp32(x * s)), -127, 127);
-    returns (q int8 [M, K], sx fp32 [M] = fp32(eta / 127))."""
+    For each token (row) x:
+        eta = max|x_k|, floored at eps, then clamped to bounds = (lo, hi)
+              (the gain clamp; None means no clamp);
+        s   = fp32(127 / eta);
+        q_k = rint(fp32(x_k * s)) clamped to [-127, 127], halves to even;
+        sx  = fp32(eta / 127), the dequantisation scale returned.
+    Returns (q int8 [M, K], sx fp32 [M])."""
     x = np.asarray(X, dtype=np.float32)
     if x.ndim == 1:
         x = x.reshape(1, -1)
     if not np.all(np.isfinite(x)):
         raise ValueError("non-finite input")
-    eta = np.max(np.abs(x), axis=1) if x.shape[1] else np.zeros(x.shape[0], F32)
-    eta = np.maximum(eta, F32(eps)).astype(np.float32)
-    if eta_min is not None and eta_max is not None:
-        eta = np.clip(eta, F32(eta_min), F32(eta_max)).astype(np.float32)
-    s = (F32(QMAX) / eta).astype(np.float32)
-    q = np.clip(np.rint(x * s[:, None]), -QMAX, QMAX).astype(np.int8)
-    sx = (eta / F32(QMAX)).astype(np.float32)
+    lo, hi = (F32(0.0), F32(np.inf)) if bounds is None else (F32(bounds[0]), F32(bounds[1]))
+    M, K = x.shape
+    q = np.zeros((M, K), dtype=np.int8)
+    sx = np.empty(M, dtype=np.float32)
+    for i in range(M):
+        amax = np.max(np.abs(x[i])) if K else F32(0.0)
+        eta = min(max(max(F32(amax), F32(eps)), lo), hi)     # fp32 throughout
+        s = F32(F32(QMAX) / eta)
+        q[i] = np.clip(np.rint(x[i] * s), -QMAX, QMAX).astype(np.int8)
+        sx[i] = F32(eta / F32(QMAX))
     return q, sx
 
 
@@ -464,85 +474,77 @@ def fwht512(X: np.ndarray, normalize: bool = True) -> np.ndarray:
     return fwht_block(blocks, normalize).reshape(x.shape)
 
 
-def rms_factor(x_row: np.ndarray) -> np.float32:
-    """r = fp32(1 / fp32(sqrt(fp32(mean(x^2)) + fp32(1e-6)))) (Hetman-2b s.4).
-    The mean of squares is formed in fp64 and rounded once; inputs whose
-    squares sum exactly in fp32 (every |x| a power of two, for instance) give
-    the same r from any summation order."""
-    x64 = np.asarray(x_row, dtype=np.float64)
-    ms = F32(np.sum(x64 * x64) / x64.size)
-    t = F32(ms + RMS_EPS)
-    return F32(F32(1.0) / np.sqrt(t, dtype=np.float32))
+def mean_of_squares(x_row: np.ndarray) -> np.float32:
+    """var = the fp32 nearest (ties to even) to the exact mean of the fp32
+    squares fp32(x_k * x_k) of one token (Hetman-2b s.4: x.pow(2).mean over
+    the last axis, in fp32).  The page fixes no summation order; the exact
+    mean rounded once is the value every order approximates (the reading
+    taken for the absmean scale as well).  The squares are summed exactly as
+    integer counts of 2**-149."""
+    x = np.asarray(x_row, dtype=np.float32).ravel()
+    if x.size == 0:
+        raise ValueError("empty token")
+    sq = (x * x).astype(np.float32)
+    if not np.all(np.isfinite(sq)):
+        raise ValueError("a square is not finite in fp32")
+    return round_rational_to_f32(exact_abs_sum_units(sq), x.size << 149)
 
 
-def rmsnorm_fwht_quant(X: np.ndarray, eta_min=ETA_MIN_BITLINEAR,
-                       eta_max=ETA_MAX_BITLINEAR, rms_weight=None,
-                       rmsnorm: bool = True, fwht: bool = True, eps=ACT_EPS):
-    """BitLinear activation prologue (Hetman-2b s.5: RMSNorm -> blockwise
-    normalised FWHT-512 -> per-token int8 with gain clamp), evaluated through
-    the exact cancellation of positive per-token factors.  Either stage can be
-    switched off (factor 1).
-
-    With z = FWHT_unnormalised(g * x) (fp32, butterfly order above; z = g * x
-    without the FWHT), r the RMS factor and c = fp32(1/sqrt(512)), the
-    rotated activation is r*c*z and its absmax is eta_true = r*c*max|z|.
-    Absmax codes do not change under a positive per-token factor, so while
-    the eps floor and the [eta_min, eta_max] clamp leave eta_true as it is, q
-    is the plain quantiser applied to z with eta = max|z| (q = 0 for a zero
-    token) and the dequantisation scale is eta_true/127.  When the floor or
-    the clamp moves eta to eta_eff, the codes are
-    q = clamp(rint(fp32(z * m)), -127, 127) with
-    m = fp32(fp32(r*c) * fp32(127/eta_eff)) and sx = fp32(eta_eff/127); here r
-    is the fp32 factor of ``rms_factor``.
-
-    Returns (q int8 [M, K], sx fp32 [M], sx_exact fp64 [M], bound bool [M]);
-    sx_exact is eta_eff/127 in fp64 (with the fp64 RMS factor when nothing
-    binds) for tolerance checks."""
-    xin = np.asarray(X, dtype=np.float32)
-    if xin.ndim == 1:
-        xin = xin.reshape(1, -1)
-    x = xin
-    if rms_weight is not None:
-        x = (x * np.asarray(rms_weight, dtype=np.float32)[None, :]).astype(np.float32)
-    z = fwht512(x, normalize=False) if fwht else x.copy()
-    c32 = FWHT_NORM if fwht else F32(1.0)
-    M = x.shape[0]
-    q = np.empty(x.shape, dtype=np.int8)
-    sx = np.empty(M, dtype=np.float32)
-    sx_exact = np.empty(M, dtype=np.float64)
-    bound = np.zeros(M, dtype=bool)
-    for i in range(M):
-        x64 = xin[i].astype(np.float64)
-        r64 = 1.0 / np.sqrt(np.mean(x64 * x64) + float(RMS_EPS)) if rmsnorm else 1.0
-        eta_z = F32(np.max(np.abs(z[i]))) if z.shape[1] else F32(0)
-        eta_true = r64 * float(c32) * float(eta_z)
-        eta_eff = max(eta_true, float(F32(eps)))
-        if eta_min is not None and eta_max is not None:
-            eta_eff = min(max(eta_eff, float(F32(eta_min))), float(F32(eta_max)))
-        if eta_eff == eta_true:
-            if eta_z == 0:
-                q[i] = 0
-            else:
-                s = F32(F32(QMAX) / eta_z)
-                q[i] = np.clip(np.rint(z[i] * s), -QMAX, QMAX).astype(np.int8)
-            sx[i] = F32(eta_true / QMAX)
-            sx_exact[i] = eta_true / QMAX
-        else:
-            bound[i] = True
-            e32 = F32(eta_eff)
-            r = rms_factor(xin[i]) if rmsnorm else F32(1.0)
-            m = F32(F32(r * c32) * F32(F32(QMAX) / e32))
-            q[i] = np.clip(np.rint(z[i] * m), -QMAX, QMAX).astype(np.int8)
-            sx[i] = F32(e32 / F32(QMAX))
-            sx_exact[i] = float(e32) / QMAX
-    return q, sx, sx_exact, bound
+def rms_factor(x_row: np.ndarray, rms_eps=RMS_EPS) -> np.float32:
+    """r = fp32(1 / fp32(sqrt(fp32(var + eps)))) with var = mean_of_squares
+    (Hetman-2b s.4: rsqrt(variance + eps) in fp32; the reciprocal square
+    root is read as a correctly rounded square root followed by a correctly
+    rounded division)."""
+    t = F32(mean_of_squares(x_row) + F32(rms_eps))
+    return F32(F32(1.0) / np.sqrt(t))
 
 
-def rmsnorm_fwht_quant_literal(X: np.ndarray, eta_min=ETA_MIN_BITLINEAR,
-                               eta_max=ETA_MAX_BITLINEAR):
-    """The same prologue evaluated step by step in fp64 (RMSNorm, normalised
-    FWHT, clamp, scale, round) -- used only to bound how far the fp32 fold
-    above can move a code (by at most one, at rounding boundaries)."""
+def rmsnorm(X: np.ndarray, weight=None, rms_eps=RMS_EPS) -> np.ndarray:
+    """Hetman-2b s.4 SubLayerRMSNorm in fp32: token x becomes
+    fp32(fp32(x * r) * g) with r = rms_factor(x) and g the norm weight
+    (ones when None, a product that changes nothing)."""
+    x = np.asarray(X, dtype=np.float32)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    out = np.empty_like(x)
+    for i in range(x.shape[0]):
+        y = (x[i] * rms_factor(x[i], rms_eps)).astype(np.float32)
+        if weight is not None:
+            y = (y * np.asarray(weight, dtype=np.float32)).astype(np.float32)
+        out[i] = y
+    return out
+
+
+BITLINEAR_BOUNDS = (ETA_MIN_BITLINEAR, ETA_MAX_BITLINEAR)
+
+
+def bitlinear_prologue(X: np.ndarray, bounds=BITLINEAR_BOUNDS, rms_weight=None,
+                       rmsnorm_on: bool = True, fwht: bool = True, eps=ACT_EPS,
+                       rms_eps=RMS_EPS):
+    """Activation path of Hetman-2b s.5 BitLinear.forward, steps 1-3, in the
+    page's order and in fp32:
+        1. RMSNorm (s.4), ``rmsnorm`` above;
+        2. blockwise FWHT-512 with the 1/sqrt(512) factor (s.1), ``fwht512``;
+        3. the per-token int8 quantiser with eps 1e-6 and the gain clamp
+           [0.05, 40] (s.2), ``quant_act_int8``.
+    Steps 1 and 2 can be switched off.  The page converts each step's result
+    back to the input dtype; here every intermediate stays fp32 (the page's
+    own behaviour for an fp32 input; a bf16 input widens to fp32 exactly).
+    Returns (q int8 [M, K], sx fp32 [M])."""
+    x = np.asarray(X, dtype=np.float32)
+    if x.ndim == 1:
+        x = x.reshape(1, -1)
+    if rmsnorm_on:
+        x = rmsnorm(x, rms_weight, rms_eps)
+    if fwht:
+        x = fwht512(x, normalize=True)
+    return quant_act_int8(x, eps, bounds)
+
+
+def bitlinear_prologue_fp64(X: np.ndarray, bounds=BITLINEAR_BOUNDS):
+    """The same three steps in fp64, with the Hadamard rotation as a product
+    with the Sylvester matrix -- used only to bound how far the fp32 chain's
+    roundings move a code (by one, at rounding boundaries)."""
     x = np.asarray(X, dtype=np.float64)
     ms = np.mean(x * x, axis=1, keepdims=True)
     xn = x / np.sqrt(ms + 1e-6)
@@ -550,8 +552,8 @@ def rmsnorm_fwht_quant_literal(X: np.ndarray, eta_min=ETA_MIN_BITLINEAR,
     M, K = x.shape
     xr = (xn.reshape(M, K // FWHT_BLOCK, FWHT_BLOCK) @ H.T).reshape(M, K)
     eta = np.maximum(np.max(np.abs(xr), axis=1), 1e-6)
-    if eta_min is not None and eta_max is not None:
-        eta = np.clip(eta, eta_min, eta_max)
+    if bounds is not None:
+        eta = np.clip(eta, bounds[0], bounds[1])
     q = np.clip(np.rint(xr * (127.0 / eta)[:, None]), -127, 127).astype(np.int8)
     return q, eta / 127.0
 
@@ -621,7 +623,7 @@ def ternary_linear(X: np.ndarray, W: np.ndarray, granularity: str = "tensor",
     contract, rescale.  Returns a dict of every intermediate."""
     packed, gam = pack_ternary(W, granularity, mode)
     if prologue:
-        q, sx, _, _ = rmsnorm_fwht_quant(X)
+        q, sx = bitlinear_prologue(X)
     else:
         q, sx = quant_act_int8(X)
     k = np.asarray(W).shape[1]

@@ -288,6 +288,14 @@ def test_act_quant_golden():
         assert sx[0] == F32(1.0)
 
 
+def test_act_quant_scale_is_one_division_golden():
+    for a, b in _golden("act_quant_scale_cases.txt"):
+        x = np.array([[float.fromhex(v.strip()) for v in a.split(",")]], np.float32)
+        want = np.array([[int(v) for v in b.split(",")]], np.int8)
+        q, _ = oracle.quant_act_int8(x)
+        np.testing.assert_array_equal(q, want)
+
+
 def test_act_quant_argmax_hits_127_and_bounds():
     X = ti.activations(11, 64, 777)
     q, sx = oracle.quant_act_int8(X)
@@ -318,8 +326,8 @@ def test_act_quant_gain_clamp():
     rng = np.random.default_rng(42)
     big = (rng.standard_normal((2, 512)) * 500).astype(np.float32)
     tiny = (rng.standard_normal((2, 512)) * 1e-5).astype(np.float32)
-    _, sb = oracle.quant_act_int8(big, eta_min=0.05, eta_max=40.0)
-    _, st = oracle.quant_act_int8(tiny, eta_min=0.05, eta_max=40.0)
+    _, sb = oracle.quant_act_int8(big, bounds=(0.05, 40.0))
+    _, st = oracle.quant_act_int8(tiny, bounds=(0.05, 40.0))
     np.testing.assert_array_equal(sb, np.float32(np.float32(40.0) / np.float32(127)))
     np.testing.assert_array_equal(st, np.float32(np.float32(0.05) / np.float32(127)))
 
@@ -403,57 +411,271 @@ def test_fwht_blockwise_independent_blocks():
         oracle.fwht512(np.zeros((1, 500), np.float32))
 
 
-# ------------------------------------------------------------ prologue (fold)
+# ------------------------------------------------------------ prologue
 
-def test_fold_matches_literal_chain_up_to_boundaries():
+def _is_nearest_f32(v, exact):
+    """v is the fp32 nearest to the rational `exact`, ties to the even
+    significand (checked with exact rationals against both neighbours)."""
+    v = F32(v)
+    up = np.nextafter(v, F32(np.inf))
+    dn = np.nextafter(v, F32(0)) if v > 0 else F32(0)
+    d0 = abs(Fraction(float(v)) - exact)
+    du = abs(Fraction(float(up)) - exact)
+    dd = abs(Fraction(float(dn)) - exact)
+    if d0 > du or d0 > dd:
+        return False
+    if d0 == du or (v > 0 and d0 == dd):
+        return (int(np.array([v]).view(np.uint32)[0]) & 1) == 0
+    return True
+
+
+def test_mean_of_squares_is_the_nearest_fp32_to_the_exact_mean():
+    rng = np.random.default_rng(4)
+    rows = [rng.standard_normal(512), rng.standard_t(3, 4096), rng.standard_normal(3) * 1e-3,
+            rng.standard_normal(64) * 2.0**-60, rng.standard_normal(7) * 2.0**40,
+            np.array([3.0]), rng.standard_t(1, 1000)]
+    for x in rows:
+        x = np.asarray(x, np.float32)
+        sq = [Fraction(float(v)) for v in (x * x).astype(np.float32)]
+        exact = sum(sq, Fraction(0)) / len(sq)
+        assert _is_nearest_f32(oracle.mean_of_squares(x), exact)
+    g = _golden_dict("prologue_cases.txt")
+    for key in ("tie_even", "tie_above", "fp64_wrong"):
+        xs, want = g[key].split("->")
+        x = np.array([float.fromhex(v.strip()) if "p" in v else float(v)
+                      for v in xs.split(",")], np.float32)
+        assert oracle.mean_of_squares(x) == F32(float.fromhex(want.strip()) if "p" in want
+                                                else float(want))
+
+
+def _decimal_rsqrt(var, eps):
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    return float(1 / (Decimal(float(var)) + Decimal(float(eps))).sqrt())
+
+
+def test_rms_factor_exact_cases_and_ulp_bound():
+    # all |x| = 16: the mean is 256 exactly, fp32(256 + 1e-6) = 256 (1e-6 is
+    # below half the spacing 2^-15), sqrt 16, r = 1/16 exactly
+    x = np.where(np.arange(512) % 3 == 0, -16.0, 16.0).astype(np.float32)
+    assert oracle.rms_factor(x) == F32(0.0625)
+    # all x = 2^-10: the mean is 2^-20 and eps is about as large, so it must
+    # enter: r = 1/sqrt(2^-20 + fp32(1e-6)), not 1024
+    x = np.full(64, 2.0**-10, np.float32)
+    r = oracle.rms_factor(x)
+    want = _decimal_rsqrt(2.0**-20, F32(1e-6))
+    assert abs(float(r) - want) <= 2 * float(np.spacing(F32(want)))
+    assert abs(float(r) - 1024.0) > 100
+    # random tokens: three roundings after the exact mean, within 2 ulp
+    rng = np.random.default_rng(5)
+    for scale in (1.0, 1e-3, 30.0):
+        x = (rng.standard_t(3, 2048) * scale).astype(np.float32)
+        var = sum((Fraction(float(v)) for v in (x * x).astype(np.float32)), Fraction(0)) / x.size
+        want = _decimal_rsqrt(float(var), F32(1e-6))
+        r = oracle.rms_factor(x)
+        assert abs(float(r) - want) <= 2 * float(np.spacing(F32(want)))
+
+
+def _nearest_f32(exact):
+    """fp32 nearest to a non-negative rational or Decimal `exact` (ties to
+    even), found by comparing it with the neighbours of a float guess."""
+    from decimal import Decimal
+    ex = Fraction(exact) if not isinstance(exact, Decimal) else Fraction(str(exact))
+    v = F32(float(ex))
+    for _ in range(4):
+        up, dn = np.nextafter(v, F32(np.inf)), np.nextafter(v, F32(0))
+        if abs(Fraction(float(up)) - ex) < abs(Fraction(float(v)) - ex):
+            v = up
+        elif abs(Fraction(float(dn)) - ex) < abs(Fraction(float(v)) - ex):
+            v = dn
+        else:
+            break
+    for w in (np.nextafter(v, F32(np.inf)), np.nextafter(v, F32(0))):
+        if abs(Fraction(float(w)) - ex) == abs(Fraction(float(v)) - ex):
+            if int(np.array([w]).view(np.uint32)[0]) % 2 == 0:
+                v = w
+    return v
+
+
+def _rmsnorm_by_rationals(x, g):
+    """Hetman-2b s.4 evaluated on exact rationals, rounding to fp32 after
+    each operation the page performs in fp32, left to right:
+    var = mean(x^2), rsqrt(var + eps), then x * rsqrt * weight."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 60
+    sq = [_nearest_f32(Fraction(float(v)) ** 2) for v in x]
+    var = _nearest_f32(sum((Fraction(float(v)) for v in sq), Fraction(0)) / len(sq))
+    t = _nearest_f32(Fraction(float(var)) + Fraction(float(F32(1e-6))))
+    root = _nearest_f32(Decimal(float(t)).sqrt())
+    r = _nearest_f32(1 / Fraction(float(root)))
+    out = []
+    for v, w in zip(x, g):
+        a = _nearest_f32(abs(Fraction(float(v)) * Fraction(float(r))))
+        a = a if v >= 0 else -a
+        b = _nearest_f32(abs(Fraction(float(a)) * Fraction(float(w))))
+        out.append(b if (a >= 0) == (w >= 0) else -b)
+    return r, np.array(out, np.float32)
+
+
+def test_rmsnorm_matches_the_page_expression_on_rationals():
+    rng = np.random.default_rng(72)
+    for i in range(24):
+        K = int(rng.choice([4, 9, 64]))
+        x = (rng.standard_t(3, K) * 10.0 ** rng.uniform(-3, 2)).astype(np.float32)
+        g = rng.uniform(0.25, 3.0, K).astype(np.float32)
+        r, want = _rmsnorm_by_rationals(x, g)
+        assert oracle.rms_factor(x) == r, i
+        np.testing.assert_array_equal(oracle.rmsnorm(x, g)[0], want)
+
+
+def test_act_quant_codes_on_rationals_sweep():
+    # s = fp32(127 / eta) and q = rint(fp32(x * s)) evaluated on exact
+    # rationals for many tokens: a scale formed as 1 / (eta / 127), or a
+    # product rounded differently, moves some of these codes
+    rng = np.random.default_rng(73)
+    X = (rng.standard_normal((120, 48)) * 10.0 ** rng.uniform(-2, 2, (120, 1))).astype(np.float32)
+    q, sx = oracle.quant_act_int8(X)
+    for i in range(X.shape[0]):
+        eta = Fraction(float(np.max(np.abs(X[i]))))
+        s = Fraction(float(_nearest_f32(127 / eta)))
+        for k in range(X.shape[1]):
+            p = Fraction(float(X[i, k])) * s
+            a = Fraction(float(_nearest_f32(abs(p))))
+            want = _round_half_even(a) * (1 if p >= 0 else -1)
+            assert q[i, k] == max(-127, min(127, want)), (i, k)
+        assert sx[i] == _nearest_f32(eta / 127)
+
+
+def test_rmsnorm_weight_is_applied_per_element():
+    X = ti.activations(71, 3, 1024, dist="student_t3")
+    base = oracle.rmsnorm(X)
+    np.testing.assert_array_equal(oracle.rmsnorm(X, -np.ones(1024, np.float32)), -base)
+    np.testing.assert_array_equal(oracle.rmsnorm(X, np.full(1024, 8.0, np.float32)), base * 8)
+    onehot = np.zeros(1024, np.float32)
+    onehot[613] = 1.0
+    y = oracle.rmsnorm(X, onehot)
+    assert np.count_nonzero(y[:, np.arange(1024) != 613]) == 0
+    np.testing.assert_array_equal(y[:, 613], base[:, 613])
+
+
+def test_prologue_spike_golden():
+    g = _golden_dict("prologue_cases.txt")
+    x = np.zeros((1, 512), np.float32)
+    x[0, int(g["spike_index"])] = float(g["spike_value"])
+    assert oracle.mean_of_squares(x[0]) == F32(float(g["spike_var"]))
+    q, sx = oracle.bitlinear_prologue(x)
+    want = np.concatenate([np.full(256, 127), np.full(256, -127)]).astype(np.int8)
+    np.testing.assert_array_equal(q[0], want)
+    assert sx[0] == _f32(int(g["spike_sx_bits"], 16))
+    assert sx[0] == F32(F32(float(g["spike_eta"])) / F32(127))
+
+
+def _round_half_even(fr):
+    f = fr.numerator // fr.denominator
+    rem = fr - f
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and f % 2):
+        return f + 1
+    return f
+
+
+def test_prologue_integer_tokens_against_exact_rationals():
+    # tokens of +-16: RMSNorm gives r = 1/16 exactly and +-1 values, the
+    # unnormalised transform z = H x is the integer Sylvester product, and
+    # every code is 127 z / max|z| rounded, up to the fp32 products' few ulp
+    # (only codes within 1e-4 of a half-integer may differ, by one)
+    rng = np.random.default_rng(61)
+    X = (rng.choice([-16.0, 16.0], size=(4, 1024))).astype(np.float32)
+    H = oracle.hadamard_matrix(512)
+    q, sx = oracle.bitlinear_prologue(X)
+    for i in range(4):
+        z = np.concatenate([H @ (X[i, b * 512:(b + 1) * 512] / 16).astype(np.int64)
+                            for b in range(2)])
+        zmax = int(np.max(np.abs(z)))
+        exact_eta = zmax / np.sqrt(512.0)
+        assert abs(float(sx[i]) - exact_eta / 127) <= 1e-6 * exact_eta / 127
+        for k in range(1024):
+            v = Fraction(127 * int(z[k]), zmax)
+            dist = abs(v - (v.numerator // v.denominator) - Fraction(1, 2))
+            if dist > Fraction(1, 10000):
+                assert q[i, k] == _round_half_even(v), (i, k)
+            else:
+                assert abs(int(q[i, k]) - _round_half_even(v)) <= 1
+
+
+def test_prologue_matches_fp64_chain_up_to_boundaries():
     X = ti.activations(5105, 64, 4096, dist="student_t3")
-    q, sx, sx_exact, bound = oracle.rmsnorm_fwht_quant(X)
-    ql, sxl = oracle.rmsnorm_fwht_quant_literal(X)
-    assert not bound.any()
+    q, sx = oracle.bitlinear_prologue(X)
+    ql, sxl = oracle.bitlinear_prologue_fp64(X)
     d = np.abs(q.astype(int) - ql.astype(int))
     assert d.max() <= 1
     assert np.mean(d) < 1e-3
-    np.testing.assert_allclose(sx_exact, sxl, rtol=1e-6)
-    np.testing.assert_allclose(sx, sxl, rtol=2e-7)
+    np.testing.assert_allclose(sx, sxl, rtol=1e-6)
 
 
-def test_fold_clamp_branches_exact_inputs():
+def test_prologue_clamp_bound_tokens():
     rng = np.random.default_rng(9)
     K = 4096
-    # (a) upper clamp: one block carries a Hadamard row pattern, the rest zero
     H = oracle.hadamard_matrix(512)
+    # (a) upper clamp: one block carries 8 x a Hadamard row, the rest is zero;
+    # after RMSNorm and the rotation its energy sits in one value, 64 > 40
     xa = np.zeros(K, np.float32)
     xa[1024:1536] = (H[37] * 2.0**3).astype(np.float32)
-    # (b) lower clamp: all |x| = 2^-20 (RMSNorm eps dominates)
+    # (b) lower clamp: all |x| = 2^-20, so eps dominates RMSNorm's denominator
     xb = (rng.choice([-1.0, 1.0], size=K) * 2.0**-20).astype(np.float32)
     # (c) zero token
     xc = np.zeros(K, np.float32)
     X = np.stack([xa, xb, xc])
-    q, sx, sx_exact, bound = oracle.rmsnorm_fwht_quant(X)
-    assert bound.all()
-    assert sx[0] == np.float32(np.float32(40.0) / np.float32(127))
-    assert sx[1] == np.float32(np.float32(0.05) / np.float32(127))
+    q, sx = oracle.bitlinear_prologue(X)
+    assert sx[0] == F32(F32(40.0) / F32(127))
+    assert sx[1] == F32(F32(0.05) / F32(127))
+    assert sx[2] == F32(F32(0.05) / F32(127))
     assert not q[2].any()
-    # (a): z has one non-zero entry 512*8 at index 1024+37; r = 2^-3*sqrt(8)
-    # (up to fp32 rounding), so the code there is rint(4096*m) with m as defined
     nz = np.nonzero(q[0])[0]
     np.testing.assert_array_equal(nz, [1024 + 37])
-    r = oracle.rms_factor(xa)
-    m = np.float32(np.float32(r * oracle.FWHT_NORM) *
-                   np.float32(np.float32(127) / np.float32(40.0)))
-    assert q[0, 1024 + 37] == np.clip(np.rint(np.float32(4096.0) * m), -127, 127)
-    assert q[0, 1024 + 37] == 127   # eta_true = 64 > 40, so the peak saturates
-    # (b): compare with fp64 evaluation of the literal chain
-    ql, _ = oracle.rmsnorm_fwht_quant_literal(X[1:2])
-    assert np.abs(q[1].astype(int) - ql[0].astype(int)).max() <= 1
+    assert q[0, 1024 + 37] == 127
+    ql, _ = oracle.bitlinear_prologue_fp64(X)
+    assert np.abs(q.astype(int) - ql.astype(int)).max() <= 1
 
 
-def test_fold_power_of_two_scaling_invariance():
-    X = ti.activations(77, 4, 1024, dist="student_t3")
-    q0, s0, _, _ = oracle.rmsnorm_fwht_quant(X)
-    q1, s1, _, _ = oracle.rmsnorm_fwht_quant(X * np.float32(8.0))
+def test_prologue_off_reduces_to_plain_quantiser():
+    X = ti.activations(91, 6, 1024, dtype="f32")
+    X[2] = 0
+    q0, s0 = oracle.quant_act_int8(X)
+    q1, s1 = oracle.bitlinear_prologue(X, bounds=None, rmsnorm_on=False, fwht=False)
     np.testing.assert_array_equal(q0, q1)
-    np.testing.assert_allclose(s0, s1, rtol=1e-6)   # RMSNorm removes the factor
+    np.testing.assert_array_equal(s0, s1)
+    q2, s2 = oracle.quant_act_int8(X * 100, bounds=(0.05, 40.0))
+    q3, s3 = oracle.bitlinear_prologue(X * 100, rmsnorm_on=False, fwht=False)
+    np.testing.assert_array_equal(q2, q3)
+    np.testing.assert_array_equal(s2, s3)
+
+
+def test_prologue_rmsnorm_of_power_of_two_magnitudes():
+    # every |x| = 2^a (a >= 3): the mean of squares is 4^a exactly, eps is
+    # below half its spacing, r = 2^-a exactly, so RMSNorm only rescales by a
+    # power of two and the codes are the plain quantiser's codes of x
+    rng = np.random.default_rng(93)
+    for a in (3, 7):
+        X = (rng.choice([-1.0, 1.0], size=(3, 640)) * 2.0**a).astype(np.float32)
+        q0, s0 = oracle.quant_act_int8(X)
+        q1, s1 = oracle.bitlinear_prologue(X, bounds=None, fwht=False)
+        np.testing.assert_array_equal(q0, q1)
+        np.testing.assert_array_equal(s1, s0 * F32(2.0**-a))
+
+
+def test_prologue_fwht_of_integer_tokens_is_exact():
+    # without RMSNorm, |x| <= 2^14 integers: the transform is exact and the
+    # codes are those of the plain quantiser applied to fp32(z * c)
+    rng = np.random.default_rng(94)
+    X = rng.integers(-2**10, 2**10, size=(3, 1024)).astype(np.float32)
+    H = oracle.hadamard_matrix(512)
+    z = np.concatenate([X[:, :512].astype(np.int64) @ H.T,
+                        X[:, 512:].astype(np.int64) @ H.T], axis=1)
+    xr = (z.astype(np.float32) * oracle.FWHT_NORM).astype(np.float32)
+    q0, s0 = oracle.quant_act_int8(xr, bounds=(0.05, 40.0))
+    q1, s1 = oracle.bitlinear_prologue(X, rmsnorm_on=False)
+    np.testing.assert_array_equal(q0, q1)
+    np.testing.assert_array_equal(s0, s1)
 
 
 # ------------------------------------------------------------ contraction
@@ -523,35 +745,6 @@ def test_whole_layer_tiny_matches_gemv_emulation():
             assert acc == r["acc"][m, o]
             y = float(acc) * float(r["scale"][0]) * float(r["sx"][m])
             assert abs(y - r["y"][m, o]) <= 1e-12 * max(1.0, abs(y))
-
-
-def test_prologue_off_reduces_to_plain_quantiser():
-    X = ti.activations(91, 6, 1024, dtype="f32")
-    X[2] = 0
-    q0, s0 = oracle.quant_act_int8(X)
-    q1, s1, _, _ = oracle.rmsnorm_fwht_quant(X, eta_min=None, eta_max=None,
-                                             rmsnorm=False, fwht=False)
-    np.testing.assert_array_equal(q0[[0, 1, 3, 4, 5]], q1[[0, 1, 3, 4, 5]])
-    np.testing.assert_array_equal(s0[[0, 1, 3, 4, 5]], s1[[0, 1, 3, 4, 5]])
-    assert not q1[2].any()
-    # with the clamp the bound branch is the plain clamped quantiser as well
-    q2, s2 = oracle.quant_act_int8(X * 100, eta_min=0.05, eta_max=40.0)
-    q3, s3, _, b3 = oracle.rmsnorm_fwht_quant(X * 100, rmsnorm=False, fwht=False)
-    assert b3.all()
-    np.testing.assert_array_equal(q2, q3)
-    np.testing.assert_array_equal(s2, s3)
-
-
-def test_prologue_rmsnorm_only_codes_equal_plain():
-    # RMSNorm alone multiplies each token by a positive factor: same codes
-    X = ti.activations(92, 8, 640)
-    q0, _ = oracle.quant_act_int8(X)
-    q1, _, sxe, b = oracle.rmsnorm_fwht_quant(X, eta_min=None, eta_max=None, fwht=False)
-    assert not b.any()
-    np.testing.assert_array_equal(q0, q1)
-    x64 = X.astype(np.float64)
-    r = 1 / np.sqrt(np.mean(x64 * x64, axis=1) + 1e-6)
-    np.testing.assert_allclose(sxe, r * np.max(np.abs(x64), axis=1) / 127, rtol=1e-12)
 
 
 # ---------------------------------------------------------------- 1-bit signs
