@@ -125,14 +125,17 @@ tq_status tq_pack_ternary(const float* W, int64_t N, int64_t K, tq_gran g,
  *   s = fp32(127/eta); q = clamp(rint(fp32(x*s)), -127, 127);
  *   sx = fp32(eta/127).  Bit-exact: q and sx.
  * Prologue path (rmsnorm and/or fwht_block = 512, K % 512 == 0 for FWHT):
- *   z = FWHT_unnormalised(g * x) blockwise in fp32 (stages h = 1..256), r the
- *   RMS factor 1/sqrt(mean(x^2) + rms_eps) (1 without rmsnorm), c = fp32(1/sqrt(512))
- *   (1 without FWHT).  The RMSNorm output rotated and normalised is r*c*z, and
- *   its absmax codes equal those of z while the eps floor and the clamp leave
- *   eta_true = r*c*max|z| unchanged: q = clamp(rint(fp32(z * fp32(127/max|z|))))
- *   and sx = eta_true/127.  Otherwise q = clamp(rint(fp32(z*m))) with
- *   m = fp32(fp32(r*c) * fp32(127/eta_eff)) and sx = fp32(eta_eff/127).
- *   q is bit-exact given r; sx is exact to fp32 rounding of r.
+ *   Hetman-2b s.5 BitLinear.forward's order, every step in fp32:
+ *   1. RMSNorm (s.4): var = the fp32 nearest to the exact mean of the fp32
+ *      squares fp32(x*x) (ties to even; the page fixes no summation order),
+ *      r = fp32(1 / fp32(sqrt(fp32(var + rms_eps)))), x <- fp32(fp32(x*r)*g)
+ *      with g = rms_weight (the product is skipped when rms_weight is NULL);
+ *      rms_weight is read only with rmsnorm;
+ *   2. FWHT (s.1): blockwise, stages h = 1..256, then x <- fp32(x * c) with
+ *      c = fp32(1/sqrt(512));
+ *   3. the plain quantiser above on the result.
+ *   Bit-exact: q and sx.  Inputs whose squares overflow fp32 (|x| >= 2^64)
+ *   are outside the contract.
  * Errors: NULL pointers, M < 0, K <= 0, K % 512 != 0 with FWHT, fwht_block
  * not 0 or 512, xdt not F32/BF16, K > 32768 with a prologue (UNSUPPORTED). */
 tq_status tq_quant_act_int8(const void* X, tq_dtype xdt, int64_t M, int64_t K,

@@ -13,12 +13,15 @@
 //     with (1e-6, 0.05, 40).
 // BitRASP core_math.py, fake_quant_int, is the same per-token absmax scheme.
 //
-// The fused prologue uses the cancellation of positive per-token factors in
-// absmax quantisation: the normalised, rotated token is r*c*z with
-// z = FWHT_unnormalised(g*x), so while neither the eps floor nor the gain
-// clamp moves eta_true = r*c*max|z| the codes are those of z itself and only
-// the dequantisation scale carries r*c.  Codes then depend on no
-// order-sensitive reduction.
+// The fused prologue runs the three steps in that order on fp32 values held
+// in registers: RMSNorm (var = mean of the fp32 squares, r = 1/sqrt(var +
+// eps) as a correctly rounded square root and division, x * r * g), the
+// FWHT and its factor, then the quantiser.  var is the fp32 nearest to the
+// exact mean of the squares: an fp64 sum decides it unless it lies within
+// its error bound of an fp32 rounding midpoint, and then the squares are
+// summed exactly in integer exponent bins.  Every later step is a fixed
+// sequence of correctly rounded fp32 operations, so codes and scales do not
+// depend on the reduction order.
 
 #include "tq_device.hpp"
 #include "tq_internal.hpp"
@@ -260,25 +263,116 @@ __global__ __launch_bounds__(kNT) void k_fwht512(const T* __restrict__ X, int64_
 
 // ------------------------------------------------------------ prologue path
 
-// One block per token.  Each wave holds NB 512-element segments in
-// registers (segment wave + 4*j), lane l holding elements 8l .. 8l+7 of each.
-template <typename T, int NB, bool VEC>
-__global__ __launch_bounds__(kNT) void k_quant_prologue(
+// Relative error bound of the fp64 mean of squares: each fp32 square is exact
+// in fp64 and passes through at most NB * 8 sequential additions in a
+// thread, six in the wave tree and sixteen across waves, then one division
+// by K: under 160 roundings of 2^-53 each, far below 2^-40.
+constexpr double kVarThr = 0x1p-40;
+
+// fp32 nearest (ties to even) to (sum_b bins[b] * 2^(b-1)) / n quanta of
+// 2^-149, over the whole fp32 range (subnormals included).  One thread, on
+// LDS words `T` (kVarLimbs of scratch).  bins[b] < 2^40 (a token of at most
+// 2^16 squares of 24-bit significands) shifted by at most 253 bits fit 11
+// limbs of 32 bits.
+constexpr int kVarLimbs = 11;
+__device__ float exact_mean_squares(const unsigned long long* bins, uint32_t n, uint32_t* T) {
+  for (int i = 0; i < kVarLimbs; ++i) T[i] = 0u;
+  for (int b = 1; b < 255; ++b) {
+    const unsigned long long v = bins[b];
+    if (v == 0ull) continue;
+    const int sh = b - 1, li = sh >> 5, bo = sh & 31;
+    const unsigned long long lo = v << bo;
+    const unsigned long long hi = bo ? (v >> (64 - bo)) : 0ull;
+    const uint32_t add[3] = {static_cast<uint32_t>(lo), static_cast<uint32_t>(lo >> 32),
+                             static_cast<uint32_t>(hi)};
+    unsigned long long carry = 0ull;
+    for (int j = 0; li + j < kVarLimbs; ++j) {
+      if (j >= 3 && carry == 0ull) break;
+      const unsigned long long t =
+          static_cast<unsigned long long>(T[li + j]) + (j < 3 ? add[j] : 0u) + carry;
+      T[li + j] = static_cast<uint32_t>(t);
+      carry = t >> 32;
+    }
+  }
+  // long division by n, limb by limb from the top: T becomes the quotient
+  unsigned long long rem = 0ull;
+  for (int i = kVarLimbs - 1; i >= 0; --i) {
+    const unsigned long long cur = (rem << 32) | T[i];
+    T[i] = static_cast<uint32_t>(cur / n);
+    rem = cur % n;
+  }
+  int lead = -1;
+  for (int i = kVarLimbs - 1; i >= 0 && lead < 0; --i)
+    if (T[i]) lead = i * 32 + 31 - __clz(static_cast<int>(T[i]));
+  const bool half = 2ull * rem == n, above = 2ull * rem > n;
+  if (lead < 24) {
+    // below 2^-125 the fp32 spacing is one quantum: round the quotient
+    uint32_t u = T[0];
+    if (above || (half && (u & 1u))) ++u;
+    return __uint_as_float(u);  // u <= 2^24 is that value's bit pattern
+  }
+  const int shift = lead - 23;
+  auto bit = [&](int p) { return (T[p >> 5] >> (p & 31)) & 1u; };
+  uint32_t mant = 0u;
+  for (int p = lead; p >= shift; --p) mant = (mant << 1) | bit(p);
+  const uint32_t guard = bit(shift - 1);
+  bool sticky = rem != 0ull;
+  for (int p = shift - 2; p >= 0 && !sticky; --p) sticky = bit(p) != 0u;
+  int e = shift;
+  if (guard && (sticky || (mant & 1u))) ++mant;
+  if (mant == (1u << 24)) {
+    mant >>= 1;
+    ++e;
+  }
+  // mant * 2^(e - 149) with mant in [2^23, 2^24): biased exponent e + 1
+  return __uint_as_float((static_cast<uint32_t>(e + 1) << 23) | (mant & 0x7FFFFFu));
+}
+
+// fp32 rounding of an fp64 mean of squares whose relative error is at most
+// kVarThr; true when it lies too close to an fp32 rounding midpoint to
+// decide (then *v is not final).
+__device__ inline bool var_from_fp64(double mean, float* v) {
+  const float f = __double2float_rn(mean);
+  *v = f;
+  if (mean == 0.0) return false;  // every square is zero
+  const uint32_t fb = __float_as_uint(f);
+  const double fd = static_cast<double>(f);
+  const double up = static_cast<double>(__uint_as_float(fb + 1u));
+  double dist = fabs(0.5 * (fd + up) - mean);
+  if (fb != 0u) dist = fmin(dist, fabs(mean - 0.5 * (fd + static_cast<double>(__uint_as_float(fb - 1u)))));
+  return dist <= kVarThr * mean;
+}
+
+__device__ inline void square_bin_add(unsigned long long* bins, float sq) {
+  const uint32_t u = __float_as_uint(sq);
+  const uint32_t e = u >> 23;
+  const uint32_t m = (u & 0x7FFFFFu) | (e ? 0x800000u : 0u);
+  atomicAdd(&bins[e ? e : 1u], static_cast<unsigned long long>(m));
+}
+
+// One block of NW waves per token.  Each wave holds NB 512-element segments
+// in registers (segment wave + NW * j), lane l holding elements 8l .. 8l+7
+// of each; the token is read once.
+template <typename T, int NW, int NB, bool VEC>
+__global__ __launch_bounds__(NW * kWave) void k_quant_prologue(
     const T* __restrict__ X, int64_t K, float eps, int clamp, float lo, float hi,
     int rmsnorm, float rms_eps, const float* __restrict__ gweight, int fwht,
     int8_t* __restrict__ q, float* __restrict__ sx) {
-  __shared__ float sh[kWavesPerBlock];
+  __shared__ double part[NW];
+  __shared__ float pmax[NW];
+  __shared__ unsigned long long bins[256];
+  __shared__ uint32_t limbs[kVarLimbs];
+  __shared__ float var_sh;
   const int64_t row = blockIdx.x;
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const T* x = X + row * K;
   const int64_t nseg = (K + 511) / 512;
   float v[NB][8];
-  float ss = 0.f;
   // every segment's load goes out before the first one is used
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int64_t seg = wave + kWavesPerBlock * j;
+    const int64_t seg = wave + NW * j;
     const int64_t base = seg * 512 + 8 * lane;
     if (seg < nseg) {
       load8<T, VEC>(x + base, K - base, v[j]);
@@ -287,78 +381,100 @@ __global__ __launch_bounds__(kNT) void k_quant_prologue(
       for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
     }
   }
-#pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const int64_t seg = wave + kWavesPerBlock * j;
-    const int64_t base = seg * 512 + 8 * lane;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
-    if (gweight != nullptr && seg < nseg) {
-      float g[8];
-      load8<float, false>(gweight + base, K - base, g);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[j][e] = v[j][e] * g[e];
-    }
-    if (fwht) fwht512_wave(v[j]);
-  }
-  float r = 1.f;
   if (rmsnorm) {
-    const float sum_sq = block_sum<kNT>(ss, sh);
-    const float ms = sum_sq / static_cast<float>(K);
-    const float t = ms + rms_eps;
-    r = 1.f / sqrtf(t);
+    // var: the fp32 nearest to the exact mean of the fp32 squares
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc += static_cast<double>(v[j][e] * v[j][e]);
+    acc = wave_sum(acc);
+    if (lane == 0) part[wave] = acc;
+    __syncthreads();
+    double S = 0.0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) S += part[w];
+    float var;
+    if (var_from_fp64(S / static_cast<double>(K), &var)) {  // uniform over the block
+      for (int b = threadIdx.x; b < 256; b += NW * kWave) bins[b] = 0ull;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) square_bin_add(bins, v[j][e] * v[j][e]);
+      __syncthreads();
+      if (threadIdx.x == 0) var_sh = exact_mean_squares(bins, static_cast<uint32_t>(K), limbs);
+      __syncthreads();
+      var = var_sh;
+    }
+    // sqrtf and / are the correctly rounded operations under the build's
+    // -fhip-fp32-correctly-rounded-divide-sqrt (__fsqrt_rn is the hardware
+    // approximation on this toolchain unless rounded OCML operations are on)
+    const float r = 1.f / sqrtf(var + rms_eps);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = v[j][e] * r;
+      const int64_t seg = wave + NW * j;
+      const int64_t base = seg * 512 + 8 * lane;
+      if (gweight != nullptr && seg < nseg) {
+        float g[8];
+        load8<float, false>(gweight + base, K - base, g);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[j][e] = v[j][e] * g[e];
+      }
+    }
   }
-  float zmax = 0.f;
+  if (fwht) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      fwht512_wave(v[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = v[j][e] * kFwhtNorm;
+    }
+  }
+  float amax = 0.f;
 #pragma unroll
   for (int j = 0; j < NB; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) zmax = fmaxf(zmax, fabsf(v[j][e]));
-  // block max of |z| (non-negative: DPP wave maxima, lane 63 holds them)
-  zmax = wave_max_last(zmax);
-  if (lane == kWave - 1) sh[wave] = zmax;
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+  // block max of |x| (non-negative: DPP wave maxima, lane 63 holds them)
+  amax = wave_max_last(amax);
+  if (lane == kWave - 1) pmax[wave] = amax;
   __syncthreads();
-  zmax = sh[0];
+  amax = pmax[0];
 #pragma unroll
-  for (int w = 1; w < kWavesPerBlock; ++w) zmax = fmaxf(zmax, sh[w]);
-  const float rc = r * (fwht ? kFwhtNorm : 1.f);
-  const float eta_true = rc * zmax;
-  float eta = fmaxf(eta_true, eps);
+  for (int w = 1; w < NW; ++w) amax = fmaxf(amax, pmax[w]);
+  float eta = fmaxf(amax, eps);
   if (clamp) eta = fminf(fmaxf(eta, lo), hi);
-  float mult, sxv;
-  if (eta == eta_true) {
-    mult = zmax > 0.f ? 127.f / zmax : 0.f;
-    sxv = eta_true / 127.f;
-  } else {
-    mult = rc * (127.f / eta);
-    sxv = eta / 127.f;
-  }
+  const float s = 127.f / eta;
   int8_t* qo = q + row * K;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int64_t seg = wave + kWavesPerBlock * j;
+    const int64_t seg = wave + NW * j;
     if (seg >= nseg) continue;
     const int64_t base = seg * 512 + 8 * lane;
     uint32_t b[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) b[e] = quant_byte(v[j][e], mult);
+    for (int e = 0; e < 8; ++e) b[e] = quant_byte(v[j][e], s);
     store8_q<VEC>(qo + base, K - base, b);
   }
-  if (threadIdx.x == 0) sx[row] = sxv;
+  if (threadIdx.x == 0) sx[row] = eta / 127.f;
 }
 
 template <typename T, bool VEC>
 hipError_t prologue_dispatch(const T* X, int64_t M, int64_t K, const ActParams& p,
                              int8_t* q, float* sx, hipStream_t s) {
-  const int64_t per_wave = (K + 2047) / 2048;  // segments per wave
-#define TQ_PROLOGUE(NBV)                                                            \
-  hipLaunchKernelGGL((k_quant_prologue<T, NBV, VEC>), dim3(M), dim3(kNT), 0, s, X, K, \
-                     p.eps, p.clamp, p.eta_min, p.eta_max, p.rmsnorm, p.rms_eps,    \
+  const int64_t nseg = (K + 511) / 512;
+#define TQ_PROLOGUE(NWV, NBV)                                                             \
+  hipLaunchKernelGGL((k_quant_prologue<T, NWV, NBV, VEC>), dim3(M), dim3(NWV * kWave), 0, \
+                     s, X, K, p.eps, p.clamp, p.eta_min, p.eta_max, p.rmsnorm, p.rms_eps, \
                      p.rms_weight, p.fwht, q, sx)
-  if (per_wave <= 1) TQ_PROLOGUE(1);
-  else if (per_wave <= 2) TQ_PROLOGUE(2);
-  else if (per_wave <= 4) TQ_PROLOGUE(4);
-  else if (per_wave <= 8) TQ_PROLOGUE(8);
-  else TQ_PROLOGUE(16);
+  if (nseg <= 4) TQ_PROLOGUE(4, 1);
+  else if (nseg <= 8) TQ_PROLOGUE(8, 1);
+  else if (nseg <= 16) TQ_PROLOGUE(16, 1);
+  else if (nseg <= 32) TQ_PROLOGUE(16, 2);
+  else TQ_PROLOGUE(16, 4);
 #undef TQ_PROLOGUE
   return hipGetLastError();
 }

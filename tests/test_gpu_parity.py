@@ -80,8 +80,8 @@ def ref_pack(name, j=0, mode="ternary"):
 def ref_quant(name, j=0, b=None):
     X = ti.workload_activations(name, j, b)
     if ti.WORKLOADS[name].get("prologue"):
-        q, sx, sxe, bound = oracle.rmsnorm_fwht_quant(X)
-        return X, q, sx, sxe
+        q, sx = oracle.bitlinear_prologue(X)
+        return X, q, sx, sx.astype(np.float64)
     q, sx = oracle.quant_act_int8(X)
     return X, q, sx, sx.astype(np.float64)
 
@@ -258,7 +258,7 @@ def test_quant_clamp_and_ties():
                   rng.standard_normal(512).astype(np.float32)])
     say("quant clamp")
     q, sx = tq.tq_quant_act_int8(dev(X), clamp=(0.05, 40.0))
-    qr, sr = oracle.quant_act_int8(X, eta_min=0.05, eta_max=40.0)
+    qr, sr = oracle.quant_act_int8(X, bounds=(0.05, 40.0))
     np.testing.assert_array_equal(host(q), qr)
     np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sr))
     T = np.zeros((3, 8), np.float32)
@@ -311,33 +311,42 @@ def test_fwht512_integer_exact_and_spike():
 # ----------------------------------------------------------------- prologue
 
 def test_prologue_bitlinear_workload():
-    X, q_ref, sx_ref, sxe = ref_quant("bitlinear")
+    X, q_ref, sx_ref, _ = ref_quant("bitlinear")
     say(f"prologue bitlinear {X.shape}")
     q, sx = tq.tq_quant_act_int8(dev_bf16(X), clamp=(0.05, 40.0), rmsnorm=True,
                                  fwht_block=512)
     np.testing.assert_array_equal(host(q), q_ref)
-    np.testing.assert_allclose(host(sx).astype(np.float64), sxe, rtol=2e-6)
+    np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sx_ref))
 
 
 @pytest.mark.parametrize("rmsnorm,fwht", [(True, False), (False, True), (True, True)])
-@pytest.mark.parametrize("M,K", [(3, 512), (2, 1536), (4, 8192), (1, 32768)])
-def test_prologue_variants(rmsnorm, fwht, M, K):
-    X = ti.activations(1200 + M + K, M, K, dist="student_t3", dtype="f32")
+@pytest.mark.parametrize("M,K", [(3, 512), (2, 1536), (4, 8192), (1, 32768), (5, 2048),
+                                 (2, 16384)])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_prologue_variants(rmsnorm, fwht, M, K, dtype):
+    X = ti.activations(1200 + M + K, M, K, dist="student_t3", dtype=dtype)
+    if M >= 3:
+        X[1] = 0.0                                  # zero token
     g = (1.0 + 0.25 * ti.activations(7, 1, K, dtype="f32")[0]).astype(np.float32)
-    say(f"prologue rms={rmsnorm} fwht={fwht} {M}x{K}")
+    say(f"prologue rms={rmsnorm} fwht={fwht} {M}x{K} {dtype}")
     for weight in (None, g):
-        q, sx = tq.tq_quant_act_int8(dev(X), clamp=(0.05, 40.0), rmsnorm=rmsnorm,
+        q, sx = tq.tq_quant_act_int8(x_to_device(X, dtype), clamp=(0.05, 40.0), rmsnorm=rmsnorm,
                                      rms_weight=None if weight is None else dev(weight),
                                      fwht_block=512 if fwht else 0)
-        qr, sr, sxe, bound = oracle.rmsnorm_fwht_quant(X, rms_weight=weight, rmsnorm=rmsnorm,
-                                                       fwht=fwht)
-        qg, sg = host(q), host(sx).astype(np.float64)
-        free = ~bound
-        # rows where the clamp binds take their codes through the fp32 RMS
-        # factor, whose summation order is free: allow one step there
-        np.testing.assert_array_equal(qg[free], qr[free])
-        assert np.abs(qg[bound].astype(int) - qr[bound].astype(int)).max(initial=0) <= 1
-        np.testing.assert_allclose(sg, sxe, rtol=2e-6)
+        qr, sr = oracle.bitlinear_prologue(X, rms_weight=weight, rmsnorm_on=rmsnorm, fwht=fwht)
+        np.testing.assert_array_equal(host(q), qr)
+        np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sr))
+
+
+@pytest.mark.parametrize("M,K", [(3, 1000), (2, 7), (1, 4100)])
+def test_prologue_rmsnorm_ragged_rows(M, K):
+    # RMSNorm without the transform takes any K (a partial last segment)
+    X = ti.activations(1300 + M + K, M, K, dist="student_t3", dtype="f32")
+    say(f"prologue rmsnorm ragged {M}x{K}")
+    q, sx = tq.tq_quant_act_int8(dev(X), rmsnorm=True)
+    qr, sr = oracle.bitlinear_prologue(X, bounds=None, fwht=False)
+    np.testing.assert_array_equal(host(q), qr)
+    np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sr))
 
 
 def test_prologue_clamp_branches():
@@ -345,19 +354,37 @@ def test_prologue_clamp_branches():
     K = 4096
     H = oracle.hadamard_matrix(512)
     xa = np.zeros(K, np.float32)
-    xa[1024:1536] = (H[37] * 2.0**3).astype(np.float32)          # eta_true 64 > 40
+    xa[1024:1536] = (H[37] * 2.0**3).astype(np.float32)          # eta 64 > 40
     xb = (rng.choice([-1.0, 1.0], size=K) * 2.0**-20).astype(np.float32)  # < 0.05
     xc = np.zeros(K, np.float32)
     xd = (rng.choice([-1.0, 1.0], size=K) * 2.0**5).astype(np.float32)    # no clamp
-    X = np.stack([xa, xb, xc, xd])
+    xe = (rng.standard_normal(K) * 1e-4).astype(np.float32)       # eps and clamp near
+    X = np.stack([xa, xb, xc, xd, xe])
     say("prologue clamp branches")
     q, sx = tq.tq_quant_act_int8(dev(X), clamp=(0.05, 40.0), rmsnorm=True, fwht_block=512)
-    qr, sr, sxe, bound = oracle.rmsnorm_fwht_quant(X)
-    assert list(bound) == [True, True, True, False]
+    qr, sr = oracle.bitlinear_prologue(X)
     np.testing.assert_array_equal(host(q), qr)
-    sxg = host(sx)
-    np.testing.assert_array_equal(f32_bits(sxg[:3]), f32_bits(sr[:3]))
-    np.testing.assert_allclose(sxg[3], sxe[3], rtol=2e-6)
+    np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sr))
+
+
+def test_prologue_exact_mean_of_squares_fallback():
+    # tokens whose mean of squares sits on, or 2^-82 above, an fp32 rounding
+    # midpoint (zero-padded to a 512-block: the mean is divided by a power of
+    # two, so it stays a midpoint), and one an fp64 sum rounds the wrong way:
+    # the device must take its exact integer path and agree with the oracle
+    rows = [[2.0, 2.0, 2.0**-11, 2.0**-11], [2.0, 2.0, 2.0**-11, 2.0**-11 + 2.0**-30],
+            [2.0, 2.0**-11, 2.0**-40, 0.0], [2.0**-70, 2.0**-75, 0.0, 0.0],
+            [1e-20, 3e-21, 2e-23, 0.0]]
+    X = np.zeros((len(rows), 512), np.float32)
+    for i, r in enumerate(rows):
+        X[i, [3, 100, 300, 511]] = r
+    say("prologue exact-mean fallback")
+    for fwht in (False, True):
+        q, sx = tq.tq_quant_act_int8(dev(X), clamp=(0.05, 40.0), rmsnorm=True,
+                                     fwht_block=512 if fwht else 0)
+        qr, sr = oracle.bitlinear_prologue(X, fwht=fwht)
+        np.testing.assert_array_equal(host(q), qr)
+        np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(sr))
 
 
 # --------------------------------------------------------------- contraction
@@ -704,7 +731,7 @@ def test_quant_ternary_gemv_matches_two_calls(M, N, K, dtype, gran):
     sc = scale if gran == "row" else scale[:1]
     Xd, pd, sd = x_to_device(X, dtype), dev(packed), dev(sc)
     say(f"quant+gemv M={M} N={N} K={K} {dtype} {gran}")
-    qr, sr = oracle.quant_act_int8(X, eta_min=0.05, eta_max=40.0)
+    qr, sr = oracle.quant_act_int8(X, bounds=(0.05, 40.0))
     for ydt in ("f32", "bf16", "i32"):
         Y, q, sx = tq.tq_quant_ternary_gemv(Xd, pd, sd, N, K, gran, ydt, clamp=(0.05, 40.0))
         q2, sx2 = tq.tq_quant_act_int8(Xd, clamp=(0.05, 40.0))
@@ -729,8 +756,9 @@ def test_quant_ternary_gemv_with_prologue_and_empty():
     say("quant+gemv prologue")
     Y, q, sx = tq.tq_quant_ternary_gemv(dev(X), dev(packed), dev(scale), 40, 1024, "tensor",
                                         "f32", clamp=(0.05, 40.0), rmsnorm=True, fwht_block=512)
-    qr, srr, sxe, bound = oracle.rmsnorm_fwht_quant(X, rmsnorm=True, fwht=True)
+    qr, srr = oracle.bitlinear_prologue(X)
     np.testing.assert_array_equal(host(q), qr)
+    np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(srr))
     acc_ref, y_ref = _contract_ref(qr, packed, 1024, scale, host(sx))
     assert_y_close(host(Y), y_ref)
     # N == 0 still quantises
