@@ -390,13 +390,9 @@ def pack_binary1(W: np.ndarray, granularity: str = "row"):
 
 
 def contract_signs(q: np.ndarray, packed: np.ndarray, k: int) -> np.ndarray:
-    """acc[m, o] = sum_k q[m, k] * b[o, k] over the unpacked +-1 weights, in
-    int64, checked to fit int32."""
-    b = unpack_signs(packed, k).astype(np.int64)
-    acc = np.asarray(q, dtype=np.int64) @ b.T
-    if acc.size and (acc.max() > 2**31 - 1 or acc.min() < -2**31):
-        raise OverflowError("accumulator exceeds int32")
-    return acc
+    """acc[m, o] = sum_k q[m, k] * b[o, k] over the unpacked +-1 weights,
+    exact, int64."""
+    return _exact_integer_product(q, unpack_signs(packed, k))
 
 
 # --------------------------------------------------------------------------
@@ -575,16 +571,28 @@ def hadamard_matrix(n: int) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 
-def contract(q: np.ndarray, packed: np.ndarray, k: int) -> np.ndarray:
-    """acc[m, o] = sum_k q[m, k] * w[o, k] in int64 over the unpacked weight
-    codes (the add/sub/skip contraction of Foundry "Native Matmul Kernel" and
-    Hetman-2b s.7, which is this integer matrix product).  Returns int64 and
-    checks that every value fits in int32."""
-    w = unpack_codes(packed, k).astype(np.int64)
-    acc = np.asarray(q, dtype=np.int64) @ w.T
+def _exact_integer_product(q: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """q [M, K] times w^T for integer-valued q (|q| <= 128) and w in
+    {-1, 0, +1}, as a float64 matrix product: every product and every partial
+    sum is an integer of magnitude at most 128 K < 2**53, so each step of the
+    library's product is exact in any order and the result is the exact
+    integer sum.  Returns int64, checked to fit int32."""
+    q = np.asarray(q)
+    k = q.shape[-1] if q.ndim else 0
+    if 128 * k >= 2**53:
+        raise ValueError("K too large for an exact float64 product")
+    acc = (q.astype(np.float64) @ np.asarray(w, dtype=np.float64).T).astype(np.int64)
     if acc.size and (acc.max() > 2**31 - 1 or acc.min() < -2**31):
         raise OverflowError("accumulator exceeds int32")
     return acc
+
+
+def contract(q: np.ndarray, packed: np.ndarray, k: int) -> np.ndarray:
+    """acc[m, o] = sum_k q[m, k] * w[o, k] over the unpacked weight codes (the
+    add/sub/skip contraction of Foundry "Native Matmul Kernel" and Hetman-2b
+    s.7, which is this integer matrix product), exact (see
+    ``_exact_integer_product``).  Returns int64."""
+    return _exact_integer_product(q, unpack_codes(packed, k))
 
 
 def contract_rows(q: np.ndarray, packed: np.ndarray, k: int, rows) -> np.ndarray:

@@ -705,6 +705,33 @@ def test_contraction_three_references_agree():
                     assert acc[m, o] == sum(int(q[m, k]) * int(w[o, k]) for k in range(K))
 
 
+def test_contraction_equals_int64_product_at_scale():
+    # the float64 product is exact for integer operands: check it against
+    # numpy's int64 matrix product (integer arithmetic, no rounding) on
+    # shapes with several thousand terms per sum and extreme values
+    rng = np.random.default_rng(41)
+    for (M, N, K) in [(7, 40, 16384), (33, 257, 4096), (2, 5, 6912)]:
+        q = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+        q[0] = 127
+        if M > 1:
+            q[1] = -128
+        w = ti.random_ternary(M + N + K, N, K)
+        w[0] = 1
+        w[-1] = -1
+        want = q.astype(np.int64) @ w.astype(np.int64).T
+        np.testing.assert_array_equal(oracle.contract(q, oracle.pack_codes(w), K), want)
+    b = np.where(rng.standard_normal((9, 1024)) >= 0, 1, -1).astype(np.int8)
+    q = rng.integers(-127, 128, size=(3, 1024)).astype(np.int8)
+    np.testing.assert_array_equal(oracle.contract_signs(q, oracle.pack_signs(b), 1024),
+                                  q.astype(np.int64) @ b.astype(np.int64).T)
+
+
+def test_bf16_rounding_golden():
+    for a, b in _golden("bf16_rounding.txt"):
+        got = oracle.bf16_round_from_f64(np.array([float.fromhex(a)]))[0]
+        assert float(got) == float.fromhex(b), a
+
+
 def test_contraction_all_plus_one_and_bounds():
     q = ti.random_int8(20, 4, 512)
     w = np.ones((3, 512), np.int8)
