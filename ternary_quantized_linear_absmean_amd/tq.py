@@ -126,11 +126,58 @@ def _stream(stream) -> int | None:
 
 
 def _dev(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    return t
+
+
+def _arg(t, name: str, dtypes, shape=None, numel=None, like=None, min_numel=None) -> torch.Tensor:
+    """Check one tensor argument before anything is launched: dtype, then
+    exact shape or element count (or at least min_numel elements), then
+    contiguity (`like` is accepted for symmetry; _devices checks placement).  The C entry points see raw pointers only, so a buffer
+    of the wrong size or type would be read or written out of bounds."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(map(str, dtypes))}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements, got {t.numel()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return t
+
+
+def _devices(**tensors) -> None:
+    """Every tensor argument is a device tensor, all on one device (checked
+    after the dtype and size checks of _arg)."""
+    first = None
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        _dev(t, name)
+        if first is None:
+            first = t
+        elif t.device != first.device:
+            raise ValueError(f"{name} must be on {first.device}, got {t.device}")
+
+
+def _enum(table: dict, value: str, name: str) -> int:
+    if value not in table:
+        raise ValueError(f"{name} must be one of {sorted(table)}, got {value!r}")
+    return table[value]
+
+
+def _scale_numel(granularity: str, N: int) -> int:
+    return N if _enum(GRANULARITY, granularity, "granularity") == 1 else 1
 
 
 _ACT_DT = {torch.float32: 0, torch.bfloat16: 1}
@@ -165,19 +212,27 @@ def tq_pack_ternary(W: torch.Tensor, granularity: str = "tensor", mode: str = "t
                     packed: torch.Tensor | None = None, scale: torch.Tensor | None = None,
                     workspace: torch.Tensor | None = None, stream=None):
     """W [N, K] fp32 -> (packed uint8 [N, K/4], scale fp32 [1] or [N])."""
-    _dev(W, "W")
-    if W.dtype != torch.float32 or W.dim() != 2:
-        raise ValueError("W must be a 2-D float32 tensor")
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("W must be a 2-D tensor [N, K]")
     N, K = W.shape
+    _arg(W, "W", torch.float32)
+    ns = _scale_numel(granularity, N)
+    _enum(MODES, mode, "mode")
     if packed is None:
         packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
     if scale is None:
-        scale = torch.empty((1 if granularity == "tensor" else N,), dtype=torch.float32,
-                            device=W.device)
+        scale = torch.empty((ns,), dtype=torch.float32, device=W.device)
+    _arg(packed, "packed", torch.uint8, numel=N * (K // 4), like=W)
+    _arg(scale, "scale", torch.float32, numel=ns, like=W)
     need = tq_pack_workspace_bytes(N, K, granularity)
     if workspace is None and need:
         workspace = torch.empty((need,), dtype=torch.uint8, device=W.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if workspace is not None:
+        _arg(workspace, "workspace", torch.uint8, like=W)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace must hold at least {need} bytes")
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _devices(W=W, packed=packed, scale=scale, workspace=workspace)
     _check(_lib.tq_pack_ternary(W.data_ptr(), N, K, GRANULARITY[granularity], MODES[mode],
                                 _ptr(packed), _ptr(scale), _ptr(workspace), ws_bytes,
                                 _stream(stream)), "tq_pack_ternary")
@@ -192,19 +247,26 @@ def tq_pack_binary1(W: torch.Tensor, granularity: str = "row",
                     packed: torch.Tensor | None = None, scale: torch.Tensor | None = None,
                     workspace: torch.Tensor | None = None, stream=None):
     """W [N, K] fp32 -> (packed uint8 [N, K/8] signs, scale fp32 [1] or [N])."""
-    _dev(W, "W")
-    if W.dtype != torch.float32 or W.dim() != 2:
-        raise ValueError("W must be a 2-D float32 tensor")
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("W must be a 2-D tensor [N, K]")
     N, K = W.shape
+    _arg(W, "W", torch.float32)
+    ns = _scale_numel(granularity, N)
     if packed is None:
         packed = torch.empty((N, K // 8), dtype=torch.uint8, device=W.device)
     if scale is None:
-        scale = torch.empty((1 if granularity == "tensor" else N,), dtype=torch.float32,
-                            device=W.device)
+        scale = torch.empty((ns,), dtype=torch.float32, device=W.device)
+    _arg(packed, "packed", torch.uint8, numel=N * (K // 8), like=W)
+    _arg(scale, "scale", torch.float32, numel=ns, like=W)
     need = tq_pack_workspace_bytes(N, K, granularity)
     if workspace is None and need:
         workspace = torch.empty((need,), dtype=torch.uint8, device=W.device)
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if workspace is not None:
+        _arg(workspace, "workspace", torch.uint8, like=W)
+        if workspace.numel() < need:
+            raise ValueError(f"workspace must hold at least {need} bytes")
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _devices(W=W, packed=packed, scale=scale, workspace=workspace)
     _check(_lib.tq_pack_binary1(W.data_ptr(), N, K, GRANULARITY[granularity], _ptr(packed),
                                 _ptr(scale), _ptr(workspace), ws_bytes, _stream(stream)),
            "tq_pack_binary1")
@@ -213,7 +275,16 @@ def tq_pack_binary1(W: torch.Tensor, granularity: str = "row",
 
 # ------------------------------------------------------------ activations
 
-def _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block) -> TqActOpts:
+def _act_in(X, name="X"):
+    if not isinstance(X, torch.Tensor) or X.dim() != 2:
+        raise ValueError(f"{name} must be a 2-D tensor [M, K]")
+    _arg(X, name, tuple(_ACT_DT))
+    return X.shape
+
+
+def _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block, K=None, like=None) -> TqActOpts:
+    if rms_weight is not None:
+        _arg(rms_weight, "rms_weight", torch.float32, numel=K, like=like)
     return TqActOpts(eps=eps, clamp=1 if clamp else 0,
                      eta_min=clamp[0] if clamp else 0.0, eta_max=clamp[1] if clamp else 0.0,
                      rmsnorm=1 if rmsnorm else 0, rms_eps=rms_eps,
@@ -226,15 +297,15 @@ def tq_quant_act_int8(X: torch.Tensor, eps: float = 1e-6, clamp=None, rmsnorm: b
                       sx: torch.Tensor | None = None, stream=None):
     """X [M, K] fp32/bf16 -> (q int8 [M, K], sx fp32 [M]).  ``clamp`` is an
     (eta_min, eta_max) pair or None."""
-    _dev(X, "X")
-    if X.dtype not in _ACT_DT or X.dim() != 2:
-        raise ValueError("X must be a 2-D float32 or bfloat16 tensor")
-    M, K = X.shape
+    M, K = _act_in(X)
     if q is None:
         q = torch.empty((M, K), dtype=torch.int8, device=X.device)
     if sx is None:
         sx = torch.empty((M,), dtype=torch.float32, device=X.device)
-    opts = _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block)
+    _arg(q, "q", torch.int8, shape=(M, K), like=X)
+    _arg(sx, "sx", torch.float32, numel=M, like=X)
+    opts = _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block, K, X)
+    _devices(X=X, q=q, sx=sx, rms_weight=rms_weight)
     _check(_lib.tq_quant_act_int8(X.data_ptr(), _ACT_DT[X.dtype], M, K, ctypes.byref(opts),
                                   _ptr(q), _ptr(sx), _stream(stream)), "tq_quant_act_int8")
     return q, sx
@@ -243,12 +314,11 @@ def tq_quant_act_int8(X: torch.Tensor, eps: float = 1e-6, clamp=None, rmsnorm: b
 def tq_fwht512(X: torch.Tensor, normalize: bool = True, Y: torch.Tensor | None = None,
                stream=None) -> torch.Tensor:
     """Blockwise FWHT-512 along the last axis of X [M, K] -> fp32 [M, K]."""
-    _dev(X, "X")
-    if X.dtype not in _ACT_DT or X.dim() != 2:
-        raise ValueError("X must be a 2-D float32 or bfloat16 tensor")
-    M, K = X.shape
+    M, K = _act_in(X)
     if Y is None:
         Y = torch.empty((M, K), dtype=torch.float32, device=X.device)
+    _arg(Y, "Y", torch.float32, shape=(M, K), like=X)
+    _devices(X=X, Y=Y)
     _check(_lib.tq_fwht512(X.data_ptr(), _ACT_DT[X.dtype], M, K, 1 if normalize else 0,
                            _ptr(Y), _stream(stream)), "tq_fwht512")
     return Y
@@ -256,18 +326,22 @@ def tq_fwht512(X: torch.Tensor, normalize: bool = True, Y: torch.Tensor | None =
 
 # ------------------------------------------------------------ contraction
 
-def _contract(fn, name, q, sx, packed, scale, N, K, granularity, out_dtype, Y, stream):
-    _dev(q, "q")
-    _dev(sx, "sx")
-    _dev(packed, "packed")
-    _dev(scale, "scale")
-    if q.dtype != torch.int8 or packed.dtype != torch.uint8:
-        raise ValueError("q must be int8 and packed uint8")
+def _contract(fn, name, q, sx, packed, scale, N, K, granularity, out_dtype, Y, stream,
+              bits=2):
+    if not isinstance(q, torch.Tensor) or q.dim() != 2:
+        raise ValueError("q must be a 2-D tensor [M, K]")
     M = q.shape[0]
+    _arg(q, "q", torch.int8, shape=(M, K))
+    _arg(sx, "sx", torch.float32, numel=M, like=q)
+    _arg(packed, "packed", torch.uint8, min_numel=N * (K * bits // 8), like=q)
+    _arg(scale, "scale", torch.float32, min_numel=_scale_numel(granularity, N), like=q)
+    ydt = _enum(DTYPES, out_dtype, "out_dtype")
     if Y is None:
         Y = torch.empty((M, N), dtype=_Y_TORCH[out_dtype], device=q.device)
+    _arg(Y, "Y", _Y_TORCH[out_dtype], shape=(M, N), like=q)
+    _devices(q=q, sx=sx, packed=packed, scale=scale, Y=Y)
     _check(fn(q.data_ptr(), sx.data_ptr(), M, packed.data_ptr(), scale.data_ptr(),
-              GRANULARITY[granularity], N, K, _ptr(Y), DTYPES[out_dtype], _stream(stream)),
+              GRANULARITY[granularity], N, K, _ptr(Y), ydt, _stream(stream)),
            name)
     return Y
 
@@ -283,7 +357,7 @@ def tq_binary1_gemv(q, sx, packed, scale, N: int, K: int, granularity: str = "ro
                     out_dtype: str = "f32", Y=None, stream=None) -> torch.Tensor:
     """tq_ternary_gemv with 1-bit sign-packed weights (packed [N, K/8])."""
     return _contract(_lib.tq_binary1_gemv, "tq_binary1_gemv", q, sx, packed, scale, N, K,
-                     granularity, out_dtype, Y, stream)
+                     granularity, out_dtype, Y, stream, bits=1)
 
 
 def tq_ternary_gemm(q, sx, packed, scale, N: int, K: int, granularity: str = "tensor",
@@ -301,19 +375,23 @@ def tq_quant_ternary_gemv(X: torch.Tensor, packed, scale, N: int, K: int,
                           Y: torch.Tensor | None = None, stream=None):
     """Quantise X [M, K] (M <= 16) and apply the decode GEMV in one call ->
     (Y [M, N], q int8 [M, K], sx fp32 [M])."""
-    _dev(X, "X")
-    _dev(packed, "packed")
-    _dev(scale, "scale")
-    if X.dtype not in _ACT_DT or X.dim() != 2:
-        raise ValueError("X must be a 2-D float32 or bfloat16 tensor")
-    M = X.shape[0]
+    M, KX = _act_in(X)
+    if KX != K:
+        raise ValueError(f"X must have K = {K} columns, got {KX}")
+    _arg(packed, "packed", torch.uint8, min_numel=N * (K // 4), like=X)
+    _arg(scale, "scale", torch.float32, min_numel=_scale_numel(granularity, N), like=X)
+    _enum(DTYPES, out_dtype, "out_dtype")
     if q is None:
         q = torch.empty((M, K), dtype=torch.int8, device=X.device)
     if sx is None:
         sx = torch.empty((M,), dtype=torch.float32, device=X.device)
     if Y is None:
         Y = torch.empty((M, N), dtype=_Y_TORCH[out_dtype], device=X.device)
-    opts = _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block)
+    _arg(q, "q", torch.int8, shape=(M, K), like=X)
+    _arg(sx, "sx", torch.float32, numel=M, like=X)
+    _arg(Y, "Y", _Y_TORCH[out_dtype], shape=(M, N), like=X)
+    opts = _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block, K, X)
+    _devices(X=X, packed=packed, scale=scale, q=q, sx=sx, Y=Y, rms_weight=rms_weight)
     _check(_lib.tq_quant_ternary_gemv(X.data_ptr(), _ACT_DT[X.dtype], M, ctypes.byref(opts),
                                       packed.data_ptr(), scale.data_ptr(),
                                       GRANULARITY[granularity], N, K, _ptr(q), _ptr(sx),
@@ -330,19 +408,27 @@ def tq_swiglu_gemv(X: torch.Tensor, packed_gate, scale_gate, packed_up, scale_up
                    sx: torch.Tensor | None = None, H: torch.Tensor | None = None, stream=None):
     """Gate and up projections of X [M, K] (M <= 16) with the SwiGLU-clamp
     epilogue -> (H [M, N], q int8 [M, K], sx fp32 [M])."""
-    for t, name in ((X, "X"), (packed_gate, "packed_gate"), (scale_gate, "scale_gate"),
-                    (packed_up, "packed_up"), (scale_up, "scale_up")):
-        _dev(t, name)
-    if X.dtype not in _ACT_DT or X.dim() != 2:
-        raise ValueError("X must be a 2-D float32 or bfloat16 tensor")
-    M = X.shape[0]
+    M, KX = _act_in(X)
+    if KX != K:
+        raise ValueError(f"X must have K = {K} columns, got {KX}")
+    ns = _scale_numel(granularity, N)
+    for t, name in ((packed_gate, "packed_gate"), (packed_up, "packed_up")):
+        _arg(t, name, torch.uint8, min_numel=N * (K // 4), like=X)
+    for t, name in ((scale_gate, "scale_gate"), (scale_up, "scale_up")):
+        _arg(t, name, torch.float32, min_numel=ns, like=X)
+    _enum(DTYPES, out_dtype, "out_dtype")
     if q is None:
         q = torch.empty((M, K), dtype=torch.int8, device=X.device)
     if sx is None:
         sx = torch.empty((M,), dtype=torch.float32, device=X.device)
     if H is None:
         H = torch.empty((M, N), dtype=_Y_TORCH[out_dtype], device=X.device)
-    opts = _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block)
+    _arg(q, "q", torch.int8, shape=(M, K), like=X)
+    _arg(sx, "sx", torch.float32, numel=M, like=X)
+    _arg(H, "H", _Y_TORCH[out_dtype], shape=(M, N), like=X)
+    opts = _opts(eps, clamp, rmsnorm, rms_eps, rms_weight, fwht_block, K, X)
+    _devices(X=X, packed_gate=packed_gate, scale_gate=scale_gate, packed_up=packed_up,
+             scale_up=scale_up, q=q, sx=sx, H=H, rms_weight=rms_weight)
     _check(_lib.tq_swiglu_gemv(X.data_ptr(), _ACT_DT[X.dtype], M, ctypes.byref(opts),
                                packed_gate.data_ptr(), scale_gate.data_ptr(),
                                packed_up.data_ptr(), scale_up.data_ptr(),
@@ -358,10 +444,16 @@ def tq_ffn_swiglu_decode(X: torch.Tensor, gate, up, down, d_model: int, d_ffn: i
                          stream=None):
     """Decode FFN: gate, up, down are (packed, scale) pairs.  Returns
     (Y [M, d_model], buffers) where buffers holds q_x, sx_x, H, q_h, sx_h."""
-    _dev(X, "X")
-    if X.dtype not in _ACT_DT or X.dim() != 2:
-        raise ValueError("X must be a 2-D float32 or bfloat16 tensor")
-    M = X.shape[0]
+    M, KX = _act_in(X)
+    if KX != d_model:
+        raise ValueError(f"X must have d_model = {d_model} columns, got {KX}")
+    ns_f, ns_m = _scale_numel(granularity, d_ffn), _scale_numel(granularity, d_model)
+    for (pk, sc), name, nrow, ncol, ns in ((gate, "gate", d_ffn, d_model, ns_f),
+                                           (up, "up", d_ffn, d_model, ns_f),
+                                           (down, "down", d_model, d_ffn, ns_m)):
+        _arg(pk, f"{name} packed", torch.uint8, min_numel=nrow * (ncol // 4), like=X)
+        _arg(sc, f"{name} scale", torch.float32, min_numel=ns, like=X)
+    _enum(DTYPES, out_dtype, "out_dtype")
     b = dict(buffers or {})
     dv = X.device
     b.setdefault("q_x", torch.empty((M, d_model), dtype=torch.int8, device=dv))
@@ -371,7 +463,14 @@ def tq_ffn_swiglu_decode(X: torch.Tensor, gate, up, down, d_model: int, d_ffn: i
     b.setdefault("sx_h", torch.empty((M,), dtype=torch.float32, device=dv))
     if Y is None:
         Y = torch.empty((M, d_model), dtype=_Y_TORCH[out_dtype], device=dv)
+    for key, dt, shp in (("q_x", torch.int8, (M, d_model)), ("sx_x", torch.float32, (M,)),
+                         ("H", torch.float32, (M, d_ffn)), ("q_h", torch.int8, (M, d_ffn)),
+                         ("sx_h", torch.float32, (M,))):
+        _arg(b[key], key, dt, shape=shp, like=X)
+    _arg(Y, "Y", _Y_TORCH[out_dtype], shape=(M, d_model), like=X)
     opts = _opts(eps, clamp, False, 1e-6, None, 0)
+    _devices(X=X, gate_packed=gate[0], gate_scale=gate[1], up_packed=up[0], up_scale=up[1],
+             down_packed=down[0], down_scale=down[1], Y=Y, **b)
     _check(_lib.tq_ffn_swiglu_decode(
         X.data_ptr(), _ACT_DT[X.dtype], M, ctypes.byref(opts), gate[0].data_ptr(),
         gate[1].data_ptr(), up[0].data_ptr(), up[1].data_ptr(), down[0].data_ptr(),
@@ -386,18 +485,15 @@ def tq_ternary_backward_input(dY: torch.Tensor, packed, scale, K: int,
                               accumulate: bool = False, stream=None) -> torch.Tensor:
     """dX [M, K] fp32 = (dY [M, N] * gamma) contracted with the packed codes
     over N; with accumulate the result is added to the given dX."""
-    for t, name in ((dY, "dY"), (packed, "packed"), (scale, "scale")):
-        _dev(t, name)
-    if dY.dtype not in _ACT_DT or dY.dim() != 2:
-        raise ValueError("dY must be a 2-D float32 or bfloat16 tensor")
-    M, N = dY.shape
+    M, N = _act_in(dY, "dY")
+    _arg(packed, "packed", torch.uint8, min_numel=N * (K // 4), like=dY)
+    _arg(scale, "scale", torch.float32, min_numel=_scale_numel(granularity, N), like=dY)
     if dX is None:
         if accumulate:
             raise ValueError("accumulate needs dX")
         dX = torch.empty((M, K), dtype=torch.float32, device=dY.device)
-    _dev(dX, "dX")
-    if dX.dtype != torch.float32 or tuple(dX.shape) != (M, K):
-        raise ValueError("dX must be float32 [M, K]")
+    _arg(dX, "dX", torch.float32, shape=(M, K), like=dY)
+    _devices(dY=dY, packed=packed, scale=scale, dX=dX)
     _check(_lib.tq_ternary_backward_input(dY.data_ptr(), _ACT_DT[dY.dtype], M,
                                           packed.data_ptr(), scale.data_ptr(),
                                           GRANULARITY[granularity], N, K, dX.data_ptr(),
@@ -410,21 +506,16 @@ def tq_ternary_backward_weight(X: torch.Tensor, dY: torch.Tensor, dW: torch.Tens
                                accumulate: bool = False, stream=None) -> torch.Tensor:
     """dW [N, K] fp32 = dY^T X over the M tokens; with accumulate the result
     is added to the given dW."""
-    for t, name in ((X, "X"), (dY, "dY")):
-        _dev(t, name)
-        if t.dtype not in _ACT_DT or t.dim() != 2:
-            raise ValueError(f"{name} must be a 2-D float32 or bfloat16 tensor")
-    M, K = X.shape
-    if dY.shape[0] != M:
+    M, K = _act_in(X)
+    MY, N = _act_in(dY, "dY")
+    if MY != M:
         raise ValueError("X and dY must have the same number of rows")
-    N = dY.shape[1]
     if dW is None:
         if accumulate:
             raise ValueError("accumulate needs dW")
         dW = torch.empty((N, K), dtype=torch.float32, device=X.device)
-    _dev(dW, "dW")
-    if dW.dtype != torch.float32 or tuple(dW.shape) != (N, K):
-        raise ValueError("dW must be float32 [N, K]")
+    _arg(dW, "dW", torch.float32, shape=(N, K), like=X)
+    _devices(X=X, dY=dY, dW=dW)
     _check(_lib.tq_ternary_backward_weight(X.data_ptr(), _ACT_DT[X.dtype], dY.data_ptr(),
                                            _ACT_DT[dY.dtype], M, N, K, dW.data_ptr(),
                                            1 if accumulate else 0, _stream(stream)),
@@ -438,17 +529,21 @@ def tq_pack_ternary_threshold(W: torch.Tensor, granularity: str = "tensor",
                               scale: torch.Tensor | None = None, stream=None):
     """Threshold ternarization + 2-bit packing of W [N, K] fp32 -> (packed
     uint8 [N, K/4], scale fp32 [1] or [N])."""
-    _dev(W, "W")
-    if W.dtype != torch.float32 or W.dim() != 2:
-        raise ValueError("W must be a 2-D float32 tensor")
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("W must be a 2-D tensor [N, K]")
     N, K = W.shape
+    _arg(W, "W", torch.float32)
+    ns = _scale_numel(granularity, N)
+    _enum(THRESHOLDS, kind, "kind")
     if packed is None:
         packed = torch.empty((N, K // 4), dtype=torch.uint8, device=W.device)
     if scale is None:
-        scale = torch.empty((N if granularity == "row" else 1,), dtype=torch.float32,
-                            device=W.device)
+        scale = torch.empty((ns,), dtype=torch.float32, device=W.device)
+    _arg(packed, "packed", torch.uint8, numel=N * (K // 4), like=W)
+    _arg(scale, "scale", torch.float32, numel=ns, like=W)
     nws = tq_pack_workspace_bytes(N, K, granularity)
     ws = torch.empty((max(nws, 8),), dtype=torch.uint8, device=W.device)
+    _devices(W=W, packed=packed, scale=scale)
     _check(_lib.tq_pack_ternary_threshold(W.data_ptr(), N, K, GRANULARITY[granularity],
                                           THRESHOLDS[kind], value, packed.data_ptr(),
                                           scale.data_ptr(), ws.data_ptr(), ws.numel(),
@@ -467,6 +562,8 @@ def tq_convert_codes(src: torch.Tensor, src_fmt: str, dst_fmt: str,
     _dev(dst, "dst")
     if dst.dtype != torch.uint8 or dst.numel() != src.numel():
         raise ValueError("dst must be uint8 with src's size")
+    _enum(CODES, src_fmt, "src_fmt")
+    _enum(CODES, dst_fmt, "dst_fmt")
     _check(_lib.tq_convert_codes(src.data_ptr(), CODES[src_fmt], dst.data_ptr(), CODES[dst_fmt],
                                  src.numel(), _stream(stream)), "tq_convert_codes")
     return dst
@@ -483,6 +580,7 @@ def tq_unpack_codes(packed: torch.Tensor, fmt: str, numel: int,
     _dev(out, "out")
     if out.dtype != torch.int8 or out.numel() != numel:
         raise ValueError("out must be int8 with numel elements")
+    _enum(CODES, fmt, "fmt")
     _check(_lib.tq_unpack_codes(packed.data_ptr(), CODES[fmt], numel, out.data_ptr(),
                                 _stream(stream)), "tq_unpack_codes")
     return out

@@ -280,3 +280,84 @@ def test_product_path_has_no_cpu_fallback():
             src = open(os.path.join(pkg, fn)).read()
             assert not re.search(r"^\s*(import|from)\s+oracle", src, re.M), fn
             assert "numpy" not in src, fn
+
+
+# ------------------------------------------------ binding argument checks
+
+torch = pytest.importorskip("torch")
+
+
+def _raises(match, fn, *a, **k):
+    with pytest.raises(ValueError, match=match):
+        fn(*a, **k)
+
+
+def _t(shape, dtype):
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_contraction_checks_every_buffer():
+    # host tensors: the shape and dtype checks run first, so each mismatch
+    # below is reported before the device check (which a correct host tensor
+    # reaches last); nothing is ever launched
+    i8, f32, u8 = torch.int8, torch.float32, torch.uint8
+    q, sx, pk, sc = _t((2, 64), i8), _t((2,), f32), _t((10, 16), u8), _t((1,), f32)
+    for fn in (tqmod.tq_ternary_gemv, tqmod.tq_ternary_gemm):
+        _raises("must be a device tensor", fn, q, sx, pk, sc, 10, 64)
+        _raises("q must have shape", fn, _t((2, 60), i8), sx, pk, sc, 10, 64)
+        _raises("q must have dtype", fn, _t((2, 64), f32), sx, pk, sc, 10, 64)
+        _raises("sx must hold 2", fn, q, _t((3,), f32), pk, sc, 10, 64)
+        _raises("packed must hold at least 160", fn, q, sx, _t((9, 16), u8), sc, 10, 64)
+        _raises("scale must hold at least 10", fn, q, sx, pk, sc, 10, 64, "row")
+        _raises("Y must have dtype torch.float32", fn, q, sx, pk, sc, 10, 64, "tensor", "f32",
+                Y=_t((2, 10), torch.bfloat16))
+        _raises("Y must have shape", fn, q, sx, pk, sc, 10, 64, "tensor", "bf16",
+                Y=_t((2, 11), torch.bfloat16))
+        _raises("granularity must be one of", fn, q, sx, pk, sc, 10, 64, "rows")
+        _raises("out_dtype must be one of", fn, q, sx, pk, sc, 10, 64, "tensor", "f16")
+    _raises("packed must hold at least 80", tqmod.tq_binary1_gemv, q, sx, _t((79,), u8),
+            _t((10,), f32), 10, 64)
+
+
+def test_binding_quant_pack_and_fused_checks():
+    f32, u8, i8 = torch.float32, torch.uint8, torch.int8
+    X = _t((3, 512), f32)
+    _raises("must be a device tensor", tqmod.tq_quant_act_int8, X)
+    _raises("X must have dtype", tqmod.tq_quant_act_int8, _t((3, 512), torch.float16))
+    _raises("q must have shape", tqmod.tq_quant_act_int8, X, q=_t((3, 511), i8))
+    _raises("sx must hold 3", tqmod.tq_quant_act_int8, X, sx=_t((2,), f32))
+    _raises("rms_weight must hold 512", tqmod.tq_quant_act_int8, X, rmsnorm=True,
+            rms_weight=_t((511,), f32))
+    _raises("Y must have shape", tqmod.tq_fwht512, X, Y=_t((3, 256), f32))
+    W = _t((8, 64), f32)
+    _raises("packed must hold 128", tqmod.tq_pack_ternary, W, packed=_t((8, 15), u8))
+    _raises("scale must hold 8", tqmod.tq_pack_ternary, W, "row", scale=_t((1,), f32))
+    _raises("workspace must hold at least", tqmod.tq_pack_ternary, W, "tensor",
+            packed=_t((8, 16), u8), scale=_t((1,), f32), workspace=_t((8,), u8))
+    _raises("mode must be one of", tqmod.tq_pack_ternary, W, "tensor", "tern")
+    _raises("packed must hold 64", tqmod.tq_pack_binary1, W, packed=_t((8, 16), u8))
+    _raises("kind must be one of", tqmod.tq_pack_ternary_threshold, W, "tensor", "rel")
+    pk, sc = _t((10, 128), u8), _t((1,), f32)
+    _raises("X must have K = 512", tqmod.tq_quant_ternary_gemv, _t((2, 256), f32), pk, sc, 10,
+            512)
+    _raises("Y must have dtype", tqmod.tq_quant_ternary_gemv, _t((2, 512), f32), pk, sc, 10, 512,
+            Y=_t((2, 10), torch.int32))
+    _raises("packed_up must hold at least", tqmod.tq_swiglu_gemv, _t((2, 512), f32), pk, sc,
+            _t((10, 127), u8), sc, 10, 512, "tensor")
+    _raises("H must have shape", tqmod.tq_swiglu_gemv, _t((2, 512), f32), pk, sc, pk, sc, 10, 512,
+            "tensor", H=_t((2, 9), f32))
+    g, u, d = (_t((16, 8), u8), _t((16,), f32)), (_t((16, 8), u8), _t((16,), f32)), \
+        (_t((32, 4), u8), _t((32,), f32))
+    _raises("down packed must hold at least", tqmod.tq_ffn_swiglu_decode, _t((1, 32), f32), g, u,
+            (_t((32, 3), u8), _t((32,), f32)), 32, 16)
+    _raises("sx_h must have shape", tqmod.tq_ffn_swiglu_decode, _t((1, 32), f32), g, u, d, 32, 16,
+            buffers={"sx_h": _t((2,), f32)})
+    _raises("packed must hold at least", tqmod.tq_ternary_backward_input, _t((4, 10), f32),
+            _t((10, 15), u8), sc, 64)
+
+
+def test_package_exports_every_entry_point():
+    import ternary_quantized_linear_absmean_amd as pkg
+    for name in declared_functions():
+        assert name in pkg.__all__, name
+        assert getattr(pkg, name) is getattr(tqmod, name)
