@@ -4,24 +4,25 @@
 
 Workload (the headline): decode GEMV, W 4096x4096 ternary from N(0, 0.02)
 fp32 (per-tensor absmean scale, packed 4 MiB), one bf16 token ~N(0, 1)
-quantised per token to int8, fp32 output.  One step = per-token int8
-quantisation of the token + the packed-weight GEMV with its fused scale
-epilogue.  Steps rotate over 128 distinct packed-weight buffers (512 MiB,
-more than twice the 256 MB Infinity Cache) so that the weight stream comes
-from HBM, as it does when a decode pass walks through a model's layers.
+quantised per token to int8, fp32 output.  One step is one decode token
+through a stack of 128 such layers, each with its own packed weight
+(512 MiB in all, more than twice the 256 MB Infinity Cache, so the weights
+stream from HBM): 128 launches of the fused quantise + GEMV entry point.
+--steps K times exactly K steps (K x 128 launches) after W untimed ones.
 Inputs are resident in HBM before timing starts.  Launches are captured in a
 HIP graph (torch.cuda.CUDAGraph) so that the host never paces the GPU.
 
-Prints one JSON line.  ``value`` is algorithmic bytes of the step over its
-time (GB/s).  ``roofline`` describes the GEMV kernel: its algorithmic bytes
-per launch over its average launch time, against 8 TB/s.  ``cpu_baseline``
-times the CPU oracle on a bounded sample of the same workload.  ``extra``
-carries the prefill GEMM (int8 MFMA TOPS), a 4096^3 GEMM (one full round of
-wide tiles) with the vendor int8 GEMM beside it, the BitLinear prologue, the FFN
-decode shapes, the pack kernels (absmean, threshold, code-format
-conversion), the steady-state GEMV rate (stacked projections in one launch),
-1-bit binary weights, the SwiGLU decode FFN and the backward of the prefill
-layer.
+Prints one JSON line.  ``value`` is algorithmic bytes over time (GB/s).
+``roofline`` describes the GEMV kernel: its algorithmic bytes per launch over
+its average launch time (a step's time / 128), against 8 TB/s.
+``cpu_baseline`` times the CPU oracle on all five workloads, over the host's
+cores (run first, before the GPU is touched).  ``extra`` carries the prefill
+GEMM (int8 MFMA TOPS), a 4096^3 GEMM (one full round of wide tiles) with the
+vendor int8 GEMM beside it, the BitLinear prologue and GEMM, the FFN decode
+shapes, the pack kernels, the steady-state GEMV rate (stacked projections in
+one launch), 1-bit binary weights, the SwiGLU decode FFN, the backward of the
+prefill layer and, under ``context``, reference floors of the device
+(launch, pure read, int8 matrix-core chain, vendor int8 GEMMs).
 """
 from __future__ import annotations
 
@@ -45,11 +46,15 @@ POOL = 128                     # distinct packed weights in the rotation
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2048)
-    p.add_argument("--warmup", type=int, default=256)
+    p.add_argument("--steps", type=int, default=32,
+                   help="timed steps; one step = one token through 128 layers")
+    p.add_argument("--warmup", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--cpu-seconds", type=float, default=30.0,
+                   help="time budget of the CPU oracle over the five workloads")
+    p.add_argument("--cpu-runs", type=int, default=5,
+                   help="runs per workload for the CPU median (fewer past the budget)")
     p.add_argument("--only", default="",
                    help="comma list of extra workloads to run: "
                         "prefill,square,bitlinear,pack,ffn,steady,binary1,ffn_decode,backward,"
@@ -146,6 +151,12 @@ def main():
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        sys.exit(2)
+    # the CPU oracle runs first, in forked workers, before the GPU is touched
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args.cpu_seconds, args.cpu_runs)
+
     import numpy as np
     import torch
 
@@ -167,7 +178,7 @@ def main():
     ybuf = torch.empty((1, N), dtype=torch.float32, device=dev)
 
     def decode_pass():
-        # one decode step = per-token int8 quantisation + GEMV + scale epilogue
+        # one step: the token through 128 layers, each quantise + GEMV + epilogue
         for p in pool:
             tq.tq_quant_ternary_gemv(X, p, scale, N, K, "tensor", "f32", q=qbuf, sx=sxbuf,
                                      Y=ybuf)
@@ -184,26 +195,32 @@ def main():
     g_step = capture(torch, decode_pass)
     g_gemv = capture(torch, gemv_pass)
     g_two = capture(torch, decode_pass_two_calls)
-    reps_w = max(1, args.warmup // POOL)
-    reps = max(1, args.steps // POOL)
-    steps = reps * POOL
-    timed_graph(torch, g_step, reps_w)
-    timed_graph(torch, g_gemv, reps_w)
+    for _ in range(args.warmup):
+        g_step.replay()
+    timed_graph(torch, g_gemv, max(1, args.warmup))
 
-    # timed region: exactly `steps` steps between synchronisations
+    # timed region: exactly `steps` steps between synchronisations, each
+    # between its own pair of events (their spread gives the median)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    sec_per_pass = timed_graph(torch, g_step, reps)
+    ev[0].record()
+    for i in range(args.steps):
+        g_step.replay()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    step_s = sec_per_pass / POOL
+    per_step = [ev[i].elapsed_time(ev[i + 1]) / 1e3 for i in range(args.steps)]
+    step_s = ev[0].elapsed_time(ev[-1]) / 1e3 / args.steps
+    med_step_s = sorted(per_step)[len(per_step) // 2]
+    launch_s, med_launch_s = step_s / POOL, med_step_s / POOL
+    b_launch = fused_bytes(1, N, K, 2, False)
     b_gemv = gemv_bytes(1, N, K, False)
-    b_step = fused_bytes(1, N, K, 2, False)
-    value = b_step / step_s / 1e9
+    value = POOL * b_launch / step_s / 1e9
 
-    gemv_s = timed_graph(torch, g_gemv, reps) / POOL
+    gemv_s = timed_graph(torch, g_gemv, max(4, args.steps // 4)) / POOL
     gemv_gbs = b_gemv / gemv_s / 1e9
-    two_s = timed_graph(torch, g_two, reps) / POOL
+    two_s = timed_graph(torch, g_two, max(4, args.steps // 4)) / POOL
     traffic = counter_traffic()
 
     result = {
@@ -211,8 +228,8 @@ def main():
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": steps,
-        "warmup": reps_w * POOL,
+        "steps": args.steps,
+        "warmup": args.warmup,
         "ms_per_step": round(step_s * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -221,18 +238,24 @@ def main():
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) bf16 token)",
         "config": {"workload": "decode GEMV: bf16 token 1x4096 -> per-token int8, "
                                "packed ternary W 4096x4096 (per-tensor absmean), fp32 out; "
-                               f"{POOL} distinct weight buffers in rotation",
-                   "M": 1, "N": N, "K": K, "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                               f"one step = the token through {POOL} such layers with "
+                               f"distinct weights ({POOL} launches, 512 MiB of weights)",
+                   "M": 1, "N": N, "K": K, "layers_per_step": POOL,
+                   "launches_timed": args.steps * POOL,
+                   "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "entry_point": "tq_quant_ternary_gemv (quantise + GEMV, one launch)",
-                   "two_call_step_us": round(two_s * 1e6, 3),
+                   "median_ms_per_step": round(med_step_s * 1e3, 6),
+                   "two_call_launch_us": round(two_s * 1e6, 3),
                    "kernel_source_sha256_16": source_digest(),
                    "timed_wall_s": round(wall, 4)},
-        # the step is one launch of the fused quantise + GEMV kernel, so its
-        # average launch time is the step time measured above
+        # each launch of the step is one launch of the fused quantise + GEMV
+        # kernel, so its average launch time is the step time over 128
         "roofline": {"bound": "hbm", "kernel": "k_gemv_dot<bf16 X, K<=4096> (tq_quant_ternary_gemv)",
-                     "achieved": round(value, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(value / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": b_step, "avg_launch_us": round(step_s * 1e6, 3)},
+                     "achieved": round(b_launch / launch_s / 1e9, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(b_launch / launch_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "bytes_per_launch": b_launch,
+                     "avg_launch_us": round(launch_s * 1e6, 3),
+                     "median_launch_us": round(med_launch_s * 1e6, 3)},
         "gemv_int8_input": {"kernel": "k_gemv_dot<int8 q, K<=4096> (tq_ternary_gemv)",
                             "bytes_per_launch": b_gemv, "avg_launch_us": round(gemv_s * 1e6, 3),
                             "GBs": round(gemv_gbs, 2)},
@@ -243,8 +266,8 @@ def main():
         result["extra"] = extras(torch, np, ti, tq, dev, only)
     if args.copy_calibration:
         result["copy_calibration"] = copy_calibration(torch, dev)
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(np, ti, args.cpu_seconds)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 
@@ -553,39 +576,82 @@ def extra_backward(torch, ti, tq, dev):
     return {"backward_prefill_2048x11008x4096": out}
 
 
+def _probes():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "ternary_quantized_linear_absmean_amd",
+                                   "libtq_probes.so"))
+    lib.tqp_empty.argtypes = [ctypes.c_void_p]
+    lib.tqp_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tqp_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    for f in (lib.tqp_empty, lib.tqp_read, lib.tqp_mfma_i8, lib.tqp_mfma_chains):
+        f.restype = ctypes.c_int
+    return lib
+
+
 def extra_context(torch, dev):
-    """Reference points, not this library's work: what a plain torch kernel
-    needs to stream 4 MiB per launch under the same 128-buffer rotation and
-    graph replay (the floor a 4 MiB decode GEMV sits on), and the vendor
-    int8 GEMM (hipBLASLt through torch._int_mm, int8 weights) on the prefill
-    shape."""
+    """Reference floors of the device, not this library's work, under the
+    same graph replay and buffer rotation as the layer: the cost of a launch
+    (an empty kernel, and a one-element torch op), a pure streaming read of
+    4 MiB (one 16-byte load per lane) and of larger buffers, a torch copy of
+    4 MiB, a chain of independent int8 matrix-core products (the sustained
+    int8 rate), and the vendor int8 GEMM (hipBLASLt through torch._int_mm,
+    int8 weights) on the prefill shape and at 8192^3."""
     out = {}
+    lib = _probes()
+    st = lambda: torch.cuda.current_stream().cuda_stream  # noqa: E731
+
+    def per_launch(fn, n, reps=16):
+        g = capture(torch, lambda: [fn() for _ in range(n)])
+        timed_graph(torch, g, 2)
+        return timed_graph(torch, g, reps) / n
+
+    t = per_launch(lambda: lib.tqp_empty(st()), POOL)
+    out["empty_kernel"] = {"us": round(t * 1e6, 3)}
+    one = torch.zeros(1, dtype=torch.float32, device=dev)
+    t = per_launch(lambda: one.add_(1.0), POOL)
+    out["torch_one_element_add"] = {"us": round(t * 1e6, 3)}
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    reads = {}
+    for mib, n in ((4, POOL), (16, 32), (64, 8), (256, 2)):
+        bufs = [torch.ones(mib << 18, dtype=torch.int32, device=dev) for _ in range(n)]
+        t = per_launch(lambda: [lib.tqp_read(b.data_ptr(), mib << 20, sink.data_ptr(), st())
+                                for b in bufs], 1, reps=max(4, 64 // n))
+        reads[f"{mib}MiB"] = {"us": round(t / n * 1e6, 3),
+                              "GBs": round((mib << 20) * n / t / 1e9, 1), "rotation": n}
+        del bufs
+    out["pure_read_rotating"] = reads
     pool = [torch.ones(1 << 20, dtype=torch.int32, device=dev) for _ in range(POOL)]
     dst = torch.empty(1 << 20, dtype=torch.int32, device=dev)
-    res = torch.empty((), dtype=torch.int32, device=dev)
     g = capture(torch, lambda: [dst.copy_(p) for p in pool])
     timed_graph(torch, g, 2)
     t = timed_graph(torch, g, 16) / POOL
     out["torch_copy_4MiB_rotating"] = {"us": round(t * 1e6, 3),
                                        "GBs_read_plus_write": round(8 * 2**20 / t / 1e9, 1)}
-    g = capture(torch, lambda: [torch.amax(p, dim=0, out=res) for p in pool])
-    timed_graph(torch, g, 2)
-    t = timed_graph(torch, g, 16) / POOL
-    out["torch_amax_4MiB_rotating"] = {"us": round(t * 1e6, 3),
-                                       "GBs_read": round(4 * 2**20 / t / 1e9, 1)}
     del pool
-    try:
-        M, N, K = 2048, 11008, 4096
-        A = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
-        B = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev)
-        g = capture(torch, lambda: [torch._int_mm(A, B.t()) for _ in range(8)])
-        warm(torch, g)
-        t = timed_graph(torch, g, 5) / 8
-        out["vendor_int8_gemm_prefill"] = {"api": "torch._int_mm (int8 x int8 -> int32)",
-                                           "shape": [M, N, K], "us": round(t * 1e6, 2),
-                                           "TOPS": round(2.0 * M * N * K / t / 1e12, 1)}
-    except Exception as e:  # the reference is optional context
-        out["vendor_int8_gemm_prefill"] = {"error": str(e)[:200]}
+    # int8 matrix-core chain: two waves per SIMD on every CU
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    blocks, iters = 2 * cus, 512
+    res = torch.zeros(blocks, dtype=torch.int32, device=dev)
+    g = capture(torch, lambda: lib.tqp_mfma_i8(blocks, iters, res.data_ptr(), st()))
+    warm(torch, g)
+    t = timed_graph(torch, g, 10)
+    ops = blocks * 4 * iters * lib.tqp_mfma_chains() * 2 * 32 * 32 * 32
+    out["int8_mfma_chain"] = {"instruction": "v_mfma_i32_32x32x32_i8", "us": round(t * 1e6, 2),
+                              "TOPS": round(ops / t / 1e12, 1),
+                              "pct_int8_peak": round(100 * ops / t / 1e12 / INT8_PEAK_TOPS, 2)}
+    for name, (M, N, K) in (("vendor_int8_gemm_prefill", (2048, 11008, 4096)),
+                            ("vendor_int8_gemm_8192", (8192, 8192, 8192))):
+        try:
+            A = torch.randint(-127, 128, (M, K), dtype=torch.int8, device=dev)
+            B = torch.randint(-1, 2, (N, K), dtype=torch.int8, device=dev)
+            g = capture(torch, lambda: [torch._int_mm(A, B.t()) for _ in range(4)])
+            warm(torch, g)
+            t = timed_graph(torch, g, 5) / 4
+            out[name] = {"api": "torch._int_mm (int8 x int8 -> int32)", "shape": [M, N, K],
+                         "us": round(t * 1e6, 2), "TOPS": round(2.0 * M * N * K / t / 1e12, 1)}
+            del A, B
+        except Exception as e:  # the reference is optional context
+            out[name] = {"error": str(e)[:200]}
     return out
 
 
@@ -604,30 +670,152 @@ def copy_calibration(torch, dev):
             "launches": 3}
 
 
-def cpu_baseline(np, ti, seconds):
-    """The oracle on the host: per-token quantisation + integer contraction
-    + fp64 epilogue for the decode workload, repeated for ~`seconds`."""
+# ------------------------------------------------------------- CPU oracle
+
+def host_threads():
+    """Worker count on this host: every core, at most the share the runner
+    allows (OMP_NUM_THREADS, else 16)."""
+    n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    cap = int(env) if env.isdigit() and int(env) > 0 else 16
+    return max(1, min(n, cap))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+# Worker functions of the CPU leg: each applies one oracle function to a
+# block of rows (weights) or tokens (activations).  Per-row scales, codes and
+# per-token quantisation are independent across rows and tokens, so splitting
+# them changes no arithmetic.
+def _cpu_pack_rows(W, mode):
     import oracle
-    N, K = ti.WORKLOADS["decode"]["mats"][0]
-    W = ti.workload_weights("decode")
-    X = ti.workload_activations("decode")
-    packed, scale = oracle.pack_ternary(W, "tensor")
-    n = 0
+    return oracle.pack_ternary(W, "row", mode)
+
+
+def _cpu_codes(W, gam, mode):
+    import oracle
+    q = oracle.ternarize(W, gam) if mode == "ternary" else oracle.binarize(W)
+    return oracle.pack_codes(q)
+
+
+def _cpu_quant(X):
+    import oracle
+    return oracle.quant_act_int8(X)
+
+
+def _cpu_prologue(X):
+    import oracle
+    return oracle.bitlinear_prologue(X)
+
+
+def _cpu_map(pool, fn, A, *extra):
+    import numpy as np
+    parts = [a for a in np.array_split(A, pool._max_workers) if len(a)]
+    return list(pool.map(fn, parts, *[[e] * len(parts) for e in extra]))
+
+
+def _cpu_pack(pool, W, gran, mode):
+    import numpy as np
+    import oracle
+    if gran == "row":
+        outs = _cpu_map(pool, _cpu_pack_rows, W, mode)
+        return np.concatenate([o[0] for o in outs]), np.concatenate([o[1] for o in outs])
+    gam = oracle.absmean_scales(W, "tensor")          # one exact sum over the tensor
+    return np.concatenate(_cpu_map(pool, _cpu_codes, W, gam, mode)), gam
+
+
+def _cpu_act(pool, X, prologue):
+    import numpy as np
+    outs = _cpu_map(pool, _cpu_prologue if prologue else _cpu_quant, X)
+    return np.concatenate([o[0] for o in outs]), np.concatenate([o[1] for o in outs])
+
+
+def _cpu_layer(pool, X, W, gran, mode, prologue, packed=None):
+    """One pass of the layer on the oracle: pack, quantise, contract,
+    rescale.  Returns the three stage times (s) and the packed weight."""
+    import oracle
     t0 = time.perf_counter()
-    while True:
-        q, sx = oracle.quant_act_int8(X)
-        acc = oracle.contract(q, packed, K)
-        oracle.epilogue(acc, scale, sx)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    per = el / n
-    b = gemv_bytes(1, N, K, False) + quant_bytes(1, K, 2)
-    return {"value": round(b / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n} decode steps (quant + contraction + epilogue, 1x4096x4096) in "
-                      f"{el:.1f} s, numpy int64 on one host thread",
-            "ms_per_step": round(per * 1e3, 3)}
+    if packed is None:
+        packed = _cpu_pack(pool, W, gran, mode)
+    t1 = time.perf_counter()
+    q, sx = _cpu_act(pool, X, prologue)
+    t2 = time.perf_counter()
+    oracle.epilogue(oracle.contract(q, packed[0], W.shape[1]), packed[1], sx)
+    t3 = time.perf_counter()
+    return (t1 - t0, t2 - t1, t3 - t2), packed
+
+
+def cpu_baseline(budget_s, runs):
+    """The oracle on the host for all five workloads: each stage's median
+    over up to `runs` passes (fewer once the workload's share of the budget
+    is spent, at least one).  Packing, quantisation and pack codes run on
+    `threads` forked workers over blocks of rows or tokens; the exact
+    float64 contraction runs on the BLAS with the same thread count."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    import oracle  # noqa: F401  (loaded before the workers fork)
+    import tq_inputs as ti
+
+    threads = host_threads()
+    share = {"tiny": 0.02, "decode": 0.18, "ffn": 0.2, "prefill": 0.35, "bitlinear": 0.25}
+    out = {}
+    t_all = time.perf_counter()
+    with threadpool_limits(threads), \
+            cf.ProcessPoolExecutor(threads, mp_context=mp.get_context("fork")) as pool:
+        for name, cfg in ti.WORKLOADS.items():
+            mode = cfg["modes"][0]
+            jobs = []
+            for j, (n, k) in enumerate(cfg["mats"]):
+                W = ti.workload_weights(name, j)
+                for b in cfg["batches"]:
+                    jobs.append((j, b, W, ti.workload_activations(name, j, b)))
+            stages = []
+            t0 = time.perf_counter()
+            while True:
+                packed = {}
+                run = np.zeros(3)
+                for j, b, W, X in jobs:
+                    t, packed[j] = _cpu_layer(pool, X, W, cfg["gran"], mode,
+                                              cfg.get("prologue", False), packed.get(j))
+                    run += np.array(t)
+                stages.append(run)
+                if len(stages) >= runs or time.perf_counter() - t0 > share[name] * budget_s:
+                    break
+            med = np.median(np.array(stages), axis=0)
+            rec = {"runs": len(stages), "pack_s": round(float(med[0]), 4),
+                   "quant_s": round(float(med[1]), 4),
+                   "contract_epilogue_s": round(float(med[2]), 4)}
+            if name == "decode":
+                n, k = cfg["mats"][0]
+                step = fused_bytes(1, n, k, 2, False)
+                rec["decode_step_GBs"] = round(step / float(med[1] + med[2]) / 1e9, 4)
+            if name in ("prefill", "bitlinear"):
+                n, k = cfg["mats"][0]
+                m = cfg["batches"][0]
+                rec["contract_GOPS"] = round(2.0 * m * n * k / float(med[2]) / 1e9, 2)
+            out[name] = rec
+    d = out["decode"]
+    return {"value": d["decode_step_GBs"], "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "each workload's whole layer once per run (pack, quantise, exact "
+                      "contraction, fp64 epilogue), median of the runs; value = the decode "
+                      "workload's step (quantise + contraction + epilogue of one bf16 token "
+                      "through 4096x4096) in GB/s",
+            "nproc": os.cpu_count(), "threads": threads, "cpu_model": cpu_model(),
+            "wall_s": round(time.perf_counter() - t_all, 1), "workloads": out}
 
 
 if __name__ == "__main__":

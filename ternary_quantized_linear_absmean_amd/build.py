@@ -2,9 +2,11 @@
 
     python -m ternary_quantized_linear_absmean_amd.build
 
-Each source in csrc/ is compiled to an object under _build/ (in parallel),
-then linked into ternary_quantized_linear_absmean_amd/libtq.so.  The build
-always recompiles.  Importing this module loads nothing from the library.
+Each library source in csrc/ is compiled to an object under _build/ (in
+parallel), then linked into ternary_quantized_linear_absmean_amd/libtq.so.
+csrc/bench_probes.hip (reference kernels the benchmark times beside the
+layer, not part of the library) becomes libtq_probes.so.  The build always
+recompiles.  Importing this module loads nothing from the library.
 """
 from __future__ import annotations
 
@@ -20,6 +22,9 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
+# reference kernels for the benchmark's context figures; not part of libtq
+PROBES_SRC = "bench_probes.hip"
+PROBES_LIB = os.path.join(PKG, "libtq_probes.so")
 
 ARCH = "gfx950"
 SOURCES = ["tq_api.hip", "k_pack.hip", "k_quant.hip", "k_gemv.hip", "k_gemm.hip", "k_bwd.hip"]
@@ -70,8 +75,11 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
     os.replace(tmp, LIB)
+    tmp = PROBES_LIB + ".tmp"
+    _run([cc, *COMPILE_FLAGS, "-shared", os.path.join(CSRC, PROBES_SRC), "-o", tmp])
+    os.replace(tmp, PROBES_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBES_LIB}")
     return LIB
 
 
