@@ -59,6 +59,9 @@ def parse():
                    help="comma list of extra workloads to run: "
                         "prefill,square,bitlinear,pack,ffn,steady,binary1,ffn_decode,backward,"
                         "context")
+    p.add_argument("--batches", default="",
+                   help="comma list: token counts the ffn, binary1 and ffn_decode workloads "
+                        "run (default: all of theirs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain 256 MiB device copy (for counter scaling)")
     return p.parse_args()
@@ -263,7 +266,8 @@ def main():
 
     if not args.no_extra:
         only = set(x for x in args.only.split(",") if x)
-        result["extra"] = extras(torch, np, ti, tq, dev, only)
+        batches = set(int(x) for x in args.batches.split(",") if x)
+        result["extra"] = extras(torch, np, ti, tq, dev, only, batches)
     if args.copy_calibration:
         result["copy_calibration"] = copy_calibration(torch, dev)
     if cpu is not None:
@@ -271,9 +275,10 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def extras(torch, np, ti, tq, dev, only=frozenset()):
+def extras(torch, np, ti, tq, dev, only=frozenset(), batches=frozenset()):
     out = {}
     want = (lambda name: not only or name in only)
+    keep = (lambda bs: [b for b in bs if not batches or b in batches])
     if want("prefill") or want("pack"):
         out.update(extra_prefill(torch, ti, tq, dev, want))
     if want("square"):
@@ -281,13 +286,13 @@ def extras(torch, np, ti, tq, dev, only=frozenset()):
     if want("bitlinear"):
         out.update(extra_bitlinear(torch, ti, tq, dev))
     if want("ffn"):
-        out.update(extra_ffn(torch, ti, tq, dev))
+        out.update(extra_ffn(torch, ti, tq, dev, keep))
     if want("steady"):
         out.update(extra_steady(torch, ti, tq, dev))
     if want("binary1"):
-        out.update(extra_binary1(torch, ti, tq, dev))
+        out.update(extra_binary1(torch, ti, tq, dev, keep))
     if want("ffn_decode"):
-        out.update(extra_ffn_decode(torch, ti, tq, dev))
+        out.update(extra_ffn_decode(torch, ti, tq, dev, keep))
     if want("backward"):
         out.update(extra_backward(torch, ti, tq, dev))
     if want("context"):
@@ -413,7 +418,7 @@ def extra_bitlinear(torch, ti, tq, dev):
     return out
 
 
-def extra_ffn(torch, ti, tq, dev):
+def extra_ffn(torch, ti, tq, dev, keep=list):
     out = {}
     # FFN decode shapes (per-row scales), GEMV rotation over 64 buffers each
     ffn = {}
@@ -422,7 +427,7 @@ def extra_ffn(torch, ti, tq, dev):
         p0, s0 = tq.tq_pack_ternary(W, "row")
         del W
         pool = [p0.clone() for _ in range(64)]
-        for b in ti.WORKLOADS["ffn"]["batches"]:
+        for b in keep(ti.WORKLOADS["ffn"]["batches"]):
             Xf = torch.from_numpy(ti.workload_activations("ffn", j, b)).to(dev).to(torch.bfloat16)
             qf, sf = tq.tq_quant_act_int8(Xf)
             Yf = torch.empty((b, N), dtype=torch.float32, device=dev)
@@ -468,7 +473,7 @@ def extra_steady(torch, ti, tq, dev):
     return {"gemv_steady_state": out}
 
 
-def extra_binary1(torch, ti, tq, dev):
+def extra_binary1(torch, ti, tq, dev, keep=list):
     """1-bit sign-packed binary weights (R*C/8 bytes) against the same binary
     weights in the 2-bit code format, decode GEMV 4096x4096 per-row scales,
     1 and 16 tokens, the packed weights rotating over 512 MiB per form."""
@@ -478,7 +483,7 @@ def extra_binary1(torch, ti, tq, dev):
     p2, s2 = tq.tq_pack_ternary(W, "row", "binary")
     del W
     out = {}
-    for b in (1, 16):
+    for b in keep([1, 16]):
         X = torch.from_numpy(ti.workload_activations("bitlinear", 0, b)[:b]).to(dev)
         q, sx = tq.tq_quant_act_int8(X)
         Y = torch.empty((b, N), dtype=torch.float32, device=dev)
@@ -498,7 +503,7 @@ def extra_binary1(torch, ti, tq, dev):
     return {"binary_gemv": out}
 
 
-def extra_ffn_decode(torch, ti, tq, dev):
+def extra_ffn_decode(torch, ti, tq, dev, keep=list):
     """Decode FFN with the SwiGLU clamp (gate/up 6912x2560, down 2560x6912,
     per-row scales): tq_ffn_swiglu_decode, two launches per step, the three
     packed matrices rotating over 40 sets (about 530 MB)."""
@@ -511,7 +516,7 @@ def extra_ffn_decode(torch, ti, tq, dev):
     sets = [[(p.clone(), s) for (p, s) in mats] for _ in range(40)]
     wbytes = 3 * d_ffn * d_model // 4 + 4 * (2 * d_ffn + d_model)
     out = {}
-    for b in (1, 4, 16):
+    for b in keep([1, 4, 16]):
         X = torch.from_numpy(ti.workload_activations("ffn", 0, b)).to(dev).to(torch.bfloat16)
         Y, buf = tq.tq_ffn_swiglu_decode(X, *mats, d_model, d_ffn)
         g = capture(torch, lambda: [tq.tq_ffn_swiglu_decode(X, *st, d_model, d_ffn, buffers=buf,
