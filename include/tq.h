@@ -113,6 +113,24 @@ tq_status tq_pack_ternary(const float* W, int64_t N, int64_t K, tq_gran g,
                           tq_wmode mode, uint8_t* packed, float* scale,
                           void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* tq_pack_ternary without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same inputs, outputs, results (bit for
+ * bit) and errors as tq_pack_ternary.  The per-tensor path's partial sums,
+ * flag and exponent bins live in a static device array of the library,
+ * 16 KiB per GPU (the path needs 10.5 KiB, independent of N and K; a larger
+ * need would be TQ_ERR_WORKSPACE), kept until the process ends; the per-row
+ * path uses no scratch.  The array's device address is looked up on a
+ * device's first call (hipGetSymbolAddress, a host query: make that first
+ * call outside graph capture if the capture mode forbids it).  No call
+ * allocates or frees memory.  All calls on one GPU share its array: calls
+ * that overlap in time on that GPU (other streams, other host threads) race
+ * and give undefined results; calls ordered on one stream are safe, each
+ * writing every scratch word it reads first. */
+tq_status tq_pack_ternary_noalloc(const float* W, int64_t N, int64_t K, tq_gran g,
+                                  tq_wmode mode, uint8_t* packed, float* scale,
+                                  hipStream_t stream);
+
 /* Per-token symmetric int8 quantisation (Hetman-2b s.2
  * SymmetricActivationQuantizer, reduced per token as its code does; BitRASP
  * ``fake_quant_int``), with an optional BitLinear prologue (Hetman-2b s.5).

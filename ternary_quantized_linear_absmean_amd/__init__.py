@@ -8,6 +8,7 @@ when the library has not been built (there is no fallback path).
 from __future__ import annotations
 
 __all__ = ["tq_packed_bytes", "tq_pack_workspace_bytes", "tq_pack_ternary",
+           "tq_pack_ternary_noalloc",
            "tq_quant_act_int8", "tq_fwht512", "tq_ternary_gemv", "tq_ternary_gemm",
            "tq_quant_ternary_gemv",
            "tq_packed1_bytes", "tq_pack_binary1", "tq_binary1_gemv",

@@ -5,8 +5,17 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "tq.h"
 #include "tq_internal.hpp"
+
+// Scratch of tq_pack_ternary_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  In host code `scratch` names only a
+// host-side stand-in; the device address comes from hipGetSymbolAddress
+// (scratch_ptr below), resolved once per device with that device current.
+constexpr size_t kNoallocScratchBytes = 16384;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -37,6 +46,29 @@ tq_status check_contract(const int8_t* q, const float* sx, int64_t M,
   if (!aligned(sx, 4) || !aligned(scale, 4)) return TQ_ERR_ALIGN;
   if (!aligned(Y, ydt == TQ_BF16 ? 2 : 4)) return TQ_ERR_ALIGN;
   return TQ_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices];  // device address of `scratch`, per device
+
+// The current device's copy of `scratch`, its address looked up on the
+// device's first call.
+hipError_t scratch_ptr(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_dev[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 tq::GemmArgs make_args(const int8_t* q, const float* sx, int64_t M, const uint8_t* packed,
@@ -88,6 +120,24 @@ tq_status tq_pack_ternary(const float* W, int64_t N, int64_t K, tq_gran g, tq_wm
     return hip_status(tq::launch_pack_tensor(W, N * K, mode, packed, scale, ws, stream));
   }
   return hip_status(tq::launch_pack_rows(W, N, K, mode, packed, scale, stream));
+}
+
+tq_status tq_pack_ternary_noalloc(const float* W, int64_t N, int64_t K, tq_gran g,
+                                  tq_wmode mode, uint8_t* packed, float* scale,
+                                  hipStream_t stream) {
+  if (N < 0 || K <= 0 || (K % 4) != 0) return TQ_ERR_SHAPE;
+  if (g != TQ_PER_TENSOR && g != TQ_PER_ROW) return TQ_ERR_UNSUPPORTED;
+  if (mode != TQ_TERNARY_ABSMEAN && mode != TQ_BINARY_SIGN) return TQ_ERR_UNSUPPORTED;
+  if (K >= kMaxNumelPack || N >= kMaxNumelPack / K) return TQ_ERR_UNSUPPORTED;
+  if (N == 0) return TQ_OK;
+  if (!W || !packed || !scale) return TQ_ERR_NULL;
+  if (!aligned(W, 4) || !aligned(scale, 4)) return TQ_ERR_ALIGN;
+  if (g == TQ_PER_ROW) return hip_status(tq::launch_pack_rows(W, N, K, mode, packed, scale, stream));
+  if (tq::pack_tensor_ws_bytes() > kNoallocScratchBytes) return TQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const hipError_t e = scratch_ptr(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(tq::launch_pack_tensor(W, N * K, mode, packed, scale, ws, stream));
 }
 
 // Checks of tq_quant_act_int8; fills p and tells whether a prologue is on.

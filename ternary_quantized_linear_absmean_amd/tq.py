@@ -33,6 +33,7 @@ MODES = {"ternary": 0, "binary": 1}
 THRESHOLDS = {"relative": 0, "absolute": 1}
 CODES = {"native": 0, "f0": 1, "f1": 2}
 EXPORTED = ["tq_packed_bytes", "tq_pack_workspace_bytes", "tq_pack_ternary",
+            "tq_pack_ternary_noalloc",
             "tq_quant_act_int8", "tq_fwht512", "tq_ternary_gemv", "tq_ternary_gemm",
             "tq_quant_ternary_gemv", "tq_packed1_bytes", "tq_pack_binary1",
             "tq_binary1_gemv", "tq_swiglu_gemv", "tq_ffn_swiglu_decode",
@@ -57,6 +58,8 @@ _lib.tq_pack_workspace_bytes.argtypes = [_i64, _i64, _int]
 _lib.tq_pack_workspace_bytes.restype = ctypes.c_size_t
 _lib.tq_pack_ternary.argtypes = [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.tq_pack_ternary.restype = _int
+_lib.tq_pack_ternary_noalloc.argtypes = [_vp, _i64, _i64, _int, _int, _vp, _vp, _vp]
+_lib.tq_pack_ternary_noalloc.restype = _int
 _lib.tq_quant_act_int8.argtypes = [_vp, _int, _i64, _i64, ctypes.POINTER(TqActOpts), _vp, _vp, _vp]
 _lib.tq_quant_act_int8.restype = _int
 _lib.tq_fwht512.argtypes = [_vp, _int, _i64, _i64, _int, _vp, _vp]
@@ -236,6 +239,25 @@ def tq_pack_ternary(W: torch.Tensor, granularity: str = "tensor", mode: str = "t
     _check(_lib.tq_pack_ternary(W.data_ptr(), N, K, GRANULARITY[granularity], MODES[mode],
                                 _ptr(packed), _ptr(scale), _ptr(workspace), ws_bytes,
                                 _stream(stream)), "tq_pack_ternary")
+    return packed, scale
+
+
+def tq_pack_ternary_noalloc(W: torch.Tensor, packed: torch.Tensor, scale: torch.Tensor,
+                            granularity: str = "tensor", mode: str = "ternary", stream=None):
+    """tq_pack_ternary with the library's static scratch instead of a
+    workspace: the caller passes both outputs and nothing is allocated."""
+    if not isinstance(W, torch.Tensor) or W.dim() != 2:
+        raise ValueError("W must be a 2-D tensor [N, K]")
+    N, K = W.shape
+    _arg(W, "W", torch.float32)
+    ns = _scale_numel(granularity, N)
+    _enum(MODES, mode, "mode")
+    _arg(packed, "packed", torch.uint8, numel=N * (K // 4))
+    _arg(scale, "scale", torch.float32, numel=ns)
+    _devices(W=W, packed=packed, scale=scale)
+    _check(_lib.tq_pack_ternary_noalloc(W.data_ptr(), N, K, GRANULARITY[granularity],
+                                        MODES[mode], packed.data_ptr(), scale.data_ptr(),
+                                        _stream(stream)), "tq_pack_ternary_noalloc")
     return packed, scale
 
 

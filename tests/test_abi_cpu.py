@@ -4,6 +4,7 @@ declares, and rejects bad arguments before touching HIP.
 No call here can reach a kernel launch: each one fails validation or is an
 empty (M == 0 / N == 0) call, which returns before any HIP call.
 """
+import ctypes
 import os
 import re
 
@@ -361,3 +362,19 @@ def test_package_exports_every_entry_point():
     for name in declared_functions():
         assert name in pkg.__all__, name
         assert getattr(pkg, name) is getattr(tqmod, name)
+
+
+def test_noalloc_pack_validation():
+    # argument errors return before any HIP call (no device is touched)
+    f = lib.tq_pack_ternary_noalloc
+    buf = (ctypes.c_float * 64)()
+    out = (ctypes.c_uint8 * 16)()
+    sc = (ctypes.c_float * 4)()
+    p = lambda o: ctypes.cast(o, ctypes.c_void_p)  # noqa: E731
+    assert f(p(buf), 4, 6, 0, 0, p(out), p(sc), None) == SHAPE
+    assert f(p(buf), -1, 8, 0, 0, p(out), p(sc), None) == SHAPE
+    assert f(p(buf), 4, 8, 2, 0, p(out), p(sc), None) == UNSUP
+    assert f(p(buf), 4, 8, 0, 5, p(out), p(sc), None) == UNSUP
+    assert f(None, 4, 8, 0, 0, p(out), p(sc), None) == NULL
+    assert f(p(buf), 0, 8, 0, 0, None, None, None) == OK
+    assert f(p(buf), 1 << 21, 1 << 20, 0, 0, p(out), p(sc), None) == UNSUP

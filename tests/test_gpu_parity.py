@@ -3,8 +3,8 @@
 Bars: packed bytes, scales of the plain paths, int8 codes and int32
 accumulators bit-exact; fp32 outputs within 1e-5 relative of the fp64
 oracle value; bf16 outputs within one bf16 step of the oracle's rounding.
-Full-size workloads are checked completely where the oracle is quick and on
-sampled output columns (every token) for the large GEMMs.
+Full-size workloads are checked on every output (the oracle's contraction
+is an exact float64 product of the unpacked codes).
 """
 import functools
 import sys
