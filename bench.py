@@ -588,7 +588,10 @@ def _probes():
     lib.tqp_empty.argtypes = [ctypes.c_void_p]
     lib.tqp_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
     lib.tqp_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
-    for f in (lib.tqp_empty, lib.tqp_read, lib.tqp_mfma_i8, lib.tqp_mfma_chains):
+    lib.tqp_mfma_i8_data.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p]
+    for f in (lib.tqp_empty, lib.tqp_read, lib.tqp_mfma_i8, lib.tqp_mfma_i8_data,
+              lib.tqp_mfma_chains):
         f.restype = ctypes.c_int
     return lib
 
@@ -644,6 +647,33 @@ def extra_context(torch, dev):
     out["int8_mfma_chain"] = {"instruction": "v_mfma_i32_32x32x32_i8", "us": round(t * 1e6, 2),
                               "TOPS": round(ops / t / 1e12, 1),
                               "pct_int8_peak": round(100 * ops / t / 1e12 / INT8_PEAK_TOPS, 2)}
+    # the same chains on random operands, one pair per chain
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    src = torch.randint(-128, 128, (lib.tqp_mfma_chains() * 2 * 1024,), dtype=torch.int8,
+                        device=dev, generator=gen)
+    g = capture(torch, lambda: lib.tqp_mfma_i8_data(blocks, iters, src.data_ptr(),
+                                                    res.data_ptr(), st()))
+    warm(torch, g)
+    t = timed_graph(torch, g, 10)
+    out["int8_mfma_chain_random_operands"] = {
+        "instruction": "v_mfma_i32_32x32x32_i8", "us": round(t * 1e6, 2),
+        "TOPS": round(ops / t / 1e12, 1),
+        "pct_int8_peak": round(100 * ops / t / 1e12 / INT8_PEAK_TOPS, 2)}
+    # random int8 A with random ternary B (-1, 0, +1): the operand mix of this
+    # library's contraction
+    tern = src.clone().view(-1, 2, 1024)
+    tern[:, 1] = torch.randint(-1, 2, (tern.shape[0], 1024), dtype=torch.int8, device=dev,
+                               generator=gen)
+    tern = tern.reshape(-1).contiguous()
+    g = capture(torch, lambda: lib.tqp_mfma_i8_data(blocks, iters, tern.data_ptr(),
+                                                    res.data_ptr(), st()))
+    warm(torch, g)
+    t = timed_graph(torch, g, 10)
+    out["int8_mfma_chain_random_int8_x_ternary"] = {
+        "instruction": "v_mfma_i32_32x32x32_i8", "us": round(t * 1e6, 2),
+        "TOPS": round(ops / t / 1e12, 1),
+        "pct_int8_peak": round(100 * ops / t / 1e12 / INT8_PEAK_TOPS, 2)}
     for name, (M, N, K) in (("vendor_int8_gemm_prefill", (2048, 11008, 4096)),
                             ("vendor_int8_gemm_8192", (8192, 8192, 8192))):
         try:

@@ -7,7 +7,8 @@
 //   - tqp_read: a pure streaming read, one 16-byte load per lane, the floor
 //     of a kernel that must move a given number of bytes once;
 //   - tqp_mfma_i8: independent chains of v_mfma_i32_32x32x32_i8 with
-//     operands in registers, the sustained int8 matrix-core rate.
+//     operands in registers, the sustained int8 matrix-core rate (one operand
+//     pair for all chains, or, tqp_mfma_i8_data, random operands per chain).
 // The kernels keep their loads and products alive by a data-dependent store
 // that never happens for the inputs bench.py passes (and is harmless if it
 // does: one word per wave into `sink`).
@@ -66,6 +67,42 @@ __global__ __launch_bounds__(256) void k_mfma_i8(int iters, int* __restrict__ ou
   if (s == 0x7FFFFFF1) out[blockIdx.x] = s;
 }
 
+// The same chains with operands taken from `src` (random bytes): every
+// chain multiplies its own A and B fragments, so consecutive products switch
+// the multipliers' inputs as a matrix product's do.  src holds at least
+// kChains * 2 * 64 * 16 bytes.
+__global__ __launch_bounds__(256) void k_mfma_i8_data(int iters, const v4i* __restrict__ src,
+                                                     int* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  v4i a[kChains], b[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c) {
+    a[c] = src[(2 * c) * 64 + lane];
+    b[c] = src[(2 * c + 1) * 64 + lane];
+  }
+  v16i acc[kChains];
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[c][v] = c;
+  // the B operand rotates over the chains; unrolled over the rotations so
+  // that every operand is a fixed register (iters is a multiple of kChains)
+  for (int it = 0; it < iters; it += kChains) {
+#pragma unroll
+    for (int r = 0; r < kChains; ++r)
+#pragma unroll
+      for (int c = 0; c < kChains; ++c)
+        acc[c] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[c], b[(c + r) & (kChains - 1)], acc[c],
+                                                       0, 0, 0);
+  }
+  int s = 0;
+#pragma unroll
+  for (int c = 0; c < kChains; ++c)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s += acc[c][v];
+  if (s == 0x7FFFFFF1) out[blockIdx.x] = s;
+}
+
 }  // namespace
 
 extern "C" {
@@ -92,6 +129,17 @@ int tqp_read(const void* p, int64_t bytes, unsigned* sink, hipStream_t s) {
 int tqp_mfma_i8(int blocks, int iters, int* out, hipStream_t s) {
   if (blocks <= 0 || iters <= 0 || out == nullptr) return -1;
   hipLaunchKernelGGL(k_mfma_i8, dim3(blocks), dim3(256), 0, s, iters, out);
+  return static_cast<int>(hipGetLastError());
+}
+
+// as tqp_mfma_i8 with operands from src (kChains * 2 * 1024 bytes, 16-byte
+// aligned); iters a multiple of kChains
+int tqp_mfma_i8_data(int blocks, int iters, const void* src, int* out, hipStream_t s) {
+  if (blocks <= 0 || iters <= 0 || iters % kChains != 0 || out == nullptr || src == nullptr ||
+      (reinterpret_cast<uintptr_t>(src) & 15u) != 0u)
+    return -1;
+  hipLaunchKernelGGL(k_mfma_i8_data, dim3(blocks), dim3(256), 0, s, iters,
+                     static_cast<const v4i*>(src), out);
   return static_cast<int>(hipGetLastError());
 }
 
