@@ -331,7 +331,9 @@ __global__ __launch_bounds__(kNTs) void k_gemv_lds(
 // is done by four staging waves and leaves the int8 token in LDS,
 // byte-transposed to the order of decode_codes_strided (seven operations
 // per 32-bit word) and swizzled so that the lanes' 16-byte reads fall in
-// distinct banks.  Per-wave maxima and byte sums go through small LDS arrays,
+// distinct banks.  With ternary codes a staging lane takes whole 16-value
+// units: 16-byte loads, the transposed unit built in registers and stored
+// with one 16-byte LDS write.  Per-wave maxima and byte sums go through small LDS arrays,
 // so the token costs two barriers.  Products use v_dot4 and
 // sum_k q*(c-1) = sum_k q*c - sum_k q as in the tiled kernels; the wave sum
 // is a DPP reduction.
@@ -425,10 +427,25 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   // 1. the staging waves' quads of the token (reads past K return zero)
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<void*>(src), static_cast<short>(0), K * kEl, kBufRaw);
-  RawQuad<SRC> rq[kRounds];
+  // BITS 2: a staging lane takes whole 16-value units (16 * kEl bytes in
+  // kEl 16-byte loads); BITS 1: quads, as the 8 x 4 layout needs
+  constexpr int kUnitsL = S * 4096 / 16 / kStageNT;
+  constexpr int kLdU = kEl;
+  RawQuad<SRC> rq[BITS == 2 ? 1 : kRounds];
+  v4i ru[BITS == 2 ? kUnitsL * kLdU : 1];
   if (stager) {
+    if constexpr (BITS == 2) {
 #pragma unroll
-    for (int i = 0; i < kRounds; ++i) rq[i] = load_quad<SRC>(xr, tid + kStageNT * i);
+      for (int i = 0; i < kUnitsL; ++i)
+#pragma unroll
+        for (int j = 0; j < kLdU; ++j)
+          ru[i * kLdU + j] = __builtin_bit_cast(
+              v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                       xr, ((tid + kStageNT * i) * kLdU + j) * 16, 0, 0));
+    } else {
+#pragma unroll
+      for (int i = 0; i < kRounds; ++i) rq[i] = load_quad<SRC>(xr, tid + kStageNT * i);
+    }
   }
   // 2. the wave's row in row group rg: chunk lane + 64*sl of each slice,
   // and the row's scale.  Rows >= N (also whole groups past the end) read
@@ -473,11 +490,26 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   if (SRC != 0) {
     if (stager) {
       float mx = 0.f;
+      if constexpr (BITS == 2) {
 #pragma unroll
-      for (int i = 0; i < kRounds; ++i) {
-        float v[4];
-        quad_to_f32<SRC>(rq[i], v);  // zeros past K
-        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+        for (int i = 0; i < kUnitsL * kLdU; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w = static_cast<uint32_t>(ru[i][e]);
+            if constexpr (SRC == 1) {
+              mx = fmaxf(mx, fabsf(__uint_as_float(w)));
+            } else {
+              mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(w << 16)),
+                                   fabsf(__uint_as_float(w & 0xFFFF0000u))));
+            }
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < kRounds; ++i) {
+          float v[4];
+          quad_to_f32<SRC>(rq[i], v);  // zeros past K
+          mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+        }
       }
       mx = wave_max_last(mx);
       if (lane == kWave - 1) wave_max_part[wave] = mx;
@@ -498,7 +530,42 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
     }
   }
   // 5. int8 token -> transposed, swizzled LDS; byte sums
-  if (stager) {
+  if (stager && BITS == 2) {
+    int bsum = 0;
+    const int nunit = K >> 4;
+#pragma unroll
+    for (int i = 0; i < kUnitsL; ++i) {
+      const int u = tid + kStageNT * i;
+      if (u < nunit) {
+        uint32_t d[4];  // quad b: values 4b .. 4b+3 as int8 codes
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          if constexpr (SRC == 0) {
+            d[b] = static_cast<uint32_t>(ru[i][b]);
+          } else {
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int val = 4 * b + e;  // value of the unit
+              if constexpr (SRC == 1) {
+                v[e] = __uint_as_float(static_cast<uint32_t>(ru[i * kLdU + val / 4][val % 4]));
+              } else {
+                const uint32_t w = static_cast<uint32_t>(ru[i * kLdU + val / 8][(val % 8) / 2]);
+                v[e] = __uint_as_float((val & 1) ? (w & 0xFFFF0000u) : (w << 16));
+              }
+            }
+            d[b] = quant_byte(v[0], sc) | (quant_byte(v[1], sc) << 8) |
+                   (quant_byte(v[2], sc) << 16) | (quant_byte(v[3], sc) << 24);
+            if (blockIdx.x == 0) reinterpret_cast<uint32_t*>(q_out)[4 * u + b] = d[b];
+          }
+          bsum = byte_sum(d[b], bsum);
+        }
+        *reinterpret_cast<v4i*>(xt + dot_slot(u)) = transpose_bytes4x4(d[0], d[1], d[2], d[3]);
+      }
+    }
+    bsum = wave_isum_last(bsum);
+    if (lane == kWave - 1) wave_sum_part[wave] = bsum;
+  } else if (stager) {
     int bsum = 0;
 #pragma unroll
     for (int i = 0; i < kRounds; ++i) {
