@@ -818,6 +818,7 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
   // spread over the stage, the loads do not reach the memory system in one
   // burst from every wave at once)
   static_assert(CA + CB == 4 * FM && CA == CB, "one load and one store piece per group");
+  static_assert(FM == FN, "one A and one B fragment read per group");
   auto compute = [&](int buf, Regs& st, Regs& ld, int64_t kld) {
     const uint8_t* sa = lds + buf * kWStage + ard;
     const uint8_t* sb = lds + buf * kWStage + brd;
@@ -828,21 +829,19 @@ __global__ __launch_bounds__(kWNT, 1) void k_gemm_wide(
     for (int j = 0; j < FN; ++j) bc[j] = *reinterpret_cast<const v4i*>(sb + j * 32 * kWLD);
 #pragma unroll
     for (int kk = 0; kk < kWBK / 32; ++kk) {
-      if (kk + 1 < kWBK / 32) {
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          an[i] = *reinterpret_cast<const v4i*>(sa + i * 32 * kWLD + 32 * (kk + 1));
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bn[j] = *reinterpret_cast<const v4i*>(sb + j * 32 * kWLD + 32 * (kk + 1));
-      }
-      // the reads for the next K step stay ahead of this step's products
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ac[i], bc[j], acc[i][j], 0, 0, 0);
+        // the next K step's fragments, two reads per group of products: a
+        // burst of eight per wave fills the LDS command queue and stalls
+        // the products behind it
+        if (kk + 1 < kWBK / 32) {
+          an[i] = *reinterpret_cast<const v4i*>(sa + i * 32 * kWLD + 32 * (kk + 1));
+          bn[i] = *reinterpret_cast<const v4i*>(sb + i * 32 * kWLD + 32 * (kk + 1));
+        }
         put_piece(st, buf ^ 1, kk * FM + i);
         load_piece(ld, kld, kk * FM + i);
         __builtin_amdgcn_sched_barrier(0);
