@@ -31,6 +31,7 @@
 // more than the main loop's last third.
 
 #include <type_traits>
+#include <utility>
 
 #include "tq_device.hpp"
 #include "tq_internal.hpp"
@@ -431,6 +432,18 @@ __device__ inline void store_acc32_staged(const v16i (&acc)[FM][FN], int64_t mb,
 constexpr int kBufFlags = 0x00020000;  // raw buffer, 32-bit data format
 constexpr int kKS = kBK / 32;          // MFMA K steps per stage
 
+template <int I>
+using ic = std::integral_constant<int, I>;
+// f(ic<0>{}), ..., f(ic<N-1>{}) in order
+template <int... I, class F>
+__device__ __forceinline__ void static_for_impl(std::integer_sequence<int, I...>, F&& f) {
+  (f(ic<I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(std::make_integer_sequence<int, N>{}, f);
+}
+
 __device__ inline int swz(int row, int chunk) {
   return row * kBK + 16 * (chunk ^ (((row >> 1) ^ (row >> 4)) & 3));
 }
@@ -455,7 +468,10 @@ constexpr int fast_lds_size() {
 // covers KG x 64 of K; group g contracts the stage's 64-deep sub-tile g into
 // its own accumulators, and the groups' sums meet in LDS at the end (exact
 // int32 additions).  KG = 2 gives small grids twice the waves per tile.
-template <int BM, int BN, int WM, int WN, int YT, int KG = 1>
+// The loads of stage kt+D go out while stage kt is contracted, so D-1 stages
+// of compute cover a load's latency; D+1 register sets hold the stages in
+// flight.
+template <int BM, int BN, int WM, int WN, int YT, int KG = 1, int D = 2>
 __device__ __forceinline__ void gemm_fast_tile(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
@@ -489,24 +505,28 @@ __device__ __forceinline__ void gemm_fast_tile(
   const __amdgpu_buffer_rsrc_t rb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(packed), static_cast<short>(0), static_cast<int>(N * rowbytes),
       kBufFlags);
-  // per-thread global offsets and LDS slots, fixed for the K loop
+  // per-thread global offsets and LDS slots, fixed for the K loop.  Chunks
+  // are numbered sub-tile by sub-tile, four to a row: the 16 lanes of a
+  // quarter-wave store four consecutive rows of one sub-tile, a pattern free
+  // of bank conflicts under the swizzle.  (Rows of two sub-tiles lie a
+  // multiple of 256 bytes apart, on the same banks.)
   uint32_t aoff[CA];
   int ast[CA];
 #pragma unroll
   for (int i = 0; i < CA; ++i) {
     const int c = tid + NT * i;
-    const int r = c / CPR, ch = c % CPR;
-    aoff[i] = static_cast<uint32_t>((m0 + r) * K + 16 * ch);
-    ast[i] = (ch / 4) * ASZ + swz(r, ch % 4);
+    const int sub = c / (4 * BM), r = (c / 4) % BM, cc = c % 4;
+    aoff[i] = static_cast<uint32_t>((m0 + r) * K + 64 * sub + 16 * cc);
+    ast[i] = sub * ASZ + swz(r, cc);
   }
   uint32_t boff[CB];
   int bst[CB];
 #pragma unroll
   for (int i = 0; i < CB; ++i) {
     const int c = tid + NT * i;
-    const int r = c / CPR, wi = c % CPR;
-    boff[i] = static_cast<uint32_t>((n0 + r) * rowbytes + 4 * wi);
-    bst[i] = (wi / 4) * BSZ + swz(r, wi % 4);
+    const int sub = c / (4 * BN), r = (c / 4) % BN, cc = c % 4;
+    boff[i] = static_cast<uint32_t>((n0 + r) * rowbytes + 16 * sub + 4 * cc);
+    bst[i] = sub * BSZ + swz(r, cc);
   }
   // this group's fragments: sub-tile grp of each stage
   int ard[FM][kKS], brd[FN][kKS];
@@ -520,8 +540,30 @@ __device__ __forceinline__ void gemm_fast_tile(
 
   typedef v4i ARegs[CA];
   typedef uint32_t BRegs[CB];
-  ARegs ra0, ra1, ra2;
-  BRegs rb0, rb1, rb2;
+  constexpr int P = D + 1;
+  static_assert(D >= 2 && D <= 5, "load distance");
+  // named sets, picked by compile-time index (an array of sets allocates
+  // worse once the loop is unrolled)
+  ARegs ra0, ra1, ra2, ra3, ra4, ra5;
+  BRegs rb0, rb1, rb2, rb3, rb4, rb5;
+  auto aset = [&](auto I) -> ARegs& {
+    constexpr int i = decltype(I)::value % P;
+    if constexpr (i == 0) return ra0;
+    else if constexpr (i == 1) return ra1;
+    else if constexpr (i == 2) return ra2;
+    else if constexpr (i == 3) return ra3;
+    else if constexpr (i == 4) return ra4;
+    else return ra5;
+  };
+  auto bset = [&](auto I) -> BRegs& {
+    constexpr int i = decltype(I)::value % P;
+    if constexpr (i == 0) return rb0;
+    else if constexpr (i == 1) return rb1;
+    else if constexpr (i == 2) return rb2;
+    else if constexpr (i == 3) return rb3;
+    else if constexpr (i == 4) return rb4;
+    else return rb5;
+  };
   // piece p of a stage: p < CA an activation chunk, else a packed word
   auto load_piece = [&](int64_t kt, ARegs& a, BRegs& b, int p) {
     const int soa = static_cast<int>(kt * kBK * KG), sob = static_cast<int>(kt * (kBK / 4) * KG);
@@ -554,9 +596,9 @@ __device__ __forceinline__ void gemm_fast_tile(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
 
   const int64_t nk = K / (kBK * KG);
-  // one stage: contract stage kt from LDS, move stage kt+1 (loaded during
-  // the previous stage) from registers into the other LDS half, load stage
-  // kt+2.  The pieces of the move and the loads go out after each group of
+  // one stage: contract stage kt from LDS, move stage kt+1 (loaded D-1
+  // stages earlier) from registers into the other LDS half, load stage
+  // kt+D.  The pieces of the move and the loads go out after each group of
   // FN products, so that neither arrives in one burst from every wave.  In
   // the main loop (GUARD false) every stage issues its
   // loads and stores unconditionally: a branch around the loads would leave
@@ -569,7 +611,7 @@ __device__ __forceinline__ void gemm_fast_tile(
                    auto guard) {
     constexpr bool GUARD = decltype(guard)::value;
     const int buf = static_cast<int>(kt & 1);
-    const bool do_load = !GUARD || kt + 2 < nk, do_store = !GUARD || kt + 1 < nk;
+    const bool do_load = !GUARD || kt + D < nk, do_store = !GUARD || kt + 1 < nk;
     v4i ac[FM], an[FM], bc[FN], bn[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) ac[i] = *reinterpret_cast<const v4i*>(&As[(buf) * SA + ard[i][0]]);
@@ -595,7 +637,7 @@ __device__ __forceinline__ void gemm_fast_tile(
 #pragma unroll
         for (int p = g; p < kPieces; p += kGroups) {
           if (do_store) store_piece(buf ^ 1, a_next, b_next, p);
-          if (do_load) load_piece(kt + 2, a_far, b_far, p);
+          if (do_load) load_piece(kt + D, a_far, b_far, p);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -609,20 +651,23 @@ __device__ __forceinline__ void gemm_fast_tile(
   using Free = std::false_type;
   using Guarded = std::true_type;
 
-  load_stage(0, ra0, rb0);
-  load_stage(1, ra1, rb1);
+  static_for<D>([&](auto J) { load_stage(J.value, aset(J), bset(J)); });
   store_stage(0, ra0, rb0);
   __syncthreads();
-  // register sets rotate with period three: stage kt reads set (kt+1)%3 and
-  // fills set (kt+2)%3
+  // register sets rotate with period P: stage kt reads set (kt+1)%P and
+  // fills set (kt+D)%P
   int64_t kt = 0;
-  for (; kt + 3 <= nk; kt += 3) {
-    stage(kt, ra1, rb1, ra2, rb2, Free{});
-    stage(kt + 1, ra2, rb2, ra0, rb0, Free{});
-    stage(kt + 2, ra0, rb0, ra1, rb1, Free{});
+  for (; kt + P <= nk; kt += P) {
+    static_for<P>([&](auto J) {
+      stage(kt + J.value, aset(ic<J.value + 1>{}), bset(ic<J.value + 1>{}), aset(ic<J.value + D>{}),
+            bset(ic<J.value + D>{}), Free{});
+    });
   }
-  if (kt < nk) stage(kt, ra1, rb1, ra2, rb2, Guarded{});
-  if (kt + 1 < nk) stage(kt + 1, ra2, rb2, ra0, rb0, Guarded{});
+  static_for<P - 1>([&](auto J) {
+    if (kt + J.value < nk)
+      stage(kt + J.value, aset(ic<J.value + 1>{}), bset(ic<J.value + 1>{}), aset(ic<J.value + D>{}),
+            bset(ic<J.value + D>{}), Guarded{});
+  });
 
   if constexpr (KG > 1) {
     // groups 1.. leave their sums in LDS (the staging tiles are free after
@@ -678,7 +723,7 @@ __device__ __forceinline__ void gemm_fast_tile(
                            M, N, Y, ep + wl * staged_lds_words<FN>());
 }
 
-template <int BM, int BN, int WM, int WN, int YT, int KG>
+template <int BM, int BN, int WM, int WN, int YT, int KG, int D>
 __global__ __launch_bounds__(WM* WN* KG* kWave, WM* WN* KG >= 16 ? 1 : 2) void k_gemm_fast(
     const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
     const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
@@ -686,23 +731,263 @@ __global__ __launch_bounds__(WM* WN* KG* kWave, WM* WN* KG >= 16 ? 1 : 2) void k
   __shared__ __attribute__((aligned(16))) uint8_t lds[fast_lds_size<BM, BN, WM, WN, KG>()];
   int64_t tm, tn;
   xcd_tile(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, gm, tm, tn);
-  gemm_fast_tile<BM, BN, WM, WN, YT, KG>(q, sx, M, packed, scale, per_row, N, K, Y, tm, tn,
-                                         lds);
+  gemm_fast_tile<BM, BN, WM, WN, YT, KG, D>(q, sx, M, packed, scale, per_row, N, K, Y, tm, tn,
+                                            lds);
 }
 
-template <int BM, int BN, int WM, int WN, int KG = 1>
+template <int BM, int BN, int WM, int WN, int KG = 1, int D = 2>
 hipError_t gemm_fast_launch(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
   const int64_t grid = tiles_m * tiles_n;
   const int64_t gm = xcd_group_m(tiles_m, tiles_n, BM, BN);
   constexpr int NT = WM * WN * KG * kWave;
 #define TQ_GEMM_FAST(YTV)                                                                      \
-  hipLaunchKernelGGL((k_gemm_fast<BM, BN, WM, WN, YTV, KG>), dim3(grid), dim3(NT), 0, s, a.q, \
+  hipLaunchKernelGGL((k_gemm_fast<BM, BN, WM, WN, YTV, KG, D>), dim3(grid), dim3(NT), 0, s, a.q, \
                      a.sx, a.M, a.packed, a.scale, a.per_row, a.N, a.K, a.Y, gm)
   if (a.ydt == TQ_F32) TQ_GEMM_FAST(TQ_F32);
   else if (a.ydt == TQ_BF16) TQ_GEMM_FAST(TQ_BF16);
   else TQ_GEMM_FAST(TQ_I32);
 #undef TQ_GEMM_FAST
+  return hipGetLastError();
+}
+
+// Small grids with few token rows (at most one 32 x 64 tile per CU, e.g. 128
+// x 4096): the tiles are too few to hide a load's latency behind other
+// workgroups, and each tile walks a long K.  Four waves hold the same
+// 32 FM x 32 FN tile and split K between them: wave w takes the 128-deep
+// blocks w, w + KG, w + 2 KG, ..., keeps D of them in flight in registers,
+// and meets the other waves only once, at the end.
+//   - tokens: loaded eight lanes to a 128-byte row (16 bytes each, whole
+//     cache lines), written into one of the wave's two private LDS slots and
+//     read back as MFMA fragments.  A fragment read straight from global
+//     memory would touch 32 rows per load, four times the cache-line lookups
+//     of the row-wise load; the slot is the wave's own, so no barrier is
+//     needed.  Rows are 128 bytes apart and chunk c of row w sits at
+//     position c ^ sw(w): both the row writes and the fragment reads (16
+//     consecutive rows, one chunk) fall on distinct banks;
+//   - codes: lane (r, h) = (l % 32, l / 32) loads the 16 packed bytes of
+//     column 32 j + r that cover K offsets 64 h .. 64 h + 63 of the block,
+//     and MFMA step s decodes word s of them: the 16 codes of K offsets
+//     64 h + 16 s .., the same 16 K values as the token chunk 4 h + s that
+//     the lane's fragment holds.
+// The products pair equal K values, so the sums are exact whatever order the
+// matrix unit takes inside a step.  Loads past a wave's last block go
+// through a buffer descriptor of zero size: they return zeros and touch no
+// memory, and stay unconditional so that the compiler can count the loads
+// in flight.  At the end wave w owns the column fragments [w FN / KG,
+// (w + 1) FN / KG) (fragment w when FN < KG), adds the other waves' partial
+// sums of them from LDS (exact int32 additions) and stores them with the
+// staged epilogue.
+constexpr int kRBK = 128;  // K per block
+
+template <int FM, int FN, int KG>
+constexpr int reg_own() { return FN >= KG ? FN / KG : 1; }
+template <int FM, int FN, int KG>
+constexpr int reg_lds_bytes() {
+  constexpr int slots = KG * 2 * FM * 32 * kRBK;
+  constexpr int red = FN * (KG - 1) * FM * 16 * kWave * 4;
+  constexpr int epi = (KG * staged_lds_words<reg_own<FM, FN, KG>()>() + 32 * FM + 32 * FN) * 4;
+  return slots > red ? (slots > epi ? slots : epi) : (red > epi ? red : epi);
+}
+
+template <int FM, int FN, int KG, int D, int YT>
+__global__ __launch_bounds__(KG* kWave) void k_gemm_reg(
+    const int8_t* __restrict__ q, const float* __restrict__ sx, int64_t M,
+    const uint8_t* __restrict__ packed, const float* __restrict__ scale, int per_row,
+    int64_t N, int64_t K, void* __restrict__ Y, int64_t gm) {
+  constexpr int BM = 32 * FM, BN = 32 * FN;
+  constexpr int OWN = reg_own<FM, FN, KG>();
+  constexpr int SLOT = FM * 32 * kRBK;  // bytes of one token slot
+  static_assert(FN % KG == 0 || KG % FN == 0, "column ownership");
+  static_assert(D >= 2 && D <= 5, "blocks in flight");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[reg_lds_bytes<FM, FN, KG>()];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  int64_t tm, tn;
+  xcd_tile(blockIdx.x, (M + BM - 1) / BM, (N + BN - 1) / BN, gm, tm, tn);
+  const int64_t m0 = tm * BM, n0 = tn * BN;
+  const int64_t rowbytes = K >> 2;
+  const int r = lane & 31, h = lane >> 5;
+
+  const __amdgpu_buffer_rsrc_t ra_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(q), static_cast<short>(0), static_cast<int>(M * K), kBufFlags);
+  const __amdgpu_buffer_rsrc_t rb_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed), static_cast<short>(0), static_cast<int>(N * rowbytes),
+      kBufFlags);
+  const __amdgpu_buffer_rsrc_t ra_none = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<int8_t*>(q), static_cast<short>(0), 0, kBufFlags);
+  const __amdgpu_buffer_rsrc_t rb_none = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(packed), static_cast<short>(0), 0, kBufFlags);
+  // token chunk t of a block: rows 8t .. 8t+7 of the tile, chunk lane % 8
+  auto sw = [](int w) { return (w ^ (w >> 3)) & 7; };
+  uint32_t aoff[4 * FM], boff[FN];
+  int wst[4 * FM], frd[FM][4];
+#pragma unroll
+  for (int t = 0; t < 4 * FM; ++t) {
+    const int w = 8 * t + lane / 8;
+    aoff[t] = static_cast<uint32_t>((m0 + w) * K + 16 * (lane % 8));
+    wst[t] = w * kRBK + 16 * ((lane % 8) ^ sw(w));
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int w = 32 * i + r;
+      frd[i][s] = w * kRBK + 16 * ((4 * h + s) ^ sw(w));
+    }
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    boff[j] = static_cast<uint32_t>((n0 + 32 * j + r) * rowbytes + 16 * h);
+  const int nb = static_cast<int>(K / kRBK);
+  const int nbw = wave < nb ? (nb - wave + KG - 1) / KG : 0;  // this wave's blocks
+
+  v16i acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+  struct Blk {
+    v4i a[4 * FM];
+    v4i b[FN];
+  };
+  Blk s0, s1, s2, s3, s4;
+  auto set = [&](auto I) -> Blk& {
+    constexpr int i = decltype(I)::value % D;
+    if constexpr (i == 0) return s0;
+    else if constexpr (i == 1) return s1;
+    else if constexpr (i == 2) return s2;
+    else if constexpr (i == 3) return s3;
+    else return s4;
+  };
+  // block jw of this wave (K offset (wave + KG jw) * 128)
+  auto load_blk = [&](int jw, Blk& x) {
+    const bool live = jw < nbw;
+    const int blk = wave + KG * jw;
+    const __amdgpu_buffer_rsrc_t ra = live ? ra_rsrc : ra_none;
+    const __amdgpu_buffer_rsrc_t rb = live ? rb_rsrc : rb_none;
+    const int sa = live ? blk * kRBK : 0, sb = live ? blk * (kRBK / 4) : 0;
+#pragma unroll
+    for (int t = 0; t < 4 * FM; ++t)
+      x.a[t] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[t], sa, 0));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      x.b[j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rb, boff[j], sb, 0));
+  };
+  auto compute_blk = [&](const Blk& x, int jw) {
+    uint8_t* const slot = lds + (wave * 2 + (jw & 1)) * SLOT;
+#pragma unroll
+    for (int t = 0; t < 4 * FM; ++t) *reinterpret_cast<v4i*>(slot + wst[t]) = x.a[t];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      v4i af[FM], bd[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const v4i*>(slot + frd[i][s]);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bd[j] = decode_signed_natural(static_cast<uint32_t>(x.b[j][s]));
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bd[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  static_for<D>([&](auto J) { load_blk(J.value, set(J)); });
+  int jw = 0;
+  // the scheduling barriers keep each block's refill right after its
+  // products (left free, the scheduler sinks every load below the last
+  // block's products, and each pass then waits for all of them)
+  for (; jw + D <= nbw; jw += D) {
+    static_for<D>([&](auto J) {
+      compute_blk(set(J), jw + J.value);
+      __builtin_amdgcn_sched_barrier(0);
+      load_blk(jw + J.value + D, set(J));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+  static_for<D - 1>([&](auto J) {
+    if (jw + J.value < nbw) compute_blk(set(J), jw + J.value);
+  });
+  __syncthreads();  // the slots overlap the exchange area
+
+  // exchange: every fragment goes to its owner; the others leave it in LDS
+  auto owner = [](int j) { return FN >= KG ? j / OWN : j; };
+  int* const red = reinterpret_cast<int*>(lds);
+  auto slot_of = [&](int j, int w) {  // partial sums of fragment j from wave w
+    const int o = owner(j);
+    return ((j * (KG - 1) + (w < o ? w : w - 1)) * FM) * 16 * kWave;
+  };
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if (owner(j) == wave) continue;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        red[slot_of(j, wave) + (i * 16 + v) * kWave + lane] = acc[i][j][v];
+  }
+  __syncthreads();
+  v16i own[FM][OWN];
+  const int j0 = FN >= KG ? wave * OWN : wave;
+  const bool owns = j0 < FN;
+#pragma unroll
+  for (int t = 0; t < OWN; ++t)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      v16i x = acc[i][0];
+#pragma unroll
+      for (int j = 1; j < FN; ++j)
+        if (j == j0 + t) x = acc[i][j];
+      if (owns) {
+#pragma unroll
+        for (int w = 0; w < KG; ++w) {
+          if (w == wave) continue;
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            x[v] += red[slot_of(j0 + t, w) + (i * 16 + v) * kWave + lane];
+        }
+      }
+      own[i][t] = x;
+    }
+
+  // staged epilogue (the exchange area is free once every wave is past it)
+  int* const ep = reinterpret_cast<int*>(lds);
+  float* const sxs = reinterpret_cast<float*>(ep + KG * staged_lds_words<OWN>());
+  float* const gms = sxs + BM;
+  __syncthreads();
+  if (YT != TQ_I32) {
+    for (int x = tid; x < BM; x += KG * kWave) {
+      const int64_t m = m0 + x;
+      sxs[x] = sx[m < M ? m : M - 1];
+    }
+    for (int x = tid; x < BN; x += KG * kWave) {
+      const int64_t n = n0 + x;
+      gms[x] = scale[per_row ? (n < N ? n : N - 1) : 0];
+    }
+  }
+  __syncthreads();
+  if (owns)
+    store_acc32_staged<YT>(own, m0, n0 + 32 * j0, lane, sxs, gms + 32 * j0, M, N, Y,
+                           ep + wave * staged_lds_words<OWN>());
+}
+
+template <int FM, int FN, int KG, int D>
+hipError_t gemm_reg_launch(const GemmArgs& a, hipStream_t s) {
+  constexpr int BM = 32 * FM, BN = 32 * FN;
+  const int64_t tiles_m = (a.M + BM - 1) / BM, tiles_n = (a.N + BN - 1) / BN;
+  const int64_t gm = xcd_group_m(tiles_m, tiles_n, BM, BN);
+#define TQ_GEMM_REG(YTV)                                                                    \
+  hipLaunchKernelGGL((k_gemm_reg<FM, FN, KG, D, YTV>), dim3(tiles_m * tiles_n),              \
+                     dim3(KG * kWave), 0, s, a.q, a.sx, a.M, a.packed, a.scale, a.per_row, a.N, \
+                     a.K, a.Y, gm)
+  if (a.ydt == TQ_F32) TQ_GEMM_REG(TQ_F32);
+  else if (a.ydt == TQ_BF16) TQ_GEMM_REG(TQ_BF16);
+  else TQ_GEMM_REG(TQ_I32);
+#undef TQ_GEMM_REG
   return hipGetLastError();
 }
 
@@ -906,6 +1191,10 @@ hipError_t gemm_fast_dispatch(const GemmArgs& a, hipStream_t s) {
   // wide tiles run one workgroup per CU: they pay off when every round of
   // tiles, the last one included, fills at least half of the chip
   const int64_t cus = device_cus() > 0 ? device_cus() : 256;
+  // at most one 32 x 64 tile per CU: K split over four waves (measured
+  // 10.1 against 12.0 us at 128 x 4096 x 4096 and 12.8 against 16.3 us at
+  // 64 x 2560 x 6912; with more tiles the staged tiles below are faster)
+  if (a.K % kRBK == 0 && tiles(32, 64) <= cus) return gemm_reg_launch<1, 2, 4, 4>(a, s);
   const int64_t tw = tiles(kWBM, kWBN), last = tw % cus;
   if (tw >= cus && (last == 0 || 2 * last >= cus) && a.K % (2 * kWBK) == 0)
     return gemm_wide_launch(a, s);

@@ -570,6 +570,41 @@ def test_gemm_small_grid_tiles(M, N, K):
                        q, packed, sc, sx)
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 64, 128), (17, 4096, 128), (100, 4000, 384),
+                                   (64, 2560, 6912), (128, 4096, 1152), (33, 4096, 11008),
+                                   (128, 4096, 4096), (5, 130, 640)])
+def test_gemm_register_tiles(M, N, K):
+    # at most one 32 x 64 tile per CU and K % 128 == 0: four waves split the
+    # 128-deep blocks of K (one block: three waves hold none; 3, 5, 9 or 86
+    # blocks: unequal shares and the pipeline's tail), ragged in M and N;
+    # every output
+    q = ti.random_int8(M + 5 * K, M, K)
+    w = ti.random_ternary(N + 5 * K, N, K)
+    packed = oracle.pack_codes(w)
+    scale = (np.abs(ti.activations(N + 7, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(M + 8, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    say(f"gemm register tiles M={M} N={N} K={K}")
+    for gran, sc in (("row", scale), ("tensor", scale[:1])):
+        _check_outputs(tq.tq_ternary_gemm, dev(q), dev(sx), dev(packed), dev(sc), N, K, gran,
+                       q, packed, sc, sx)
+
+
+def test_gemm_register_tiles_extremes():
+    # |acc| = 127 K at K = 11008 in both signs, over the four waves' shares
+    M, N, K = 40, 96, 11008
+    q = np.full((M, K), 127, np.int8)
+    q[1::2] = -127
+    w = np.ones((N, K), np.int8)
+    w[1::3] = -1
+    w[2::3, ::2] = 0
+    packed = oracle.pack_codes(w)
+    scale = np.array([0.25], np.float32)
+    sx = np.linspace(0.5, 2.0, M).astype(np.float32)
+    say("gemm register tiles extremes")
+    _check_outputs(tq.tq_ternary_gemm, dev(q), dev(sx), dev(packed), dev(scale), N, K,
+                   "tensor", q, packed, scale, sx)
+
+
 def _rne_bf16_bits(y32):
     # round-to-nearest-even of finite fp32 values to bf16, on the bit pattern
     u = np.ascontiguousarray(y32, np.float32).view(np.uint32).astype(np.uint64)
