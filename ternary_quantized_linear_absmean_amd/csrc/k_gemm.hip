@@ -10,7 +10,10 @@
 // each packed word is read from global memory once per workgroup tile,
 // decoded once into signed int8 in LDS, and fed to v_mfma_i32_32x32x32_i8.
 //
-// Three kernels, picked by shape:
+// Four kernels, picked by shape:
+//   - k_gemm_reg (K % 128 == 0, aligned, at most one 32 x 64 tile per CU):
+//     four waves split K over one tile, operands in registers several
+//     blocks ahead, tokens re-laid through a private LDS slot per wave;
 //   - k_gemm_fast (K % 64 == 0, aligned): both operand tiles staged through a
 //     double-buffered, swizzled LDS tile, eight- or four-wave workgroups,
 //     two workgroups per CU (see the fast-path notes below);
