@@ -57,8 +57,8 @@ def parse():
                    help="runs per workload for the CPU median (fewer past the budget)")
     p.add_argument("--only", default="",
                    help="comma list of extra workloads to run: "
-                        "prefill,square,bitlinear,pack,ffn,steady,binary1,ffn_decode,backward,"
-                        "context")
+                        "prefill,square,bitlinear,smallgemm,pack,ffn,steady,binary1,ffn_decode,"
+                        "backward,context")
     p.add_argument("--batches", default="",
                    help="comma list: token counts the ffn, binary1 and ffn_decode workloads "
                         "run (default: all of theirs)")
@@ -285,6 +285,8 @@ def extras(torch, np, ti, tq, dev, only=frozenset(), batches=frozenset()):
         out.update(extra_square(torch, tq, dev))
     if want("bitlinear"):
         out.update(extra_bitlinear(torch, ti, tq, dev))
+    if want("smallgemm"):
+        out.update(extra_small_gemm(torch, ti, tq, dev))
     if want("ffn"):
         out.update(extra_ffn(torch, ti, tq, dev, keep))
     if want("steady"):
@@ -415,6 +417,51 @@ def extra_bitlinear(torch, ti, tq, dev):
     out["bitlinear_gemm"] = {"shape": [512, 4096, 4096], "us": round(t * 1e6, 2),
                              "TOPS": round(tops, 1),
                              "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)}
+    out["vendor_int8_gemm_bitlinear"] = vendor_int8_gemm(torch, dev, qb, 4096, 4096, reps)
+    return out
+
+
+def vendor_int8_gemm(torch, dev, q, N, K, reps):
+    """The vendor int8 GEMM (torch._int_mm, int8 weights: four times the
+    packed weight's bytes) on the same tokens, as context."""
+    try:
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(N + K)
+        B = torch.randint(-1, 2, (N, K), generator=gen, device=dev).to(torch.int8)
+        g = capture(torch, lambda: [torch._int_mm(q, B.t()) for _ in range(reps)])
+        warm(torch, g)
+        t = timed_graph(torch, g, 5) / reps
+        return {"api": "torch._int_mm (int8 x int8 -> int32)", "us": round(t * 1e6, 2),
+                "TOPS": round(2.0 * q.shape[0] * N * K / t / 1e12, 1)}
+    except Exception as e:  # the reference is optional context
+        return {"error": str(e)[:200]}
+
+
+def extra_small_gemm(torch, ti, tq, dev):
+    """GEMMs with few token rows (at most one 32 x 64 tile per CU: the
+    K-split register-fed tiles), fp32 out, per-row gamma, next to the vendor
+    int8 GEMM: 128 tokens through a 4096 x 4096 projection and 64 tokens
+    through the FFN down projection 2560 x 6912."""
+    out = {}
+    reps = 8
+    for M, (N, K), name in ((128, (4096, 4096), "gemm_128x4096x4096"),
+                            (64, (2560, 6912), "gemm_64x2560x6912")):
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(M * N + K)
+        W = torch.randn((N, K), generator=gen, device=dev) * 0.02
+        packed, scale = tq.tq_pack_ternary(W, "row")
+        X = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+        q, sx = tq.tq_quant_act_int8(X)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        g = capture(torch, lambda: [tq.tq_ternary_gemm(q, sx, packed, scale, N, K, "row", "f32",
+                                                       Y=Y) for _ in range(reps)])
+        warm(torch, g)
+        t = timed_graph(torch, g, 5) / reps
+        tops = 2.0 * M * N * K / t / 1e12
+        out[name] = {"shape": [M, N, K], "out": "f32", "kernel": "k_gemm_reg",
+                     "us": round(t * 1e6, 2), "TOPS": round(tops, 1),
+                     "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2),
+                     "vendor_int8_gemm": vendor_int8_gemm(torch, dev, q, N, K, reps)}
     return out
 
 
