@@ -172,6 +172,13 @@ __global__ __launch_bounds__(NT) void k_quant_small(const T* __restrict__ X, int
 // v_permlane16_swap / v_permlane32_swap of v with itself for 16 / 32 (the
 // first result holds, in the upper lane of each pair, the lower one's value,
 // the second result the reverse).  The moves leave the values untouched.
+// a row permutation that has a source lane for every lane (the mirrors):
+// no old value to keep, so no move to initialise one
+template <int CTRL>
+__device__ inline int dpp_all(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
+}
+
 template <int LM>
 __device__ inline float lane_xor(float v) {
   const int i = __float_as_int(v);
@@ -180,9 +187,9 @@ __device__ inline float lane_xor(float v) {
   } else if constexpr (LM == 2) {
     return __int_as_float(dpp_get<0x4E>(i));
   } else if constexpr (LM == 4) {
-    return __int_as_float(dpp_get<0x1B>(dpp_get<0x141>(i)));
+    return __int_as_float(dpp_get<0x1B>(dpp_all<0x141>(i)));
   } else if constexpr (LM == 8) {
-    return __int_as_float(dpp_get<0x141>(dpp_get<0x140>(i)));
+    return __int_as_float(dpp_get<0x141>(dpp_all<0x140>(i)));
   } else {
     static_assert(LM == 16 || LM == 32, "lane distance");
     const unsigned u = static_cast<unsigned>(i);
@@ -201,14 +208,14 @@ __device__ inline float lane_xor(float v) {
   }
 }
 
+// The lower lane of a pair takes v + other, the upper other - v: both are
+// other + (+-1 * v), the product exact, so the one rounding is that of the
+// sum or difference (and the lane move folds into the add).
 template <int LM>
 __device__ inline void fwht_lane_stage(float (&v)[8], int lane) {
-  const bool upper = (lane & LM) != 0;
+  const float sgn = (lane & LM) != 0 ? -1.f : 1.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float other = lane_xor<LM>(v[e]);
-    v[e] = upper ? (other - v[e]) : (v[e] + other);
-  }
+  for (int e = 0; e < 8; ++e) v[e] = lane_xor<LM>(v[e]) + sgn * v[e];
 }
 
 // In-place FWHT of one 512-block held by a wave: lane l holds elements
@@ -368,8 +375,10 @@ __global__ __launch_bounds__(NW * kWave) void k_quant_prologue(
   const int lane = threadIdx.x & (kWave - 1);
   const T* x = X + row * K;
   const int64_t nseg = (K + 511) / 512;
-  float v[NB][8];
-  // every segment's load goes out before the first one is used
+  float v[NB][8], g[NB][8];
+  // every segment's load goes out before the first one is used, the RMSNorm
+  // weight's too (it does not depend on the token)
+  const bool gw = rmsnorm && gweight != nullptr;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int64_t seg = wave + NW * j;
@@ -379,6 +388,14 @@ __global__ __launch_bounds__(NW * kWave) void k_quant_prologue(
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[j][e] = 0.f;
+    }
+  }
+  if (gw) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int64_t seg = wave + NW * j;
+      const int64_t base = seg * 512 + 8 * lane;
+      if (seg < nseg) load8<float, false>(gweight + base, K - base, g[j]);
     }
   }
   if (rmsnorm) {
@@ -394,8 +411,12 @@ __global__ __launch_bounds__(NW * kWave) void k_quant_prologue(
     double S = 0.0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) S += part[w];
+    // S / K; for K a power of two S scaled by 2^-log2(K), the same
+    // correctly rounded value without the division's instruction sequence
+    const double mean = (K & (K - 1)) == 0 ? ldexp(S, -__builtin_ctzll(static_cast<unsigned long long>(K)))
+                                           : S / static_cast<double>(K);
     float var;
-    if (var_from_fp64(S / static_cast<double>(K), &var)) {  // uniform over the block
+    if (var_from_fp64(mean, &var)) {  // uniform over the block
       for (int b = threadIdx.x; b < 256; b += NW * kWave) bins[b] = 0ull;
       __syncthreads();
 #pragma unroll
@@ -415,13 +436,9 @@ __global__ __launch_bounds__(NW * kWave) void k_quant_prologue(
     for (int j = 0; j < NB; ++j) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[j][e] = v[j][e] * r;
-      const int64_t seg = wave + NW * j;
-      const int64_t base = seg * 512 + 8 * lane;
-      if (gweight != nullptr && seg < nseg) {
-        float g[8];
-        load8<float, false>(gweight + base, K - base, g);
+      if (gw && wave + NW * j < nseg) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[j][e] = v[j][e] * g[e];
+        for (int e = 0; e < 8; ++e) v[j][e] = v[j][e] * g[j][e];
       }
     }
   }
