@@ -21,6 +21,8 @@
 // int32 partial tiles through LDS, and the epilogue applies
 // y = acc * gamma * sx in fp32.
 
+#include <type_traits>
+
 #include "tq_device.hpp"
 #include "tq_internal.hpp"
 
@@ -600,14 +602,36 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   asm volatile("" ::"v"(ra.g));
   if constexpr (DUAL) asm volatile("" ::"v"(ra.g2));
   asm volatile("" ::"v"(sx_in));
+  // With the token quantised here (SRC != 0), the first row's weights have
+  // mostly landed by the time the staging waves finish, and every wave would
+  // then decode at once.  The other waves, idle until the barrier, decode
+  // their first row before it.
+  constexpr bool PRE = SRC != 0 && BITS == 2 && (!DUAL || kSl <= 2);  // (registers)
+  v4i pre[PRE ? kSl : 1][4], pre2[PRE && DUAL ? kSl : 1][4];
+  if constexpr (PRE) {
+    if (!stager) {
+#pragma unroll
+      for (int sl = 0; sl < kSl; ++sl) {
+        const uint32_t words[4] = {ra.w[sl].x, ra.w[sl].y, ra.w[sl].z, ra.w[sl].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pre[sl][j] = decode_codes_strided(words[j]);
+        if constexpr (DUAL) {
+          const uint32_t words2[4] = {ra.w2[sl].x, ra.w2[sl].y, ra.w2[sl].z, ra.w2[sl].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) pre2[sl][j] = decode_codes_strided(words2[j]);
+        }
+      }
+    }
+  }
   __syncthreads();
   int tsum = 0;
 #pragma unroll
   for (int w = 0; w < kStageWaves; ++w) tsum += wave_sum_part[w];
   const float sxv = SRC == 0 ? sx_in : tok_sx;
 
-  // 6. contraction of the wave's row in group rg
-  auto finish = [&](int64_t rg, const Row& r) {
+  // 6. contraction of the wave's row in group rg (P: its codes are in `pre`)
+  auto finish_p = [&](int64_t rg, const Row& r, auto predecoded) {
+    constexpr bool P = decltype(predecoded)::value;
     const int64_t n = rg * kRowsD + wave;
     int acc = 0, acc2 = 0;
 #pragma unroll
@@ -619,7 +643,11 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
         if (16 * unit >= K) break;    // this chunk, and every later one, is past K
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const v4i cd = decode_codes_strided(words[j]);
+          v4i cd;
+          if constexpr (P && PRE)
+            cd = pre[sl][j];
+          else
+            cd = decode_codes_strided(words[j]);
           const v4i x = *reinterpret_cast<const v4i*>(xt + dot_slot(unit + j));
           acc = __builtin_amdgcn_sdot4(x.x, cd.x, acc, false);
           acc = __builtin_amdgcn_sdot4(x.y, cd.y, acc, false);
@@ -627,7 +655,11 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
           acc = __builtin_amdgcn_sdot4(x.w, cd.w, acc, false);
           if constexpr (DUAL) {
             const uint32_t words2[4] = {r.w2[sl].x, r.w2[sl].y, r.w2[sl].z, r.w2[sl].w};
-            const v4i cu = decode_codes_strided(words2[j]);
+            v4i cu;
+            if constexpr (P && PRE)
+              cu = pre2[sl][j];
+            else
+              cu = decode_codes_strided(words2[j]);
             acc2 = __builtin_amdgcn_sdot4(x.x, cu.x, acc2, false);
             acc2 = __builtin_amdgcn_sdot4(x.y, cu.y, acc2, false);
             acc2 = __builtin_amdgcn_sdot4(x.z, cu.z, acc2, false);
@@ -675,26 +707,41 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
         static_cast<uint16_t*>(Y)[n] = f32_to_bf16(y);
     }
   };
+  auto finish = [&](int64_t rg, const Row& r) { finish_p(rg, r, std::false_type{}); };
+  // the first row group: decoded before the barrier unless a staging wave
+  auto finish_first = [&](int64_t rg, const Row& r) {
+    if (PRE && !stager)
+      finish_p(rg, r, std::true_type{});
+    else
+      finish_p(rg, r, std::false_type{});
+  };
   // Row groups rg, rg + gridDim.x, ...: the next group's row is loaded
   // before the current one is contracted, alternating two named register
   // sets so that no copy of a load in flight is needed.  The last group
   // issues no load: a load past the end would still have to return before
   // the wave may end.
   const int64_t step = gridDim.x;
+  if (rg + step >= nrg) {
+    finish_first(rg, ra);
+    return;
+  }
+  load_row(rg + step, rb);
+  finish_first(rg, ra);
+  rg += step;
   for (;;) {
-    if (rg + step >= nrg) {
-      finish(rg, ra);
-      break;
-    }
-    load_row(rg + step, rb);
-    finish(rg, ra);
-    rg += step;
     if (rg + step >= nrg) {
       finish(rg, rb);
       break;
     }
     load_row(rg + step, ra);
     finish(rg, rb);
+    rg += step;
+    if (rg + step >= nrg) {
+      finish(rg, ra);
+      break;
+    }
+    load_row(rg + step, rb);
+    finish(rg, ra);
     rg += step;
   }
 }
