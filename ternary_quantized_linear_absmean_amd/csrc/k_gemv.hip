@@ -264,8 +264,7 @@ __global__ __launch_bounds__(kNTs) void k_gemv_lds(
       load16_act<SRC>(src, off, v);
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        d[b] = quant_byte(v[4 * b], s) | (quant_byte(v[4 * b + 1], s) << 8) |
-               (quant_byte(v[4 * b + 2], s) << 16) | (quant_byte(v[4 * b + 3], s) << 24);
+        d[b] = quant_word(v[4 * b], v[4 * b + 1], v[4 * b + 2], v[4 * b + 3], s);
       if (blockIdx.x == 0)
         *reinterpret_cast<uint4*>(q_out + off) = make_uint4(d[0], d[1], d[2], d[3]);
     }
@@ -556,8 +555,7 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
                 v[e] = __uint_as_float((val & 1) ? (w & 0xFFFF0000u) : (w << 16));
               }
             }
-            d[b] = quant_byte(v[0], sc) | (quant_byte(v[1], sc) << 8) |
-                   (quant_byte(v[2], sc) << 16) | (quant_byte(v[3], sc) << 24);
+            d[b] = quant_word(v[0], v[1], v[2], v[3], sc);
             if (blockIdx.x == 0) reinterpret_cast<uint32_t*>(q_out)[4 * u + b] = d[b];
           }
           bsum = byte_sum(d[b], bsum);
@@ -579,8 +577,7 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
         } else {
           float v[4];
           quad_to_f32<SRC>(rq[i], v);
-          d = quant_byte(v[0], sc) | (quant_byte(v[1], sc) << 8) |
-              (quant_byte(v[2], sc) << 16) | (quant_byte(v[3], sc) << 24);
+          d = quant_word(v[0], v[1], v[2], v[3], sc);
           if (blockIdx.x == 0) reinterpret_cast<uint32_t*>(q_out)[qi] = d;
         }
         // BITS 2: quad qi is word b = qi % 4 of unit qi / 4; its byte s goes
@@ -996,8 +993,7 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
       const float sc = tok_sc[m];
 #pragma unroll
       for (int b = 0; b < 4; ++b)
-        d[b] = quant_byte(v[4 * b], sc) | (quant_byte(v[4 * b + 1], sc) << 8) |
-               (quant_byte(v[4 * b + 2], sc) << 16) | (quant_byte(v[4 * b + 3], sc) << 24);
+        d[b] = quant_word(v[4 * b], v[4 * b + 1], v[4 * b + 2], v[4 * b + 3], sc);
       if (blockIdx.x == 0)
         *reinterpret_cast<uint4*>(q_out + 16 * static_cast<int64_t>(c)) =
             make_uint4(d[0], d[1], d[2], d[3]);

@@ -66,12 +66,13 @@ __device__ inline void load8(const T* p, int64_t valid, float (&v)[8]) {
   }
 }
 
+// b[i]: code i in the low byte (quant_bits)
 template <bool VEC>
 __device__ inline void store8_q(int8_t* p, int64_t valid, const uint32_t (&b)[8]) {
   if (VEC && valid >= 8) {
     uint2 o;
-    o.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-    o.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+    o.x = pack_low_bytes(b[0], b[1], b[2], b[3]);
+    o.y = pack_low_bytes(b[4], b[5], b[6], b[7]);
     *reinterpret_cast<uint2*>(p) = o;
   } else {
 #pragma unroll
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(kNT) void k_quant_plain(const T* __restrict__ X, in
     load8<T, VEC>(x + 8 * c, K - 8 * c, v);
     uint32_t b[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) b[i] = quant_byte(v[i], s);
+    for (int i = 0; i < 8; ++i) b[i] = quant_bits(v[i], s);
     store8_q<VEC>(qo + 8 * c, K - 8 * c, b);
   }
   if (threadIdx.x == 0) sx[row] = eta / 127.f;
@@ -158,7 +159,7 @@ __global__ __launch_bounds__(NT) void k_quant_small(const T* __restrict__ X, int
     if (c < nchunk) {
       uint32_t b[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) b[e] = quant_byte(v[i][e], s);
+      for (int e = 0; e < 8; ++e) b[e] = quant_bits(v[i][e], s);
       store8_q<VEC>(qo + 8 * c, K - 8 * c, b);
     }
   }
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(NW * kWave) void k_quant_prologue(
     const int64_t base = seg * 512 + 8 * lane;
     uint32_t b[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) b[e] = quant_byte(v[j][e], s);
+    for (int e = 0; e < 8; ++e) b[e] = quant_bits(v[j][e], s);
     store8_q<VEC>(qo + base, K - base, b);
   }
   if (threadIdx.x == 0) sx[row] = eta / 127.f;

@@ -131,10 +131,26 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // round half to even, clamp to [-127, 127], as a byte
-__device__ inline uint32_t quant_byte(float x, float s) {
-  float t = __builtin_rintf(x * s);
-  t = fminf(fmaxf(t, -127.f), 127.f);
-  return static_cast<uint32_t>(static_cast<int>(t)) & 0xFFu;
+// The code rint(x * s) clamped to [-127, 127], as int8 in the low byte of
+// the result (the upper bytes are not zero).  Clamping first and adding
+// 1.5 * 2^23 gives that code: for |t| < 2^22 the fp32 sum rounds to the
+// nearest integer, ties to even, as rint does, and holds it in two's
+// complement in its low bits (the clamp also sends NaN to -127 either way).
+__device__ inline uint32_t quant_bits(float x, float s) {
+  const float t = fminf(fmaxf(x * s, -127.f), 127.f);
+  return __float_as_uint(t + 12582912.f);
+}
+
+// the low bytes of b0..b3 as one word, b0 in byte 0
+__device__ inline uint32_t pack_low_bytes(uint32_t b0, uint32_t b1, uint32_t b2, uint32_t b3) {
+  const uint32_t lo = __builtin_amdgcn_perm(b1, b0, 0x0c0c0400u);
+  const uint32_t hi = __builtin_amdgcn_perm(b3, b2, 0x0c0c0400u);
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+
+// four codes, the first in byte 0
+__device__ inline uint32_t quant_word(float a, float b, float c, float d, float s) {
+  return pack_low_bytes(quant_bits(a, s), quant_bits(b, s), quant_bits(c, s), quant_bits(d, s));
 }
 
 // --------------------------------------------------------- 2-bit decoding
