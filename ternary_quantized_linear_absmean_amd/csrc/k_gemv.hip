@@ -603,7 +603,9 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   // mostly landed by the time the staging waves finish, and every wave would
   // then decode at once.  The other waves, idle until the barrier, decode
   // their first row before it.
-  constexpr bool PRE = SRC != 0 && BITS == 2 && (!DUAL || kSl <= 2);  // (registers)
+  // (Not for the SwiGLU pair: there the split first row group measured
+  // slower, with or without the early decode.)
+  constexpr bool PRE = SRC != 0 && BITS == 2 && !DUAL;
   v4i pre[PRE ? kSl : 1][4], pre2[PRE && DUAL ? kSl : 1][4];
   if constexpr (PRE) {
     if (!stager) {
@@ -718,28 +720,47 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   // issues no load: a load past the end would still have to return before
   // the wave may end.
   const int64_t step = gridDim.x;
-  if (rg + step >= nrg) {
-    finish_first(rg, ra);
-    return;
-  }
-  load_row(rg + step, rb);
-  finish_first(rg, ra);
-  rg += step;
-  for (;;) {
+  if constexpr (PRE) {
     if (rg + step >= nrg) {
-      finish(rg, rb);
-      break;
-    }
-    load_row(rg + step, ra);
-    finish(rg, rb);
-    rg += step;
-    if (rg + step >= nrg) {
-      finish(rg, ra);
-      break;
+      finish_first(rg, ra);
+      return;
     }
     load_row(rg + step, rb);
-    finish(rg, ra);
+    finish_first(rg, ra);
     rg += step;
+    for (;;) {
+      if (rg + step >= nrg) {
+        finish(rg, rb);
+        break;
+      }
+      load_row(rg + step, ra);
+      finish(rg, rb);
+      rg += step;
+      if (rg + step >= nrg) {
+        finish(rg, ra);
+        break;
+      }
+      load_row(rg + step, rb);
+      finish(rg, ra);
+      rg += step;
+    }
+  } else {
+    for (;;) {
+      if (rg + step >= nrg) {
+        finish(rg, ra);
+        break;
+      }
+      load_row(rg + step, rb);
+      finish(rg, ra);
+      rg += step;
+      if (rg + step >= nrg) {
+        finish(rg, rb);
+        break;
+      }
+      load_row(rg + step, ra);
+      finish(rg, rb);
+      rg += step;
+    }
   }
 }
 
