@@ -572,7 +572,7 @@ def test_gemm_small_grid_tiles(M, N, K):
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 128), (17, 4096, 128), (100, 4000, 384),
                                    (64, 2560, 6912), (128, 4096, 1152), (33, 4096, 11008),
-                                   (128, 4096, 4096), (5, 130, 640)])
+                                   (128, 4096, 4096), (5, 130, 640), (33, 1, 256), (100, 3, 128)])
 def test_gemm_register_tiles(M, N, K):
     # at most one 32 x 64 tile per CU and K % 128 == 0: four waves split the
     # 128-deep blocks of K (one block: three waves hold none; 3, 5, 9 or 86
