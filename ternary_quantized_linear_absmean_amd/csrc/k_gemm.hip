@@ -325,6 +325,12 @@ __global__ __launch_bounds__(WM* WN* kWave, 2) void k_gemm(
 template <int FN>
 constexpr int staged_lds_words() { return 32 * (32 * FN + 8); }
 
+// The output is written once and not read again by the kernel: its 16-byte
+// stores are non-temporal (measured 3% faster at 4096^3, 7% at 512 x 4096 x
+// 4096, where every tile's epilogue falls in the same few microseconds).
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v2u __attribute__((ext_vector_type(2)));
+
 template <int YT, int FM, int FN>
 __device__ inline void store_acc32_staged(const v16i (&acc)[FM][FN], int64_t mb, int64_t nb,
                                           int lane, const float* sxl, const float* gml,
@@ -369,7 +375,7 @@ __device__ inline void store_acc32_staged(const v16i (&acc)[FM][FN], int64_t mb,
       const int64_t o = m * N + n;
       if (YT == TQ_I32) {
         if (vec && n + 3 < N) {
-          *reinterpret_cast<v4i*>(static_cast<int*>(Y) + o) = a;
+          __builtin_nontemporal_store(a, reinterpret_cast<v4i*>(static_cast<int*>(Y) + o));
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -381,8 +387,8 @@ __device__ inline void store_acc32_staged(const v16i (&acc)[FM][FN], int64_t mb,
         for (int e = 0; e < 4; ++e) y[e] = static_cast<float>(a[e]) * (gv[e] * sv[t]);
         if (YT == TQ_F32) {
           if (vec && n + 3 < N) {
-            *reinterpret_cast<float4*>(static_cast<float*>(Y) + o) =
-                make_float4(y[0], y[1], y[2], y[3]);
+            const v4f t = {y[0], y[1], y[2], y[3]};
+            __builtin_nontemporal_store(t, reinterpret_cast<v4f*>(static_cast<float*>(Y) + o));
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -390,8 +396,8 @@ __device__ inline void store_acc32_staged(const v16i (&acc)[FM][FN], int64_t mb,
           }
         } else {
           if (vec && n + 3 < N) {
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + o) =
-                make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+            const v2u t = {pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
+            __builtin_nontemporal_store(t, reinterpret_cast<v2u*>(static_cast<uint16_t*>(Y) + o));
           } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e)
