@@ -217,9 +217,13 @@ __global__ __launch_bounds__(kNTs) void k_gemv_lds(
     for (int u = 0; u < kUnrollS; ++u) {
       const int64_t sb = sb0 + kWavesS * u;
       const int64_t off = sb * 64 + g * 16;
-      wv[u] = (n_ok && sb < nsb && off + 16 <= rowbytes)
-                  ? *reinterpret_cast<const uint4*>(wrow + off)
-                  : make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+      typedef unsigned v4u __attribute__((ext_vector_type(4)));
+      if (n_ok && sb < nsb && off + 16 <= rowbytes) {
+        const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(wrow + off));
+        wv[u] = make_uint4(v.x, v.y, v.z, v.w);
+      } else {
+        wv[u] = make_uint4(0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u);
+      }
     }
   };
   uint4 wv[kUnrollS];
@@ -350,6 +354,10 @@ constexpr int kStageNT = kStageWaves * kWave;
 static_assert(kRowsD >= kStageWaves, "row-per-wave kernel needs at least four waves");
 constexpr int kMaxSlices = 4;        // K <= 16384
 constexpr int kBufRaw = 0x00020000;  // raw buffer resource, 32-bit data format
+// Cache policy of the packed-weight loads: non-temporal.  A launch reads each
+// weight byte once; marked so, the 4 MiB decode stream arrived sooner (same-box
+// A/B, 4096 x 4096: 3.34 -> 3.17 us fused, 3.00 -> 2.88 us from int8 codes).
+constexpr int kStreamAux = 2;
 
 // Four consecutive token values in their storage type.
 template <int SRC>
@@ -466,11 +474,11 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
     for (int sl = 0; sl < kSl; ++sl) {
       if (BITS == 2) {
         w[sl] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + kWave * sl) * 16, 0, 0));
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, (lane + kWave * sl) * 16, 0, kStreamAux));
       } else {
         typedef uint32_t u2 __attribute__((ext_vector_type(2)));
         const u2 v = __builtin_bit_cast(
-            u2, __builtin_amdgcn_raw_buffer_load_b64(wr, (lane + kWave * sl) * 8, 0, 0));
+            u2, __builtin_amdgcn_raw_buffer_load_b64(wr, (lane + kWave * sl) * 8, 0, kStreamAux));
         w[sl] = make_uint4(v.x, v.y, 0u, 0u);
       }
     }
@@ -956,14 +964,17 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
     const int kbl = kb < nkb ? kb : 0;
     if (BITS == 2) {
       wv[i] = __builtin_bit_cast(
-          uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, fr * rowbytes + 64 * kbl + 16 * fg, 0, 0));
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, fr * rowbytes + 64 * kbl + 16 * fg, 0,
+                                                       kStreamAux));
       if constexpr (DUAL)
         wv2[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               wr2, fr * rowbytes + 64 * kbl + 16 * fg, 0, 0));
+                                               wr2, fr * rowbytes + 64 * kbl + 16 * fg, 0,
+                                               kStreamAux));
     } else {
       typedef uint32_t u2 __attribute__((ext_vector_type(2)));
       const u2 v = __builtin_bit_cast(
-          u2, __builtin_amdgcn_raw_buffer_load_b64(wr, fr * rowbytes + 32 * kbl + 8 * fg, 0, 0));
+          u2, __builtin_amdgcn_raw_buffer_load_b64(wr, fr * rowbytes + 32 * kbl + 8 * fg, 0,
+                                                   kStreamAux));
       wv[i] = make_uint4(v.x, v.y, 0u, 0u);
     }
   }
