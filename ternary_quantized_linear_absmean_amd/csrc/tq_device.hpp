@@ -193,6 +193,19 @@ __device__ inline v4i decode_codes_strided(uint32_t w) {
   return out;
 }
 
+// The 16 codes of a packed word in strided order as above, but without
+// shifting codes 4b + 1 and 4b + 2 down: out.y holds 4 * code, out.z
+// 16 * code (both still positive bytes), so a product with them is scaled by
+// 4 or 16 and is accumulated apart.  Five integer operations.
+__device__ inline v4i decode_codes_scaled(uint32_t w) {
+  v4i out;
+  out.x = static_cast<int>(w & 0x03030303u);
+  out.y = static_cast<int>(w & 0x0C0C0C0Cu);
+  out.z = static_cast<int>(w & 0x30303030u);
+  out.w = static_cast<int>((w >> 6) & 0x03030303u);
+  return out;
+}
+
 // Codes 0..2 in each byte -> signed values -1..+1 (0x7F + c never carries
 // out of its byte; flipping the top bit then gives c - 1 in two's complement).
 __device__ inline uint32_t codes_to_signed(uint32_t c) {
