@@ -633,7 +633,8 @@ def _probes():
     lib = ctypes.CDLL(os.path.join(ROOT, "ternary_quantized_linear_absmean_amd",
                                    "libtq_probes.so"))
     lib.tqp_empty.argtypes = [ctypes.c_void_p]
-    lib.tqp_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.tqp_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                             ctypes.c_void_p]
     lib.tqp_mfma_i8.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     lib.tqp_mfma_i8_data.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_void_p]
@@ -647,7 +648,8 @@ def extra_context(torch, dev):
     """Reference floors of the device, not this library's work, under the
     same graph replay and buffer rotation as the layer: the cost of a launch
     (an empty kernel, and a one-element torch op), a pure streaming read of
-    4 MiB (one 16-byte load per lane) and of larger buffers, a torch copy of
+    4 MiB (one 16-byte load per lane; default and non-temporal cache policy)
+    and of larger buffers, a torch copy of
     4 MiB, a chain of independent int8 matrix-core products (the sustained
     int8 rate), and the vendor int8 GEMM (hipBLASLt through torch._int_mm,
     int8 weights) on the prefill shape and at 8192^3."""
@@ -666,15 +668,17 @@ def extra_context(torch, dev):
     t = per_launch(lambda: one.add_(1.0), POOL)
     out["torch_one_element_add"] = {"us": round(t * 1e6, 3)}
     sink = torch.zeros(1024, dtype=torch.int32, device=dev)
-    reads = {}
+    reads, reads_nt = {}, {}
     for mib, n in ((4, POOL), (16, 32), (64, 8), (256, 2)):
         bufs = [torch.ones(mib << 18, dtype=torch.int32, device=dev) for _ in range(n)]
-        t = per_launch(lambda: [lib.tqp_read(b.data_ptr(), mib << 20, sink.data_ptr(), st())
-                                for b in bufs], 1, reps=max(4, 64 // n))
-        reads[f"{mib}MiB"] = {"us": round(t / n * 1e6, 3),
-                              "GBs": round((mib << 20) * n / t / 1e9, 1), "rotation": n}
+        for nt, into in ((0, reads), (1, reads_nt)):
+            t = per_launch(lambda: [lib.tqp_read(b.data_ptr(), mib << 20, sink.data_ptr(), nt,
+                                                 st()) for b in bufs], 1, reps=max(4, 64 // n))
+            into[f"{mib}MiB"] = {"us": round(t / n * 1e6, 3),
+                                 "GBs": round((mib << 20) * n / t / 1e9, 1), "rotation": n}
         del bufs
     out["pure_read_rotating"] = reads
+    out["pure_read_rotating_nontemporal"] = reads_nt
     pool = [torch.ones(1 << 20, dtype=torch.int32, device=dev) for _ in range(POOL)]
     dst = torch.empty(1 << 20, dtype=torch.int32, device=dev)
     g = capture(torch, lambda: [dst.copy_(p) for p in pool])

@@ -5,7 +5,9 @@
 // measure what the device itself allows for the shapes the layer runs at:
 //   - tqp_empty: one empty workgroup, the cost of a launch;
 //   - tqp_read: a pure streaming read, one 16-byte load per lane, the floor
-//     of a kernel that must move a given number of bytes once;
+//     of a kernel that must move a given number of bytes once (nt = 1: the
+//     loads marked non-temporal, as the layer's weight loads are; 0: the
+//     default cache policy);
 //   - tqp_mfma_i8: independent chains of v_mfma_i32_32x32x32_i8 with
 //     operands in registers, the sustained int8 matrix-core rate (one operand
 //     pair for all chains, or, tqp_mfma_i8_data, random operands per chain).
@@ -23,12 +25,15 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 
 __global__ void k_empty() {}
 
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
 // n16 16-byte chunks, one per lane; grid = ceil(n16 / 256) workgroups of 256
-__global__ __launch_bounds__(256) void k_read(const uint4* __restrict__ p, int64_t n16,
+template <bool NT>
+__global__ __launch_bounds__(256) void k_read(const v4u* __restrict__ p, int64_t n16,
                                               unsigned* __restrict__ sink) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= n16) return;
-  const uint4 v = p[i];
+  const v4u v = NT ? __builtin_nontemporal_load(p + i) : p[i];
   const unsigned x = v.x ^ v.y ^ v.z ^ v.w;
   if (x == 0x9E3779B9u) sink[blockIdx.x & 1023] = x;
 }
@@ -112,15 +117,20 @@ int tqp_empty(hipStream_t s) {
   return static_cast<int>(hipGetLastError());
 }
 
-// bytes must be a multiple of 16 and p 16-byte aligned
-int tqp_read(const void* p, int64_t bytes, unsigned* sink, hipStream_t s) {
+// bytes must be a multiple of 16 and p 16-byte aligned; nt selects the
+// non-temporal cache policy for the loads
+int tqp_read(const void* p, int64_t bytes, unsigned* sink, int nt, hipStream_t s) {
   if (p == nullptr || sink == nullptr || bytes <= 0 || (bytes & 15) != 0 ||
       (reinterpret_cast<uintptr_t>(p) & 15u) != 0u)
     return -1;
   const int64_t n16 = bytes / 16;
   const int64_t grid = (n16 + 255) / 256;
-  hipLaunchKernelGGL(k_read, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
-                     static_cast<const uint4*>(p), n16, sink);
+  if (nt)
+    hipLaunchKernelGGL(k_read<true>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                       static_cast<const v4u*>(p), n16, sink);
+  else
+    hipLaunchKernelGGL(k_read<false>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                       static_cast<const v4u*>(p), n16, sink);
   return static_cast<int>(hipGetLastError());
 }
 
