@@ -361,35 +361,43 @@ def extra_prefill(torch, ti, tq, dev, want):
 
 def extra_square(torch, tq, dev):
     """GEMM 4096 x 4096 x 4096 -> bf16: 256 tiles of 256 x 256, one full
-    round of the wide-tile kernel (one workgroup per CU), next to the vendor
-    int8 GEMM on the same shape."""
-    M = N = K = 4096
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(4096)
-    W = torch.randn((N, K), generator=gen, device=dev) * 0.02
-    packed, scale = tq.tq_pack_ternary(W, "tensor")
-    X = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
-    q, sx = tq.tq_quant_act_int8(X)
-    Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    reps = 8
-    g = capture(torch, lambda: [tq.tq_ternary_gemm(q, sx, packed, scale, N, K, "tensor", "bf16",
-                                                   Y=Y) for _ in range(reps)])
-    warm(torch, g)
-    t = timed_graph(torch, g, 5) / reps
-    tops = 2.0 * M * N * K / t / 1e12
-    out = {"gemm_4096x4096x4096": {"shape": [M, N, K], "out": "bf16", "kernel": "k_gemm_wide",
-                                   "us": round(t * 1e6, 2), "TOPS": round(tops, 1),
-                                   "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)}}
-    try:
-        B = (torch.randint(-1, 2, (N, K), generator=gen, device=dev)).to(torch.int8)
-        g = capture(torch, lambda: [torch._int_mm(q, B.t()) for _ in range(reps)])
+    round of the wide-tile kernel (one workgroup per CU), and 8192^3: four
+    full rounds, where the start and the epilogue of a round weigh least;
+    each next to the vendor int8 GEMM on the same shape (ternary int8 B)."""
+    out = {}
+    for M in (4096, 8192):
+        N = K = M
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(M)
+        W = torch.randn((N, K), generator=gen, device=dev) * 0.02
+        packed, scale = tq.tq_pack_ternary(W, "tensor")
+        del W
+        X = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+        q, sx = tq.tq_quant_act_int8(X)
+        del X
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        reps = 8
+        g = capture(torch, lambda: [tq.tq_ternary_gemm(q, sx, packed, scale, N, K, "tensor",
+                                                       "bf16", Y=Y) for _ in range(reps)])
         warm(torch, g)
         t = timed_graph(torch, g, 5) / reps
-        out["vendor_int8_gemm_4096x4096x4096"] = {
-            "api": "torch._int_mm (int8 x int8 -> int32)", "us": round(t * 1e6, 2),
-            "TOPS": round(2.0 * M * N * K / t / 1e12, 1)}
-    except Exception as e:  # the reference is optional context
-        out["vendor_int8_gemm_4096x4096x4096"] = {"error": str(e)[:200]}
+        tops = 2.0 * M * N * K / t / 1e12
+        name = f"{M}x{N}x{K}"
+        out[f"gemm_{name}"] = {"shape": [M, N, K], "out": "bf16", "kernel": "k_gemm_wide",
+                               "us": round(t * 1e6, 2), "TOPS": round(tops, 1),
+                               "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 2)}
+        del g, Y
+        try:
+            B = (torch.randint(-1, 2, (N, K), generator=gen, device=dev)).to(torch.int8)
+            g = capture(torch, lambda: [torch._int_mm(q, B.t()) for _ in range(reps)])
+            warm(torch, g)
+            t = timed_graph(torch, g, 5) / reps
+            out[f"vendor_int8_gemm_{name}"] = {
+                "api": "torch._int_mm (int8 x int8 -> int32)", "us": round(t * 1e6, 2),
+                "TOPS": round(2.0 * M * N * K / t / 1e12, 1)}
+            del g, B
+        except Exception as e:  # the reference is optional context
+            out[f"vendor_int8_gemm_{name}"] = {"error": str(e)[:200]}
     return out
 
 

@@ -554,6 +554,23 @@ def test_gemm_wide_tiles(M, N, K):
                        q, packed, sc, sx)
 
 
+def test_gemm_wide_tiles_8192_cubed_sampled():
+    # four full rounds of 256 x 256 tiles at K = 8192 (the largest square
+    # shape the benchmark times): every token row, sampled weight rows that
+    # include the first and last of a tile, each output checked in full
+    M = N = K = 8192
+    q = ti.random_int8(M + K + 1, M, K)
+    w = ti.random_ternary(N + K + 1, N, K)
+    packed = oracle.pack_codes(w)
+    del w
+    scale = np.array([0.0173], dtype=np.float32)
+    sx = (np.abs(ti.activations(M + 37, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    cols = np.unique(np.concatenate([_sample_cols(N, 8192, n=48), [255, 256, 4095, 4096]]))
+    say(f"gemm wide tiles M=N=K={M}, {cols.size} sampled weight rows")
+    _check_outputs(tq.tq_ternary_gemm, dev(q), dev(sx), dev(packed), dev(scale), N, K,
+                   "tensor", q, packed, scale, sx, cols=cols)
+
+
 @pytest.mark.parametrize("M,N,K", [(256, 4096, 4096), (200, 3000, 512), (33, 8000, 768),
                                    (130, 260, 256)])
 def test_gemm_small_grid_tiles(M, N, K):
