@@ -504,19 +504,24 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   if (SRC != 0) {
     if (stager) {
       float mx = 0.f;
-      if constexpr (BITS == 2) {
+      if constexpr (BITS == 2 && SRC == 2) {
+        // bf16: for finite values the order of |x| is that of the unsigned
+        // integer of its 15 low bits, so two values at a time by a packed max
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        u16x2 m = {0, 0};
 #pragma unroll
         for (int i = 0; i < kUnitsL * kLdU; ++i)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w = static_cast<uint32_t>(ru[i][e]);
-            if constexpr (SRC == 1) {
-              mx = fmaxf(mx, fabsf(__uint_as_float(w)));
-            } else {
-              mx = fmaxf(mx, fmaxf(fabsf(__uint_as_float(w << 16)),
-                                   fabsf(__uint_as_float(w & 0xFFFF0000u))));
-            }
-          }
+          for (int e = 0; e < 4; ++e)
+            m = __builtin_elementwise_max(
+                m, __builtin_bit_cast(u16x2, static_cast<uint32_t>(ru[i][e]) & 0x7FFF7FFFu));
+        mx = __uint_as_float(static_cast<uint32_t>(m.x > m.y ? m.x : m.y) << 16);
+      } else if constexpr (BITS == 2) {
+#pragma unroll
+        for (int i = 0; i < kUnitsL * kLdU; ++i)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            mx = fmaxf(mx, fabsf(__uint_as_float(static_cast<uint32_t>(ru[i][e]))));
       } else {
 #pragma unroll
         for (int i = 0; i < kRounds; ++i) {
@@ -529,22 +534,27 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
       if (lane == kWave - 1) wave_max_part[wave] = mx;
     }
     __syncthreads();
-    if (stager) {
+    // the staging waves need 127 / eta; eta / 127 (for the epilogue) is
+    // formed by the first wave that does not stage, off their path
+    constexpr int kSxTid = (kRowsD > kStageWaves ? kStageWaves : 0) * kWave;
+    if (stager || tid == kSxTid) {
       float amax = 0.f;
 #pragma unroll
       for (int w = 0; w < kStageWaves; ++w) amax = fmaxf(amax, wave_max_part[w]);
       float eta = fmaxf(amax, eps);
       if (clamp) eta = fminf(fmaxf(eta, lo), hi);
-      sc = 127.f / eta;
-      if (tid == 0) {
+      if (stager) sc = 127.f / eta;
+      if (tid == kSxTid) {
         const float sxv = eta / 127.f;
         tok_sx = sxv;
         if (blockIdx.x == 0) sx_io[0] = sxv;
       }
     }
   }
-  // 5. int8 token -> transposed, swizzled LDS; byte sums
-  if (stager && BITS == 2) {
+  // 5. int8 token -> transposed, swizzled LDS; byte sums.  Without an eta
+  // clamp every |x| <= eta and the codes need no clamp (quant_word_unclamped).
+  auto stage_units = [&](auto clamped) {
+    constexpr bool CL = decltype(clamped)::value;
     int bsum = 0;
     const int nunit = K >> 4;
 #pragma unroll
@@ -568,7 +578,8 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
                 v[e] = __uint_as_float((val & 1) ? (w & 0xFFFF0000u) : (w << 16));
               }
             }
-            d[b] = quant_word(v[0], v[1], v[2], v[3], sc);
+            d[b] = CL ? quant_word(v[0], v[1], v[2], v[3], sc)
+                      : quant_word_unclamped(v[0], v[1], v[2], v[3], sc);
             if (blockIdx.x == 0) reinterpret_cast<uint32_t*>(q_out)[4 * u + b] = d[b];
           }
           bsum = byte_sum(d[b], bsum);
@@ -578,6 +589,12 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
     }
     bsum = wave_isum_last(bsum);
     if (lane == kWave - 1) wave_sum_part[wave] = bsum;
+  };
+  if (stager && BITS == 2) {
+    if (SRC == 0 || clamp)
+      stage_units(std::true_type{});
+    else
+      stage_units(std::false_type{});
   } else if (stager) {
     int bsum = 0;
 #pragma unroll

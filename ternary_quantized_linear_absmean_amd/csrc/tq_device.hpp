@@ -153,6 +153,19 @@ __device__ inline uint32_t quant_word(float a, float b, float c, float d, float 
   return pack_low_bytes(quant_bits(a, s), quant_bits(b, s), quant_bits(c, s), quant_bits(d, s));
 }
 
+// quant_bits without the clamp, for s = 127 / eta with eta >= |x|: then
+// |x * s| <= 127 * (1 + 2^-24) before its rounding, so the product rounds to
+// at most 127 + 2^-17 and the code to at most 127 in magnitude.
+__device__ inline uint32_t quant_bits_unclamped(float x, float s) {
+  const float t = x * s;
+  return __float_as_uint(t + 12582912.f);
+}
+
+__device__ inline uint32_t quant_word_unclamped(float a, float b, float c, float d, float s) {
+  return pack_low_bytes(quant_bits_unclamped(a, s), quant_bits_unclamped(b, s),
+                        quant_bits_unclamped(c, s), quant_bits_unclamped(d, s));
+}
+
 // --------------------------------------------------------- 2-bit decoding
 
 // 4x4 byte transpose: out[s] holds byte s of d0, d1, d2, d3 (in that order).

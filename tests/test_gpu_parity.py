@@ -765,8 +765,11 @@ FUSED_CASES = [
 ]
 
 
+@pytest.mark.parametrize("bounds", [(0.05, 40.0), None])
 @pytest.mark.parametrize("M,N,K,dtype,gran", FUSED_CASES)
-def test_quant_ternary_gemv_matches_two_calls(M, N, K, dtype, gran):
+def test_quant_ternary_gemv_matches_two_calls(M, N, K, dtype, gran, bounds):
+    # bounds None: no gain clamp, every |x| <= eta (the single-token kernel
+    # then quantises without clamping the codes)
     X = ti.activations(3000 + M + N + K, M, K, dtype=dtype)
     if M >= 3:
         X[1] = 0.0
@@ -775,11 +778,11 @@ def test_quant_ternary_gemv_matches_two_calls(M, N, K, dtype, gran):
     scale = (np.abs(ti.activations(N + 5, 1, N, dtype="f32")[0]) * 0.02 + 1e-3).astype(np.float32)
     sc = scale if gran == "row" else scale[:1]
     Xd, pd, sd = x_to_device(X, dtype), dev(packed), dev(sc)
-    say(f"quant+gemv M={M} N={N} K={K} {dtype} {gran}")
-    qr, sr = oracle.quant_act_int8(X, bounds=(0.05, 40.0))
+    say(f"quant+gemv M={M} N={N} K={K} {dtype} {gran} bounds={bounds}")
+    qr, sr = oracle.quant_act_int8(X, bounds=bounds)
     for ydt in ("f32", "bf16", "i32"):
-        Y, q, sx = tq.tq_quant_ternary_gemv(Xd, pd, sd, N, K, gran, ydt, clamp=(0.05, 40.0))
-        q2, sx2 = tq.tq_quant_act_int8(Xd, clamp=(0.05, 40.0))
+        Y, q, sx = tq.tq_quant_ternary_gemv(Xd, pd, sd, N, K, gran, ydt, clamp=bounds)
+        q2, sx2 = tq.tq_quant_act_int8(Xd, clamp=bounds)
         Y2 = tq.tq_ternary_gemv(q2, sx2, pd, sd, N, K, gran, ydt)
         np.testing.assert_array_equal(host(q), host(q2))
         np.testing.assert_array_equal(f32_bits(host(sx)), f32_bits(host(sx2)))
