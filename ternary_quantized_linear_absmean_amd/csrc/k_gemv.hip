@@ -414,7 +414,7 @@ __device__ inline int dot_slot(int u) { return (u ^ (((u >> 3) ^ (u >> 4)) & 3))
 // DUAL (SwiGLU, BITS 2): every wave also contracts the row of a second
 // matrix (packed2, scale2) against the same staged token, and the epilogue
 // writes h = clamp(silu(g) * u, -clampv, clampv) from the two outputs g and u.
-template <int SRC, int S, int BITS, bool DUAL>
+template <int SRC, int S, int BITS, bool DUAL, bool EARLY = true>
 __global__ __launch_bounds__(kNTd) void k_gemv_dot(
     const void* __restrict__ src, float eps, int clamp, float lo, float hi,
     int8_t* __restrict__ q_out, float* __restrict__ sx_io,
@@ -632,10 +632,12 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   // With the token quantised here (SRC != 0), the first row's weights have
   // mostly landed by the time the staging waves finish, and every wave would
   // then decode at once.  The other waves, idle until the barrier, decode
-  // their first row before it.
+  // their first row before it (EARLY).  The barrier then also waits for the
+  // slowest of the workgroup's weights; where every lane's slices are full
+  // (K = 4096 or 8192) the launcher measured the plain order faster.
   // (Not for the SwiGLU pair: there the split first row group measured
   // slower, with or without the early decode.)
-  constexpr bool PRE = SRC != 0 && BITS == 2 && !DUAL;
+  constexpr bool PRE = EARLY && SRC != 0 && BITS == 2 && !DUAL;
   v4i pre[PRE ? kSl : 1][4], pre2[PRE && DUAL ? kSl : 1][4];
   if constexpr (PRE) {
     if (!stager) {
@@ -805,7 +807,7 @@ struct DualArgs {
   float clampv = 0.f;
 };
 
-template <int SRC, int S, int BITS, bool DUAL>
+template <int SRC, int S, int BITS, bool DUAL, bool EARLY = true>
 hipError_t gemv_dot_launch_s(const void* src, const ActParams* p, int8_t* q_out, float* sx,
                              const GemmArgs& a, const DualArgs& d, hipStream_t s) {
   // one workgroup per row group up to two per compute unit (the resident
@@ -815,7 +817,7 @@ hipError_t gemv_dot_launch_s(const void* src, const ActParams* p, int8_t* q_out,
   const int64_t grid = groups < cap ? groups : cap;
   const float eps = p ? p->eps : 0.f, lo = p ? p->eta_min : 0.f, hi = p ? p->eta_max : 0.f;
   const int clamp = p ? p->clamp : 0;
-  hipLaunchKernelGGL((k_gemv_dot<SRC, S, BITS, DUAL>), dim3(grid), dim3(kNTd),
+  hipLaunchKernelGGL((k_gemv_dot<SRC, S, BITS, DUAL, EARLY>), dim3(grid), dim3(kNTd),
                      static_cast<size_t>(a.K), s, src, eps, clamp, lo, hi, q_out, sx, a.packed,
                      a.scale, a.per_row, a.N, static_cast<int>(a.K), a.Y, a.ydt, d.packed2,
                      d.scale2, d.clampv);
@@ -825,8 +827,22 @@ hipError_t gemv_dot_launch_s(const void* src, const ActParams* p, int8_t* q_out,
 template <int SRC, int BITS = 2, bool DUAL = false>
 hipError_t gemv_dot_launch(const void* src, const ActParams* p, int8_t* q_out, float* sx,
                            const GemmArgs& a, hipStream_t s, const DualArgs& d = DualArgs()) {
-  if (a.K <= 4096) return gemv_dot_launch_s<SRC, 1, BITS, DUAL>(src, p, q_out, sx, a, d, s);
-  if (a.K <= 8192) return gemv_dot_launch_s<SRC, 2, BITS, DUAL>(src, p, q_out, sx, a, d, s);
+  // The early decode of the first row (quantising kernels only) measured
+  // slower where the slices are exactly full at one or two slices (same-box
+  // A/B: 4096 x 4096 3.16 -> 3.05 us, 11008 x 4096 5.11 -> 4.71, 4096 x 8192
+  // 4.17 -> 4.11) and faster elsewhere (K = 1024, 2560, 3072, 6912, 16384:
+  // 1-4%).
+  constexpr bool kEarlyMatters = SRC != 0 && BITS == 2 && !DUAL;
+  if (a.K <= 4096) {
+    if constexpr (kEarlyMatters)
+      if (a.K == 4096) return gemv_dot_launch_s<SRC, 1, BITS, DUAL, false>(src, p, q_out, sx, a, d, s);
+    return gemv_dot_launch_s<SRC, 1, BITS, DUAL>(src, p, q_out, sx, a, d, s);
+  }
+  if (a.K <= 8192) {
+    if constexpr (kEarlyMatters)
+      if (a.K == 8192) return gemv_dot_launch_s<SRC, 2, BITS, DUAL, false>(src, p, q_out, sx, a, d, s);
+    return gemv_dot_launch_s<SRC, 2, BITS, DUAL>(src, p, q_out, sx, a, d, s);
+  }
   return gemv_dot_launch_s<SRC, kMaxSlices, BITS, DUAL>(src, p, q_out, sx, a, d, s);
 }
 

@@ -747,6 +747,8 @@ def test_end_to_end_bitlinear_binary_and_ternary():
 
 FUSED_CASES = [
     (1, 4096, 4096, "bf16", "tensor"),   # the decode workload shape: one launch
+    (1, 11008, 4096, "f32", "row"),      # K = 4096 (no early decode), row groups looped
+    (1, 200, 8192, "bf16", "row"),       # K = 8192: two full slices, no early decode
     (4, 300, 2560, "f32", "row"),
     (3, 77, 64, "bf16", "tensor"),
     (1, 5, 6912, "bf16", "row"),
