@@ -1221,8 +1221,9 @@ hipError_t gemm_fast_dispatch(const GemmArgs& a, hipStream_t s) {
   // tiles, the last one included, fills at least half of the chip
   const int64_t cus = device_cus() > 0 ? device_cus() : 256;
   // at most one 32 x 64 tile per CU: K split over four waves (measured
-  // 10.1 against 12.0 us at 128 x 4096 x 4096 and 12.8 against 16.3 us at
-  // 64 x 2560 x 6912; with more tiles the staged tiles below are faster)
+  // 9.1 against 12.0 us at 128 x 4096 x 4096 and 11.0 against 16.3 us at
+  // 64 x 2560 x 6912; with up to two tiles per CU the staged tiles below
+  // stay 2-7% faster, e.g. 11.9 against 12.2-12.3 us at 160-256 x 4096 x 4096)
   if (a.K % kRBK == 0 && tiles(32, 64) <= cus) return gemm_reg_launch<1, 2, 4, 4>(a, s);
   const int64_t tw = tiles(kWBM, kWBN), last = tw % cus;
   if (tw >= cus && (last == 0 || 2 * last >= cus) && a.K % (2 * kWBK) == 0)
