@@ -834,6 +834,15 @@ def _cpu_act(pool, X, prologue):
     return np.concatenate([o[0] for o in outs]), np.concatenate([o[1] for o in outs])
 
 
+class _SerialPool:
+    """The pool interface of _cpu_map on the calling thread (one worker)."""
+    _max_workers = 1
+
+    @staticmethod
+    def map(fn, *iterables):
+        return list(map(fn, *iterables))
+
+
 def _cpu_layer(pool, X, W, gran, mode, prologue, packed=None):
     """One pass of the layer on the oracle: pack, quantise, contract,
     rescale.  Returns the three stage times (s) and the packed weight."""
@@ -867,6 +876,7 @@ def cpu_baseline(budget_s, runs):
     threads = host_threads()
     share = {"tiny": 0.02, "decode": 0.18, "ffn": 0.2, "prefill": 0.35, "bitlinear": 0.25}
     out = {}
+    kept = {}  # workload -> (jobs, packed weights) for the single-thread leg
     t_all = time.perf_counter()
     with threadpool_limits(threads), \
             cf.ProcessPoolExecutor(threads, mp_context=mp.get_context("fork")) as pool:
@@ -889,6 +899,8 @@ def cpu_baseline(budget_s, runs):
                 stages.append(run)
                 if len(stages) >= runs or time.perf_counter() - t0 > share[name] * budget_s:
                     break
+            if name in ("tiny", "decode"):
+                kept[name] = (jobs, packed)
             med = np.median(np.array(stages), axis=0)
             rec = {"runs": len(stages), "pack_s": round(float(med[0]), 4),
                    "quant_s": round(float(med[1]), 4),
@@ -902,12 +914,38 @@ def cpu_baseline(budget_s, runs):
                 m = cfg["batches"][0]
                 rec["contract_GOPS"] = round(2.0 * m * n * k / float(med[2]) / 1e9, 2)
             out[name] = rec
+    # the first two workloads once more on one thread (BLAS included): the
+    # tiny layer whole, the decode step (quantise + contraction + epilogue)
+    # with the weight packed above
+    with threadpool_limits(1):
+        for name, (jobs, packed) in kept.items():
+            cfg = ti.WORKLOADS[name]
+            runs1 = []
+            for _ in range(max(1, runs)):
+                run = np.zeros(3)
+                for j, b, W, X in jobs:
+                    t, _ = _cpu_layer(_SerialPool, X, W, cfg["gran"], cfg["modes"][0],
+                                      cfg.get("prologue", False),
+                                      None if name == "tiny" else packed[j])
+                    run += np.array(t)
+                runs1.append(run)
+            med = np.median(np.array(runs1), axis=0)
+            rec = {"runs": len(runs1), "quant_s": round(float(med[1]), 4),
+                   "contract_epilogue_s": round(float(med[2]), 4)}
+            if name == "tiny":
+                rec["pack_s"] = round(float(med[0]), 4)
+            else:
+                n, k = cfg["mats"][0]
+                rec["decode_step_GBs"] = round(fused_bytes(1, n, k, 2, False)
+                                               / float(med[1] + med[2]) / 1e9, 4)
+            out[name]["single_thread"] = rec
     d = out["decode"]
     return {"value": d["decode_step_GBs"], "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": "each workload's whole layer once per run (pack, quantise, exact "
                       "contraction, fp64 epilogue), median of the runs; value = the decode "
                       "workload's step (quantise + contraction + epilogue of one bf16 token "
-                      "through 4096x4096) in GB/s",
+                      "through 4096x4096) in GB/s; the tiny and decode workloads also on one "
+                      "thread (single_thread)",
             "nproc": os.cpu_count(), "threads": threads, "cpu_model": cpu_model(),
             "wall_s": round(time.perf_counter() - t_all, 1), "workloads": out}
 
