@@ -83,11 +83,18 @@ def fused_bytes(M, N, K, xbytes, per_row):
 
 
 def source_digest():
+    """sha256 (16 hex digits) of the decode kernel's sources with comments
+    and whitespace removed: an edit of the code changes it, an edit of a
+    comment does not."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)   # block comments
+        text = re.sub(r"//[^\n]*", " ", text)                  # line comments
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

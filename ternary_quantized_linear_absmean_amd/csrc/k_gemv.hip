@@ -341,10 +341,11 @@ __global__ __launch_bounds__(kNTs) void k_gemv_lds(
 // their own and are shifted back once per row (exact: int32 sums of
 // multiples of 4 or 16; same-box A/B against the seven-operation decode,
 // 4096 x 4096: int8 codes in 2.89 -> 2.82 us, fused 3.16-3.21 -> 3.14-3.15 us,
-// 4096 x 16384 fused 6.61 -> 6.38 us, the SwiGLU pair 2-7% faster).  With ternary codes a staging lane takes whole 16-value
-// units: 16-byte loads, the transposed unit built in registers and stored
-// with one 16-byte LDS write.  Per-wave maxima and byte sums go through small LDS arrays,
-// so the token costs two barriers.  Products use v_dot4 and
+// 4096 x 16384 fused 6.61 -> 6.38 us, the SwiGLU pair 2-7% faster).  With
+// ternary codes a staging lane takes whole 16-value units: 16-byte loads,
+// the transposed unit built in registers and stored with one 16-byte LDS
+// write.  Per-wave maxima and byte sums go through small LDS arrays, so the
+// token costs two barriers.  Products use v_dot4 and
 // sum_k q*(c-1) = sum_k q*c - sum_k q as in the tiled kernels; the wave sum
 // is a DPP reduction.
 #ifndef TQ_GEMV_DOT_WAVES

@@ -67,3 +67,17 @@ def test_source_digest_covers_the_decode_kernel_sources():
     names = sorted(os.path.basename(f) for f in b.KERNEL_SOURCES)
     assert names == ["k_gemv.hip", "tq_device.hpp"]
     assert len(b.source_digest()) == 16 and b.source_digest() == b.source_digest()
+
+
+def test_source_digest_ignores_comments_not_code(tmp_path):
+    b = _bench()
+    src = tmp_path / "k.hip"
+    hdr = tmp_path / "d.hpp"
+    hdr.write_text("inline int f(int x) { return x + 1; }\n")
+    b.KERNEL_SOURCES = [str(src), str(hdr)]
+    src.write_text("__global__ void k(int* p) {\n  p[0] = 1;  // store\n}\n")
+    d0 = b.source_digest()
+    src.write_text("/* a kernel */\n__global__ void k(int* p) {\n\n  p[0] = 1;   // the store\n}\n")
+    assert b.source_digest() == d0
+    src.write_text("__global__ void k(int* p) {\n  p[0] = 2;  // store\n}\n")
+    assert b.source_digest() != d0
