@@ -1382,3 +1382,77 @@ def test_format_roundtrip_through_gemv():
     assert torch.equal(back, p)
     vals = host(tq.tq_unpack_codes(f0, "f0", 64 * 256)).reshape(64, 256)
     assert np.array_equal(vals, oracle.unpack_codes(host(p), 256))
+
+
+def test_graph_replays_match_eager():
+    # The launches the benchmark replays from graphs: each call made eagerly,
+    # then all of them captured in one graph, replayed three times with eager
+    # work between the replays (the outputs cleared by a fill kernel first);
+    # every replay's outputs equal the eager ones bit for bit.
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2024)
+    W = torch.randn((4096, 4096), device=DEV, generator=g) * 0.02
+    Wd = torch.randn((2560, 6912), device=DEV, generator=g) * 0.02
+    Wg = torch.randn((6912, 2560), device=DEV, generator=g) * 0.02
+    Wu = torch.randn((6912, 2560), device=DEV, generator=g) * 0.02
+    x1 = torch.randn((1, 4096), device=DEV, generator=g).to(torch.bfloat16)
+    xf = torch.randn((1, 2560), device=DEV, generator=g).to(torch.bfloat16)
+    x4 = torch.randn((4, 6912), device=DEV, generator=g).to(torch.bfloat16)
+    xb = torch.randn((512, 4096), device=DEV, generator=g).to(torch.bfloat16)
+    x64 = torch.randn((64, 4096), device=DEV, generator=g).to(torch.bfloat16)
+    xw = torch.randn((4096, 4096), device=DEV, generator=g).to(torch.bfloat16)
+    pk, sk = tq.tq_pack_ternary(W, "tensor")
+    pd, sd = tq.tq_pack_ternary(Wd, "row")
+    pg, sg = tq.tq_pack_ternary(Wg, "row")
+    pu, su = tq.tq_pack_ternary(Wu, "row")
+    p1, s1 = tq.tq_pack_binary1(W, "row")
+    q1, sx1 = tq.tq_quant_act_int8(x1)
+    q4, sx4 = tq.tq_quant_act_int8(x4)
+    qb, sxb = tq.tq_quant_act_int8(xb)
+    q64, sx64 = tq.tq_quant_act_int8(x64)
+    qw, sxw = tq.tq_quant_act_int8(xw)
+    calls = [
+        ("pack per tensor", lambda: tq.tq_pack_ternary(W, "tensor")),
+        ("fused decode step", lambda: tq.tq_quant_ternary_gemv(x1, pk, sk, 4096, 4096, "tensor",
+                                                                 "f32")),
+        ("prologue quantiser", lambda: tq.tq_quant_act_int8(xb, clamp=(0.05, 40.0), rmsnorm=True,
+                                                              fwht_block=512)),
+        ("gemm 512 rows", lambda: (tq.tq_ternary_gemm(qb, sxb, pk, sk, 4096, 4096, "tensor",
+                                                      "f32"),)),
+        ("gemm 64 rows (register tiles)", lambda: (tq.tq_ternary_gemm(q64, sx64, pk, sk, 4096,
+                                                                      4096, "tensor", "f32"),)),
+        ("gemm 4096^3 (wide tiles)", lambda: (tq.tq_ternary_gemm(qw, sxw, pk, sk, 4096, 4096,
+                                                                 "tensor", "bf16"),)),
+        ("matrix-core gemv, 4 tokens", lambda: (tq.tq_ternary_gemv(q4, sx4, pd, sd, 2560, 6912,
+                                                                   "row", "f32"),)),
+        ("1-bit gemv", lambda: (tq.tq_binary1_gemv(q1, sx1, p1, s1, 4096, 4096, "row", "f32"),)),
+        ("swiglu pair", lambda: tq.tq_swiglu_gemv(xf, pg, sg, pu, su, 6912, 2560)),
+    ]
+    eager = []
+    for name, fn in calls:
+        eager.append([t.clone() for t in fn()])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for name, fn in calls:
+            fn()                                   # allocations and first use outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        outs = [fn() for name, fn in calls]
+    other = torch.randn((512, 512), device=DEV, generator=g)
+    for r in range(3):
+        for o in outs:
+            for t in o:
+                t.zero_()
+        other = other @ other.t() * 1e-3            # unrelated eager work between replays
+        graph.replay()
+        torch.cuda.synchronize()
+        for (name, _), o, e in zip(calls, outs, eager):
+            for i, (t, te) in enumerate(zip(o, e)):
+                same = torch.equal(t.view(torch.uint8) if t.dtype != torch.uint8 else t,
+                                   te.view(torch.uint8) if te.dtype != torch.uint8 else te)
+                assert same, f"replay {r}: {name}, output {i} differs from the eager call"
+    say("graph replays: all outputs bit-identical to the eager calls")
