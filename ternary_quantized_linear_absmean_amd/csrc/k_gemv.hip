@@ -1155,30 +1155,46 @@ __global__ __launch_bounds__(kMfmaMaxWaves* kWave) void k_gemv_mfma(
     for (int i = 0; i < 4; ++i) red[(nw + wave) * 256 + (4 * fg + i) * 16 + fr] = acc2[i];
   }
   __syncthreads();
-  if (!eout) return;
-  int tot = 0;
-  for (int w = 0; w < nw; ++w) tot += red[w * 256 + tid];
-  const int64_t o = static_cast<int64_t>(em) * N + n0 + en;
-  if constexpr (DUAL) {
-    int tot2 = 0;
-    for (int w = 0; w < nw; ++w) tot2 += red[(nw + w) * 256 + tid];
-    const float gv = static_cast<float>(tot) * (egam * esx);
-    const float uv = static_cast<float>(tot2) * (egam2 * esx);
-    const float h = fminf(fmaxf(gv / (1.f + expf(-gv)) * uv, -clampv), clampv);
-    if (ydt == TQ_F32)
-      static_cast<float*>(Y)[o] = h;
-    else
-      static_cast<uint16_t*>(Y)[o] = f32_to_bf16(h);
-    return;
-  }
-  if (ydt == TQ_I32) {
-    static_cast<int*>(Y)[o] = tot;
-  } else {
-    const float y = static_cast<float>(tot) * (egam * esx);
-    if (ydt == TQ_F32)
-      static_cast<float*>(Y)[o] = y;
-    else
-      static_cast<uint16_t*>(Y)[o] = f32_to_bf16(y);
+  // output t = 16 m + n of the tile: token m, row n0 + n
+  auto emit = [&](int t, float gam, float gam2, float sxe) {
+    int tot = 0;
+    for (int w = 0; w < nw; ++w) tot += red[w * 256 + t];
+    const int64_t o = static_cast<int64_t>(t >> 4) * N + n0 + (t & 15);
+    if constexpr (DUAL) {
+      int tot2 = 0;
+      for (int w = 0; w < nw; ++w) tot2 += red[(nw + w) * 256 + t];
+      const float gv = static_cast<float>(tot) * (gam * sxe);
+      const float uv = static_cast<float>(tot2) * (gam2 * sxe);
+      const float h = fminf(fmaxf(gv / (1.f + expf(-gv)) * uv, -clampv), clampv);
+      if (ydt == TQ_F32)
+        static_cast<float*>(Y)[o] = h;
+      else
+        static_cast<uint16_t*>(Y)[o] = f32_to_bf16(h);
+      return;
+    }
+    if (ydt == TQ_I32) {
+      static_cast<int*>(Y)[o] = tot;
+    } else {
+      const float y = static_cast<float>(tot) * (gam * sxe);
+      if (ydt == TQ_F32)
+        static_cast<float*>(Y)[o] = y;
+      else
+        static_cast<uint16_t*>(Y)[o] = f32_to_bf16(y);
+    }
+  };
+  if (eout) emit(tid, egam, egam2, esx);
+  // fewer than 256 threads (one to three waves, K < 1024): the rest of the
+  // tile, its operands loaded here
+  for (int t = tid + nt; t < kMfmaRows * kMfmaRows; t += nt) {
+    const int m = t >> 4, n = t & 15;
+    if (m >= M || n0 + n >= N) continue;
+    float gam = 0.f, gam2 = 0.f, sxe = 0.f;
+    if (ydt != TQ_I32) {
+      gam = scale[per_row ? n0 + n : 0];
+      if (DUAL) gam2 = scale2[per_row ? n0 + n : 0];
+      sxe = SRC == 0 ? sx_io[m] : tok_sx[m];
+    }
+    emit(t, gam, gam2, sxe);
   }
 }
 

@@ -762,6 +762,9 @@ FUSED_CASES = [
     (3, 45, 6912, "bf16", "row"),        # matrix-core kernel, two blocks per wave
     (4, 19, 256, "bf16", "tensor"),      # matrix-core kernel, one wave
     (16, 30, 2560, "f32", "row"),        # past four tokens: quantiser + GEMV
+    (16, 40, 6912, "f32", "row"),        # fp32 tokens staged in two register batches
+    (16, 33, 768, "bf16", "tensor"),     # 48 units per token: per-unit maxima
+    (5, 21, 1024, "f32", "row"),         # 64 units per token: a wave spans two tokens
     (2, 90, 32768, "bf16", "row"),
     (1, 9, 65536, "f32", "tensor"),
 ]
@@ -834,11 +837,14 @@ def test_gemv_kernel_boundaries(M, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(2, 19, 256), (5, 70, 16384), (16, 37, 6912), (16, 40, 7424),
-                                   (16, 21, 7680), (9, 33, 4096)])
+                                   (16, 21, 7680), (9, 33, 4096), (16, 19, 256), (12, 40, 512),
+                                   (16, 35, 768)])
 def test_gemv_matrix_core_boundaries(M, N, K):
     # 2..16 tokens on matrix cores: one wave (K = 256), four blocks per wave
     # (K = 16384), token staging above 64 KiB of LDS up to its 120 KiB limit,
-    # and one step past it (K = 7680 at 16 tokens, another kernel)
+    # and one step past it (K = 7680 at 16 tokens, another kernel); fewer
+    # threads than the 256 outputs of a tile (K = 256, 512, 768 with more
+    # tokens than four per wave)
     q = ti.random_int8(41 + M + K, M, K)
     w = ti.random_ternary(42 + K, N, K)
     packed = oracle.pack_codes(w)
@@ -917,7 +923,7 @@ def _check1(qd, sxd, pd, sd, N, K, gran, q, packed, scale, sx):
 # slices, a slice cut short), 2..16 tokens on matrix cores (K % 256 == 0),
 # and the simple kernel (other K)
 BIN1_CASES = [(1, 4096, 4096), (1, 70, 2560), (1, 37, 16384), (1, 45, 8320), (1, 19, 128), (1, 23, 4160), (1, 11, 64),
-              (2, 33, 256), (4, 300, 2560), (16, 40, 6912), (7, 21, 16384),
+              (2, 33, 256), (4, 300, 2560), (16, 40, 6912), (7, 21, 16384), (16, 29, 256),
               (1, 9, 8), (3, 17, 24), (16, 5, 1000), (1, 30, 2600), (5, 12, 136)]
 
 
@@ -1002,7 +1008,8 @@ def _assert_h_close(h, href):
 
 SWIGLU_CASES = [(1, 6912, 2560, "bf16", "row"), (4, 6912, 2560, "f32", "row"),
                 (16, 300, 4096, "bf16", "tensor"), (2, 33, 256, "f32", "row"),
-                (3, 70, 1000, "bf16", "row"), (1, 50, 4100, "f32", "tensor")]
+                (3, 70, 1000, "bf16", "row"), (1, 50, 4100, "f32", "tensor"),
+                (16, 33, 512, "f32", "row")]   # two waves for a 16 x 16 tile
 
 
 @pytest.mark.parametrize("M,N,K,dtype,gran", SWIGLU_CASES)
