@@ -567,8 +567,12 @@ def extra_binary1(torch, ti, tq, dev, keep=list):
 
 def extra_ffn_decode(torch, ti, tq, dev, keep=list):
     """Decode FFN with the SwiGLU clamp (gate/up 6912x2560, down 2560x6912,
-    per-row scales): tq_ffn_swiglu_decode, two launches per step, the three
-    packed matrices rotating over 40 sets (about 530 MB)."""
+    per-row scales): tq_ffn_swiglu_decode, the three packed matrices rotating
+    over 40 sets (about 530 MB).  Each stage quantises inside its GEMV
+    launch at one token, and at up to four tokens where M * K <= 16384;
+    otherwise the quantiser runs as a launch of its own (the library's
+    dispatch rule, restated here to label the record): two launches per step
+    at one token, three at four, four at sixteen."""
     d_model, d_ffn = 2560, 6912
     mats = []
     for W in (ti.normal_weights(ti.weight_seed(ti.WORKLOADS["ffn"]["cfg"], 2), d_ffn, d_model),
@@ -589,8 +593,10 @@ def extra_ffn_decode(torch, ti, tq, dev, keep=list):
         nbytes = (wbytes + 2 * b * d_model + (b * d_model + 4 * b) + 2 * 4 * b * d_ffn +
                   (b * d_ffn + 4 * b) + 4 * b * d_model)
         gb = nbytes / t / 1e9
+        fused = [b == 1 or (b <= 4 and b * k <= 16384) for k in (d_model, d_ffn)]
         out[f"b{b}"] = {"us": round(t * 1e6, 3), "bytes": nbytes, "GBs": round(gb, 1),
-                        "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1), "launches": 2}
+                        "pct_hbm_peak": round(100 * gb / HBM_PEAK_GBS, 1),
+                        "launches": sum(1 if f else 2 for f in fused)}
     del sets
     return {"ffn_swiglu_decode": out}
 

@@ -242,10 +242,11 @@ tq_status tq_swiglu_gemv(const void* X, tq_dtype xdt, int64_t M, const tq_act_op
                          int64_t N, int64_t K, float clamp_val, int8_t* q, float* sx,
                          void* H, tq_dtype hdt, hipStream_t stream);
 
-/* The whole decode FFN in two launches: tq_swiglu_gemv (N = d_ffn,
+/* The whole decode FFN as two calls, tq_swiglu_gemv (N = d_ffn,
  * K = d_model, H fp32) and then tq_quant_ternary_gemv(H, TQ_F32, M, plain
  * quantiser, packed_down [d_model, d_ffn/4], scale_down, g, d_model, d_ffn,
- * q_h, sx_h, Y, ydt).  opts applies to X only; H is quantised per token with
+ * q_h, sx_h, Y, ydt): two launches where both stages fuse their quantiser
+ * (one token), up to four where neither does.  opts applies to X only; H is quantised per token with
  * the plain quantiser (eps 1e-6, no clamp).  Every check of both stages runs
  * before anything is launched.  All buffers are the caller's: q_x [M,
  * d_model], sx_x [M], H [M, d_ffn] fp32, q_h [M, d_ffn], sx_h [M], Y [M,
