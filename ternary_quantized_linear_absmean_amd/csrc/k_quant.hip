@@ -358,6 +358,27 @@ __device__ inline void square_bin_add(unsigned long long* bins, float sq) {
   atomicAdd(&bins[e ? e : 1u], static_cast<unsigned long long>(m));
 }
 
+// fp64 wave sum in the six DPP levels of wave_isum_last, each double moved
+// as its two words; lane 63 holds the sum.
+template <int CTRL, int ROWS = 0xF>
+__device__ inline double dpp_get_f64(double v) {
+  const unsigned long long u = static_cast<unsigned long long>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(dpp_get<CTRL, ROWS>(static_cast<int>(u)));
+  const uint32_t hi = static_cast<uint32_t>(dpp_get<CTRL, ROWS>(static_cast<int>(u >> 32)));
+  return __longlong_as_double(
+      static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
+__device__ inline double wave_sum_last(double v) {
+  v += dpp_get_f64<0xB1>(v);
+  v += dpp_get_f64<0x4E>(v);
+  v += dpp_get_f64<0x141>(v);
+  v += dpp_get_f64<0x140>(v);
+  v += dpp_get_f64<0x142, 0xA>(v);
+  v += dpp_get_f64<0x143, 0xC>(v);
+  return v;
+}
+
 // One block of NW waves per token.  Each wave holds NB 512-element segments
 // in registers (segment wave + NW * j), lane l holding elements 8l .. 8l+7
 // of each; the token is read once.
@@ -406,8 +427,8 @@ __global__ __launch_bounds__(NW * kWave) void k_quant_prologue(
     for (int j = 0; j < NB; ++j)
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc += static_cast<double>(v[j][e] * v[j][e]);
-    acc = wave_sum(acc);
-    if (lane == 0) part[wave] = acc;
+    acc = wave_sum_last(acc);
+    if (lane == kWave - 1) part[wave] = acc;
     __syncthreads();
     double S = 0.0;
 #pragma unroll
