@@ -1059,6 +1059,59 @@ def test_ffn_swiglu_decode_workload(b):
     np.testing.assert_array_equal(host(Y2), host(Y))
 
 
+# ------------------------------------------------- decode family, random shapes
+
+def _random_decode_cases(n=40, seed=20261204):
+    # seeded shapes for the 1..16-token kernels: M uniform in 1..16, K a
+    # multiple of 256 (matrix-core kernels, down to one or two waves, which
+    # leave fewer threads than a 16 x 16 tile has outputs), of 64 or of 16,
+    # up to 8192; N in 1..300
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        M = int(rng.integers(1, 17))
+        unit = int(rng.choice([256, 64, 16], p=[0.6, 0.25, 0.15]))
+        K = unit * int(rng.integers(1, 8192 // unit + 1))
+        N = int(rng.integers(1, 301))
+        gran = str(rng.choice(["tensor", "row"]))
+        xdt = str(rng.choice(["bf16", "f32"]))
+        if i % 4 == 0:  # one to three waves and more than four tokens per wave
+            M, K = 5 + i % 12, 256 * (1 + i % 3)
+        cases.append((i, M, N, K, gran, xdt))
+    return cases
+
+
+@pytest.mark.parametrize("i,M,N,K,gran,xdt", _random_decode_cases())
+def test_decode_family_random_shapes(i, M, N, K, gran, xdt):
+    q = ti.random_int8(12000 + i, M, K)
+    packed = oracle.pack_codes(ti.random_ternary(13000 + i, N, K))
+    up = oracle.pack_codes(ti.random_ternary(13500 + i, N, K))
+    scale = (np.abs(ti.activations(14000 + i, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    scale_up = (np.abs(ti.activations(14200 + i, 1, N, dtype="f32")[0]) + 0.01).astype(np.float32)
+    sx = (np.abs(ti.activations(14500 + i, 1, M, dtype="f32")[0]) * 0.01 + 1e-3).astype(np.float32)
+    sc, scu = (scale, scale_up) if gran == "row" else (scale[:1], scale_up[:1])
+    say(f"decode random #{i} M={M} N={N} K={K} {gran} {xdt}")
+    # int8 tokens, ternary and 1-bit codes
+    _check_outputs(tq.tq_ternary_gemv, dev(q), dev(sx), dev(packed), dev(sc), N, K, gran,
+                   q, packed, sc, sx)
+    signs = oracle.pack_signs(np.where(ti.normal_weights(16000 + i, N, K) >= 0, 1, -1)
+                              .astype(np.int8))
+    _check1(dev(q), dev(sx), dev(signs), dev(sc), N, K, gran, q, signs, sc, sx)
+    # float tokens: the quantiser fused (or not) with the GEMV and the SwiGLU pair
+    X = ti.activations(15000 + i, M, K, dtype=xdt)
+    qr, sr = oracle.quant_act_int8(X)
+    Xd = x_to_device(X, xdt)
+    Y, qd, sxd = tq.tq_quant_ternary_gemv(Xd, dev(packed), dev(sc), N, K, gran, "f32")
+    np.testing.assert_array_equal(host(qd), qr)
+    np.testing.assert_array_equal(f32_bits(host(sxd)), f32_bits(sr))
+    g = oracle.epilogue(oracle.contract(qr, packed, K), sc, sr)
+    assert_y_close(host(Y), g)
+    u = oracle.epilogue(oracle.contract(qr, up, K), scu, sr)
+    H, qh, sxh = tq.tq_swiglu_gemv(Xd, dev(packed), dev(sc), dev(up), dev(scu), N, K, gran, 10.0)
+    np.testing.assert_array_equal(host(qh), qr)
+    _assert_h_close(host(H), oracle.swiglu_clamped(g, u, 10.0))
+
+
 # ------------------------------------------------------------ backward input
 
 # Bounds of the backward products.  The products dY * gamma * w are exact, so
