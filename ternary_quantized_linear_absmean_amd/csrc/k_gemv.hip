@@ -552,6 +552,23 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
       }
     }
   }
+  // The codes workgroup 0 writes back (SRC != 0) are stored at the end of
+  // the kernel: stores and loads share one counter, so a store issued here
+  // would make the next wait for a token load also wait for the weights.
+  uint32_t qk[BITS == 2 && SRC != 0 ? kUnitsL : 1][4];
+  auto flush_q = [&]() {
+    if constexpr (BITS == 2 && SRC != 0) {
+      if (stager && blockIdx.x == 0) {
+#pragma unroll
+        for (int i = 0; i < kUnitsL; ++i) {
+          const int u = tid + kStageNT * i;
+          if (u < (K >> 4))
+            *reinterpret_cast<uint4*>(q_out + 16 * static_cast<int64_t>(u)) =
+                make_uint4(qk[i][0], qk[i][1], qk[i][2], qk[i][3]);
+        }
+      }
+    }
+  };
   // 5. int8 token -> transposed, swizzled LDS; byte sums.  Without an eta
   // clamp every |x| <= eta and the codes need no clamp (quant_word_unclamped).
   auto stage_units = [&](auto clamped) {
@@ -581,7 +598,7 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
             }
             d[b] = CL ? quant_word(v[0], v[1], v[2], v[3], sc)
                       : quant_word_unclamped(v[0], v[1], v[2], v[3], sc);
-            if (blockIdx.x == 0) reinterpret_cast<uint32_t*>(q_out)[4 * u + b] = d[b];
+            qk[i][b] = d[b];
           }
           bsum = byte_sum(d[b], bsum);
         }
@@ -760,6 +777,7 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
   if constexpr (PRE) {
     if (rg + step >= nrg) {
       finish_first(rg, ra);
+      flush_q();
       return;
     }
     load_row(rg + step, rb);
@@ -799,6 +817,7 @@ __global__ __launch_bounds__(kNTd) void k_gemv_dot(
       rg += step;
     }
   }
+  flush_q();
 }
 
 // Second matrix of the SwiGLU pair (DUAL launches only).
