@@ -209,21 +209,83 @@ __device__ inline float lane_xor(float v) {
   }
 }
 
-// The lower lane of a pair takes v + other, the upper other - v: both are
-// other + (+-1 * v), the product exact, so the one rounding is that of the
-// sum or difference (and the lane move folds into the add).
+// Cross-lane butterflies with the sign carried: a lane takes own + k * other
+// with k = +1 in the lower lane of a pair and -1 in the upper one, one fused
+// multiply-add of an exact product, so one rounding, that of the sum or
+// difference.  The upper lane's result is the negated butterfly difference
+// (round to nearest even is symmetric); partners of a stage differ only in
+// that stage's lane bit, so they always carry the same sign, and after the
+// six stages lane l holds its values times (-1)^popcount(l).  For lane
+// distances 1 and 2 the lane move is the fma's own DPP source operand
+// (v_fmac_f32 with DPP, written out: the compiler does not fold a move into
+// it), for 4 and 8 a DPP move and then the fma with the second DPP step;
+// each block starts with the two wait states a DPP read of a VGPR written by
+// the instruction before it needs.  16 and 32 move through permlane swaps.
+#define TQ_FMAC_DPP8(CTRL)                                                              \
+  asm volatile("s_nop 1\n\t"                                                            \
+               "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+               "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+               "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+               "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+               "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+               "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+               "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+               "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf bound_ctrl:1"      \
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]),     \
+                 "+v"(v[6]), "+v"(v[7])                                                   \
+               : "v"(k))
+#define TQ_MOV_FMAC_DPP8(CTRL1, CTRL2)                                                   \
+  do {                                                                                  \
+    float t0, t1, t2, t3, t4, t5, t6, t7;                                               \
+    asm volatile("s_nop 1\n\t"                                                          \
+                 "v_mov_b32_dpp %0, %8 " CTRL1 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_mov_b32_dpp %1, %9 " CTRL1 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_mov_b32_dpp %2, %10 " CTRL1 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_mov_b32_dpp %3, %11 " CTRL1 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_mov_b32_dpp %4, %12 " CTRL1 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_mov_b32_dpp %5, %13 " CTRL1 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_mov_b32_dpp %6, %14 " CTRL1 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_mov_b32_dpp %7, %15 " CTRL1 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "s_nop 1\n\t"                                                          \
+                 "v_fmac_f32_dpp %8, %0, %16 " CTRL2 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_fmac_f32_dpp %9, %1, %16 " CTRL2 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_fmac_f32_dpp %10, %2, %16 " CTRL2 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_fmac_f32_dpp %11, %3, %16 " CTRL2 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_fmac_f32_dpp %12, %4, %16 " CTRL2 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_fmac_f32_dpp %13, %5, %16 " CTRL2 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_fmac_f32_dpp %14, %6, %16 " CTRL2 " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t" \
+                 "v_fmac_f32_dpp %15, %7, %16 " CTRL2 " row_mask:0xf bank_mask:0xf bound_ctrl:1" \
+                 : "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5),        \
+                   "=&v"(t6), "=&v"(t7), "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]),    \
+                   "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])                           \
+                 : "v"(k));                                                             \
+  } while (0)
+
 template <int LM>
 __device__ inline void fwht_lane_stage(float (&v)[8], int lane) {
-  const float sgn = (lane & LM) != 0 ? -1.f : 1.f;
+  const float k = (lane & LM) != 0 ? -1.f : 1.f;
+  if constexpr (LM == 1) {
+    TQ_FMAC_DPP8("quad_perm:[1,0,3,2]");
+  } else if constexpr (LM == 2) {
+    TQ_FMAC_DPP8("quad_perm:[2,3,0,1]");
+  } else if constexpr (LM == 4) {  // half-row mirror, then quad reversal: lane ^ 4
+    TQ_MOV_FMAC_DPP8("row_half_mirror", "quad_perm:[3,2,1,0]");
+  } else if constexpr (LM == 8) {  // row mirror, then half-row mirror: lane ^ 8
+    TQ_MOV_FMAC_DPP8("row_mirror", "row_half_mirror");
+  } else {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = lane_xor<LM>(v[e]) + sgn * v[e];
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(lane_xor<LM>(v[e]), k, v[e]);
+  }
 }
+#undef TQ_FMAC_DPP8
+#undef TQ_MOV_FMAC_DPP8
 
 // In-place FWHT of one 512-block held by a wave: lane l holds elements
 // 8l .. 8l+7.  Stages h = 1, 2, 4 pair elements inside a lane; stages
 // h = 8 .. 256 pair lane l with lane l ^ (h/8).  The lower index of a pair
-// takes a + b and the upper a - b, a being the lower element.
-__device__ inline void fwht512_wave(float (&v)[8]) {
+// takes a + b and the upper a - b, a being the lower element.  Returns the
+// lane's sign s (+-1): v then holds s times the transform.
+__device__ inline float fwht512_wave(float (&v)[8]) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -242,6 +304,7 @@ __device__ inline void fwht512_wave(float (&v)[8]) {
   fwht_lane_stage<8>(v, lane);
   fwht_lane_stage<16>(v, lane);
   fwht_lane_stage<32>(v, lane);
+  return (__builtin_popcount(lane) & 1) ? -1.f : 1.f;
 }
 
 template <typename T, bool VEC>
@@ -254,11 +317,11 @@ __global__ __launch_bounds__(kNT) void k_fwht512(const T* __restrict__ X, int64_
   const int64_t off = seg * 512 + 8 * lane;
   float v[8];
   load8<T, VEC>(X + off, 8, v);
-  fwht512_wave(v);
-  if (normalize) {
+  const float sg = fwht512_wave(v);
+  // the lane's sign and the factor in one exact product
+  const float f = normalize ? sg * kFwhtNorm : sg;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = v[e] * kFwhtNorm;
-  }
+  for (int e = 0; e < 8; ++e) v[e] = v[e] * f;
   float* y = Y + off;
   if (VEC) {
     reinterpret_cast<float4*>(y)[0] = make_float4(v[0], v[1], v[2], v[3]);
@@ -467,9 +530,9 @@ __global__ __launch_bounds__(NW * kWave) void k_quant_prologue(
   if (fwht) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      fwht512_wave(v[j]);
+      const float f = fwht512_wave(v[j]) * kFwhtNorm;  // +-kFwhtNorm, exact
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[j][e] = v[j][e] * kFwhtNorm;
+      for (int e = 0; e < 8; ++e) v[j][e] = v[j][e] * f;
     }
   }
   float amax = 0.f;
