@@ -261,6 +261,19 @@ __device__ inline float lane_xor(float v) {
                  : "v"(k));                                                             \
   } while (0)
 
+// The plain form for the standalone transform, whose fp32 output keeps the
+// butterflies' signed zeros: the lower lane of a pair takes other + v, the
+// upper other - v (other + (+-1 * v): the product is exact, so the one
+// rounding is that of the sum; the lane move folds into the add).  The
+// carried-sign form below can turn a zero difference into -0.0, which only
+// the prologue, whose codes and maximum do not see the sign of zero, takes.
+template <int LM>
+__device__ inline void fwht_lane_stage_plain(float (&v)[8], int lane) {
+  const float sgn = (lane & LM) != 0 ? -1.f : 1.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = lane_xor<LM>(v[e]) + sgn * v[e];
+}
+
 template <int LM>
 __device__ inline void fwht_lane_stage(float (&v)[8], int lane) {
   const float k = (lane & LM) != 0 ? -1.f : 1.f;
@@ -285,7 +298,7 @@ __device__ inline void fwht_lane_stage(float (&v)[8], int lane) {
 // h = 8 .. 256 pair lane l with lane l ^ (h/8).  The lower index of a pair
 // takes a + b and the upper a - b, a being the lower element.  Returns the
 // lane's sign s (+-1): v then holds s times the transform.
-__device__ inline float fwht512_wave(float (&v)[8]) {
+__device__ inline void fwht8_in_lane(float (&v)[8]) {
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -297,6 +310,10 @@ __device__ inline float fwht512_wave(float (&v)[8]) {
       }
     }
   }
+}
+
+__device__ inline float fwht512_wave(float (&v)[8]) {
+  fwht8_in_lane(v);
   const int lane = threadIdx.x & (kWave - 1);
   fwht_lane_stage<1>(v, lane);
   fwht_lane_stage<2>(v, lane);
@@ -305,6 +322,18 @@ __device__ inline float fwht512_wave(float (&v)[8]) {
   fwht_lane_stage<16>(v, lane);
   fwht_lane_stage<32>(v, lane);
   return (__builtin_popcount(lane) & 1) ? -1.f : 1.f;
+}
+
+// the same transform in the plain form, signed zeros as the butterflies give
+__device__ inline void fwht512_wave_plain(float (&v)[8]) {
+  fwht8_in_lane(v);
+  const int lane = threadIdx.x & (kWave - 1);
+  fwht_lane_stage_plain<1>(v, lane);
+  fwht_lane_stage_plain<2>(v, lane);
+  fwht_lane_stage_plain<4>(v, lane);
+  fwht_lane_stage_plain<8>(v, lane);
+  fwht_lane_stage_plain<16>(v, lane);
+  fwht_lane_stage_plain<32>(v, lane);
 }
 
 template <typename T, bool VEC>
@@ -317,11 +346,11 @@ __global__ __launch_bounds__(kNT) void k_fwht512(const T* __restrict__ X, int64_
   const int64_t off = seg * 512 + 8 * lane;
   float v[8];
   load8<T, VEC>(X + off, 8, v);
-  const float sg = fwht512_wave(v);
-  // the lane's sign and the factor in one exact product
-  const float f = normalize ? sg * kFwhtNorm : sg;
+  fwht512_wave_plain(v);
+  if (normalize) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = v[e] * f;
+    for (int e = 0; e < 8; ++e) v[e] = v[e] * kFwhtNorm;
+  }
   float* y = Y + off;
   if (VEC) {
     reinterpret_cast<float4*>(y)[0] = make_float4(v[0], v[1], v[2], v[3]);

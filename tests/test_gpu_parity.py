@@ -308,6 +308,22 @@ def test_fwht512_integer_exact_and_spike():
     assert abs(np.max(np.abs(Y)) - 4.4194) < 1e-4
 
 
+@pytest.mark.parametrize("normalize", [False, True])
+def test_fwht512_signed_zeros(normalize):
+    # outputs that are exact zeros, from constant rows, rows of -0.0 and of
+    # mixed zeros, and a row whose halves cancel: the signs of the zeros
+    # must be the butterflies' own
+    rows = [np.full(512, 3.0), np.full(512, -0.0), np.where(np.arange(512) % 2, -0.0, 0.0),
+            np.concatenate([np.full(256, 1.5), np.full(256, -1.5)]),
+            np.where(np.arange(512) % 3 == 0, 2.0**-20, -(2.0**-20))]
+    X = np.stack(rows).astype(np.float32)
+    say(f"fwht signed zeros norm={normalize}")
+    Y = host(tq.tq_fwht512(dev(X), normalize))
+    Yr = oracle.fwht512(X, normalize)
+    assert np.any(Yr == 0) and np.any(np.signbit(Yr) & (Yr == 0))
+    np.testing.assert_array_equal(f32_bits(Y), f32_bits(Yr))
+
+
 # ----------------------------------------------------------------- prologue
 
 def test_prologue_bitlinear_workload():
